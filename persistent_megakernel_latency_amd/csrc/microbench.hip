@@ -1,0 +1,358 @@
+// Microbenchmarks that size the megakernel's tiles and synchronisation on gfx950.
+//
+// The Hazy Research Llama-1B megakernel, as the persistent-threads history page
+// (section 6) describes it, wins by keeping weight loads streaming across
+// operator boundaries; whether that is possible depends on three numbers of the
+// machine, measured here:
+//   1. the streaming-read ceiling of HBM for tile-shaped reads (contiguous
+//      64 KiB blocks, as a worker's staging slot loads them), with and without
+//      an agent-scope acquire/release per tile;
+//   2. the throughput of device-scope atomics on one address (the work queue's
+//      head and a shared dependency counter are such addresses);
+//   3. the latency of a release/acquire round trip between two workgroups on
+//      different XCDs (each XCD has its own L2).
+// Each result is printed as one JSON line.  All waits are bounded by a
+// wall-clock budget read from s_memrealtime (100 MHz), so no kernel here can
+// spin forever.
+#include <hip/hip_runtime.h>
+
+#include <chrono>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#define CHECK(x)                                                              \
+  do {                                                                        \
+    hipError_t e_ = (x);                                                      \
+    if (e_ != hipSuccess) {                                                   \
+      fprintf(stderr, "HIP error %s at %s:%d\n", hipGetErrorString(e_),       \
+              __FILE__, __LINE__);                                            \
+      exit(1);                                                                \
+    }                                                                         \
+  } while (0)
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+static constexpr unsigned long long kSpinBudgetTicks = 200000000ull;  // 2 s
+
+// ---------------------------------------------------------------------------
+// 1. tile-shaped streaming read.  Block b reads blocks of 64 KiB (16 uint4 per
+// thread, 256 threads) at tile index b, b+grid, ...  `mode` bits:
+//   1: an agent-scope acquire fence before each tile;
+//   2: a release fence plus a relaxed atomic add on a shared counter after
+//      each tile (the fenced publish pattern);
+//   4: non-temporal weight loads;
+//   8: fence-free publish: 16 results stored with device-coherent (sc1)
+//      stores, a wait for their completion, then a relaxed atomic add;
+//  16: fence-free consume: a device-coherent poll of a counter, then the
+//      tile's 8 KiB input vector read with device-coherent (sc1) loads;
+//  32: as 16 but the input vector read with plain loads.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_tile_read(const uint4* __restrict__ src,
+                                                   long n_tiles, int mode,
+                                                   unsigned* counters,
+                                                   unsigned* sink,
+                                                   const float* xvec,
+                                                   float* results) {
+  const int t = threadIdx.x;
+  uint32_t acc = 0;
+  __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc((void*)xvec, 0, 8192, 0x00020000);
+  for (long tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
+    if (mode & 1) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (mode & 48) {
+      const unsigned c = __hip_atomic_load(counters + 1024 + (blockIdx.x & 7) * 64, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+      u32x4 xa, xb;
+      if (mode & 16) {
+        xa = __builtin_amdgcn_raw_buffer_load_b128(xr, t * 32, 0, 16);
+        xb = __builtin_amdgcn_raw_buffer_load_b128(xr, t * 32 + 16, 0, 16);
+      } else {
+        xa = __builtin_amdgcn_raw_buffer_load_b128(xr, t * 32, 0, 0);
+        xb = __builtin_amdgcn_raw_buffer_load_b128(xr, t * 32 + 16, 0, 0);
+      }
+      acc += c ^ xa.x ^ xa.w ^ xb.y ^ xb.z;
+    }
+    const u32x4* p = reinterpret_cast<const u32x4*>(src) + tile * 4096;  // 4096 x 16 B = 64 KiB
+    u32x4 v[16];
+    if (mode & 4) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = __builtin_nontemporal_load(p + j * 256 + t);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = p[j * 256 + t];
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+    if (mode & 2) {
+      if (t == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __hip_atomic_fetch_add(counters + (blockIdx.x & 7) * 64, 1u,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    if (mode & 8) {
+      if (t < 64) {
+        if (t < 16)
+          __hip_atomic_store(results + (blockIdx.x * 16 + t), (float)(acc & 255u), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0);
+        if (t == 0)
+          __hip_atomic_fetch_add(counters + (blockIdx.x & 7) * 64, 1u, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+  if (acc == 0x9e3779b9u) sink[blockIdx.x * blockDim.x + t] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// 2. same-address atomics: lane 0 of every block does `iters` fetch-adds on
+// ctr[(block % n_addr) * 64].
+// ---------------------------------------------------------------------------
+__global__ void k_atomic(unsigned* ctr, int iters, int n_addr, unsigned* sink) {
+  if (threadIdx.x != 0) return;
+  unsigned s = 0;
+  unsigned* c = ctr + (blockIdx.x % n_addr) * 64;
+  for (int i = 0; i < iters; ++i)
+    s += __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  sink[blockIdx.x] = s;
+}
+
+// ---------------------------------------------------------------------------
+// 3. release/acquire ping-pong between block 0 and block `peer`.  With the
+// round-robin dispatch of workgroups over the 8 XCDs, peer=1 sits on another
+// XCD and peer=8 on the same one.  Blocks other than the two exit at once.
+// out[0] = total ticks, out[1] = 1 if a wait ran out of budget.
+// ---------------------------------------------------------------------------
+__global__ void k_pingpong(unsigned* flags, int iters, int peer,
+                           unsigned long long* out) {
+  if (threadIdx.x != 0) return;
+  if (blockIdx.x != 0 && (int)blockIdx.x != peer) return;
+  const bool first = blockIdx.x == 0;
+  unsigned* mine = flags + (first ? 0 : 64);
+  unsigned* theirs = flags + (first ? 64 : 0);
+  const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+  bool timed_out = false;
+  for (int i = 1; i <= iters && !timed_out; ++i) {
+    if (first) __hip_atomic_store(mine, (unsigned)i, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned long long w0 = __builtin_amdgcn_s_memrealtime();
+    while (__hip_atomic_load(theirs, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < (unsigned)i) {
+      if (__builtin_amdgcn_s_memrealtime() - w0 > kSpinBudgetTicks) { timed_out = true; break; }
+    }
+    if (!first) __hip_atomic_store(mine, (unsigned)i, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  const unsigned long long t1 = __builtin_amdgcn_s_memrealtime();
+  if (first) {
+    out[0] = t1 - t0;
+    out[1] = timed_out ? 1ull : 0ull;
+  } else if (timed_out) {
+    out[1] = 1ull;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 4. cross-XCD message passing: pair k = (block 2k producer, block 2k+1
+// consumer); round-robin dispatch puts them on different XCDs.  The producer
+// writes `words` words of value i, publishes flag = i; the consumer waits for
+// flag >= i, reads the words, counts those != i, then acks i.  proto:
+//   0: producer device-coherent (sc1) stores + wait; consumer sc1 loads
+//   1: producer sc1 stores + wait; consumer plain loads
+//   2: producer plain stores + agent release fence; consumer agent acquire
+//      fence + plain loads (the compiler's memory-model lowering)
+//   3: producer plain stores + wait (no fence); consumer sc1 loads
+// errs[0] = stale words seen, errs[1] = waits that ran out of budget,
+// errs[2] = ticks spent by pair 0's consumer.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void k_mp(unsigned* flags, unsigned* data, int words, int iters,
+                                           int proto, unsigned long long* errs) {
+  const int pair = blockIdx.x >> 1;
+  const bool producer = (blockIdx.x & 1) == 0;
+  unsigned* flag = flags + pair * 128;
+  unsigned* ack = flags + pair * 128 + 64;
+  unsigned* d = data + (size_t)pair * words;
+  const int lane = threadIdx.x;
+  unsigned long long stale = 0, timeouts = 0;
+  const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+  for (int i = 1; i <= iters; ++i) {
+    if (producer) {
+      const unsigned long long w0 = __builtin_amdgcn_s_memrealtime();
+      bool ok = true;
+      while (__hip_atomic_load(ack, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (unsigned)(i - 1)) {
+        if (__builtin_amdgcn_s_memrealtime() - w0 > kSpinBudgetTicks) { ok = false; break; }
+      }
+      if (!ok) { ++timeouts; break; }
+      if (proto == 2) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      for (int w = lane; w < words; w += 64) {
+        if (proto == 0 || proto == 1)
+          __hip_atomic_store(d + w, (unsigned)i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else
+          d[w] = (unsigned)i;
+      }
+      if (proto == 2) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      else __builtin_amdgcn_s_waitcnt(0);
+      if (lane == 0) __hip_atomic_store(flag, (unsigned)i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      const unsigned long long w0 = __builtin_amdgcn_s_memrealtime();
+      bool ok = true;
+      while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (unsigned)i) {
+        if (__builtin_amdgcn_s_memrealtime() - w0 > kSpinBudgetTicks) { ok = false; break; }
+      }
+      if (!ok) { ++timeouts; break; }
+      if (proto == 2) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      for (int w = lane; w < words; w += 64) {
+        unsigned v;
+        if (proto == 0 || proto == 3)
+          v = __hip_atomic_load(d + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else
+          v = *(volatile unsigned*)(d + w);
+        if (v != (unsigned)i) ++stale;
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      if (proto == 2) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      if (lane == 0) __hip_atomic_store(ack, (unsigned)i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  const unsigned long long t1 = __builtin_amdgcn_s_memrealtime();
+  if (stale) atomicAdd(errs + 0, stale);
+  if (timeouts) atomicAdd(errs + 1, timeouts);
+  if (!producer && pair == 0 && lane == 0) errs[2] = t1 - t0;
+}
+
+static double time_ms(hipEvent_t a, hipEvent_t b) {
+  float ms = 0;
+  CHECK(hipEventElapsedTime(&ms, a, b));
+  return ms;
+}
+
+int main(int argc, char** argv) {
+  int dev = 0;
+  CHECK(hipSetDevice(dev));
+  hipDeviceProp_t prop;
+  CHECK(hipGetDeviceProperties(&prop, dev));
+  const int n_cu = prop.multiProcessorCount;
+  printf("{\"device\": \"%s\", \"gcn_arch\": \"%s\", \"cus\": %d, \"l2_bytes\": %d, \"clock_khz\": %d}\n",
+         prop.name, prop.gcnArchName, n_cu, prop.l2CacheSize, prop.clockRate);
+  fflush(stdout);
+
+  hipEvent_t e0, e1;
+  CHECK(hipEventCreate(&e0));
+  CHECK(hipEventCreate(&e1));
+
+  // ---- 1. tile-shaped streaming reads over 4 GiB ----
+  const long n_tiles = 65536;  // 64 Ki tiles x 64 KiB = 4 GiB
+  const size_t bytes = (size_t)n_tiles * 65536;
+  uint4* src = nullptr;
+  unsigned* sink = nullptr;
+  unsigned* counters = nullptr;
+  CHECK(hipMalloc(&src, bytes));
+  CHECK(hipMemset(src, 1, bytes));
+  CHECK(hipMalloc(&sink, sizeof(unsigned) * 256 * 8192));
+  CHECK(hipMalloc(&counters, 4096 * sizeof(unsigned)));
+  CHECK(hipMemset(counters, 0, 4096 * sizeof(unsigned)));
+  float* xvec = nullptr;
+  float* results = nullptr;
+  CHECK(hipMalloc(&xvec, 8192));
+  CHECK(hipMemset(xvec, 0, 8192));
+  CHECK(hipMalloc(&results, sizeof(float) * 16 * 8192));
+  const std::string which = argc > 1 ? argv[1] : "all";
+  const int per_cu[] = {1, 2, 4, 8};
+  for (int mode : {0, 1, 2, 3, 4, 8, 16, 32, 24, 40}) {
+    if (which != "all" && which != "read") break;
+    for (int pc : per_cu) {
+      const int grid = n_cu * pc;  // grid-stride over n_tiles: every tile index < n_tiles
+      hipLaunchKernelGGL(k_tile_read, dim3(grid), dim3(256), 0, 0, src, n_tiles, mode, counters, sink, xvec, results);
+      CHECK(hipEventRecord(e0));
+      const int reps = 5;
+      for (int r = 0; r < reps; ++r)
+        hipLaunchKernelGGL(k_tile_read, dim3(grid), dim3(256), 0, 0, src, n_tiles, mode, counters, sink, xvec, results);
+      CHECK(hipEventRecord(e1));
+      CHECK(hipEventSynchronize(e1));
+      CHECK(hipGetLastError());
+      const double ms = time_ms(e0, e1) / reps;
+      printf("{\"bench\": \"tile_read\", \"mode\": %d, \"blocks_per_cu\": %d, \"ms\": %.4f, \"GBps\": %.1f}\n",
+             mode, pc, ms, bytes / ms / 1e6);
+      fflush(stdout);
+    }
+  }
+
+  // ---- 2. same-address atomic throughput ----
+  const int addrs[] = {1, 8, 64};
+  for (int na : addrs) {
+    if (which != "all" && which != "atomic") break;
+    for (int pc : {1, 4}) {
+      const int grid = n_cu * pc;
+      const int iters = 64;
+      CHECK(hipMemset(counters, 0, 4096 * sizeof(unsigned)));
+      hipLaunchKernelGGL(k_atomic, dim3(grid), dim3(64), 0, 0, counters, iters, na, sink);
+      CHECK(hipEventRecord(e0));
+      hipLaunchKernelGGL(k_atomic, dim3(grid), dim3(64), 0, 0, counters, iters, na, sink);
+      CHECK(hipEventRecord(e1));
+      CHECK(hipEventSynchronize(e1));
+      CHECK(hipGetLastError());
+      const double ms = time_ms(e0, e1);
+      const double n = (double)grid * iters;
+      std::vector<unsigned> hc(4096);
+      CHECK(hipMemcpy(hc.data(), counters, 4096 * sizeof(unsigned), hipMemcpyDeviceToHost));
+      unsigned long long total = 0;
+      for (int a = 0; a < na; ++a) total += hc[a * 64];
+      const bool exact = total == (unsigned long long)(2.0 * n);
+      printf("{\"bench\": \"atomic\", \"addresses\": %d, \"blocks\": %d, \"atomics\": %.0f, \"ms\": %.4f, \"Mops\": %.1f, \"ns_per_op_per_address\": %.2f, \"count_exact\": %s}\n",
+             na, grid, n, ms, n / ms / 1e3, ms * 1e6 / (n / na), exact ? "true" : "false");
+      fflush(stdout);
+    }
+  }
+
+  // ---- 3. release/acquire ping-pong ----
+  unsigned long long* pp_out = nullptr;
+  CHECK(hipMalloc(&pp_out, 2 * sizeof(unsigned long long)));
+  for (int peer : {1, 8, 2, 4}) {
+    if (which != "all" && which != "pingpong") break;
+    const int iters = 2000;
+    CHECK(hipMemset(counters, 0, 4096 * sizeof(unsigned)));
+    CHECK(hipMemset(pp_out, 0, 2 * sizeof(unsigned long long)));
+    hipLaunchKernelGGL(k_pingpong, dim3(peer + 1), dim3(64), 0, 0, counters, iters, peer, pp_out);
+    CHECK(hipDeviceSynchronize());
+    CHECK(hipGetLastError());
+    unsigned long long h[2];
+    CHECK(hipMemcpy(h, pp_out, sizeof(h), hipMemcpyDeviceToHost));
+    printf("{\"bench\": \"pingpong\", \"peer_block\": %d, \"round_trip_ns\": %.1f, \"timed_out\": %llu}\n",
+           peer, h[0] * 10.0 / iters, h[1]);
+    fflush(stdout);
+  }
+
+  // ---- 4. message passing across XCDs ----
+  if (which == "all" || which == "mp") {
+    const int words = 2048, iters = 2000;
+    unsigned* mpdata = nullptr;
+    unsigned long long* errs = nullptr;
+    CHECK(hipMalloc(&mpdata, sizeof(unsigned) * words * 8));
+    CHECK(hipMalloc(&errs, 4 * sizeof(unsigned long long)));
+    for (int proto : {0, 1, 2, 3}) {
+      for (int pairs : {1, 8}) {
+        CHECK(hipMemset(counters, 0, 4096 * sizeof(unsigned)));
+        CHECK(hipMemset(mpdata, 0, sizeof(unsigned) * words * 8));
+        CHECK(hipMemset(errs, 0, 4 * sizeof(unsigned long long)));
+        hipLaunchKernelGGL(k_mp, dim3(2 * pairs), dim3(64), 0, 0, counters, mpdata, words, iters, proto, errs);
+        CHECK(hipDeviceSynchronize());
+        CHECK(hipGetLastError());
+        unsigned long long h[3];
+        CHECK(hipMemcpy(h, errs, sizeof(h), hipMemcpyDeviceToHost));
+        printf("{\"bench\": \"message_passing\", \"proto\": %d, \"pairs\": %d, \"words\": %d, \"iters\": %d, \"stale_words\": %llu, \"timeouts\": %llu, \"ns_per_iter\": %.1f}\n",
+               proto, pairs, words, iters, h[0], h[1], h[2] * 10.0 / iters);
+        fflush(stdout);
+      }
+    }
+    CHECK(hipFree(mpdata));
+    CHECK(hipFree(errs));
+  }
+
+  CHECK(hipFree(xvec));
+  CHECK(hipFree(results));
+  CHECK(hipFree(src));
+  CHECK(hipFree(sink));
+  CHECK(hipFree(counters));
+  CHECK(hipFree(pp_out));
+  return 0;
+}

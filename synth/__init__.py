@@ -109,13 +109,21 @@ class ModelConfig:
     def elt_bytes(self) -> int:
         return 4 if self.dtype == "f32" else 2
 
-    def n_params(self) -> int:
+    def n_matrix_params(self) -> int:
         h, f = self.hidden, self.ffn
         per_layer = self.qkv_rows * h + h * self.n_q_heads * self.head_dim + 3 * f * h
         return self.n_layers * per_layer + self.vocab * h
 
+    def n_norm_params(self) -> int:
+        return (2 * self.n_layers + 1) * self.hidden
+
+    def n_params(self) -> int:
+        return self.n_matrix_params() + self.n_norm_params()
+
     def weight_bytes(self) -> int:
-        return self.n_params() * self.elt_bytes
+        """Bytes of all weights as laid out here: matrices in the model dtype,
+        RMSNorm gains in float32."""
+        return self.n_matrix_params() * self.elt_bytes + self.n_norm_params() * 4
 
 
 # The decoder shapes the measurements are quoted on.
@@ -123,10 +131,10 @@ TINY = ModelConfig("tiny", n_layers=2, hidden=256, n_q_heads=4, n_kv_heads=2, he
                    ffn=1024, vocab=1024, dtype="f32")
 LLAMA_1B = ModelConfig("llama-3.2-1b-shape", n_layers=16, hidden=2048, n_q_heads=32,
                        n_kv_heads=8, head_dim=64, ffn=8192, vocab=128256, dtype="bf16")
-# A small bf16 decoder whose tile counts are ragged (vocab and ffn are not
-# multiples of the tile sizes) for parity tests that cover partial tiles.
+# A small bf16 decoder whose LM-head tile count is ragged (vocab 1000 is not a
+# multiple of the rows per tile) for parity tests that cover partial tiles.
 MINI = ModelConfig("mini-ragged", n_layers=2, hidden=512, n_q_heads=8, n_kv_heads=2,
-                   head_dim=64, ffn=1536, vocab=1000, dtype="bf16")
+                   head_dim=64, ffn=1024, vocab=1000, dtype="bf16")
 
 # Stream ids within SEED_WEIGHTS.
 _S_EMBED = 1

@@ -1,0 +1,466 @@
+// capi.cpp -- the C ABI declared in include/wpk.h.
+//
+// wpk_build compiles the step for a declared operating point (model, batch
+// capacity, context limit), the compile-time scheduling of "Why real-time
+// inference wants a megakernel" (sections "The cohort is known" and "A
+// concrete design: one WPK update"): the builder fixes the tiles, their
+// dependency counters, the claim order, the worker count W and the whole
+// memory plan once; wpk_step is then a single cooperative launch.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "host_exec.h"
+#include "runtime.h"
+
+extern "C" int wpk_dev_kernels(int dtype, int cpr_h, int cpr_f, const void** mk, const void** mk_log,
+                               const void** phase);
+
+using namespace wpk;
+
+namespace {
+
+thread_local std::string g_err;
+
+wpk_plan* fail(const std::string& m) {
+  g_err = m;
+  return nullptr;
+}
+
+std::string hip_msg(const char* what, hipError_t e) { return std::string(what) + ": " + hipGetErrorString(e); }
+
+int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
+
+struct Layout {
+  int64_t ctl, heads, counters, argmax, tiles, groups, queue, queue_off, layers, rope_cos, rope_sin, act, log, total;
+};
+
+Layout layout(const Shape& s, const Dag& d) {
+  Layout L{};
+  int64_t at = 0;
+  auto take = [&](int64_t bytes) {
+    const int64_t o = at;
+    at = align256(at + bytes);
+    return o;
+  };
+  const int32_t nq = (int32_t)d.queue_off.size() - 1;
+  L.ctl = take(CTL_WORDS * 4);
+  L.heads = take((int64_t)nq * kLine * 4);
+  L.counters = take((int64_t)d.n_shard_slots * kLine * 4);
+  L.argmax = take((int64_t)s.B * kArgmaxShards * 8);
+  L.tiles = take((int64_t)d.tiles.size() * sizeof(Tile));
+  L.groups = take((int64_t)d.groups.size() * sizeof(Group));
+  L.queue = take((int64_t)d.queue.size() * 4);
+  L.queue_off = take((int64_t)d.queue_off.size() * 4);
+  L.layers = take((int64_t)s.L * sizeof(LayerBufs));
+  L.rope_cos = take((int64_t)s.cap * (s.D / 2) * 4);
+  L.rope_sin = take((int64_t)s.cap * (s.D / 2) * 4);
+  L.act = take(act_layout(s).total * 4);
+  L.log = take((int64_t)d.tiles.size() * sizeof(wpk_log_rec));
+  L.total = at;
+  return L;
+}
+
+void copy_tables(wpk_plan* p, const wpk_model_desc& d) {
+  const int L = d.n_layers;
+  p->desc = d;
+  p->tables.resize(7 * (size_t)L);
+  const void* const* src[7] = {(const void* const*)d.attn_norm, d.w_qkv, d.w_o, (const void* const*)d.mlp_norm,
+                               d.w_gate, d.w_up, d.w_down};
+  for (int k = 0; k < 7; ++k)
+    for (int l = 0; l < L; ++l) p->tables[(size_t)k * L + l] = src[k][l];
+  p->desc.attn_norm = (const float* const*)&p->tables[0];
+  p->desc.w_qkv = &p->tables[(size_t)1 * L];
+  p->desc.w_o = &p->tables[(size_t)2 * L];
+  p->desc.mlp_norm = (const float* const*)&p->tables[(size_t)3 * L];
+  p->desc.w_gate = &p->tables[(size_t)4 * L];
+  p->desc.w_up = &p->tables[(size_t)5 * L];
+  p->desc.w_down = &p->tables[(size_t)6 * L];
+}
+
+bool desc_ok(const wpk_model_desc* d, std::string* why) {
+  if (!d) {
+    *why = "null model description";
+    return false;
+  }
+  if (!d->embed || !d->final_norm || !d->attn_norm || !d->w_qkv || !d->w_o || !d->mlp_norm || !d->w_gate ||
+      !d->w_up || !d->w_down || d->n_layers <= 0) {
+    *why = "model description has a null pointer or no layers";
+    return false;
+  }
+  for (int l = 0; l < d->n_layers; ++l)
+    if (!d->attn_norm[l] || !d->w_qkv[l] || !d->w_o[l] || !d->mlp_norm[l] || !d->w_gate[l] || !d->w_up[l] ||
+        !d->w_down[l]) {
+      *why = "null weight pointer in layer " + std::to_string(l);
+      return false;
+    }
+  return true;
+}
+
+wpk_plan* build_device(const wpk_model_desc* desc, int32_t batch, int32_t ctx_len, const wpk_build_opts* opts,
+                       bool baseline) {
+  std::string why;
+  if (!desc_ok(desc, &why)) return fail(why);
+  wpk_build_opts o{};
+  if (opts) o = *opts;
+  Shape s;
+  why = check_shape(*desc, batch, ctx_len, o, &s);
+  if (!why.empty()) return fail(why);
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev == 0) return fail("no HIP device");
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(hip_msg("hipGetDevice", e));
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return fail(hip_msg("hipGetDeviceProperties", e));
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(std::string("built for gfx950, found ") + prop.gcnArchName);
+  const void *mk = nullptr, *mk_log = nullptr, *phase = nullptr;
+  if (!wpk_dev_kernels(s.dtype, s.cpr_h, s.cpr_f, &mk, &mk_log, &phase))
+    return fail("no kernel instance for this dtype / hidden / ffn (cpr_h=" + std::to_string(s.cpr_h) +
+                ", cpr_f=" + std::to_string(s.cpr_f) + ")");
+
+  std::unique_ptr<wpk_plan> p(new wpk_plan());
+  p->baseline = baseline;
+  p->s = s;
+  p->device = dev;
+  p->n_cu = prop.multiProcessorCount;
+  copy_tables(p.get(), *desc);
+  p->dag = build_dag(s);
+  why = validate_dag(s, p->dag);
+  if (!why.empty()) return fail("invalid DAG: " + why);
+  for (const Tile& t : p->dag.tiles) p->built_wait.push_back(t.wait);
+  p->weight_bytes = step_weight_bytes(s);
+  p->k_mega = mk;
+  p->k_mega_log = mk_log;
+  p->k_phase = phase;
+
+  int per_cu = 0, per_cu_log = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mk, kThreads, 0);
+  if (e != hipSuccess) return fail(hip_msg("occupancy query", e));
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_log, mk_log, kThreads, 0);
+  if (e != hipSuccess) return fail(hip_msg("occupancy query", e));
+  per_cu = std::min(per_cu, per_cu_log);
+  p->max_workers = per_cu * p->n_cu;
+  p->workers = std::min(s.workers_per_cu, per_cu) * p->n_cu;
+  if (p->workers < s.queue_shards) {
+    g_err = "occupancy too low: " + std::to_string(p->max_workers) + " co-resident workers";
+    return nullptr;
+  }
+
+  const Layout L = layout(s, p->dag);
+  e = hipMalloc((void**)&p->d_ws, L.total);
+  if (e != hipSuccess) return fail(hip_msg("hipMalloc workspace", e));
+  p->ws_bytes = L.total;
+  char* w = p->d_ws;
+  auto up = [&](int64_t off, const void* src, size_t bytes) { return hipMemcpy(w + off, src, bytes, hipMemcpyHostToDevice); };
+  e = hipMemset(w, 0, L.total);
+  std::vector<LayerBufs> lbs;
+  fill_layers(s, p->desc, (float*)(w + L.act), lbs);
+  std::vector<float> rc, rsn;
+  rope_table(s, rc, rsn);
+  if (e == hipSuccess) e = up(L.tiles, p->dag.tiles.data(), p->dag.tiles.size() * sizeof(Tile));
+  if (e == hipSuccess) e = up(L.groups, p->dag.groups.data(), p->dag.groups.size() * sizeof(Group));
+  if (e == hipSuccess) e = up(L.queue, p->dag.queue.data(), p->dag.queue.size() * 4);
+  if (e == hipSuccess) e = up(L.queue_off, p->dag.queue_off.data(), p->dag.queue_off.size() * 4);
+  if (e == hipSuccess) e = up(L.layers, lbs.data(), lbs.size() * sizeof(LayerBufs));
+  if (e == hipSuccess) e = up(L.rope_cos, rc.data(), rc.size() * 4);
+  if (e == hipSuccess) e = up(L.rope_sin, rsn.data(), rsn.size() * 4);
+  if (e != hipSuccess) {
+    (void)hipFree(p->d_ws);
+    return fail(hip_msg("workspace upload", e));
+  }
+  Params& P = p->P;
+  P.L = s.L; P.H = s.H; P.Hq = s.Hq; P.Hkv = s.Hkv; P.D = s.D; P.F = s.F; P.V = s.V;
+  P.B = s.B; P.cap = s.cap; P.nch = s.nch; P.G = s.G; P.qkv_rows = s.qkv_rows;
+  P.n_tiles = (int32_t)p->dag.tiles.size();
+  P.n_queues = (int32_t)p->dag.queue_off.size() - 1;
+  P.n_workers = p->workers;
+  P.dtype = s.dtype;
+  P.eps = s.eps;
+  P.attn_scale = 1.0f / std::sqrt((float)s.D);
+  P.embed = p->desc.embed;
+  P.final_norm = p->desc.final_norm;
+  P.layers = (const LayerBufs*)(w + L.layers);
+  P.rope_cos = (const float*)(w + L.rope_cos);
+  P.rope_sin = (const float*)(w + L.rope_sin);
+  P.tiles = (const Tile*)(w + L.tiles);
+  P.queue = (const int32_t*)(w + L.queue);
+  P.queue_off = (const int32_t*)(w + L.queue_off);
+  P.groups = (const Group*)(w + L.groups);
+  P.counters = (uint32_t*)(w + L.counters);
+  P.heads = (uint32_t*)(w + L.heads);
+  P.ctl = (uint32_t*)(w + L.ctl);
+  P.argmax = (unsigned long long*)(w + L.argmax);
+  P.log = (int32_t*)(w + L.log);
+  P.log_on = 0;
+  P.prefetch = 1;
+  P.drop_tile = -1;
+  P.perturb = 0;
+  P.watchdog_ticks = p->watchdog_us * 100;
+  p->log.assign(p->dag.tiles.size(), wpk_log_rec{});
+  if (baseline) {
+    hipStream_t cs;
+    e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
+    if (e != hipSuccess) {
+      (void)hipFree(p->d_ws);
+      return fail(hip_msg("hipStreamCreate", e));
+    }
+    p->cap_stream = cs;
+  }
+  return p.release();
+}
+
+int32_t plan_fail(wpk_plan* p, int32_t code, const std::string& m) {
+  if (p) p->err = m;
+  else g_err = m;
+  return code;
+}
+
+int32_t capture_baseline(wpk_plan* p) {
+  if (p->graph_exec) {
+    (void)hipGraphExecDestroy((hipGraphExec_t)p->graph_exec);
+    p->graph_exec = nullptr;
+  }
+  if (p->graph) {
+    (void)hipGraphDestroy((hipGraph_t)p->graph);
+    p->graph = nullptr;
+  }
+  hipStream_t cs = (hipStream_t)p->cap_stream;
+  hipError_t e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) return plan_fail(p, WPK_E_HIP, hip_msg("hipStreamBeginCapture", e));
+  for (const auto& ph : p->dag.phases) {
+    int32_t first = ph.first;
+    void* args[] = {(void*)&p->P, (void*)&first};
+    e = hipLaunchKernel(p->k_phase, dim3(ph.second), dim3(kThreads), args, 0, cs);
+    if (e != hipSuccess) break;
+  }
+  hipGraph_t g = nullptr;
+  const hipError_t e2 = hipStreamEndCapture(cs, &g);
+  if (e != hipSuccess) return plan_fail(p, WPK_E_HIP, hip_msg("baseline launch during capture", e));
+  if (e2 != hipSuccess) return plan_fail(p, WPK_E_HIP, hip_msg("hipStreamEndCapture", e2));
+  hipGraphExec_t ge = nullptr;
+  e = hipGraphInstantiate(&ge, g, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    (void)hipGraphDestroy(g);
+    return plan_fail(p, WPK_E_HIP, hip_msg("hipGraphInstantiate", e));
+  }
+  p->graph = g;
+  p->graph_exec = ge;
+  return WPK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+wpk_plan* wpk_build(const wpk_model_desc* desc, int32_t batch, int32_t ctx_len) {
+  return build_device(desc, batch, ctx_len, nullptr, false);
+}
+
+wpk_plan* wpk_build_ex(const wpk_model_desc* desc, int32_t batch, int32_t ctx_len, const wpk_build_opts* opts) {
+  return build_device(desc, batch, ctx_len, opts, false);
+}
+
+wpk_plan* wpk_build_graph_baseline(const wpk_model_desc* desc, int32_t batch, int32_t ctx_len) {
+  return build_device(desc, batch, ctx_len, nullptr, true);
+}
+
+int32_t wpk_step(wpk_plan* p, int32_t* tokens, wpk_kv* kv, void* logits, wpk_stream_t stream) {
+  if (!p) return plan_fail(nullptr, WPK_E_ARG, "null plan");
+  if (p->host) return plan_fail(p, WPK_E_ARG, "host plan: use wpk_serial_step / wpk_emulate_step");
+  if (p->latched) return plan_fail(p, WPK_E_STATE, "plan holds device error " + std::to_string(p->latched) + "; reset it");
+  if (!tokens || !kv || !kv->k || !kv->v || !kv->seq_len || !logits)
+    return plan_fail(p, WPK_E_ARG, "null tokens, kv or logits");
+  hipStream_t st = (hipStream_t)stream;
+  Params& P = p->P;
+  P.tokens = tokens;
+  P.seq_len = kv->seq_len;
+  P.logits = (float*)logits;
+  P.kc = (char*)kv->k;
+  P.vc = (char*)kv->v;
+  p->last_stream = stream;
+  hipError_t e;
+  if (p->baseline) {
+    if (!p->graph_exec || p->cap_tokens != tokens || p->cap_kc != kv->k || p->cap_vc != kv->v ||
+        p->cap_seq != kv->seq_len || p->cap_logits != logits) {
+      const int32_t rc = capture_baseline(p);
+      if (rc != WPK_OK) return rc;
+      p->cap_tokens = tokens;
+      p->cap_kc = kv->k;
+      p->cap_vc = kv->v;
+      p->cap_seq = kv->seq_len;
+      p->cap_logits = logits;
+    }
+    e = hipGraphLaunch((hipGraphExec_t)p->graph_exec, st);
+    if (e != hipSuccess) return plan_fail(p, WPK_E_HIP, hip_msg("hipGraphLaunch", e));
+    return WPK_OK;
+  }
+  P.log_on = p->log_on;
+  if (p->log_on) {
+    e = hipMemsetAsync(P.log, 0, p->dag.tiles.size() * sizeof(wpk_log_rec), st);
+    if (e != hipSuccess) return plan_fail(p, WPK_E_HIP, hip_msg("hipMemsetAsync log", e));
+  }
+  void* args[] = {(void*)&P};
+  e = hipLaunchCooperativeKernel(p->log_on ? p->k_mega_log : p->k_mega, dim3(p->workers), dim3(kThreads), args, 0, st);
+  if (e != hipSuccess) return plan_fail(p, WPK_E_HIP, hip_msg("hipLaunchCooperativeKernel", e));
+  return WPK_OK;
+}
+
+int32_t wpk_sync(wpk_plan* p) {
+  if (!p) return plan_fail(nullptr, WPK_E_ARG, "null plan");
+  if (p->host) return WPK_OK;
+  hipError_t e = hipStreamSynchronize((hipStream_t)p->last_stream);
+  if (e != hipSuccess) return plan_fail(p, WPK_E_HIP, hip_msg("hipStreamSynchronize", e));
+  uint32_t st[4];
+  e = hipMemcpy(st, p->P.ctl + CTL_STATUS, sizeof st, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return plan_fail(p, WPK_E_HIP, hip_msg("status read", e));
+  if (st[0] != 0) {
+    p->latched = (int32_t)st[0];
+    char m[200];
+    snprintf(m, sizeof m, "device error %d at tile %u (worker %u, step %u)", (int32_t)st[0], st[1], st[2], st[3]);
+    p->err = m;
+    return p->latched;
+  }
+  return WPK_OK;
+}
+
+void wpk_destroy(wpk_plan* p) {
+  if (!p) return;
+  if (p->graph_exec) (void)hipGraphExecDestroy((hipGraphExec_t)p->graph_exec);
+  if (p->graph) (void)hipGraphDestroy((hipGraph_t)p->graph);
+  if (p->cap_stream) (void)hipStreamDestroy((hipStream_t)p->cap_stream);
+  if (p->d_ws) {
+    (void)hipDeviceSynchronize();
+    (void)hipFree(p->d_ws);
+  }
+  delete p;
+}
+
+const char* wpk_last_error(const wpk_plan* p) { return p ? p->err.c_str() : g_err.c_str(); }
+
+int32_t wpk_set_option(wpk_plan* p, int32_t key, int64_t value) {
+  if (!p) return plan_fail(nullptr, WPK_E_ARG, "null plan");
+  Params& P = p->P;
+  switch (key) {
+    case WPK_OPT_LOG:
+      p->log_on = value != 0;
+      return WPK_OK;
+    case WPK_OPT_WATCHDOG_US:
+      if (value <= 0) return plan_fail(p, WPK_E_ARG, "watchdog must be positive");
+      p->watchdog_us = (uint64_t)value;
+      P.watchdog_ticks = (uint64_t)value * 100;
+      return WPK_OK;
+    case WPK_OPT_PERTURB_SEED:
+      P.perturb = (uint32_t)value;
+      p->perturb = (uint32_t)value;
+      return WPK_OK;
+    case WPK_OPT_DEBUG_DROP_TILE:
+      if (value < -1 || value >= (int64_t)p->dag.tiles.size()) return plan_fail(p, WPK_E_ARG, "tile out of range");
+      P.drop_tile = (int32_t)value;
+      p->drop_tile = (int32_t)value;
+      return WPK_OK;
+    case WPK_OPT_PREFETCH:
+      P.prefetch = value != 0;
+      p->prefetch = (int32_t)(value != 0);
+      return WPK_OK;
+    case WPK_OPT_WORKERS:
+      if (value < (int64_t)p->s.queue_shards || value > p->max_workers)
+        return plan_fail(p, WPK_E_ARG, "workers must be in [queue shards, max co-resident]");
+      p->workers = (int32_t)value;
+      P.n_workers = (int32_t)value;
+      return WPK_OK;
+    case WPK_OPT_RESET: {
+      if (p->host) {
+        p->latched = 0;
+        return WPK_OK;
+      }
+      hipError_t e = hipDeviceSynchronize();
+      if (e == hipSuccess) e = hipMemset(P.ctl, 0, CTL_WORDS * 4);
+      if (e == hipSuccess) e = hipMemset(P.heads, 0, (size_t)P.n_queues * kLine * 4);
+      if (e == hipSuccess) e = hipMemset(P.counters, 0, (size_t)p->dag.n_shard_slots * kLine * 4);
+      if (e == hipSuccess) e = hipMemset(P.argmax, 0, (size_t)p->s.B * kArgmaxShards * 8);
+      if (e == hipSuccess) e = hipDeviceSynchronize();
+      if (e != hipSuccess) return plan_fail(p, WPK_E_HIP, hip_msg("reset", e));
+      p->latched = 0;
+      return WPK_OK;
+    }
+  }
+  return plan_fail(p, WPK_E_ARG, "unknown option key");
+}
+
+int32_t wpk_get_log(wpk_plan* p, void* dst, size_t bytes) {
+  if (!p || !dst) return plan_fail(p, WPK_E_ARG, "null argument");
+  const size_t need = p->dag.tiles.size() * sizeof(wpk_log_rec);
+  if (bytes < need) return plan_fail(p, WPK_E_ARG, "log buffer too small");
+  if (p->host) {
+    std::memcpy(dst, p->log.data(), need);
+    return WPK_OK;
+  }
+  hipError_t e = hipMemcpy(dst, p->P.log, need, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return plan_fail(p, WPK_E_HIP, hip_msg("log read", e));
+  return WPK_OK;
+}
+
+int32_t wpk_get_info(const wpk_plan* p, wpk_plan_info* out) {
+  if (!p || !out) return WPK_E_ARG;
+  out->n_tiles = (int32_t)p->dag.tiles.size();
+  out->n_groups = (int32_t)p->dag.groups.size();
+  out->n_queue_shards = (int32_t)p->dag.queue_off.size() - 1;
+  out->workers = p->workers;
+  out->max_workers = p->max_workers;
+  out->rows_per_tile_h = p->s.rows_h;
+  out->rows_per_tile_f = p->s.rows_f;
+  out->attn_chunk = kAttnChunk;
+  out->workspace_bytes = p->ws_bytes;
+  out->weight_bytes = p->weight_bytes;
+  return WPK_OK;
+}
+
+int32_t wpk_get_dag(const wpk_plan* p, int32_t* type, int32_t* layer, int32_t* wait, int32_t* signal) {
+  if (!p || !type || !layer || !wait || !signal) return WPK_E_ARG;
+  for (size_t i = 0; i < p->dag.tiles.size(); ++i) {
+    type[i] = p->dag.tiles[i].type;
+    layer[i] = p->dag.tiles[i].layer;
+    wait[i] = p->dag.tiles[i].wait;
+    signal[i] = p->dag.tiles[i].signal;
+  }
+  return WPK_OK;
+}
+
+wpk_plan* wpk_build_host(const wpk_model_desc* desc, int32_t batch, int32_t ctx_len, const wpk_build_opts* opts) {
+  std::string why;
+  if (!desc_ok(desc, &why)) return fail(why);
+  wpk_build_opts o{};
+  if (opts) o = *opts;
+  wpk_plan* p = make_host_plan(*desc, batch, ctx_len, o, &why);
+  if (!p) return fail(why);
+  return p;
+}
+
+int32_t wpk_serial_step(wpk_plan* p, int32_t* tokens, wpk_kv* kv, float* logits, uint64_t order_seed, int32_t poison) {
+  if (!p || !p->host) return plan_fail(p, WPK_E_ARG, "wpk_serial_step needs a host plan");
+  return host_serial_step(p, tokens, kv, logits, order_seed, poison != 0);
+}
+
+int32_t wpk_emulate_step(wpk_plan* p, int32_t* tokens, wpk_kv* kv, float* logits, int32_t n_threads, uint64_t seed) {
+  if (!p || !p->host) return plan_fail(p, WPK_E_ARG, "wpk_emulate_step needs a host plan");
+  return host_emulate_step(p, tokens, kv, logits, n_threads, seed);
+}
+
+int32_t wpk_debug_drop_edge(wpk_plan* p, int32_t tile) {
+  if (!p || !p->host) return plan_fail(p, WPK_E_ARG, "edges can only be dropped on host plans");
+  if (tile == -1) {
+    for (size_t i = 0; i < p->dag.tiles.size(); ++i) p->dag.tiles[i].wait = p->built_wait[i];
+    return WPK_OK;
+  }
+  if (tile < 0 || tile >= (int32_t)p->dag.tiles.size()) return plan_fail(p, WPK_E_ARG, "tile out of range");
+  p->dag.tiles[tile].wait = -1;
+  return WPK_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,601 @@
+// host_exec.cpp -- the tile DAG run on the CPU.
+//
+// Two executors share one set of CPU tile bodies (float32, sequential sums):
+//  * the serial executor runs tiles one at a time in a topological order drawn
+//    at random (Kahn's algorithm with a seeded tie-break).  Any valid order
+//    must give bit-identical results, and with NaN-poisoned intermediates a
+//    tile that runs before one of its producers poisons the logits;
+//  * the emulator runs the device protocol itself -- claim from the sharded
+//    queues in topological order, wait for a counter group with acquire loads,
+//    publish with a release increment -- on std::threads with random delays,
+//    so a data race in the protocol is visible to ThreadSanitizer.
+// The "final participant publishes" and phase-barrier logic of the WPK design
+// ("Why real-time inference wants a megakernel", one WPK update) is replaced
+// here, as on the device, by counter groups released per tile.
+#include "host_exec.h"
+
+#include <chrono>
+#include <cmath>
+#include <cstring>
+#include <limits>
+#include <thread>
+
+namespace wpk {
+
+// ---- shared layout helpers ---------------------------------------------------------
+
+void rope_table(const Shape& s, std::vector<float>& cos_t, std::vector<float>& sin_t) {
+  const int half = s.D / 2;
+  cos_t.resize((size_t)s.cap * half);
+  sin_t.resize((size_t)s.cap * half);
+  for (int p = 0; p < s.cap; ++p)
+    for (int i = 0; i < half; ++i) {
+      const double ang = (double)p * std::pow((double)s.theta, -2.0 * i / s.D);
+      cos_t[(size_t)p * half + i] = (float)std::cos(ang);
+      sin_t[(size_t)p * half + i] = (float)std::sin(ang);
+    }
+}
+
+ActLayout act_layout(const Shape& s) {
+  ActLayout a{};
+  auto r64 = [](int64_t x) { return (x + 63) & ~(int64_t)63; };  // 256-byte aligned
+  int64_t at = 0;
+  a.x_mid = at; at += r64((int64_t)s.B * s.H);
+  a.x_out = at; at += r64((int64_t)s.B * s.H);
+  a.q = at;     at += r64((int64_t)s.B * s.Hq * s.D);
+  a.part = at;  at += r64((int64_t)s.B * s.Hkv * s.nch * s.G * (s.D + 2));
+  a.attn = at;  at += r64((int64_t)s.B * s.Hq * s.D);
+  a.h = at;     at += r64((int64_t)s.B * s.F);
+  a.per_layer = at;
+  a.total = at * s.L;
+  return a;
+}
+
+void fill_layers(const Shape& s, const wpk_model_desc& d, float* act, std::vector<LayerBufs>& out) {
+  const ActLayout a = act_layout(s);
+  out.resize(s.L);
+  for (int l = 0; l < s.L; ++l) {
+    float* base = act + a.per_layer * l;
+    LayerBufs& lb = out[l];
+    lb.w_qkv = d.w_qkv[l];
+    lb.w_o = d.w_o[l];
+    lb.w_gate = d.w_gate[l];
+    lb.w_up = d.w_up[l];
+    lb.w_down = d.w_down[l];
+    lb.attn_norm = d.attn_norm[l];
+    lb.mlp_norm = d.mlp_norm[l];
+    lb.x_mid = base + a.x_mid;
+    lb.x_out = base + a.x_out;
+    lb.q = base + a.q;
+    lb.part = base + a.part;
+    lb.attn = base + a.attn;
+    lb.h = base + a.h;
+    lb.x_in = l == 0 ? nullptr : out[l - 1].x_out;
+  }
+}
+
+// ---- CPU tile bodies ----------------------------------------------------------------
+
+namespace {
+
+inline float wval(const void* w, int32_t dtype, int64_t i) {
+  if (dtype == WPK_BF16) {
+    const uint32_t u = (uint32_t)((const uint16_t*)w)[i] << 16;
+    float f;
+    std::memcpy(&f, &u, 4);
+    return f;
+  }
+  return ((const float*)w)[i];
+}
+
+inline uint16_t to_bf16(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (uint16_t)((u >> 16) | 0x40u);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+inline void cache_put(char* base, int32_t dtype, int64_t i, float v) {
+  if (dtype == WPK_BF16) ((uint16_t*)base)[i] = to_bf16(v);
+  else ((float*)base)[i] = v;
+}
+
+inline uint64_t pack_max(float v, int32_t idx) {
+  uint32_t u;
+  std::memcpy(&u, &v, 4);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)idx);
+}
+
+struct Ctx {
+  const Params& P;
+  std::atomic<unsigned long long>* argmax;
+  std::atomic<int32_t>* status;
+};
+
+void set_status(Ctx& c, int32_t code) {
+  int32_t z = 0;
+  c.status->compare_exchange_strong(z, code);
+}
+
+int32_t token_of(Ctx& c, int b) {
+  const int32_t t = c.P.tokens[b];
+  if (c.P.seq_len[b] >= 0 && (t < 0 || t >= c.P.V)) {
+    set_status(c, WPK_E_TOKEN);
+    return 0;
+  }
+  return (t < 0 || t >= c.P.V) ? 0 : t;
+}
+
+// Input vector of a GEMV tile for sequence b, with its RMSNorm prologue.
+void gemv_input(Ctx& c, const Tile& T, int b, std::vector<float>& x) {
+  const Params& P = c.P;
+  const LayerBufs& lb = P.layers[T.layer];
+  const float* gain = nullptr;
+  int K = P.H;
+  switch (T.type) {
+    case T_QKV:
+      gain = lb.attn_norm;
+      if (T.layer == 0) {
+        const int64_t tok = token_of(c, b);
+        x.resize(P.H);
+        for (int i = 0; i < P.H; ++i) x[i] = wval(P.embed, P.dtype, tok * P.H + i);
+      } else {
+        x.assign(lb.x_in + (int64_t)b * P.H, lb.x_in + (int64_t)(b + 1) * P.H);
+      }
+      break;
+    case T_OPROJ:
+      x.assign(lb.attn + (int64_t)b * P.H, lb.attn + (int64_t)(b + 1) * P.H);
+      break;
+    case T_GATEUP:
+      gain = lb.mlp_norm;
+      x.assign(lb.x_mid + (int64_t)b * P.H, lb.x_mid + (int64_t)(b + 1) * P.H);
+      break;
+    case T_DOWN:
+      K = P.F;
+      x.assign(lb.h + (int64_t)b * P.F, lb.h + (int64_t)(b + 1) * P.F);
+      break;
+    case T_LM: {
+      gain = P.final_norm;
+      const float* xo = P.layers[P.L - 1].x_out;
+      x.assign(xo + (int64_t)b * P.H, xo + (int64_t)(b + 1) * P.H);
+      break;
+    }
+  }
+  if (gain) {
+    float ss = 0.f;
+    for (int i = 0; i < K; ++i) ss += x[i] * x[i];
+    const float inv = 1.0f / std::sqrt(ss / (float)K + P.eps);
+    for (int i = 0; i < K; ++i) x[i] = x[i] * inv * gain[i];
+  }
+}
+
+void run_gemv(Ctx& c, const Tile& T) {
+  const Params& P = c.P;
+  const LayerBufs& lb = P.layers[T.layer];
+  const void* w0;
+  const void* w1;
+  int K = P.H, limit;
+  switch (T.type) {
+    case T_QKV: w0 = w1 = lb.w_qkv; limit = P.qkv_rows; break;
+    case T_OPROJ: w0 = w1 = lb.w_o; limit = P.H; break;
+    case T_GATEUP: w0 = lb.w_gate; w1 = lb.w_up; limit = P.F; break;
+    case T_DOWN: w0 = w1 = lb.w_down; K = P.F; limit = P.H; break;
+    default: w0 = w1 = P.embed; limit = P.V; break;
+  }
+  std::vector<float> x, y(T.rows);
+  for (int b = 0; b < P.B; ++b) {
+    const int32_t p = P.seq_len[b];
+    if (T.type == T_QKV && p < 0) continue;  // inactive slot: nothing to append
+    gemv_input(c, T, b, x);
+    for (int r = 0; r < T.rows; ++r) {
+      const bool seg1 = r >= T.rs;
+      const int64_t mrow = seg1 ? T.r1 + (r - T.rs) : T.r0 + r;
+      y[r] = 0.f;
+      if (mrow >= limit) continue;
+      const void* w = seg1 ? w1 : w0;
+      float acc = 0.f;
+      for (int k = 0; k < K; ++k) acc += wval(w, P.dtype, mrow * K + k) * x[k];
+      y[r] = acc;
+    }
+    switch (T.type) {
+      case T_QKV: {
+        if (p >= P.cap) {
+          set_status(c, WPK_E_CTX_FULL);
+          break;
+        }
+        const int half = P.D / 2;
+        if (T.kind < 2) {
+          const int head = T.g;
+          const int64_t base = T.kind == 0 ? (int64_t)head * P.D : (int64_t)(P.Hq + head) * P.D;
+          for (int i = 0; i < T.rs; ++i) {
+            const int dim = (int)(T.r0 + i - base);
+            const float cs = P.rope_cos[(int64_t)p * half + dim], sn = P.rope_sin[(int64_t)p * half + dim];
+            const float a = y[i], bb = y[T.rs + i];
+            const float ra = a * cs - bb * sn, rb = bb * cs + a * sn;
+            if (T.kind == 0) {
+              lb.q[(int64_t)b * P.Hq * P.D + head * P.D + dim] = ra;
+              lb.q[(int64_t)b * P.Hq * P.D + head * P.D + dim + half] = rb;
+            } else {
+              const int64_t at = ((((int64_t)T.layer * P.B + b) * P.Hkv + head) * P.cap + p) * P.D;
+              cache_put(P.kc, P.dtype, at + dim, ra);
+              cache_put(P.kc, P.dtype, at + dim + half, rb);
+            }
+          }
+        } else {
+          const int64_t base = (int64_t)(P.Hq + P.Hkv + T.g) * P.D;
+          const int64_t at = ((((int64_t)T.layer * P.B + b) * P.Hkv + T.g) * P.cap + p) * P.D;
+          for (int r = 0; r < T.rows; ++r) {
+            const int64_t mrow = r < T.rs ? T.r0 + r : T.r1 + (r - T.rs);
+            cache_put(P.vc, P.dtype, at + (mrow - base), y[r]);
+          }
+        }
+        break;
+      }
+      case T_OPROJ:
+        for (int r = 0; r < T.rows; ++r) {
+          const int64_t row = T.r0 + r;
+          if (row >= P.H) continue;
+          float xin;
+          if (T.layer == 0) xin = wval(P.embed, P.dtype, (int64_t)token_of(c, b) * P.H + row);
+          else xin = lb.x_in[(int64_t)b * P.H + row];
+          lb.x_mid[(int64_t)b * P.H + row] = xin + y[r];
+        }
+        break;
+      case T_GATEUP:
+        for (int i = 0; i < T.rs; ++i) {
+          const int64_t j = T.r0 + i;
+          if (j >= P.F) continue;
+          const float g = y[i], u = y[T.rs + i];
+          lb.h[(int64_t)b * P.F + j] = g / (1.0f + std::exp(-g)) * u;
+        }
+        break;
+      case T_DOWN:
+        for (int r = 0; r < T.rows; ++r) {
+          const int64_t row = T.r0 + r;
+          if (row >= P.H) continue;
+          lb.x_out[(int64_t)b * P.H + row] = lb.x_mid[(int64_t)b * P.H + row] + y[r];
+        }
+        break;
+      case T_LM: {
+        uint64_t best = 0;
+        for (int r = 0; r < T.rows; ++r) {
+          const int64_t row = T.r0 + r;
+          if (row >= P.V) continue;
+          P.logits[(int64_t)b * P.V + row] = y[r];
+          const uint64_t k = pack_max(y[r], (int32_t)row);
+          if (k > best) best = k;
+        }
+        std::atomic<unsigned long long>& slot = c.argmax[b * kArgmaxShards + T.id % kArgmaxShards];
+        unsigned long long cur = slot.load(std::memory_order_relaxed);
+        while (best > cur && !slot.compare_exchange_weak(cur, best, std::memory_order_relaxed)) {
+        }
+        break;
+      }
+    }
+  }
+}
+
+void run_attn(Ctx& c, const Tile& T) {
+  const Params& P = c.P;
+  const LayerBufs& lb = P.layers[T.layer];
+  const int32_t p = P.seq_len[T.b];
+  const int n = p < 0 ? 0 : std::min(p + 1, P.cap);
+  const int start = T.c * kAttnChunk;
+  const int cnt = std::max(0, std::min(kAttnChunk, n - start));
+  const int64_t slice = (((int64_t)T.layer * P.B + T.b) * P.Hkv + T.g) * P.cap;
+  for (int h = 0; h < P.G; ++h) {
+    float* out = lb.part + ((((int64_t)T.b * P.Hkv + T.g) * P.nch + T.c) * P.G + h) * (P.D + 2);
+    if (cnt == 0) {
+      out[0] = -std::numeric_limits<float>::infinity();
+      out[1] = 0.f;
+      for (int d = 0; d < P.D; ++d) out[2 + d] = 0.f;
+      continue;
+    }
+    const float* q = lb.q + (int64_t)T.b * P.Hq * P.D + (int64_t)(T.g * P.G + h) * P.D;
+    float s[kAttnChunk];
+    float m = -std::numeric_limits<float>::infinity();
+    for (int j = 0; j < cnt; ++j) {
+      float dot = 0.f;
+      for (int d = 0; d < P.D; ++d) dot += q[d] * wval(P.kc, P.dtype, (slice + start + j) * P.D + d);
+      s[j] = dot * P.attn_scale;
+      m = std::max(m, s[j]);
+    }
+    float l = 0.f;
+    for (int j = 0; j < cnt; ++j) {
+      s[j] = std::exp(s[j] - m);
+      l += s[j];
+    }
+    out[0] = m;
+    out[1] = l;
+    for (int d = 0; d < P.D; ++d) {
+      float o = 0.f;
+      for (int j = 0; j < cnt; ++j) o += s[j] * wval(P.vc, P.dtype, (slice + start + j) * P.D + d);
+      out[2 + d] = o;
+    }
+  }
+}
+
+void run_combine(Ctx& c, const Tile& T) {
+  const Params& P = c.P;
+  const LayerBufs& lb = P.layers[T.layer];
+  const int32_t p = P.seq_len[T.b];
+  const int n = p < 0 ? 0 : std::min(p + 1, P.cap);
+  const int nact = (n + kAttnChunk - 1) / kAttnChunk;
+  for (int h = 0; h < P.G; ++h) {
+    float* dst = lb.attn + (int64_t)T.b * P.Hq * P.D + (int64_t)(T.g * P.G + h) * P.D;
+    if (nact == 0) {
+      for (int d = 0; d < P.D; ++d) dst[d] = 0.f;
+      continue;
+    }
+    auto part = [&](int ch) {
+      return lb.part + ((((int64_t)T.b * P.Hkv + T.g) * P.nch + ch) * P.G + h) * (P.D + 2);
+    };
+    float M = -std::numeric_limits<float>::infinity();
+    for (int ch = 0; ch < nact; ++ch) M = std::max(M, part(ch)[0]);
+    float L = 0.f;
+    for (int ch = 0; ch < nact; ++ch) L += part(ch)[1] * std::exp(part(ch)[0] - M);
+    for (int d = 0; d < P.D; ++d) {
+      float o = 0.f;
+      for (int ch = 0; ch < nact; ++ch) o += part(ch)[2 + d] * std::exp(part(ch)[0] - M);
+      dst[d] = o / L;
+    }
+  }
+}
+
+void run_argmax(Ctx& c) {
+  const Params& P = c.P;
+  for (int b = 0; b < P.B; ++b) {
+    unsigned long long best = 0;
+    for (int s = 0; s < kArgmaxShards; ++s) {
+      best = std::max(best, (unsigned long long)c.argmax[b * kArgmaxShards + s].load(std::memory_order_relaxed));
+      c.argmax[b * kArgmaxShards + s].store(0, std::memory_order_relaxed);
+    }
+    const int32_t p = P.seq_len[b];
+    if (p < 0 || p >= P.cap) continue;
+    P.tokens[b] = (int32_t)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFu));
+    P.seq_len[b] = p + 1;
+  }
+}
+
+void run_tile(Ctx& c, const Tile& T) {
+  switch (T.type) {
+    case T_ATTN: run_attn(c, T); break;
+    case T_COMBINE: run_combine(c, T); break;
+    case T_ARGMAX: run_argmax(c); break;
+    default: run_gemv(c, T); break;
+  }
+}
+
+Params host_params(wpk_plan* p, int32_t* tokens, wpk_kv* kv, float* logits) {
+  const Shape& s = p->s;
+  Params P{};
+  P.L = s.L; P.H = s.H; P.Hq = s.Hq; P.Hkv = s.Hkv; P.D = s.D; P.F = s.F; P.V = s.V;
+  P.B = s.B; P.cap = s.cap; P.nch = s.nch; P.G = s.G; P.qkv_rows = s.qkv_rows;
+  P.n_tiles = (int32_t)p->dag.tiles.size();
+  P.dtype = s.dtype;
+  P.eps = s.eps;
+  P.attn_scale = 1.0f / std::sqrt((float)s.D);
+  P.embed = p->desc.embed;
+  P.final_norm = p->desc.final_norm;
+  P.layers = p->hw.layers.data();
+  P.rope_cos = p->hw.rope_cos.data();
+  P.rope_sin = p->hw.rope_sin.data();
+  P.tokens = tokens;
+  P.seq_len = kv->seq_len;
+  P.logits = logits;
+  P.kc = (char*)kv->k;
+  P.vc = (char*)kv->v;
+  P.tiles = p->dag.tiles.data();
+  P.groups = p->dag.groups.data();
+  return P;
+}
+
+void poison(wpk_plan* p, const Params& P) {
+  const float nan = std::numeric_limits<float>::quiet_NaN();
+  std::fill(p->hw.act.begin(), p->hw.act.end(), nan);
+  std::fill(P.logits, P.logits + (int64_t)P.B * P.V, nan);
+  // the slot each active sequence is about to append: a read of it before the
+  // tile that writes it sees NaN
+  for (int b = 0; b < P.B; ++b) {
+    const int32_t pos = P.seq_len[b];
+    if (pos < 0 || pos >= P.cap) continue;
+    for (int l = 0; l < P.L; ++l)
+      for (int g = 0; g < P.Hkv; ++g) {
+        const int64_t at = ((((int64_t)l * P.B + b) * P.Hkv + g) * P.cap + pos) * P.D;
+        for (int d = 0; d < P.D; ++d) {
+          cache_put(P.kc, P.dtype, at + d, nan);
+          cache_put(P.vc, P.dtype, at + d, nan);
+        }
+      }
+  }
+}
+
+uint64_t mix64(uint64_t z) {
+  z += 0x9E3779B97F4A7C15ULL;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+  return z ^ (z >> 31);
+}
+
+bool args_ok(wpk_plan* p, int32_t* tokens, wpk_kv* kv, float* logits) {
+  if (!p || !p->host) return false;
+  if (!tokens || !kv || !kv->k || !kv->v || !kv->seq_len || !logits) {
+    p->err = "null argument";
+    return false;
+  }
+  return true;
+}
+
+}  // namespace
+
+wpk_plan* make_host_plan(const wpk_model_desc& d, int32_t batch, int32_t ctx_len, const wpk_build_opts& o,
+                         std::string* err) {
+  Shape s;
+  std::string e = check_shape(d, batch, ctx_len, o, &s);
+  if (!e.empty()) {
+    *err = e;
+    return nullptr;
+  }
+  std::unique_ptr<wpk_plan> p(new wpk_plan());
+  p->host = true;
+  p->s = s;
+  p->desc = d;
+  // keep our own copy of the per-layer pointer tables
+  p->tables.resize(7 * (size_t)s.L);
+  const void* const* src[7] = {(const void* const*)d.attn_norm, d.w_qkv, d.w_o, (const void* const*)d.mlp_norm,
+                               d.w_gate, d.w_up, d.w_down};
+  for (int k = 0; k < 7; ++k)
+    for (int l = 0; l < s.L; ++l) p->tables[(size_t)k * s.L + l] = src[k][l];
+  p->desc.attn_norm = (const float* const*)&p->tables[0];
+  p->desc.w_qkv = &p->tables[(size_t)1 * s.L];
+  p->desc.w_o = &p->tables[(size_t)2 * s.L];
+  p->desc.mlp_norm = (const float* const*)&p->tables[(size_t)3 * s.L];
+  p->desc.w_gate = &p->tables[(size_t)4 * s.L];
+  p->desc.w_up = &p->tables[(size_t)5 * s.L];
+  p->desc.w_down = &p->tables[(size_t)6 * s.L];
+  p->dag = build_dag(s);
+  e = validate_dag(s, p->dag);
+  if (!e.empty()) {
+    *err = "invalid DAG: " + e;
+    return nullptr;
+  }
+  for (const Tile& t : p->dag.tiles) p->built_wait.push_back(t.wait);
+  p->weight_bytes = step_weight_bytes(s);
+  const ActLayout a = act_layout(s);
+  p->hw.act.assign((size_t)a.total, 0.f);
+  fill_layers(s, p->desc, p->hw.act.data(), p->hw.layers);
+  rope_table(s, p->hw.rope_cos, p->hw.rope_sin);
+  p->hw.argmax.reset(new std::atomic<unsigned long long>[(size_t)s.B * kArgmaxShards]);
+  for (int i = 0; i < s.B * kArgmaxShards; ++i) p->hw.argmax[i].store(0);
+  p->log.assign(p->dag.tiles.size(), wpk_log_rec{});
+  return p.release();
+}
+
+int32_t host_serial_step(wpk_plan* p, int32_t* tokens, wpk_kv* kv, float* logits, uint64_t seed, bool poison_on) {
+  if (!args_ok(p, tokens, kv, logits)) return WPK_E_ARG;
+  Params P = host_params(p, tokens, kv, logits);
+  if (poison_on) poison(p, P);
+  std::atomic<int32_t> status{0};
+  Ctx c{P, p->hw.argmax.get(), &status};
+  const auto& tiles = p->dag.tiles;
+  const auto& groups = p->dag.groups;
+  const int32_t n = (int32_t)tiles.size();
+  std::vector<std::vector<int32_t>> waiters(groups.size());
+  std::vector<int32_t> ready, count(groups.size(), 0);
+  for (const Tile& t : tiles) {
+    if (t.wait < 0) ready.push_back(t.id);
+    else waiters[t.wait].push_back(t.id);
+  }
+  std::fill(p->log.begin(), p->log.end(), wpk_log_rec{});
+  uint64_t rng = seed;
+  int32_t done = 0;
+  while (!ready.empty()) {
+    rng = mix64(rng);
+    const size_t k = (size_t)(rng % ready.size());
+    const int32_t id = ready[k];
+    ready[k] = ready.back();
+    ready.pop_back();
+    const Tile& T = tiles[id];
+    wpk_log_rec& L = p->log[id];
+    L.exec_count += 1;
+    L.wait_delta = T.wait < 0 ? 0 : count[T.wait] - groups[T.wait].producers;
+    L.worker = 0;
+    L.claim = done;
+    L.t_start = 2 * (int64_t)done;
+    run_tile(c, T);
+    L.t_end = 2 * (int64_t)done + 1;
+    ++done;
+    if (T.signal >= 0 && ++count[T.signal] == groups[T.signal].producers)
+      for (int32_t w : waiters[T.signal]) ready.push_back(w);
+  }
+  if (done != n) {
+    p->err = "serial executor stalled: " + std::to_string(n - done) + " tiles never became ready";
+    return WPK_E_TIMEOUT;
+  }
+  return status.load();
+}
+
+int32_t host_emulate_step(wpk_plan* p, int32_t* tokens, wpk_kv* kv, float* logits, int32_t n_threads,
+                          uint64_t seed) {
+  if (!args_ok(p, tokens, kv, logits)) return WPK_E_ARG;
+  const Dag& d = p->dag;
+  const int32_t nq = (int32_t)d.queue_off.size() - 1;
+  if (n_threads < nq || n_threads > 256) {
+    p->err = "n_threads must be in [queue shards, 256]";
+    return WPK_E_ARG;
+  }
+  Params P = host_params(p, tokens, kv, logits);
+  std::atomic<int32_t> status{0};
+  Ctx c{P, p->hw.argmax.get(), &status};
+  std::unique_ptr<std::atomic<uint32_t>[]> counters(new std::atomic<uint32_t>[d.n_shard_slots]);
+  for (int i = 0; i < d.n_shard_slots; ++i) counters[i].store(0);
+  std::unique_ptr<std::atomic<uint32_t>[]> heads(new std::atomic<uint32_t>[nq]);
+  for (int i = 0; i < nq; ++i) heads[i].store(0);
+  const int32_t n = (int32_t)d.tiles.size();
+  std::unique_ptr<std::atomic<int32_t>[]> exec(new std::atomic<int32_t>[n]);
+  for (int i = 0; i < n; ++i) exec[i].store(0);
+  std::atomic<int32_t> abort{0};
+  std::fill(p->log.begin(), p->log.end(), wpk_log_rec{});
+  const auto t0 = std::chrono::steady_clock::now();
+  auto now_ns = [&] {
+    return (int64_t)std::chrono::duration_cast<std::chrono::nanoseconds>(std::chrono::steady_clock::now() - t0).count();
+  };
+  auto worker = [&](int w) {
+    const int q = w % nq;
+    const int32_t qb = d.queue_off[q], qn = d.queue_off[q + 1] - qb;
+    uint64_t rng = mix64(seed ^ (uint64_t)w * 0x9E37ULL);
+    for (;;) {
+      const uint32_t ci = heads[q].fetch_add(1, std::memory_order_relaxed);
+      if ((int32_t)ci >= qn || abort.load(std::memory_order_relaxed)) break;
+      const int32_t id = d.queue[qb + ci];
+      const Tile& T = d.tiles[id];
+      rng = mix64(rng);
+      for (uint64_t k = rng % 8; k; --k) std::this_thread::yield();
+      int32_t delta = 0;
+      if (T.wait >= 0) {
+        const Group& G = d.groups[T.wait];
+        const auto w0 = std::chrono::steady_clock::now();
+        for (;;) {
+          uint32_t sum = 0;
+          for (int s = 0; s < G.shards; ++s) sum += counters[G.shard0 + s].load(std::memory_order_acquire);
+          if ((int32_t)(sum - (uint32_t)G.producers) >= 0) {
+            delta = (int32_t)(sum - (uint32_t)G.producers);
+            break;
+          }
+          if (abort.load(std::memory_order_relaxed)) return;
+          if (std::chrono::steady_clock::now() - w0 > std::chrono::seconds(20)) {
+            int32_t z = 0;
+            status.compare_exchange_strong(z, WPK_E_TIMEOUT);
+            abort.store(1);
+            return;
+          }
+          std::this_thread::yield();
+        }
+      }
+      wpk_log_rec& L = p->log[id];
+      L.wait_delta = delta;
+      L.worker = w;
+      L.claim = (int32_t)ci;
+      L.t_start = now_ns();
+      exec[id].fetch_add(1, std::memory_order_relaxed);
+      run_tile(c, T);
+      L.t_end = now_ns();
+      if (T.signal >= 0) {
+        const Group& G = d.groups[T.signal];
+        counters[G.shard0 + T.shard].fetch_add(1, std::memory_order_release);
+      }
+    }
+  };
+  std::vector<std::thread> th;
+  for (int w = 0; w < n_threads; ++w) th.emplace_back(worker, w);
+  for (auto& t : th) t.join();
+  for (int i = 0; i < n; ++i) p->log[i].exec_count = exec[i].load();
+  if (abort.load()) {
+    p->err = "emulated worker timed out waiting on a counter";
+    return WPK_E_TIMEOUT;
+  }
+  return status.load();
+}
+
+}  // namespace wpk

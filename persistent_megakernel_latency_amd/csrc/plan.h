@@ -1,0 +1,117 @@
+// plan.h -- the compiled form of one decode step, shared by the host builder,
+// the host executors and the gfx950 kernels.
+//
+// The step is a DAG of tiles.  Every tile waits on at most one counter group
+// and signals exactly one: a group counts the tiles that produce the tensor
+// region its consumers read, so a consumer starts as soon as its own inputs
+// are complete instead of at an operator boundary (the tile-to-tile tensor
+// edges of "One Megakernel is Not Enough", Table I, cross-kernel readiness;
+// the per-chunk dependency counters of the Llama-1B megakernel described in
+// "persistent-threads-megakernels", section 6).
+#pragma once
+#include <stdint.h>
+
+namespace wpk {
+
+enum TileType : int32_t {
+  T_QKV = 0,      // RMSNorm prologue, QKV rows, RoPE + KV-append epilogue
+  T_ATTN = 1,     // split-KV decode attention partial over one KV chunk
+  T_COMBINE = 2,  // merge of the partials of one (sequence, kv head)
+  T_OPROJ = 3,    // output projection + residual
+  T_GATEUP = 4,   // RMSNorm prologue, gate and up rows, SwiGLU epilogue
+  T_DOWN = 5,     // down projection + residual
+  T_LM = 6,       // final RMSNorm prologue, tied LM-head rows, partial argmax
+  T_ARGMAX = 7,   // greedy token, seq_len advance (output conversion)
+  T_NTYPES = 8
+};
+
+// One tile: 64 bytes, loaded with scalar loads by a worker.
+struct Tile {
+  int32_t type, layer, wait, signal;  // wait/signal: counter group id or -1
+  int32_t shard;                      // counter shard of `signal` this tile increments
+  int32_t r0, r1, rs;                 // GEMV: rows [r0, r0+rs) then [r1, r1+(rows-rs)) of its matrix
+  int32_t rows;                       // GEMV: row capacity of the tile
+  int32_t b, g, c;                    // ATTN: sequence, kv head, KV chunk; COMBINE: b, g; QKV: head in g
+  int32_t kind;                       // QKV: 0 q rows, 1 k rows, 2 v rows
+  int32_t id;                         // tile id (index into the tile table and the log)
+  int32_t pad0, pad1;
+};
+static_assert(sizeof(Tile) == 64, "tile descriptor is 64 bytes");
+
+// A counter group: `producers` tiles increment it once per step, spread over
+// `shards` counters (each on its own 256-byte line) so that same-address
+// atomics do not serialise.  Step e (from 0) is complete when the shards sum
+// to (e + 1) * producers (modulo 2^32).
+struct Group {
+  int32_t producers, shard0, shards, pad;
+};
+
+constexpr int kThreads = 256;                         // threads per worker (4 wave64)
+constexpr int kWaves = kThreads / 64;
+constexpr int kChunks = 16;                           // 16-byte weight chunks per thread
+constexpr int kSlotBytes = kThreads * kChunks * 16;   // one staging slot: 64 KiB
+constexpr int kLine = 64;                             // uint32 stride of independent counters (256 B)
+constexpr int kAttnChunk = 64;                        // KV positions per attention partial
+constexpr int kHeadDim = 64;                          // the only head size built
+constexpr int kMaxGroupHeads = 4;                     // q heads per kv head
+constexpr int kArgmaxShards = 16;
+constexpr int kMaxShards = 16;
+constexpr int kMaxBatch = 4;
+
+// Control block: word offsets, each field on its own 256-byte line.
+enum : int32_t {
+  CTL_EPOCH = 0,     // steps completed
+  CTL_EXIT = 64,     // workers that left the current step
+  CTL_STATUS = 128,  // [0] error code, [1] tile, [2] worker, [3] epoch
+  CTL_ABORT = 192,   // nonzero: every worker stops
+  CTL_WORDS = 256
+};
+
+// Per-layer pointers: weights (caller-owned) and this layer's activations.
+struct LayerBufs {
+  const void* w_qkv;
+  const void* w_o;
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+  const float* attn_norm;
+  const float* mlp_norm;
+  const float* x_in;  // [B][H] layer input; nullptr for layer 0 (embedding gather)
+  float* x_mid;       // [B][H] after attention
+  float* x_out;       // [B][H] after the MLP
+  float* q;           // [B][Hq*D] rotated queries
+  float* part;        // [B][Hkv][nch][G][D+2] attention partials (m, l, o[D])
+  float* attn;        // [B][Hq*D] attention output
+  float* h;           // [B][F] SwiGLU output
+};
+
+// Everything a worker needs, passed by value to the kernel.
+struct Params {
+  int32_t L, H, Hq, Hkv, D, F, V, B, cap, nch, G, qkv_rows;
+  int32_t n_tiles, n_queues, n_workers, dtype;
+  float eps, attn_scale;
+  const void* embed;
+  const float* final_norm;
+  const LayerBufs* layers;
+  const float* rope_cos;  // [cap][D/2]
+  const float* rope_sin;  // [cap][D/2]
+  int32_t* tokens;
+  int32_t* seq_len;
+  float* logits;          // [B][V]
+  char* kc;               // [L][B][Hkv][cap][D]
+  char* vc;
+  const Tile* tiles;
+  const int32_t* queue;     // tile ids of all claim queues, concatenated
+  const int32_t* queue_off; // queue q holds queue[queue_off[q] .. queue_off[q+1])
+  const Group* groups;
+  uint32_t* counters;       // group shards, stride kLine
+  uint32_t* heads;          // claim head of each queue, stride kLine
+  uint32_t* ctl;            // control block
+  unsigned long long* argmax;  // [B][kArgmaxShards] packed (value, index) maxima
+  int32_t* log;             // wpk_log_rec per tile (8 int32 each)
+  int32_t log_on, prefetch, drop_tile;
+  uint32_t perturb;
+  uint64_t watchdog_ticks;  // s_memrealtime ticks (100 MHz)
+};
+
+}  // namespace wpk

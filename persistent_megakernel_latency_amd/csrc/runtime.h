@@ -1,0 +1,76 @@
+// runtime.h -- the plan object behind the C ABI (host side).
+#pragma once
+#include <atomic>
+#include <memory>
+#include <string>
+#include <vector>
+
+#include "builder.h"
+#include "plan.h"
+#include "wpk.h"
+
+namespace wpk {
+
+// Host memory for a plan that runs on the CPU (serial executor / emulator).
+struct HostWorkspace {
+  std::vector<float> act;                     // all per-layer activation buffers
+  std::vector<LayerBufs> layers;
+  std::vector<float> rope_cos, rope_sin;      // [cap][D/2]
+  std::unique_ptr<std::atomic<unsigned long long>[]> argmax;  // [B][kArgmaxShards]
+};
+
+// RoPE table: cos/sin of pos * theta^(-2i/D), computed in float64, stored float32.
+void rope_table(const Shape& s, std::vector<float>& cos_t, std::vector<float>& sin_t);
+
+// Bytes of the per-layer activation buffers and their placement.
+struct ActLayout {
+  int64_t x_mid, x_out, q, part, attn, h, per_layer;  // float offsets within a layer
+  int64_t total;                                      // floats for all layers
+};
+ActLayout act_layout(const Shape& s);
+
+// Fill per-layer LayerBufs given the weight tables and an activation arena.
+void fill_layers(const Shape& s, const wpk_model_desc& d, float* act, std::vector<LayerBufs>& out);
+
+}  // namespace wpk
+
+struct wpk_plan {
+  bool host = false;      // compiled for the host executors only
+  bool baseline = false;  // per-operator hipGraph baseline
+  wpk::Shape s{};
+  wpk::Dag dag;
+  std::vector<int32_t> built_wait;  // waits as built (restored by wpk_debug_drop_edge(-1))
+  wpk_model_desc desc{};
+  std::vector<const void*> tables;  // copies of the caller's per-layer pointer tables
+  std::string err;
+  std::vector<wpk_log_rec> log;     // host copy of the last log
+  int32_t latched = 0;              // device error seen by wpk_sync
+  int32_t log_on = 0, prefetch = 1, drop_tile = -1;
+  uint32_t perturb = 0;
+  uint64_t watchdog_us = 2000000;
+  int64_t weight_bytes = 0;
+
+  // host executors
+  wpk::HostWorkspace hw;
+
+  // device side (filled by the C ABI on a GPU)
+  int device = -1;
+  int n_cu = 0;
+  int workers = 0, max_workers = 0;
+  char* d_ws = nullptr;             // one allocation holding everything the plan owns
+  int64_t ws_bytes = 0;
+  wpk::Params P{};                  // device pointers; step I/O filled per call
+  const void* k_mega = nullptr;     // kernel handles
+  const void* k_mega_log = nullptr;
+  const void* k_phase = nullptr;
+  void* last_stream = nullptr;
+  // baseline graph
+  void* graph_exec = nullptr;
+  void* graph = nullptr;
+  void* cap_tokens = nullptr;
+  void* cap_kc = nullptr;
+  void* cap_vc = nullptr;
+  void* cap_seq = nullptr;
+  void* cap_logits = nullptr;
+  void* cap_stream = nullptr;
+};

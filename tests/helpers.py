@@ -1,0 +1,92 @@
+"""Shared test plumbing: host descriptors, KV state, DAG/log checks."""
+from __future__ import annotations
+
+import re
+import os
+from typing import Dict, List
+
+import numpy as np
+
+import persistent_megakernel_latency_amd as wpk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_symbols() -> List[str]:
+    """Function names include/wpk.h declares."""
+    src = open(os.path.join(ROOT, "include", "wpk.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(wpk_[a-z_]+)\s*\(", src)))
+
+
+def host_desc(cfg, weights: Dict[str, object]) -> wpk.ModelDesc:
+    """A descriptor pointing at numpy arrays (for the host executors)."""
+    keep = []
+
+    def ptr(a):
+        a = np.ascontiguousarray(a)
+        keep.append(a)
+        return a.ctypes.data
+
+    ptrs = {"embed": ptr(weights["embed"]), "final_norm": ptr(np.asarray(weights["final_norm"], np.float32))}
+    for key in ("attn_norm", "w_qkv", "w_o", "mlp_norm", "w_gate", "w_up", "w_down"):
+        ptrs[key] = [ptr(lw[key]) for lw in weights["layers"]]
+    return wpk.ModelDesc(cfg, ptrs, keep)
+
+
+def dummy_desc(cfg) -> wpk.ModelDesc:
+    """Non-null but never dereferenced pointers, for building a DAG only."""
+    fake = 0x1000
+    ptrs = {"embed": fake, "final_norm": fake}
+    for key in ("attn_norm", "w_qkv", "w_o", "mlp_norm", "w_gate", "w_up", "w_down"):
+        ptrs[key] = [fake] * cfg.n_layers
+    return wpk.ModelDesc(cfg, ptrs)
+
+
+class HostState:
+    """KV cache, seq_len and token buffers in host memory, shaped for a plan."""
+
+    def __init__(self, kc: np.ndarray, vc: np.ndarray, seq_len: np.ndarray, tokens: np.ndarray, vocab: int):
+        self.kc = np.ascontiguousarray(kc).copy()
+        self.vc = np.ascontiguousarray(vc).copy()
+        self.seq_len = np.ascontiguousarray(seq_len, dtype=np.int32).copy()
+        self.tokens = np.ascontiguousarray(tokens, dtype=np.int32).copy()
+        self.logits = np.zeros((len(self.tokens), vocab), np.float32)
+        self.kv = wpk.wpk_kv(self.kc.ctypes.data, self.vc.ctypes.data, self.seq_len.ctypes.data)
+
+    def serial(self, plan, seed: int, poison: bool = False) -> int:
+        return wpk.wpk_serial_step(plan, self.tokens.ctypes.data, self.kv, self.logits.ctypes.data, seed, poison)
+
+    def emulate(self, plan, threads: int, seed: int) -> int:
+        return wpk.wpk_emulate_step(plan, self.tokens.ctypes.data, self.kv, self.logits.ctypes.data, threads, seed)
+
+
+def dag_edges(wait: List[int], signal: List[int]):
+    """Producer lists per group: edge u -> v iff signal[u] == wait[v]."""
+    prod: Dict[int, List[int]] = {}
+    for u, s in enumerate(signal):
+        if s >= 0:
+            prod.setdefault(s, []).append(u)
+    return prod
+
+
+def check_log(log, wait, signal, canonical_only: bool = False) -> None:
+    """Canonical log: every tile ran once with its counter exactly complete;
+    and the raw order is a linear extension of the DAG (every producer ended
+    before its consumer started)."""
+    n = len(wait)
+    ex = np.array([log[i].exec_count for i in range(n)])
+    de = np.array([log[i].wait_delta for i in range(n)])
+    assert np.all(ex == 1), f"tiles not run exactly once: {np.nonzero(ex != 1)[0][:10]}"
+    assert np.all(de == 0), f"counters not exactly complete at start: {np.nonzero(de != 0)[0][:10]}"
+    if canonical_only:
+        return
+    start = np.array([log[i].t_start for i in range(n)], dtype=np.int64)
+    end = np.array([log[i].t_end for i in range(n)], dtype=np.int64)
+    prod = dag_edges(wait, signal)
+    for v in range(n):
+        g = wait[v]
+        if g < 0:
+            continue
+        pe = end[prod[g]]
+        assert pe.max() <= start[v], f"tile {v} started before producer ended"

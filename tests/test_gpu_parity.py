@@ -1,0 +1,199 @@
+"""GPU parity: the megakernel (through the C ABI) against the CPU oracle.
+
+Bars: float32 runs max |logit error| <= 1e-4; bf16-weight runs <= 2e-2;
+greedy tokens identical (a mismatch is accepted only as a reported near tie,
+oracle top-2 margin within 4x the measured error); the canonical per-tile log
+(every tile exactly once, counter exactly complete at start) identical to the
+serial executor's, and the raw device order a linear extension of the DAG.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import persistent_megakernel_latency_amd as wpk
+import synth
+from tests.gpu_helpers import GpuPlan, announce, tokens_agree
+from tests.helpers import check_log
+
+pytestmark = pytest.mark.gpu
+
+
+def _tiny_prefilled(prompt_len=64, cap=80, gain_std=0.1):
+    cfg = synth.TINY
+    w = synth.make_weights(cfg, gain_std=gain_std)
+    model = oracle.Model(cfg, w)
+    prompt = synth.prompt_tokens(cfg, 1, prompt_len)
+    kc, vc = model.new_cache(1, cap)
+    sl = np.zeros(1, np.int32)
+    _, tok = model.prefill(prompt, kc, vc, sl)
+    return cfg, w, model, kc, vc, sl, tok
+
+
+def _teacher_forced(g: GpuPlan, model, kc, vc, sl, tok, steps, tol, name, log=True):
+    """Runs `steps` steps feeding the oracle's tokens; returns max logit error."""
+    worst = 0.0
+    ties = []
+    if log:
+        wpk.check(wpk.wpk_set_option(g.plan, wpk.WPK_OPT_LOG, 1), g.plan)
+    ty, layer, wait, signal = g.dag()
+    for s in range(steps):
+        announce(f"{name} step {s}")
+        g.set_tokens(tok)
+        g.step()
+        gk, gv, gsl, gtok, glog = g.state()
+        olog, otok = model.step(tok, kc, vc, sl)
+        for b in range(len(tok)):
+            if sl[b] < 0:
+                continue
+            err = float(np.max(np.abs(glog[b] - olog[b])))
+            worst = max(worst, err)
+            assert err <= tol, f"{name} step {s} seq {b}: max |logit err| {err}"
+            ok, why = tokens_agree(int(gtok[b]), int(otok[b]), olog[b], err)
+            assert ok, f"{name} step {s} seq {b}: {why}"
+            if why:
+                ties.append(why)
+        assert np.array_equal(gsl, sl)
+        if log:
+            check_log(g.log(), wait, signal)
+        tok = otok
+    if ties:
+        print(f"{name}: near ties {ties}")
+    return worst
+
+
+def test_tiny_fp32_teacher_forced():
+    cfg, w, model, kc, vc, sl, tok = _tiny_prefilled()
+    g = GpuPlan(cfg, w, 1, kc.shape[3], kc, vc, sl, tok)
+    worst = _teacher_forced(g, model, kc, vc, sl, tok, 8, 1e-4, "tiny")
+    # the appended keys/values match the oracle's cache at float32 rounding
+    gk, gv, _, _, _ = g.state()
+    assert np.max(np.abs(gk - kc)) < 1e-5 and np.max(np.abs(gv - vc)) < 1e-5
+    print("tiny max logit error", worst)
+    g.close()
+
+
+def test_tiny_free_running_matches_golden_tokens():
+    import json
+    import os
+    gold = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "tiny_greedy.json")))
+    cfg, w, model, kc, vc, sl, tok = _tiny_prefilled(gold["prompt_len"], gain_std=0.0)
+    g = GpuPlan(cfg, w, 1, kc.shape[3], kc, vc, sl, tok)
+    got = []
+    for s in range(gold["steps"]):
+        announce(f"tiny free-running step {s}")
+        got.append(int(g.tokens.cpu()[0]))
+        g.step()  # tokens chain on the device: no host round trip
+    assert got == gold["greedy_tokens"]
+    g.close()
+
+
+def test_mini_bf16_batch_ragged_inactive():
+    cfg = synth.MINI
+    w = synth.make_weights(cfg, gain_std=0.1)
+    model = oracle.Model(cfg, w)
+    cap = 200
+    lens = np.array([63, -1, 64, 190], np.int32)
+    kc, vc = synth.synthetic_kv(cfg, 4, cap, np.maximum(lens, 0))
+    tok = np.array([5, 6, 7, 999], np.int32)
+    g = GpuPlan(cfg, w, 4, cap, kc, vc, lens, tok)
+    k0 = kc.copy()
+    worst = _teacher_forced(g, model, kc, vc, lens, tok, 3, 2e-2, "mini-b4")
+    gk, gv, gsl, gtok, _ = g.state()
+    assert gtok[1] == 6 and gsl[1] == -1
+    assert np.array_equal(gk[:, 1], k0[:, 1])
+    print("mini max logit error", worst)
+    g.close()
+
+
+@pytest.fixture(scope="module")
+def llama():
+    cfg = synth.LLAMA_1B
+    announce("generating Llama-1B-shaped weights")
+    w = synth.make_weights(cfg, gain_std=0.1)
+    return cfg, w
+
+
+def test_llama_1b_batch1_teacher_forced(llama):
+    cfg, w = llama
+    model = oracle.Model(cfg, w)
+    cap, ctx = 576, 496
+    kc, vc = synth.synthetic_kv(cfg, 1, cap, np.array([ctx]))
+    sl = np.array([ctx], np.int32)
+    tok = synth.prompt_tokens(cfg, 1, ctx)[:, -1].copy()
+    announce("llama-1b build")
+    g = GpuPlan(cfg, w, 1, cap, kc, vc, sl, tok)
+    worst = _teacher_forced(g, model, kc, vc, sl, tok, 3, 2e-2, "llama-1b")
+    print("llama-1b max logit error", worst)
+    g.close()
+
+
+def test_graph_baseline_equals_megakernel_bitwise():
+    cfg = synth.MINI
+    w = synth.make_weights(cfg, gain_std=0.1)
+    cap = 130
+    lens = np.array([100, 7], np.int32)
+    kc, vc = synth.synthetic_kv(cfg, 2, cap, lens)
+    tok = np.array([1, 2], np.int32)
+    announce("mini megakernel vs hipGraph baseline")
+    a = GpuPlan(cfg, w, 2, cap, kc, vc, lens, tok)
+    b = GpuPlan(cfg, w, 2, cap, kc, vc, lens, tok, baseline=True, desc=a.desc)
+    for s in range(3):
+        a.step()
+        b.step()
+        sa, sb = a.state(), b.state()
+        for x, y in zip(sa, sb):
+            assert np.array_equal(x, y), f"step {s}"
+    a.close()
+    b.close()
+
+
+def test_determinism_perturbation_and_prefetch_off():
+    cfg, w, model, kc, vc, sl, tok = _tiny_prefilled(prompt_len=30, cap=64)
+    outs = []
+    for variant in ("base", "again", "perturb", "noprefetch"):
+        announce(f"tiny determinism {variant}")
+        g = GpuPlan(cfg, w, 1, 64, kc, vc, sl, tok)
+        if variant == "perturb":
+            wpk.check(wpk.wpk_set_option(g.plan, wpk.WPK_OPT_PERTURB_SEED, 1234), g.plan)
+        if variant == "noprefetch":
+            wpk.check(wpk.wpk_set_option(g.plan, wpk.WPK_OPT_PREFETCH, 0), g.plan)
+        for _ in range(3):
+            g.step()
+        outs.append(g.state())
+        g.close()
+    for o in outs[1:]:
+        for x, y in zip(outs[0], o):
+            assert np.array_equal(x, y)
+
+
+def test_watchdog_reports_a_missing_publish_and_recovers():
+    cfg, w, model, kc, vc, sl, tok = _tiny_prefilled(prompt_len=20, cap=64)
+    g = GpuPlan(cfg, w, 1, 64, kc, vc, sl, tok)
+    ty, layer, wait, signal = g.dag()
+    victim = next(i for i in range(len(ty)) if ty[i] == 4 and layer[i] == 0)  # a gate/up tile
+    wpk.check(wpk.wpk_set_option(g.plan, wpk.WPK_OPT_WATCHDOG_US, 20000), g.plan)
+    wpk.check(wpk.wpk_set_option(g.plan, wpk.WPK_OPT_DEBUG_DROP_TILE, victim), g.plan)
+    announce("tiny watchdog (dropped publish)")
+    rc = g.step(check=False)
+    assert rc == wpk.WPK_E_TIMEOUT
+    msg = wpk.wpk_last_error(g.plan)
+    assert "tile" in msg
+    # the tile named is one that waited on the victim's group
+    named = int(msg.split("tile ")[1].split()[0])
+    assert wait[named] == signal[victim]
+    assert wpk.wpk_step(g.plan, g.tokens.data_ptr(), g.kv, g.logits.data_ptr(), 0) == wpk.WPK_E_STATE
+    # reset, restore the inputs, run clean
+    wpk.check(wpk.wpk_set_option(g.plan, wpk.WPK_OPT_DEBUG_DROP_TILE, -1), g.plan)
+    wpk.check(wpk.wpk_set_option(g.plan, wpk.WPK_OPT_RESET, 1), g.plan)
+    g2 = GpuPlan(cfg, w, 1, 64, kc, vc, sl, tok)
+    g.kc.copy_(g2.kc)
+    g.vc.copy_(g2.vc)
+    g.seq_len.copy_(g2.seq_len)
+    g.set_tokens(tok)
+    announce("tiny after reset")
+    g.step()
+    g2.step()
+    for x, y in zip(g.state(), g2.state()):
+        assert np.array_equal(x, y)
+    g.close()
+    g2.close()

@@ -1,0 +1,186 @@
+"""CPU tests of the tile-graph builder, the serial DAG executor, the threaded
+protocol emulator and the C-ABI surface (no GPU)."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle
+import persistent_megakernel_latency_amd as wpk
+import synth
+from tests.helpers import HostState, check_log, dummy_desc, header_symbols, host_desc
+
+
+def test_library_exports_every_declared_symbol():
+    declared = header_symbols()
+    assert "wpk_build" in declared and "wpk_step" in declared
+    lib = wpk.lib()
+    missing = [s for s in declared if not hasattr(lib, s)]
+    assert missing == []
+    assert sorted(wpk.symbols()) == declared
+
+
+def test_build_errors_are_reported():
+    d = dummy_desc(synth.TINY)
+    assert not wpk.wpk_build_host(d.desc, 0, 64)
+    assert "batch" in wpk.wpk_last_error(None)
+    d.desc.head_dim = 32
+    assert not wpk.wpk_build_host(d.desc, 1, 64)
+    assert "head_dim" in wpk.wpk_last_error(None)
+
+
+def _info_and_dag(cfg, batch, cap, **opts):
+    d = dummy_desc(cfg)
+    o = wpk.wpk_build_opts(**opts) if opts else None
+    p = wpk.wpk_build_host(d.desc, batch, cap, o)
+    assert p, wpk.wpk_last_error(None)
+    info = wpk.wpk_get_info(p)
+    dag = wpk.wpk_get_dag(p, info.n_tiles)
+    wpk.wpk_destroy(p)
+    return info, dag
+
+
+def test_llama_1b_dag_shape():
+    cfg = synth.LLAMA_1B
+    info, (ty, layer, wait, signal) = _info_and_dag(cfg, 1, 576)
+    ty = np.array(ty)
+    # per layer: QKV 3072/16 = 192, attention 8 kv heads x 9 chunks, 8 combines,
+    # o-proj 2048/16, gate/up 8192/8, down 2048/4; then 128256/16 LM tiles + argmax
+    per_layer = {0: 192, 1: 72, 2: 8, 3: 128, 4: 1024, 5: 512}
+    for t, n in per_layer.items():
+        assert np.sum(ty == t) == 16 * n
+    assert np.sum(ty == 6) == 8016 and np.sum(ty == 7) == 1
+    assert info.n_tiles == 16 * sum(per_layer.values()) + 8016 + 1
+    assert info.rows_per_tile_h == 16 and info.rows_per_tile_f == 4
+    assert info.weight_bytes == synth.LLAMA_1B.weight_bytes()
+    # every consumer's producers precede it (the claim order is topological)
+    last_prod = {}
+    for u, s in enumerate(signal):
+        if s >= 0:
+            last_prod[s] = u
+    for v, g in enumerate(wait):
+        if g >= 0:
+            assert last_prod[g] < v
+
+
+@pytest.mark.parametrize("tile_bytes", [4096, 16384, 65536])
+def test_dag_validates_for_tile_sizes(tile_bytes):
+    for cfg in (synth.TINY, synth.MINI):
+        info, _ = _info_and_dag(cfg, 2, 100, tile_bytes=tile_bytes)
+        assert info.n_tiles > 0
+
+
+def _tiny_setup(prompt_len=16, cap=40, gain_std=0.1):
+    cfg = synth.TINY
+    w = synth.make_weights(cfg, gain_std=gain_std)
+    model = oracle.Model(cfg, w)
+    prompt = synth.prompt_tokens(cfg, 1, prompt_len)
+    kc, vc = model.new_cache(1, cap)
+    sl = np.zeros(1, np.int32)
+    _, tok = model.prefill(prompt, kc, vc, sl)
+    return cfg, w, model, kc, vc, sl, tok
+
+
+def test_serial_executor_matches_oracle_and_is_order_independent():
+    cfg, w, model, kc, vc, sl, tok = _tiny_setup()
+    d = host_desc(cfg, w)
+    plan = wpk.wpk_build_host(d.desc, 1, kc.shape[3])
+    assert plan, wpk.wpk_last_error(None)
+    n = wpk.wpk_get_info(plan).n_tiles
+    _, _, wait, signal = wpk.wpk_get_dag(plan, n)
+    ref_state = None
+    for step in range(3):
+        # the oracle's step (teacher-forced input tok)
+        ok_, ov_, osl = kc.copy(), vc.copy(), sl.copy()
+        olog, otok = model.step(tok, ok_, ov_, osl)
+        results = []
+        for seed in range(12 if step == 0 else 3):
+            st = HostState(kc, vc, sl, tok, cfg.vocab)
+            assert st.serial(plan, seed, poison=(seed % 2 == 1)) == 0, wpk.wpk_last_error(plan)
+            rc, log = wpk.wpk_get_log(plan, n)
+            assert rc == 0
+            check_log(log, wait, signal)
+            results.append(st)
+        for st in results[1:]:
+            assert np.array_equal(st.logits, results[0].logits)
+            assert np.array_equal(st.kc, results[0].kc) and np.array_equal(st.vc, results[0].vc)
+        st = results[0]
+        assert np.max(np.abs(st.logits[0] - olog[0])) < 1e-4
+        assert st.tokens[0] == otok[0] and st.seq_len[0] == osl[0]
+        kc, vc, sl, tok = ok_, ov_, osl, otok  # continue from the oracle's state
+
+
+def test_dropped_edge_is_caught_by_nan_poison():
+    cfg, w, model, kc, vc, sl, tok = _tiny_setup()
+    d = host_desc(cfg, w)
+    plan = wpk.wpk_build_host(d.desc, 1, kc.shape[3])
+    n = wpk.wpk_get_info(plan).n_tiles
+    ty, layer, wait, signal = wpk.wpk_get_dag(plan, n)
+    # an output-projection tile of layer 1 no longer waits for the attention combine
+    victim = next(i for i in range(n) if ty[i] == 3 and layer[i] == 1)
+    assert wpk.wpk_debug_drop_edge(plan, victim) == 0
+    poisoned = 0
+    for seed in range(8):
+        st = HostState(kc, vc, sl, tok, cfg.vocab)
+        st.serial(plan, seed, poison=True)
+        poisoned += int(np.isnan(st.logits).any())
+    assert poisoned > 0
+    assert wpk.wpk_debug_drop_edge(plan, -1) == 0
+    st = HostState(kc, vc, sl, tok, cfg.vocab)
+    assert st.serial(plan, 0, poison=True) == 0 and not np.isnan(st.logits).any()
+    wpk.wpk_destroy(plan)
+
+
+@pytest.mark.parametrize("threads", [8, 33])
+def test_emulated_protocol_matches_serial(threads):
+    cfg, w, model, kc, vc, sl, tok = _tiny_setup()
+    d = host_desc(cfg, w)
+    plan = wpk.wpk_build_host(d.desc, 1, kc.shape[3])
+    n = wpk.wpk_get_info(plan).n_tiles
+    _, _, wait, signal = wpk.wpk_get_dag(plan, n)
+    ref = HostState(kc, vc, sl, tok, cfg.vocab)
+    assert ref.serial(plan, 0) == 0
+    for seed in range(3):
+        st = HostState(kc, vc, sl, tok, cfg.vocab)
+        assert st.emulate(plan, threads, seed) == 0, wpk.wpk_last_error(plan)
+        rc, log = wpk.wpk_get_log(plan, n)
+        check_log(log, wait, signal)
+        assert np.array_equal(st.logits, ref.logits)
+        assert st.tokens[0] == ref.tokens[0] and st.seq_len[0] == ref.seq_len[0]
+    wpk.wpk_destroy(plan)
+
+
+def test_batch_with_inactive_slot_and_ragged_lengths():
+    cfg = synth.MINI
+    w = synth.make_weights(cfg, gain_std=0.1)
+    model = oracle.Model(cfg, w)
+    cap = 140  # 3 KV chunks, the last one partial
+    lens = np.array([63, -1, 64, 129], np.int32)  # chunk edges and an inactive slot
+    kc, vc = synth.synthetic_kv(cfg, 4, cap, np.maximum(lens, 0))
+    tok = np.array([5, 6, 7, 999], np.int32)
+    d = host_desc(cfg, w)
+    plan = wpk.wpk_build_host(d.desc, 4, cap)
+    assert plan, wpk.wpk_last_error(None)
+    st = HostState(kc, vc, lens, tok, cfg.vocab)
+    assert st.serial(plan, 3, poison=True) == 0
+    ok_, ov_, osl = kc.copy(), vc.copy(), lens.copy()
+    olog, otok = model.step(tok, ok_, ov_, osl)
+    for b in (0, 2, 3):
+        assert np.max(np.abs(st.logits[b] - olog[b])) < 2e-3
+        assert st.tokens[b] == otok[b]
+    assert st.tokens[1] == 6 and st.seq_len.tolist() == osl.tolist()
+    assert np.array_equal(st.kc[:, 1], kc[:, 1])
+    wpk.wpk_destroy(plan)
+
+
+def test_full_cache_and_bad_token_are_errors():
+    cfg, w, model, kc, vc, sl, tok = _tiny_setup(prompt_len=4, cap=4)
+    d = host_desc(cfg, w)
+    plan = wpk.wpk_build_host(d.desc, 1, 4)
+    st = HostState(kc, vc, sl, tok, cfg.vocab)
+    assert st.serial(plan, 0) == wpk.WPK_E_CTX_FULL
+    cfg, w, model, kc, vc, sl, tok = _tiny_setup(prompt_len=4, cap=8)
+    d = host_desc(cfg, w)
+    plan = wpk.wpk_build_host(d.desc, 1, 8)
+    st = HostState(kc, vc, sl, np.array([cfg.vocab + 5], np.int32), cfg.vocab)
+    assert st.serial(plan, 0) == wpk.WPK_E_TOKEN

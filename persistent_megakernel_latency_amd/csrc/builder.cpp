@@ -37,6 +37,7 @@ std::string check_shape(const wpk_model_desc& d, int32_t batch, int32_t ctx_len,
   s.eps = d.rms_eps;
   if (s.L <= 0 || s.H <= 0 || s.Hq <= 0 || s.Hkv <= 0 || s.F <= 0 || s.V <= 0)
     return "model dimensions must be positive";
+  if (s.L > kMaxLayers) return "at most 32 layers";
   if (d.dtype != WPK_F32 && d.dtype != WPK_BF16) return "dtype must be WPK_F32 or WPK_BF16";
   if (!d.tied_embeddings) return "only tied embeddings (lm_head = embed) are built";
   if (s.D != kHeadDim) return "head_dim must be 64";

@@ -12,6 +12,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "host_exec.h"
 #include "runtime.h"
@@ -186,6 +187,20 @@ wpk_plan* build_device(const wpk_model_desc* desc, int32_t batch, int32_t ctx_le
   P.embed = p->desc.embed;
   P.final_norm = p->desc.final_norm;
   P.layers = (const LayerBufs*)(w + L.layers);
+  {
+    const ActLayout a = act_layout(s);
+    P.act = (float*)(w + L.act);
+    P.act_layer = a.per_layer;
+    P.off_x_mid = (int32_t)a.x_mid;
+    P.off_x_out = (int32_t)a.x_out;
+    P.off_q = (int32_t)a.q;
+    P.off_part = (int32_t)a.part;
+    P.off_attn = (int32_t)a.attn;
+    P.off_h = (int32_t)a.h;
+    for (int l = 0; l < s.L; ++l)
+      P.lw[l] = LayerW{p->desc.w_qkv[l], p->desc.w_o[l], p->desc.w_gate[l], p->desc.w_up[l], p->desc.w_down[l],
+                       p->desc.attn_norm[l], p->desc.mlp_norm[l]};
+  }
   P.rope_cos = (const float*)(w + L.rope_cos);
   P.rope_sin = (const float*)(w + L.rope_sin);
   P.tiles = (const Tile*)(w + L.tiles);
@@ -321,9 +336,28 @@ int32_t wpk_sync(wpk_plan* p) {
   if (e != hipSuccess) return plan_fail(p, WPK_E_HIP, hip_msg("status read", e));
   if (st[0] != 0) {
     p->latched = (int32_t)st[0];
-    char m[200];
+    char m[320];
     snprintf(m, sizeof m, "device error %d at tile %u (worker %u, step %u)", (int32_t)st[0], st[1], st[2], st[3]);
     p->err = m;
+    if ((int32_t)st[0] == WPK_E_TIMEOUT) {
+      // Name the root cause: the first counter group (groups are numbered in
+      // topological order) that did not receive all of its increments.
+      std::vector<uint32_t> ctr((size_t)p->dag.n_shard_slots * kLine);
+      if (hipMemcpy(ctr.data(), p->P.counters, ctr.size() * 4, hipMemcpyDeviceToHost) == hipSuccess) {
+        for (size_t g = 0; g < p->dag.groups.size(); ++g) {
+          const Group& G = p->dag.groups[g];
+          uint32_t sum = 0;
+          for (int s = 0; s < G.shards; ++s) sum += ctr[(size_t)(G.shard0 + s) * kLine];
+          const uint32_t target = (st[3] + 1u) * (uint32_t)G.producers;
+          if ((int32_t)(sum - target) < 0) {
+            snprintf(m, sizeof m, "; first incomplete group %zu: %d of %d publishes this step", g,
+                     (int32_t)(sum - st[3] * (uint32_t)G.producers), G.producers);
+            p->err += m;
+            break;
+          }
+        }
+      }
+    }
     return p->latched;
   }
   return WPK_OK;

@@ -379,6 +379,15 @@ Params host_params(wpk_plan* p, int32_t* tokens, wpk_kv* kv, float* logits) {
   P.embed = p->desc.embed;
   P.final_norm = p->desc.final_norm;
   P.layers = p->hw.layers.data();
+  const ActLayout a = act_layout(s);
+  P.act = p->hw.act.data();
+  P.act_layer = a.per_layer;
+  P.off_x_mid = (int32_t)a.x_mid;
+  P.off_x_out = (int32_t)a.x_out;
+  P.off_q = (int32_t)a.q;
+  P.off_part = (int32_t)a.part;
+  P.off_attn = (int32_t)a.attn;
+  P.off_h = (int32_t)a.h;
   P.rope_cos = p->hw.rope_cos.data();
   P.rope_sin = p->hw.rope_sin.data();
   P.tokens = tokens;

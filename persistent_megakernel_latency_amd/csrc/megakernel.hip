@@ -116,6 +116,35 @@ __device__ __forceinline__ u32x4 ld_sc1_x4(const float* base, int32_t float_off)
   return __builtin_amdgcn_raw_buffer_load_b128(r, float_off * 4, 0, 16 /* sc1 */);
 }
 
+// Read-only tables (tiles, groups, queues) through the constant address space:
+// uniform loads from it become scalar loads that do not count against the
+// vector-memory counter the weight stream uses.
+template <class T>
+__device__ __forceinline__ T cload(const T* p, int i) {
+  static_assert(sizeof(T) % 4 == 0, "table entries are whole 32-bit words");
+  T v;
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int W = sizeof(T) / 4;
+  const int32_t __attribute__((address_space(4)))* src =
+      (const int32_t __attribute__((address_space(4)))*)(const void*)p + (size_t)i * W;
+  int32_t w[W];
+#pragma unroll
+  for (int k = 0; k < W; ++k) w[k] = src[k];
+  __builtin_memcpy(&v, w, sizeof(T));
+#else
+  v = p[i];  // the host compilation pass never runs device code
+#endif
+  return v;
+}
+
+// Activations of layer l (one arena, fixed offsets per layer).
+__device__ __forceinline__ float* act(const Params& P, int l, int32_t off) {
+  return P.act + (size_t)l * P.act_layer + off;
+}
+__device__ __forceinline__ const float* x_in(const Params& P, int l) {
+  return l == 0 ? nullptr : act(P, l - 1, P.off_x_out);
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
 
@@ -239,16 +268,15 @@ __device__ __forceinline__ void stage_gemv(const void* w0, const void* w1, int r
   const int t = wpk_tid();
 #pragma unroll
   for (int j = 0; j < kChunks; ++j) {
+    // Rows past the tile or the matrix are clamped to a valid row, so every
+    // load is unconditional; their (duplicate) sums are never stored.
     const int flat = j * kThreads + t;
-    const int row = flat / CPR;
+    const int row = min(flat / CPR, rows - 1);
     const int col = flat % CPR;
     const bool seg1 = row >= rs;
-    const int mrow = seg1 ? r1 + (row - rs) : r0 + row;
+    const int mrow = min(seg1 ? r1 + (row - rs) : r0 + row, limit - 1);
     const char* base = (const char*)(seg1 ? w1 : w0);
-    if (row < rows && mrow < limit)
-      s.c[j] = ld_nt(base + (size_t)mrow * (CPR * 16) + (size_t)col * 16);
-    else
-      s.c[j] = u32x4{0u, 0u, 0u, 0u};
+    s.c[j] = ld_nt(base + (size_t)mrow * (CPR * 16) + (size_t)col * 16);
   }
 }
 
@@ -259,16 +287,16 @@ __device__ __forceinline__ void gemv_input(const Params& P, const Tile& T, int b
                                            float (&x)[Geo<CPR>::LPR * WT_<WT>::EPC], Smem<WT>& sm) {
   constexpr int EPC = WT_<WT>::EPC, LPR = Geo<CPR>::LPR;
   const int t = wpk_tid();
-  const LayerBufs& lb = P.layers[T.layer];
+  const LayerW& lw = P.lw[T.layer];
   const float* src = nullptr;
   const float* gain = nullptr;
   int K = P.H;
   switch (T.type) {
-    case T_QKV: src = lb.x_in; gain = lb.attn_norm; break;
-    case T_OPROJ: src = lb.attn; break;
-    case T_GATEUP: src = lb.x_mid; gain = lb.mlp_norm; break;
-    case T_DOWN: src = lb.h; K = P.F; break;
-    default: src = P.layers[P.L - 1].x_out; gain = P.final_norm; break;
+    case T_QKV: src = x_in(P, T.layer); gain = lw.attn_norm; break;
+    case T_OPROJ: src = act(P, T.layer, P.off_attn); break;
+    case T_GATEUP: src = act(P, T.layer, P.off_x_mid); gain = lw.mlp_norm; break;
+    case T_DOWN: src = act(P, T.layer, P.off_h); K = P.F; break;
+    default: src = act(P, P.L - 1, P.off_x_out); gain = P.final_norm; break;
   }
 #pragma unroll
   for (int k = 0; k < LPR; ++k) {
@@ -352,7 +380,7 @@ template <typename WT, int CPR>
 __device__ __forceinline__ void gemv_tile(const Params& P, const Tile& T, const Slot& s, Smem<WT>& sm) {
   using G = Geo<CPR>;
   const int t = wpk_tid();
-  const LayerBufs& lb = P.layers[T.layer];
+  const int l = T.layer;
   for (int b = 0; b < P.B; ++b) {
     const int32_t p = ld_sc1(&P.seq_len[b]);
     if (T.type == T_QKV && p < 0) continue;  // inactive slot: nothing to append
@@ -384,7 +412,7 @@ __device__ __forceinline__ void gemv_tile(const Params& P, const Tile& T, const 
             const float a = y[t], bb = y[T.rs + t];
             const float ra = a * cs - bb * sn, rb = bb * cs + a * sn;
             if (T.kind == 0) {
-              float* q = lb.q + (size_t)b * P.Hq * P.D + head * P.D;
+              float* q = act(P, l, P.off_q) + (size_t)b * P.Hq * P.D + head * P.D;
               st_sc1(q + dim, ra);
               st_sc1(q + dim + half, rb);
             } else {
@@ -416,21 +444,21 @@ __device__ __forceinline__ void gemv_tile(const Params& P, const Tile& T, const 
             const WT* e = (const WT*)P.embed + (size_t)tok * P.H + row;
             xin = sizeof(WT) == 2 ? bf16_lo(*(const uint16_t*)e) : *(const float*)e;
           } else {
-            xin = ld_sc1(lb.x_in + (size_t)b * P.H + row);
+            xin = ld_sc1(x_in(P, l) + (size_t)b * P.H + row);
           }
-          st_sc1(lb.x_mid + (size_t)b * P.H + row, xin + y[t]);
+          st_sc1(act(P, l, P.off_x_mid) + (size_t)b * P.H + row, xin + y[t]);
         }
         break;
       case T_GATEUP:
         if (t < T.rs && T.r0 + t < P.F) {
           const float g = y[t], u = y[T.rs + t];
-          st_sc1(lb.h + (size_t)b * P.F + T.r0 + t, g / (1.0f + __expf(-g)) * u);
+          st_sc1(act(P, l, P.off_h) + (size_t)b * P.F + T.r0 + t, g / (1.0f + __expf(-g)) * u);
         }
         break;
       case T_DOWN:
         if (t < T.rows && T.r0 + t < P.H) {
           const int row = T.r0 + t;
-          st_sc1(lb.x_out + (size_t)b * P.H + row, ld_sc1(lb.x_mid + (size_t)b * P.H + row) + y[t]);
+          st_sc1(act(P, l, P.off_x_out) + (size_t)b * P.H + row, ld_sc1(act(P, l, P.off_x_mid) + (size_t)b * P.H + row) + y[t]);
         }
         break;
       case T_LM:
@@ -475,11 +503,9 @@ __device__ __forceinline__ void stage_attn(const Params& P, const Tile& T, Slot&
     const int flat = j * kThreads + t;
     const bool isv = flat >= KCH;
     const int f = isv ? flat - KCH : flat;
-    const int pos = start + f / CPP, dc = f % CPP;
-    if (pos < P.cap)
-      s.c[j] = ld_nt((isv ? P.vc : P.kc) + ((slice + pos) * kHeadDim) * sizeof(WT) + (size_t)dc * 16);
-    else
-      s.c[j] = u32x4{0u, 0u, 0u, 0u};
+    const int pos = min(start + f / CPP, P.cap - 1);  // positions past the capacity are never used
+    const int dc = f % CPP;
+    s.c[j] = ld_nt((isv ? P.vc : P.kc) + ((slice + pos) * kHeadDim) * sizeof(WT) + (size_t)dc * 16);
   }
   // Define the whole slot on every path: with entries left undefined here the
   // optimiser can no longer keep the slot in registers and spills it to
@@ -499,12 +525,11 @@ __device__ __forceinline__ void attn_tile(const Params& P, const Tile& T, const 
   constexpr int CPP = kHeadDim * sizeof(WT) / 16, KCH = kAttnChunk * CPP, EPC = WT_<WT>::EPC;
   constexpr int PITCH = WT_<WT>::PITCH;
   const int t = wpk_tid(), lane = t & 63, wave = t >> 6;
-  const LayerBufs& lb = P.layers[T.layer];
   const int32_t p = ld_sc1(&P.seq_len[T.b]);
   const int n = p < 0 ? 0 : min(p + 1, P.cap);
   const int start = T.c * kAttnChunk;
   const int cnt = max(0, min(kAttnChunk, n - start));
-  float* out = lb.part + ((((size_t)T.b * P.Hkv + T.g) * P.nch + T.c) * P.G) * (P.D + 2);
+  float* out = act(P, T.layer, P.off_part) + ((((size_t)T.b * P.Hkv + T.g) * P.nch + T.c) * P.G) * (P.D + 2);
   if (cnt == 0) {
     if (wave < P.G) {
       float* o = out + wave * (P.D + 2);
@@ -535,7 +560,7 @@ __device__ __forceinline__ void attn_tile(const Params& P, const Tile& T, const 
   }
   // queries of the group (written by this step's QKV tiles)
   if (wave < P.G)
-    sm.qs[wave][lane] = ld_sc1(lb.q + (size_t)T.b * P.Hq * P.D + (size_t)(T.g * P.G + wave) * P.D + lane);
+    sm.qs[wave][lane] = ld_sc1(act(P, T.layer, P.off_q) + (size_t)T.b * P.Hq * P.D + (size_t)(T.g * P.G + wave) * P.D + lane);
   __syncthreads();
   // position p was appended by this step's QKV tiles after the chunk was staged
   if (p >= start && p < start + kAttnChunk && p < P.cap && t < 2 * kHeadDim) {
@@ -581,12 +606,11 @@ template <typename WT>
 __device__ __forceinline__ void combine_tile(const Params& P, const Tile& T) {
   const int t = wpk_tid(), lane = t & 63, wave = t >> 6;
   if (wave >= P.G) return;
-  const LayerBufs& lb = P.layers[T.layer];
   const int32_t p = ld_sc1(&P.seq_len[T.b]);
   const int n = p < 0 ? 0 : min(p + 1, P.cap);
   const int nact = (n + kAttnChunk - 1) / kAttnChunk;
-  float* dst = lb.attn + (size_t)T.b * P.Hq * P.D + (size_t)(T.g * P.G + wave) * P.D;
-  const float* part = lb.part + (((size_t)T.b * P.Hkv + T.g) * P.nch * P.G + wave) * (P.D + 2);
+  float* dst = act(P, T.layer, P.off_attn) + (size_t)T.b * P.Hq * P.D + (size_t)(T.g * P.G + wave) * P.D;
+  const float* part = act(P, T.layer, P.off_part) + (((size_t)T.b * P.Hkv + T.g) * P.nch * P.G + wave) * (P.D + 2);
   const size_t stride = (size_t)P.G * (P.D + 2);
   if (nact == 0) {
     st_sc1(dst + lane, 0.f);
@@ -626,12 +650,12 @@ __device__ __forceinline__ void argmax_tile(const Params& P) {
 
 template <typename WT, int CPR_H, int CPR_F>
 __device__ __forceinline__ void stage(const Params& P, const Tile& T, Slot& s) {
-  const LayerBufs& lb = P.layers[T.layer];
+  const LayerW& lw = P.lw[T.layer];
   switch (T.type) {
-    case T_QKV: stage_gemv<CPR_H>(lb.w_qkv, lb.w_qkv, T.r0, T.r1, T.rs, T.rows, P.qkv_rows, s); break;
-    case T_OPROJ: stage_gemv<CPR_H>(lb.w_o, lb.w_o, T.r0, T.r1, T.rs, T.rows, P.H, s); break;
-    case T_GATEUP: stage_gemv<CPR_H>(lb.w_gate, lb.w_up, T.r0, T.r1, T.rs, T.rows, P.F, s); break;
-    case T_DOWN: stage_gemv<CPR_F>(lb.w_down, lb.w_down, T.r0, T.r1, T.rs, T.rows, P.H, s); break;
+    case T_QKV: stage_gemv<CPR_H>(lw.w_qkv, lw.w_qkv, T.r0, T.r1, T.rs, T.rows, P.qkv_rows, s); break;
+    case T_OPROJ: stage_gemv<CPR_H>(lw.w_o, lw.w_o, T.r0, T.r1, T.rs, T.rows, P.H, s); break;
+    case T_GATEUP: stage_gemv<CPR_H>(lw.w_gate, lw.w_up, T.r0, T.r1, T.rs, T.rows, P.F, s); break;
+    case T_DOWN: stage_gemv<CPR_F>(lw.w_down, lw.w_down, T.r0, T.r1, T.rs, T.rows, P.H, s); break;
     case T_LM: stage_gemv<CPR_H>(P.embed, P.embed, T.r0, T.r1, T.rs, T.rows, P.V, s); break;
     case T_ATTN: stage_attn<WT>(P, T, s); break;
     default: break;
@@ -657,7 +681,7 @@ __device__ __forceinline__ void run_tile(const Params& P, const Tile& T, const S
 // step.  Bounded: past the watchdog budget it latches WPK_E_TIMEOUT naming the
 // tile and raises the abort flag, which every other waiting worker also sees.
 __device__ __forceinline__ bool wait_group(const Params& P, const Tile& T, uint32_t epoch, int32_t* delta) {
-  const Group G = P.groups[T.wait];
+  const Group G = cload(P.groups, T.wait);
   const uint32_t target = (epoch + 1u) * (uint32_t)G.producers;
   const int lane = wpk_tid() & 63;
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
@@ -692,15 +716,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const uint32_t epoch = ld_sc1(&P.ctl[CTL_EPOCH]);
   const bool dead = ld_sc1(&P.ctl[CTL_STATUS]) != 0u;
   const int q = w % P.n_queues;
-  const int qb = P.queue_off[q], qn = P.queue_off[q + 1] - qb;
+  const int qb = cload(P.queue_off, q), qn = cload(P.queue_off, q + 1) - qb;
   uint32_t* head = P.heads + (size_t)q * kLine;
   if (t == 0) sm.first = dead ? qn : (int)atomic_add(head, 1u);
   __syncthreads();
-  int ci = sm.first;
+  int ci = __builtin_amdgcn_readfirstlane(sm.first);
   int parity = 0;
   while (ci < qn) {
-    const int id = __builtin_amdgcn_readfirstlane(P.queue[qb + ci]);
-    const Tile T = P.tiles[id];
+    const int id = cload(P.queue, qb + ci);
+    const Tile T = cload(P.tiles, id);
     Slot s;
     if (P.prefetch) stage<WT, CPR_H, CPR_F>(P, T, s);
     if (wave == 0) {
@@ -739,11 +763,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         *(uint64_t*)(rec + 6) = t_end;
       }
       if (T.signal >= 0 && id != P.drop_tile) {
-        const Group G = P.groups[T.signal];
+        const Group G = cload(P.groups, T.signal);
         atomic_add(&P.counters[(size_t)(G.shard0 + T.shard) * kLine], 1u);
       }
     }
-    ci = sm.next[parity];
+    ci = __builtin_amdgcn_readfirstlane(sm.next[parity]);
     parity ^= 1;
   }
   // leave the step; the last worker out rewinds the queues and advances the epoch
@@ -765,7 +789,7 @@ template <typename WT, int CPR_H, int CPR_F>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void phase_kernel(Params P, int first) {
   __shared__ Smem<WT> sm;
   const int id = first + (int)blockIdx.x;
-  const Tile T = P.tiles[id];
+  const Tile T = cload(P.tiles, id);
   Slot s;
   stage<WT, CPR_H, CPR_F>(P, T, s);
   run_tile<WT, CPR_H, CPR_F>(P, T, s, sm);

@@ -220,6 +220,45 @@ __global__ __launch_bounds__(64) void k_mp(unsigned* flags, unsigned* data, int 
   if (!producer && pair == 0 && lane == 0) errs[2] = t1 - t0;
 }
 
+// ---------------------------------------------------------------------------
+// 5. latency of one dependent access, by cache policy: lane 0 of one block
+// follows a pointer chain idx = p[idx] (stride 4 KiB + 64 B within `words`
+// words) `iters` times with buffer loads of cache policy `aux` (0 plain,
+// 1 sc0, 16 sc1, 17 sc0|sc1, 2 nt); mode 1: each step is instead a
+// device-scope fetch-add with return; mode 2: an sc1 store followed by a wait
+// for its completion.  out[0] = ticks, out[1] = final index (keeps the chain).
+// ---------------------------------------------------------------------------
+template <int AUX>
+__device__ __forceinline__ uint32_t chase(__amdgpu_buffer_rsrc_t r, uint32_t idx) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, idx * 4, 0, AUX);
+}
+__global__ void k_latency(uint32_t* p, uint32_t words, int iters, int aux, int mode, unsigned long long* out) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)p, 0, words * 4, 0x00020000);
+  uint32_t idx = 0;
+  const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+  for (int i = 0; i < iters; ++i) {
+    if (mode == 1) {
+      idx = __hip_atomic_fetch_add(p + idx, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) % words;
+    } else if (mode == 2) {
+      __hip_atomic_store(p + (words - 1 - (i & 1023)), (uint32_t)i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_s_waitcnt(0);
+    } else {
+      switch (aux) {
+        case 0: idx = chase<0>(r, idx); break;
+        case 1: idx = chase<1>(r, idx); break;
+        case 16: idx = chase<16>(r, idx); break;
+        case 17: idx = chase<17>(r, idx); break;
+        default: idx = chase<2>(r, idx); break;
+      }
+      idx %= words;
+    }
+  }
+  const unsigned long long t1 = __builtin_amdgcn_s_memrealtime();
+  out[0] = t1 - t0;
+  out[1] = idx;
+}
+
 static double time_ms(hipEvent_t a, hipEvent_t b) {
   float ms = 0;
   CHECK(hipEventElapsedTime(&ms, a, b));
@@ -346,6 +385,36 @@ int main(int argc, char** argv) {
     }
     CHECK(hipFree(mpdata));
     CHECK(hipFree(errs));
+  }
+
+  // ---- 5. access latency by cache policy ----
+  if (which == "all" || which == "latency") {
+    unsigned long long* lo = nullptr;
+    CHECK(hipMalloc(&lo, 2 * sizeof(unsigned long long)));
+    for (uint32_t words : {1u << 18, 1u << 28}) {  // 1 MiB (cache resident), 1 GiB (HBM)
+      std::vector<uint32_t> chain(words);
+      const uint32_t stride = 1040;  // 4 KiB + 64 B in words
+      for (uint32_t i = 0; i < words; ++i) chain[i] = (uint32_t)(((uint64_t)i + stride) % words);
+      uint32_t* d = reinterpret_cast<uint32_t*>(src);  // reuse the 4 GiB read buffer
+      CHECK(hipMemcpy(d, chain.data(), (size_t)words * 4, hipMemcpyHostToDevice));
+      for (int mode = 0; mode < 3; ++mode) {
+        for (int aux : {0, 1, 16, 17, 2}) {
+          if (mode != 0 && aux != 0) continue;
+          const int iters = 2000;
+          hipLaunchKernelGGL(k_latency, dim3(1), dim3(64), 0, 0, d, words, iters, aux, mode, lo);  // warm
+          hipLaunchKernelGGL(k_latency, dim3(1), dim3(64), 0, 0, d, words, iters, aux, mode, lo);
+          CHECK(hipDeviceSynchronize());
+          CHECK(hipGetLastError());
+          unsigned long long h[2];
+          CHECK(hipMemcpy(h, lo, sizeof(h), hipMemcpyDeviceToHost));
+          printf("{\"bench\": \"latency\", \"bytes\": %llu, \"mode\": \"%s\", \"aux\": %d, \"ns\": %.1f}\n",
+                 (unsigned long long)words * 4, mode == 0 ? "load" : (mode == 1 ? "atomic_add_ret" : "sc1_store_wait"),
+                 aux, h[0] * 10.0 / iters);
+          fflush(stdout);
+        }
+      }
+    }
+    CHECK(hipFree(lo));
   }
 
   CHECK(hipFree(xvec));

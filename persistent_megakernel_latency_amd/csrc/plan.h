@@ -57,6 +57,7 @@ constexpr int kMaxGroupHeads = 4;                     // q heads per kv head
 constexpr int kArgmaxShards = 16;
 constexpr int kMaxShards = 16;
 constexpr int kMaxBatch = 4;
+constexpr int kMaxLayers = 32;
 
 // Control block: word offsets, each field on its own 256-byte line.
 enum : int32_t {
@@ -85,6 +86,18 @@ struct LayerBufs {
   float* h;           // [B][F] SwiGLU output
 };
 
+// Per-layer weights as the kernels see them: kept inside the kernel arguments
+// so that a tile's base pointers are scalar loads from constant memory.
+struct LayerW {
+  const void* w_qkv;
+  const void* w_o;
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+  const float* attn_norm;
+  const float* mlp_norm;
+};
+
 // Everything a worker needs, passed by value to the kernel.
 struct Params {
   int32_t L, H, Hq, Hkv, D, F, V, B, cap, nch, G, qkv_rows;
@@ -92,7 +105,12 @@ struct Params {
   float eps, attn_scale;
   const void* embed;
   const float* final_norm;
-  const LayerBufs* layers;
+  const LayerBufs* layers;  // host executors: per-layer pointers in host memory
+  // device kernels: activations of layer l at act + l * act_layer + off_*
+  float* act;
+  int64_t act_layer;
+  int32_t off_x_mid, off_x_out, off_q, off_part, off_attn, off_h;
+  LayerW lw[kMaxLayers];
   const float* rope_cos;  // [cap][D/2]
   const float* rope_sin;  // [cap][D/2]
   int32_t* tokens;

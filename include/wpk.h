@@ -155,6 +155,25 @@ typedef struct wpk_log_rec {
   int64_t t_start;      /* s_memrealtime (100 MHz) after the wait was satisfied */
   int64_t t_end;        /* s_memrealtime before the tile published */
 } wpk_log_rec;
+/* Copies the n_tiles tile records.  On a device plan, when `bytes` holds
+ * 3 * n_tiles + max_workers records, the rest follows in two parts:
+ *  - max_workers worker records (slot w = workgroup w; only the first
+ *    `workers` are written): exec_count = the HW_ID hardware register (wave,
+ *    SIMD, CU, shader engine), wait_delta = the XCC_ID register, worker = w,
+ *    claim = 0, t_start / t_end = s_memrealtime at kernel entry / before the
+ *    exit count;
+ *  - n_tiles timing records (wpk_tile_timing, 64 bytes each, by tile id).
+ * All times are s_memrealtime ticks (100 MHz); a logged step also waits for
+ * each slot's loads before its arithmetic, so it runs slightly slower. */
+typedef struct wpk_tile_timing {
+  int64_t t_claim;         /* control wave took the tile (before waiting on its group) */
+  int64_t t_inputs;        /* inputs staged in LDS (last batch row) */
+  int64_t t_slot_ready;    /* the last compute wave had its staged weights (last batch row) */
+  int64_t t_compute_done;  /* the last compute wave finished its arithmetic */
+  int64_t t_partials;      /* all partial sums ready: the control wave passed barrier B */
+  int64_t t_end;           /* epilogue stores complete, before the publish */
+  int64_t reserved[2];
+} wpk_tile_timing;
 int32_t wpk_get_log(wpk_plan* plan, void* host_dst, size_t bytes);
 
 /* Shape of the built DAG. */

@@ -421,4 +421,29 @@ std::string validate_dag(const Shape& s, const Dag& d) {
   return "";
 }
 
+std::string check_device_geometry(const Shape& s, const Dag& d) {
+  // byte offsets inside one matrix or one (layer, sequence, kv head) cache
+  // slice are 32-bit and bounded by the buffer resource's 2^31 - 1 records
+  const int64_t lim = 0x7FFFFFFF;
+  const int64_t rb_h = (int64_t)s.cpr_h * 16, rb_f = (int64_t)s.cpr_f * 16;
+  if ((int64_t)s.V * rb_h > lim || (int64_t)s.qkv_rows * rb_h > lim || (int64_t)s.F * rb_h > lim ||
+      (int64_t)s.H * rb_f > lim || (int64_t)s.cap * s.D * s.elt > lim)
+    return "a weight matrix or a KV cache slice exceeds 2 GiB";
+  // a 4 KiB slice of a tile holds 256 / cpr whole rows when a row is shorter
+  // than a slice; segments, tiles and matrices must break on whole slices
+  for (const Tile& t : d.tiles) {
+    if (t.type != T_QKV && t.type != T_OPROJ && t.type != T_GATEUP && t.type != T_DOWN && t.type != T_LM)
+      continue;
+    const int32_t cpr = t.type == T_DOWN ? s.cpr_f : s.cpr_h;
+    const int32_t sr = cpr >= kThreads ? 1 : kThreads / cpr;
+    if (t.rows < sr || t.rows % sr || t.rs % sr || t.r0 % sr || t.r1 % sr)
+      return "tile_bytes too small for whole 4 KiB row slices";
+  }
+  const int32_t sr_h = s.cpr_h >= kThreads ? 1 : kThreads / s.cpr_h;
+  const int32_t sr_f = s.cpr_f >= kThreads ? 1 : kThreads / s.cpr_f;
+  if (s.V % sr_h || s.qkv_rows % sr_h || s.F % sr_h || s.H % sr_h || s.H % sr_f)
+    return "vocab and projection row counts must fill whole 4 KiB slices";
+  return "";
+}
+
 }  // namespace wpk

@@ -47,6 +47,10 @@ Dag build_dag(const Shape& s);
 // the producers of the group it waits on.  Empty string when valid.
 std::string validate_dag(const Shape& s, const Dag& d);
 
+// Extra constraints of the gfx950 kernels: 32-bit offsets within a matrix or
+// a KV cache slice, and GEMV tiles made of whole 4 KiB row slices.
+std::string check_device_geometry(const Shape& s, const Dag& d);
+
 // Weight bytes one step streams (matrices once each, norm gains once each).
 int64_t step_weight_bytes(const Shape& s);
 

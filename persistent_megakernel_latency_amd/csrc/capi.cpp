@@ -19,6 +19,7 @@
 
 extern "C" int wpk_dev_kernels(int dtype, int cpr_h, int cpr_f, const void** mk, const void** mk_log,
                                const void** phase);
+extern "C" int wpk_dev_block_threads();
 
 using namespace wpk;
 
@@ -39,7 +40,7 @@ struct Layout {
   int64_t ctl, heads, counters, argmax, tiles, groups, queue, queue_off, layers, rope_cos, rope_sin, act, log, total;
 };
 
-Layout layout(const Shape& s, const Dag& d) {
+Layout layout(const Shape& s, const Dag& d, int32_t max_workers) {
   Layout L{};
   int64_t at = 0;
   auto take = [&](int64_t bytes) {
@@ -60,7 +61,8 @@ Layout layout(const Shape& s, const Dag& d) {
   L.rope_cos = take((int64_t)s.cap * (s.D / 2) * 4);
   L.rope_sin = take((int64_t)s.cap * (s.D / 2) * 4);
   L.act = take(act_layout(s).total * 4);
-  L.log = take((int64_t)d.tiles.size() * sizeof(wpk_log_rec));
+  // tile records, worker records, tile timings (two record sizes each)
+  L.log = take((3 * (int64_t)d.tiles.size() + max_workers) * sizeof(wpk_log_rec));
   L.total = at;
   return L;
 }
@@ -134,6 +136,8 @@ wpk_plan* build_device(const wpk_model_desc* desc, int32_t batch, int32_t ctx_le
   p->dag = build_dag(s);
   why = validate_dag(s, p->dag);
   if (!why.empty()) return fail("invalid DAG: " + why);
+  why = check_device_geometry(s, p->dag);
+  if (!why.empty()) return fail(why);
   for (const Tile& t : p->dag.tiles) p->built_wait.push_back(t.wait);
   p->weight_bytes = step_weight_bytes(s);
   p->k_mega = mk;
@@ -141,9 +145,10 @@ wpk_plan* build_device(const wpk_model_desc* desc, int32_t batch, int32_t ctx_le
   p->k_phase = phase;
 
   int per_cu = 0, per_cu_log = 0;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mk, kThreads, 0);
+  const int block = wpk_dev_block_threads();
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mk, block, 0);
   if (e != hipSuccess) return fail(hip_msg("occupancy query", e));
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_log, mk_log, kThreads, 0);
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_log, mk_log, block, 0);
   if (e != hipSuccess) return fail(hip_msg("occupancy query", e));
   per_cu = std::min(per_cu, per_cu_log);
   p->max_workers = per_cu * p->n_cu;
@@ -153,7 +158,7 @@ wpk_plan* build_device(const wpk_model_desc* desc, int32_t batch, int32_t ctx_le
     return nullptr;
   }
 
-  const Layout L = layout(s, p->dag);
+  const Layout L = layout(s, p->dag, p->max_workers);
   e = hipMalloc((void**)&p->d_ws, L.total);
   if (e != hipSuccess) return fail(hip_msg("hipMalloc workspace", e));
   p->ws_bytes = L.total;
@@ -212,6 +217,7 @@ wpk_plan* build_device(const wpk_model_desc* desc, int32_t batch, int32_t ctx_le
   P.ctl = (uint32_t*)(w + L.ctl);
   P.argmax = (unsigned long long*)(w + L.argmax);
   P.log = (int32_t*)(w + L.log);
+  P.log_workers = p->max_workers;
   P.log_on = 0;
   P.prefetch = 1;
   P.drop_tile = -1;
@@ -251,7 +257,7 @@ int32_t capture_baseline(wpk_plan* p) {
   for (const auto& ph : p->dag.phases) {
     int32_t first = ph.first;
     void* args[] = {(void*)&p->P, (void*)&first};
-    e = hipLaunchKernel(p->k_phase, dim3(ph.second), dim3(kThreads), args, 0, cs);
+    e = hipLaunchKernel(p->k_phase, dim3(ph.second), dim3(wpk_dev_block_threads()), args, 0, cs);
     if (e != hipSuccess) break;
   }
   hipGraph_t g = nullptr;
@@ -317,11 +323,12 @@ int32_t wpk_step(wpk_plan* p, int32_t* tokens, wpk_kv* kv, void* logits, wpk_str
   }
   P.log_on = p->log_on;
   if (p->log_on) {
-    e = hipMemsetAsync(P.log, 0, p->dag.tiles.size() * sizeof(wpk_log_rec), st);
+    e = hipMemsetAsync(P.log, 0, (3 * p->dag.tiles.size() + p->max_workers) * sizeof(wpk_log_rec), st);
     if (e != hipSuccess) return plan_fail(p, WPK_E_HIP, hip_msg("hipMemsetAsync log", e));
   }
   void* args[] = {(void*)&P};
-  e = hipLaunchCooperativeKernel(p->log_on ? p->k_mega_log : p->k_mega, dim3(p->workers), dim3(kThreads), args, 0, st);
+  e = hipLaunchCooperativeKernel(p->log_on ? p->k_mega_log : p->k_mega, dim3(p->workers),
+                                 dim3(wpk_dev_block_threads()), args, 0, st);
   if (e != hipSuccess) return plan_fail(p, WPK_E_HIP, hip_msg("hipLaunchCooperativeKernel", e));
   return WPK_OK;
 }
@@ -435,7 +442,9 @@ int32_t wpk_get_log(wpk_plan* p, void* dst, size_t bytes) {
     std::memcpy(dst, p->log.data(), need);
     return WPK_OK;
   }
-  hipError_t e = hipMemcpy(dst, p->P.log, need, hipMemcpyDeviceToHost);
+  // with room for them, the worker record slots and the tile timings follow
+  const size_t full = (3 * p->dag.tiles.size() + p->max_workers) * sizeof(wpk_log_rec);
+  hipError_t e = hipMemcpy(dst, p->P.log, bytes >= full ? full : need, hipMemcpyDeviceToHost);
   if (e != hipSuccess) return plan_fail(p, WPK_E_HIP, hip_msg("log read", e));
   return WPK_OK;
 }

@@ -3,9 +3,9 @@
 // Structure (what the pages describe, re-designed for MI355X):
 //  * A megakernel owns the multi-operation program and the coordination between
 //    operations ("Why real-time inference wants a megakernel", "The unit of
-//    execution"); the host launches once per step and the GPU walks the schedule:
-//    wait for the dependencies, run, signal the consumers (section "What the
-//    megakernel changes").
+//    execution"); the host launches once per step and the GPU walks the
+//    schedule: wait for the dependencies, run, signal the consumers (section
+//    "What the megakernel changes").
 //  * Workers are resident workgroups, several per CU, all co-resident
 //    (cooperative launch), that claim tiles from device-side queues in a
 //    topological order.  Each worker has one staging slot: the claimed tile's
@@ -17,20 +17,28 @@
 //  * Dependencies are counter groups (tile-to-tile tensor edges, Table I), not
 //    operator barriers.
 //
-// gfx950 specifics, measured with microbench.hip on an MI355X:
+// A worker is one control wave plus four compute waves.  On CDNA a wave can
+// only consume its loads in issue order (one vector-memory counter), so a wave
+// that keeps 64 KiB of weights in flight cannot also take a quick round trip to
+// a counter or an activation.  The roles are therefore split: the compute
+// waves only stream weights and multiply (they issue the next tile's weight
+// loads the moment they finish the current tile), while the control wave
+// claims tiles, polls counters, stages activations into LDS, runs the
+// epilogues, stores results and publishes.  The two sides meet at two
+// workgroup barriers per tile (A: inputs staged; B: partial sums ready).
+//
+// Synchronisation, measured with microbench.hip on an MI355X:
 //  * An agent-scope acquire fence (L2 invalidate) per 64 KiB tile cut streaming
 //    reads from 6.2 to 2.2 TB/s and a release fence (L2 write-back) to 1.2 TB/s,
-//    because each of the 8 XCDs has its own L2.  The kernel therefore uses no
-//    fences in its hot path: tile outputs are written with device-coherent
-//    (sc1, write-through) stores and a wait for their completion, counters are
-//    bumped with relaxed device-scope atomics (performed past the L2s), and
-//    consumers read counters and activations with device-coherent (sc1) loads.
-//    A cross-XCD message-passing test of exactly this protocol saw no stale
-//    word in 2000 x 8 rounds; plain stores in its place were stale.
+//    because each of the 8 XCDs has its own L2.  No fence is used in the hot
+//    path: the control wave writes tile outputs with device-coherent (sc1,
+//    write-through) stores, waits for their completion, then bumps the counter
+//    with a relaxed device-scope atomic (performed past the L2s); consumers
+//    read counters and activations with device-coherent (sc1) loads.  A
+//    cross-XCD message-passing test of exactly this protocol saw no stale word
+//    in 2000 x 8 rounds; plain stores in its place were stale.
 //  * One address takes ~88 M atomics/s, so each counter group is spread over up
 //    to 16 shards and tiles are claimed from 8 queues.
-//  * Weights stream with 16-byte non-temporal loads, 16 per thread, so a worker
-//    keeps a whole 64 KiB tile in flight.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -41,30 +49,36 @@
 namespace wpk {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kBlock = kThreads + 64;  // one control wave + four compute waves
 
 struct Slot {
-  u32x4 c[kChunks];
+  u32x4 c[kChunks];  // the tile's weights (or K/V chunk)
+  u32x4 g[2];        // RMSNorm gains of this thread's columns (fp32 bits; 1.0 without a norm)
 };
 
 template <typename WT>
 struct WT_ {
-  static constexpr int EPC = 16 / sizeof(WT);   // elements per 16-byte chunk
+  static constexpr int EPC = 16 / sizeof(WT);              // elements per 16-byte chunk
   static constexpr int PITCH = sizeof(WT) == 2 ? 66 : 65;  // LDS row pitch of a K/V chunk (conflict-free)
 };
 
-template <typename WT>
+template <typename WT, int KMAX>
 struct Smem {
-  float red[kWaves][64];
-  float yrow[64];
-  float nrm[kWaves];
+  float xs[KMAX];                              // activation row of the current GEMV tile
+  float red[kWaves][64];                       // per compute wave partial row sums
+  float outs[kMaxGroupHeads][kHeadDim + 2];    // attention partial (m, l, o) per q head
   float qs[kMaxGroupHeads][kHeadDim];
   float ps[kMaxGroupHeads][kAttnChunk];
   WT ks[kAttnChunk * WT_<WT>::PITCH];
   WT vs[kAttnChunk * WT_<WT>::PITCH];
-  int next[2];
+  int pos[kMaxBatch];  // seq_len of each sequence at step start
+  int tok[kMaxBatch];  // input token of each sequence (validated)
+  int ids[2];          // claim index of the next tile, by iteration parity
+  uint64_t t_ready, t_done;  // logged steps: compute wave 1 saw its slot, finished its arithmetic
   int first;
-  int ok;
-  int delta;
+  int stop;
 };
 
 // The thread index, made opaque to the optimiser.  Inside the persistent tile
@@ -72,11 +86,11 @@ struct Smem {
 // arithmetic out of the loop and keep it all live, which multiplies the
 // register footprint of the merged kernel (the register-pressure cost of
 // megakernels the persistent-threads page discusses in section 4).
-__device__ __forceinline__ int wpk_tid() {
-  int t = (int)threadIdx.x;
-  asm volatile("" : "+v"(t));
-  return t;
+__device__ __forceinline__ int opaque(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
 }
+__device__ __forceinline__ int wpk_tid() { return opaque((int)threadIdx.x); }
 
 // ---- memory primitives ------------------------------------------------------------------
 
@@ -118,7 +132,7 @@ __device__ __forceinline__ u32x4 ld_sc1_x4(const float* base, int32_t float_off)
 
 // Read-only tables (tiles, groups, queues) through the constant address space:
 // uniform loads from it become scalar loads that do not count against the
-// vector-memory counter the weight stream uses.
+// vector-memory counter.
 template <class T>
 __device__ __forceinline__ T cload(const T* p, int i) {
   static_assert(sizeof(T) % 4 == 0, "table entries are whole 32-bit words");
@@ -154,7 +168,6 @@ __device__ __forceinline__ uint16_t to_bf16(float f) {
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
-// Elements of one 16-byte chunk as floats.
 template <typename WT>
 __device__ __forceinline__ void unpack(u32x4 c, float* o);
 template <>
@@ -168,12 +181,9 @@ __device__ __forceinline__ void unpack<float>(u32x4 c, float* o) {
 }
 
 template <typename WT>
-__device__ __forceinline__ float dot_chunk(u32x4 c, const float* x, float acc) {
-  float w[WT_<WT>::EPC];
-  unpack<WT>(c, w);
-#pragma unroll
-  for (int e = 0; e < WT_<WT>::EPC; ++e) acc = fmaf(w[e], x[e], acc);
-  return acc;
+__device__ __forceinline__ float elt(const WT* a, int i) {
+  if (sizeof(WT) == 2) return bf16_lo(((const uint16_t*)a)[i]);
+  return ((const float*)a)[i];
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -192,20 +202,6 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// Sum over all threads of the worker; every thread gets the result.
-template <typename WT>
-__device__ __forceinline__ float block_sum(float v, Smem<WT>& sm) {
-  v = wave_sum(v);
-  const int t = wpk_tid();
-  if ((t & 63) == 0) sm.nrm[t >> 6] = v;
-  __syncthreads();
-  float s = 0.f;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) s += sm.nrm[w];
-  __syncthreads();
-  return s;
-}
-
 // Reduce-scatter of N per-lane values over the 64 lanes of a wave: after it,
 // lane l holds the wave-wide sum of value index scatter_index<N>(l).
 template <int N>
@@ -216,8 +212,9 @@ __device__ __forceinline__ float wave_reduce_scatter(float (&v)[N], int lane) {
     const bool up = (lane & m) != 0;
 #pragma unroll
     for (int i = 0; i < n / 2; ++i) {
-      const float send = up ? v[i] : v[i + n / 2];
-      const float keep = up ? v[i + n / 2] : v[i];
+      const float lo = v[i], hi = v[i + n / 2];  // selects on values, not on an index
+      const float send = up ? lo : hi;
+      const float keep = up ? hi : lo;
       v[i] = keep + __shfl_xor(send, m);
     }
   }
@@ -246,128 +243,8 @@ __device__ __forceinline__ void latch_error(const Params& P, int32_t code, int32
   st_sc1(&P.ctl[CTL_ABORT], 1u);
 }
 
-// ---- GEMV tiles ----------------------------------------------------------------------------
-//
-// A GEMV tile is `rows` weight rows (two segments, so RoPE pairs (i, i+D/2) and
-// gate/up pairs land in one tile) of a matrix with K columns, CPR 16-byte
-// chunks per row.  Thread t owns chunk j*256 + t of the tile for j < 16, so
-// each of its 16 loads is one fully coalesced 4 KiB wavefront-set of the tile.
-
-template <int CPR>
-struct Geo {
-  static constexpr int LPR = CPR >= kThreads ? CPR / kThreads : 1;  // chunks of one row per thread
-  static constexpr int NV = kChunks / LPR;                          // rows a thread contributes to
-  static constexpr int ROWS = kThreads * kChunks / CPR;             // rows of a full tile
-  static constexpr int WPR = CPR >= kThreads ? kWaves : CPR / 64;   // waves sharing a row
-  static_assert(CPR >= 64 && ROWS <= 64, "unsupported row length");
-};
-
-template <int CPR>
-__device__ __forceinline__ void stage_gemv(const void* w0, const void* w1, int r0, int r1, int rs, int rows,
-                                           int limit, Slot& s) {
-  const int t = wpk_tid();
-#pragma unroll
-  for (int j = 0; j < kChunks; ++j) {
-    // Rows past the tile or the matrix are clamped to a valid row, so every
-    // load is unconditional; their (duplicate) sums are never stored.
-    const int flat = j * kThreads + t;
-    const int row = min(flat / CPR, rows - 1);
-    const int col = flat % CPR;
-    const bool seg1 = row >= rs;
-    const int mrow = min(seg1 ? r1 + (row - rs) : r0 + row, limit - 1);
-    const char* base = (const char*)(seg1 ? w1 : w0);
-    s.c[j] = ld_nt(base + (size_t)mrow * (CPR * 16) + (size_t)col * 16);
-  }
-}
-
-// This thread's activations for sequence b (the columns of its chunks), with
-// the RMSNorm prologue for the operators that have one.
-template <typename WT, int CPR>
-__device__ __forceinline__ void gemv_input(const Params& P, const Tile& T, int b, int tok,
-                                           float (&x)[Geo<CPR>::LPR * WT_<WT>::EPC], Smem<WT>& sm) {
-  constexpr int EPC = WT_<WT>::EPC, LPR = Geo<CPR>::LPR;
-  const int t = wpk_tid();
-  const LayerW& lw = P.lw[T.layer];
-  const float* src = nullptr;
-  const float* gain = nullptr;
-  int K = P.H;
-  switch (T.type) {
-    case T_QKV: src = x_in(P, T.layer); gain = lw.attn_norm; break;
-    case T_OPROJ: src = act(P, T.layer, P.off_attn); break;
-    case T_GATEUP: src = act(P, T.layer, P.off_x_mid); gain = lw.mlp_norm; break;
-    case T_DOWN: src = act(P, T.layer, P.off_h); K = P.F; break;
-    default: src = act(P, P.L - 1, P.off_x_out); gain = P.final_norm; break;
-  }
-#pragma unroll
-  for (int k = 0; k < LPR; ++k) {
-    const int col = CPR >= kThreads ? k * kThreads + t : t % CPR;
-    if (src == nullptr) {  // layer-0 input: the embedding row of the token (input conversion)
-      const u32x4 c = *(const u32x4*)((const char*)P.embed + ((size_t)tok * P.H * sizeof(WT)) + (size_t)col * 16);
-      unpack<WT>(c, &x[k * EPC]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < EPC; e += 4) {
-        const u32x4 c = ld_sc1_x4(src, b * K + col * EPC + e);
-        x[k * EPC + e + 0] = __uint_as_float(c.x);
-        x[k * EPC + e + 1] = __uint_as_float(c.y);
-        x[k * EPC + e + 2] = __uint_as_float(c.z);
-        x[k * EPC + e + 3] = __uint_as_float(c.w);
-      }
-    }
-  }
-  if (gain) {
-    float ss = 0.f;
-    if (CPR >= kThreads || t < CPR) {
-#pragma unroll
-      for (int i = 0; i < LPR * EPC; ++i) ss = fmaf(x[i], x[i], ss);
-    }
-    ss = block_sum(ss, sm);
-    const float inv = 1.0f / sqrtf(ss / (float)K + P.eps);
-#pragma unroll
-    for (int k = 0; k < LPR; ++k) {
-      const int col = CPR >= kThreads ? k * kThreads + t : t % CPR;
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) x[k * EPC + e] = x[k * EPC + e] * inv * gain[col * EPC + e];
-    }
-  }
-}
-
-// Row sums of the tile for the thread's activations, into sm.yrow[0 .. ROWS).
-template <typename WT, int CPR>
-__device__ __forceinline__ void gemv_rows(const Slot& s, const float (&x)[Geo<CPR>::LPR * WT_<WT>::EPC],
-                                          Smem<WT>& sm) {
-  using G = Geo<CPR>;
-  constexpr int EPC = WT_<WT>::EPC;
-  const int t = wpk_tid(), lane = t & 63, wave = t >> 6;
-  float acc[G::NV];
-#pragma unroll
-  for (int v = 0; v < G::NV; ++v) acc[v] = 0.f;
-#pragma unroll
-  for (int j = 0; j < kChunks; ++j) {
-    // Opaque copy: keeps the compiler from hoisting the unpacked (2x wider)
-    // weights out of the caller's batch loop, which would double the slot's
-    // register footprint.
-    u32x4 c = s.c[j];
-    asm volatile("" : "+v"(c));
-    acc[j / G::LPR] = dot_chunk<WT>(c, &x[(j % G::LPR) * EPC], acc[j / G::LPR]);
-  }
-  const float r = wave_reduce_scatter<G::NV>(acc, lane);
-  if (lane < G::NV) sm.red[wave][scatter_index<G::NV>(lane)] = r;
-  __syncthreads();
-  if (t < G::ROWS) {
-    float y = 0.f;
-    if (CPR >= kThreads) {
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) y += sm.red[w][t];
-    } else {
-      constexpr int S = kThreads / CPR;  // rows interleaved per value index
-      const int v = t / S, grp = t % S;
-#pragma unroll
-      for (int w = 0; w < G::WPR; ++w) y += sm.red[grp * G::WPR + w][v];
-    }
-    sm.yrow[t] = y;
-  }
-  __syncthreads();
+__device__ __forceinline__ bool is_gemv(int type) {
+  return type == T_QKV || type == T_OPROJ || type == T_GATEUP || type == T_DOWN || type == T_LM;
 }
 
 __device__ __forceinline__ unsigned long long pack_max(float v, int idx) {
@@ -376,178 +253,162 @@ __device__ __forceinline__ unsigned long long pack_max(float v, int idx) {
   return ((unsigned long long)u << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)idx);
 }
 
-template <typename WT, int CPR>
-__device__ __forceinline__ void gemv_tile(const Params& P, const Tile& T, const Slot& s, Smem<WT>& sm) {
-  using G = Geo<CPR>;
-  const int t = wpk_tid();
-  const int l = T.layer;
-  for (int b = 0; b < P.B; ++b) {
-    const int32_t p = ld_sc1(&P.seq_len[b]);
-    if (T.type == T_QKV && p < 0) continue;  // inactive slot: nothing to append
-    int tok = 0;
-    if (T.layer == 0 && (T.type == T_QKV || T.type == T_OPROJ)) {
-      tok = P.tokens[b];
-      if (tok < 0 || tok >= P.V) {
-        if (p >= 0 && t == 0) latch_error(P, WPK_E_TOKEN, T.id);
-        tok = 0;
-      }
-    }
-    float x[G::LPR * WT_<WT>::EPC];
-    gemv_input<WT, CPR>(P, T, b, tok, x, sm);
-    gemv_rows<WT, CPR>(s, x, sm);
-    const float* y = sm.yrow;
-    switch (T.type) {
-      case T_QKV: {
-        if (p >= P.cap) {
-          if (t == 0) latch_error(P, WPK_E_CTX_FULL, T.id);
-          break;
-        }
-        const int half = P.D / 2;
-        if (T.kind < 2) {
-          const int head = T.g;
-          const int base = T.kind == 0 ? head * P.D : (P.Hq + head) * P.D;
-          if (t < T.rs) {
-            const int dim = T.r0 + t - base;
-            const float cs = P.rope_cos[p * half + dim], sn = P.rope_sin[p * half + dim];
-            const float a = y[t], bb = y[T.rs + t];
-            const float ra = a * cs - bb * sn, rb = bb * cs + a * sn;
-            if (T.kind == 0) {
-              float* q = act(P, l, P.off_q) + (size_t)b * P.Hq * P.D + head * P.D;
-              st_sc1(q + dim, ra);
-              st_sc1(q + dim + half, rb);
-            } else {
-              const size_t at = ((((size_t)T.layer * P.B + b) * P.Hkv + head) * P.cap + p) * P.D;
-              WT* kc = (WT*)P.kc + at;
-              if (sizeof(WT) == 2) {
-                st_sc1((uint16_t*)kc + dim, to_bf16(ra));
-                st_sc1((uint16_t*)kc + dim + half, to_bf16(rb));
-              } else {
-                st_sc1((float*)kc + dim, ra);
-                st_sc1((float*)kc + dim + half, rb);
-              }
-            }
-          }
-        } else if (t < T.rows) {
-          const int base = (P.Hq + P.Hkv + T.g) * P.D;
-          const int mrow = t < T.rs ? T.r0 + t : T.r1 + (t - T.rs);
-          const size_t at = ((((size_t)T.layer * P.B + b) * P.Hkv + T.g) * P.cap + p) * P.D + (mrow - base);
-          if (sizeof(WT) == 2) st_sc1((uint16_t*)P.vc + at, to_bf16(y[t]));
-          else st_sc1((float*)P.vc + at, y[t]);
-        }
-        break;
-      }
-      case T_OPROJ:
-        if (t < T.rows && T.r0 + t < P.H) {
-          const int row = T.r0 + t;
-          float xin;
-          if (T.layer == 0) {
-            const WT* e = (const WT*)P.embed + (size_t)tok * P.H + row;
-            xin = sizeof(WT) == 2 ? bf16_lo(*(const uint16_t*)e) : *(const float*)e;
-          } else {
-            xin = ld_sc1(x_in(P, l) + (size_t)b * P.H + row);
-          }
-          st_sc1(act(P, l, P.off_x_mid) + (size_t)b * P.H + row, xin + y[t]);
-        }
-        break;
-      case T_GATEUP:
-        if (t < T.rs && T.r0 + t < P.F) {
-          const float g = y[t], u = y[T.rs + t];
-          st_sc1(act(P, l, P.off_h) + (size_t)b * P.F + T.r0 + t, g / (1.0f + __expf(-g)) * u);
-        }
-        break;
-      case T_DOWN:
-        if (t < T.rows && T.r0 + t < P.H) {
-          const int row = T.r0 + t;
-          st_sc1(act(P, l, P.off_x_out) + (size_t)b * P.H + row, ld_sc1(act(P, l, P.off_x_mid) + (size_t)b * P.H + row) + y[t]);
-        }
-        break;
-      case T_LM:
-        if (t < 64) {
-          const int row = T.r0 + t;
-          unsigned long long key = 0;
-          if (t < T.rows && row < P.V) {
-            P.logits[(size_t)b * P.V + row] = y[t];
-            key = pack_max(y[t], row);
-          }
-#pragma unroll
-          for (int m = 1; m < 64; m <<= 1) {
-            const unsigned long long o = __shfl_xor(key, m);
-            key = o > key ? o : key;
-          }
-          if (t == 0)
-            __hip_atomic_fetch_max(&P.argmax[b * kArgmaxShards + T.id % kArgmaxShards], key, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-        }
-        break;
-    }
-    __syncthreads();
-  }
-}
-
-// ---- attention ---------------------------------------------------------------------------
+// ---- GEMV geometry ------------------------------------------------------------------------
 //
-// Split-KV decode attention (the chunked KV of FlashInfer's persistent kernel and
-// the partial + reduction tasks of ThunderMLA, "persistent-threads-megakernels"
-// section 6): one tile handles 64 cached positions of one (sequence, kv head)
-// for all the q heads of its group; the K/V chunk is the tile's staged "weights".
+// A GEMV tile is `rows` weight rows (two segments, so RoPE pairs (i, i+D/2) and
+// gate/up pairs land in one tile) of a matrix with K columns, CPR 16-byte
+// chunks per row.  Compute thread tc owns chunk j*256 + tc of the tile for
+// j < 16, so each of its 16 loads is one fully coalesced 4 KiB piece.
 
-template <typename WT>
-__device__ __forceinline__ void stage_attn(const Params& P, const Tile& T, Slot& s) {
-  constexpr int CPP = kHeadDim * sizeof(WT) / 16;  // chunks per position
-  constexpr int KCH = kAttnChunk * CPP;            // chunks of K (and of V) per tile
-  const int t = wpk_tid();
-  const size_t slice = (((size_t)T.layer * P.B + T.b) * P.Hkv + T.g) * P.cap;
-  const int start = T.c * kAttnChunk;
-#pragma unroll
-  for (int j = 0; j < 2 * KCH / kThreads; ++j) {
-    const int flat = j * kThreads + t;
-    const bool isv = flat >= KCH;
-    const int f = isv ? flat - KCH : flat;
-    const int pos = min(start + f / CPP, P.cap - 1);  // positions past the capacity are never used
-    const int dc = f % CPP;
-    s.c[j] = ld_nt((isv ? P.vc : P.kc) + ((slice + pos) * kHeadDim) * sizeof(WT) + (size_t)dc * 16);
+template <int CPR>
+struct Geo {
+  static constexpr int LPR = CPR >= kThreads ? CPR / kThreads : 1;  // chunks of one row per thread
+  static constexpr int NV = kChunks / LPR;                          // rows a thread contributes to
+  static constexpr int ROWS = kThreads * kChunks / CPR;             // rows of a full tile
+  static constexpr int WPR = CPR >= kThreads ? kWaves : CPR / 64;   // compute waves sharing a row
+  static_assert(CPR >= 64 && ROWS <= 64, "unsupported row length");
+};
+
+// ============================ compute waves ===================================================
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)p, 0, 0x7FFFFFFF, 0x00020000);
+}
+
+// Stages the tile's weights into the slot: chunk j of thread tc is 16 bytes at
+// lane offset tc*16 into slice j, a 4 KiB run of memory at a wave-uniform
+// offset.  One load site serves every tile type, so the slot is never copied
+// between code paths; the per-type work is scalar.  Each load is one buffer
+// load (resource and slice offset in scalar registers, one lane offset):
+//  * GEMV: slice j is row (j / SPR) * SR of the tile (SR = 256 / CPR rows per
+//    slice for short rows, SPR = CPR / 256 slices per row for long ones); the
+//    device plan keeps segment boundaries and tile sizes on whole slices, so a
+//    slice never straddles the two row segments.  Slices past a short tile or
+//    past the matrix re-read its last valid slice (their sums are never stored).
+//  * ATTN: slices of K then V of the tile's KV chunk; lanes past the cache
+//    capacity read its last chunk (those positions are never used).
+//  * the remaining slots of an attention tile and every slot of a combine or
+//    argmax tile read one 16-byte word (no HBM traffic; the value is unused).
+template <typename WT, int CPR_H, int CPR_F>
+__device__ __forceinline__ void stage(const Params& P, const Tile& T, Slot& s, uint32_t voff) {
+  constexpr int RB = kHeadDim * (int)sizeof(WT);  // K/V bytes per position
+  constexpr int PPS = 4096 / RB;                  // positions per slice
+  constexpr int NS = kAttnChunk / PPS;            // slices of K (and of V)
+  const LayerW& lw = P.lw[T.layer];
+  const int ty = T.type;
+  const bool gemv = is_gemv(ty), attn = ty == T_ATTN;
+  const void* w0 = P.embed;
+  const void* w1 = P.embed;
+  int limit = P.V, cpr = CPR_H;
+  switch (ty) {
+    case T_QKV: w0 = w1 = lw.w_qkv; limit = P.qkv_rows; break;
+    case T_OPROJ: w0 = w1 = lw.w_o; limit = P.H; break;
+    case T_GATEUP: w0 = lw.w_gate; w1 = lw.w_up; limit = P.F; break;
+    case T_DOWN: w0 = w1 = lw.w_down; limit = P.H; cpr = CPR_F; break;
+    case T_ATTN: {
+      const size_t sl = ((((size_t)T.layer * P.B + T.b) * P.Hkv + T.g) * P.cap) * RB;
+      w0 = P.kc + sl;
+      w1 = P.vc + sl;
+      break;
+    }
+    default: break;
   }
-  // Define the whole slot on every path: with entries left undefined here the
-  // optimiser can no longer keep the slot in registers and spills it to
-  // scratch, serialising the weight loads.
+  // RMSNorm gains of the columns this thread multiplies (loaded ahead of the
+  // weights, so waiting for them does not wait for the weights)
+  static_assert(CPR_H <= kThreads, "gains in the slot cover one chunk per thread");
+  constexpr int EPC = WT_<WT>::EPC;
+  const float* gain = ty == T_QKV ? lw.attn_norm : ty == T_GATEUP ? lw.mlp_norm : ty == T_LM ? P.final_norm : nullptr;
+  if (gain) {
+    const uint32_t goff = (voff / 16u % (uint32_t)CPR_H) * (EPC * 4);
+    const __amdgpu_buffer_rsrc_t rg = rsrc(gain);
+    s.g[0] = __builtin_amdgcn_raw_buffer_load_b128(rg, goff, 0, 0);
+    s.g[1] = EPC == 8 ? __builtin_amdgcn_raw_buffer_load_b128(rg, goff + 16u, 0, 0) : s.g[0];
+  } else {
+    s.g[0] = s.g[1] = u32x4{0x3f800000u, 0x3f800000u, 0x3f800000u, 0x3f800000u};
+  }
+  const __amdgpu_buffer_rsrc_t rs0 = rsrc(w0), rs1 = rsrc(w1);
+  const int sh_spr = cpr >= kThreads ? __builtin_ctz(cpr / kThreads) : 0;
+  const int sr = cpr >= kThreads ? 1 : kThreads / cpr;
+  const int rowb = cpr * 16;
 #pragma unroll
-  for (int j = 2 * KCH / kThreads; j < kChunks; ++j) s.c[j] = u32x4{0u, 0u, 0u, 0u};
+  for (int j = 0; j < kChunks; ++j) {
+    // GEMV slice
+    const int row = min((j >> sh_spr) * sr, T.rows - sr);
+    const bool seg1 = row >= T.rs;
+    const int mrow = min(seg1 ? T.r1 + (row - T.rs) : T.r0 + row, limit - sr);
+    const int g_off = mrow * rowb + (j & ((1 << sh_spr) - 1)) * 4096;
+    // attention slice
+    const int p0 = min(T.c * kAttnChunk + (j % NS) * PPS, P.cap - 1);
+    const bool a_real = j < 2 * NS;
+    const int a_off = a_real ? p0 * RB : 0;
+    const uint32_t a_last = a_real ? (uint32_t)(P.cap - p0) * RB - 16u : 0u;
+    const int soff = gemv ? g_off : (attn ? a_off : 0);
+    const uint32_t last = gemv ? 0xFFFFFFF0u : (attn ? a_last : 0u);
+    const bool one = gemv ? seg1 : (attn && j >= NS && a_real);
+    s.c[j] = __builtin_amdgcn_raw_buffer_load_b128(one ? rs1 : rs0, min(voff, last), soff, 2 /* nt */);
+  }
 }
 
-template <typename WT>
-__device__ __forceinline__ float lds_elt(const WT* a, int i) {
-  if (sizeof(WT) == 2) return bf16_lo(((const uint16_t*)a)[i]);
-  return ((const float*)a)[i];
+// Partial row sums of the staged tile against the activation row in LDS
+// (times the RMSNorm gains the slot carries, for the K = hidden operators).
+template <typename WT, int CPR, bool GAIN, int KMAX>
+__device__ __forceinline__ void cmp_gemv(const Slot& s, Smem<WT, KMAX>& sm, int tc0) {
+  const int tc = opaque(tc0);
+  using G = Geo<CPR>;
+  constexpr int EPC = WT_<WT>::EPC;
+  static_assert(!GAIN || G::LPR == 1, "gains cover one column chunk per thread");
+  const int lane = tc & 63, cw = tc >> 6;
+  float acc[G::NV];
+#pragma unroll
+  for (int v = 0; v < G::NV; ++v) acc[v] = 0.f;
+  float x[EPC];  // one column chunk: held for the whole tile when LPR == 1
+  if (G::LPR == 1) {
+    const int col = CPR >= kThreads ? tc : tc % CPR;
+#pragma unroll
+    for (int e = 0; e < EPC; e += 4) {
+      const f32x4 v = *(const f32x4*)&sm.xs[col * EPC + e];
+      x[e] = v.x; x[e + 1] = v.y; x[e + 2] = v.z; x[e + 3] = v.w;
+    }
+    if (GAIN) {
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) x[e] *= __uint_as_float(s.g[e / 4][e % 4]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kChunks; ++j) {
+    if (G::LPR > 1) {  // chunks cycle through LPR columns: read this one from LDS
+      const int col = (j % G::LPR) * kThreads + tc;
+#pragma unroll
+      for (int e = 0; e < EPC; e += 4) {
+        const f32x4 v = *(const f32x4*)&sm.xs[col * EPC + e];
+        x[e] = v.x; x[e + 1] = v.y; x[e + 2] = v.z; x[e + 3] = v.w;
+      }
+    }
+    float w[EPC];
+    unpack<WT>(s.c[j], w);
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[j / G::LPR] = fmaf(w[e], x[e], acc[j / G::LPR]);
+  }
+  const float r = wave_reduce_scatter<G::NV>(acc, lane);
+  if (lane < G::NV) sm.red[cw][scatter_index<G::NV>(lane)] = r;
 }
 
-template <typename WT>
-__device__ __forceinline__ void attn_tile(const Params& P, const Tile& T, const Slot& s, Smem<WT>& sm) {
+// Staged K/V chunk -> LDS rows, except the row of the position being appended
+// this step, which the control wave writes (it was staged before it existed).
+template <typename WT, int KMAX>
+__device__ __forceinline__ void dump_kv(const Params& P, const Tile& T, const Slot& s, Smem<WT, KMAX>& sm, int tc0) {
+  const int tc = opaque(tc0);
   constexpr int CPP = kHeadDim * sizeof(WT) / 16, KCH = kAttnChunk * CPP, EPC = WT_<WT>::EPC;
   constexpr int PITCH = WT_<WT>::PITCH;
-  const int t = wpk_tid(), lane = t & 63, wave = t >> 6;
-  const int32_t p = ld_sc1(&P.seq_len[T.b]);
-  const int n = p < 0 ? 0 : min(p + 1, P.cap);
-  const int start = T.c * kAttnChunk;
-  const int cnt = max(0, min(kAttnChunk, n - start));
-  float* out = act(P, T.layer, P.off_part) + ((((size_t)T.b * P.Hkv + T.g) * P.nch + T.c) * P.G) * (P.D + 2);
-  if (cnt == 0) {
-    if (wave < P.G) {
-      float* o = out + wave * (P.D + 2);
-      st_sc1(o + 2 + lane, 0.f);
-      if (lane == 0) {
-        st_sc1(o, -INFINITY);
-        st_sc1(o + 1, 0.f);
-      }
-    }
-    return;
-  }
-  // staged K/V chunk -> LDS, one row per position
+  const int p = sm.pos[T.b];
+  const int skip = p - T.c * kAttnChunk;
 #pragma unroll
   for (int j = 0; j < 2 * KCH / kThreads; ++j) {
-    const int flat = j * kThreads + t;
+    const int flat = j * kThreads + tc;
     const bool isv = flat >= KCH;
     const int f = isv ? flat - KCH : flat;
     const int pos = f / CPP, dc = f % CPP;
+    if (pos == skip) continue;
     WT* dst = (isv ? sm.vs : sm.ks) + pos * PITCH + dc * EPC;
     if (sizeof(WT) == 2) {
       uint32_t* d32 = (uint32_t*)dst;  // row pitch 132 B keeps 4-byte alignment
@@ -558,132 +419,446 @@ __device__ __forceinline__ void attn_tile(const Params& P, const Tile& T, const 
       d[2] = __uint_as_float(s.c[j].z); d[3] = __uint_as_float(s.c[j].w);
     }
   }
-  // queries of the group (written by this step's QKV tiles)
-  if (wave < P.G)
-    sm.qs[wave][lane] = ld_sc1(act(P, T.layer, P.off_q) + (size_t)T.b * P.Hq * P.D + (size_t)(T.g * P.G + wave) * P.D + lane);
-  __syncthreads();
-  // position p was appended by this step's QKV tiles after the chunk was staged
-  if (p >= start && p < start + kAttnChunk && p < P.cap && t < 2 * kHeadDim) {
-    const size_t at = ((((size_t)T.layer * P.B + T.b) * P.Hkv + T.g) * P.cap + p) * kHeadDim;
-    const bool isv = t >= kHeadDim;
-    const int d = t & (kHeadDim - 1);
-    WT* dst = (isv ? sm.vs : sm.ks) + (p - start) * PITCH + d;
-    const WT* src = (const WT*)(isv ? P.vc : P.kc) + at + d;
-    if (sizeof(WT) == 2) *(uint16_t*)dst = ld_sc1((const uint16_t*)src);
-    else *(float*)dst = ld_sc1((const float*)src);
-  }
-  __syncthreads();
-  // scores: wave h = q head, lane j = position
-  float m = -INFINITY, l = 0.f;
-  if (wave < P.G) {
-    float sc = -INFINITY;
-    if (lane < cnt) {
-      float dot = 0.f;
-      const WT* kr = sm.ks + lane * PITCH;
-#pragma unroll 16
-      for (int d = 0; d < kHeadDim; ++d) dot = fmaf(sm.qs[wave][d], lds_elt<WT>(kr, d), dot);
-      sc = dot * P.attn_scale;
+}
+
+__device__ __forceinline__ int attn_count(const Params& P, const Tile& T, int p) {
+  const int n = p < 0 ? 0 : min(p + 1, P.cap);
+  return max(0, min(kAttnChunk, n - T.c * kAttnChunk));
+}
+
+// Attention partial: compute wave h = q head h of the group, lane = position
+// (scores) then lane = head dimension (weighted values).  Both loops are
+// unrolled so that the LDS reads of a row are in flight together.
+template <typename WT, int KMAX>
+__device__ __forceinline__ void cmp_attn(const Params& P, const Tile& T, Smem<WT, KMAX>& sm, int tc0) {
+  const int tc = opaque(tc0);
+  constexpr int PITCH = WT_<WT>::PITCH;
+  const int lane = tc & 63, h = tc >> 6;
+  const int cnt = attn_count(P, T, sm.pos[T.b]);
+  if (h >= P.G || cnt == 0) return;
+  float sc = -INFINITY;
+  if (lane < cnt) {
+    const WT* kr = sm.ks + lane * PITCH;
+    float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
+#pragma unroll
+    for (int d = 0; d < kHeadDim; d += 4) {
+      const f32x4 q = *(const f32x4*)&sm.qs[h][d];
+      d0 = fmaf(q.x, elt<WT>(kr, d), d0);
+      d1 = fmaf(q.y, elt<WT>(kr, d + 1), d1);
+      d2 = fmaf(q.z, elt<WT>(kr, d + 2), d2);
+      d3 = fmaf(q.w, elt<WT>(kr, d + 3), d3);
     }
-    m = wave_max(sc);
-    const float e = lane < cnt ? __expf(sc - m) : 0.f;
-    l = wave_sum(e);
-    sm.ps[wave][lane] = e;
+    sc = ((d0 + d1) + (d2 + d3)) * P.attn_scale;
   }
-  __syncthreads();
-  if (wave < P.G) {
-    float o = 0.f;
-    for (int j = 0; j < cnt; ++j) o = fmaf(sm.ps[wave][j], lds_elt<WT>(sm.vs + j * PITCH, lane), o);
-    float* dst = out + wave * (P.D + 2);
-    st_sc1(dst + 2 + lane, o);
-    if (lane == 0) {
-      st_sc1(dst, m);
-      st_sc1(dst + 1, l);
+  const float m = wave_max(sc);
+  const float e = lane < cnt ? __expf(sc - m) : 0.f;
+  const float l = wave_sum(e);
+  sm.ps[h][lane] = e;
+  float o = 0.f;
+  for (int j0 = 0; j0 < cnt; j0 += 8) {
+    const f32x4 pa = *(const f32x4*)&sm.ps[h][j0];
+    const f32x4 pb = *(const f32x4*)&sm.ps[h][j0 + 4];
+    const float pw[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float v = elt<WT>(sm.vs + (j0 + u) * PITCH, lane);
+      o = fmaf(pw[u], j0 + u < cnt ? v : 0.f, o);  // rows past the chunk's positions hold no data
     }
+  }
+  sm.outs[h][2 + lane] = o;
+  if (lane == 0) {
+    sm.outs[h][0] = m;
+    sm.outs[h][1] = l;
   }
 }
 
-template <typename WT>
-__device__ __forceinline__ void combine_tile(const Params& P, const Tile& T) {
-  const int t = wpk_tid(), lane = t & 63, wave = t >> 6;
-  if (wave >= P.G) return;
-  const int32_t p = ld_sc1(&P.seq_len[T.b]);
+// Merge of the attention partials of one (sequence, kv head): compute wave h
+// merges q head h (lane = head dimension), reading the chunks in batches of
+// 16 with all of a batch's loads in flight together, and rescaling the running
+// sums when a batch raises the maximum.  The wave waits for its stores, so the
+// tile is complete when the control wave publishes after barrier B.
+template <typename WT, int KMAX>
+__device__ __forceinline__ void cmp_combine(const Params& P, const Tile& T, const Smem<WT, KMAX>& sm, int tc0) {
+  const int tc = opaque(tc0);
+  const int lane = tc & 63, h = tc >> 6;
+  if (h >= P.G) return;
+  const int p = sm.pos[T.b];
   const int n = p < 0 ? 0 : min(p + 1, P.cap);
   const int nact = (n + kAttnChunk - 1) / kAttnChunk;
-  float* dst = act(P, T.layer, P.off_attn) + (size_t)T.b * P.Hq * P.D + (size_t)(T.g * P.G + wave) * P.D;
-  const float* part = act(P, T.layer, P.off_part) + (((size_t)T.b * P.Hkv + T.g) * P.nch * P.G + wave) * (P.D + 2);
-  const size_t stride = (size_t)P.G * (P.D + 2);
-  if (nact == 0) {
-    st_sc1(dst + lane, 0.f);
-    return;
+  float* dst = act(P, T.layer, P.off_attn) + (size_t)T.b * P.Hq * P.D + (size_t)(T.g * P.G + h) * P.D;
+  const float* part = act(P, T.layer, P.off_part) + (((size_t)T.b * P.Hkv + T.g) * P.nch * P.G + h) * (P.D + 2);
+  const int stride = P.G * (P.D + 2);
+  float M = -INFINITY, L = 0.f, O = 0.f;
+  for (int c0 = 0; c0 < nact; c0 += 16) {
+    const int nb = min(16, nact - c0);
+    const int k = lane & 15;
+    const float* pk = part + (size_t)(c0 + min(k, nb - 1)) * stride;
+    const float mk = ld_sc1(pk), lk = ld_sc1(pk + 1);
+    float o[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) o[c] = c < nb ? ld_sc1(part + (size_t)(c0 + c) * stride + 2 + lane) : 0.f;
+    float mb = mk;
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) mb = fmaxf(mb, __shfl_xor(mb, m));
+    const float Mn = fmaxf(M, mb);
+    const float keep = __expf(M - Mn);
+    const float wk = k < nb ? __expf(mk - Mn) : 0.f;
+    float lb = wk * lk;
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) lb += __shfl_xor(lb, m);
+    float ob = 0.f;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) ob = fmaf(__shfl(wk, c), o[c], ob);
+    L = fmaf(L, keep, lb);
+    O = fmaf(O, keep, ob);
+    M = Mn;
   }
-  float M = -INFINITY;
-  for (int c = 0; c < nact; ++c) M = fmaxf(M, ld_sc1(part + c * stride));
-  float L = 0.f, o = 0.f;
-  for (int c = 0; c < nact; ++c) {
-    const float w = __expf(ld_sc1(part + c * stride) - M);
-    L = fmaf(ld_sc1(part + c * stride + 1), w, L);
-    o = fmaf(ld_sc1(part + c * stride + 2 + lane), w, o);
-  }
-  st_sc1(dst + lane, o / L);
+  st_sc1(dst + lane, nact == 0 ? 0.f : O / L);
+  __builtin_amdgcn_s_waitcnt(0);
 }
 
-// Output conversion: greedy token and sequence advance.
-__device__ __forceinline__ void argmax_tile(const Params& P) {
-  const int t = wpk_tid();
-  if (t < P.B) {
-    unsigned long long best = 0;
-    for (int s = 0; s < kArgmaxShards; ++s) {
-      unsigned long long* a = &P.argmax[t * kArgmaxShards + s];
-      const unsigned long long v = __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      best = v > best ? v : best;
-      __hip_atomic_store(a, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    const int32_t p = ld_sc1(&P.seq_len[t]);
-    if (p >= 0 && p < P.cap) {
-      st_sc1(&P.tokens[t], (int32_t)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull)));
-      st_sc1(&P.seq_len[t], p + 1);
-    }
-  }
-}
-
-// ---- dispatch -------------------------------------------------------------------------------
-
-template <typename WT, int CPR_H, int CPR_F>
-__device__ __forceinline__ void stage(const Params& P, const Tile& T, Slot& s) {
-  const LayerW& lw = P.lw[T.layer];
-  switch (T.type) {
-    case T_QKV: stage_gemv<CPR_H>(lw.w_qkv, lw.w_qkv, T.r0, T.r1, T.rs, T.rows, P.qkv_rows, s); break;
-    case T_OPROJ: stage_gemv<CPR_H>(lw.w_o, lw.w_o, T.r0, T.r1, T.rs, T.rows, P.H, s); break;
-    case T_GATEUP: stage_gemv<CPR_H>(lw.w_gate, lw.w_up, T.r0, T.r1, T.rs, T.rows, P.F, s); break;
-    case T_DOWN: stage_gemv<CPR_F>(lw.w_down, lw.w_down, T.r0, T.r1, T.rs, T.rows, P.H, s); break;
-    case T_LM: stage_gemv<CPR_H>(P.embed, P.embed, T.r0, T.r1, T.rs, T.rows, P.V, s); break;
-    case T_ATTN: stage_attn<WT>(P, T, s); break;
-    default: break;
-  }
-}
-
-template <typename WT, int CPR_H, int CPR_F>
-__device__ __forceinline__ void run_tile(const Params& P, const Tile& T, const Slot& s, Smem<WT>& sm) {
+template <typename WT, int CPR_H, int CPR_F, int KMAX>
+__device__ __forceinline__ void compute(const Params& P, const Tile& T, const Slot& s, Smem<WT, KMAX>& sm, int tc) {
   switch (T.type) {
     case T_QKV:
     case T_OPROJ:
     case T_GATEUP:
-    case T_LM: gemv_tile<WT, CPR_H>(P, T, s, sm); break;
-    case T_DOWN: gemv_tile<WT, CPR_F>(P, T, s, sm); break;
-    case T_ATTN: attn_tile<WT>(P, T, s, sm); break;
-    case T_COMBINE: combine_tile<WT>(P, T); break;
-    case T_ARGMAX: argmax_tile(P); break;
+    case T_LM: cmp_gemv<WT, CPR_H, true>(s, sm, tc); break;
+    case T_DOWN: cmp_gemv<WT, CPR_F, false>(s, sm, tc); break;
+    case T_ATTN: cmp_attn<WT>(P, T, sm, tc); break;
+    case T_COMBINE: cmp_combine<WT>(P, T, sm, tc); break;
+    default: break;  // argmax is control-wave work
+  }
+}
+
+// ============================ control wave ====================================================
+
+// Stages the activation row of a GEMV tile for sequence b into LDS, applying
+// the RMSNorm prologue (x / sqrt(mean(x^2) + eps) * gain) for the operators
+// that have one; the embedding row of the token is layer 0's input (device-side
+// input conversion).
+template <typename WT, int K, bool EMBED, int KMAX>
+__device__ __forceinline__ void ctl_input(const Params& P, const float* src, const float* gain, int b,
+                                          Smem<WT, KMAX>& sm, int lane0) {
+  const int lane = opaque(lane0);
+  constexpr int NQ = K / 256;  // 1 KiB pieces of the row: 16 bytes per lane each
+  static_assert(K % 256 == 0, "row length");
+  if (!EMBED || src != nullptr) {
+    // Device-coherent (sc1) loads straight into LDS: every piece in flight at
+    // once, no registers held; then the norm, if any, in place.
+    const __amdgpu_buffer_rsrc_t r = rsrc(src + (size_t)b * K);
+#pragma unroll
+    for (int i = 0; i < NQ; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)&sm.xs[256 * i], 16,
+                                               (uint32_t)lane * 16u, 1024 * i, 0, 16 /* sc1 */);
+    __builtin_amdgcn_s_waitcnt(0);
+    if (!gain) return;
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      const f32x4 v = *(const f32x4*)&sm.xs[256 * i + 4 * lane];
+      ss = fmaf(v.x, v.x, ss); ss = fmaf(v.y, v.y, ss); ss = fmaf(v.z, v.z, ss); ss = fmaf(v.w, v.w, ss);
+    }
+    ss = wave_sum(ss);
+    const float inv = 1.0f / sqrtf(ss / (float)K + P.eps);
+    asm volatile("" ::: "memory");  // re-read the row rather than hold K/64 values in registers
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      f32x4 v = *(const f32x4*)&sm.xs[256 * i + 4 * lane];
+      v.x *= inv; v.y *= inv; v.z *= inv; v.w *= inv;
+      *(f32x4*)&sm.xs[256 * i + 4 * lane] = v;
+    }
+    return;
+  }
+  if constexpr (!EMBED) return;
+  // layer 0: the token's embedding row (model dtype -> fp32), with the norm;
+  // the compute waves apply the gains, which they stage with the weights
+  constexpr int EPC = WT_<WT>::EPC;
+  constexpr int NG = K / (64 * EPC);  // 16-byte chunks per lane
+  static_assert(K % (64 * EPC) == 0, "row length");
+  float v[NG * EPC];
+  const char* row = (const char*)P.embed + (size_t)sm.tok[b] * K * sizeof(WT);
+#pragma unroll
+  for (int g = 0; g < NG; ++g) unpack<WT>(*(const u32x4*)(row + (size_t)(lane + 64 * g) * 16), &v[g * EPC]);
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < NG * EPC; ++i) ss = fmaf(v[i], v[i], ss);
+  ss = wave_sum(ss);
+  const float inv = 1.0f / sqrtf(ss / (float)K + P.eps);
+#pragma unroll
+  for (int g = 0; g < NG; ++g)
+#pragma unroll
+    for (int c = 0; c < EPC; c += 4) {
+      f32x4 o;
+      o.x = v[g * EPC + c] * inv;
+      o.y = v[g * EPC + c + 1] * inv;
+      o.z = v[g * EPC + c + 2] * inv;
+      o.w = v[g * EPC + c + 3] * inv;
+      *(f32x4*)&sm.xs[(lane + 64 * g) * EPC + c] = o;
+    }
+}
+
+// Values the epilogue needs, loaded together with the inputs.
+struct EpiIn {
+  float res;     // residual row (o-proj, down)
+  float cs, sn;  // RoPE cos/sin (q and k rows)
+};
+
+template <typename WT, int KMAX>
+__device__ __forceinline__ EpiIn ctl_preload(const Params& P, const Tile& T, int b, const Smem<WT, KMAX>& sm,
+                                             int lane0) {
+  const int lane = opaque(lane0);
+  EpiIn e{0.f, 1.f, 0.f};
+  const int p = sm.pos[b];
+  switch (T.type) {
+    case T_QKV:
+      if (T.kind < 2 && lane < T.rs && p >= 0 && p < P.cap) {
+        const int base = T.kind == 0 ? T.g * P.D : (P.Hq + T.g) * P.D;
+        const int dim = T.r0 + lane - base;
+        e.cs = P.rope_cos[p * (P.D / 2) + dim];
+        e.sn = P.rope_sin[p * (P.D / 2) + dim];
+      }
+      break;
+    case T_OPROJ:
+      if (lane < T.rows && T.r0 + lane < P.H) {
+        const int row = T.r0 + lane;
+        if (T.layer == 0) {
+          const WT* ep = (const WT*)P.embed + (size_t)sm.tok[b] * P.H + row;
+          e.res = sizeof(WT) == 2 ? bf16_lo(*(const uint16_t*)ep) : *(const float*)ep;
+        } else {
+          e.res = ld_sc1(x_in(P, T.layer) + (size_t)b * P.H + row);
+        }
+      }
+      break;
+    case T_DOWN:
+      if (lane < T.rows && T.r0 + lane < P.H) e.res = ld_sc1(act(P, T.layer, P.off_x_mid) + (size_t)b * P.H + T.r0 + lane);
+      break;
+    default:
+      break;
+  }
+  return e;
+}
+
+// Full row sum of row `lane` of the tile from the compute waves' partials.
+template <int CPR, typename WT, int KMAX>
+__device__ __forceinline__ float row_sum(const Smem<WT, KMAX>& sm, int lane) {
+  using G = Geo<CPR>;
+  float y = 0.f;
+  if (lane < G::ROWS) {
+    if (CPR >= kThreads) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) y += sm.red[w][lane];
+    } else {
+      constexpr int S = kThreads / CPR;  // rows interleaved per value index
+      const int v = lane / S, grp = lane % S;
+#pragma unroll
+      for (int w = 0; w < G::WPR; ++w) y += sm.red[grp * G::WPR + w][v];
+    }
+  }
+  return y;
+}
+
+template <typename WT, int CPR, int KMAX>
+__device__ __forceinline__ void ctl_gemv_out(const Params& P, const Tile& T, int b, const Smem<WT, KMAX>& sm,
+                                             const EpiIn& e, int lane0) {
+  const int lane = opaque(lane0);
+  const float y = row_sum<CPR>(sm, lane);
+  const float y2 = __shfl(y, min(lane + T.rs, 63));  // the paired row (RoPE / gate-up)
+  const int l = T.layer;
+  const int p = sm.pos[b];
+  switch (T.type) {
+    case T_QKV: {
+      if (p < 0) break;  // inactive slot: nothing to append
+      if (p >= P.cap) {
+        if (lane == 0) latch_error(P, WPK_E_CTX_FULL, T.id);
+        break;
+      }
+      const int half = P.D / 2;
+      if (T.kind < 2) {
+        if (lane < T.rs) {
+          const int head = T.g;
+          const int base = T.kind == 0 ? head * P.D : (P.Hq + head) * P.D;
+          const int dim = T.r0 + lane - base;
+          const float ra = y * e.cs - y2 * e.sn, rb = y2 * e.cs + y * e.sn;
+          if (T.kind == 0) {
+            float* q = act(P, l, P.off_q) + (size_t)b * P.Hq * P.D + head * P.D;
+            st_sc1(q + dim, ra);
+            st_sc1(q + dim + half, rb);
+          } else {
+            const size_t at = ((((size_t)l * P.B + b) * P.Hkv + head) * P.cap + p) * P.D;
+            if (sizeof(WT) == 2) {
+              st_sc1((uint16_t*)P.kc + at + dim, to_bf16(ra));
+              st_sc1((uint16_t*)P.kc + at + dim + half, to_bf16(rb));
+            } else {
+              st_sc1((float*)P.kc + at + dim, ra);
+              st_sc1((float*)P.kc + at + dim + half, rb);
+            }
+          }
+        }
+      } else if (lane < T.rows) {
+        const int base = (P.Hq + P.Hkv + T.g) * P.D;
+        const int mrow = lane < T.rs ? T.r0 + lane : T.r1 + (lane - T.rs);
+        const size_t at = ((((size_t)l * P.B + b) * P.Hkv + T.g) * P.cap + p) * P.D + (mrow - base);
+        if (sizeof(WT) == 2) st_sc1((uint16_t*)P.vc + at, to_bf16(y));
+        else st_sc1((float*)P.vc + at, y);
+      }
+      break;
+    }
+    case T_OPROJ:
+      if (lane < T.rows && T.r0 + lane < P.H) st_sc1(act(P, l, P.off_x_mid) + (size_t)b * P.H + T.r0 + lane, e.res + y);
+      break;
+    case T_GATEUP:
+      if (lane < T.rs && T.r0 + lane < P.F)
+        st_sc1(act(P, l, P.off_h) + (size_t)b * P.F + T.r0 + lane, y / (1.0f + __expf(-y)) * y2);
+      break;
+    case T_DOWN:
+      if (lane < T.rows && T.r0 + lane < P.H) st_sc1(act(P, l, P.off_x_out) + (size_t)b * P.H + T.r0 + lane, e.res + y);
+      break;
+    case T_LM: {
+      const int row = T.r0 + lane;
+      unsigned long long key = 0;
+      if (lane < T.rows && row < P.V) {
+        P.logits[(size_t)b * P.V + row] = y;
+        key = pack_max(y, row);
+      }
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) {
+        const unsigned long long o = __shfl_xor(key, m);
+        key = o > key ? o : key;
+      }
+      if (lane == 0)
+        __hip_atomic_fetch_max(&P.argmax[b * kArgmaxShards + T.id % kArgmaxShards], key, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+  }
+}
+
+// Attention inputs: the group's queries and the K/V row appended this step.
+template <typename WT, int KMAX>
+__device__ __forceinline__ void ctl_attn_in(const Params& P, const Tile& T, Smem<WT, KMAX>& sm, int lane0) {
+  const int lane = opaque(lane0);
+  constexpr int PITCH = WT_<WT>::PITCH;
+  const int p = sm.pos[T.b];
+  const int start = T.c * kAttnChunk;
+  if (attn_count(P, T, p) == 0) return;
+  const float* q = act(P, T.layer, P.off_q) + (size_t)T.b * P.Hq * P.D + (size_t)T.g * P.G * P.D;
+  float qv[kMaxGroupHeads];
+#pragma unroll
+  for (int h = 0; h < kMaxGroupHeads; ++h) qv[h] = h < P.G ? ld_sc1(q + h * P.D + lane) : 0.f;
+  if (p >= start && p < start + kAttnChunk && p < P.cap) {
+    const size_t at = ((((size_t)T.layer * P.B + T.b) * P.Hkv + T.g) * P.cap + p) * kHeadDim + lane;
+    WT* kd = sm.ks + (p - start) * PITCH + lane;
+    WT* vd = sm.vs + (p - start) * PITCH + lane;
+    if (sizeof(WT) == 2) {
+      *(uint16_t*)kd = ld_sc1((const uint16_t*)P.kc + at);
+      *(uint16_t*)vd = ld_sc1((const uint16_t*)P.vc + at);
+    } else {
+      *(float*)kd = ld_sc1((const float*)P.kc + at);
+      *(float*)vd = ld_sc1((const float*)P.vc + at);
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < kMaxGroupHeads; ++h)
+    if (h < P.G) sm.qs[h][lane] = qv[h];
+}
+
+template <typename WT, int KMAX>
+__device__ __forceinline__ void ctl_attn_out(const Params& P, const Tile& T, const Smem<WT, KMAX>& sm, int lane0) {
+  const int lane = opaque(lane0);
+  const bool empty = attn_count(P, T, sm.pos[T.b]) == 0;
+  float* out = act(P, T.layer, P.off_part) + ((((size_t)T.b * P.Hkv + T.g) * P.nch + T.c) * P.G) * (P.D + 2);
+  for (int h = 0; h < P.G; ++h) {
+    float* o = out + h * (P.D + 2);
+    st_sc1(o + 2 + lane, empty ? 0.f : sm.outs[h][2 + lane]);
+    if (lane == 0) {
+      st_sc1(o, empty ? -INFINITY : sm.outs[h][0]);
+      st_sc1(o + 1, empty ? 0.f : sm.outs[h][1]);
+    }
+  }
+}
+
+// Output conversion: greedy token and sequence advance.  Lane b*16 + s takes
+// shard s of sequence b (and clears it for the next step); a 16-lane max
+// reduction gives the packed (value, lowest index) maximum.
+template <typename WT, int KMAX>
+__device__ __forceinline__ void ctl_argmax(const Params& P, const Smem<WT, KMAX>& sm, int lane0) {
+  const int lane = opaque(lane0);
+  static_assert(kMaxBatch * kArgmaxShards <= 64, "one lane per shard");
+  const int b = lane / kArgmaxShards;
+  unsigned long long best = 0;
+  if (b < P.B)
+    best = __hip_atomic_exchange(&P.argmax[lane], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+  for (int m = 1; m < kArgmaxShards; m <<= 1) {
+    const unsigned long long o = __shfl_xor(best, m);
+    best = o > best ? o : best;
+  }
+  if (b < P.B && lane % kArgmaxShards == 0) {
+    const int p = sm.pos[b];
+    if (p >= 0 && p < P.cap) {
+      st_sc1(&P.tokens[b], (int32_t)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull)));
+      st_sc1(&P.seq_len[b], p + 1);
+    }
+  }
+}
+
+template <typename WT, int CPR_H, int CPR_F, int KMAX>
+__device__ __forceinline__ EpiIn ctl_pre(const Params& P, const Tile& T, int b, Smem<WT, KMAX>& sm, int lane,
+                                         int& xkey) {
+  constexpr int KH = CPR_H * 16 / sizeof(WT), KF = CPR_F * 16 / sizeof(WT);
+  EpiIn e{0.f, 1.f, 0.f};
+  if (is_gemv(T.type)) {
+    // one activation row serves consecutive tiles of an operator (batch 1)
+    const int key = T.layer * T_NTYPES + T.type;
+    e = ctl_preload<WT>(P, T, b, sm, lane);
+    if (P.B > 1 || key != xkey) {
+      // the activation row and RMSNorm gain of each GEMV operator; a null
+      // source is layer 0's embedding row, a null gain a plain copy
+      const int ty = T.type, l = T.layer;
+      if (ty == T_DOWN) {
+        ctl_input<WT, KF, false>(P, act(P, l, P.off_h), nullptr, b, sm, lane);
+      } else {
+        const float* src = ty == T_QKV ? x_in(P, l)
+                         : ty == T_OPROJ ? act(P, l, P.off_attn)
+                         : ty == T_GATEUP ? act(P, l, P.off_x_mid)
+                                          : act(P, P.L - 1, P.off_x_out);
+        const float* gain = ty == T_QKV ? P.lw[l].attn_norm
+                          : ty == T_GATEUP ? P.lw[l].mlp_norm
+                          : ty == T_LM ? P.final_norm
+                                       : nullptr;
+        ctl_input<WT, KH, true>(P, src, gain, b, sm, lane);
+      }
+      xkey = P.B > 1 ? -1 : key;
+    }
+  } else if (T.type == T_ATTN) {
+    ctl_attn_in<WT>(P, T, sm, lane);
+  }
+  return e;
+}
+
+template <typename WT, int CPR_H, int CPR_F, int KMAX>
+__device__ __forceinline__ void ctl_post(const Params& P, const Tile& T, int b, Smem<WT, KMAX>& sm, const EpiIn& e,
+                                         int lane) {
+  switch (T.type) {
+    case T_DOWN: ctl_gemv_out<WT, CPR_F>(P, T, b, sm, e, lane); break;
+    case T_QKV:
+    case T_OPROJ:
+    case T_GATEUP:
+    case T_LM: ctl_gemv_out<WT, CPR_H>(P, T, b, sm, e, lane); break;
+    case T_ATTN: ctl_attn_out<WT>(P, T, sm, lane); break;
+    case T_ARGMAX: ctl_argmax<WT>(P, sm, lane); break;
     default: break;
   }
 }
 
-// Wave 0 of a worker waits until the tile's counter group is complete for this
+// The control wave waits until the tile's counter group is complete for this
 // step.  Bounded: past the watchdog budget it latches WPK_E_TIMEOUT naming the
 // tile and raises the abort flag, which every other waiting worker also sees.
-__device__ __forceinline__ bool wait_group(const Params& P, const Tile& T, uint32_t epoch, int32_t* delta) {
+__device__ __forceinline__ bool wait_group(const Params& P, const Tile& T, uint32_t epoch, int32_t* delta,
+                                           int lane) {
   const Group G = cload(P.groups, T.wait);
   const uint32_t target = (epoch + 1u) * (uint32_t)G.producers;
-  const int lane = wpk_tid() & 63;
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
   for (;;) {
     const uint32_t v = lane < G.shards ? ld_sc1(&P.counters[(size_t)(G.shard0 + lane) * kLine]) : 0u;
@@ -706,73 +881,208 @@ __device__ __forceinline__ uint32_t hash32(uint32_t x) {
   return x;
 }
 
-// The worker loop: claim (from this worker's queue, in topological order),
-// stage the tile's weights, wait for its counter group, run it, publish.
-template <typename WT, int CPR_H, int CPR_F, bool LOG>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void megakernel(Params P) {
-  __shared__ Smem<WT> sm;
-  const int t = wpk_tid(), lane = t & 63, wave = t >> 6;
-  const int w = blockIdx.x;
-  const uint32_t epoch = ld_sc1(&P.ctl[CTL_EPOCH]);
-  const bool dead = ld_sc1(&P.ctl[CTL_STATUS]) != 0u;
-  const int q = w % P.n_queues;
-  const int qb = cload(P.queue_off, q), qn = cload(P.queue_off, q + 1) - qb;
-  uint32_t* head = P.heads + (size_t)q * kLine;
-  if (t == 0) sm.first = dead ? qn : (int)atomic_add(head, 1u);
-  __syncthreads();
-  int ci = __builtin_amdgcn_readfirstlane(sm.first);
-  int parity = 0;
-  while (ci < qn) {
-    const int id = cload(P.queue, qb + ci);
+// ============================ the worker loops ================================================
+
+template <typename WT, int CPR_H, int CPR_F, bool LOG, int KMAX>
+__device__ __forceinline__ void control_loop(const Params& P, Smem<WT, KMAX>& sm, int cur, int qb, int qn,
+                                             uint32_t* head, uint32_t epoch, int lane0) {
+  int it = 0;
+  int done_group = -1;  // a group already seen complete this step (groups never un-complete)
+  int xkey = -1;        // which activation row sm.xs holds
+  while (cur < qn) {
+    // lane index made opaque per tile, so per-lane address arithmetic of all
+    // tile types is not hoisted out of the loop and kept live across it
+    const int lane = opaque(lane0);
+    const uint64_t t_claim = LOG ? __builtin_amdgcn_s_memrealtime() : 0;
+    const int id = cload(P.queue, qb + cur);
     const Tile T = cload(P.tiles, id);
-    Slot s;
-    if (P.prefetch) stage<WT, CPR_H, CPR_F>(P, T, s);
-    if (wave == 0) {
-      uint32_t next = 0;
-      if (lane == 0) next = atomic_add(head, 1u);
-      int32_t delta = 0;
-      bool ok = true;
-      if (T.wait >= 0) ok = wait_group(P, T, epoch, &delta);
-      if (lane == 0) {
-        sm.next[parity] = (int)next;
-        sm.ok = ok;
-        sm.delta = delta;
-      }
+    uint32_t nx = 0;
+    if (lane == 0) nx = atomic_add(head, 1u);
+    int32_t delta = 0;
+    bool ok = true;
+    if (T.wait >= 0 && (LOG || T.wait != done_group)) {
+      ok = wait_group(P, T, epoch, &delta, lane);
+      if (ok) done_group = T.wait;
     }
-    __syncthreads();
-    if (!sm.ok) break;
-    if (!P.prefetch) stage<WT, CPR_H, CPR_F>(P, T, s);
-    if (P.perturb) {
+    nx = __shfl(nx, 0);
+    if (lane == 0) {
+      sm.ids[(it + 1) & 1] = (int)nx;
+      sm.stop = ok ? 0 : 1;
+    }
+    if (!ok) {
+      __syncthreads();  // A
+      __syncthreads();  // B
+      break;
+    }
+    if (P.perturb)
       for (uint32_t k = hash32((uint32_t)id ^ P.perturb) & 31u; k; --k) __builtin_amdgcn_s_sleep(8);
-    }
     const uint64_t t_start = LOG ? __builtin_amdgcn_s_memrealtime() : 0;
-    run_tile<WT, CPR_H, CPR_F>(P, T, s, sm);
-    // publish: every wave's device-coherent stores have completed, then one
-    // relaxed device-scope increment of the tile's counter shard
+    const int npairs = is_gemv(T.type) ? P.B : 1;
+    uint64_t t_inputs = 0, t_partials = 0, t_ready = 0, t_done = 0;
+    for (int b = 0; b < npairs; ++b) {
+      const EpiIn e = ctl_pre<WT, CPR_H, CPR_F>(P, T, b, sm, lane, xkey);
+      if (LOG) {
+        t_inputs = __builtin_amdgcn_s_memrealtime();
+        if (lane == 0) sm.t_ready = sm.t_done = 0;
+      }
+      __syncthreads();  // A: inputs staged
+      __syncthreads();  // B: partial sums ready
+      if (LOG) {
+        t_partials = __builtin_amdgcn_s_memrealtime();
+        t_ready = sm.t_ready;
+        t_done = sm.t_done;
+      }
+      ctl_post<WT, CPR_H, CPR_F>(P, T, b, sm, e, lane);
+    }
+    // publish: this wave made every global store of the tile; once they have
+    // completed, one relaxed device-scope increment of the tile's counter shard
     __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (t == 0) {
+    if (lane == 0) {
       if (LOG) {
         int32_t* rec = P.log + (size_t)id * 8;
         __hip_atomic_fetch_add(rec, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        rec[1] = sm.delta;
-        rec[2] = w;
-        rec[3] = ci;
+        rec[1] = delta;
+        rec[2] = (int32_t)blockIdx.x;
+        rec[3] = cur;
         const uint64_t t_end = __builtin_amdgcn_s_memrealtime();
         *(uint64_t*)(rec + 4) = t_start;
         *(uint64_t*)(rec + 6) = t_end;
+        uint64_t* tm = (uint64_t*)(P.log + ((size_t)P.n_tiles + P.log_workers) * 8) + (size_t)id * 8;
+        tm[0] = t_claim;
+        tm[1] = t_inputs;
+        tm[2] = t_ready;
+        tm[3] = t_done;
+        tm[4] = t_partials;
+        tm[5] = t_end;
       }
       if (T.signal >= 0 && id != P.drop_tile) {
         const Group G = cload(P.groups, T.signal);
         atomic_add(&P.counters[(size_t)(G.shard0 + T.shard) * kLine], 1u);
       }
     }
-    ci = __builtin_amdgcn_readfirstlane(sm.next[parity]);
-    parity ^= 1;
+    cur = (int)nx;
+    ++it;
   }
-  // leave the step; the last worker out rewinds the queues and advances the epoch
-  __builtin_amdgcn_s_waitcnt(0);
+}
+
+// Redefines the slot in place (no copy), once per batch row: the unpacked
+// weights then depend on the row and are not hoisted out of the batch loop,
+// where they would need twice the slot's registers.
+__device__ __forceinline__ void launder(Slot& s) {
+  asm volatile("" : "+v"(s.c[0]), "+v"(s.c[1]), "+v"(s.c[2]), "+v"(s.c[3]), "+v"(s.c[4]), "+v"(s.c[5]),
+               "+v"(s.c[6]), "+v"(s.c[7]));
+  asm volatile("" : "+v"(s.c[8]), "+v"(s.c[9]), "+v"(s.c[10]), "+v"(s.c[11]), "+v"(s.c[12]), "+v"(s.c[13]),
+               "+v"(s.c[14]), "+v"(s.c[15]));
+}
+
+template <typename WT, int CPR_H, int CPR_F, bool LOG, int KMAX>
+__device__ __forceinline__ void compute_loop(const Params& P, Smem<WT, KMAX>& sm, int cur, int qb, int qn, int tc0) {
+  const uint32_t voff = (uint32_t)tc0 * 16u;
+  Slot s;
+#pragma unroll
+  for (int j = 0; j < kChunks; ++j) s.c[j] = u32x4{0u, 0u, 0u, 0u};
+  int it = -1;  // claim iteration of the current tile
+  int nx = cur;
+  while (nx < qn) {
+    // The slot is free (the previous tile's arithmetic is done and its
+    // barrier B passed, so the control wave is already running that tile's
+    // epilogue): stage this tile's weights; they stream in while the control
+    // wave publishes, claims, waits for the tile's inputs and stages them.
+    const Tile T = cload(P.tiles, cload(P.queue, qb + nx));
+    stage<WT, CPR_H, CPR_F>(P, T, s, voff);
+    ++it;
+    const int tc = opaque(tc0);
+    const int npairs = is_gemv(T.type) ? P.B : 1;
+    bool stop = false;
+    for (int b = 0; b < npairs; ++b) {
+      if (T.type == T_ATTN && attn_count(P, T, sm.pos[T.b]) > 0) dump_kv<WT>(P, T, s, sm, tc);
+      __syncthreads();  // A
+      if (__builtin_amdgcn_readfirstlane(sm.stop)) {
+        __syncthreads();  // B
+        stop = true;
+        break;
+      }
+      if (LOG) {  // timing only: the slot's loads are complete here (latest compute wave)
+        __builtin_amdgcn_s_waitcnt(0);
+        if ((tc & 63) == 0)
+          __hip_atomic_fetch_max(&sm.t_ready, (uint64_t)__builtin_amdgcn_s_memrealtime(), __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+      launder(s);
+      compute<WT, CPR_H, CPR_F>(P, T, s, sm, tc);
+      if (LOG && (tc & 63) == 0)
+        __hip_atomic_fetch_max(&sm.t_done, (uint64_t)__builtin_amdgcn_s_memrealtime(), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
+      __syncthreads();  // B
+    }
+    if (stop) break;
+    // Keep the next tile's loads after this tile's arithmetic: hoisting them
+    // above it would keep two slots live.
+    __builtin_amdgcn_sched_barrier(0);
+    nx = __builtin_amdgcn_readfirstlane(sm.ids[(it + 1) & 1]);
+  }
+}
+
+template <int CPR_H, int CPR_F, typename WT>
+constexpr int kmax() {
+  return (CPR_H > CPR_F ? CPR_H : CPR_F) * 16 / (int)sizeof(WT);
+}
+
+// Step start: sequence positions and tokens (both fixed until the step's last
+// tile), the worker's first claim.
+template <typename WT, int KMAX>
+__device__ __forceinline__ void step_start(const Params& P, Smem<WT, KMAX>& sm, int lane, int first) {
+  if (lane < P.B) {
+    const int32_t p = ld_sc1(&P.seq_len[lane]);
+    int32_t tk = ld_sc1(&P.tokens[lane]);
+    if (tk < 0 || tk >= P.V) {
+      if (p >= 0) latch_error(P, WPK_E_TOKEN, -1);
+      tk = 0;
+    }
+    sm.pos[lane] = p;
+    sm.tok[lane] = tk;
+  }
+  if (lane == 0) {
+    sm.first = first;
+    sm.stop = 0;
+  }
+}
+
+// The worker loop: claim (from this worker's queue, in topological order),
+// stage the tile's weights, wait for its counter group, run it, publish.
+template <typename WT, int CPR_H, int CPR_F, bool LOG>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void megakernel(Params P) {
+  constexpr int KMAX = kmax<CPR_H, CPR_F, WT>();
+  __shared__ Smem<WT, KMAX> sm;
+  const int t = wpk_tid(), lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int q = (int)blockIdx.x % P.n_queues;
+  const int qb = cload(P.queue_off, q), qn = cload(P.queue_off, q + 1) - qb;
+  uint32_t* head = P.heads + (size_t)q * kLine;
+  uint32_t epoch = 0;
+  const uint64_t t_entry = LOG ? __builtin_amdgcn_s_memrealtime() : 0;
+  if (wave == 0) {
+    epoch = ld_sc1(&P.ctl[CTL_EPOCH]);
+    const bool dead = ld_sc1(&P.ctl[CTL_STATUS]) != 0u;
+    int first = 0;
+    if (lane == 0) first = dead ? qn : (int)atomic_add(head, 1u);
+    step_start<WT>(P, sm, lane, first);
+  }
   __syncthreads();
+  const int cur = __builtin_amdgcn_readfirstlane(sm.first);
+  if (wave == 0) control_loop<WT, CPR_H, CPR_F, LOG>(P, sm, cur, qb, qn, head, epoch, lane);
+  else compute_loop<WT, CPR_H, CPR_F, LOG>(P, sm, cur, qb, qn, t - 64);
+  // leave the step; the last worker out rewinds the queues and advances the epoch
+  __syncthreads();
+  if (LOG && t == 0) {
+    // worker record after the tile records: hardware placement, residency span
+    int32_t* rec = P.log + ((size_t)P.n_tiles + blockIdx.x) * 8;
+    rec[0] = (int32_t)__builtin_amdgcn_s_getreg((31 << 11) | 4);   // HW_ID: wave, SIMD, CU, SE
+    rec[1] = (int32_t)__builtin_amdgcn_s_getreg((31 << 11) | 20);  // XCC_ID
+    rec[2] = (int32_t)blockIdx.x;
+    rec[3] = 0;
+    *(uint64_t*)(rec + 4) = t_entry;
+    *(uint64_t*)(rec + 6) = __builtin_amdgcn_s_memrealtime();
+  }
   if (t == 0) {
     const uint32_t old = atomic_add(&P.ctl[CTL_EXIT], 1u);
     if (old == (uint32_t)P.n_workers - 1u) {
@@ -783,16 +1093,40 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   }
 }
 
-// One operator of the conventional baseline: one workgroup per tile, no
-// counters; kernel boundaries order the operators.
+// One operator of the conventional baseline: one workgroup per tile, the same
+// tile bodies and roles, no counters; kernel boundaries order the operators.
 template <typename WT, int CPR_H, int CPR_F>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void phase_kernel(Params P, int first) {
-  __shared__ Smem<WT> sm;
-  const int id = first + (int)blockIdx.x;
-  const Tile T = cload(P.tiles, id);
-  Slot s;
-  stage<WT, CPR_H, CPR_F>(P, T, s);
-  run_tile<WT, CPR_H, CPR_F>(P, T, s, sm);
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void phase_kernel(Params P, int first) {
+  constexpr int KMAX = kmax<CPR_H, CPR_F, WT>();
+  __shared__ Smem<WT, KMAX> sm;
+  const int t = wpk_tid(), lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const Tile T = cload(P.tiles, first + (int)blockIdx.x);
+  if (wave == 0) step_start<WT>(P, sm, lane, 0);
+  __syncthreads();
+  const int npairs = is_gemv(T.type) ? P.B : 1;
+  // the roles never share registers: the slot is live only in the compute waves
+  if (wave == 0) {
+    int xkey = -1;
+    for (int b = 0; b < npairs; ++b) {
+      const EpiIn e = ctl_pre<WT, CPR_H, CPR_F>(P, T, b, sm, lane, xkey);
+      __syncthreads();  // A
+      __syncthreads();  // B
+      ctl_post<WT, CPR_H, CPR_F>(P, T, b, sm, e, lane);
+    }
+  } else {
+    const int tc = t - 64;
+    Slot s;
+#pragma unroll
+    for (int j = 0; j < kChunks; ++j) s.c[j] = u32x4{0u, 0u, 0u, 0u};
+    stage<WT, CPR_H, CPR_F>(P, T, s, (uint32_t)tc * 16u);
+    for (int b = 0; b < npairs; ++b) {
+      if (T.type == T_ATTN && attn_count(P, T, sm.pos[T.b]) > 0) dump_kv<WT>(P, T, s, sm, tc);
+      __syncthreads();  // A
+      launder(s);
+      compute<WT, CPR_H, CPR_F>(P, T, s, sm, tc);
+      __syncthreads();  // B
+    }
+  }
 }
 
 }  // namespace wpk
@@ -808,10 +1142,13 @@ extern "C" int wpk_dev_kernels(int dtype, int cpr_h, int cpr_f, const void** mk,
     *phase = reinterpret_cast<const void*>(&phase_kernel<WT, H, F>);            \
     return 1;                                                                   \
   }
-  WPK_INST(WPK_F32, float, 64, 256)      // tiny: hidden 256, ffn 1024, f32
-  WPK_INST(WPK_BF16, uint16_t, 256, 1024)  // Llama-3.2-1B shape: hidden 2048, ffn 8192, bf16
-  WPK_INST(WPK_BF16, uint16_t, 64, 128)  // hidden 512, ffn 1024, bf16
-  WPK_INST(WPK_BF16, uint16_t, 64, 256)  // hidden 512, ffn 2048, bf16
+  WPK_INST(WPK_F32, float, 64, 256)        // hidden 256, ffn 1024, f32 (tiny)
+  WPK_INST(WPK_BF16, uint16_t, 256, 1024)  // hidden 2048, ffn 8192, bf16 (Llama-3.2-1B shape)
+  WPK_INST(WPK_BF16, uint16_t, 64, 128)    // hidden 512, ffn 1024, bf16
+  WPK_INST(WPK_BF16, uint16_t, 64, 256)    // hidden 512, ffn 2048, bf16
 #undef WPK_INST
   return 0;
 }
+
+// Threads per worker the kernels are built for (one control wave + compute waves).
+extern "C" int wpk_dev_block_threads() { return wpk::kBlock; }

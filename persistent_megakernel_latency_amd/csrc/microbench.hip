@@ -15,6 +15,7 @@
 // wall-clock budget read from s_memrealtime (100 MHz), so no kernel here can
 // spin forever.
 #include <hip/hip_runtime.h>
+#include <algorithm>
 
 #include <chrono>
 #include <cstdio>
@@ -259,6 +260,128 @@ __global__ void k_latency(uint32_t* p, uint32_t words, int iters, int aux, int m
   out[1] = idx;
 }
 
+// ---- residency: how many workgroups of a given size and LDS / VGPR / SGPR
+// footprint the dispatcher keeps on the GPU at once.  Every wave stays until
+// the block's end (all threads spin, then a barrier); thread 0 records when
+// the block ran and the host counts the largest number of overlapping blocks.
+#define WPK_CLOBBER_V128 "v0","v1","v2","v3","v4","v5","v6","v7","v8","v9","v10","v11","v12","v13","v14","v15","v16","v17","v18","v19","v20","v21","v22","v23","v24","v25","v26","v27","v28","v29","v30","v31","v32","v33","v34","v35","v36","v37","v38","v39","v40","v41","v42","v43","v44","v45","v46","v47","v48","v49","v50","v51","v52","v53","v54","v55","v56","v57","v58","v59","v60","v61","v62","v63","v64","v65","v66","v67","v68","v69","v70","v71","v72","v73","v74","v75","v76","v77","v78","v79","v80","v81","v82","v83","v84","v85","v86","v87","v88","v89","v90","v91","v92","v93","v94","v95","v96","v97","v98","v99","v100","v101","v102","v103","v104","v105","v106","v107","v108","v109","v110","v111","v112","v113","v114","v115","v116","v117","v118","v119"
+#define WPK_CLOBBER_V148 "v0","v1","v2","v3","v4","v5","v6","v7","v8","v9","v10","v11","v12","v13","v14","v15","v16","v17","v18","v19","v20","v21","v22","v23","v24","v25","v26","v27","v28","v29","v30","v31","v32","v33","v34","v35","v36","v37","v38","v39","v40","v41","v42","v43","v44","v45","v46","v47","v48","v49","v50","v51","v52","v53","v54","v55","v56","v57","v58","v59","v60","v61","v62","v63","v64","v65","v66","v67","v68","v69","v70","v71","v72","v73","v74","v75","v76","v77","v78","v79","v80","v81","v82","v83","v84","v85","v86","v87","v88","v89","v90","v91","v92","v93","v94","v95","v96","v97","v98","v99","v100","v101","v102","v103","v104","v105","v106","v107","v108","v109","v110","v111","v112","v113","v114","v115","v116","v117","v118","v119","v120","v121","v122","v123","v124","v125","v126","v127","v128","v129","v130","v131","v132","v133","v134","v135","v136","v137","v138","v139","v140","v141","v142","v143","v144","v145","v146","v147"
+#define WPK_CLOBBER_S100 "s8","s9","s10","s11","s12","s13","s14","s15","s16","s17","s18","s19","s20","s21","s22","s23","s24","s25","s26","s27","s28","s29","s30","s31","s32","s33","s34","s35","s36","s37","s38","s39","s40","s41","s42","s43","s44","s45","s46","s47","s48","s49","s50","s51","s52","s53","s54","s55","s56","s57","s58","s59","s60","s61","s62","s63","s64","s65","s66","s67","s68","s69","s70","s71","s72","s73","s74","s75","s76","s77","s78","s79","s80","s81","s82","s83","s84","s85","s86","s87","s88","s89","s90","s91","s92","s93","s94","s95","s96","s97","s98","s99"
+template <int NT, int LDSB, int VG, bool SG>
+__global__ __launch_bounds__(NT) void k_resid(unsigned long long* out, int spin_ticks, int salt) {
+  __shared__ float buf[LDSB / 4];
+  for (int i = threadIdx.x; i < LDSB / 4; i += NT) buf[i] = (float)(i + salt);
+  if (VG == 128) asm volatile("" ::: WPK_CLOBBER_V128);
+  if (VG == 148) asm volatile("" ::: WPK_CLOBBER_V148);
+  if (SG) asm volatile("" ::: WPK_CLOBBER_S100);
+  __syncthreads();
+  const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+  while (__builtin_amdgcn_s_memrealtime() - t0 < (unsigned long long)spin_ticks) __builtin_amdgcn_s_sleep(10);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned long long t1 = __builtin_amdgcn_s_memrealtime();
+    out[2 * blockIdx.x] = t0;
+    out[2 * blockIdx.x + 1] = t1 + (unsigned long long)(buf[(salt & 63) + 1] > 1e30f);
+  }
+}
+
+template <int NT, int LDSB, int VG, bool SG>
+static void resid_case(unsigned long long* d_out, int blocks) {
+  const int spin = 3000;  // 30 us at 100 MHz
+  void* fn = reinterpret_cast<void*>(&k_resid<NT, LDSB, VG, SG>);
+  int per_cu = 0;
+  CHECK(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, NT, 0));
+  int salt = 0;
+  void* args[] = {&d_out, (void*)&spin, &salt};
+  const hipError_t e = hipLaunchCooperativeKernel(fn, dim3(blocks), dim3(NT), args, 0, 0);
+  if (e != hipSuccess) {
+    printf("{\"bench\": \"residency\", \"threads\": %d, \"lds\": %d, \"vgprs\": %d, \"sgpr100\": %d, \"blocks\": %d, "
+           "\"occupancy_api_per_cu\": %d, \"error\": \"%s\"}\n", NT, LDSB, VG, (int)SG, blocks, per_cu, hipGetErrorString(e));
+    fflush(stdout);
+    (void)hipGetLastError();
+    return;
+  }
+  CHECK(hipDeviceSynchronize());
+  CHECK(hipGetLastError());
+  std::vector<unsigned long long> h(2 * (size_t)blocks);
+  CHECK(hipMemcpy(h.data(), d_out, h.size() * 8, hipMemcpyDeviceToHost));
+  std::vector<std::pair<unsigned long long, int>> ev;
+  for (int b = 0; b < blocks; ++b) {
+    ev.push_back({h[2 * b], 1});
+    ev.push_back({h[2 * b + 1], -1});
+  }
+  std::sort(ev.begin(), ev.end(), [](const std::pair<unsigned long long, int>& a, const std::pair<unsigned long long, int>& b) {
+    return a.first != b.first ? a.first < b.first : a.second < b.second;
+  });
+  int cur = 0, best = 0;
+  for (auto& x : ev) best = std::max(best, cur += x.second);
+  printf("{\"bench\": \"residency\", \"threads\": %d, \"lds\": %d, \"vgprs\": %d, \"sgpr100\": %d, \"blocks\": %d, "
+         "\"occupancy_api_per_cu\": %d, \"max_concurrent\": %d}\n", NT, LDSB, VG, (int)SG, blocks, per_cu, best);
+  fflush(stdout);
+}
+
+// ---- poll storm: blocks 1.. poll (device-scope loads, each waiting for the
+// previous) one of n_addr counters; block 0 meanwhile does dependent
+// atomic adds on counter 0.  out[b] = ticks for the block's loop.
+__global__ void k_poll(unsigned* ctr, int iters, int n_addr, int with_atomic, unsigned long long* out, unsigned* sink) {
+  if (threadIdx.x != 0) return;
+  const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+  unsigned s = 0;
+  if (blockIdx.x == 0 && with_atomic) {
+    for (int i = 0; i < iters; ++i) s += __hip_atomic_fetch_add(ctr + (s & 0u), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else if (blockIdx.x != 0) {
+    unsigned* c = ctr + (size_t)(blockIdx.x % n_addr) * 64;
+    for (int i = 0; i < iters; ++i) s += __hip_atomic_load(c + (s & 0u), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  out[blockIdx.x] = __builtin_amdgcn_s_memrealtime() - t0;
+  sink[blockIdx.x] = s;
+}
+
+// ---- ping-pong under load: blocks 0 and 1 (64 threads, on different XCDs)
+// bounce a counter with relaxed device-scope atomic adds and polls, the
+// publish/poll pair of the megakernel's protocol; blocks 2.. (256 threads)
+// stream 64 KiB tiles with non-temporal loads until block 0 finishes.
+// out[0] = ticks for `iters` round trips, out[1] = 1 if a wait ran out.
+__global__ __launch_bounds__(256) void k_pp_loaded(unsigned* ctr, int iters, const uint4* src, long n_tiles,
+                                                   unsigned long long* out, unsigned* sink) {
+  const int t = threadIdx.x;
+  if (blockIdx.x < 2) {
+    if (t != 0) return;
+    const bool first = blockIdx.x == 0;
+    unsigned* mine = ctr + (first ? 0 : 64);
+    unsigned* theirs = ctr + (first ? 64 : 0);
+    const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+    bool timed_out = false;
+    for (int i = 1; i <= iters && !timed_out; ++i) {
+      if (first) __hip_atomic_fetch_add(mine, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const unsigned long long w0 = __builtin_amdgcn_s_memrealtime();
+      while (__hip_atomic_load(theirs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (unsigned)i) {
+        if (__builtin_amdgcn_s_memrealtime() - w0 > kSpinBudgetTicks) { timed_out = true; break; }
+      }
+      if (!first) __hip_atomic_fetch_add(mine, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (first) {
+      out[0] = __builtin_amdgcn_s_memrealtime() - t0;
+      out[1] = timed_out ? 1 : 0;
+      __hip_atomic_store(ctr + 128, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // streamers stop
+    }
+    return;
+  }
+  uint32_t acc = 0;
+  const long nb = gridDim.x - 2;
+  for (long tile = blockIdx.x - 2; tile < n_tiles; tile += nb) {
+    if (__hip_atomic_load(ctr + 128, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) break;
+    const u32x4* p = reinterpret_cast<const u32x4*>(src) + tile * 4096;
+    u32x4 v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = __builtin_nontemporal_load(p + j * 256 + t);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+    if (tile + nb >= n_tiles) tile = blockIdx.x - 2 - nb;  // wrap around until told to stop
+  }
+  if (acc == 0x9e3779b9u) sink[blockIdx.x * blockDim.x + t] = acc;
+}
+
 static double time_ms(hipEvent_t a, hipEvent_t b) {
   float ms = 0;
   CHECK(hipEventElapsedTime(&ms, a, b));
@@ -296,6 +419,68 @@ int main(int argc, char** argv) {
   CHECK(hipMemset(xvec, 0, 8192));
   CHECK(hipMalloc(&results, sizeof(float) * 16 * 8192));
   const std::string which = argc > 1 ? argv[1] : "all";
+  if (which == "poll") {
+    const int blocks = 513, iters = 2000;
+    unsigned long long* d_out = nullptr;
+    unsigned* ctr = nullptr;
+    unsigned* snk = nullptr;
+    CHECK(hipMalloc(&d_out, sizeof(unsigned long long) * blocks));
+    CHECK(hipMalloc(&ctr, sizeof(unsigned) * 64 * 256));
+    CHECK(hipMalloc(&snk, sizeof(unsigned) * blocks));
+    CHECK(hipMemset(ctr, 0, sizeof(unsigned) * 64 * 256));
+    for (int with_atomic : {0, 1})
+      for (int n_addr : {1, 4, 16, 64, 256}) {
+        hipLaunchKernelGGL(k_poll, dim3(blocks), dim3(64), 0, 0, ctr, iters, n_addr, with_atomic, d_out, snk);
+        CHECK(hipDeviceSynchronize());
+        CHECK(hipGetLastError());
+        std::vector<unsigned long long> h(blocks);
+        CHECK(hipMemcpy(h.data(), d_out, sizeof(unsigned long long) * blocks, hipMemcpyDeviceToHost));
+        double poll = 0;
+        for (int b = 1; b < blocks; ++b) poll += (double)h[b];
+        poll = poll / (blocks - 1) * 10.0 / iters;  // ns per dependent poll
+        printf("{\"bench\": \"poll_storm\", \"pollers\": %d, \"addresses\": %d, \"with_atomic\": %d, "
+               "\"ns_per_poll\": %.1f, \"atomic_ns\": %.1f, \"polls_per_s_per_address\": %.3g}\n",
+               blocks - 1, n_addr, with_atomic, poll, with_atomic ? h[0] * 10.0 / iters : 0.0,
+               (blocks - 1) / (double)n_addr / (poll * 1e-9));
+        fflush(stdout);
+      }
+    CHECK(hipFree(d_out));
+    CHECK(hipFree(ctr));
+    CHECK(hipFree(snk));
+    return 0;
+  }
+  if (which == "resid") {
+    unsigned long long* d_out = nullptr;
+    CHECK(hipMalloc(&d_out, sizeof(unsigned long long) * 2 * 4 * n_cu));
+    resid_case<320, 16384, 0, false>(d_out, 2 * n_cu);
+    resid_case<320, 53840, 148, true>(d_out, 2 * n_cu);
+    resid_case<320, 53840, 128, true>(d_out, 2 * n_cu);
+    resid_case<320, 16384, 148, false>(d_out, 2 * n_cu);
+    resid_case<256, 53840, 148, true>(d_out, 2 * n_cu);
+    resid_case<576, 53840, 148, true>(d_out, n_cu);
+    resid_case<576, 53840, 128, true>(d_out, n_cu);
+    resid_case<320, 16384, 128, false>(d_out, 3 * n_cu);
+    CHECK(hipFree(d_out));
+    return 0;
+  }
+  if (which == "ppload") {
+    unsigned long long* d_out = nullptr;
+    CHECK(hipMalloc(&d_out, sizeof(unsigned long long) * 2));
+    for (int streamers : {0, 256, 512, 768}) {
+      CHECK(hipMemset(counters, 0, 4096 * sizeof(unsigned)));
+      const int iters = 2000;
+      hipLaunchKernelGGL(k_pp_loaded, dim3(2 + streamers), dim3(256), 0, 0, counters, iters, src, n_tiles, d_out, sink);
+      CHECK(hipDeviceSynchronize());
+      CHECK(hipGetLastError());
+      unsigned long long h[2];
+      CHECK(hipMemcpy(h, d_out, sizeof(h), hipMemcpyDeviceToHost));
+      printf("{\"bench\": \"pingpong_under_load\", \"streaming_blocks\": %d, \"round_trip_ns\": %.1f, \"timed_out\": %llu}\n",
+             streamers, h[0] * 10.0 / iters, h[1]);
+      fflush(stdout);
+    }
+    CHECK(hipFree(d_out));
+    return 0;
+  }
   const int per_cu[] = {1, 2, 4, 8};
   for (int mode : {0, 1, 2, 3, 4, 8, 16, 32, 24, 40}) {
     if (which != "all" && which != "read") break;

@@ -126,7 +126,8 @@ struct Params {
   uint32_t* heads;          // claim head of each queue, stride kLine
   uint32_t* ctl;            // control block
   unsigned long long* argmax;  // [B][kArgmaxShards] packed (value, index) maxima
-  int32_t* log;             // wpk_log_rec per tile (8 int32 each)
+  int32_t* log;             // wpk_log_rec per tile, then per worker slot, then per-tile timings
+  int32_t log_workers;      // worker record slots in the log (co-resident maximum)
   int32_t log_on, prefetch, drop_tile;
   uint32_t perturb;
   uint64_t watchdog_ticks;  // s_memrealtime ticks (100 MHz)

@@ -885,7 +885,7 @@ __device__ __forceinline__ uint32_t hash32(uint32_t x) {
 
 template <typename WT, int CPR_H, int CPR_F, bool LOG, int KMAX>
 __device__ __forceinline__ void control_loop(const Params& P, Smem<WT, KMAX>& sm, int cur, int qb, int qn,
-                                             uint32_t* head, uint32_t epoch, int lane0) {
+                                             uint32_t epoch, int lane0) {
   int it = 0;
   int done_group = -1;  // a group already seen complete this step (groups never un-complete)
   int xkey = -1;        // which activation row sm.xs holds
@@ -896,19 +896,13 @@ __device__ __forceinline__ void control_loop(const Params& P, Smem<WT, KMAX>& sm
     const uint64_t t_claim = LOG ? __builtin_amdgcn_s_memrealtime() : 0;
     const int id = cload(P.queue, qb + cur);
     const Tile T = cload(P.tiles, id);
-    uint32_t nx = 0;
-    if (lane == 0) nx = atomic_add(head, 1u);
     int32_t delta = 0;
     bool ok = true;
     if (T.wait >= 0 && (LOG || T.wait != done_group)) {
       ok = wait_group(P, T, epoch, &delta, lane);
       if (ok) done_group = T.wait;
     }
-    nx = __shfl(nx, 0);
-    if (lane == 0) {
-      sm.ids[(it + 1) & 1] = (int)nx;
-      sm.stop = ok ? 0 : 1;
-    }
+    if (lane == 0) sm.stop = ok ? 0 : 1;
     if (!ok) {
       __syncthreads();  // A
       __syncthreads();  // B
@@ -960,7 +954,8 @@ __device__ __forceinline__ void control_loop(const Params& P, Smem<WT, KMAX>& sm
         atomic_add(&P.counters[(size_t)(G.shard0 + T.shard) * kLine], 1u);
       }
     }
-    cur = (int)nx;
+    // the next claim, written by compute wave 1 before this tile's barrier B
+    cur = __builtin_amdgcn_readfirstlane(sm.ids[(it + 1) & 1]);
     ++it;
   }
 }
@@ -976,7 +971,8 @@ __device__ __forceinline__ void launder(Slot& s) {
 }
 
 template <typename WT, int CPR_H, int CPR_F, bool LOG, int KMAX>
-__device__ __forceinline__ void compute_loop(const Params& P, Smem<WT, KMAX>& sm, int cur, int qb, int qn, int tc0) {
+__device__ __forceinline__ void compute_loop(const Params& P, Smem<WT, KMAX>& sm, int cur, int qb, int qn,
+                                             uint32_t* head, int tc0) {
   const uint32_t voff = (uint32_t)tc0 * 16u;
   Slot s;
 #pragma unroll
@@ -989,6 +985,12 @@ __device__ __forceinline__ void compute_loop(const Params& P, Smem<WT, KMAX>& sm
     // epilogue): stage this tile's weights; they stream in while the control
     // wave publishes, claims, waits for the tile's inputs and stages them.
     const Tile T = cload(P.tiles, cload(P.queue, qb + nx));
+    // Claim the next tile here rather than in the control wave: a wave's
+    // memory operations complete in issue order, so an atomic (slow while the
+    // weights stream) would hold up every later wait of the control wave,
+    // while here it returns ahead of the weights this wave waits for anyway.
+    uint32_t ahead = 0;
+    if (tc0 == 0) ahead = atomic_add(head, 1u);
     stage<WT, CPR_H, CPR_F>(P, T, s, voff);
     ++it;
     const int tc = opaque(tc0);
@@ -1008,6 +1010,7 @@ __device__ __forceinline__ void compute_loop(const Params& P, Smem<WT, KMAX>& sm
           __hip_atomic_fetch_max(&sm.t_ready, (uint64_t)__builtin_amdgcn_s_memrealtime(), __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_WORKGROUP);
       }
+      if (b == 0 && tc == 0) sm.ids[(it + 1) & 1] = (int)ahead;  // for the control wave, read after B
       launder(s);
       compute<WT, CPR_H, CPR_F>(P, T, s, sm, tc);
       if (LOG && (tc & 63) == 0)
@@ -1063,14 +1066,15 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
   if (wave == 0) {
     epoch = ld_sc1(&P.ctl[CTL_EPOCH]);
     const bool dead = ld_sc1(&P.ctl[CTL_STATUS]) != 0u;
+    // the first claim; compute wave 1 then claims each next tile
     int first = 0;
     if (lane == 0) first = dead ? qn : (int)atomic_add(head, 1u);
     step_start<WT>(P, sm, lane, first);
   }
   __syncthreads();
   const int cur = __builtin_amdgcn_readfirstlane(sm.first);
-  if (wave == 0) control_loop<WT, CPR_H, CPR_F, LOG>(P, sm, cur, qb, qn, head, epoch, lane);
-  else compute_loop<WT, CPR_H, CPR_F, LOG>(P, sm, cur, qb, qn, t - 64);
+  if (wave == 0) control_loop<WT, CPR_H, CPR_F, LOG>(P, sm, cur, qb, qn, epoch, lane);
+  else compute_loop<WT, CPR_H, CPR_F, LOG>(P, sm, cur, qb, qn, head, t - 64);
   // leave the step; the last worker out rewinds the queues and advances the epoch
   __syncthreads();
   if (LOG && t == 0) {

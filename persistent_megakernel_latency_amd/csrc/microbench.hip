@@ -342,6 +342,15 @@ __global__ void k_poll(unsigned* ctr, int iters, int n_addr, int with_atomic, un
 // publish/poll pair of the megakernel's protocol; blocks 2.. (256 threads)
 // stream 64 KiB tiles with non-temporal loads until block 0 finishes.
 // out[0] = ticks for `iters` round trips, out[1] = 1 if a wait ran out.
+// A scalar load that misses the scalar cache (glc), waited in the same asm
+// statement: a poll that does not queue behind the vector memory pipeline.
+__device__ __forceinline__ unsigned sload_glc(const unsigned* p) {
+  unsigned v;
+  asm volatile("s_load_dword %0, %1, 0x0 glc\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  return v;
+}
+
+template <bool SCALAR_POLL>
 __global__ __launch_bounds__(256) void k_pp_loaded(unsigned* ctr, int iters, const uint4* src, long n_tiles,
                                                    unsigned long long* out, unsigned* sink) {
   const int t = threadIdx.x;
@@ -355,7 +364,8 @@ __global__ __launch_bounds__(256) void k_pp_loaded(unsigned* ctr, int iters, con
     for (int i = 1; i <= iters && !timed_out; ++i) {
       if (first) __hip_atomic_fetch_add(mine, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const unsigned long long w0 = __builtin_amdgcn_s_memrealtime();
-      while (__hip_atomic_load(theirs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (unsigned)i) {
+      while ((SCALAR_POLL ? sload_glc(theirs) : __hip_atomic_load(theirs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) <
+             (unsigned)i) {
         if (__builtin_amdgcn_s_memrealtime() - w0 > kSpinBudgetTicks) { timed_out = true; break; }
       }
       if (!first) __hip_atomic_fetch_add(mine, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -466,16 +476,20 @@ int main(int argc, char** argv) {
   if (which == "ppload") {
     unsigned long long* d_out = nullptr;
     CHECK(hipMalloc(&d_out, sizeof(unsigned long long) * 2));
+    for (int scalar : {0, 1})
     for (int streamers : {0, 256, 512, 768}) {
       CHECK(hipMemset(counters, 0, 4096 * sizeof(unsigned)));
       const int iters = 2000;
-      hipLaunchKernelGGL(k_pp_loaded, dim3(2 + streamers), dim3(256), 0, 0, counters, iters, src, n_tiles, d_out, sink);
+      if (scalar)
+        hipLaunchKernelGGL(k_pp_loaded<true>, dim3(2 + streamers), dim3(256), 0, 0, counters, iters, src, n_tiles, d_out, sink);
+      else
+        hipLaunchKernelGGL(k_pp_loaded<false>, dim3(2 + streamers), dim3(256), 0, 0, counters, iters, src, n_tiles, d_out, sink);
       CHECK(hipDeviceSynchronize());
       CHECK(hipGetLastError());
       unsigned long long h[2];
       CHECK(hipMemcpy(h, d_out, sizeof(h), hipMemcpyDeviceToHost));
-      printf("{\"bench\": \"pingpong_under_load\", \"streaming_blocks\": %d, \"round_trip_ns\": %.1f, \"timed_out\": %llu}\n",
-             streamers, h[0] * 10.0 / iters, h[1]);
+      printf("{\"bench\": \"pingpong_under_load\", \"poll\": \"%s\", \"streaming_blocks\": %d, \"round_trip_ns\": %.1f, \"timed_out\": %llu}\n",
+             scalar ? "scalar_glc" : "vector_sc1", streamers, h[0] * 10.0 / iters, h[1]);
       fflush(stdout);
     }
     CHECK(hipFree(d_out));

@@ -954,6 +954,7 @@ __device__ __forceinline__ void control_loop(const Params& P, Smem<WT, KMAX>& sm
         atomic_add(&P.counters[(size_t)(G.shard0 + T.shard) * kLine], 1u);
       }
     }
+    __syncthreads();  // C: published; the compute waves may load the next tile
     // the next claim, written by compute wave 1 before this tile's barrier B
     cur = __builtin_amdgcn_readfirstlane(sm.ids[(it + 1) & 1]);
     ++it;
@@ -1023,6 +1024,7 @@ __device__ __forceinline__ void compute_loop(const Params& P, Smem<WT, KMAX>& sm
     // above it would keep two slots live.
     __builtin_amdgcn_sched_barrier(0);
     nx = __builtin_amdgcn_readfirstlane(sm.ids[(it + 1) & 1]);
+    __syncthreads();  // C
   }
 }
 

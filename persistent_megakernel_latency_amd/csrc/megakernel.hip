@@ -61,18 +61,25 @@ struct Slot {
 template <typename WT>
 struct WT_ {
   static constexpr int EPC = 16 / sizeof(WT);              // elements per 16-byte chunk
-  static constexpr int PITCH = sizeof(WT) == 2 ? 66 : 65;  // LDS row pitch of a K/V chunk (conflict-free)
+  // LDS pitch (elements) of K rows [position][dim] and of transposed V rows
+  // [dim][position]: 16-byte aligned rows, so each lane reads its row with
+  // 16-byte loads (8 lanes of a pass cover all 32 banks)
+  static constexpr int KP = sizeof(WT) == 2 ? 72 : 68;
 };
 
 template <typename WT, int KMAX>
-struct Smem {
-  float xs[KMAX];                              // activation row of the current GEMV tile
+struct alignas(16) Smem {
+  union alignas(16) {
+    float xs[KMAX];  // activation row of the current GEMV tile
+    struct {
+      WT ks[kAttnChunk * WT_<WT>::KP];  // attention tiles: K chunk, row per position
+      WT vt[kHeadDim * WT_<WT>::KP];    // V chunk transposed, row per head dimension
+    };
+  };
   float red[kWaves][64];                       // per compute wave partial row sums
   float outs[kMaxGroupHeads][kHeadDim + 2];    // attention partial (m, l, o) per q head
-  float qs[kMaxGroupHeads][kHeadDim];
-  float ps[kMaxGroupHeads][kAttnChunk];
-  WT ks[kAttnChunk * WT_<WT>::PITCH];
-  WT vs[kAttnChunk * WT_<WT>::PITCH];
+  alignas(16) float qs[kMaxGroupHeads][kHeadDim];
+  alignas(16) float ps[kMaxGroupHeads][kAttnChunk];
   int pos[kMaxBatch];  // seq_len of each sequence at step start
   int tok[kMaxBatch];  // input token of each sequence (validated)
   int ids[2];          // claim index of the next tile, by iteration parity
@@ -399,24 +406,27 @@ template <typename WT, int KMAX>
 __device__ __forceinline__ void dump_kv(const Params& P, const Tile& T, const Slot& s, Smem<WT, KMAX>& sm, int tc0) {
   const int tc = opaque(tc0);
   constexpr int CPP = kHeadDim * sizeof(WT) / 16, KCH = kAttnChunk * CPP, EPC = WT_<WT>::EPC;
-  constexpr int PITCH = WT_<WT>::PITCH;
+  constexpr int KP = WT_<WT>::KP;
   const int p = sm.pos[T.b];
   const int skip = p - T.c * kAttnChunk;
 #pragma unroll
   for (int j = 0; j < 2 * KCH / kThreads; ++j) {
     const int flat = j * kThreads + tc;
-    const bool isv = flat >= KCH;
+    const bool isv = flat >= KCH;  // uniform per j
     const int f = isv ? flat - KCH : flat;
     const int pos = f / CPP, dc = f % CPP;
     if (pos == skip) continue;
-    WT* dst = (isv ? sm.vs : sm.ks) + pos * PITCH + dc * EPC;
-    if (sizeof(WT) == 2) {
-      uint32_t* d32 = (uint32_t*)dst;  // row pitch 132 B keeps 4-byte alignment
-      d32[0] = s.c[j].x; d32[1] = s.c[j].y; d32[2] = s.c[j].z; d32[3] = s.c[j].w;
+    if (!isv) {
+      *(u32x4*)(sm.ks + pos * KP + dc * EPC) = s.c[j];
     } else {
-      float* d = (float*)dst;
-      d[0] = __uint_as_float(s.c[j].x); d[1] = __uint_as_float(s.c[j].y);
-      d[2] = __uint_as_float(s.c[j].z); d[3] = __uint_as_float(s.c[j].w);
+      float w[EPC];
+      unpack<WT>(s.c[j], w);
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        WT* d = sm.vt + (dc * EPC + e) * KP + pos;
+        if (sizeof(WT) == 2) *(uint16_t*)d = (uint16_t)(__float_as_uint(w[e]) >> 16);
+        else *(float*)d = w[e];
+      }
     }
   }
 }
@@ -432,40 +442,50 @@ __device__ __forceinline__ int attn_count(const Params& P, const Tile& T, int p)
 template <typename WT, int KMAX>
 __device__ __forceinline__ void cmp_attn(const Params& P, const Tile& T, Smem<WT, KMAX>& sm, int tc0) {
   const int tc = opaque(tc0);
-  constexpr int PITCH = WT_<WT>::PITCH;
+  constexpr int KP = WT_<WT>::KP, EPC = WT_<WT>::EPC;
   const int lane = tc & 63, h = tc >> 6;
   const int cnt = attn_count(P, T, sm.pos[T.b]);
   if (h >= P.G || cnt == 0) return;
   float sc = -INFINITY;
   if (lane < cnt) {
-    const WT* kr = sm.ks + lane * PITCH;
-    float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
+    const WT* kr = sm.ks + lane * KP;
+    float d0 = 0.f, d1 = 0.f;
 #pragma unroll
-    for (int d = 0; d < kHeadDim; d += 4) {
-      const f32x4 q = *(const f32x4*)&sm.qs[h][d];
-      d0 = fmaf(q.x, elt<WT>(kr, d), d0);
-      d1 = fmaf(q.y, elt<WT>(kr, d + 1), d1);
-      d2 = fmaf(q.z, elt<WT>(kr, d + 2), d2);
-      d3 = fmaf(q.w, elt<WT>(kr, d + 3), d3);
+    for (int d = 0; d < kHeadDim; d += EPC) {
+      float k[EPC];
+      unpack<WT>(*(const u32x4*)(kr + d), k);
+#pragma unroll
+      for (int e = 0; e < EPC; e += 4) {
+        const f32x4 q = *(const f32x4*)&sm.qs[h][d + e];
+        d0 = fmaf(q.x, k[e], d0);
+        d1 = fmaf(q.y, k[e + 1], d1);
+        d0 = fmaf(q.z, k[e + 2], d0);
+        d1 = fmaf(q.w, k[e + 3], d1);
+      }
     }
-    sc = ((d0 + d1) + (d2 + d3)) * P.attn_scale;
+    sc = (d0 + d1) * P.attn_scale;
   }
   const float m = wave_max(sc);
   const float e = lane < cnt ? __expf(sc - m) : 0.f;
   const float l = wave_sum(e);
   sm.ps[h][lane] = e;
-  float o = 0.f;
-  for (int j0 = 0; j0 < cnt; j0 += 8) {
-    const f32x4 pa = *(const f32x4*)&sm.ps[h][j0];
-    const f32x4 pb = *(const f32x4*)&sm.ps[h][j0 + 4];
-    const float pw[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+  // weighted values: lane = head dimension, its transposed V row read 16 bytes
+  // at a time; positions past the chunk's count hold no data
+  const WT* vr = sm.vt + lane * KP;
+  float o0 = 0.f, o1 = 0.f;
+  for (int j0 = 0; j0 < cnt; j0 += EPC) {
+    float v[EPC];
+    unpack<WT>(*(const u32x4*)(vr + j0), v);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float v = elt<WT>(sm.vs + (j0 + u) * PITCH, lane);
-      o = fmaf(pw[u], j0 + u < cnt ? v : 0.f, o);  // rows past the chunk's positions hold no data
+    for (int u = 0; u < EPC; u += 4) {
+      const f32x4 pw = *(const f32x4*)&sm.ps[h][j0 + u];
+      o0 = fmaf(pw.x, j0 + u < cnt ? v[u] : 0.f, o0);
+      o1 = fmaf(pw.y, j0 + u + 1 < cnt ? v[u + 1] : 0.f, o1);
+      o0 = fmaf(pw.z, j0 + u + 2 < cnt ? v[u + 2] : 0.f, o0);
+      o1 = fmaf(pw.w, j0 + u + 3 < cnt ? v[u + 3] : 0.f, o1);
     }
   }
-  sm.outs[h][2 + lane] = o;
+  sm.outs[h][2 + lane] = o0 + o1;
   if (lane == 0) {
     sm.outs[h][0] = m;
     sm.outs[h][1] = l;
@@ -738,7 +758,7 @@ __device__ __forceinline__ void ctl_gemv_out(const Params& P, const Tile& T, int
 template <typename WT, int KMAX>
 __device__ __forceinline__ void ctl_attn_in(const Params& P, const Tile& T, Smem<WT, KMAX>& sm, int lane0) {
   const int lane = opaque(lane0);
-  constexpr int PITCH = WT_<WT>::PITCH;
+  constexpr int KP = WT_<WT>::KP;
   const int p = sm.pos[T.b];
   const int start = T.c * kAttnChunk;
   if (attn_count(P, T, p) == 0) return;
@@ -748,8 +768,8 @@ __device__ __forceinline__ void ctl_attn_in(const Params& P, const Tile& T, Smem
   for (int h = 0; h < kMaxGroupHeads; ++h) qv[h] = h < P.G ? ld_sc1(q + h * P.D + lane) : 0.f;
   if (p >= start && p < start + kAttnChunk && p < P.cap) {
     const size_t at = ((((size_t)T.layer * P.B + T.b) * P.Hkv + T.g) * P.cap + p) * kHeadDim + lane;
-    WT* kd = sm.ks + (p - start) * PITCH + lane;
-    WT* vd = sm.vs + (p - start) * PITCH + lane;
+    WT* kd = sm.ks + (p - start) * KP + lane;
+    WT* vd = sm.vt + lane * KP + (p - start);
     if (sizeof(WT) == 2) {
       *(uint16_t*)kd = ld_sc1((const uint16_t*)P.kc + at);
       *(uint16_t*)vd = ld_sc1((const uint16_t*)P.vc + at);
@@ -833,6 +853,7 @@ __device__ __forceinline__ EpiIn ctl_pre(const Params& P, const Tile& T, int b, 
     }
   } else if (T.type == T_ATTN) {
     ctl_attn_in<WT>(P, T, sm, lane);
+    xkey = -1;  // the K/V chunk overlays the activation row
   }
   return e;
 }

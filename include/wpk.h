@@ -142,7 +142,8 @@ const char* wpk_last_error(const wpk_plan* plan);
 #define WPK_OPT_PERTURB_SEED 3    /* != 0: sleep a pseudo-random time before each tile */
 #define WPK_OPT_DEBUG_DROP_TILE 4 /* >= 0: that tile never publishes (watchdog test) */
 #define WPK_OPT_RESET 5           /* clear the latched error, counters, queues and epoch */
-#define WPK_OPT_PREFETCH 6        /* 1 (default): stage a tile's weights before waiting on its counter */
+#define WPK_OPT_PREFETCH 6        /* 1 (default): stage a tile's weights before its inputs are complete;
+                                     0: only after (an ablation of the weight prefetch) */
 #define WPK_OPT_WORKERS 7         /* number of resident workers W (<= the built maximum) */
 int32_t wpk_set_option(wpk_plan* plan, int32_t key, int64_t value);
 

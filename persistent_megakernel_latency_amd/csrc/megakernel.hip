@@ -282,11 +282,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p) {
   return __builtin_amdgcn_make_buffer_rsrc((void*)p, 0, 0x7FFFFFFF, 0x00020000);
 }
 
-// Stages the tile's weights into the slot: chunk j of thread tc is 16 bytes at
+// Where slice j of a tile's weights is: chunk j of thread tc is 16 bytes at
 // lane offset tc*16 into slice j, a 4 KiB run of memory at a wave-uniform
-// offset.  One load site serves every tile type, so the slot is never copied
-// between code paths; the per-type work is scalar.  Each load is one buffer
-// load (resource and slice offset in scalar registers, one lane offset):
+// offset, read with one buffer load (resource and slice offset in scalar
+// registers, one lane offset):
 //  * GEMV: slice j is row (j / SPR) * SR of the tile (SR = 256 / CPR rows per
 //    slice for short rows, SPR = CPR / 256 slices per row for long ones); the
 //    device plan keeps segment boundaries and tile sizes on whole slices, so a
@@ -297,33 +296,69 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p) {
 //  * the remaining slots of an attention tile and every slot of a combine or
 //    argmax tile read one 16-byte word (no HBM traffic; the value is unused).
 template <typename WT, int CPR_H, int CPR_F>
-__device__ __forceinline__ void stage(const Params& P, const Tile& T, Slot& s, uint32_t voff) {
-  constexpr int RB = kHeadDim * (int)sizeof(WT);  // K/V bytes per position
-  constexpr int PPS = 4096 / RB;                  // positions per slice
-  constexpr int NS = kAttnChunk / PPS;            // slices of K (and of V)
-  const LayerW& lw = P.lw[T.layer];
-  const int ty = T.type;
-  const bool gemv = is_gemv(ty), attn = ty == T_ATTN;
-  const void* w0 = P.embed;
-  const void* w1 = P.embed;
-  int limit = P.V, cpr = CPR_H;
-  switch (ty) {
-    case T_QKV: w0 = w1 = lw.w_qkv; limit = P.qkv_rows; break;
-    case T_OPROJ: w0 = w1 = lw.w_o; limit = P.H; break;
-    case T_GATEUP: w0 = lw.w_gate; w1 = lw.w_up; limit = P.F; break;
-    case T_DOWN: w0 = w1 = lw.w_down; limit = P.H; cpr = CPR_F; break;
-    case T_ATTN: {
-      const size_t sl = ((((size_t)T.layer * P.B + T.b) * P.Hkv + T.g) * P.cap) * RB;
-      w0 = P.kc + sl;
-      w1 = P.vc + sl;
-      break;
+struct SliceMap {
+  static constexpr int RB = kHeadDim * (int)sizeof(WT);  // K/V bytes per position
+  static constexpr int PPS = 4096 / RB;                  // positions per slice
+  static constexpr int NS = kAttnChunk / PPS;            // slices of K (and of V)
+  __amdgpu_buffer_rsrc_t rs0, rs1;
+  bool gemv, attn;
+  int limit, sh_spr, sr, rowb;
+
+  __device__ __forceinline__ SliceMap(const Params& P, const Tile& T) {
+    const LayerW& lw = P.lw[T.layer];
+    const int ty = T.type;
+    gemv = is_gemv(ty);
+    attn = ty == T_ATTN;
+    const void* w0 = P.embed;
+    const void* w1 = P.embed;
+    limit = P.V;
+    int cpr = CPR_H;
+    switch (ty) {
+      case T_QKV: w0 = w1 = lw.w_qkv; limit = P.qkv_rows; break;
+      case T_OPROJ: w0 = w1 = lw.w_o; limit = P.H; break;
+      case T_GATEUP: w0 = lw.w_gate; w1 = lw.w_up; limit = P.F; break;
+      case T_DOWN: w0 = w1 = lw.w_down; limit = P.H; cpr = CPR_F; break;
+      case T_ATTN: {
+        const size_t sl = ((((size_t)T.layer * P.B + T.b) * P.Hkv + T.g) * P.cap) * RB;
+        w0 = P.kc + sl;
+        w1 = P.vc + sl;
+        break;
+      }
+      default: break;
     }
-    default: break;
+    rs0 = rsrc(w0);
+    rs1 = rsrc(w1);
+    sh_spr = cpr >= kThreads ? __builtin_ctz(cpr / kThreads) : 0;
+    sr = cpr >= kThreads ? 1 : kThreads / cpr;
+    rowb = cpr * 16;
   }
-  // RMSNorm gains of the columns this thread multiplies (loaded ahead of the
-  // weights, so waiting for them does not wait for the weights)
+  // slice j: its resource, its byte offset, and the largest lane offset that
+  // stays inside valid data
+  __device__ __forceinline__ void at(const Params& P, const Tile& T, int j, __amdgpu_buffer_rsrc_t& r, int& soff,
+                                     uint32_t& last) const {
+    const int row = min((j >> sh_spr) * sr, T.rows - sr);
+    const bool seg1 = row >= T.rs;
+    const int mrow = min(seg1 ? T.r1 + (row - T.rs) : T.r0 + row, limit - sr);
+    const int g_off = mrow * rowb + (j & ((1 << sh_spr) - 1)) * 4096;
+    const int p0 = min(T.c * kAttnChunk + (j % NS) * PPS, P.cap - 1);
+    const bool a_real = j < 2 * NS;
+    const int a_off = a_real ? p0 * RB : 0;
+    const uint32_t a_last = a_real ? (uint32_t)(P.cap - p0) * RB - 16u : 0u;
+    soff = gemv ? g_off : (attn ? a_off : 0);
+    last = gemv ? 0xFFFFFFF0u : (attn ? a_last : 0u);
+    r = (gemv ? seg1 : (attn && j >= NS && a_real)) ? rs1 : rs0;
+  }
+};
+
+// Stages the tile's weights into the slot, and the RMSNorm gains of the
+// columns this thread multiplies (loaded first, so waiting for them does not
+// wait for the weights).  Combine and argmax tiles read nothing of use.
+template <typename WT, int CPR_H, int CPR_F>
+__device__ __forceinline__ void stage(const Params& P, const Tile& T, Slot& s, uint32_t voff) {
   static_assert(CPR_H <= kThreads, "gains in the slot cover one chunk per thread");
   constexpr int EPC = WT_<WT>::EPC;
+  const LayerW& lw = P.lw[T.layer];
+  const int ty = T.type;
   const float* gain = ty == T_QKV ? lw.attn_norm : ty == T_GATEUP ? lw.mlp_norm : ty == T_LM ? P.final_norm : nullptr;
   if (gain) {
     const uint32_t goff = (voff / 16u % (uint32_t)CPR_H) * (EPC * 4);
@@ -333,28 +368,18 @@ __device__ __forceinline__ void stage(const Params& P, const Tile& T, Slot& s, u
   } else {
     s.g[0] = s.g[1] = u32x4{0x3f800000u, 0x3f800000u, 0x3f800000u, 0x3f800000u};
   }
-  const __amdgpu_buffer_rsrc_t rs0 = rsrc(w0), rs1 = rsrc(w1);
-  const int sh_spr = cpr >= kThreads ? __builtin_ctz(cpr / kThreads) : 0;
-  const int sr = cpr >= kThreads ? 1 : kThreads / cpr;
-  const int rowb = cpr * 16;
+  const SliceMap<WT, CPR_H, CPR_F> m(P, T);
 #pragma unroll
   for (int j = 0; j < kChunks; ++j) {
-    // GEMV slice
-    const int row = min((j >> sh_spr) * sr, T.rows - sr);
-    const bool seg1 = row >= T.rs;
-    const int mrow = min(seg1 ? T.r1 + (row - T.rs) : T.r0 + row, limit - sr);
-    const int g_off = mrow * rowb + (j & ((1 << sh_spr) - 1)) * 4096;
-    // attention slice
-    const int p0 = min(T.c * kAttnChunk + (j % NS) * PPS, P.cap - 1);
-    const bool a_real = j < 2 * NS;
-    const int a_off = a_real ? p0 * RB : 0;
-    const uint32_t a_last = a_real ? (uint32_t)(P.cap - p0) * RB - 16u : 0u;
-    const int soff = gemv ? g_off : (attn ? a_off : 0);
-    const uint32_t last = gemv ? 0xFFFFFFF0u : (attn ? a_last : 0u);
-    const bool one = gemv ? seg1 : (attn && j >= NS && a_real);
-    s.c[j] = __builtin_amdgcn_raw_buffer_load_b128(one ? rs1 : rs0, min(voff, last), soff, 2 /* nt */);
+    __amdgpu_buffer_rsrc_t r;
+    int soff;
+    uint32_t last;
+    m.at(P, T, j, r, soff, last);
+    s.c[j] = __builtin_amdgcn_raw_buffer_load_b128(r, min(voff, last), soff, 2 /* nt */);
   }
 }
+
+
 
 // Partial row sums of the staged tile against the activation row in LDS
 // (times the RMSNorm gains the slot carries, for the K = hidden operators).
@@ -904,12 +929,27 @@ __device__ __forceinline__ uint32_t hash32(uint32_t x) {
 
 // ============================ the worker loops ================================================
 
+// Publishes a worker's run of LM-head tiles at once: their logits stores and
+// argmax updates have completed, then one increment by the run's length (the
+// group counts its total over all shards, so any shard serves).
+__device__ __forceinline__ void flush_lm(const Params& P, int group, int& count, int lane) {
+  __builtin_amdgcn_s_waitcnt(0);
+  if (lane == 0) {
+    const Group G = cload(P.groups, group);
+    atomic_add(&P.counters[(size_t)(G.shard0 + (int)blockIdx.x % G.shards) * kLine], (uint32_t)count);
+  }
+  count = 0;
+}
+
 template <typename WT, int CPR_H, int CPR_F, bool LOG, int KMAX>
 __device__ __forceinline__ void control_loop(const Params& P, Smem<WT, KMAX>& sm, int cur, int qb, int qn,
                                              uint32_t epoch, int lane0) {
   int it = 0;
   int done_group = -1;  // a group already seen complete this step (groups never un-complete)
   int xkey = -1;        // which activation row sm.xs holds
+  // LM-head tiles feed only the final argmax: a worker publishes its run of
+  // them with one wait and one increment when the run ends
+  int lm_group = -1, lm_count = 0;
   while (cur < qn) {
     // lane index made opaque per tile, so per-lane address arithmetic of all
     // tile types is not hoisted out of the loop and kept live across it
@@ -917,6 +957,7 @@ __device__ __forceinline__ void control_loop(const Params& P, Smem<WT, KMAX>& sm
     const uint64_t t_claim = LOG ? __builtin_amdgcn_s_memrealtime() : 0;
     const int id = cload(P.queue, qb + cur);
     const Tile T = cload(P.tiles, id);
+    if (lm_count && T.type != T_LM) flush_lm(P, lm_group, lm_count, lane);
     int32_t delta = 0;
     bool ok = true;
     if (T.wait >= 0 && (LOG || T.wait != done_group)) {
@@ -924,6 +965,7 @@ __device__ __forceinline__ void control_loop(const Params& P, Smem<WT, KMAX>& sm
       if (ok) done_group = T.wait;
     }
     if (lane == 0) sm.stop = ok ? 0 : 1;
+    if (!P.prefetch) __syncthreads();  // W: the compute waves may load the weights now
     if (!ok) {
       __syncthreads();  // A
       __syncthreads();  // B
@@ -951,7 +993,13 @@ __device__ __forceinline__ void control_loop(const Params& P, Smem<WT, KMAX>& sm
     }
     // publish: this wave made every global store of the tile; once they have
     // completed, one relaxed device-scope increment of the tile's counter shard
-    __builtin_amdgcn_s_waitcnt(0);
+    const bool batch = T.type == T_LM && T.signal >= 0;
+    if (batch) {
+      lm_group = T.signal;
+      lm_count += id != P.drop_tile;
+    } else {
+      __builtin_amdgcn_s_waitcnt(0);
+    }
     if (lane == 0) {
       if (LOG) {
         int32_t* rec = P.log + (size_t)id * 8;
@@ -970,16 +1018,20 @@ __device__ __forceinline__ void control_loop(const Params& P, Smem<WT, KMAX>& sm
         tm[4] = t_partials;
         tm[5] = t_end;
       }
-      if (T.signal >= 0 && id != P.drop_tile) {
+      if (!batch && T.signal >= 0 && id != P.drop_tile) {
         const Group G = cload(P.groups, T.signal);
         atomic_add(&P.counters[(size_t)(G.shard0 + T.shard) * kLine], 1u);
       }
     }
-    __syncthreads();  // C: published; the compute waves may load the next tile
+    // C: published; the compute waves may load the next tile.  LM-head tiles
+    // skip it: only the final argmax depends on them, so their epilogue may
+    // queue behind the next weights, which then stream without a gap.
+    if (T.type != T_LM) __syncthreads();
     // the next claim, written by compute wave 1 before this tile's barrier B
     cur = __builtin_amdgcn_readfirstlane(sm.ids[(it + 1) & 1]);
     ++it;
   }
+  if (lm_count) flush_lm(P, lm_group, lm_count, lane0);
 }
 
 // Redefines the slot in place (no copy), once per batch row: the unpacked
@@ -1013,6 +1065,9 @@ __device__ __forceinline__ void compute_loop(const Params& P, Smem<WT, KMAX>& sm
     // while here it returns ahead of the weights this wave waits for anyway.
     uint32_t ahead = 0;
     if (tc0 == 0) ahead = atomic_add(head, 1u);
+    // without weight prefetch (an ablation), the weights are loaded only once
+    // the control wave has seen the tile's inputs complete (barrier W)
+    if (!P.prefetch) __syncthreads();  // W
     stage<WT, CPR_H, CPR_F>(P, T, s, voff);
     ++it;
     const int tc = opaque(tc0);
@@ -1045,7 +1100,7 @@ __device__ __forceinline__ void compute_loop(const Params& P, Smem<WT, KMAX>& sm
     // above it would keep two slots live.
     __builtin_amdgcn_sched_barrier(0);
     nx = __builtin_amdgcn_readfirstlane(sm.ids[(it + 1) & 1]);
-    __syncthreads();  // C
+    if (T.type != T_LM) __syncthreads();  // C
   }
 }
 

@@ -204,8 +204,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(sequences shard across GPUs with no exchange; see the design notes)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: this build runs on a "
+              "single GPU (batched sequences would shard across GPUs with no exchange)", file=sys.stderr)
         sys.exit(2)
     print(json.dumps(run(args)))
 

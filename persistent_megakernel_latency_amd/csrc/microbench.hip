@@ -392,6 +392,12 @@ __global__ __launch_bounds__(256) void k_pp_loaded(unsigned* ctr, int iters, con
   if (acc == 0x9e3779b9u) sink[blockIdx.x * blockDim.x + t] = acc;
 }
 
+// ---- plain copy of a known number of bytes: the calibration kernel for the
+// FETCH_SIZE / WRITE_SIZE hardware counters (16 bytes per thread per step).
+__global__ __launch_bounds__(256) void k_copy(const u32x4* __restrict__ src, u32x4* __restrict__ dst, long n16) {
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n16; i += (long)gridDim.x * 256) dst[i] = src[i];
+}
+
 static double time_ms(hipEvent_t a, hipEvent_t b) {
   float ms = 0;
   CHECK(hipEventElapsedTime(&ms, a, b));
@@ -471,6 +477,26 @@ int main(int argc, char** argv) {
     resid_case<576, 53840, 128, true>(d_out, n_cu);
     resid_case<320, 16384, 128, false>(d_out, 3 * n_cu);
     CHECK(hipFree(d_out));
+    return 0;
+  }
+  if (which == "copy") {
+    // 1 GiB from the read buffer into a second buffer, five times
+    const size_t cbytes = (size_t)1 << 30;
+    u32x4* dst = nullptr;
+    CHECK(hipMalloc(&dst, cbytes));
+    for (int r = 0; r < 5; ++r) {
+      CHECK(hipEventRecord(e0));
+      hipLaunchKernelGGL(k_copy, dim3(n_cu * 8), dim3(256), 0, 0, reinterpret_cast<const u32x4*>(src), dst,
+                         (long)(cbytes / 16));
+      CHECK(hipEventRecord(e1));
+      CHECK(hipEventSynchronize(e1));
+      CHECK(hipGetLastError());
+      const double ms = time_ms(e0, e1);
+      printf("{\"bench\": \"copy\", \"bytes_read\": %zu, \"bytes_written\": %zu, \"ms\": %.4f, \"GBps\": %.1f}\n",
+             cbytes, cbytes, ms, 2.0 * cbytes / (ms * 1e6));
+      fflush(stdout);
+    }
+    CHECK(hipFree(dst));
     return 0;
   }
   if (which == "ppload") {

@@ -45,7 +45,8 @@ std::string check_shape(const wpk_model_desc& d, int32_t batch, int32_t ctx_len,
   s.G = s.Hq / s.Hkv;
   if (s.G > kMaxGroupHeads) return "at most 4 q heads per kv head";
   if (s.Hq * s.D != s.H) return "n_q_heads * head_dim must equal hidden";
-  if (batch < 1 || batch > kMaxBatch) return "batch must be in [1, 4]";
+  if (batch < 1 || batch > kMaxBatch) return "batch must be in [1, 32]";
+  s.wide = batch > kMaxBatchGemv;
   if (ctx_len < 1) return "ctx_len must be positive";
   if (!(d.rms_eps >= 0.0f) || !(d.rope_theta > 0.0f)) return "rms_eps >= 0 and rope_theta > 0 required";
   s.elt = d.dtype == WPK_F32 ? 4 : 2;
@@ -68,6 +69,17 @@ std::string check_shape(const wpk_model_desc& d, int32_t batch, int32_t ctx_len,
   while (rq * 2 <= std::min(s.rows_h, s.D)) rq *= 2;
   s.rows_qkv = rq;
   if (s.rows_f > 64) s.rows_f = 64;
+  if (s.wide) {
+    // matrix-core tiles: 16 rows over all sequences; K in 128-element steps
+    // (four compute waves x 32), passes of at most 2048, operand pieces of 1024
+    if (s.dtype != WPK_BF16) return "batches above 4 need bf16 weights";
+    for (int32_t k : {s.H, s.F}) {
+      if (k % 128) return "batches above 4 need hidden and ffn to be multiples of 128";
+      if (k > kGemmWK && k % kGemmWK) return "batches above 4 need hidden and ffn <= 2048 or multiples of 2048";
+      if (k > kGemmXK && k < kGemmWK) return "batches above 4 need hidden and ffn <= 1024 or multiples of 2048";
+    }
+    s.rows_h = s.rows_qkv = s.rows_f = kGemmRows;
+  }
   s.workers_per_cu = o.workers_per_cu ? o.workers_per_cu : 2;
   if (s.workers_per_cu < 1 || s.workers_per_cu > 8) return "workers_per_cu must be in [1, 8]";
   s.queue_shards = o.queue_shards ? o.queue_shards : 8;
@@ -126,6 +138,13 @@ Dag build_dag(const Shape& s) {
     for (auto& g : g_attn) g = e.group();
     for (auto& g : g_comb) g = e.group();
     const int32_t g_o = e.group(), g_gu = e.group(), g_dn = e.group();
+    // wide plans: each sequence's attention input is normalised once (NORM),
+    // and the QKV tiles wait on those instead of on the previous layer
+    int32_t g_qkv_in = g_x;
+    if (s.wide) {
+      g_qkv_in = e.group();
+      for (int32_t b = 0; b < s.B; ++b) e.tile(T_NORM, l, g_x, g_qkv_in).b = b;
+    }
 
     // QKV: for each kv group, the q heads of the group, then its k head, then
     // its v head, so attention of group g depends on a contiguous run.
@@ -137,13 +156,13 @@ Dag build_dag(const Shape& s) {
         const int32_t base = kind == 0 ? head * D : (kind == 1 ? (s.Hq + g) * D : (s.Hq + s.Hkv + g) * D);
         if (kind < 2) {
           for (int32_t i0 = 0; i0 < half; i0 += rs_q) {
-            Tile& t = e.gemv(T_QKV, l, g_x, g_attn[g], base + i0, base + half + i0, rs_q, s.rows_qkv);
+            Tile& t = e.gemv(T_QKV, l, g_qkv_in, g_attn[g], base + i0, base + half + i0, rs_q, s.rows_qkv);
             t.kind = kind;
             t.g = head;
           }
         } else {
           for (int32_t i0 = 0; i0 < D; i0 += s.rows_qkv) {
-            Tile& t = e.gemv(T_QKV, l, g_x, g_attn[g], base + i0, base + i0 + rs_q, rs_q, s.rows_qkv);
+            Tile& t = e.gemv(T_QKV, l, g_qkv_in, g_attn[g], base + i0, base + i0 + rs_q, rs_q, s.rows_qkv);
             t.kind = 2;
             t.g = head;
           }
@@ -164,12 +183,23 @@ Dag build_dag(const Shape& s) {
         t.b = b;
         t.g = g;
       }
-    for (int32_t r = 0; r < s.H; r += s.rows_h) e.gemv(T_OPROJ, l, g_o, g_gu, r, r + s.rows_h, s.rows_h, s.rows_h);
+    if (s.wide) {  // o-proj -> per-sequence MLP norm -> gate/up
+      const int32_t g_xm = e.group();
+      for (int32_t r = 0; r < s.H; r += s.rows_h) e.gemv(T_OPROJ, l, g_o, g_xm, r, r + s.rows_h, s.rows_h, s.rows_h);
+      for (int32_t b = 0; b < s.B; ++b) e.tile(T_NORM2, l, g_xm, g_gu).b = b;
+    } else {
+      for (int32_t r = 0; r < s.H; r += s.rows_h) e.gemv(T_OPROJ, l, g_o, g_gu, r, r + s.rows_h, s.rows_h, s.rows_h);
+    }
     const int32_t rs_gu = s.rows_h / 2;
     for (int32_t j = 0; j < s.F; j += rs_gu) e.gemv(T_GATEUP, l, g_gu, g_dn, j, j, rs_gu, s.rows_h);
     const int32_t g_next = e.group();  // x of the next layer, or the LM head's input
     for (int32_t r = 0; r < s.H; r += s.rows_f) e.gemv(T_DOWN, l, g_dn, g_next, r, r + s.rows_f, s.rows_f, s.rows_f);
     g_x = g_next;
+  }
+  if (s.wide) {  // the final norm once per sequence
+    const int32_t g_nf = e.group();
+    for (int32_t b = 0; b < s.B; ++b) e.tile(T_NORMF, s.L - 1, g_x, g_nf).b = b;
+    g_x = g_nf;
   }
   const int32_t g_am = e.group();
   for (int32_t r = 0; r < s.V; r += s.rows_h) e.gemv(T_LM, s.L - 1, g_x, g_am, r, r + s.rows_h, s.rows_h, s.rows_h);
@@ -268,6 +298,11 @@ void outputs(const Shape& s, const Tile& t, std::vector<std::pair<int64_t, int64
     case T_ARGMAX:
       out.emplace_back(0, s.B);
       break;
+    case T_NORM:
+    case T_NORM2:
+    case T_NORMF:
+      out.emplace_back(t.b, t.b + 1);  // one sequence's normalised row
+      break;
   }
 }
 
@@ -282,7 +317,17 @@ void inputs(const Shape& s, const Tile& t, std::vector<Need>& need) {
   const int32_t l = t.layer;
   switch (t.type) {
     case T_QKV:
+      if (s.wide) need.push_back({l, T_NORM, 0, s.B});
+      else if (l > 0) need.push_back({l - 1, T_DOWN, 0, s.H});
+      break;
+    case T_NORM:
       if (l > 0) need.push_back({l - 1, T_DOWN, 0, s.H});
+      break;
+    case T_NORM2:
+      need.push_back({l, T_OPROJ, 0, s.H});
+      break;
+    case T_NORMF:
+      need.push_back({s.L - 1, T_DOWN, 0, s.H});
       break;
     case T_ATTN: {
       const int64_t qa = (int64_t)t.g * s.G * s.D;
@@ -302,13 +347,15 @@ void inputs(const Shape& s, const Tile& t, std::vector<Need>& need) {
       need.push_back({l, T_COMBINE, 0, (int64_t)s.B * s.Hq * s.D});
       break;
     case T_GATEUP:
-      need.push_back({l, T_OPROJ, 0, s.H});
+      if (s.wide) need.push_back({l, T_NORM2, 0, s.B});
+      else need.push_back({l, T_OPROJ, 0, s.H});
       break;
     case T_DOWN:
       need.push_back({l, T_GATEUP, 0, s.F});
       break;
     case T_LM:
-      need.push_back({s.L - 1, T_DOWN, 0, s.H});
+      if (s.wide) need.push_back({s.L - 1, T_NORMF, 0, s.B});
+      else need.push_back({s.L - 1, T_DOWN, 0, s.H});
       break;
     case T_ARGMAX:
       need.push_back({s.L - 1, T_LM, 0, s.V});

@@ -21,6 +21,7 @@ struct Shape {
   int32_t rows_qkv;  // rows of a QKV tile (RoPE pairs (i, i+D/2) stay together)
   int32_t rows_f;    // rows of a K=ffn GEMV tile
   int32_t tile_bytes, workers_per_cu, queue_shards;
+  int32_t wide;      // batch above kMaxBatchGemv: matrix-core tiles and per-sequence norm tiles
   float theta, eps;
 };
 

@@ -46,6 +46,13 @@ ActLayout act_layout(const Shape& s) {
   a.part = at;  at += r64((int64_t)s.B * s.Hkv * s.nch * s.G * (s.D + 2));
   a.attn = at;  at += r64((int64_t)s.B * s.Hq * s.D);
   a.h = at;     at += r64((int64_t)s.B * s.F);
+  // bf16 [32][K] operands take 16 * K floats; rows past the batch stay zero
+  const int64_t wb = s.wide ? (int64_t)kMaxBatch : 0;  // two bf16 planes of 32 rows
+  a.xn1 = at;   at += r64(wb * s.H);
+  a.xattn = at; at += r64(wb * s.Hq * s.D);
+  a.xn2 = at;   at += r64(wb * s.H);
+  a.xh = at;    at += r64(wb * s.F);
+  a.xnf = at;   at += r64(wb * s.H);
   a.per_layer = at;
   a.total = at * s.L;
   return a;
@@ -70,6 +77,11 @@ void fill_layers(const Shape& s, const wpk_model_desc& d, float* act, std::vecto
     lb.part = base + a.part;
     lb.attn = base + a.attn;
     lb.h = base + a.h;
+    lb.xn1 = (uint16_t*)(base + a.xn1);
+    lb.xattn = (uint16_t*)(base + a.xattn);
+    lb.xn2 = (uint16_t*)(base + a.xn2);
+    lb.xh = (uint16_t*)(base + a.xh);
+    lb.xnf = (uint16_t*)(base + a.xnf);
     lb.x_in = l == 0 ? nullptr : out[l - 1].x_out;
   }
 }
@@ -100,6 +112,21 @@ inline void cache_put(char* base, int32_t dtype, int64_t i, float v) {
   else ((float*)base)[i] = v;
 }
 
+inline float bf16v(uint16_t h) {
+  const uint32_t u = (uint32_t)h << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+// Stores v as the hi/lo bf16 pair of a wide operand buffer [2][32][K].
+inline void xput(uint16_t* x, int K, int b, int i, float v) {
+  const int64_t at = (int64_t)b * K + i;
+  const uint16_t hi = to_bf16(v);
+  x[at] = hi;
+  x[(int64_t)kMaxBatch * K + at] = to_bf16(v - bf16v(hi));
+}
+
 inline uint64_t pack_max(float v, int32_t idx) {
   uint32_t u;
   std::memcpy(&u, &v, 4);
@@ -127,10 +154,31 @@ int32_t token_of(Ctx& c, int b) {
   return (t < 0 || t >= c.P.V) ? 0 : t;
 }
 
-// Input vector of a GEMV tile for sequence b, with its RMSNorm prologue.
+// A wide operand element: the hi and lo bf16 planes of a [2][32][K] buffer.
+inline float xget(const uint16_t* x, int K, int b, int i) {
+  const int64_t at = (int64_t)b * K + i;
+  return bf16v(x[at]) + bf16v(x[(int64_t)kMaxBatch * K + at]);
+}
+
+// Input vector of a GEMV tile for sequence b, with its RMSNorm prologue.  In
+// a wide plan it is the operand row the norm tile or the producer wrote.
 void gemv_input(Ctx& c, const Tile& T, int b, std::vector<float>& x) {
   const Params& P = c.P;
   const LayerBufs& lb = P.layers[T.layer];
+  if (P.wide) {
+    const uint16_t* src = nullptr;
+    int K = P.H;
+    switch (T.type) {
+      case T_QKV: src = lb.xn1; break;
+      case T_OPROJ: src = lb.xattn; break;
+      case T_GATEUP: src = lb.xn2; break;
+      case T_DOWN: src = lb.xh; K = P.F; break;
+      default: src = P.layers[P.L - 1].xnf; break;
+    }
+    x.resize(K);
+    for (int i = 0; i < K; ++i) x[i] = xget(src, K, b, i);
+    return;
+  }
   const float* gain = nullptr;
   int K = P.H;
   switch (T.type) {
@@ -247,7 +295,9 @@ void run_gemv(Ctx& c, const Tile& T) {
           const int64_t j = T.r0 + i;
           if (j >= P.F) continue;
           const float g = y[i], u = y[T.rs + i];
-          lb.h[(int64_t)b * P.F + j] = g / (1.0f + std::exp(-g)) * u;
+          const float hv = g / (1.0f + std::exp(-g)) * u;
+          if (P.wide) xput(lb.xh, P.F, b, j, hv);
+          else lb.h[(int64_t)b * P.F + j] = hv;
         }
         break;
       case T_DOWN:
@@ -323,9 +373,14 @@ void run_combine(Ctx& c, const Tile& T) {
   const int n = p < 0 ? 0 : std::min(p + 1, P.cap);
   const int nact = (n + kAttnChunk - 1) / kAttnChunk;
   for (int h = 0; h < P.G; ++h) {
-    float* dst = lb.attn + (int64_t)T.b * P.Hq * P.D + (int64_t)(T.g * P.G + h) * P.D;
+    const int64_t at = (int64_t)T.b * P.Hq * P.D + (int64_t)(T.g * P.G + h) * P.D;
+    float* dst = lb.attn + at;
+    auto put = [&](int d, float v) {
+      if (P.wide) xput(lb.xattn, P.Hq * P.D, T.b, (T.g * P.G + h) * P.D + d, v);  // the o-proj operand
+      else dst[d] = v;
+    };
     if (nact == 0) {
-      for (int d = 0; d < P.D; ++d) dst[d] = 0.f;
+      for (int d = 0; d < P.D; ++d) put(d, 0.f);
       continue;
     }
     auto part = [&](int ch) {
@@ -338,7 +393,7 @@ void run_combine(Ctx& c, const Tile& T) {
     for (int d = 0; d < P.D; ++d) {
       float o = 0.f;
       for (int ch = 0; ch < nact; ++ch) o += part(ch)[2 + d] * std::exp(part(ch)[0] - M);
-      dst[d] = o / L;
+      put(d, o / L);
     }
   }
 }
@@ -358,8 +413,45 @@ void run_argmax(Ctx& c) {
   }
 }
 
+// Wide plans: one sequence's row, normalised and scaled by the gain, rounded
+// to the bf16 operand of the matrix-core tiles.
+void run_norm(Ctx& c, const Tile& T) {
+  const Params& P = c.P;
+  const LayerBufs& lb = P.layers[T.layer];
+  const int b = T.b, K = P.H;
+  std::vector<float> x(K);
+  const float* gain;
+  uint16_t* dst;
+  if (T.type == T_NORM) {
+    gain = lb.attn_norm;
+    dst = lb.xn1;
+    if (T.layer == 0) {
+      const int64_t tok = token_of(c, b);
+      for (int i = 0; i < K; ++i) x[i] = wval(P.embed, P.dtype, tok * K + i);
+    } else {
+      for (int i = 0; i < K; ++i) x[i] = lb.x_in[(int64_t)b * K + i];
+    }
+  } else if (T.type == T_NORM2) {
+    gain = lb.mlp_norm;
+    dst = lb.xn2;
+    for (int i = 0; i < K; ++i) x[i] = lb.x_mid[(int64_t)b * K + i];
+  } else {
+    const LayerBufs& last = P.layers[P.L - 1];
+    gain = P.final_norm;
+    dst = last.xnf;
+    for (int i = 0; i < K; ++i) x[i] = last.x_out[(int64_t)b * K + i];
+  }
+  float ss = 0.f;
+  for (int i = 0; i < K; ++i) ss += x[i] * x[i];
+  const float inv = 1.0f / std::sqrt(ss / (float)K + P.eps);
+  for (int i = 0; i < K; ++i) xput(dst, K, b, i, x[i] * inv * gain[i]);
+}
+
 void run_tile(Ctx& c, const Tile& T) {
   switch (T.type) {
+    case T_NORM:
+    case T_NORM2:
+    case T_NORMF: run_norm(c, T); break;
     case T_ATTN: run_attn(c, T); break;
     case T_COMBINE: run_combine(c, T); break;
     case T_ARGMAX: run_argmax(c); break;
@@ -388,6 +480,12 @@ Params host_params(wpk_plan* p, int32_t* tokens, wpk_kv* kv, float* logits) {
   P.off_part = (int32_t)a.part;
   P.off_attn = (int32_t)a.attn;
   P.off_h = (int32_t)a.h;
+  P.wide = s.wide;
+  P.off_xn1 = (int32_t)a.xn1;
+  P.off_xattn = (int32_t)a.xattn;
+  P.off_xn2 = (int32_t)a.xn2;
+  P.off_xh = (int32_t)a.xh;
+  P.off_xnf = (int32_t)a.xnf;
   P.rope_cos = p->hw.rope_cos.data();
   P.rope_sin = p->hw.rope_sin.data();
   P.tokens = tokens;
@@ -402,7 +500,11 @@ Params host_params(wpk_plan* p, int32_t* tokens, wpk_kv* kv, float* logits) {
 
 void poison(wpk_plan* p, const Params& P) {
   const float nan = std::numeric_limits<float>::quiet_NaN();
-  std::fill(p->hw.act.begin(), p->hw.act.end(), nan);
+  // a float NaN whose two halves are bf16 NaNs too, for the bf16 operand rows
+  const uint32_t nan2 = 0x7FC07FC0u;
+  float nanw;
+  std::memcpy(&nanw, &nan2, 4);
+  std::fill(p->hw.act.begin(), p->hw.act.end(), nanw);
   std::fill(P.logits, P.logits + (int64_t)P.B * P.V, nan);
   // the slot each active sequence is about to append: a read of it before the
   // tile that writes it sees NaN

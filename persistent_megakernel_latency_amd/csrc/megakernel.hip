@@ -823,27 +823,31 @@ __device__ __forceinline__ void ctl_attn_out(const Params& P, const Tile& T, con
   }
 }
 
-// Output conversion: greedy token and sequence advance.  Lane b*16 + s takes
-// shard s of sequence b (and clears it for the next step); a 16-lane max
-// reduction gives the packed (value, lowest index) maximum.
+// Output conversion: greedy token and sequence advance.  Lane b*16 + s of a
+// group of four sequences takes shard s of sequence b (and clears it for the
+// next step); a 16-lane max reduction gives the packed (value, lowest index)
+// maximum.
 template <typename WT, int KMAX>
 __device__ __forceinline__ void ctl_argmax(const Params& P, const Smem<WT, KMAX>& sm, int lane0) {
   const int lane = opaque(lane0);
-  static_assert(kMaxBatch * kArgmaxShards <= 64, "one lane per shard");
-  const int b = lane / kArgmaxShards;
-  unsigned long long best = 0;
-  if (b < P.B)
-    best = __hip_atomic_exchange(&P.argmax[lane], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  constexpr int SEQS = 64 / kArgmaxShards;
+  for (int b0 = 0; b0 < P.B; b0 += SEQS) {
+    const int b = b0 + lane / kArgmaxShards;
+    unsigned long long best = 0;
+    if (b < P.B)
+      best = __hip_atomic_exchange(&P.argmax[(size_t)b0 * kArgmaxShards + lane], 0ull, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-  for (int m = 1; m < kArgmaxShards; m <<= 1) {
-    const unsigned long long o = __shfl_xor(best, m);
-    best = o > best ? o : best;
-  }
-  if (b < P.B && lane % kArgmaxShards == 0) {
-    const int p = sm.pos[b];
-    if (p >= 0 && p < P.cap) {
-      st_sc1(&P.tokens[b], (int32_t)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull)));
-      st_sc1(&P.seq_len[b], p + 1);
+    for (int m = 1; m < kArgmaxShards; m <<= 1) {
+      const unsigned long long o = __shfl_xor(best, m);
+      best = o > best ? o : best;
+    }
+    if (b < P.B && lane % kArgmaxShards == 0) {
+      const int p = sm.pos[b];
+      if (p >= 0 && p < P.cap) {
+        st_sc1(&P.tokens[b], (int32_t)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull)));
+        st_sc1(&P.seq_len[b], p + 1);
+      }
     }
   }
 }

@@ -22,7 +22,12 @@ enum TileType : int32_t {
   T_DOWN = 5,     // down projection + residual
   T_LM = 6,       // final RMSNorm prologue, tied LM-head rows, partial argmax
   T_ARGMAX = 7,   // greedy token, seq_len advance (output conversion)
-  T_NTYPES = 8
+  // wide plans (batch above kMaxBatchGemv) normalise each sequence's row once,
+  // into the bf16 operand the matrix-core tiles read
+  T_NORM = 8,     // attention-input RMSNorm (layer 0: of the embedding row)
+  T_NORM2 = 9,    // MLP-input RMSNorm
+  T_NORMF = 10,   // final RMSNorm before the LM head
+  T_NTYPES = 11
 };
 
 // One tile: 64 bytes, loaded with scalar loads by a worker.
@@ -31,7 +36,7 @@ struct Tile {
   int32_t shard;                      // counter shard of `signal` this tile increments
   int32_t r0, r1, rs;                 // GEMV: rows [r0, r0+rs) then [r1, r1+(rows-rs)) of its matrix
   int32_t rows;                       // GEMV: row capacity of the tile
-  int32_t b, g, c;                    // ATTN: sequence, kv head, KV chunk; COMBINE: b, g; QKV: head in g
+  int32_t b, g, c;                    // ATTN: sequence, kv head, KV chunk; COMBINE, NORM*: b (, g); QKV: head
   int32_t kind;                       // QKV: 0 q rows, 1 k rows, 2 v rows
   int32_t id;                         // tile id (index into the tile table and the log)
   int32_t pad0, pad1;
@@ -56,7 +61,11 @@ constexpr int kHeadDim = 64;                          // the only head size buil
 constexpr int kMaxGroupHeads = 4;                     // q heads per kv head
 constexpr int kArgmaxShards = 16;
 constexpr int kMaxShards = 16;
-constexpr int kMaxBatch = 4;
+constexpr int kMaxBatch = 32;
+constexpr int kMaxBatchGemv = 4;   // above it a plan is wide: matrix-core tiles over all sequences
+constexpr int kGemmRows = 16;      // weight rows of a wide (matrix-core) tile
+constexpr int kGemmWK = 2048;      // K elements of one weight pass of a wide tile (64 KiB of bf16 rows)
+constexpr int kGemmXK = 1024;      // K elements of one staged operand piece (16 sequences, 32 KiB bf16)
 constexpr int kMaxLayers = 32;
 
 // Control block: word offsets, each field on its own 256-byte line.
@@ -84,6 +93,15 @@ struct LayerBufs {
   float* part;        // [B][Hkv][nch][G][D+2] attention partials (m, l, o[D])
   float* attn;        // [B][Hq*D] attention output
   float* h;           // [B][F] SwiGLU output
+  // Wide plans: operands of the matrix-core tiles as a pair of bf16 planes,
+  // hi [32][K] then lo [32][K], with value = hi + lo (hi is the value rounded
+  // to bf16, lo the remainder rounded to bf16: about 16 significant bits).
+  // Rows past B stay zero.
+  uint16_t* xn1;      // normalised attention input
+  uint16_t* xattn;    // attention output
+  uint16_t* xn2;      // normalised MLP input
+  uint16_t* xh;       // SwiGLU output
+  uint16_t* xnf;      // normalised final hidden state (last layer only)
 };
 
 // Per-layer weights as the kernels see them: kept inside the kernel arguments
@@ -110,6 +128,8 @@ struct Params {
   float* act;
   int64_t act_layer;
   int32_t off_x_mid, off_x_out, off_q, off_part, off_attn, off_h;
+  // wide plans: bf16 operand buffers, offsets in floats from the layer's base
+  int32_t wide, off_xn1, off_xattn, off_xn2, off_xh, off_xnf;
   LayerW lw[kMaxLayers];
   const float* rope_cos;  // [cap][D/2]
   const float* rope_sin;  // [cap][D/2]

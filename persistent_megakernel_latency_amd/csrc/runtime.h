@@ -24,7 +24,9 @@ void rope_table(const Shape& s, std::vector<float>& cos_t, std::vector<float>& s
 
 // Bytes of the per-layer activation buffers and their placement.
 struct ActLayout {
-  int64_t x_mid, x_out, q, part, attn, h, per_layer;  // float offsets within a layer
+  int64_t x_mid, x_out, q, part, attn, h;  // float offsets within a layer
+  int64_t xn1, xattn, xn2, xh, xnf;        // wide plans: bf16 hi/lo planes [2][32][K] (float offsets; 0 size otherwise)
+  int64_t per_layer;
   int64_t total;                                      // floats for all layers
 };
 ActLayout act_layout(const Shape& s);

@@ -184,3 +184,51 @@ def test_full_cache_and_bad_token_are_errors():
     plan = wpk.wpk_build_host(d.desc, 1, 8)
     st = HostState(kc, vc, sl, np.array([cfg.vocab + 5], np.int32), cfg.vocab)
     assert st.serial(plan, 0) == wpk.WPK_E_TOKEN
+
+
+@pytest.mark.parametrize("batch", [8, 32])
+def test_wide_batch_plan_matches_oracle(batch):
+    """Batches above four use the matrix-core layout: norm tiles write bf16
+    operand rows, every projection tile covers 16 weight rows for all
+    sequences.  The serial executor of that DAG against the oracle, with
+    ragged lengths, an inactive slot and NaN poison."""
+    cfg = synth.MINI
+    w = synth.make_weights(cfg, gain_std=0.1)
+    model = oracle.Model(cfg, w)
+    cap = 140
+    rng = np.random.default_rng(batch)
+    lens = rng.integers(1, cap - 1, size=batch).astype(np.int32)
+    lens[0], lens[-1] = 63, 129
+    lens[1] = -1
+    kc, vc = synth.synthetic_kv(cfg, batch, cap, np.maximum(lens, 0))
+    tok = rng.integers(0, cfg.vocab, size=batch).astype(np.int32)
+    d = host_desc(cfg, w)
+    plan = wpk.wpk_build_host(d.desc, batch, cap)
+    assert plan, wpk.wpk_last_error(None)
+    info = wpk.wpk_get_info(plan)
+    assert info.rows_per_tile_h == 16 and info.rows_per_tile_f == 16
+    ty, _, wait, signal = wpk.wpk_get_dag(plan, info.n_tiles)
+    assert np.sum(np.array(ty) == 8) == cfg.n_layers * batch  # attention-norm rows
+    ok_, ov_, osl = kc.copy(), vc.copy(), lens.copy()
+    olog, otok = model.step(tok, ok_, ov_, osl)
+    ref = None
+    for seed in (0, 5):
+        st = HostState(kc, vc, lens, tok, cfg.vocab)
+        assert st.serial(plan, seed, poison=True) == 0, wpk.wpk_last_error(plan)
+        rc, log = wpk.wpk_get_log(plan, info.n_tiles)
+        check_log(log, wait, signal)
+        if ref is None:
+            ref = st
+        else:
+            assert np.array_equal(st.logits, ref.logits)
+    st = ref
+    act = [b for b in range(batch) if lens[b] >= 0]
+    for b in act:
+        err = np.max(np.abs(st.logits[b] - olog[b]))
+        assert err < 1e-3, (b, err)  # hi/lo operands keep about 16 significant bits
+        top2 = np.sort(olog[b])[-2:]
+        if top2[1] - top2[0] > 4e-2:
+            assert st.tokens[b] == otok[b]
+    assert st.tokens[1] == tok[1] and st.seq_len.tolist() == osl.tolist()
+    assert np.array_equal(st.kc[:, 1], kc[:, 1])
+    wpk.wpk_destroy(plan)

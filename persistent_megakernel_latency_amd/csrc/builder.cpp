@@ -70,15 +70,11 @@ std::string check_shape(const wpk_model_desc& d, int32_t batch, int32_t ctx_len,
   s.rows_qkv = rq;
   if (s.rows_f > 64) s.rows_f = 64;
   if (s.wide) {
-    // matrix-core tiles: 16 rows over all sequences; K in 128-element steps
-    // (four compute waves x 32), passes of at most 2048, operand pieces of 1024
+    // matrix-core tiles: 64 rows (one head of QKV) x 512-column slices of K
     if (s.dtype != WPK_BF16) return "batches above 4 need bf16 weights";
-    for (int32_t k : {s.H, s.F}) {
-      if (k % 128) return "batches above 4 need hidden and ffn to be multiples of 128";
-      if (k > kGemmWK && k % kGemmWK) return "batches above 4 need hidden and ffn <= 2048 or multiples of 2048";
-      if (k > kGemmXK && k < kGemmWK) return "batches above 4 need hidden and ffn <= 1024 or multiples of 2048";
-    }
-    s.rows_h = s.rows_qkv = s.rows_f = kGemmRows;
+    if (s.H % kWideK || s.F % kWideK) return "batches above 4 need hidden and ffn to be multiples of 512";
+    if (s.D != kWideRows) return "batches above 4 need head_dim 64";
+    s.rows_h = s.rows_qkv = s.rows_f = kWideRows;
   }
   s.workers_per_cu = o.workers_per_cu ? o.workers_per_cu : 2;
   if (s.workers_per_cu < 1 || s.workers_per_cu > 8) return "workers_per_cu must be in [1, 8]";
@@ -125,12 +121,105 @@ struct Emitter {
     t.rows = rows;
     return t;
   }
+  // The slices of one wide row block: slice c waits on wait_of(c); all signal
+  // `signal`.
+  template <class F>
+  void wide(int32_t type, int32_t layer, F wait_of, int32_t signal, int32_t r0, int32_t r1, int32_t rs,
+            int32_t K, int32_t kind = -1, int32_t head = 0) {
+    const int32_t nsl = K / kWideK;
+    for (int32_t c = 0; c < nsl; ++c) {
+      Tile& t = gemv(type, layer, wait_of(c), signal, r0, r1, rs, kWideRows);
+      t.b = nsl;
+      t.c = c;
+      t.fix = d.n_fix;
+      t.pslot = d.n_pslots;
+      t.kind = kind;
+      t.g = head;
+    }
+    d.n_fix += 1;
+    d.n_pslots += nsl;
+  }
 };
+
+}  // namespace
+
+namespace {
+
+Dag finish_dag(const Shape& s, Emitter& e);
+
+// Wide plans (batch above kMaxBatchGemv).  Per layer: a norm tile per
+// sequence; QKV row blocks of one head each (two segments, dimensions
+// [0, D/2) and [D/2, D), so a RoPE pair is rows i and i + D/2 of the tile), attention of kv head g waiting on its q, k and v heads;
+// output-projection slices, each waiting only on the combines of the heads in
+// its K slice; a norm tile per sequence; gate/up row blocks (32 gate + 32 up
+// rows); down slices, each waiting only on the gate/up row blocks of its K
+// slice.  Then a final norm tile per sequence and the LM-head row blocks.
+void build_wide(const Shape& s, Emitter& e) {
+  const int32_t D = s.D;
+  const int32_t n_os = s.H / kWideK;            // o-proj K slices
+  const int32_t n_ds = s.F / kWideK;            // down K slices
+  const int32_t hpb = kWideRows / 2;             // h columns per gate/up row block
+  auto same = [](int32_t w) { return [w](int32_t) { return w; }; };
+  int32_t g_x = -1;
+  for (int32_t l = 0; l < s.L; ++l) {
+    const int32_t g_qkv_in = e.group();
+    for (int32_t b = 0; b < s.B; ++b) e.tile(T_NORM, l, g_x, g_qkv_in).b = b;
+    std::vector<int32_t> g_attn(s.Hkv), g_comb(s.B * s.Hkv), g_o(n_os), g_dn(n_ds);
+    for (auto& g : g_attn) g = e.group();
+    for (auto& g : g_comb) g = e.group();
+    for (auto& g : g_o) g = e.group();
+    const int32_t g_xm = e.group(), g_gu = e.group();
+    for (auto& g : g_dn) g = e.group();
+    const int32_t g_next = e.group();
+    for (int32_t g = 0; g < s.Hkv; ++g) {
+      for (int32_t k = 0; k < s.G; ++k) {
+        const int32_t head = g * s.G + k;
+        e.wide(T_QKV, l, same(g_qkv_in), g_attn[g], head * D, head * D + D / 2, D / 2, s.H, 0, head);
+      }
+      const int32_t kb = (s.Hq + g) * D, vb = (s.Hq + s.Hkv + g) * D;
+      e.wide(T_QKV, l, same(g_qkv_in), g_attn[g], kb, kb + D / 2, D / 2, s.H, 1, g);
+      e.wide(T_QKV, l, same(g_qkv_in), g_attn[g], vb, vb + D / 2, D / 2, s.H, 2, g);
+    }
+    for (int32_t b = 0; b < s.B; ++b)
+      for (int32_t g = 0; g < s.Hkv; ++g)
+        for (int32_t c = 0; c < s.nch; ++c) {
+          Tile& t = e.tile(T_ATTN, l, g_attn[g], g_comb[b * s.Hkv + g]);
+          t.b = b;
+          t.g = g;
+          t.c = c;
+        }
+    for (int32_t b = 0; b < s.B; ++b)
+      for (int32_t g = 0; g < s.Hkv; ++g) {
+        // the o-proj slice holding this kv head's q heads
+        Tile& t = e.tile(T_COMBINE, l, g_comb[b * s.Hkv + g], g_o[g * s.G * D / kWideK]);
+        t.b = b;
+        t.g = g;
+      }
+    for (int32_t r = 0; r < s.H; r += kWideRows)
+      e.wide(T_OPROJ, l, [&](int32_t c) { return g_o[c]; }, g_xm, r, r + kWideRows, kWideRows, s.H);
+    for (int32_t b = 0; b < s.B; ++b) e.tile(T_NORM2, l, g_xm, g_gu).b = b;
+    for (int32_t j = 0; j < s.F; j += hpb)
+      e.wide(T_GATEUP, l, same(g_gu), g_dn[j / kWideK], j, j, hpb, s.H);
+    for (int32_t r = 0; r < s.H; r += kWideRows)
+      e.wide(T_DOWN, l, [&](int32_t c) { return g_dn[c]; }, g_next, r, r + kWideRows, kWideRows, s.F);
+    g_x = g_next;
+  }
+  const int32_t g_nf = e.group();
+  for (int32_t b = 0; b < s.B; ++b) e.tile(T_NORMF, s.L - 1, g_x, g_nf).b = b;
+  const int32_t g_am = e.group();
+  for (int32_t r = 0; r < s.V; r += kWideRows)
+    e.wide(T_LM, s.L - 1, same(g_nf), g_am, r, r + kWideRows, kWideRows, s.H);
+  e.tile(T_ARGMAX, s.L - 1, g_am, -1);
+}
 
 }  // namespace
 
 Dag build_dag(const Shape& s) {
   Emitter e;
+  if (s.wide) {
+    build_wide(s, e);
+    return finish_dag(s, e);
+  }
   const int32_t D = s.D, half = s.D / 2;
   int32_t g_x = -1;  // group the current layer's QKV tiles wait on (-1: layer 0)
   for (int32_t l = 0; l < s.L; ++l) {
@@ -138,13 +227,7 @@ Dag build_dag(const Shape& s) {
     for (auto& g : g_attn) g = e.group();
     for (auto& g : g_comb) g = e.group();
     const int32_t g_o = e.group(), g_gu = e.group(), g_dn = e.group();
-    // wide plans: each sequence's attention input is normalised once (NORM),
-    // and the QKV tiles wait on those instead of on the previous layer
-    int32_t g_qkv_in = g_x;
-    if (s.wide) {
-      g_qkv_in = e.group();
-      for (int32_t b = 0; b < s.B; ++b) e.tile(T_NORM, l, g_x, g_qkv_in).b = b;
-    }
+    const int32_t g_qkv_in = g_x;
 
     // QKV: for each kv group, the q heads of the group, then its k head, then
     // its v head, so attention of group g depends on a contiguous run.
@@ -183,28 +266,22 @@ Dag build_dag(const Shape& s) {
         t.b = b;
         t.g = g;
       }
-    if (s.wide) {  // o-proj -> per-sequence MLP norm -> gate/up
-      const int32_t g_xm = e.group();
-      for (int32_t r = 0; r < s.H; r += s.rows_h) e.gemv(T_OPROJ, l, g_o, g_xm, r, r + s.rows_h, s.rows_h, s.rows_h);
-      for (int32_t b = 0; b < s.B; ++b) e.tile(T_NORM2, l, g_xm, g_gu).b = b;
-    } else {
-      for (int32_t r = 0; r < s.H; r += s.rows_h) e.gemv(T_OPROJ, l, g_o, g_gu, r, r + s.rows_h, s.rows_h, s.rows_h);
-    }
+    for (int32_t r = 0; r < s.H; r += s.rows_h) e.gemv(T_OPROJ, l, g_o, g_gu, r, r + s.rows_h, s.rows_h, s.rows_h);
     const int32_t rs_gu = s.rows_h / 2;
     for (int32_t j = 0; j < s.F; j += rs_gu) e.gemv(T_GATEUP, l, g_gu, g_dn, j, j, rs_gu, s.rows_h);
     const int32_t g_next = e.group();  // x of the next layer, or the LM head's input
     for (int32_t r = 0; r < s.H; r += s.rows_f) e.gemv(T_DOWN, l, g_dn, g_next, r, r + s.rows_f, s.rows_f, s.rows_f);
     g_x = g_next;
   }
-  if (s.wide) {  // the final norm once per sequence
-    const int32_t g_nf = e.group();
-    for (int32_t b = 0; b < s.B; ++b) e.tile(T_NORMF, s.L - 1, g_x, g_nf).b = b;
-    g_x = g_nf;
-  }
   const int32_t g_am = e.group();
   for (int32_t r = 0; r < s.V; r += s.rows_h) e.gemv(T_LM, s.L - 1, g_x, g_am, r, r + s.rows_h, s.rows_h, s.rows_h);
   e.tile(T_ARGMAX, s.L - 1, g_am, -1);
+  return finish_dag(s, e);
+}
 
+namespace {
+
+Dag finish_dag(const Shape& s, Emitter& e) {
   Dag& d = e.d;
   // producers and shards
   for (const Tile& t : d.tiles)
@@ -241,6 +318,8 @@ Dag build_dag(const Shape& s) {
   return d;
 }
 
+}  // namespace
+
 namespace {
 
 // Half-open interval set with coverage queries.
@@ -267,8 +346,22 @@ struct Cover {
   }
 };
 
+bool is_gemm(int32_t type) {
+  return type == T_QKV || type == T_OPROJ || type == T_GATEUP || type == T_DOWN || type == T_LM;
+}
+
+// Output rows of a GEMM operator, and (wide plans) its K slices: the flat
+// index of row r of slice c is c * rows + r.
+int64_t gemm_rows(const Shape& s, int32_t type) {
+  return type == T_QKV ? s.qkv_rows : type == T_LM ? s.V : type == T_GATEUP ? s.F : s.H;
+}
+int32_t gemm_slices(const Shape& s, int32_t type) {
+  return s.wide ? (type == T_DOWN ? s.F : s.H) / kWideK : 1;
+}
+
 // The region of its operator's output tensor a tile writes, as intervals of a
-// flat index, keyed by (layer, type).
+// flat index, keyed by (layer, type).  A wide GEMM tile writes its rows of its
+// K slice (the partial sums the row block's last slice adds up).
 void outputs(const Shape& s, const Tile& t, std::vector<std::pair<int64_t, int64_t>>& out) {
   out.clear();
   auto clip = [](int64_t a, int64_t b, int64_t lim) { return std::make_pair(std::min(a, lim), std::min(b, lim)); };
@@ -277,14 +370,21 @@ void outputs(const Shape& s, const Tile& t, std::vector<std::pair<int64_t, int64
     case T_OPROJ:
     case T_DOWN:
     case T_LM: {
-      const int64_t lim = t.type == T_QKV ? s.qkv_rows : (t.type == T_LM ? s.V : s.H);
-      out.push_back(clip(t.r0, t.r0 + t.rs, lim));
-      if (t.rows > t.rs) out.push_back(clip(t.r1, t.r1 + (t.rows - t.rs), lim));
+      const int64_t lim = gemm_rows(s, t.type), at = s.wide ? (int64_t)t.c * lim : 0;
+      auto p = clip(t.r0, t.r0 + t.rs, lim);
+      out.emplace_back(at + p.first, at + p.second);
+      if (t.rows > t.rs) {
+        p = clip(t.r1, t.r1 + (t.rows - t.rs), lim);
+        out.emplace_back(at + p.first, at + p.second);
+      }
       break;
     }
-    case T_GATEUP:
-      out.push_back(clip(t.r0, t.r0 + t.rs, s.F));  // h rows (gate and up rows pair up)
+    case T_GATEUP: {
+      const int64_t at = s.wide ? (int64_t)t.c * s.F : 0;
+      auto p = clip(t.r0, t.r0 + t.rs, s.F);  // h rows (gate and up rows pair up)
+      out.emplace_back(at + p.first, at + p.second);
       break;
+    }
     case T_ATTN: {
       const int64_t i = ((int64_t)t.b * s.Hkv + t.g) * s.nch + t.c;
       out.emplace_back(i, i + 1);
@@ -315,19 +415,62 @@ struct Need {
 void inputs(const Shape& s, const Tile& t, std::vector<Need>& need) {
   need.clear();
   const int32_t l = t.layer;
+  if (s.wide) {
+    // rows [a, b) of a GEMM operator's output: every K slice of them
+    auto rows = [&](int32_t layer, int32_t type, int64_t a, int64_t b) {
+      const int64_t lim = gemm_rows(s, type);
+      for (int32_t c = 0; c < gemm_slices(s, type); ++c) need.push_back({layer, type, c * lim + a, c * lim + b});
+    };
+    switch (t.type) {
+      case T_NORM:
+        if (l > 0) rows(l - 1, T_DOWN, 0, s.H);
+        break;
+      case T_QKV:
+        need.push_back({l, T_NORM, 0, s.B});
+        break;
+      case T_ATTN: {
+        const int64_t qa = (int64_t)t.g * s.G * s.D, ka = ((int64_t)s.Hq + t.g) * s.D,
+                      va = ((int64_t)s.Hq + s.Hkv + t.g) * s.D;
+        rows(l, T_QKV, qa, qa + (int64_t)s.G * s.D);
+        rows(l, T_QKV, ka, ka + s.D);
+        rows(l, T_QKV, va, va + s.D);
+        break;
+      }
+      case T_COMBINE: {
+        const int64_t i = ((int64_t)t.b * s.Hkv + t.g) * s.nch;
+        need.push_back({l, T_ATTN, i, i + s.nch});
+        break;
+      }
+      case T_OPROJ:  // the attention output columns of its K slice, every sequence
+        for (int32_t b = 0; b < s.B; ++b) {
+          const int64_t a = (int64_t)b * s.Hq * s.D + (int64_t)t.c * kWideK;
+          need.push_back({l, T_COMBINE, a, a + kWideK});
+        }
+        break;
+      case T_NORM2:
+        rows(l, T_OPROJ, 0, s.H);
+        break;
+      case T_GATEUP:
+        need.push_back({l, T_NORM2, 0, s.B});
+        break;
+      case T_DOWN:  // the h columns of its K slice
+        rows(l, T_GATEUP, (int64_t)t.c * kWideK, (int64_t)(t.c + 1) * kWideK);
+        break;
+      case T_NORMF:
+        rows(s.L - 1, T_DOWN, 0, s.H);
+        break;
+      case T_LM:
+        need.push_back({s.L - 1, T_NORMF, 0, s.B});
+        break;
+      case T_ARGMAX:
+        rows(s.L - 1, T_LM, 0, s.V);
+        break;
+    }
+    return;
+  }
   switch (t.type) {
     case T_QKV:
-      if (s.wide) need.push_back({l, T_NORM, 0, s.B});
-      else if (l > 0) need.push_back({l - 1, T_DOWN, 0, s.H});
-      break;
-    case T_NORM:
       if (l > 0) need.push_back({l - 1, T_DOWN, 0, s.H});
-      break;
-    case T_NORM2:
-      need.push_back({l, T_OPROJ, 0, s.H});
-      break;
-    case T_NORMF:
-      need.push_back({s.L - 1, T_DOWN, 0, s.H});
       break;
     case T_ATTN: {
       const int64_t qa = (int64_t)t.g * s.G * s.D;
@@ -347,15 +490,13 @@ void inputs(const Shape& s, const Tile& t, std::vector<Need>& need) {
       need.push_back({l, T_COMBINE, 0, (int64_t)s.B * s.Hq * s.D});
       break;
     case T_GATEUP:
-      if (s.wide) need.push_back({l, T_NORM2, 0, s.B});
-      else need.push_back({l, T_OPROJ, 0, s.H});
+      need.push_back({l, T_OPROJ, 0, s.H});
       break;
     case T_DOWN:
       need.push_back({l, T_GATEUP, 0, s.F});
       break;
     case T_LM:
-      if (s.wide) need.push_back({s.L - 1, T_NORMF, 0, s.B});
-      else need.push_back({s.L - 1, T_DOWN, 0, s.H});
+      need.push_back({s.L - 1, T_DOWN, 0, s.H});
       break;
     case T_ARGMAX:
       need.push_back({s.L - 1, T_LM, 0, s.V});
@@ -413,10 +554,7 @@ std::string validate_dag(const Shape& s, const Dag& d) {
       at = p.second;
     }
     const int32_t type = kv.first.second;
-    const int64_t want = type == T_QKV ? s.qkv_rows
-                         : type == T_OPROJ || type == T_DOWN ? s.H
-                         : type == T_GATEUP ? s.F
-                         : type == T_LM ? s.V
+    const int64_t want = is_gemm(type) ? gemm_rows(s, type) * gemm_slices(s, type)
                          : type == T_ATTN ? (int64_t)s.B * s.Hkv * s.nch
                          : type == T_COMBINE ? (int64_t)s.B * s.Hq * s.D
                                              : s.B;
@@ -476,6 +614,7 @@ std::string check_device_geometry(const Shape& s, const Dag& d) {
   if ((int64_t)s.V * rb_h > lim || (int64_t)s.qkv_rows * rb_h > lim || (int64_t)s.F * rb_h > lim ||
       (int64_t)s.H * rb_f > lim || (int64_t)s.cap * s.D * s.elt > lim)
     return "a weight matrix or a KV cache slice exceeds 2 GiB";
+  if (s.wide) return "";  // wide tiles address rows per lane and clamp a ragged last block
   // a 4 KiB slice of a tile holds 256 / cpr whole rows when a row is shorter
   // than a slice; segments, tiles and matrices must break on whole slices
   for (const Tile& t : d.tiles) {

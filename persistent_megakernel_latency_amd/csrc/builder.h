@@ -31,6 +31,8 @@ struct Dag {
   std::vector<int32_t> queue;      // claim queues, concatenated
   std::vector<int32_t> queue_off;  // n_queues + 1 offsets
   int32_t n_shard_slots = 0;
+  int32_t n_fix = 0;     // wide plans: row blocks (arrival counters)
+  int32_t n_pslots = 0;  // wide plans: partial-sum slots (one per wide GEMM tile)
   // runs of tiles of one (layer, type), in order: the operators of the
   // conventional one-kernel-per-operator baseline
   std::vector<std::pair<int32_t, int32_t>> phases;

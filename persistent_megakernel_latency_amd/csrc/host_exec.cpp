@@ -232,19 +232,48 @@ void run_gemv(Ctx& c, const Tile& T) {
     default: w0 = w1 = P.embed; limit = P.V; break;
   }
   std::vector<float> x, y(T.rows);
+  // wide plans: this tile's K slice; its partial sums go to its slot, and the
+  // row block's last slice adds all slots in slice order
+  const int k0 = P.wide ? T.c * kWideK : 0, k1 = P.wide ? k0 + kWideK : K;
+  auto part = [&](int slice, int r, int b) -> float& {
+    return P.wpart[(int64_t)(T.pslot + slice) * kWidePart + ((b / 16) * kWideRows + r) * 16 + b % 16];
+  };
+  if (P.wide) {
+    for (int b = 0; b < P.B; ++b) {
+      gemv_input(c, T, b, x);
+      for (int r = 0; r < T.rows; ++r) {
+        const bool seg1 = r >= T.rs;
+        const int64_t mrow = std::min<int64_t>(seg1 ? T.r1 + (r - T.rs) : T.r0 + r, limit - 1);
+        const void* w = seg1 ? w1 : w0;
+        float acc = 0.f;
+        for (int k = k0; k < k1; ++k) acc += wval(w, P.dtype, mrow * K + k) * x[k];
+        part(T.c, r, b) = acc;
+      }
+    }
+    const uint32_t old = __atomic_fetch_add(&P.fixc[(int64_t)T.fix * kLine], 1u, __ATOMIC_ACQ_REL);
+    if ((int32_t)(old + 1u) != T.b) return;  // not the row block's last slice
+  }
   for (int b = 0; b < P.B; ++b) {
     const int32_t p = P.seq_len[b];
-    if (T.type == T_QKV && p < 0) continue;  // inactive slot: nothing to append
-    gemv_input(c, T, b, x);
-    for (int r = 0; r < T.rows; ++r) {
-      const bool seg1 = r >= T.rs;
-      const int64_t mrow = seg1 ? T.r1 + (r - T.rs) : T.r0 + r;
-      y[r] = 0.f;
-      if (mrow >= limit) continue;
-      const void* w = seg1 ? w1 : w0;
-      float acc = 0.f;
-      for (int k = 0; k < K; ++k) acc += wval(w, P.dtype, mrow * K + k) * x[k];
-      y[r] = acc;
+    if (T.type == T_QKV && p < 0) continue;
+    if (P.wide) {
+      for (int r = 0; r < T.rows; ++r) {
+        float acc = 0.f;
+        for (int sl = 0; sl < T.b; ++sl) acc += part(sl, r, b);
+        y[r] = acc;
+      }
+    } else {
+      gemv_input(c, T, b, x);
+      for (int r = 0; r < T.rows; ++r) {
+        const bool seg1 = r >= T.rs;
+        const int64_t mrow = seg1 ? T.r1 + (r - T.rs) : T.r0 + r;
+        y[r] = 0.f;
+        if (mrow >= limit) continue;
+        const void* w = seg1 ? w1 : w0;
+        float acc = 0.f;
+        for (int k = 0; k < K; ++k) acc += wval(w, P.dtype, mrow * K + k) * x[k];
+        y[r] = acc;
+      }
     }
     switch (T.type) {
       case T_QKV: {
@@ -486,6 +515,8 @@ Params host_params(wpk_plan* p, int32_t* tokens, wpk_kv* kv, float* logits) {
   P.off_xn2 = (int32_t)a.xn2;
   P.off_xh = (int32_t)a.xh;
   P.off_xnf = (int32_t)a.xnf;
+  P.wpart = p->hw.wpart.data();
+  P.fixc = p->hw.fixc.data();
   P.rope_cos = p->hw.rope_cos.data();
   P.rope_sin = p->hw.rope_sin.data();
   P.tokens = tokens;
@@ -505,6 +536,7 @@ void poison(wpk_plan* p, const Params& P) {
   float nanw;
   std::memcpy(&nanw, &nan2, 4);
   std::fill(p->hw.act.begin(), p->hw.act.end(), nanw);
+  std::fill(p->hw.wpart.begin(), p->hw.wpart.end(), nan);
   std::fill(P.logits, P.logits + (int64_t)P.B * P.V, nan);
   // the slot each active sequence is about to append: a read of it before the
   // tile that writes it sees NaN
@@ -576,6 +608,8 @@ wpk_plan* make_host_plan(const wpk_model_desc& d, int32_t batch, int32_t ctx_len
   const ActLayout a = act_layout(s);
   p->hw.act.assign((size_t)a.total, 0.f);
   fill_layers(s, p->desc, p->hw.act.data(), p->hw.layers);
+  p->hw.wpart.assign((size_t)p->dag.n_pslots * kWidePart, 0.f);
+  p->hw.fixc.assign((size_t)p->dag.n_fix * kLine, 0u);
   rope_table(s, p->hw.rope_cos, p->hw.rope_sin);
   p->hw.argmax.reset(new std::atomic<unsigned long long>[(size_t)s.B * kArgmaxShards]);
   for (int i = 0; i < s.B * kArgmaxShards; ++i) p->hw.argmax[i].store(0);
@@ -586,6 +620,7 @@ wpk_plan* make_host_plan(const wpk_model_desc& d, int32_t batch, int32_t ctx_len
 int32_t host_serial_step(wpk_plan* p, int32_t* tokens, wpk_kv* kv, float* logits, uint64_t seed, bool poison_on) {
   if (!args_ok(p, tokens, kv, logits)) return WPK_E_ARG;
   Params P = host_params(p, tokens, kv, logits);
+  std::fill(p->hw.fixc.begin(), p->hw.fixc.end(), 0u);
   if (poison_on) poison(p, P);
   std::atomic<int32_t> status{0};
   Ctx c{P, p->hw.argmax.get(), &status};
@@ -637,6 +672,7 @@ int32_t host_emulate_step(wpk_plan* p, int32_t* tokens, wpk_kv* kv, float* logit
     return WPK_E_ARG;
   }
   Params P = host_params(p, tokens, kv, logits);
+  std::fill(p->hw.fixc.begin(), p->hw.fixc.end(), 0u);
   std::atomic<int32_t> status{0};
   Ctx c{P, p->hw.argmax.get(), &status};
   std::unique_ptr<std::atomic<uint32_t>[]> counters(new std::atomic<uint32_t>[d.n_shard_slots]);

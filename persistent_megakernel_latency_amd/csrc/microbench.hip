@@ -404,6 +404,54 @@ static double time_ms(hipEvent_t a, hipEvent_t b) {
   return ms;
 }
 
+
+// ---------------------------------------------------------------------------
+// X/W streaming: each 256-thread block reads 64 KiB weight tiles from HBM
+// (non-temporal) and, per tile, XR x 64 KiB of a small activation buffer that
+// stays in L2 (device-coherent loads), either into registers in batches of 16
+// loads per thread (LDSX = false) or straight into a 32 KiB LDS area with
+// LDS-direct loads in batches of 8 per thread (LDSX = true).
+// ---------------------------------------------------------------------------
+template <bool LDSX>
+__global__ __launch_bounds__(256) void k_xw(const u32x4* __restrict__ w, long n_tiles, const float* xbuf,
+                                            int xr, unsigned* sink) {
+  __shared__ u32x4 lds[2048];  // 32 KiB
+  const int t = threadIdx.x;
+  uint32_t acc = 0;
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)xbuf, 0, 262144, 0x00020000);
+  for (long tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
+    const u32x4* p = w + tile * 4096;
+    u32x4 v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = __builtin_nontemporal_load(p + j * 256 + t);
+    for (int b = 0; b < xr * 16; b += 16) {
+      if (!LDSX) {
+        u32x4 x[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          x[j] = __builtin_amdgcn_raw_buffer_load_b128(r, ((uint32_t)((tile * 7 + b + j) * 256 + t) * 16u) & 262143u, 0, 16);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc += x[j].x ^ x[j].w;
+      } else {
+        const int wv = t >> 6, ln = t & 63;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                r, (__attribute__((address_space(3))) void*)&lds[wv * 512 + j * 64],
+                16, ((uint32_t)((tile * 7 + b + h * 8 + j) * 256 + t) * 16u) & 262143u, 0, 0, 16);
+          __builtin_amdgcn_s_waitcnt(0);
+          acc += lds[wv * 512 + (ln + h) % 512].x;
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+  }
+  if (acc == 0x9e3779b9u) sink[blockIdx.x * blockDim.x + t] = acc;
+}
+
 int main(int argc, char** argv) {
   int dev = 0;
   CHECK(hipSetDevice(dev));
@@ -477,6 +525,37 @@ int main(int argc, char** argv) {
     resid_case<576, 53840, 128, true>(d_out, n_cu);
     resid_case<320, 16384, 128, false>(d_out, 3 * n_cu);
     CHECK(hipFree(d_out));
+    return 0;
+  }
+  if (which == "xw") {
+    // weight tiles over 4 GiB plus xr x their bytes of L2-resident activations
+    float* xb = nullptr;
+    CHECK(hipMalloc(&xb, 262144));
+    CHECK(hipMemset(xb, 0, 262144));
+    for (int ldsx : {0, 1})
+      for (int xr : {0, 1, 2, 4})
+        for (int per_cu : {1, 2}) {
+          const int grid = n_cu * per_cu;
+          for (int rep = 0; rep < 2; ++rep) {
+            CHECK(hipEventRecord(e0));
+            if (ldsx)
+              hipLaunchKernelGGL(k_xw<true>, dim3(grid), dim3(256), 0, 0, reinterpret_cast<const u32x4*>(src),
+                                 n_tiles, xb, xr, sink);
+            else
+              hipLaunchKernelGGL(k_xw<false>, dim3(grid), dim3(256), 0, 0, reinterpret_cast<const u32x4*>(src),
+                                 n_tiles, xb, xr, sink);
+            CHECK(hipEventRecord(e1));
+            CHECK(hipEventSynchronize(e1));
+            CHECK(hipGetLastError());
+            const double ms = time_ms(e0, e1);
+            if (rep == 1)
+              printf("{\"bench\": \"xw\", \"lds_direct\": %d, \"x_per_w\": %d, \"blocks_per_cu\": %d, "
+                     "\"ms\": %.3f, \"w_GBps\": %.1f, \"total_GBps\": %.1f}\n",
+                     ldsx, xr, per_cu, ms, bytes / (ms * 1e6), bytes * (1.0 + xr) / (ms * 1e6));
+            fflush(stdout);
+          }
+        }
+    CHECK(hipFree(xb));
     return 0;
   }
   if (which == "copy") {

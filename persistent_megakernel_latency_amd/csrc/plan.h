@@ -37,9 +37,11 @@ struct Tile {
   int32_t r0, r1, rs;                 // GEMV: rows [r0, r0+rs) then [r1, r1+(rows-rs)) of its matrix
   int32_t rows;                       // GEMV: row capacity of the tile
   int32_t b, g, c;                    // ATTN: sequence, kv head, KV chunk; COMBINE, NORM*: b (, g); QKV: head
+                                      // wide GEMM tiles: b = slices of the row block, c = this tile's slice
   int32_t kind;                       // QKV: 0 q rows, 1 k rows, 2 v rows
   int32_t id;                         // tile id (index into the tile table and the log)
-  int32_t pad0, pad1;
+  int32_t fix;                        // wide GEMM tiles: row-block index (its arrival counter)
+  int32_t pslot;                      // wide GEMM tiles: partial-sum slot of the row block's slice 0
 };
 static_assert(sizeof(Tile) == 64, "tile descriptor is 64 bytes");
 
@@ -63,9 +65,12 @@ constexpr int kArgmaxShards = 16;
 constexpr int kMaxShards = 16;
 constexpr int kMaxBatch = 32;
 constexpr int kMaxBatchGemv = 4;   // above it a plan is wide: matrix-core tiles over all sequences
-constexpr int kGemmRows = 16;      // weight rows of a wide (matrix-core) tile
-constexpr int kGemmWK = 2048;      // K elements of one weight pass of a wide tile (64 KiB of bf16 rows)
-constexpr int kGemmXK = 1024;      // K elements of one staged operand piece (16 sequences, 32 KiB bf16)
+// Wide (matrix-core) tiles: 64 weight rows x a 512-column slice of K (64 KiB
+// of bf16), all sequences.  The slices of a row block each leave a partial
+// sum; the last one to finish adds them in slice order and runs the epilogue.
+constexpr int kWideRows = 64;
+constexpr int kWideK = 512;
+constexpr int kWidePart = kWideRows * kMaxBatch;  // floats of one partial-sum slot
 constexpr int kMaxLayers = 32;
 
 // Control block: word offsets, each field on its own 256-byte line.
@@ -130,6 +135,8 @@ struct Params {
   int32_t off_x_mid, off_x_out, off_q, off_part, off_attn, off_h;
   // wide plans: bf16 operand buffers, offsets in floats from the layer's base
   int32_t wide, off_xn1, off_xattn, off_xn2, off_xh, off_xnf;
+  float* wpart;             // wide plans: partial sums, kWidePart floats per slot
+  uint32_t* fixc;           // wide plans: arrival counter per row block, stride kLine
   LayerW lw[kMaxLayers];
   const float* rope_cos;  // [cap][D/2]
   const float* rope_sin;  // [cap][D/2]

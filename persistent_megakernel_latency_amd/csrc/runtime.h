@@ -17,6 +17,8 @@ struct HostWorkspace {
   std::vector<LayerBufs> layers;
   std::vector<float> rope_cos, rope_sin;      // [cap][D/2]
   std::unique_ptr<std::atomic<unsigned long long>[]> argmax;  // [B][kArgmaxShards]
+  std::vector<float> wpart;                   // wide plans: partial-sum slots
+  std::vector<uint32_t> fixc;                 // wide plans: arrival counters (stride kLine), zeroed per step
 };
 
 // RoPE table: cos/sin of pos * theta^(-2i/D), computed in float64, stored float32.

@@ -188,10 +188,12 @@ def test_full_cache_and_bad_token_are_errors():
 
 @pytest.mark.parametrize("batch", [8, 32])
 def test_wide_batch_plan_matches_oracle(batch):
-    """Batches above four use the matrix-core layout: norm tiles write bf16
-    operand rows, every projection tile covers 16 weight rows for all
-    sequences.  The serial executor of that DAG against the oracle, with
-    ragged lengths, an inactive slot and NaN poison."""
+    """Batches above four use the matrix-core layout: norm tiles write hi/lo
+    bf16 operand rows; every projection tile covers 64 weight rows and a
+    512-column K slice for all sequences, and the last slice of a row block
+    adds the partial sums in slice order.  The serial executor and the
+    threaded protocol emulator of that DAG against the oracle, with ragged
+    lengths, an inactive slot and NaN poison."""
     cfg = synth.MINI
     w = synth.make_weights(cfg, gain_std=0.1)
     model = oracle.Model(cfg, w)
@@ -206,7 +208,7 @@ def test_wide_batch_plan_matches_oracle(batch):
     plan = wpk.wpk_build_host(d.desc, batch, cap)
     assert plan, wpk.wpk_last_error(None)
     info = wpk.wpk_get_info(plan)
-    assert info.rows_per_tile_h == 16 and info.rows_per_tile_f == 16
+    assert info.rows_per_tile_h == 64 and info.rows_per_tile_f == 64
     ty, _, wait, signal = wpk.wpk_get_dag(plan, info.n_tiles)
     assert np.sum(np.array(ty) == 8) == cfg.n_layers * batch  # attention-norm rows
     ok_, ov_, osl = kc.copy(), vc.copy(), lens.copy()
@@ -221,6 +223,11 @@ def test_wide_batch_plan_matches_oracle(batch):
             ref = st
         else:
             assert np.array_equal(st.logits, ref.logits)
+    st = HostState(kc, vc, lens, tok, cfg.vocab)
+    assert st.emulate(plan, 9, 2) == 0, wpk.wpk_last_error(plan)
+    rc, log = wpk.wpk_get_log(plan, info.n_tiles)
+    check_log(log, wait, signal)
+    assert np.array_equal(st.logits, ref.logits)  # slice sums in a fixed order
     st = ref
     act = [b for b in range(batch) if lens[b] >= 0]
     for b in act:
@@ -232,3 +239,20 @@ def test_wide_batch_plan_matches_oracle(batch):
     assert st.tokens[1] == tok[1] and st.seq_len.tolist() == osl.tolist()
     assert np.array_equal(st.kc[:, 1], kc[:, 1])
     wpk.wpk_destroy(plan)
+
+
+def test_llama_1b_batch32_dag_shape():
+    """Wide Llama-1B plan: 64-row x 512-column tiles, the same tile counts per
+    operator as the batch-1 plan, a norm tile per sequence before each
+    normalised operand, and per-slice dependencies of o-proj and down."""
+    info, (ty, layer, wait, signal) = _info_and_dag(synth.LLAMA_1B, 32, 1088)
+    ty = np.array(ty)
+    per_layer = {0: 192, 3: 128, 4: 1024, 5: 512, 8: 32, 9: 32}
+    for t, n in per_layer.items():
+        assert np.sum(ty == t) == 16 * n, t
+    assert np.sum(ty == 1) == 16 * 32 * 8 * 17  # attention: sequences x kv heads x chunks
+    assert np.sum(ty == 6) == 8016 and np.sum(ty == 10) == 32 and np.sum(ty == 7) == 1
+    # down slice c waits only on the gate/up row blocks of its K slice
+    wait = np.array(wait)
+    down = np.nonzero((ty == 5) & (np.array(layer) == 0))[0]
+    assert len(set(wait[down].tolist())) == 16

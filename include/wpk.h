@@ -224,6 +224,12 @@ int32_t wpk_emulate_step(wpk_plan* plan, int32_t* tokens, wpk_kv* kv, float* log
 /* Test hook for the host executors: drop the wait of tile `tile` (it no longer
  * waits on its counter group), or with tile = -1 restore the built DAG. */
 int32_t wpk_debug_drop_edge(wpk_plan* plan, int32_t tile);
+/* Inspection hook: copies the plan's activation arena (all per-layer
+ * intermediate buffers, in the layout the host executors use, so the two can be
+ * compared buffer by buffer) into host memory.  bytes must be at least the
+ * arena size; *out_bytes receives it.  Device plans synchronize the device
+ * first.  Returns 0 or a negative WPK_E code. */
+int32_t wpk_debug_read_act(wpk_plan* plan, void* host_dst, size_t bytes, size_t* out_bytes);
 
 #ifdef __cplusplus
 }

@@ -92,6 +92,7 @@ _SIGNATURES = {
     "wpk_serial_step": (_i32, [_vp, _vp, ctypes.POINTER(wpk_kv), _vp, ctypes.c_uint64, _i32]),
     "wpk_emulate_step": (_i32, [_vp, _vp, ctypes.POINTER(wpk_kv), _vp, _i32, ctypes.c_uint64]),
     "wpk_debug_drop_edge": (_i32, [_vp, _i32]),
+    "wpk_debug_read_act": (_i32, [_vp, _vp, ctypes.c_size_t, ctypes.POINTER(ctypes.c_size_t)]),
 }
 
 _lib = None
@@ -188,6 +189,16 @@ def wpk_emulate_step(plan, tokens_ptr: int, kv: wpk_kv, logits_ptr: int, n_threa
 
 def wpk_debug_drop_edge(plan, tile: int) -> int:
     return lib().wpk_debug_drop_edge(plan, tile)
+
+
+def wpk_debug_read_act(plan):
+    """The plan's activation arena as float32 (host executors' layout)."""
+    import numpy as np
+    n = ctypes.c_size_t(0)
+    check(lib().wpk_debug_read_act(plan, None, 0, ctypes.byref(n)), plan, "wpk_debug_read_act")
+    out = np.empty(n.value // 4, np.float32)
+    check(lib().wpk_debug_read_act(plan, out.ctypes.data, n.value, ctypes.byref(n)), plan, "wpk_debug_read_act")
+    return out
 
 
 # ---- descriptor marshalling ------------------------------------------------------------

@@ -17,8 +17,8 @@
 #include "host_exec.h"
 #include "runtime.h"
 
-extern "C" int wpk_dev_kernels(int dtype, int cpr_h, int cpr_f, const void** mk, const void** mk_log,
-                               const void** phase);
+extern "C" int wpk_dev_kernels(int dtype, int cpr_h, int cpr_f, int wide, const void** mk, const void** mk_log,
+                               const void** phase, int* dyn_lds);
 extern "C" int wpk_dev_block_threads();
 
 using namespace wpk;
@@ -37,7 +37,8 @@ std::string hip_msg(const char* what, hipError_t e) { return std::string(what) +
 int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
 
 struct Layout {
-  int64_t ctl, heads, counters, argmax, tiles, groups, queue, queue_off, layers, rope_cos, rope_sin, act, log, total;
+  int64_t ctl, heads, counters, argmax, tiles, groups, queue, queue_off, layers, rope_cos, rope_sin, act, log,
+      wpart, fixc, total;
 };
 
 Layout layout(const Shape& s, const Dag& d, int32_t max_workers) {
@@ -63,6 +64,8 @@ Layout layout(const Shape& s, const Dag& d, int32_t max_workers) {
   L.act = take(act_layout(s).total * 4);
   // tile records, worker records, tile timings (two record sizes each)
   L.log = take((3 * (int64_t)d.tiles.size() + max_workers) * sizeof(wpk_log_rec));
+  L.wpart = take((int64_t)d.n_pslots * kWidePart * 4);
+  L.fixc = take((int64_t)d.n_fix * kLine * 4);
   L.total = at;
   return L;
 }
@@ -123,9 +126,15 @@ wpk_plan* build_device(const wpk_model_desc* desc, int32_t batch, int32_t ctx_le
   if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
     return fail(std::string("built for gfx950, found ") + prop.gcnArchName);
   const void *mk = nullptr, *mk_log = nullptr, *phase = nullptr;
-  if (!wpk_dev_kernels(s.dtype, s.cpr_h, s.cpr_f, &mk, &mk_log, &phase))
-    return fail("no kernel instance for this dtype / hidden / ffn (cpr_h=" + std::to_string(s.cpr_h) +
-                ", cpr_f=" + std::to_string(s.cpr_f) + ")");
+  int dyn = 0;
+  if (!wpk_dev_kernels(s.dtype, s.cpr_h, s.cpr_f, s.wide, &mk, &mk_log, &phase, &dyn))
+    return fail("no kernel instance for this dtype / hidden / ffn / batch (cpr_h=" + std::to_string(s.cpr_h) +
+                ", cpr_f=" + std::to_string(s.cpr_f) + ", wide=" + std::to_string(s.wide) + ")");
+  if (dyn > 0)
+    for (const void* k : {mk, mk_log, phase}) {
+      e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, dyn);
+      if (e != hipSuccess) return fail(hip_msg("dynamic LDS size", e));
+    }
 
   std::unique_ptr<wpk_plan> p(new wpk_plan());
   p->baseline = baseline;
@@ -143,12 +152,13 @@ wpk_plan* build_device(const wpk_model_desc* desc, int32_t batch, int32_t ctx_le
   p->k_mega = mk;
   p->k_mega_log = mk_log;
   p->k_phase = phase;
+  p->dyn_lds = dyn;
 
   int per_cu = 0, per_cu_log = 0;
   const int block = wpk_dev_block_threads();
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mk, block, 0);
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mk, block, dyn);
   if (e != hipSuccess) return fail(hip_msg("occupancy query", e));
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_log, mk_log, block, 0);
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_log, mk_log, block, dyn);
   if (e != hipSuccess) return fail(hip_msg("occupancy query", e));
   per_cu = std::min(per_cu, per_cu_log);
   p->max_workers = per_cu * p->n_cu;
@@ -202,6 +212,14 @@ wpk_plan* build_device(const wpk_model_desc* desc, int32_t batch, int32_t ctx_le
     P.off_part = (int32_t)a.part;
     P.off_attn = (int32_t)a.attn;
     P.off_h = (int32_t)a.h;
+    P.wide = s.wide;
+    P.off_xn1 = (int32_t)a.xn1;
+    P.off_xattn = (int32_t)a.xattn;
+    P.off_xn2 = (int32_t)a.xn2;
+    P.off_xh = (int32_t)a.xh;
+    P.off_xnf = (int32_t)a.xnf;
+    P.wpart = (float*)(w + L.wpart);
+    P.fixc = (uint32_t*)(w + L.fixc);
     for (int l = 0; l < s.L; ++l)
       P.lw[l] = LayerW{p->desc.w_qkv[l], p->desc.w_o[l], p->desc.w_gate[l], p->desc.w_up[l], p->desc.w_down[l],
                        p->desc.attn_norm[l], p->desc.mlp_norm[l]};
@@ -257,7 +275,7 @@ int32_t capture_baseline(wpk_plan* p) {
   for (const auto& ph : p->dag.phases) {
     int32_t first = ph.first;
     void* args[] = {(void*)&p->P, (void*)&first};
-    e = hipLaunchKernel(p->k_phase, dim3(ph.second), dim3(wpk_dev_block_threads()), args, 0, cs);
+    e = hipLaunchKernel(p->k_phase, dim3(ph.second), dim3(wpk_dev_block_threads()), args, p->dyn_lds, cs);
     if (e != hipSuccess) break;
   }
   hipGraph_t g = nullptr;
@@ -328,7 +346,7 @@ int32_t wpk_step(wpk_plan* p, int32_t* tokens, wpk_kv* kv, void* logits, wpk_str
   }
   void* args[] = {(void*)&P};
   e = hipLaunchCooperativeKernel(p->log_on ? p->k_mega_log : p->k_mega, dim3(p->workers),
-                                 dim3(wpk_dev_block_threads()), args, 0, st);
+                                 dim3(wpk_dev_block_threads()), args, p->dyn_lds, st);
   if (e != hipSuccess) return plan_fail(p, WPK_E_HIP, hip_msg("hipLaunchCooperativeKernel", e));
   return WPK_OK;
 }
@@ -425,6 +443,7 @@ int32_t wpk_set_option(wpk_plan* p, int32_t key, int64_t value) {
       if (e == hipSuccess) e = hipMemset(P.heads, 0, (size_t)P.n_queues * kLine * 4);
       if (e == hipSuccess) e = hipMemset(P.counters, 0, (size_t)p->dag.n_shard_slots * kLine * 4);
       if (e == hipSuccess) e = hipMemset(P.argmax, 0, (size_t)p->s.B * kArgmaxShards * 8);
+      if (e == hipSuccess && p->dag.n_fix) e = hipMemset(P.fixc, 0, (size_t)p->dag.n_fix * kLine * 4);
       if (e == hipSuccess) e = hipDeviceSynchronize();
       if (e != hipSuccess) return plan_fail(p, WPK_E_HIP, hip_msg("reset", e));
       p->latched = 0;
@@ -493,6 +512,22 @@ int32_t wpk_serial_step(wpk_plan* p, int32_t* tokens, wpk_kv* kv, float* logits,
 int32_t wpk_emulate_step(wpk_plan* p, int32_t* tokens, wpk_kv* kv, float* logits, int32_t n_threads, uint64_t seed) {
   if (!p || !p->host) return plan_fail(p, WPK_E_ARG, "wpk_emulate_step needs a host plan");
   return host_emulate_step(p, tokens, kv, logits, n_threads, seed);
+}
+
+int32_t wpk_debug_read_act(wpk_plan* p, void* dst, size_t bytes, size_t* out_bytes) {
+  if (!p) return plan_fail(nullptr, WPK_E_ARG, "null plan");
+  const size_t need = (size_t)act_layout(p->s).total * 4;
+  if (out_bytes) *out_bytes = need;
+  if (!dst) return WPK_OK;
+  if (bytes < need) return plan_fail(p, WPK_E_ARG, "buffer smaller than the activation arena");
+  if (p->host) {
+    std::memcpy(dst, p->hw.act.data(), need);
+    return WPK_OK;
+  }
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpy(dst, p->P.act, need, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return plan_fail(p, WPK_E_HIP, hip_msg("activation read", e));
+  return WPK_OK;
 }
 
 int32_t wpk_debug_drop_edge(wpk_plan* p, int32_t tile) {

@@ -46,7 +46,7 @@ ActLayout act_layout(const Shape& s) {
   a.part = at;  at += r64((int64_t)s.B * s.Hkv * s.nch * s.G * (s.D + 2));
   a.attn = at;  at += r64((int64_t)s.B * s.Hq * s.D);
   a.h = at;     at += r64((int64_t)s.B * s.F);
-  // bf16 [32][K] operands take 16 * K floats; rows past the batch stay zero
+  // wide operands: bf16 hi/lo planes [2][32][K] take 32 * K floats; rows past the batch stay zero
   const int64_t wb = s.wide ? (int64_t)kMaxBatch : 0;  // two bf16 planes of 32 rows
   a.xn1 = at;   at += r64(wb * s.H);
   a.xattn = at; at += r64(wb * s.Hq * s.D);
@@ -83,6 +83,7 @@ void fill_layers(const Shape& s, const wpk_model_desc& d, float* act, std::vecto
     lb.xh = (uint16_t*)(base + a.xh);
     lb.xnf = (uint16_t*)(base + a.xnf);
     lb.x_in = l == 0 ? nullptr : out[l - 1].x_out;
+    lb.final_norm = (const float*)d.final_norm;
   }
 }
 

@@ -50,6 +50,7 @@ namespace wpk {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kBlock = kThreads + 64;  // one control wave + four compute waves
 
@@ -135,6 +136,12 @@ __device__ __forceinline__ uint32_t atomic_add(uint32_t* p, uint32_t v) {
 __device__ __forceinline__ u32x4 ld_sc1_x4(const float* base, int32_t float_off) {
   const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, 0x7FFFFFFF, 0x00020000);
   return __builtin_amdgcn_raw_buffer_load_b128(r, float_off * 4, 0, 16 /* sc1 */);
+}
+
+// 16 bytes stored with a device-coherent (sc1) buffer store.
+__device__ __forceinline__ void st_sc1_x4(void* base, uint32_t byte_off, u32x4 v) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7FFFFFFF, 0x00020000);
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, 16 /* sc1 */);
 }
 
 // Read-only tables (tiles, groups, queues) through the constant address space:
@@ -522,7 +529,7 @@ __device__ __forceinline__ void cmp_attn(const Params& P, const Tile& T, Smem<WT
 // 16 with all of a batch's loads in flight together, and rescaling the running
 // sums when a batch raises the maximum.  The wave waits for its stores, so the
 // tile is complete when the control wave publishes after barrier B.
-template <typename WT, int KMAX>
+template <typename WT, bool WIDE, int KMAX>
 __device__ __forceinline__ void cmp_combine(const Params& P, const Tile& T, const Smem<WT, KMAX>& sm, int tc0) {
   const int tc = opaque(tc0);
   const int lane = tc & 63, h = tc >> 6;
@@ -558,12 +565,152 @@ __device__ __forceinline__ void cmp_combine(const Params& P, const Tile& T, cons
     O = fmaf(O, keep, ob);
     M = Mn;
   }
-  st_sc1(dst + lane, nact == 0 ? 0.f : O / L);
+  const float o = nact == 0 ? 0.f : O / L;
+  if (WIDE) {  // the o-proj operand: hi and lo bf16 planes
+    uint16_t* xa = (uint16_t*)act(P, T.layer, P.off_xattn);
+    const size_t at = (size_t)T.b * P.H + (size_t)(T.g * P.G + h) * P.D + lane;
+    const uint16_t hi = to_bf16(o);
+    st_sc1(xa + at, hi);
+    st_sc1(xa + (size_t)kMaxBatch * P.H + at, to_bf16(o - bf16_lo(hi)));
+  } else {
+    st_sc1(dst + lane, o);
+  }
   __builtin_amdgcn_s_waitcnt(0);
 }
 
-template <typename WT, int CPR_H, int CPR_F, int KMAX>
+// ---- wide (matrix-core) tiles ---------------------------------------------------------------
+//
+// Batches above four: a tile is 64 weight rows x a 512-column slice of K for
+// every sequence, on v_mfma_f32_16x16x32_bf16.  Compute wave w owns rows
+// [16w, 16w+16) of the tile; chunk j of its slot is the A fragment of k-step j
+// (lane l: row l % 16, columns 32j + 8(l / 16) .. +7).  The operand slice sits
+// in LDS as 1 KiB B fragments (lane l: sequence l % 16 of a half, the same
+// eight columns), hi and lo bf16 planes each: an operand value is hi + lo, so
+// the product keeps about 16 significant bits of the fp32 activation.  Each
+// slice leaves a partial sum of its rows; the row block's last slice to
+// arrive adds them in slice order and runs the epilogue.
+
+constexpr int kWideSteps = kWideK / 32;                     // k-steps of a slice
+constexpr int kWideFrags = kWideSteps * 2 * 2;              // x sequence halves x hi/lo planes
+constexpr int kWideKmax = kWideFrags * 256 + kWidePart;     // LDS floats: B fragments, then the partial sums
+
+__device__ __forceinline__ int wfrag(int ks, int h, int pl) { return (ks * 2 + h) * 2 + pl; }
+
+// The tile descriptor in scalar registers.  It is wave-uniform; this keeps
+// the compiler from indexing the kernel arguments (the per-layer weight
+// table) with a vector register, which it can only do from a private copy.
+__device__ __forceinline__ Tile uni(const Tile& T) {
+  int32_t w[16];
+  __builtin_memcpy(w, &T, sizeof(Tile));
+#pragma unroll
+  for (int i = 0; i < 16; ++i) w[i] = __builtin_amdgcn_readfirstlane(w[i]);
+  Tile U;
+  __builtin_memcpy(&U, w, sizeof(Tile));
+  return U;
+}
+
+template <typename WT, int KMAX>
+__device__ __forceinline__ float* cpart(Smem<WT, KMAX>& sm) {
+  return sm.xs + kWideFrags * 256;
+}
+
+// A wide tile's weight matrices (segment 0 and 1), K, row count, and the
+// operand buffer it reads.  Pointers come from the per-layer table in device
+// memory and kernel-argument values are read before they are selected: a
+// select between two kernel-argument addresses makes the compiler copy all the
+// arguments to private memory.
+struct WideOp {
+  const void* w0;
+  const void* w1;
+  const uint16_t* x;
+  int K, limit;
+};
+__device__ __forceinline__ WideOp wide_op(const Params& P, const Tile& T0) {
+  const Tile T = uni(T0);
+  const LayerBufs lb = cload(P.layers, T.layer);
+  const void* emb = P.embed;
+  int32_t H = P.H, F = P.F, V = P.V, R = P.qkv_rows;
+  asm volatile("" : "+s"(emb), "+s"(H), "+s"(F), "+s"(V), "+s"(R));
+  // the operand pointer: one of the five consecutive fields xn1 .. xnf of the
+  // table (an indexed scalar load, not a switch the compiler turns into a
+  // private lookup table)
+  const int xi = T.type == T_QKV ? 0 : T.type == T_OPROJ ? 1 : T.type == T_GATEUP ? 2 : T.type == T_DOWN ? 3 : 4;
+  const uint16_t* x = cload((const uint16_t* const*)&P.layers[T.layer].xn1, xi);
+  switch (T.type) {
+    case T_QKV: return WideOp{lb.w_qkv, lb.w_qkv, x, H, R};
+    case T_OPROJ: return WideOp{lb.w_o, lb.w_o, x, H, H};
+    case T_GATEUP: return WideOp{lb.w_gate, lb.w_up, x, H, F};
+    case T_DOWN: return WideOp{lb.w_down, lb.w_down, x, F, H};
+    default: return WideOp{emb, emb, x, H, V};  // LM head: tiles carry the last layer
+  }
+}
+
+// The slot of a wide tile: sixteen A fragments per compute wave.  Rows past
+// the matrix (a ragged last LM block) re-read its last row; their sums are
+// never stored.
+__device__ __forceinline__ void stage_wide(const Params& P, const Tile& T0, Slot& s, int tc0) {
+  const int tc = opaque(tc0);
+  const Tile T = uni(T0);
+  const int lane = tc & 63, w = __builtin_amdgcn_readfirstlane(tc >> 6);
+  const WideOp o = wide_op(P, T);
+  const bool seg1 = 16 * w >= T.rs;  // segments break on whole compute-wave row groups
+  const int r = 16 * w + (lane & 15);
+  const int mrow = min(seg1 ? T.r1 + (r - T.rs) : T.r0 + r, o.limit - 1);
+  const __amdgpu_buffer_rsrc_t rs = rsrc(seg1 ? o.w1 : o.w0);
+  const uint32_t voff = ((uint32_t)mrow * (uint32_t)o.K + (uint32_t)(T.c * kWideK + 8 * (lane >> 4))) * 2u;
+#pragma unroll
+  for (int j = 0; j < kChunks; ++j) s.c[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 64 * j, 2 /* nt */);
+}
+
+// The slice's products: per k-step, the A fragment times the hi and the lo B
+// fragment of each sequence half; then the 16 x 16 accumulators to the
+// partial-sum area, laid out as [half][tile row][16 sequences].
+template <typename WT, int KMAX>
+__device__ __forceinline__ void cmp_wide(const Params& P, const Slot& s, Smem<WT, KMAX>& sm, int tc0) {
+  const int tc = opaque(tc0);
+  const int lane = tc & 63, w = tc >> 6;
+  const bool two = P.B > 16;
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  const uint32_t* xf = (const uint32_t*)sm.xs + lane * 4;
+#pragma unroll
+  for (int ks = 0; ks < kWideSteps; ++ks) {
+    const bf16x8 a = __builtin_bit_cast(bf16x8, s.c[ks]);
+    const bf16x8 h0 = *(const bf16x8*)(xf + wfrag(ks, 0, 0) * 256);
+    const bf16x8 l0 = *(const bf16x8*)(xf + wfrag(ks, 0, 1) * 256);
+    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, h0, acc0, 0, 0, 0);
+    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, l0, acc0, 0, 0, 0);
+    if (two) {
+      const bf16x8 h1 = *(const bf16x8*)(xf + wfrag(ks, 1, 0) * 256);
+      const bf16x8 l1 = *(const bf16x8*)(xf + wfrag(ks, 1, 1) * 256);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, h1, acc1, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, l1, acc1, 0, 0, 0);
+    }
+  }
+  float* cp = cpart(sm);
+  const int row = 16 * w + 4 * (lane >> 4), s16 = lane & 15;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) cp[(row + i) * 16 + s16] = acc0[i];
+  if (two) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cp[(kWideRows + row + i) * 16 + s16] = acc1[i];
+  }
+}
+
+template <typename WT, int CPR_H, int CPR_F, bool WIDE, int KMAX>
 __device__ __forceinline__ void compute(const Params& P, const Tile& T, const Slot& s, Smem<WT, KMAX>& sm, int tc) {
+  if constexpr (WIDE) {
+    switch (T.type) {
+      case T_QKV:
+      case T_OPROJ:
+      case T_GATEUP:
+      case T_DOWN:
+      case T_LM: cmp_wide<WT>(P, s, sm, tc); break;
+      case T_ATTN: cmp_attn<WT>(P, T, sm, tc); break;
+      case T_COMBINE: cmp_combine<WT, true>(P, T, sm, tc); break;
+      default: break;  // norm and argmax tiles are control-wave work
+    }
+    return;
+  }
   switch (T.type) {
     case T_QKV:
     case T_OPROJ:
@@ -571,7 +718,7 @@ __device__ __forceinline__ void compute(const Params& P, const Tile& T, const Sl
     case T_LM: cmp_gemv<WT, CPR_H, true>(s, sm, tc); break;
     case T_DOWN: cmp_gemv<WT, CPR_F, false>(s, sm, tc); break;
     case T_ATTN: cmp_attn<WT>(P, T, sm, tc); break;
-    case T_COMBINE: cmp_combine<WT>(P, T, sm, tc); break;
+    case T_COMBINE: cmp_combine<WT, false>(P, T, sm, tc); break;
     default: break;  // argmax is control-wave work
   }
 }
@@ -852,11 +999,270 @@ __device__ __forceinline__ void ctl_argmax(const Params& P, const Smem<WT, KMAX>
   }
 }
 
-template <typename WT, int CPR_H, int CPR_F, int KMAX>
+// ---- wide tiles: control wave ---------------------------------------------------------------
+
+// The operand slice of a wide tile into LDS as B fragments: one LDS-direct
+// device-coherent load per 1 KiB fragment (lane l: sequence 16h + l % 16,
+// columns k0 + 32ks + 8(l / 16) .. +7 of the hi or lo plane), all in flight
+// together.  Sequences past the batch read the zero rows of the buffer.
+template <typename WT, int KMAX>
+__device__ __forceinline__ void ctl_stage_x(const Params& P, const Tile& T0, Smem<WT, KMAX>& sm, int lane0) {
+  const int lane = opaque(lane0);
+  const Tile T = uni(T0);
+  const WideOp o = wide_op(P, T);
+  const __amdgpu_buffer_rsrc_t r = rsrc(o.x);
+  const uint32_t voff = (uint32_t)((lane & 15) * o.K + 8 * (lane >> 4)) * 2u;
+  const int nh = P.B > 16 ? 2 : 1;
+  const int k0 = T.c * kWideK;
+  for (int h = 0; h < nh; ++h)
+#pragma unroll
+    for (int ks = 0; ks < kWideSteps; ++ks)
+#pragma unroll
+      for (int pl = 0; pl < 2; ++pl) {
+        const int soff = (pl * kMaxBatch * o.K + h * 16 * o.K + k0 + 32 * ks) * 2;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            r, (__attribute__((address_space(3))) void*)(sm.xs + wfrag(ks, h, pl) * 256), 16, voff, soff, 0,
+            16 /* sc1 */);
+      }
+  __builtin_amdgcn_s_waitcnt(0);
+}
+
+__device__ __forceinline__ void st_hilo(uint16_t* plane0, size_t plane_elems, size_t at, float v) {
+  const uint16_t hi = to_bf16(v);
+  st_sc1(plane0 + at, hi);
+  st_sc1(plane0 + plane_elems + at, to_bf16(v - bf16_lo(hi)));
+}
+
+// After barrier B of a wide tile: store this slice's partial sums, count its
+// arrival; the row block's last slice loads the others (LDS-direct, into the
+// operand area, up to 64 KiB at a time), adds all of them in slice order and
+// runs the epilogue.  Lane l holds sequence 16h + l % 16 of rows l / 16 + 4m.
+template <typename WT, int KMAX>
+__device__ __forceinline__ void ctl_wide_post(const Params& P, const Tile& T0, Smem<WT, KMAX>& sm, int lane0) {
+  const int lane = opaque(lane0);
+  const Tile T = uni(T0);
+  const int nh = P.B > 16 ? 2 : 1;
+  const int per = 4 * nh;  // 1 KiB pieces of a partial-sum slot
+  const float* cp = cpart(sm);
+  float* mine = P.wpart + (size_t)(T.pslot + T.c) * kWidePart;
+  for (int i = 0; i < per; ++i)
+    st_sc1_x4(mine, (uint32_t)(i * 64 + lane) * 16u, *(const u32x4*)(cp + (i * 64 + lane) * 4));
+  __builtin_amdgcn_s_waitcnt(0);
+  uint32_t old = 0;
+  if (lane == 0) old = atomic_add(&P.fixc[(size_t)T.fix * kLine], 1u);
+  old = __builtin_amdgcn_readfirstlane(__shfl(old, 0));
+  if ((int)old + 1 != T.b) return;
+  // the last slice: no other slice of this row block touches the counter
+  // again this step; it counts from zero in the next
+  if (lane == 0) st_sc1(&P.fixc[(size_t)T.fix * kLine], 0u);
+  float y[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) y[i] = 0.f;
+  const int q = lane >> 4, s16 = lane & 15;
+  const int fit = 16 / nh;  // slots the operand area holds
+  for (int s0 = 0; s0 < T.b; s0 += fit) {
+    const int s1 = min(T.b, s0 + fit);
+    for (int sl = s0; sl < s1; ++sl) {
+      if (sl == T.c) continue;
+      const __amdgpu_buffer_rsrc_t r = rsrc(P.wpart + (size_t)(T.pslot + sl) * kWidePart);
+      for (int i = 0; i < per; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            r, (__attribute__((address_space(3))) void*)(sm.xs + ((sl - s0) * per + i) * 256), 16,
+            (uint32_t)lane * 16u, i * 1024, 0, 16 /* sc1 */);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    for (int sl = s0; sl < s1; ++sl) {
+      const float* src = sl == T.c ? cp : sm.xs + (sl - s0) * per * 256;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int m = 0; m < 16; ++m)
+          if (h < nh) y[h * 16 + m] += src[(h * kWideRows + q + 4 * m) * 16 + s16];
+    }
+  }
+  const int l = T.layer;
+  switch (T.type) {
+    case T_QKV: {
+      const int half = P.D / 2;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (h >= nh) break;
+        const int n = 16 * h + s16;
+        const int p = n < P.B ? sm.pos[n] : -1;
+        if (p < 0) continue;  // past the batch, or an inactive slot: nothing to append
+        if (p >= P.cap) {
+          latch_error(P, WPK_E_CTX_FULL, T.id);
+          continue;
+        }
+        if (T.kind < 2) {
+          float* qd = act(P, l, P.off_q) + (size_t)n * P.Hq * P.D + T.g * P.D;
+          const size_t at = ((((size_t)l * P.B + n) * P.Hkv + T.g) * P.cap + p) * P.D;
+#pragma unroll
+          for (int m = 0; m < 8; ++m) {
+            const int dim = q + 4 * m;
+            const float a = y[h * 16 + m], b = y[h * 16 + m + 8];  // rows dim and dim + D/2
+            const float cs = P.rope_cos[p * half + dim], sn = P.rope_sin[p * half + dim];
+            const float ra = a * cs - b * sn, rb = b * cs + a * sn;
+            if (T.kind == 0) {
+              st_sc1(qd + dim, ra);
+              st_sc1(qd + dim + half, rb);
+            } else {
+              st_sc1((uint16_t*)P.kc + at + dim, to_bf16(ra));
+              st_sc1((uint16_t*)P.kc + at + dim + half, to_bf16(rb));
+            }
+          }
+        } else {
+          const size_t at = ((((size_t)l * P.B + n) * P.Hkv + T.g) * P.cap + p) * P.D;
+#pragma unroll
+          for (int m = 0; m < 16; ++m) st_sc1((uint16_t*)P.vc + at + q + 4 * m, to_bf16(y[h * 16 + m]));
+        }
+      }
+      break;
+    }
+    case T_OPROJ:
+    case T_DOWN: {
+      // o-proj: x_mid = x_in + y; down: x_out = x_mid + y (consecutive table fields)
+      const int d = T.type == T_OPROJ ? 0 : 1;
+      const LayerBufs* lbp = P.layers + l;
+      float* dst = cload((float* const*)&lbp->x_mid, d);
+      const float* res = cload((const float* const*)&lbp->x_in, d);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (h >= nh) break;
+        const int n = 16 * h + s16;
+        if (n >= P.B) continue;
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+          const int row = T.r0 + q + 4 * m;
+          float r;
+          if (res) {
+            r = ld_sc1(res + (size_t)n * P.H + row);
+          } else {  // layer 0: the residual is the token's embedding row
+            const WT* ep = (const WT*)P.embed + (size_t)sm.tok[n] * P.H + row;
+            r = sizeof(WT) == 2 ? bf16_lo(*(const uint16_t*)ep) : *(const float*)ep;
+          }
+          st_sc1(dst + (size_t)n * P.H + row, r + y[h * 16 + m]);
+        }
+      }
+      break;
+    }
+    case T_GATEUP: {
+      uint16_t* xh = (uint16_t*)act(P, l, P.off_xh);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (h >= nh) break;
+        const int n = 16 * h + s16;
+        if (n >= P.B) continue;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const float g = y[h * 16 + m], u = y[h * 16 + m + 8];  // gate row j, up row j
+          st_hilo(xh, (size_t)kMaxBatch * P.F, (size_t)n * P.F + T.r0 + q + 4 * m, g / (1.0f + __expf(-g)) * u);
+        }
+      }
+      break;
+    }
+    default: {  // LM head: logits and the block's per-sequence maximum
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (h >= nh) break;
+        const int n = 16 * h + s16;
+        unsigned long long key = 0;
+        if (n < P.B) {
+#pragma unroll
+          for (int m = 0; m < 16; ++m) {
+            const int row = T.r0 + q + 4 * m;
+            if (row < P.V) {
+              P.logits[(size_t)n * P.V + row] = y[h * 16 + m];
+              const unsigned long long k = pack_max(y[h * 16 + m], row);
+              key = k > key ? k : key;
+            }
+          }
+        }
+#pragma unroll
+        for (int x = 16; x < 64; x <<= 1) {
+          const unsigned long long o = __shfl_xor(key, x);
+          key = o > key ? o : key;
+        }
+        if (q == 0 && n < P.B)
+          __hip_atomic_fetch_max(&P.argmax[n * kArgmaxShards + T.id % kArgmaxShards], key, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+      }
+      break;
+    }
+  }
+}
+
+// A norm tile of a wide plan: one sequence's row (the embedding row at layer
+// 0), x / sqrt(mean(x^2) + eps) * gain, to the hi/lo operand planes.  Lane l
+// holds columns 512g + 8l .. +7.
+template <typename WT, int KMAX>
+__device__ __forceinline__ void ctl_norm(const Params& P, const Tile& T0, const Smem<WT, KMAX>& sm, int lane0) {
+  const int lane = opaque(lane0);
+  const Tile T = uni(T0);
+  const int l = T.layer, b = T.b, K = P.H;
+  const int ng = K / 512;
+  // Source row, gain and destination by indexing runs of consecutive pointers
+  // of the per-layer table (x_in, x_mid, x_out), (attn_norm, mlp_norm) and
+  // (xn1, xattn, xn2, xh, xnf): no select between pointers.  Final-norm tiles
+  // belong to the last layer.
+  const LayerBufs* lbp = P.layers + l;
+  const int which = T.type - T_NORM;  // 0 attention input, 1 MLP input, 2 final
+  const float* src = cload((const float* const*)&lbp->x_in, which);  // null: layer 0's embedding row
+  const float* gain = cload((const float* const*)&lbp->attn_norm, which < 2 ? which : 0);
+  const float* gf = cload((const float* const*)&lbp->final_norm, 0);
+  if (which == 2) gain = gf;
+  uint16_t* dst = cload((uint16_t* const*)&lbp->xn1, 2 * which);
+  float v[32];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    if (g >= ng) break;
+    const int e = 512 * g + 8 * lane;
+    if (src) {
+      const u32x4 a = ld_sc1_x4(src, b * K + e), c = ld_sc1_x4(src, b * K + e + 4);
+      v[8 * g + 0] = __uint_as_float(a.x); v[8 * g + 1] = __uint_as_float(a.y);
+      v[8 * g + 2] = __uint_as_float(a.z); v[8 * g + 3] = __uint_as_float(a.w);
+      v[8 * g + 4] = __uint_as_float(c.x); v[8 * g + 5] = __uint_as_float(c.y);
+      v[8 * g + 6] = __uint_as_float(c.z); v[8 * g + 7] = __uint_as_float(c.w);
+    } else {  // layer 0: the embedding row (bf16)
+      const u32x4 c = *(const u32x4*)((const uint16_t*)P.embed + (size_t)sm.tok[b] * K + e);
+      unpack<uint16_t>(c, &v[8 * g]);
+    }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i)
+    if (i < 8 * ng) ss = fmaf(v[i], v[i], ss);
+  ss = wave_sum(ss);
+  const float inv = 1.0f / sqrtf(ss / (float)K + P.eps);
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    if (g >= ng) break;
+    const int e = 512 * g + 8 * lane;
+    const f32x4 g0 = *(const f32x4*)(gain + e), g1 = *(const f32x4*)(gain + e + 4);
+    const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+      const float y0 = v[8 * g + i] * inv * gg[i], y1 = v[8 * g + i + 1] * inv * gg[i + 1];
+      const uint16_t h0 = to_bf16(y0), h1 = to_bf16(y1);
+      hw[i / 2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+      lw[i / 2] = (uint32_t)to_bf16(y0 - bf16_lo(h0)) | ((uint32_t)to_bf16(y1 - bf16_lo(h1)) << 16);
+    }
+    st_sc1_x4(dst, (uint32_t)(b * K + e) * 2u, u32x4{hw[0], hw[1], hw[2], hw[3]});
+    st_sc1_x4(dst, (uint32_t)((kMaxBatch + b) * K + e) * 2u, u32x4{lw[0], lw[1], lw[2], lw[3]});
+  }
+}
+
+template <typename WT, int CPR_H, int CPR_F, bool WIDE, int KMAX>
 __device__ __forceinline__ EpiIn ctl_pre(const Params& P, const Tile& T, int b, Smem<WT, KMAX>& sm, int lane,
                                          int& xkey) {
   constexpr int KH = CPR_H * 16 / sizeof(WT), KF = CPR_F * 16 / sizeof(WT);
   EpiIn e{0.f, 1.f, 0.f};
+  if constexpr (WIDE) {
+    if (is_gemv(T.type)) ctl_stage_x<WT>(P, T, sm, lane);
+    else if (T.type == T_ATTN) ctl_attn_in<WT>(P, T, sm, lane);
+    return e;
+  }
   if (is_gemv(T.type)) {
     // one activation row serves consecutive tiles of an operator (batch 1)
     const int key = T.layer * T_NTYPES + T.type;
@@ -887,9 +1293,25 @@ __device__ __forceinline__ EpiIn ctl_pre(const Params& P, const Tile& T, int b, 
   return e;
 }
 
-template <typename WT, int CPR_H, int CPR_F, int KMAX>
+template <typename WT, int CPR_H, int CPR_F, bool WIDE, int KMAX>
 __device__ __forceinline__ void ctl_post(const Params& P, const Tile& T, int b, Smem<WT, KMAX>& sm, const EpiIn& e,
                                          int lane) {
+  if constexpr (WIDE) {
+    switch (T.type) {
+      case T_QKV:
+      case T_OPROJ:
+      case T_GATEUP:
+      case T_DOWN:
+      case T_LM: ctl_wide_post<WT>(P, T, sm, lane); break;
+      case T_ATTN: ctl_attn_out<WT>(P, T, sm, lane); break;
+      case T_ARGMAX: ctl_argmax<WT>(P, sm, lane); break;
+      case T_NORM:
+      case T_NORM2:
+      case T_NORMF: ctl_norm<WT>(P, T, sm, lane); break;
+      default: break;
+    }
+    return;
+  }
   switch (T.type) {
     case T_DOWN: ctl_gemv_out<WT, CPR_F>(P, T, b, sm, e, lane); break;
     case T_QKV:
@@ -933,6 +1355,18 @@ __device__ __forceinline__ uint32_t hash32(uint32_t x) {
 
 // ============================ the worker loops ================================================
 
+// Barrier C (the tile is published before the compute waves stage the next
+// one) is skipped after LM-head tiles and wide tiles, whose epilogues may then
+// queue behind the next weights.  A wide tile's control wave reuses the
+// operand LDS area for the slice sums, so C stays when the next tile is an
+// attention tile (its compute waves fill that area before barrier A).
+template <bool WIDE>
+__device__ __forceinline__ bool need_c(const Params& P, const Tile& T, int nxt, int qb, int qn) {
+  if (!(T.type == T_LM || (WIDE && is_gemv(T.type)))) return true;
+  if (!WIDE || nxt >= qn) return false;
+  return cload(P.tiles, cload(P.queue, qb + nxt)).type == T_ATTN;
+}
+
 // Publishes a worker's run of LM-head tiles at once: their logits stores and
 // argmax updates have completed, then one increment by the run's length (the
 // group counts its total over all shards, so any shard serves).
@@ -945,7 +1379,7 @@ __device__ __forceinline__ void flush_lm(const Params& P, int group, int& count,
   count = 0;
 }
 
-template <typename WT, int CPR_H, int CPR_F, bool LOG, int KMAX>
+template <typename WT, int CPR_H, int CPR_F, bool LOG, bool WIDE, int KMAX>
 __device__ __forceinline__ void control_loop(const Params& P, Smem<WT, KMAX>& sm, int cur, int qb, int qn,
                                              uint32_t epoch, int lane0) {
   int it = 0;
@@ -978,10 +1412,10 @@ __device__ __forceinline__ void control_loop(const Params& P, Smem<WT, KMAX>& sm
     if (P.perturb)
       for (uint32_t k = hash32((uint32_t)id ^ P.perturb) & 31u; k; --k) __builtin_amdgcn_s_sleep(8);
     const uint64_t t_start = LOG ? __builtin_amdgcn_s_memrealtime() : 0;
-    const int npairs = is_gemv(T.type) ? P.B : 1;
+    const int npairs = !WIDE && is_gemv(T.type) ? P.B : 1;
     uint64_t t_inputs = 0, t_partials = 0, t_ready = 0, t_done = 0;
     for (int b = 0; b < npairs; ++b) {
-      const EpiIn e = ctl_pre<WT, CPR_H, CPR_F>(P, T, b, sm, lane, xkey);
+      const EpiIn e = ctl_pre<WT, CPR_H, CPR_F, WIDE>(P, T, b, sm, lane, xkey);
       if (LOG) {
         t_inputs = __builtin_amdgcn_s_memrealtime();
         if (lane == 0) sm.t_ready = sm.t_done = 0;
@@ -993,7 +1427,7 @@ __device__ __forceinline__ void control_loop(const Params& P, Smem<WT, KMAX>& sm
         t_ready = sm.t_ready;
         t_done = sm.t_done;
       }
-      ctl_post<WT, CPR_H, CPR_F>(P, T, b, sm, e, lane);
+      ctl_post<WT, CPR_H, CPR_F, WIDE>(P, T, b, sm, e, lane);
     }
     // publish: this wave made every global store of the tile; once they have
     // completed, one relaxed device-scope increment of the tile's counter shard
@@ -1029,10 +1463,11 @@ __device__ __forceinline__ void control_loop(const Params& P, Smem<WT, KMAX>& sm
     }
     // C: published; the compute waves may load the next tile.  LM-head tiles
     // skip it: only the final argmax depends on them, so their epilogue may
-    // queue behind the next weights, which then stream without a gap.
-    if (T.type != T_LM) __syncthreads();
-    // the next claim, written by compute wave 1 before this tile's barrier B
-    cur = __builtin_amdgcn_readfirstlane(sm.ids[(it + 1) & 1]);
+    // queue behind the next weights, which then stream without a gap.  The
+    // next claim was written by compute wave 1 before this tile's barrier B.
+    const int nxt = __builtin_amdgcn_readfirstlane(sm.ids[(it + 1) & 1]);
+    if (need_c<WIDE>(P, T, nxt, qb, qn)) __syncthreads();
+    cur = nxt;
     ++it;
   }
   if (lm_count) flush_lm(P, lm_group, lm_count, lane0);
@@ -1048,7 +1483,7 @@ __device__ __forceinline__ void launder(Slot& s) {
                "+v"(s.c[14]), "+v"(s.c[15]));
 }
 
-template <typename WT, int CPR_H, int CPR_F, bool LOG, int KMAX>
+template <typename WT, int CPR_H, int CPR_F, bool LOG, bool WIDE, int KMAX>
 __device__ __forceinline__ void compute_loop(const Params& P, Smem<WT, KMAX>& sm, int cur, int qb, int qn,
                                              uint32_t* head, int tc0) {
   const uint32_t voff = (uint32_t)tc0 * 16u;
@@ -1072,10 +1507,11 @@ __device__ __forceinline__ void compute_loop(const Params& P, Smem<WT, KMAX>& sm
     // without weight prefetch (an ablation), the weights are loaded only once
     // the control wave has seen the tile's inputs complete (barrier W)
     if (!P.prefetch) __syncthreads();  // W
-    stage<WT, CPR_H, CPR_F>(P, T, s, voff);
+    if (WIDE && is_gemv(T.type)) stage_wide(P, T, s, tc0);
+    else stage<WT, CPR_H, CPR_F>(P, T, s, voff);
     ++it;
     const int tc = opaque(tc0);
-    const int npairs = is_gemv(T.type) ? P.B : 1;
+    const int npairs = !WIDE && is_gemv(T.type) ? P.B : 1;
     bool stop = false;
     for (int b = 0; b < npairs; ++b) {
       if (T.type == T_ATTN && attn_count(P, T, sm.pos[T.b]) > 0) dump_kv<WT>(P, T, s, sm, tc);
@@ -1093,7 +1529,7 @@ __device__ __forceinline__ void compute_loop(const Params& P, Smem<WT, KMAX>& sm
       }
       if (b == 0 && tc == 0) sm.ids[(it + 1) & 1] = (int)ahead;  // for the control wave, read after B
       launder(s);
-      compute<WT, CPR_H, CPR_F>(P, T, s, sm, tc);
+      compute<WT, CPR_H, CPR_F, WIDE>(P, T, s, sm, tc);
       if (LOG && (tc & 63) == 0)
         __hip_atomic_fetch_max(&sm.t_done, (uint64_t)__builtin_amdgcn_s_memrealtime(), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -1104,7 +1540,7 @@ __device__ __forceinline__ void compute_loop(const Params& P, Smem<WT, KMAX>& sm
     // above it would keep two slots live.
     __builtin_amdgcn_sched_barrier(0);
     nx = __builtin_amdgcn_readfirstlane(sm.ids[(it + 1) & 1]);
-    if (T.type != T_LM) __syncthreads();  // C
+    if (need_c<WIDE>(P, T, nx, qb, qn)) __syncthreads();  // C
   }
 }
 
@@ -1135,10 +1571,28 @@ __device__ __forceinline__ void step_start(const Params& P, Smem<WT, KMAX>& sm, 
 
 // The worker loop: claim (from this worker's queue, in topological order),
 // stage the tile's weights, wait for its counter group, run it, publish.
-template <typename WT, int CPR_H, int CPR_F, bool LOG>
+// Wide instances take their LDS (about 77 KiB: the operand slice and the
+// partial sums) as dynamic shared memory: two workers still fit a CU's 160 KiB,
+// and the compiler, which only sees static LDS, keeps the register budget of
+// four waves per SIMD.
+template <typename WT, int CPR_H, int CPR_F, bool WIDE>
+struct Lds {
+  static constexpr int KMAX = WIDE ? kWideKmax : kmax<CPR_H, CPR_F, WT>();
+  using type = Smem<WT, KMAX>;
+};
+
+template <typename WT, int CPR_H, int CPR_F, bool LOG, bool WIDE>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void megakernel(Params P) {
-  constexpr int KMAX = kmax<CPR_H, CPR_F, WT>();
-  __shared__ Smem<WT, KMAX> sm;
+  using SM = typename Lds<WT, CPR_H, CPR_F, WIDE>::type;
+  SM* smp;
+  if constexpr (WIDE) {
+    extern __shared__ __align__(16) unsigned char wpk_dyn_lds[];
+    smp = reinterpret_cast<SM*>(wpk_dyn_lds);
+  } else {
+    __shared__ SM sm_static;
+    smp = &sm_static;
+  }
+  SM& sm = *smp;
   const int t = wpk_tid(), lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int q = (int)blockIdx.x % P.n_queues;
   const int qb = cload(P.queue_off, q), qn = cload(P.queue_off, q + 1) - qb;
@@ -1155,8 +1609,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
   }
   __syncthreads();
   const int cur = __builtin_amdgcn_readfirstlane(sm.first);
-  if (wave == 0) control_loop<WT, CPR_H, CPR_F, LOG>(P, sm, cur, qb, qn, epoch, lane);
-  else compute_loop<WT, CPR_H, CPR_F, LOG>(P, sm, cur, qb, qn, head, t - 64);
+  if (wave == 0) control_loop<WT, CPR_H, CPR_F, LOG, WIDE>(P, sm, cur, qb, qn, epoch, lane);
+  else compute_loop<WT, CPR_H, CPR_F, LOG, WIDE>(P, sm, cur, qb, qn, head, t - 64);
   // leave the step; the last worker out rewinds the queues and advances the epoch
   __syncthreads();
   if (LOG && t == 0) {
@@ -1181,35 +1635,44 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
 
 // One operator of the conventional baseline: one workgroup per tile, the same
 // tile bodies and roles, no counters; kernel boundaries order the operators.
-template <typename WT, int CPR_H, int CPR_F>
+template <typename WT, int CPR_H, int CPR_F, bool WIDE>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void phase_kernel(Params P, int first) {
-  constexpr int KMAX = kmax<CPR_H, CPR_F, WT>();
-  __shared__ Smem<WT, KMAX> sm;
+  using SM = typename Lds<WT, CPR_H, CPR_F, WIDE>::type;
+  SM* smp;
+  if constexpr (WIDE) {
+    extern __shared__ __align__(16) unsigned char wpk_dyn_lds[];
+    smp = reinterpret_cast<SM*>(wpk_dyn_lds);
+  } else {
+    __shared__ SM sm_static;
+    smp = &sm_static;
+  }
+  SM& sm = *smp;
   const int t = wpk_tid(), lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const Tile T = cload(P.tiles, first + (int)blockIdx.x);
   if (wave == 0) step_start<WT>(P, sm, lane, 0);
   __syncthreads();
-  const int npairs = is_gemv(T.type) ? P.B : 1;
+  const int npairs = !WIDE && is_gemv(T.type) ? P.B : 1;
   // the roles never share registers: the slot is live only in the compute waves
   if (wave == 0) {
     int xkey = -1;
     for (int b = 0; b < npairs; ++b) {
-      const EpiIn e = ctl_pre<WT, CPR_H, CPR_F>(P, T, b, sm, lane, xkey);
+      const EpiIn e = ctl_pre<WT, CPR_H, CPR_F, WIDE>(P, T, b, sm, lane, xkey);
       __syncthreads();  // A
       __syncthreads();  // B
-      ctl_post<WT, CPR_H, CPR_F>(P, T, b, sm, e, lane);
+      ctl_post<WT, CPR_H, CPR_F, WIDE>(P, T, b, sm, e, lane);
     }
   } else {
     const int tc = t - 64;
     Slot s;
 #pragma unroll
     for (int j = 0; j < kChunks; ++j) s.c[j] = u32x4{0u, 0u, 0u, 0u};
-    stage<WT, CPR_H, CPR_F>(P, T, s, (uint32_t)tc * 16u);
+    if (WIDE && is_gemv(T.type)) stage_wide(P, T, s, tc);
+    else stage<WT, CPR_H, CPR_F>(P, T, s, (uint32_t)tc * 16u);
     for (int b = 0; b < npairs; ++b) {
       if (T.type == T_ATTN && attn_count(P, T, sm.pos[T.b]) > 0) dump_kv<WT>(P, T, s, sm, tc);
       __syncthreads();  // A
       launder(s);
-      compute<WT, CPR_H, CPR_F>(P, T, s, sm, tc);
+      compute<WT, CPR_H, CPR_F, WIDE>(P, T, s, sm, tc);
       __syncthreads();  // B
     }
   }
@@ -1217,21 +1680,25 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
 
 }  // namespace wpk
 
-// Kernel handles for a (dtype, row geometry); 0 if that instance is not built.
-extern "C" int wpk_dev_kernels(int dtype, int cpr_h, int cpr_f, const void** mk, const void** mk_log,
-                               const void** phase) {
+// Kernel handles for a (dtype, row geometry, wide); 0 if that instance is not
+// built.  *dyn_lds: dynamic LDS bytes the instance is launched with.
+extern "C" int wpk_dev_kernels(int dtype, int cpr_h, int cpr_f, int wide, const void** mk, const void** mk_log,
+                               const void** phase, int* dyn_lds) {
   using namespace wpk;
-#define WPK_INST(DT, WT, H, F)                                                 \
-  if (dtype == DT && cpr_h == H && cpr_f == F) {                                \
-    *mk = reinterpret_cast<const void*>(&megakernel<WT, H, F, false>);          \
-    *mk_log = reinterpret_cast<const void*>(&megakernel<WT, H, F, true>);       \
-    *phase = reinterpret_cast<const void*>(&phase_kernel<WT, H, F>);            \
-    return 1;                                                                   \
+#define WPK_INST(DT, WT, H, F, W)                                                         \
+  if (dtype == DT && cpr_h == H && cpr_f == F && (wide != 0) == W) {                      \
+    *mk = reinterpret_cast<const void*>(&megakernel<WT, H, F, false, W>);                 \
+    *mk_log = reinterpret_cast<const void*>(&megakernel<WT, H, F, true, W>);              \
+    *phase = reinterpret_cast<const void*>(&phase_kernel<WT, H, F, W>);                   \
+    *dyn_lds = W ? (int)sizeof(typename Lds<WT, H, F, W>::type) : 0;                      \
+    return 1;                                                                             \
   }
-  WPK_INST(WPK_F32, float, 64, 256)        // hidden 256, ffn 1024, f32 (tiny)
-  WPK_INST(WPK_BF16, uint16_t, 256, 1024)  // hidden 2048, ffn 8192, bf16 (Llama-3.2-1B shape)
-  WPK_INST(WPK_BF16, uint16_t, 64, 128)    // hidden 512, ffn 1024, bf16
-  WPK_INST(WPK_BF16, uint16_t, 64, 256)    // hidden 512, ffn 2048, bf16
+  WPK_INST(WPK_F32, float, 64, 256, false)        // hidden 256, ffn 1024, f32 (tiny)
+  WPK_INST(WPK_BF16, uint16_t, 256, 1024, false)  // hidden 2048, ffn 8192, bf16 (Llama-3.2-1B shape)
+  WPK_INST(WPK_BF16, uint16_t, 64, 128, false)    // hidden 512, ffn 1024, bf16
+  WPK_INST(WPK_BF16, uint16_t, 64, 256, false)    // hidden 512, ffn 2048, bf16
+  WPK_INST(WPK_BF16, uint16_t, 256, 1024, true)   // Llama-3.2-1B shape, batches 5..32
+  WPK_INST(WPK_BF16, uint16_t, 64, 128, true)     // hidden 512, ffn 1024, batches 5..32
 #undef WPK_INST
   return 0;
 }

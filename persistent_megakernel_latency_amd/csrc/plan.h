@@ -83,6 +83,8 @@ enum : int32_t {
 };
 
 // Per-layer pointers: weights (caller-owned) and this layer's activations.
+// Field order matters to the wide kernels, which index runs of consecutive
+// pointers: (attn_norm, mlp_norm), (x_in, x_mid, x_out), (xn1 .. xnf).
 struct LayerBufs {
   const void* w_qkv;
   const void* w_o;
@@ -102,11 +104,13 @@ struct LayerBufs {
   // hi [32][K] then lo [32][K], with value = hi + lo (hi is the value rounded
   // to bf16, lo the remainder rounded to bf16: about 16 significant bits).
   // Rows past B stay zero.
+  // (xn1, xattn, xn2, xh, xnf are consecutive: the kernels index them)
   uint16_t* xn1;      // normalised attention input
   uint16_t* xattn;    // attention output
   uint16_t* xn2;      // normalised MLP input
   uint16_t* xh;       // SwiGLU output
   uint16_t* xnf;      // normalised final hidden state (last layer only)
+  const float* final_norm;  // the final RMSNorm gain (same in every layer)
 };
 
 // Per-layer weights as the kernels see them: kept inside the kernel arguments

@@ -67,6 +67,7 @@ struct wpk_plan {
   const void* k_mega = nullptr;     // kernel handles
   const void* k_mega_log = nullptr;
   const void* k_phase = nullptr;
+  int dyn_lds = 0;                  // dynamic LDS bytes of the kernels (wide plans)
   void* last_stream = nullptr;
   // baseline graph
   void* graph_exec = nullptr;

@@ -13,9 +13,11 @@ synchronize on each side; each launch is also bracketed by HIP events on the
 stream it runs on, which gives the per-step latency distribution and the
 kernel duration used for the roofline.  The same K steps are then run through
 the per-operator hipGraph baseline, and the CPU oracle is timed on a bounded
-sample of the same workload.
+sample of the same workload.  A second workload, batch 32 with per-sequence
+contexts drawn from U{256..1024} (the matrix-core path), is reported in the
+same line under "batch32", with its own graph baseline.
 
-    python bench.py [--steps 64] [--warmup 3] [--batch 1] [--no-cpu] [--no-baseline]
+    python bench.py [--steps 64] [--warmup 3] [--batch 1] [--no-cpu] [--no-baseline] [--no-batch32]
 """
 from __future__ import annotations
 
@@ -65,30 +67,17 @@ def traffic_from_profile(shash: str, per_launch_bytes: float):
     return t.get("hbm_bytes_per_launch")
 
 
-def run(args):
-    import torch
-
-    import persistent_megakernel_latency_amd as wpk
-    import synth
-
-    cfg = synth.LLAMA_1B
-    batch = args.batch
-    torch.cuda.init()
-    dev = torch.device("cuda", 0)
-    t0 = time.time()
-    weights = synth.make_weights(cfg)
-    desc, tensors = wpk.model_from_weights(cfg, weights, dev)
-    cap = int(np.ceil((CONTEXT + args.warmup + args.steps + 2) / 64.0) * 64)
-    lens0 = np.full(batch, CONTEXT, np.int32)
-    kc_np, vc_np = synth.synthetic_kv(cfg, batch, cap, lens0)
-    tok0 = synth.prompt_tokens(cfg, batch, CONTEXT)[:, -1].astype(np.int32)
+def measure(wpk, torch, cfg, desc, batch, lens0, tok0, args, dev, baseline: bool):
+    """Times K decode steps of one workload on the megakernel (and, if asked,
+    on the per-operator graph baseline) from the same starting state."""
+    cap = int(np.ceil((int(lens0.max()) + args.warmup + args.steps + 2) / 64.0) * 64)
+    kc_np, vc_np = synth_kv(cfg, batch, cap, lens0)
     kc = torch.from_numpy(kc_np.view(np.int16)).to(dev)
     vc = torch.from_numpy(vc_np.view(np.int16)).to(dev)
     seq = torch.from_numpy(lens0.copy()).to(dev)
     tokens = torch.from_numpy(tok0.copy()).to(dev)
     logits = torch.empty((batch, cfg.vocab), dtype=torch.float32, device=dev)
     kv = wpk.wpk_kv(kc.data_ptr(), vc.data_ptr(), seq.data_ptr())
-    setup_s = time.time() - t0
     stream = torch.cuda.current_stream(dev)
 
     def reset_state():
@@ -122,6 +111,51 @@ def run(args):
     info = wpk.wpk_get_info(plan)
     wall, per, byts = timed(plan, "megakernel")
     wpk.wpk_destroy(plan)
+    out = {"wall": wall, "per": per, "bytes": byts, "info": info, "kv": (kc_np, vc_np)}
+    if baseline:
+        bplan = wpk.wpk_build_graph_baseline(desc.desc, batch, cap)
+        if not bplan:
+            raise RuntimeError("baseline build: " + wpk.wpk_last_error(None))
+        bwall, bper, _ = timed(bplan, "graph baseline")
+        wpk.wpk_destroy(bplan)
+        out["baseline"] = {"value": round(bwall / args.steps * 1e6, 2), "unit": "µs/step",
+                           "latency_us": {"mean": round(float(bper.mean()), 2),
+                                          "p50": round(float(np.percentile(bper, 50)), 2),
+                                          "p95": round(float(np.percentile(bper, 95)), 2)},
+                           "megakernel_speedup": round(float(bper.mean() / per.mean()), 3)}
+    return out
+
+
+def synth_kv(cfg, batch, cap, lens):
+    import synth
+
+    return synth.synthetic_kv(cfg, batch, cap, lens)
+
+
+def lat(per):
+    return {"mean": round(float(per.mean()), 2), "p50": round(float(np.percentile(per, 50)), 2),
+            "p95": round(float(np.percentile(per, 95)), 2), "p99": round(float(np.percentile(per, 99)), 2),
+            "min": round(float(per.min()), 2)}
+
+
+def run(args):
+    import torch
+
+    import persistent_megakernel_latency_amd as wpk
+    import synth
+
+    cfg = synth.LLAMA_1B
+    batch = args.batch
+    torch.cuda.init()
+    dev = torch.device("cuda", 0)
+    t0 = time.time()
+    weights = synth.make_weights(cfg)
+    desc, tensors = wpk.model_from_weights(cfg, weights, dev)
+    lens0 = np.full(batch, CONTEXT, np.int32)
+    tok0 = synth.prompt_tokens(cfg, batch, CONTEXT)[:, -1].astype(np.int32)
+    setup_s = time.time() - t0
+    m = measure(wpk, torch, cfg, desc, batch, lens0, tok0, args, dev, not args.no_baseline)
+    wall, per, byts, info = m["wall"], m["per"], m["bytes"], m["info"]
 
     result = {
         "metric": METRIC,
@@ -140,9 +174,7 @@ def run(args):
                    "batch": batch, "context": CONTEXT, "layers": cfg.n_layers, "hidden": cfg.hidden,
                    "q_heads": cfg.n_q_heads, "kv_heads": cfg.n_kv_heads, "ffn": cfg.ffn, "vocab": cfg.vocab,
                    "workers": info.workers, "tiles_per_step": info.n_tiles},
-        "latency_us": {"mean": round(float(per.mean()), 2), "p50": round(float(np.percentile(per, 50)), 2),
-                       "p95": round(float(np.percentile(per, 95)), 2), "p99": round(float(np.percentile(per, 99)), 2),
-                       "min": round(float(per.min()), 2)},
+        "latency_us": lat(per),
         "tokens_per_s": round(batch * args.steps / wall, 1),
     }
     achieved = float(np.mean(byts) / (per.mean() * 1e-6) / 1e9)
@@ -153,20 +185,33 @@ def run(args):
                           "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                           "bytes_per_launch": round(float(np.mean(byts))), "kernel": "wpk::megakernel",
                           "kernel_us": round(float(per.mean()), 2), "source_hash": shash}
+    if "baseline" in m:
+        result["graph_baseline"] = m["baseline"]
 
-    if not args.no_baseline:
-        bplan = wpk.wpk_build_graph_baseline(desc.desc, batch, cap)
-        if not bplan:
-            raise RuntimeError("baseline build: " + wpk.wpk_last_error(None))
-        bwall, bper, _ = timed(bplan, "graph baseline")
-        wpk.wpk_destroy(bplan)
-        result["graph_baseline"] = {"value": round(bwall / args.steps * 1e6, 2), "unit": "µs/step",
-                                    "latency_us": {"mean": round(float(bper.mean()), 2),
-                                                   "p50": round(float(np.percentile(bper, 50)), 2),
-                                                   "p95": round(float(np.percentile(bper, 95)), 2)},
-                                    "megakernel_speedup": round(float(bper.mean() / per.mean()), 3)}
+    if not args.no_batch32:
+        # the batch-32 workload: contexts U{256..1024}, matrix-core projections
+        b32 = 32
+        lens32 = synth.context_lengths(b32)
+        tok32 = synth.prompt_tokens(cfg, b32, 1)[:, 0].astype(np.int32)
+        m32 = measure(wpk, torch, cfg, desc, b32, lens32, tok32, args, dev, not args.no_baseline)
+        w32, per32, by32 = m32["wall"], m32["per"], m32["bytes"]
+        gb = float(np.mean(by32) / (per32.mean() * 1e-6) / 1e9)
+        flops = 2.0 * cfg.n_matrix_params() * b32  # projections, MLP and LM head
+        result["batch32"] = {
+            "workload": "Llama-3.2-1B-shape decode step, batch 32, contexts U{256..1024}, greedy",
+            "value": round(w32 / args.steps * 1e6, 2), "unit": "µs/step", "latency_us": lat(per32),
+            "tokens_per_s": round(b32 * args.steps / w32, 1), "hbm_GBps": round(gb, 1),
+            "roofline": {"bound": "hbm", "achieved": round(gb, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(gb / HBM_PEAK_GBPS, 4), "bytes_per_launch": round(float(np.mean(by32)))},
+            "mfma": {"flops_per_step": flops, "achieved_TFLOPs": round(flops / (per32.mean() * 1e-6) / 1e12, 2),
+                     "peak_TFLOPs": 2500.0,
+                     "frac": round(flops / (per32.mean() * 1e-6) / 2.5e15, 4)},
+            "workers": m32["info"].workers, "tiles_per_step": m32["info"].n_tiles}
+        if "baseline" in m32:
+            result["batch32"]["graph_baseline"] = m32["baseline"]
 
     if not args.no_cpu:
+        kc_np, vc_np = m["kv"]
         result["cpu_baseline"] = cpu_baseline(cfg, weights, batch, kc_np, vc_np, lens0, tok0, args.cpu_seconds)
     result["setup_s"] = round(setup_s, 1)
     return result
@@ -201,6 +246,7 @@ def main():
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-baseline", action="store_true")
+    ap.add_argument("--no-batch32", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args()
     if args.gpus != 1:

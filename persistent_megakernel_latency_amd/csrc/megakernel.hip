@@ -311,11 +311,13 @@ struct SliceMap {
   bool gemv, attn;
   int limit, sh_spr, sr, rowb;
 
-  __device__ __forceinline__ SliceMap(const Params& P, const Tile& T) {
+  // active: false for an attention tile whose chunk lies past its sequence
+  // (nothing of it is read)
+  __device__ __forceinline__ SliceMap(const Params& P, const Tile& T, bool active = true) {
     const LayerW& lw = P.lw[T.layer];
     const int ty = T.type;
     gemv = is_gemv(ty);
-    attn = ty == T_ATTN;
+    attn = ty == T_ATTN && active;
     const void* w0 = P.embed;
     const void* w1 = P.embed;
     limit = P.V;
@@ -361,7 +363,7 @@ struct SliceMap {
 // columns this thread multiplies (loaded first, so waiting for them does not
 // wait for the weights).  Combine and argmax tiles read nothing of use.
 template <typename WT, int CPR_H, int CPR_F>
-__device__ __forceinline__ void stage(const Params& P, const Tile& T, Slot& s, uint32_t voff) {
+__device__ __forceinline__ void stage(const Params& P, const Tile& T, Slot& s, uint32_t voff, bool active = true) {
   static_assert(CPR_H <= kThreads, "gains in the slot cover one chunk per thread");
   constexpr int EPC = WT_<WT>::EPC;
   const LayerW& lw = P.lw[T.layer];
@@ -375,7 +377,7 @@ __device__ __forceinline__ void stage(const Params& P, const Tile& T, Slot& s, u
   } else {
     s.g[0] = s.g[1] = u32x4{0x3f800000u, 0x3f800000u, 0x3f800000u, 0x3f800000u};
   }
-  const SliceMap<WT, CPR_H, CPR_F> m(P, T);
+  const SliceMap<WT, CPR_H, CPR_F> m(P, T, active);
 #pragma unroll
   for (int j = 0; j < kChunks; ++j) {
     __amdgpu_buffer_rsrc_t r;
@@ -958,14 +960,14 @@ __device__ __forceinline__ void ctl_attn_in(const Params& P, const Tile& T, Smem
 template <typename WT, int KMAX>
 __device__ __forceinline__ void ctl_attn_out(const Params& P, const Tile& T, const Smem<WT, KMAX>& sm, int lane0) {
   const int lane = opaque(lane0);
-  const bool empty = attn_count(P, T, sm.pos[T.b]) == 0;
+  if (attn_count(P, T, sm.pos[T.b]) == 0) return;  // past the sequence: the combine never reads it
   float* out = act(P, T.layer, P.off_part) + ((((size_t)T.b * P.Hkv + T.g) * P.nch + T.c) * P.G) * (P.D + 2);
   for (int h = 0; h < P.G; ++h) {
     float* o = out + h * (P.D + 2);
-    st_sc1(o + 2 + lane, empty ? 0.f : sm.outs[h][2 + lane]);
+    st_sc1(o + 2 + lane, sm.outs[h][2 + lane]);
     if (lane == 0) {
-      st_sc1(o, empty ? -INFINITY : sm.outs[h][0]);
-      st_sc1(o + 1, empty ? 0.f : sm.outs[h][1]);
+      st_sc1(o, sm.outs[h][0]);
+      st_sc1(o + 1, sm.outs[h][1]);
     }
   }
 }
@@ -1398,7 +1400,11 @@ __device__ __forceinline__ void control_loop(const Params& P, Smem<WT, KMAX>& sm
     if (lm_count && T.type != T_LM) flush_lm(P, lm_group, lm_count, lane);
     int32_t delta = 0;
     bool ok = true;
-    if (T.wait >= 0 && (LOG || T.wait != done_group)) {
+    // an attention chunk past its sequence reads and writes nothing (its
+    // combine never reads it): it only publishes, without waiting, except in
+    // logged steps, which check that every tile starts after its producers
+    const bool idle = T.type == T_ATTN && attn_count(P, T, sm.pos[T.b]) == 0;
+    if (T.wait >= 0 && (LOG || (T.wait != done_group && !idle))) {
       ok = wait_group(P, T, epoch, &delta, lane);
       if (ok) done_group = T.wait;
     }
@@ -1508,7 +1514,7 @@ __device__ __forceinline__ void compute_loop(const Params& P, Smem<WT, KMAX>& sm
     // the control wave has seen the tile's inputs complete (barrier W)
     if (!P.prefetch) __syncthreads();  // W
     if (WIDE && is_gemv(T.type)) stage_wide(P, T, s, tc0);
-    else stage<WT, CPR_H, CPR_F>(P, T, s, voff);
+    else stage<WT, CPR_H, CPR_F>(P, T, s, voff, T.type != T_ATTN || attn_count(P, T, sm.pos[T.b]) > 0);
     ++it;
     const int tc = opaque(tc0);
     const int npairs = !WIDE && is_gemv(T.type) ? P.B : 1;
@@ -1667,7 +1673,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
 #pragma unroll
     for (int j = 0; j < kChunks; ++j) s.c[j] = u32x4{0u, 0u, 0u, 0u};
     if (WIDE && is_gemv(T.type)) stage_wide(P, T, s, tc);
-    else stage<WT, CPR_H, CPR_F>(P, T, s, (uint32_t)tc * 16u);
+    else stage<WT, CPR_H, CPR_F>(P, T, s, (uint32_t)tc * 16u,
+                                 T.type != T_ATTN || attn_count(P, T, sm.pos[T.b]) > 0);
     for (int b = 0; b < npairs; ++b) {
       if (T.type == T_ATTN && attn_count(P, T, sm.pos[T.b]) > 0) dump_kv<WT>(P, T, s, sm, tc);
       __syncthreads();  // A

@@ -83,6 +83,10 @@ std::string check_shape(const wpk_model_desc& d, int32_t batch, int32_t ctx_len,
   if (o.attn_chunk && o.attn_chunk != kAttnChunk) return "attn_chunk must be 64";
   s.qkv_rows = (s.Hq + 2 * s.Hkv) * s.D;
   s.nch = (s.cap + kAttnChunk - 1) / kAttnChunk;
+  // Batch 1-4: one KV chunk per attention tile (few tiles, as many in
+  // parallel as possible).  Wide plans have tiles to spare: as many chunks as
+  // the slot holds, so a tile's claim and hand-off cover more work.
+  s.attn_sub = s.wide ? kSlotBytes / (2 * kAttnChunk * s.D * s.elt) : 1;
   *out = s;
   return "";
 }
@@ -182,11 +186,12 @@ void build_wide(const Shape& s, Emitter& e) {
     }
     for (int32_t b = 0; b < s.B; ++b)
       for (int32_t g = 0; g < s.Hkv; ++g)
-        for (int32_t c = 0; c < s.nch; ++c) {
+        for (int32_t c = 0; c < s.nch; c += s.attn_sub) {
           Tile& t = e.tile(T_ATTN, l, g_attn[g], g_comb[b * s.Hkv + g]);
           t.b = b;
           t.g = g;
           t.c = c;
+          t.kind = std::min(s.attn_sub, s.nch - c);
         }
     for (int32_t b = 0; b < s.B; ++b)
       for (int32_t g = 0; g < s.Hkv; ++g) {
@@ -259,6 +264,7 @@ Dag build_dag(const Shape& s) {
           t.b = b;
           t.g = g;
           t.c = c;
+          t.kind = 1;
         }
     for (int32_t b = 0; b < s.B; ++b)
       for (int32_t g = 0; g < s.Hkv; ++g) {
@@ -385,9 +391,9 @@ void outputs(const Shape& s, const Tile& t, std::vector<std::pair<int64_t, int64
       out.emplace_back(at + p.first, at + p.second);
       break;
     }
-    case T_ATTN: {
+    case T_ATTN: {  // its KV chunks' partials
       const int64_t i = ((int64_t)t.b * s.Hkv + t.g) * s.nch + t.c;
-      out.emplace_back(i, i + 1);
+      out.emplace_back(i, i + t.kind);
       break;
     }
     case T_COMBINE: {

@@ -356,7 +356,18 @@ void run_gemv(Ctx& c, const Tile& T) {
   }
 }
 
+void run_attn_chunk(Ctx& c, const Tile& T);
+
+// An attention tile covers T.kind consecutive KV chunks, each its own partial.
 void run_attn(Ctx& c, const Tile& T) {
+  for (int u = 0; u < std::max(1, T.kind); ++u) {
+    Tile U = T;
+    U.c = T.c + u;
+    run_attn_chunk(c, U);
+  }
+}
+
+void run_attn_chunk(Ctx& c, const Tile& T) {
   const Params& P = c.P;
   const LayerBufs& lb = P.layers[T.layer];
   const int32_t p = P.seq_len[T.b];

@@ -298,8 +298,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p) {
 //    device plan keeps segment boundaries and tile sizes on whole slices, so a
 //    slice never straddles the two row segments.  Slices past a short tile or
 //    past the matrix re-read its last valid slice (their sums are never stored).
-//  * ATTN: slices of K then V of the tile's KV chunk; lanes past the cache
-//    capacity read its last chunk (those positions are never used).
+//  * ATTN: for each KV chunk of the tile in turn, slices of K then V; lanes
+//    past the cache capacity read its last chunk (those positions are never
+//    used); chunks past the sequence read nothing.
 //  * the remaining slots of an attention tile and every slot of a combine or
 //    argmax tile read one 16-byte word (no HBM traffic; the value is unused).
 template <typename WT, int CPR_H, int CPR_F>
@@ -311,13 +312,14 @@ struct SliceMap {
   bool gemv, attn;
   int limit, sh_spr, sr, rowb;
 
-  // active: false for an attention tile whose chunk lies past its sequence
-  // (nothing of it is read)
-  __device__ __forceinline__ SliceMap(const Params& P, const Tile& T, bool active = true) {
+  int n_valid;  // attention: positions of the sequence in the cache this step
+
+  __device__ __forceinline__ SliceMap(const Params& P, const Tile& T, int valid = 0) {
     const LayerW& lw = P.lw[T.layer];
     const int ty = T.type;
     gemv = is_gemv(ty);
-    attn = ty == T_ATTN && active;
+    attn = ty == T_ATTN;
+    n_valid = valid;
     const void* w0 = P.embed;
     const void* w1 = P.embed;
     limit = P.V;
@@ -349,13 +351,15 @@ struct SliceMap {
     const bool seg1 = row >= T.rs;
     const int mrow = min(seg1 ? T.r1 + (row - T.rs) : T.r0 + row, limit - sr);
     const int g_off = mrow * rowb + (j & ((1 << sh_spr) - 1)) * 4096;
-    const int p0 = min(T.c * kAttnChunk + (j % NS) * PPS, P.cap - 1);
-    const bool a_real = j < 2 * NS;
+    const int u = j / (2 * NS), jj = j % (2 * NS);  // chunk of the tile, slice within it
+    const int c = T.c + u;
+    const int p0 = min(c * kAttnChunk + (jj % NS) * PPS, P.cap - 1);
+    const bool a_real = u < T.kind && c * kAttnChunk < n_valid;
     const int a_off = a_real ? p0 * RB : 0;
     const uint32_t a_last = a_real ? (uint32_t)(P.cap - p0) * RB - 16u : 0u;
     soff = gemv ? g_off : (attn ? a_off : 0);
     last = gemv ? 0xFFFFFFF0u : (attn ? a_last : 0u);
-    r = (gemv ? seg1 : (attn && j >= NS && a_real)) ? rs1 : rs0;
+    r = (gemv ? seg1 : (attn && jj >= NS && a_real)) ? rs1 : rs0;
   }
 };
 
@@ -363,7 +367,7 @@ struct SliceMap {
 // columns this thread multiplies (loaded first, so waiting for them does not
 // wait for the weights).  Combine and argmax tiles read nothing of use.
 template <typename WT, int CPR_H, int CPR_F>
-__device__ __forceinline__ void stage(const Params& P, const Tile& T, Slot& s, uint32_t voff, bool active = true) {
+__device__ __forceinline__ void stage(const Params& P, const Tile& T, Slot& s, uint32_t voff, int n_valid = 0) {
   static_assert(CPR_H <= kThreads, "gains in the slot cover one chunk per thread");
   constexpr int EPC = WT_<WT>::EPC;
   const LayerW& lw = P.lw[T.layer];
@@ -377,7 +381,7 @@ __device__ __forceinline__ void stage(const Params& P, const Tile& T, Slot& s, u
   } else {
     s.g[0] = s.g[1] = u32x4{0x3f800000u, 0x3f800000u, 0x3f800000u, 0x3f800000u};
   }
-  const SliceMap<WT, CPR_H, CPR_F> m(P, T, active);
+  const SliceMap<WT, CPR_H, CPR_F> m(P, T, n_valid);
 #pragma unroll
   for (int j = 0; j < kChunks; ++j) {
     __amdgpu_buffer_rsrc_t r;
@@ -465,6 +469,30 @@ __device__ __forceinline__ void dump_kv(const Params& P, const Tile& T, const Sl
   }
 }
 
+// Positions of a sequence in the cache this step (its own position included).
+__device__ __forceinline__ int attn_valid(const Params& P, int p) { return p < 0 ? 0 : min(p + 1, P.cap); }
+
+// Slot chunks one KV chunk occupies (K then V of 64 positions).
+template <typename WT>
+constexpr int kv_chunks() {
+  return 2 * kAttnChunk * (kHeadDim * (int)sizeof(WT) / 16) / kThreads;
+}
+
+// The next KV chunk of a multi-chunk attention tile moves to the front of the
+// slot (register moves; the slot is never indexed with a run-time value).
+template <typename WT>
+__device__ __forceinline__ void slot_shift(Slot& s) {
+  constexpr int CH = kv_chunks<WT>();
+#pragma unroll
+  for (int j = 0; j + CH < kChunks; ++j) s.c[j] = s.c[j + CH];
+}
+
+__device__ __forceinline__ Tile sub_chunk(const Tile& T, int u) {
+  Tile U = T;
+  U.c = T.c + u;
+  return U;
+}
+
 __device__ __forceinline__ int attn_count(const Params& P, const Tile& T, int p) {
   const int n = p < 0 ? 0 : min(p + 1, P.cap);
   return max(0, min(kAttnChunk, n - T.c * kAttnChunk));
@@ -504,10 +532,12 @@ __device__ __forceinline__ void cmp_attn(const Params& P, const Tile& T, Smem<WT
   const float l = wave_sum(e);
   sm.ps[h][lane] = e;
   // weighted values: lane = head dimension, its transposed V row read 16 bytes
-  // at a time; positions past the chunk's count hold no data
+  // at a time over the whole chunk (all reads in flight together); positions
+  // past the chunk's count hold no data and are masked
   const WT* vr = sm.vt + lane * KP;
   float o0 = 0.f, o1 = 0.f;
-  for (int j0 = 0; j0 < cnt; j0 += EPC) {
+#pragma unroll
+  for (int j0 = 0; j0 < kAttnChunk; j0 += EPC) {
     float v[EPC];
     unpack<WT>(*(const u32x4*)(vr + j0), v);
 #pragma unroll
@@ -928,18 +958,14 @@ __device__ __forceinline__ void ctl_gemv_out(const Params& P, const Tile& T, int
   }
 }
 
-// Attention inputs: the group's queries and the K/V row appended this step.
+// Attention inputs: the K/V row appended this step, if it falls in this
+// chunk, and (first chunk of the tile only; they stay in LDS for the others)
+// the group's queries.
 template <typename WT, int KMAX>
-__device__ __forceinline__ void ctl_attn_in(const Params& P, const Tile& T, Smem<WT, KMAX>& sm, int lane0) {
-  const int lane = opaque(lane0);
+__device__ __forceinline__ void ctl_attn_patch(const Params& P, const Tile& T, Smem<WT, KMAX>& sm, int lane) {
   constexpr int KP = WT_<WT>::KP;
   const int p = sm.pos[T.b];
   const int start = T.c * kAttnChunk;
-  if (attn_count(P, T, p) == 0) return;
-  const float* q = act(P, T.layer, P.off_q) + (size_t)T.b * P.Hq * P.D + (size_t)T.g * P.G * P.D;
-  float qv[kMaxGroupHeads];
-#pragma unroll
-  for (int h = 0; h < kMaxGroupHeads; ++h) qv[h] = h < P.G ? ld_sc1(q + h * P.D + lane) : 0.f;
   if (p >= start && p < start + kAttnChunk && p < P.cap) {
     const size_t at = ((((size_t)T.layer * P.B + T.b) * P.Hkv + T.g) * P.cap + p) * kHeadDim + lane;
     WT* kd = sm.ks + (p - start) * KP + lane;
@@ -952,6 +978,22 @@ __device__ __forceinline__ void ctl_attn_in(const Params& P, const Tile& T, Smem
       *(float*)vd = ld_sc1((const float*)P.vc + at);
     }
   }
+}
+
+template <typename WT, int KMAX>
+__device__ __forceinline__ void ctl_attn_in(const Params& P, const Tile& T, Smem<WT, KMAX>& sm, int lane0,
+                                            bool first = true) {
+  const int lane = opaque(lane0);
+  if (attn_count(P, T, sm.pos[T.b]) == 0) return;
+  if (!first) {
+    ctl_attn_patch<WT>(P, T, sm, lane);
+    return;
+  }
+  const float* q = act(P, T.layer, P.off_q) + (size_t)T.b * P.Hq * P.D + (size_t)T.g * P.G * P.D;
+  float qv[kMaxGroupHeads];
+#pragma unroll
+  for (int h = 0; h < kMaxGroupHeads; ++h) qv[h] = h < P.G ? ld_sc1(q + h * P.D + lane) : 0.f;
+  ctl_attn_patch<WT>(P, T, sm, lane);
 #pragma unroll
   for (int h = 0; h < kMaxGroupHeads; ++h)
     if (h < P.G) sm.qs[h][lane] = qv[h];
@@ -1262,7 +1304,7 @@ __device__ __forceinline__ EpiIn ctl_pre(const Params& P, const Tile& T, int b, 
   EpiIn e{0.f, 1.f, 0.f};
   if constexpr (WIDE) {
     if (is_gemv(T.type)) ctl_stage_x<WT>(P, T, sm, lane);
-    else if (T.type == T_ATTN) ctl_attn_in<WT>(P, T, sm, lane);
+    else if (T.type == T_ATTN) ctl_attn_in<WT>(P, T, sm, lane, b == 0);
     return e;
   }
   if (is_gemv(T.type)) {
@@ -1289,7 +1331,7 @@ __device__ __forceinline__ EpiIn ctl_pre(const Params& P, const Tile& T, int b, 
       xkey = P.B > 1 ? -1 : key;
     }
   } else if (T.type == T_ATTN) {
-    ctl_attn_in<WT>(P, T, sm, lane);
+    ctl_attn_in<WT>(P, T, sm, lane, b == 0);
     xkey = -1;  // the K/V chunk overlays the activation row
   }
   return e;
@@ -1418,10 +1460,12 @@ __device__ __forceinline__ void control_loop(const Params& P, Smem<WT, KMAX>& sm
     if (P.perturb)
       for (uint32_t k = hash32((uint32_t)id ^ P.perturb) & 31u; k; --k) __builtin_amdgcn_s_sleep(8);
     const uint64_t t_start = LOG ? __builtin_amdgcn_s_memrealtime() : 0;
-    const int npairs = !WIDE && is_gemv(T.type) ? P.B : 1;
+    const int npairs = !WIDE && is_gemv(T.type) ? P.B : T.type == T_ATTN ? T.kind : 1;
     uint64_t t_inputs = 0, t_partials = 0, t_ready = 0, t_done = 0;
     for (int b = 0; b < npairs; ++b) {
-      const EpiIn e = ctl_pre<WT, CPR_H, CPR_F, WIDE>(P, T, b, sm, lane, xkey);
+      // an attention tile's passes are its KV chunks
+      const Tile Tb = T.type == T_ATTN ? sub_chunk(T, b) : T;
+      const EpiIn e = ctl_pre<WT, CPR_H, CPR_F, WIDE>(P, Tb, b, sm, lane, xkey);
       if (LOG) {
         t_inputs = __builtin_amdgcn_s_memrealtime();
         if (lane == 0) sm.t_ready = sm.t_done = 0;
@@ -1433,7 +1477,7 @@ __device__ __forceinline__ void control_loop(const Params& P, Smem<WT, KMAX>& sm
         t_ready = sm.t_ready;
         t_done = sm.t_done;
       }
-      ctl_post<WT, CPR_H, CPR_F, WIDE>(P, T, b, sm, e, lane);
+      ctl_post<WT, CPR_H, CPR_F, WIDE>(P, Tb, b, sm, e, lane);
     }
     // publish: this wave made every global store of the tile; once they have
     // completed, one relaxed device-scope increment of the tile's counter shard
@@ -1514,13 +1558,17 @@ __device__ __forceinline__ void compute_loop(const Params& P, Smem<WT, KMAX>& sm
     // the control wave has seen the tile's inputs complete (barrier W)
     if (!P.prefetch) __syncthreads();  // W
     if (WIDE && is_gemv(T.type)) stage_wide(P, T, s, tc0);
-    else stage<WT, CPR_H, CPR_F>(P, T, s, voff, T.type != T_ATTN || attn_count(P, T, sm.pos[T.b]) > 0);
+    else stage<WT, CPR_H, CPR_F>(P, T, s, voff, attn_valid(P, sm.pos[T.b]));
     ++it;
     const int tc = opaque(tc0);
-    const int npairs = !WIDE && is_gemv(T.type) ? P.B : 1;
+    const int npairs = !WIDE && is_gemv(T.type) ? P.B : T.type == T_ATTN ? T.kind : 1;
     bool stop = false;
     for (int b = 0; b < npairs; ++b) {
-      if (T.type == T_ATTN && attn_count(P, T, sm.pos[T.b]) > 0) dump_kv<WT>(P, T, s, sm, tc);
+      const Tile Tb = T.type == T_ATTN ? sub_chunk(T, b) : T;
+      if (T.type == T_ATTN) {
+        if (b > 0) slot_shift<WT>(s);
+        if (attn_count(P, Tb, sm.pos[T.b]) > 0) dump_kv<WT>(P, Tb, s, sm, tc);
+      }
       __syncthreads();  // A
       if (__builtin_amdgcn_readfirstlane(sm.stop)) {
         __syncthreads();  // B
@@ -1535,7 +1583,7 @@ __device__ __forceinline__ void compute_loop(const Params& P, Smem<WT, KMAX>& sm
       }
       if (b == 0 && tc == 0) sm.ids[(it + 1) & 1] = (int)ahead;  // for the control wave, read after B
       launder(s);
-      compute<WT, CPR_H, CPR_F, WIDE>(P, T, s, sm, tc);
+      compute<WT, CPR_H, CPR_F, WIDE>(P, Tb, s, sm, tc);
       if (LOG && (tc & 63) == 0)
         __hip_atomic_fetch_max(&sm.t_done, (uint64_t)__builtin_amdgcn_s_memrealtime(), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -1657,15 +1705,16 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
   const Tile T = cload(P.tiles, first + (int)blockIdx.x);
   if (wave == 0) step_start<WT>(P, sm, lane, 0);
   __syncthreads();
-  const int npairs = !WIDE && is_gemv(T.type) ? P.B : 1;
+  const int npairs = !WIDE && is_gemv(T.type) ? P.B : T.type == T_ATTN ? T.kind : 1;
   // the roles never share registers: the slot is live only in the compute waves
   if (wave == 0) {
     int xkey = -1;
     for (int b = 0; b < npairs; ++b) {
-      const EpiIn e = ctl_pre<WT, CPR_H, CPR_F, WIDE>(P, T, b, sm, lane, xkey);
+      const Tile Tb = T.type == T_ATTN ? sub_chunk(T, b) : T;
+      const EpiIn e = ctl_pre<WT, CPR_H, CPR_F, WIDE>(P, Tb, b, sm, lane, xkey);
       __syncthreads();  // A
       __syncthreads();  // B
-      ctl_post<WT, CPR_H, CPR_F, WIDE>(P, T, b, sm, e, lane);
+      ctl_post<WT, CPR_H, CPR_F, WIDE>(P, Tb, b, sm, e, lane);
     }
   } else {
     const int tc = t - 64;
@@ -1673,13 +1722,16 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
 #pragma unroll
     for (int j = 0; j < kChunks; ++j) s.c[j] = u32x4{0u, 0u, 0u, 0u};
     if (WIDE && is_gemv(T.type)) stage_wide(P, T, s, tc);
-    else stage<WT, CPR_H, CPR_F>(P, T, s, (uint32_t)tc * 16u,
-                                 T.type != T_ATTN || attn_count(P, T, sm.pos[T.b]) > 0);
+    else stage<WT, CPR_H, CPR_F>(P, T, s, (uint32_t)tc * 16u, attn_valid(P, sm.pos[T.b]));
     for (int b = 0; b < npairs; ++b) {
-      if (T.type == T_ATTN && attn_count(P, T, sm.pos[T.b]) > 0) dump_kv<WT>(P, T, s, sm, tc);
+      const Tile Tb = T.type == T_ATTN ? sub_chunk(T, b) : T;
+      if (T.type == T_ATTN) {
+        if (b > 0) slot_shift<WT>(s);
+        if (attn_count(P, Tb, sm.pos[T.b]) > 0) dump_kv<WT>(P, Tb, s, sm, tc);
+      }
       __syncthreads();  // A
       launder(s);
-      compute<WT, CPR_H, CPR_F, WIDE>(P, T, s, sm, tc);
+      compute<WT, CPR_H, CPR_F, WIDE>(P, Tb, s, sm, tc);
       __syncthreads();  // B
     }
   }

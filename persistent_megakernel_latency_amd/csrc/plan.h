@@ -38,7 +38,7 @@ struct Tile {
   int32_t rows;                       // GEMV: row capacity of the tile
   int32_t b, g, c;                    // ATTN: sequence, kv head, KV chunk; COMBINE, NORM*: b (, g); QKV: head
                                       // wide GEMM tiles: b = slices of the row block, c = this tile's slice
-  int32_t kind;                       // QKV: 0 q rows, 1 k rows, 2 v rows
+  int32_t kind;                       // QKV: 0 q rows, 1 k rows, 2 v rows; ATTN: KV chunks [c, c + kind)
   int32_t id;                         // tile id (index into the tile table and the log)
   int32_t fix;                        // wide GEMM tiles: row-block index (its arrival counter)
   int32_t pslot;                      // wide GEMM tiles: partial-sum slot of the row block's slice 0

@@ -250,7 +250,7 @@ def test_llama_1b_batch32_dag_shape():
     per_layer = {0: 192, 3: 128, 4: 1024, 5: 512, 8: 32, 9: 32}
     for t, n in per_layer.items():
         assert np.sum(ty == t) == 16 * n, t
-    assert np.sum(ty == 1) == 16 * 32 * 8 * 17  # attention: sequences x kv heads x chunks
+    assert np.sum(ty == 1) == 16 * 32 * 8 * 5  # attention: sequences x kv heads x 4-chunk groups of 17
     assert np.sum(ty == 6) == 8016 and np.sum(ty == 10) == 32 and np.sum(ty == 7) == 1
     # down slice c waits only on the gate/up row blocks of its K slice
     wait = np.array(wait)

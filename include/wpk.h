@@ -108,6 +108,10 @@ typedef struct wpk_build_opts {
   int32_t workers_per_cu;   /* resident workers per compute unit (default 2) */
   int32_t queue_shards;     /* claim queues the topological order is dealt over (default 8) */
   int32_t attn_chunk;       /* KV positions per attention partial tile (only 64 is built) */
+  int32_t forward;          /* LDS forwarding of attention partials (batches above 4): one chained
+                               tile per (sequence, kv head) walks its KV chunks and merges their
+                               partials on chip, with no combine tiles.  1: on; 0 (default) or -1:
+                               off (split tiles and combine tiles; faster at the built shapes) */
 } wpk_build_opts;
 
 typedef struct wpk_plan wpk_plan;
@@ -116,7 +120,9 @@ typedef struct wpk_plan wpk_plan;
  * workspace once and upload it.  Requirements: head_dim == 64,
  * n_q_heads * head_dim == hidden, n_q_heads / n_kv_heads <= 4, hidden and ffn
  * such that one weight row is 1..32 KiB and a power-of-two number of 16-byte
- * chunks, batch in [1, 4].  Returns NULL on error (see wpk_last_error(NULL)). */
+ * chunks, batch in [1, 32].  Batches above 4 run the projections, the MLP and
+ * the LM head on the matrix cores (bf16 weights; hidden and ffn multiples of
+ * 512, hidden at most 2048).  Returns NULL on error (see wpk_last_error(NULL)). */
 wpk_plan* wpk_build(const wpk_model_desc* desc, int32_t batch, int32_t ctx_len);
 wpk_plan* wpk_build_ex(const wpk_model_desc* desc, int32_t batch, int32_t ctx_len,
                        const wpk_build_opts* opts);

@@ -61,7 +61,8 @@ class wpk_kv(ctypes.Structure):
 
 
 class wpk_build_opts(ctypes.Structure):
-    _fields_ = [("tile_bytes", _i32), ("workers_per_cu", _i32), ("queue_shards", _i32), ("attn_chunk", _i32)]
+    _fields_ = [("tile_bytes", _i32), ("workers_per_cu", _i32), ("queue_shards", _i32), ("attn_chunk", _i32),
+                ("forward", _i32)]
 
 
 class wpk_log_rec(ctypes.Structure):

@@ -87,6 +87,9 @@ std::string check_shape(const wpk_model_desc& d, int32_t batch, int32_t ctx_len,
   // parallel as possible).  Wide plans have tiles to spare: as many chunks as
   // the slot holds, so a tile's claim and hand-off cover more work.
   s.attn_sub = s.wide ? kSlotBytes / (2 * kAttnChunk * s.D * s.elt) : 1;
+  if (o.forward < -1 || o.forward > 1) return "forward must be -1, 0 or 1";
+  s.forward = o.forward == 1;  // measured slower at the built shapes: off unless asked for
+  if (s.forward && !s.wide) return "LDS forwarding of attention partials is built for batches above 4";
   *out = s;
   return "";
 }
@@ -123,6 +126,15 @@ struct Emitter {
     t.r1 = r1;
     t.rs = rs;
     t.rows = rows;
+    return t;
+  }
+  // A chained attention tile: all KV chunks of (sequence b, kv head g).
+  Tile& attnc(int32_t layer, int32_t wait, int32_t signal, int32_t b, int32_t g, int32_t nch) {
+    Tile& t = tile(T_ATTNC, layer, wait, signal);
+    t.b = b;
+    t.g = g;
+    t.c = 0;
+    t.kind = nch;
     return t;
   }
   // The slices of one wide row block: slice c waits on wait_of(c); all signal
@@ -184,22 +196,27 @@ void build_wide(const Shape& s, Emitter& e) {
       e.wide(T_QKV, l, same(g_qkv_in), g_attn[g], kb, kb + D / 2, D / 2, s.H, 1, g);
       e.wide(T_QKV, l, same(g_qkv_in), g_attn[g], vb, vb + D / 2, D / 2, s.H, 2, g);
     }
-    for (int32_t b = 0; b < s.B; ++b)
-      for (int32_t g = 0; g < s.Hkv; ++g)
-        for (int32_t c = 0; c < s.nch; c += s.attn_sub) {
-          Tile& t = e.tile(T_ATTN, l, g_attn[g], g_comb[b * s.Hkv + g]);
+    if (s.forward) {  // each feeds the o-proj slice holding its kv head's q heads
+      for (int32_t b = 0; b < s.B; ++b)
+        for (int32_t g = 0; g < s.Hkv; ++g) e.attnc(l, g_attn[g], g_o[g * s.G * D / kWideK], b, g, s.nch);
+    } else {
+      for (int32_t b = 0; b < s.B; ++b)
+        for (int32_t g = 0; g < s.Hkv; ++g)
+          for (int32_t c = 0; c < s.nch; c += s.attn_sub) {
+            Tile& t = e.tile(T_ATTN, l, g_attn[g], g_comb[b * s.Hkv + g]);
+            t.b = b;
+            t.g = g;
+            t.c = c;
+            t.kind = std::min(s.attn_sub, s.nch - c);
+          }
+      for (int32_t b = 0; b < s.B; ++b)
+        for (int32_t g = 0; g < s.Hkv; ++g) {
+          // the o-proj slice holding this kv head's q heads
+          Tile& t = e.tile(T_COMBINE, l, g_comb[b * s.Hkv + g], g_o[g * s.G * D / kWideK]);
           t.b = b;
           t.g = g;
-          t.c = c;
-          t.kind = std::min(s.attn_sub, s.nch - c);
         }
-    for (int32_t b = 0; b < s.B; ++b)
-      for (int32_t g = 0; g < s.Hkv; ++g) {
-        // the o-proj slice holding this kv head's q heads
-        Tile& t = e.tile(T_COMBINE, l, g_comb[b * s.Hkv + g], g_o[g * s.G * D / kWideK]);
-        t.b = b;
-        t.g = g;
-      }
+    }
     for (int32_t r = 0; r < s.H; r += kWideRows)
       e.wide(T_OPROJ, l, [&](int32_t c) { return g_o[c]; }, g_xm, r, r + kWideRows, kWideRows, s.H);
     for (int32_t b = 0; b < s.B; ++b) e.tile(T_NORM2, l, g_xm, g_gu).b = b;
@@ -257,21 +274,26 @@ Dag build_dag(const Shape& s) {
         }
       }
     }
-    for (int32_t b = 0; b < s.B; ++b)
-      for (int32_t g = 0; g < s.Hkv; ++g)
-        for (int32_t c = 0; c < s.nch; ++c) {
-          Tile& t = e.tile(T_ATTN, l, g_attn[g], g_comb[b * s.Hkv + g]);
+    if (s.forward) {
+      for (int32_t b = 0; b < s.B; ++b)
+        for (int32_t g = 0; g < s.Hkv; ++g) e.attnc(l, g_attn[g], g_o, b, g, s.nch);
+    } else {
+      for (int32_t b = 0; b < s.B; ++b)
+        for (int32_t g = 0; g < s.Hkv; ++g)
+          for (int32_t c = 0; c < s.nch; ++c) {
+            Tile& t = e.tile(T_ATTN, l, g_attn[g], g_comb[b * s.Hkv + g]);
+            t.b = b;
+            t.g = g;
+            t.c = c;
+            t.kind = 1;
+          }
+      for (int32_t b = 0; b < s.B; ++b)
+        for (int32_t g = 0; g < s.Hkv; ++g) {
+          Tile& t = e.tile(T_COMBINE, l, g_comb[b * s.Hkv + g], g_o);
           t.b = b;
           t.g = g;
-          t.c = c;
-          t.kind = 1;
         }
-    for (int32_t b = 0; b < s.B; ++b)
-      for (int32_t g = 0; g < s.Hkv; ++g) {
-        Tile& t = e.tile(T_COMBINE, l, g_comb[b * s.Hkv + g], g_o);
-        t.b = b;
-        t.g = g;
-      }
+    }
     for (int32_t r = 0; r < s.H; r += s.rows_h) e.gemv(T_OPROJ, l, g_o, g_gu, r, r + s.rows_h, s.rows_h, s.rows_h);
     const int32_t rs_gu = s.rows_h / 2;
     for (int32_t j = 0; j < s.F; j += rs_gu) e.gemv(T_GATEUP, l, g_gu, g_dn, j, j, rs_gu, s.rows_h);
@@ -396,7 +418,8 @@ void outputs(const Shape& s, const Tile& t, std::vector<std::pair<int64_t, int64
       out.emplace_back(i, i + t.kind);
       break;
     }
-    case T_COMBINE: {
+    case T_COMBINE:
+    case T_ATTNC: {  // the attention output of its q heads
       const int64_t base = (int64_t)t.b * s.Hq * s.D + (int64_t)t.g * s.G * s.D;
       out.emplace_back(base, base + (int64_t)s.G * s.D);
       break;
@@ -411,6 +434,10 @@ void outputs(const Shape& s, const Tile& t, std::vector<std::pair<int64_t, int64
       break;
   }
 }
+
+// The tensor a tile type writes: a chained attention tile writes what a
+// combine tile would.
+int32_t out_type(int32_t type) { return type == T_ATTNC ? T_COMBINE : type; }
 
 struct Need {
   int32_t layer, type;
@@ -434,7 +461,8 @@ void inputs(const Shape& s, const Tile& t, std::vector<Need>& need) {
       case T_QKV:
         need.push_back({l, T_NORM, 0, s.B});
         break;
-      case T_ATTN: {
+      case T_ATTN:
+      case T_ATTNC: {
         const int64_t qa = (int64_t)t.g * s.G * s.D, ka = ((int64_t)s.Hq + t.g) * s.D,
                       va = ((int64_t)s.Hq + s.Hkv + t.g) * s.D;
         rows(l, T_QKV, qa, qa + (int64_t)s.G * s.D);
@@ -478,7 +506,8 @@ void inputs(const Shape& s, const Tile& t, std::vector<Need>& need) {
     case T_QKV:
       if (l > 0) need.push_back({l - 1, T_DOWN, 0, s.H});
       break;
-    case T_ATTN: {
+    case T_ATTN:
+    case T_ATTNC: {
       const int64_t qa = (int64_t)t.g * s.G * s.D;
       need.push_back({l, T_QKV, qa, qa + (int64_t)s.G * s.D});
       const int64_t ka = ((int64_t)s.Hq + t.g) * s.D;
@@ -543,7 +572,7 @@ std::string validate_dag(const Shape& s, const Dag& d) {
   std::vector<std::pair<int64_t, int64_t>> out;
   for (const Tile& t : d.tiles) {
     outputs(s, t, out);
-    auto& w = written[{t.layer, t.type}];
+    auto& w = written[{t.layer, out_type(t.type)}];
     for (auto& p : out)
       if (p.first < p.second) w.push_back(p);
   }
@@ -585,7 +614,7 @@ std::string validate_dag(const Shape& s, const Dag& d) {
       auto& cg = cover_of_group[t.wait];
       for (int32_t p : producers[t.wait]) {
         outputs(s, d.tiles[p], out);
-        for (auto& iv : out) cg[{d.tiles[p].layer, d.tiles[p].type}].add(iv.first, iv.second);
+        for (auto& iv : out) cg[{d.tiles[p].layer, out_type(d.tiles[p].type)}].add(iv.first, iv.second);
       }
       for (auto& c : cg) c.second.seal();
       it = cover_of_group.find(t.wait);

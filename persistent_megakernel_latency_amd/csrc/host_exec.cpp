@@ -495,6 +495,10 @@ void run_tile(Ctx& c, const Tile& T) {
     case T_NORMF: run_norm(c, T); break;
     case T_ATTN: run_attn(c, T); break;
     case T_COMBINE: run_combine(c, T); break;
+    case T_ATTNC:  // every chunk's partial, then their merge (the same tile)
+      run_attn(c, T);
+      run_combine(c, T);
+      break;
     case T_ARGMAX: run_argmax(c); break;
     default: run_gemv(c, T); break;
   }

@@ -318,7 +318,7 @@ struct SliceMap {
     const LayerW& lw = P.lw[T.layer];
     const int ty = T.type;
     gemv = is_gemv(ty);
-    attn = ty == T_ATTN;
+    attn = ty == T_ATTN || ty == T_ATTNC;
     n_valid = valid;
     const void* w0 = P.embed;
     const void* w1 = P.embed;
@@ -329,7 +329,8 @@ struct SliceMap {
       case T_OPROJ: w0 = w1 = lw.w_o; limit = P.H; break;
       case T_GATEUP: w0 = lw.w_gate; w1 = lw.w_up; limit = P.F; break;
       case T_DOWN: w0 = w1 = lw.w_down; limit = P.H; cpr = CPR_F; break;
-      case T_ATTN: {
+      case T_ATTN:
+      case T_ATTNC: {
         const size_t sl = ((((size_t)T.layer * P.B + T.b) * P.Hkv + T.g) * P.cap) * RB;
         w0 = P.kc + sl;
         w1 = P.vc + sl;
@@ -491,6 +492,82 @@ __device__ __forceinline__ Tile sub_chunk(const Tile& T, int u) {
   Tile U = T;
   U.c = T.c + u;
   return U;
+}
+
+__device__ __forceinline__ bool is_attn(int type) { return type == T_ATTN || type == T_ATTNC; }
+
+// KV chunks holding positions of the sequence this step.
+__device__ __forceinline__ int attn_active(const Params& P, int p) {
+  return (attn_valid(P, p) + kAttnChunk - 1) / kAttnChunk;
+}
+
+// Passes of a tile: the sequences of a narrow GEMV tile, the KV chunks of an
+// attention tile (a chained one: only the chunks holding positions), else one.
+template <bool WIDE>
+__device__ __forceinline__ int n_passes(const Params& P, const Tile& T, int p) {
+  if (!WIDE && is_gemv(T.type)) return P.B;
+  if (T.type == T_ATTN) return T.kind;
+  if (WIDE && T.type == T_ATTNC) return max(1, attn_active(P, p));  // at least one (empty) pass
+  return 1;
+}
+
+// The chunks of a chained attention tile the slot holds from chunk c0 on.
+template <typename WT>
+__device__ __forceinline__ Tile attn_group(const Tile& T, int c0) {
+  constexpr int S = kChunks / kv_chunks<WT>();
+  Tile G = T;
+  G.c = c0;
+  G.kind = min(S, T.kind - c0);
+  return G;
+}
+
+// Running merge of the chunk partials of a chained attention tile (control
+// wave; lane = head dimension): the combine, fed from LDS.
+struct AttnRun {
+  float M[kMaxGroupHeads], L[kMaxGroupHeads], O[kMaxGroupHeads];
+};
+__device__ __forceinline__ void attn_run_init(AttnRun& r) {
+#pragma unroll
+  for (int h = 0; h < kMaxGroupHeads; ++h) {
+    r.M[h] = -INFINITY;
+    r.L[h] = 0.f;
+    r.O[h] = 0.f;
+  }
+}
+template <typename WT, int KMAX>
+__device__ __forceinline__ void attn_run_merge(const Params& P, AttnRun& r, const Smem<WT, KMAX>& sm, int lane) {
+#pragma unroll
+  for (int h = 0; h < kMaxGroupHeads; ++h) {
+    if (h >= P.G) break;
+    // m and l are one value per head: scalar registers
+    const float m = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sm.outs[h][0])));
+    const float l = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sm.outs[h][1])));
+    const float o = sm.outs[h][2 + lane];
+    const float Mn = fmaxf(r.M[h], m);
+    const float keep = __expf(r.M[h] - Mn), w = __expf(m - Mn);
+    r.L[h] = fmaf(r.L[h], keep, l * w);
+    r.O[h] = fmaf(r.O[h], keep, o * w);
+    r.M[h] = Mn;
+  }
+}
+// The merged output of the group's q heads: fp32 rows, or the hi/lo operand
+// planes of the o-proj in a wide plan.  No chunk at all (an inactive slot): 0.
+template <bool WIDE>
+__device__ __forceinline__ void attn_run_store(const Params& P, const Tile& T, const AttnRun& r, int nact, int lane) {
+#pragma unroll
+  for (int h = 0; h < kMaxGroupHeads; ++h) {
+    if (h >= P.G) break;
+    const float o = nact == 0 ? 0.f : r.O[h] / r.L[h];
+    const size_t at = (size_t)T.b * P.H + (size_t)(T.g * P.G + h) * P.D + lane;
+    if (WIDE) {
+      uint16_t* xa = (uint16_t*)act(P, T.layer, P.off_xattn);
+      const uint16_t hi = to_bf16(o);
+      st_sc1(xa + at, hi);
+      st_sc1(xa + (size_t)kMaxBatch * P.H + at, to_bf16(o - bf16_lo(hi)));
+    } else {
+      st_sc1(act(P, T.layer, P.off_attn) + at, o);
+    }
+  }
 }
 
 __device__ __forceinline__ int attn_count(const Params& P, const Tile& T, int p) {
@@ -737,7 +814,8 @@ __device__ __forceinline__ void compute(const Params& P, const Tile& T, const Sl
       case T_GATEUP:
       case T_DOWN:
       case T_LM: cmp_wide<WT>(P, s, sm, tc); break;
-      case T_ATTN: cmp_attn<WT>(P, T, sm, tc); break;
+      case T_ATTN:
+      case T_ATTNC: cmp_attn<WT>(P, T, sm, tc); break;
       case T_COMBINE: cmp_combine<WT, true>(P, T, sm, tc); break;
       default: break;  // norm and argmax tiles are control-wave work
     }
@@ -749,7 +827,8 @@ __device__ __forceinline__ void compute(const Params& P, const Tile& T, const Sl
     case T_GATEUP:
     case T_LM: cmp_gemv<WT, CPR_H, true>(s, sm, tc); break;
     case T_DOWN: cmp_gemv<WT, CPR_F, false>(s, sm, tc); break;
-    case T_ATTN: cmp_attn<WT>(P, T, sm, tc); break;
+    case T_ATTN:
+    case T_ATTNC: cmp_attn<WT>(P, T, sm, tc); break;
     case T_COMBINE: cmp_combine<WT, false>(P, T, sm, tc); break;
     default: break;  // argmax is control-wave work
   }
@@ -1304,7 +1383,7 @@ __device__ __forceinline__ EpiIn ctl_pre(const Params& P, const Tile& T, int b, 
   EpiIn e{0.f, 1.f, 0.f};
   if constexpr (WIDE) {
     if (is_gemv(T.type)) ctl_stage_x<WT>(P, T, sm, lane);
-    else if (T.type == T_ATTN) ctl_attn_in<WT>(P, T, sm, lane, b == 0);
+    else if (is_attn(T.type)) ctl_attn_in<WT>(P, T, sm, lane, b == 0);
     return e;
   }
   if (is_gemv(T.type)) {
@@ -1330,7 +1409,7 @@ __device__ __forceinline__ EpiIn ctl_pre(const Params& P, const Tile& T, int b, 
       }
       xkey = P.B > 1 ? -1 : key;
     }
-  } else if (T.type == T_ATTN) {
+  } else if (is_attn(T.type)) {
     ctl_attn_in<WT>(P, T, sm, lane, b == 0);
     xkey = -1;  // the K/V chunk overlays the activation row
   }
@@ -1408,7 +1487,7 @@ template <bool WIDE>
 __device__ __forceinline__ bool need_c(const Params& P, const Tile& T, int nxt, int qb, int qn) {
   if (!(T.type == T_LM || (WIDE && is_gemv(T.type)))) return true;
   if (!WIDE || nxt >= qn) return false;
-  return cload(P.tiles, cload(P.queue, qb + nxt)).type == T_ATTN;
+  return is_attn(cload(P.tiles, cload(P.queue, qb + nxt)).type);
 }
 
 // Publishes a worker's run of LM-head tiles at once: their logits stores and
@@ -1445,7 +1524,7 @@ __device__ __forceinline__ void control_loop(const Params& P, Smem<WT, KMAX>& sm
     // an attention chunk past its sequence reads and writes nothing (its
     // combine never reads it): it only publishes, without waiting, except in
     // logged steps, which check that every tile starts after its producers
-    const bool idle = T.type == T_ATTN && attn_count(P, T, sm.pos[T.b]) == 0;
+    const bool idle = is_attn(T.type) && attn_count(P, T, sm.pos[T.b]) == 0;
     if (T.wait >= 0 && (LOG || (T.wait != done_group && !idle))) {
       ok = wait_group(P, T, epoch, &delta, lane);
       if (ok) done_group = T.wait;
@@ -1460,11 +1539,13 @@ __device__ __forceinline__ void control_loop(const Params& P, Smem<WT, KMAX>& sm
     if (P.perturb)
       for (uint32_t k = hash32((uint32_t)id ^ P.perturb) & 31u; k; --k) __builtin_amdgcn_s_sleep(8);
     const uint64_t t_start = LOG ? __builtin_amdgcn_s_memrealtime() : 0;
-    const int npairs = !WIDE && is_gemv(T.type) ? P.B : T.type == T_ATTN ? T.kind : 1;
+    const int npairs = n_passes<WIDE>(P, T, sm.pos[T.b]);
     uint64_t t_inputs = 0, t_partials = 0, t_ready = 0, t_done = 0;
+    AttnRun run;
+    attn_run_init(run);
     for (int b = 0; b < npairs; ++b) {
       // an attention tile's passes are its KV chunks
-      const Tile Tb = T.type == T_ATTN ? sub_chunk(T, b) : T;
+      const Tile Tb = is_attn(T.type) ? sub_chunk(T, b) : T;
       const EpiIn e = ctl_pre<WT, CPR_H, CPR_F, WIDE>(P, Tb, b, sm, lane, xkey);
       if (LOG) {
         t_inputs = __builtin_amdgcn_s_memrealtime();
@@ -1478,7 +1559,9 @@ __device__ __forceinline__ void control_loop(const Params& P, Smem<WT, KMAX>& sm
         t_done = sm.t_done;
       }
       ctl_post<WT, CPR_H, CPR_F, WIDE>(P, Tb, b, sm, e, lane);
+      if (WIDE && T.type == T_ATTNC && attn_count(P, Tb, sm.pos[T.b]) > 0) attn_run_merge(P, run, sm, lane);
     }
+    if (WIDE && T.type == T_ATTNC) attn_run_store<WIDE>(P, T, run, attn_active(P, sm.pos[T.b]), lane);
     // publish: this wave made every global store of the tile; once they have
     // completed, one relaxed device-scope increment of the tile's counter shard
     const bool batch = T.type == T_LM && T.signal >= 0;
@@ -1557,16 +1640,24 @@ __device__ __forceinline__ void compute_loop(const Params& P, Smem<WT, KMAX>& sm
     // without weight prefetch (an ablation), the weights are loaded only once
     // the control wave has seen the tile's inputs complete (barrier W)
     if (!P.prefetch) __syncthreads();  // W
+    const int valid = attn_valid(P, sm.pos[T.b]);
     if (WIDE && is_gemv(T.type)) stage_wide(P, T, s, tc0);
-    else stage<WT, CPR_H, CPR_F>(P, T, s, voff, attn_valid(P, sm.pos[T.b]));
+    else stage<WT, CPR_H, CPR_F>(P, WIDE && T.type == T_ATTNC ? attn_group<WT>(T, 0) : T, s, voff, valid);
     ++it;
     const int tc = opaque(tc0);
-    const int npairs = !WIDE && is_gemv(T.type) ? P.B : T.type == T_ATTN ? T.kind : 1;
+    const int npairs = n_passes<WIDE>(P, T, sm.pos[T.b]);
     bool stop = false;
     for (int b = 0; b < npairs; ++b) {
-      const Tile Tb = T.type == T_ATTN ? sub_chunk(T, b) : T;
-      if (T.type == T_ATTN) {
-        if (b > 0) slot_shift<WT>(s);
+      const Tile Tb = is_attn(T.type) ? sub_chunk(T, b) : T;
+      if (is_attn(T.type)) {
+        // the next KV chunk: already in the slot, or (chained tiles) the
+        // slot's next fill
+        if (b > 0) {
+          if (WIDE && T.type == T_ATTNC && b % (kChunks / kv_chunks<WT>()) == 0)
+            stage<WT, CPR_H, CPR_F>(P, attn_group<WT>(T, b), s, voff, valid);
+          else
+            slot_shift<WT>(s);
+        }
         if (attn_count(P, Tb, sm.pos[T.b]) > 0) dump_kv<WT>(P, Tb, s, sm, tc);
       }
       __syncthreads();  // A
@@ -1705,28 +1796,39 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
   const Tile T = cload(P.tiles, first + (int)blockIdx.x);
   if (wave == 0) step_start<WT>(P, sm, lane, 0);
   __syncthreads();
-  const int npairs = !WIDE && is_gemv(T.type) ? P.B : T.type == T_ATTN ? T.kind : 1;
+  const int npairs = n_passes<WIDE>(P, T, sm.pos[T.b]);
   // the roles never share registers: the slot is live only in the compute waves
   if (wave == 0) {
     int xkey = -1;
+    AttnRun run;
+    attn_run_init(run);
     for (int b = 0; b < npairs; ++b) {
-      const Tile Tb = T.type == T_ATTN ? sub_chunk(T, b) : T;
+      const Tile Tb = is_attn(T.type) ? sub_chunk(T, b) : T;
       const EpiIn e = ctl_pre<WT, CPR_H, CPR_F, WIDE>(P, Tb, b, sm, lane, xkey);
       __syncthreads();  // A
       __syncthreads();  // B
       ctl_post<WT, CPR_H, CPR_F, WIDE>(P, Tb, b, sm, e, lane);
+      if (WIDE && T.type == T_ATTNC && attn_count(P, Tb, sm.pos[T.b]) > 0) attn_run_merge(P, run, sm, lane);
     }
+    if (WIDE && T.type == T_ATTNC) attn_run_store<WIDE>(P, T, run, attn_active(P, sm.pos[T.b]), lane);
   } else {
     const int tc = t - 64;
     Slot s;
 #pragma unroll
     for (int j = 0; j < kChunks; ++j) s.c[j] = u32x4{0u, 0u, 0u, 0u};
+    const int valid = attn_valid(P, sm.pos[T.b]);
+    const uint32_t voff = (uint32_t)tc * 16u;
     if (WIDE && is_gemv(T.type)) stage_wide(P, T, s, tc);
-    else stage<WT, CPR_H, CPR_F>(P, T, s, (uint32_t)tc * 16u, attn_valid(P, sm.pos[T.b]));
+    else stage<WT, CPR_H, CPR_F>(P, WIDE && T.type == T_ATTNC ? attn_group<WT>(T, 0) : T, s, voff, valid);
     for (int b = 0; b < npairs; ++b) {
-      const Tile Tb = T.type == T_ATTN ? sub_chunk(T, b) : T;
-      if (T.type == T_ATTN) {
-        if (b > 0) slot_shift<WT>(s);
+      const Tile Tb = is_attn(T.type) ? sub_chunk(T, b) : T;
+      if (is_attn(T.type)) {
+        if (b > 0) {
+          if (WIDE && T.type == T_ATTNC && b % (kChunks / kv_chunks<WT>()) == 0)
+            stage<WT, CPR_H, CPR_F>(P, attn_group<WT>(T, b), s, voff, valid);
+          else
+            slot_shift<WT>(s);
+        }
         if (attn_count(P, Tb, sm.pos[T.b]) > 0) dump_kv<WT>(P, Tb, s, sm, tc);
       }
       __syncthreads();  // A

@@ -27,7 +27,11 @@ enum TileType : int32_t {
   T_NORM = 8,     // attention-input RMSNorm (layer 0: of the embedding row)
   T_NORM2 = 9,    // MLP-input RMSNorm
   T_NORMF = 10,   // final RMSNorm before the LM head
-  T_NTYPES = 11
+  // LDS forwarding: attention over every KV chunk of one (sequence, kv head),
+  // each chunk's partial merged on chip into the next (the combine chained
+  // onto the same worker; no partials in global memory, no combine tile)
+  T_ATTNC = 11,
+  T_NTYPES = 12
 };
 
 // One tile: 64 bytes, loaded with scalar loads by a worker.

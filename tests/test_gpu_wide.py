@@ -29,13 +29,15 @@ def _mini(batch, cap=200, seed=11):
     return cfg, w, kc, vc, lens, tok
 
 
-@pytest.mark.parametrize("batch", [8, 17, 32])
-def test_mini_wide_teacher_forced(batch):
+@pytest.mark.parametrize("batch,forward", [(8, 0), (17, 0), (32, 0), (8, 1), (32, 1)])
+def test_mini_wide_teacher_forced(batch, forward):
+    """forward 0 (default): split attention tiles and combine tiles; 1:
+    attention partials forwarded on chip by chained tiles."""
     cfg, w, kc, vc, lens, tok = _mini(batch)
     model = oracle.Model(cfg, w)
     cap = kc.shape[3]
-    announce(f"mini wide b{batch} build")
-    g = GpuPlan(cfg, w, batch, cap, kc, vc, lens, tok)
+    announce(f"mini wide b{batch} forward {forward} build")
+    g = GpuPlan(cfg, w, batch, cap, kc, vc, lens, tok, opts=wpk.wpk_build_opts(forward=forward))
     assert g.info.rows_per_tile_h == 64
     k0 = kc.copy()
     wpk.check(wpk.wpk_set_option(g.plan, wpk.WPK_OPT_LOG, 1), g.plan)

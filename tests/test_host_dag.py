@@ -250,9 +250,57 @@ def test_llama_1b_batch32_dag_shape():
     per_layer = {0: 192, 3: 128, 4: 1024, 5: 512, 8: 32, 9: 32}
     for t, n in per_layer.items():
         assert np.sum(ty == t) == 16 * n, t
-    assert np.sum(ty == 1) == 16 * 32 * 8 * 5  # attention: sequences x kv heads x 4-chunk groups of 17
+    assert np.sum(ty == 1) == 16 * 32 * 8 * 5  # attention: 4-chunk groups of the 17 chunks
+    assert np.sum(ty == 2) == 16 * 32 * 8
+    # with LDS forwarding: one chained tile per (sequence, kv head), no combine tiles
+    info, (ty2, _, _, _) = _info_and_dag(synth.LLAMA_1B, 32, 1088, forward=1)
+    ty2 = np.array(ty2)
+    assert np.sum(ty2 == 11) == 16 * 32 * 8 and np.sum(ty2 == 1) == 0 and np.sum(ty2 == 2) == 0
     assert np.sum(ty == 6) == 8016 and np.sum(ty == 10) == 32 and np.sum(ty == 7) == 1
     # down slice c waits only on the gate/up row blocks of its K slice
     wait = np.array(wait)
     down = np.nonzero((ty == 5) & (np.array(layer) == 0))[0]
     assert len(set(wait[down].tolist())) == 16
+
+
+def test_lds_forwarding_is_refused_below_batch_5():
+    d = dummy_desc(synth.MINI)
+    assert not wpk.wpk_build_host(d.desc, 4, 100, wpk.wpk_build_opts(forward=1))
+    assert "forwarding" in wpk.wpk_last_error(None)
+
+
+@pytest.mark.parametrize("cfg_name,batch,forward", [("MINI", 8, 1), ("MINI", 32, -1), ("MINI", 32, 1)])
+def test_lds_forwarded_attention_matches_split_attention(cfg_name, batch, forward):
+    """Chained attention tiles (every KV chunk of one sequence and kv head on
+    one worker, partials merged on chip, no combine tiles) against the oracle,
+    and the DAG they make: one tile per (sequence, kv head), no combine tiles."""
+    cfg = getattr(synth, cfg_name)
+    w = synth.make_weights(cfg, gain_std=0.1)
+    model = oracle.Model(cfg, w)
+    cap = 140
+    rng = np.random.default_rng(batch + 7)
+    lens = rng.integers(1, cap - 2, size=batch).astype(np.int32)
+    if batch > 1:
+        lens[1] = -1
+    kc, vc = synth.synthetic_kv(cfg, batch, cap, np.maximum(lens, 0))
+    tok = rng.integers(0, cfg.vocab, size=batch).astype(np.int32)
+    d = host_desc(cfg, w)
+    plan = wpk.wpk_build_host(d.desc, batch, cap, wpk.wpk_build_opts(forward=forward))
+    assert plan, wpk.wpk_last_error(None)
+    info = wpk.wpk_get_info(plan)
+    ty, _, wait, signal = wpk.wpk_get_dag(plan, info.n_tiles)
+    ty = np.array(ty)
+    if forward == 1:
+        assert np.sum(ty == 11) == cfg.n_layers * batch * cfg.n_kv_heads
+        assert np.sum(ty == 1) == 0 and np.sum(ty == 2) == 0
+    else:
+        assert np.sum(ty == 11) == 0 and np.sum(ty == 2) == cfg.n_layers * batch * cfg.n_kv_heads
+    st = HostState(kc, vc, lens, tok, cfg.vocab)
+    assert st.serial(plan, 5, poison=True) == 0, wpk.wpk_last_error(plan)
+    rc, log = wpk.wpk_get_log(plan, info.n_tiles)
+    check_log(log, wait, signal)
+    olog, otok = model.step(tok, kc.copy(), vc.copy(), lens.copy())
+    act = lens >= 0
+    assert np.max(np.abs(st.logits[act] - olog[act])) < 1e-3
+    assert np.array_equal(st.tokens[act], otok[act])
+    wpk.wpk_destroy(plan)

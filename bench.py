@@ -56,8 +56,8 @@ def step_bytes(cfg, batch: int, positions_before: np.ndarray) -> float:
     return w + float(np.sum(n * kv_per_pos + kv_per_pos + cfg.hidden * cfg.elt_bytes + cfg.vocab * 4))
 
 
-def traffic_from_profile(shash: str, per_launch_bytes: float):
-    path = os.path.join(ROOT, "profiles", "megakernel_llama1b_b1_traffic.json")
+def traffic_from_profile(shash: str, per_launch_bytes: float, name: str = "megakernel_llama1b_b1_traffic.json"):
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -202,7 +202,10 @@ def run(args):
             "value": round(w32 / args.steps * 1e6, 2), "unit": "µs/step", "latency_us": lat(per32),
             "tokens_per_s": round(b32 * args.steps / w32, 1), "hbm_GBps": round(gb, 1),
             "roofline": {"bound": "hbm", "achieved": round(gb, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": round(gb / HBM_PEAK_GBPS, 4), "bytes_per_launch": round(float(np.mean(by32)))},
+                         "frac": round(gb / HBM_PEAK_GBPS, 4),
+                         "traffic": traffic_from_profile(shash, float(np.mean(by32)),
+                                                         "megakernel_llama1b_b32_traffic.json"),
+                         "bytes_per_launch": round(float(np.mean(by32))), "kernel_us": round(float(per32.mean()), 2)},
             "mfma": {"flops_per_step": flops, "achieved_TFLOPs": round(flops / (per32.mean() * 1e-6) / 1e12, 2),
                      "peak_TFLOPs": 2500.0,
                      "frac": round(flops / (per32.mean() * 1e-6) / 2.5e15, 4)},

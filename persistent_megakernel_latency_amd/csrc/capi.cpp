@@ -193,6 +193,7 @@ wpk_plan* build_device(const wpk_model_desc* desc, int32_t batch, int32_t ctx_le
   Params& P = p->P;
   P.L = s.L; P.H = s.H; P.Hq = s.Hq; P.Hkv = s.Hkv; P.D = s.D; P.F = s.F; P.V = s.V;
   P.B = s.B; P.cap = s.cap; P.nch = s.nch; P.G = s.G; P.qkv_rows = s.qkv_rows;
+  P.attn_sub = s.attn_sub;
   P.n_tiles = (int32_t)p->dag.tiles.size();
   P.n_queues = (int32_t)p->dag.queue_off.size() - 1;
   P.n_workers = p->workers;

@@ -356,33 +356,19 @@ void run_gemv(Ctx& c, const Tile& T) {
   }
 }
 
-void run_attn_chunk(Ctx& c, const Tile& T);
-
-// An attention tile covers T.kind consecutive KV chunks, each its own partial.
-void run_attn(Ctx& c, const Tile& T) {
-  for (int u = 0; u < std::max(1, T.kind); ++u) {
-    Tile U = T;
-    U.c = T.c + u;
-    run_attn_chunk(c, U);
-  }
-}
-
-void run_attn_chunk(Ctx& c, const Tile& T) {
+// The partial (m, l, o[D]) of each q head of the group over one KV chunk,
+// into out[G][D+2]; false if the chunk holds no position of the sequence.
+bool attn_partial(Ctx& c, const Tile& T, int chunk, float* out) {
   const Params& P = c.P;
   const LayerBufs& lb = P.layers[T.layer];
   const int32_t p = P.seq_len[T.b];
   const int n = p < 0 ? 0 : std::min(p + 1, P.cap);
-  const int start = T.c * kAttnChunk;
+  const int start = chunk * kAttnChunk;
   const int cnt = std::max(0, std::min(kAttnChunk, n - start));
+  if (cnt == 0) return false;
   const int64_t slice = (((int64_t)T.layer * P.B + T.b) * P.Hkv + T.g) * P.cap;
   for (int h = 0; h < P.G; ++h) {
-    float* out = lb.part + ((((int64_t)T.b * P.Hkv + T.g) * P.nch + T.c) * P.G + h) * (P.D + 2);
-    if (cnt == 0) {
-      out[0] = -std::numeric_limits<float>::infinity();
-      out[1] = 0.f;
-      for (int d = 0; d < P.D; ++d) out[2 + d] = 0.f;
-      continue;
-    }
+    float* o_h = out + h * (P.D + 2);
     const float* q = lb.q + (int64_t)T.b * P.Hq * P.D + (int64_t)(T.g * P.G + h) * P.D;
     float s[kAttnChunk];
     float m = -std::numeric_limits<float>::infinity();
@@ -397,12 +383,75 @@ void run_attn_chunk(Ctx& c, const Tile& T) {
       s[j] = std::exp(s[j] - m);
       l += s[j];
     }
-    out[0] = m;
-    out[1] = l;
+    o_h[0] = m;
+    o_h[1] = l;
     for (int d = 0; d < P.D; ++d) {
       float o = 0.f;
       for (int j = 0; j < cnt; ++j) o += s[j] * wval(P.vc, P.dtype, (slice + start + j) * P.D + d);
-      out[2 + d] = o;
+      o_h[2 + d] = o;
+    }
+  }
+  return true;
+}
+
+// Running merge of partials: acc = merge(acc, part), both [G][D+2]; acc starts
+// with m = -inf, l = 0, o = 0.
+void merge_partial(const Params& P, float* acc, const float* part) {
+  for (int h = 0; h < P.G; ++h) {
+    float* a = acc + h * (P.D + 2);
+    const float* b = part + h * (P.D + 2);
+    const float M = std::max(a[0], b[0]);
+    const float ka = std::exp(a[0] - M), kb = std::exp(b[0] - M);
+    a[1] = a[1] * ka + b[1] * kb;
+    for (int d = 0; d < P.D; ++d) a[2 + d] = a[2 + d] * ka + b[2 + d] * kb;
+    a[0] = M;
+  }
+}
+
+void init_partial(const Params& P, std::vector<float>& acc) {
+  acc.assign((size_t)P.G * (P.D + 2), 0.f);
+  for (int h = 0; h < P.G; ++h) acc[(size_t)h * (P.D + 2)] = -std::numeric_limits<float>::infinity();
+}
+
+// An attention tile covers T.kind consecutive KV chunks; their partials are
+// merged on chip into one, stored at partial slot T.c / attn_sub (a tile past
+// its sequence stores nothing: the combine never reads that slot).
+void run_attn(Ctx& c, const Tile& T) {
+  const Params& P = c.P;
+  const LayerBufs& lb = P.layers[T.layer];
+  std::vector<float> acc, part((size_t)P.G * (P.D + 2));
+  init_partial(P, acc);
+  bool any = false;
+  for (int u = 0; u < std::max(1, T.kind); ++u)
+    if (attn_partial(c, T, T.c + u, part.data())) {
+      merge_partial(P, acc.data(), part.data());
+      any = true;
+    }
+  if (!any) return;
+  float* out = lb.part + (((int64_t)T.b * P.Hkv + T.g) * P.nch + T.c / P.attn_sub) * P.G * (P.D + 2);
+  std::copy(acc.begin(), acc.end(), out);
+}
+
+// A chained attention tile (LDS forwarding): every chunk's partial merged in
+// turn, then normalised into the attention output.
+void run_attnc(Ctx& c, const Tile& T) {
+  const Params& P = c.P;
+  const LayerBufs& lb = P.layers[T.layer];
+  std::vector<float> acc, part((size_t)P.G * (P.D + 2));
+  init_partial(P, acc);
+  bool any = false;
+  for (int ch = 0; ch < P.nch; ++ch)
+    if (attn_partial(c, T, ch, part.data())) {
+      merge_partial(P, acc.data(), part.data());
+      any = true;
+    }
+  for (int h = 0; h < P.G; ++h) {
+    const float* a = acc.data() + h * (P.D + 2);
+    for (int d = 0; d < P.D; ++d) {
+      const float v = any ? a[2 + d] / a[1] : 0.f;
+      const int64_t col = (int64_t)(T.g * P.G + h) * P.D + d;
+      if (P.wide) xput(lb.xattn, P.Hq * P.D, T.b, (int)col, v);
+      else lb.attn[(int64_t)T.b * P.Hq * P.D + col] = v;
     }
   }
 }
@@ -412,7 +461,8 @@ void run_combine(Ctx& c, const Tile& T) {
   const LayerBufs& lb = P.layers[T.layer];
   const int32_t p = P.seq_len[T.b];
   const int n = p < 0 ? 0 : std::min(p + 1, P.cap);
-  const int nact = (n + kAttnChunk - 1) / kAttnChunk;
+  // one partial per attention tile: the tiles holding positions
+  const int nact = ((n + kAttnChunk - 1) / kAttnChunk + P.attn_sub - 1) / P.attn_sub;
   for (int h = 0; h < P.G; ++h) {
     const int64_t at = (int64_t)T.b * P.Hq * P.D + (int64_t)(T.g * P.G + h) * P.D;
     float* dst = lb.attn + at;
@@ -495,10 +545,7 @@ void run_tile(Ctx& c, const Tile& T) {
     case T_NORMF: run_norm(c, T); break;
     case T_ATTN: run_attn(c, T); break;
     case T_COMBINE: run_combine(c, T); break;
-    case T_ATTNC:  // every chunk's partial, then their merge (the same tile)
-      run_attn(c, T);
-      run_combine(c, T);
-      break;
+    case T_ATTNC: run_attnc(c, T); break;
     case T_ARGMAX: run_argmax(c); break;
     default: run_gemv(c, T); break;
   }
@@ -509,6 +556,7 @@ Params host_params(wpk_plan* p, int32_t* tokens, wpk_kv* kv, float* logits) {
   Params P{};
   P.L = s.L; P.H = s.H; P.Hq = s.Hq; P.Hkv = s.Hkv; P.D = s.D; P.F = s.F; P.V = s.V;
   P.B = s.B; P.cap = s.cap; P.nch = s.nch; P.G = s.G; P.qkv_rows = s.qkv_rows;
+  P.attn_sub = s.attn_sub;
   P.n_tiles = (int32_t)p->dag.tiles.size();
   P.dtype = s.dtype;
   P.eps = s.eps;

@@ -470,6 +470,11 @@ __device__ __forceinline__ void dump_kv(const Params& P, const Tile& T, const Sl
   }
 }
 
+__device__ __forceinline__ int attn_count(const Params& P, const Tile& T, int p) {
+  const int n = p < 0 ? 0 : min(p + 1, P.cap);
+  return max(0, min(kAttnChunk, n - T.c * kAttnChunk));
+}
+
 // Positions of a sequence in the cache this step (its own position included).
 __device__ __forceinline__ int attn_valid(const Params& P, int p) { return p < 0 ? 0 : min(p + 1, P.cap); }
 
@@ -521,8 +526,9 @@ __device__ __forceinline__ Tile attn_group(const Tile& T, int c0) {
   return G;
 }
 
-// Running merge of the chunk partials of a chained attention tile (control
-// wave; lane = head dimension): the combine, fed from LDS.
+// Running merge of the chunk partials of an attention tile (control wave;
+// lane = head dimension), fed from LDS: a wide plan's tile stores one merged
+// partial for its chunks, a chained tile the merged and normalised output.
 struct AttnRun {
   float M[kMaxGroupHeads], L[kMaxGroupHeads], O[kMaxGroupHeads];
 };
@@ -550,6 +556,26 @@ __device__ __forceinline__ void attn_run_merge(const Params& P, AttnRun& r, cons
     r.M[h] = Mn;
   }
 }
+// The merged partial of a wide plan's attention tile, at partial slot
+// T.c / attn_sub (nothing for a tile past its sequence: never read).
+template <typename WT, int KMAX>
+__device__ __forceinline__ void attn_run_partial(const Params& P, const Tile& T, const AttnRun& r,
+                                                 const Smem<WT, KMAX>& sm, int lane) {
+  if (attn_count(P, T, sm.pos[T.b]) == 0) return;
+  float* out = act(P, T.layer, P.off_part) +
+               ((((size_t)T.b * P.Hkv + T.g) * P.nch + T.c / P.attn_sub) * P.G) * (P.D + 2);
+#pragma unroll
+  for (int h = 0; h < kMaxGroupHeads; ++h) {
+    if (h >= P.G) break;
+    float* o = out + h * (P.D + 2);
+    st_sc1(o + 2 + lane, r.O[h]);
+    if (lane == 0) {
+      st_sc1(o, r.M[h]);
+      st_sc1(o + 1, r.L[h]);
+    }
+  }
+}
+
 // The merged output of the group's q heads: fp32 rows, or the hi/lo operand
 // planes of the o-proj in a wide plan.  No chunk at all (an inactive slot): 0.
 template <bool WIDE>
@@ -570,10 +596,6 @@ __device__ __forceinline__ void attn_run_store(const Params& P, const Tile& T, c
   }
 }
 
-__device__ __forceinline__ int attn_count(const Params& P, const Tile& T, int p) {
-  const int n = p < 0 ? 0 : min(p + 1, P.cap);
-  return max(0, min(kAttnChunk, n - T.c * kAttnChunk));
-}
 
 // Attention partial: compute wave h = q head h of the group, lane = position
 // (scores) then lane = head dimension (weighted values).  Both loops are
@@ -645,7 +667,7 @@ __device__ __forceinline__ void cmp_combine(const Params& P, const Tile& T, cons
   if (h >= P.G) return;
   const int p = sm.pos[T.b];
   const int n = p < 0 ? 0 : min(p + 1, P.cap);
-  const int nact = (n + kAttnChunk - 1) / kAttnChunk;
+  const int nact = ((n + kAttnChunk - 1) / kAttnChunk + P.attn_sub - 1) / P.attn_sub;  // one partial per tile
   float* dst = act(P, T.layer, P.off_attn) + (size_t)T.b * P.Hq * P.D + (size_t)(T.g * P.G + h) * P.D;
   const float* part = act(P, T.layer, P.off_part) + (((size_t)T.b * P.Hkv + T.g) * P.nch * P.G + h) * (P.D + 2);
   const int stride = P.G * (P.D + 2);
@@ -1426,8 +1448,7 @@ __device__ __forceinline__ void ctl_post(const Params& P, const Tile& T, int b, 
       case T_GATEUP:
       case T_DOWN:
       case T_LM: ctl_wide_post<WT>(P, T, sm, lane); break;
-      case T_ATTN: ctl_attn_out<WT>(P, T, sm, lane); break;
-      case T_ARGMAX: ctl_argmax<WT>(P, sm, lane); break;
+      case T_ARGMAX: ctl_argmax<WT>(P, sm, lane); break;  // attention: merged by the caller
       case T_NORM:
       case T_NORM2:
       case T_NORMF: ctl_norm<WT>(P, T, sm, lane); break;
@@ -1559,8 +1580,9 @@ __device__ __forceinline__ void control_loop(const Params& P, Smem<WT, KMAX>& sm
         t_done = sm.t_done;
       }
       ctl_post<WT, CPR_H, CPR_F, WIDE>(P, Tb, b, sm, e, lane);
-      if (WIDE && T.type == T_ATTNC && attn_count(P, Tb, sm.pos[T.b]) > 0) attn_run_merge(P, run, sm, lane);
+      if (WIDE && is_attn(T.type) && attn_count(P, Tb, sm.pos[T.b]) > 0) attn_run_merge(P, run, sm, lane);
     }
+    if (WIDE && T.type == T_ATTN) attn_run_partial(P, T, run, sm, lane);
     if (WIDE && T.type == T_ATTNC) attn_run_store<WIDE>(P, T, run, attn_active(P, sm.pos[T.b]), lane);
     // publish: this wave made every global store of the tile; once they have
     // completed, one relaxed device-scope increment of the tile's counter shard
@@ -1808,8 +1830,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
       __syncthreads();  // A
       __syncthreads();  // B
       ctl_post<WT, CPR_H, CPR_F, WIDE>(P, Tb, b, sm, e, lane);
-      if (WIDE && T.type == T_ATTNC && attn_count(P, Tb, sm.pos[T.b]) > 0) attn_run_merge(P, run, sm, lane);
+      if (WIDE && is_attn(T.type) && attn_count(P, Tb, sm.pos[T.b]) > 0) attn_run_merge(P, run, sm, lane);
     }
+    if (WIDE && T.type == T_ATTN) attn_run_partial(P, T, run, sm, lane);
     if (WIDE && T.type == T_ATTNC) attn_run_store<WIDE>(P, T, run, attn_active(P, sm.pos[T.b]), lane);
   } else {
     const int tc = t - 64;

@@ -101,7 +101,7 @@ struct LayerBufs {
   float* x_mid;       // [B][H] after attention
   float* x_out;       // [B][H] after the MLP
   float* q;           // [B][Hq*D] rotated queries
-  float* part;        // [B][Hkv][nch][G][D+2] attention partials (m, l, o[D])
+  float* part;        // [B][Hkv][nch][G][D+2] attention partials (m, l, o[D]), one per attention tile
   float* attn;        // [B][Hq*D] attention output
   float* h;           // [B][F] SwiGLU output
   // Wide plans: operands of the matrix-core tiles as a pair of bf16 planes,
@@ -132,6 +132,7 @@ struct LayerW {
 // Everything a worker needs, passed by value to the kernel.
 struct Params {
   int32_t L, H, Hq, Hkv, D, F, V, B, cap, nch, G, qkv_rows;
+  int32_t attn_sub;  // KV chunks per attention tile: its chunks' partials merge into one (slot c / attn_sub)
   int32_t n_tiles, n_queues, n_workers, dtype;
   float eps, attn_scale;
   const void* embed;

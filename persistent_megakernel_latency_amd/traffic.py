@@ -14,6 +14,9 @@ bench.py only reports it while the sources are unchanged.
         --copy-fetch pmc_copy_FETCH_SIZE/copy_counter_collection.csv \\
         --copy-write pmc_copy_WRITE_SIZE/copy_counter_collection.csv \\
         --source-hash HASH --out profiles/megakernel_llama1b_b1_traffic.json
+
+The batch-1 instance is the default --kernel; the batch-32 (matrix-core)
+instance is "void wpk::megakernel<unsigned short, 256, 1024, false, true>".
 """
 from __future__ import annotations
 
@@ -41,7 +44,7 @@ def main() -> None:
     ap.add_argument("--write", required=True)
     ap.add_argument("--copy-fetch", required=True)
     ap.add_argument("--copy-write", required=True)
-    ap.add_argument("--kernel", default="void wpk::megakernel<unsigned short, 256, 1024, false>")
+    ap.add_argument("--kernel", default="void wpk::megakernel<unsigned short, 256, 1024, false, false>")
     ap.add_argument("--source-hash", required=True)
     ap.add_argument("--out", required=True)
     a = ap.parse_args()

@@ -127,7 +127,7 @@ wpk_plan* wpk_build(const wpk_model_desc* desc, int32_t batch, int32_t ctx_len);
 wpk_plan* wpk_build_ex(const wpk_model_desc* desc, int32_t batch, int32_t ctx_len,
                        const wpk_build_opts* opts);
 
-/* One decode step, enqueued on `stream` as a single cooperative launch.
+/* One decode step, enqueued on `stream` as a single launch.
  * tokens: device int32[batch]; on entry the current input token of each
  * sequence, on completion the greedy next token (so steps can be chained
  * without a host round trip).  logits: device float32[batch][vocab].
@@ -151,6 +151,10 @@ const char* wpk_last_error(const wpk_plan* plan);
 #define WPK_OPT_PREFETCH 6        /* 1 (default): stage a tile's weights before its inputs are complete;
                                      0: only after (an ablation of the weight prefetch) */
 #define WPK_OPT_WORKERS 7         /* number of resident workers W (<= the built maximum) */
+#define WPK_OPT_LAUNCH 8          /* 0 (default): plain launch; 1: cooperative launch (measured ~20 us
+                                     more per step).  Both are safe: claims follow the topological
+                                     order, so a worker that is not yet resident holds no tile that
+                                     anyone waits on */
 int32_t wpk_set_option(wpk_plan* plan, int32_t key, int64_t value);
 
 /* Per-tile execution log of the last logged step, one record per tile id. */

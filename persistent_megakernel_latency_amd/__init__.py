@@ -38,8 +38,10 @@ WPK_OPT_DEBUG_DROP_TILE = 4
 WPK_OPT_RESET = 5
 WPK_OPT_PREFETCH = 6
 WPK_OPT_WORKERS = 7
+WPK_OPT_LAUNCH = 8
 
-TILE_TYPES = ["qkv", "attn", "combine", "oproj", "gateup", "down", "lm", "argmax"]
+TILE_TYPES = ["qkv", "attn", "combine", "oproj", "gateup", "down", "lm", "argmax", "norm", "norm2", "normf",
+              "attnc"]
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32

@@ -5,7 +5,7 @@
 // inference wants a megakernel" (sections "The cohort is known" and "A
 // concrete design: one WPK update"): the builder fixes the tiles, their
 // dependency counters, the claim order, the worker count W and the whole
-// memory plan once; wpk_step is then a single cooperative launch.
+// memory plan once; wpk_step is then a single launch.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -346,9 +346,13 @@ int32_t wpk_step(wpk_plan* p, int32_t* tokens, wpk_kv* kv, void* logits, wpk_str
     if (e != hipSuccess) return plan_fail(p, WPK_E_HIP, hip_msg("hipMemsetAsync log", e));
   }
   void* args[] = {(void*)&P};
-  e = hipLaunchCooperativeKernel(p->log_on ? p->k_mega_log : p->k_mega, dim3(p->workers),
-                                 dim3(wpk_dev_block_threads()), args, p->dyn_lds, st);
-  if (e != hipSuccess) return plan_fail(p, WPK_E_HIP, hip_msg("hipLaunchCooperativeKernel", e));
+  if (!p->cooperative)
+    e = hipLaunchKernel(p->log_on ? p->k_mega_log : p->k_mega, dim3(p->workers), dim3(wpk_dev_block_threads()),
+                        args, p->dyn_lds, st);
+  else
+    e = hipLaunchCooperativeKernel(p->log_on ? p->k_mega_log : p->k_mega, dim3(p->workers),
+                                   dim3(wpk_dev_block_threads()), args, p->dyn_lds, st);
+  if (e != hipSuccess) return plan_fail(p, WPK_E_HIP, hip_msg("megakernel launch", e));
   return WPK_OK;
 }
 
@@ -427,6 +431,10 @@ int32_t wpk_set_option(wpk_plan* p, int32_t key, int64_t value) {
     case WPK_OPT_PREFETCH:
       P.prefetch = value != 0;
       p->prefetch = (int32_t)(value != 0);
+      return WPK_OK;
+    case WPK_OPT_LAUNCH:
+      if (value != 0 && value != 1) return plan_fail(p, WPK_E_ARG, "launch must be 0 or 1");
+      p->cooperative = (int32_t)value;
       return WPK_OK;
     case WPK_OPT_WORKERS:
       if (value < (int64_t)p->s.queue_shards || value > p->max_workers)

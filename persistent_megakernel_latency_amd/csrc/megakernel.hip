@@ -6,8 +6,8 @@
 //    execution"); the host launches once per step and the GPU walks the
 //    schedule: wait for the dependencies, run, signal the consumers (section
 //    "What the megakernel changes").
-//  * Workers are resident workgroups, several per CU, all co-resident
-//    (cooperative launch), that claim tiles from device-side queues in a
+//  * Workers are resident workgroups, several per CU (one launch of at most
+//    the co-resident count), that claim tiles from device-side queues in a
 //    topological order.  Each worker has one staging slot: the claimed tile's
 //    weights are loaded into it before the tile's dependency counter is
 //    checked, so weight streaming continues while predecessors finish

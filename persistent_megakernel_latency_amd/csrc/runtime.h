@@ -49,7 +49,7 @@ struct wpk_plan {
   std::string err;
   std::vector<wpk_log_rec> log;     // host copy of the last log
   int32_t latched = 0;              // device error seen by wpk_sync
-  int32_t log_on = 0, prefetch = 1, drop_tile = -1;
+  int32_t log_on = 0, prefetch = 1, drop_tile = -1, cooperative = 0;
   uint32_t perturb = 0;
   uint64_t watchdog_us = 2000000;
   int64_t weight_bytes = 0;

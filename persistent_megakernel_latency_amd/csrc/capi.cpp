@@ -37,7 +37,7 @@ std::string hip_msg(const char* what, hipError_t e) { return std::string(what) +
 int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
 
 struct Layout {
-  int64_t ctl, heads, counters, argmax, tiles, groups, queue, queue_off, layers, rope_cos, rope_sin, act, log,
+  int64_t ctl, heads, counters, argmax, tiles, qtiles, groups, queue, queue_off, layers, rope_cos, rope_sin, act, log,
       wpart, fixc, total;
 };
 
@@ -55,6 +55,7 @@ Layout layout(const Shape& s, const Dag& d, int32_t max_workers) {
   L.counters = take((int64_t)d.n_shard_slots * kLine * 4);
   L.argmax = take((int64_t)s.B * kArgmaxShards * 8);
   L.tiles = take((int64_t)d.tiles.size() * sizeof(Tile));
+  L.qtiles = take((int64_t)d.queue.size() * sizeof(Tile));
   L.groups = take((int64_t)d.groups.size() * sizeof(Group));
   L.queue = take((int64_t)d.queue.size() * 4);
   L.queue_off = take((int64_t)d.queue_off.size() * 4);
@@ -180,6 +181,9 @@ wpk_plan* build_device(const wpk_model_desc* desc, int32_t batch, int32_t ctx_le
   std::vector<float> rc, rsn;
   rope_table(s, rc, rsn);
   if (e == hipSuccess) e = up(L.tiles, p->dag.tiles.data(), p->dag.tiles.size() * sizeof(Tile));
+  std::vector<Tile> qt;
+  for (int32_t id : p->dag.queue) qt.push_back(p->dag.tiles[id]);
+  if (e == hipSuccess) e = up(L.qtiles, qt.data(), qt.size() * sizeof(Tile));
   if (e == hipSuccess) e = up(L.groups, p->dag.groups.data(), p->dag.groups.size() * sizeof(Group));
   if (e == hipSuccess) e = up(L.queue, p->dag.queue.data(), p->dag.queue.size() * 4);
   if (e == hipSuccess) e = up(L.queue_off, p->dag.queue_off.data(), p->dag.queue_off.size() * 4);
@@ -228,6 +232,7 @@ wpk_plan* build_device(const wpk_model_desc* desc, int32_t batch, int32_t ctx_le
   P.rope_cos = (const float*)(w + L.rope_cos);
   P.rope_sin = (const float*)(w + L.rope_sin);
   P.tiles = (const Tile*)(w + L.tiles);
+  P.qtiles = (const Tile*)(w + L.qtiles);
   P.queue = (const int32_t*)(w + L.queue);
   P.queue_off = (const int32_t*)(w + L.queue_off);
   P.groups = (const Group*)(w + L.groups);

@@ -84,6 +84,7 @@ struct alignas(16) Smem {
   int pos[kMaxBatch];  // seq_len of each sequence at step start
   int tok[kMaxBatch];  // input token of each sequence (validated)
   int ids[2];          // claim index of the next tile, by iteration parity
+  alignas(16) int tnext[2][16];  // the next tile's descriptor, by iteration parity (compute wave 1 fetches it)
   uint64_t t_ready, t_done;  // logged steps: compute wave 1 saw its slot, finished its arithmetic
   int first;
   int stop;
@@ -1505,10 +1506,33 @@ __device__ __forceinline__ uint32_t hash32(uint32_t x) {
 // operand LDS area for the slice sums, so C stays when the next tile is an
 // attention tile (its compute waves fill that area before barrier A).
 template <bool WIDE>
-__device__ __forceinline__ bool need_c(const Params& P, const Tile& T, int nxt, int qb, int qn) {
+__device__ __forceinline__ bool need_c(const Tile& T, int next_type) {
   if (!(T.type == T_LM || (WIDE && is_gemv(T.type)))) return true;
-  if (!WIDE || nxt >= qn) return false;
-  return is_attn(cload(P.tiles, cload(P.queue, qb + nxt)).type);
+  if (!WIDE || next_type < 0) return false;
+  return is_attn(next_type);
+}
+
+// Wide plans: compute wave 1, which claims the next tile, loads its descriptor
+// while its weights stream in and leaves it in LDS before barrier A, so that
+// after barrier B the compute waves stage the next weights without a
+// scalar-cache miss in between.  (Narrow plans load it in each role: there
+// the wait for wave 1 at barrier A would lie on the critical path, and the
+// control wave's load hides behind its poll for the tile's inputs.)
+__device__ __forceinline__ void put_tile(int* dst, const Tile& T, int lane) {
+  int32_t w[16];
+  __builtin_memcpy(w, &T, sizeof(Tile));
+  int v = 0;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) v = lane == k ? w[k] : v;
+  if (lane < 16) dst[lane] = v;
+}
+__device__ __forceinline__ Tile get_tile(const int* src) {
+  int32_t w[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) w[k] = __builtin_amdgcn_readfirstlane(src[k]);
+  Tile T;
+  __builtin_memcpy(&T, w, sizeof(Tile));
+  return T;
 }
 
 // Publishes a worker's run of LM-head tiles at once: their logits stores and
@@ -1537,8 +1561,8 @@ __device__ __forceinline__ void control_loop(const Params& P, Smem<WT, KMAX>& sm
     // tile types is not hoisted out of the loop and kept live across it
     const int lane = opaque(lane0);
     const uint64_t t_claim = LOG ? __builtin_amdgcn_s_memrealtime() : 0;
-    const int id = cload(P.queue, qb + cur);
-    const Tile T = cload(P.tiles, id);
+    const Tile T = WIDE && it ? get_tile(sm.tnext[it & 1]) : cload(P.qtiles, qb + cur);
+    const int id = T.id;
     if (lm_count && T.type != T_LM) flush_lm(P, lm_group, lm_count, lane);
     int32_t delta = 0;
     bool ok = true;
@@ -1621,7 +1645,8 @@ __device__ __forceinline__ void control_loop(const Params& P, Smem<WT, KMAX>& sm
     // queue behind the next weights, which then stream without a gap.  The
     // next claim was written by compute wave 1 before this tile's barrier B.
     const int nxt = __builtin_amdgcn_readfirstlane(sm.ids[(it + 1) & 1]);
-    if (need_c<WIDE>(P, T, nxt, qb, qn)) __syncthreads();
+    if (need_c<WIDE>(T, WIDE && nxt < qn ? __builtin_amdgcn_readfirstlane(sm.tnext[(it + 1) & 1][0]) : -1))
+      __syncthreads();
     cur = nxt;
     ++it;
   }
@@ -1652,11 +1677,11 @@ __device__ __forceinline__ void compute_loop(const Params& P, Smem<WT, KMAX>& sm
     // barrier B passed, so the control wave is already running that tile's
     // epilogue): stage this tile's weights; they stream in while the control
     // wave publishes, claims, waits for the tile's inputs and stages them.
-    const Tile T = cload(P.tiles, cload(P.queue, qb + nx));
     // Claim the next tile here rather than in the control wave: a wave's
     // memory operations complete in issue order, so an atomic (slow while the
     // weights stream) would hold up every later wait of the control wave,
     // while here it returns ahead of the weights this wave waits for anyway.
+    const Tile T = WIDE && it >= 0 ? get_tile(sm.tnext[(it + 1) & 1]) : cload(P.qtiles, qb + nx);
     uint32_t ahead = 0;
     if (tc0 == 0) ahead = atomic_add(head, 1u);
     // without weight prefetch (an ablation), the weights are loaded only once
@@ -1666,6 +1691,14 @@ __device__ __forceinline__ void compute_loop(const Params& P, Smem<WT, KMAX>& sm
     if (WIDE && is_gemv(T.type)) stage_wide(P, T, s, tc0);
     else stage<WT, CPR_H, CPR_F>(P, WIDE && T.type == T_ATTNC ? attn_group<WT>(T, 0) : T, s, voff, valid);
     ++it;
+    if (WIDE && tc0 < 64) {
+      // the next claim and its descriptor, read by every wave after barrier
+      // A (double-buffered by iteration parity: the current tile's copy may
+      // still be being read)
+      const int nxt = __builtin_amdgcn_readfirstlane((int)ahead);
+      if (tc0 == 0) sm.ids[(it + 1) & 1] = nxt;
+      if (nxt < qn) put_tile(sm.tnext[(it + 1) & 1], cload(P.qtiles, qb + nxt), tc0);
+    }
     const int tc = opaque(tc0);
     const int npairs = n_passes<WIDE>(P, T, sm.pos[T.b]);
     bool stop = false;
@@ -1694,7 +1727,7 @@ __device__ __forceinline__ void compute_loop(const Params& P, Smem<WT, KMAX>& sm
           __hip_atomic_fetch_max(&sm.t_ready, (uint64_t)__builtin_amdgcn_s_memrealtime(), __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_WORKGROUP);
       }
-      if (b == 0 && tc == 0) sm.ids[(it + 1) & 1] = (int)ahead;  // for the control wave, read after B
+      if (!WIDE && b == 0 && tc == 0) sm.ids[(it + 1) & 1] = (int)ahead;  // read after B
       launder(s);
       compute<WT, CPR_H, CPR_F, WIDE>(P, Tb, s, sm, tc);
       if (LOG && (tc & 63) == 0)
@@ -1707,7 +1740,8 @@ __device__ __forceinline__ void compute_loop(const Params& P, Smem<WT, KMAX>& sm
     // above it would keep two slots live.
     __builtin_amdgcn_sched_barrier(0);
     nx = __builtin_amdgcn_readfirstlane(sm.ids[(it + 1) & 1]);
-    if (need_c<WIDE>(P, T, nx, qb, qn)) __syncthreads();  // C
+    if (need_c<WIDE>(T, WIDE && nx < qn ? __builtin_amdgcn_readfirstlane(sm.tnext[(it + 1) & 1][0]) : -1))
+      __syncthreads();  // C
   }
 }
 

@@ -155,6 +155,7 @@ struct Params {
   char* kc;               // [L][B][Hkv][cap][D]
   char* vc;
   const Tile* tiles;
+  const Tile* qtiles;       // the tile table in claim-queue order: qtiles[i] = tiles[queue[i]]
   const int32_t* queue;     // tile ids of all claim queues, concatenated
   const int32_t* queue_off; // queue q holds queue[queue_off[q] .. queue_off[q+1])
   const Group* groups;

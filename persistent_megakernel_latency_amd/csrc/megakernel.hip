@@ -1205,6 +1205,32 @@ __device__ __forceinline__ void ctl_wide_post(const Params& P, const Tile& T0, S
 #pragma unroll
   for (int i = 0; i < 32; ++i) y[i] = 0.f;
   const int q = lane >> 4, s16 = lane & 15;
+  // o-proj and down: the residual, loaded together with the other slices'
+  // partial sums (one round trip for both)
+  const bool resid = T.type == T_OPROJ || T.type == T_DOWN;
+  float rv[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) rv[i] = 0.f;
+  if (resid) {
+    const LayerBufs* lbp = P.layers + T.layer;
+    // o-proj: x_in (layer 0: the embedding row); down: x_mid (consecutive table fields)
+    const float* res = cload((const float* const*)&lbp->x_in, T.type == T_OPROJ ? 0 : 1);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int n = 16 * h + s16;
+      if (h >= nh || n >= P.B) continue;
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        const int row = T.r0 + q + 4 * m;
+        if (res) {
+          rv[h * 16 + m] = ld_sc1(res + (size_t)n * P.H + row);
+        } else {
+          const WT* ep = (const WT*)P.embed + (size_t)sm.tok[n] * P.H + row;
+          rv[h * 16 + m] = sizeof(WT) == 2 ? bf16_lo(*(const uint16_t*)ep) : *(const float*)ep;
+        }
+      }
+    }
+  }
   const int fit = 16 / nh;  // slots the operand area holds
   for (int s0 = 0; s0 < T.b; s0 += fit) {
     const int s1 = min(T.b, s0 + fit);
@@ -1268,10 +1294,8 @@ __device__ __forceinline__ void ctl_wide_post(const Params& P, const Tile& T0, S
     case T_OPROJ:
     case T_DOWN: {
       // o-proj: x_mid = x_in + y; down: x_out = x_mid + y (consecutive table fields)
-      const int d = T.type == T_OPROJ ? 0 : 1;
       const LayerBufs* lbp = P.layers + l;
-      float* dst = cload((float* const*)&lbp->x_mid, d);
-      const float* res = cload((const float* const*)&lbp->x_in, d);
+      float* dst = cload((float* const*)&lbp->x_mid, T.type == T_OPROJ ? 0 : 1);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         if (h >= nh) break;
@@ -1280,14 +1304,7 @@ __device__ __forceinline__ void ctl_wide_post(const Params& P, const Tile& T0, S
 #pragma unroll
         for (int m = 0; m < 16; ++m) {
           const int row = T.r0 + q + 4 * m;
-          float r;
-          if (res) {
-            r = ld_sc1(res + (size_t)n * P.H + row);
-          } else {  // layer 0: the residual is the token's embedding row
-            const WT* ep = (const WT*)P.embed + (size_t)sm.tok[n] * P.H + row;
-            r = sizeof(WT) == 2 ? bf16_lo(*(const uint16_t*)ep) : *(const float*)ep;
-          }
-          st_sc1(dst + (size_t)n * P.H + row, r + y[h * 16 + m]);
+          st_sc1(dst + (size_t)n * P.H + row, rv[h * 16 + m] + y[h * 16 + m]);
         }
       }
       break;

@@ -74,6 +74,9 @@ std::string check_shape(const wpk_model_desc& d, int32_t batch, int32_t ctx_len,
     if (s.dtype != WPK_BF16) return "batches above 4 need bf16 weights";
     if (s.H % kWideK || s.F % kWideK) return "batches above 4 need hidden and ffn to be multiples of 512";
     if (s.D != kWideRows) return "batches above 4 need head_dim 64";
+    // the last slice of a K = hidden row block loads the other slices'
+    // partial sums and the RMSNorm sums of squares into one 64 KiB LDS area
+    if (s.H > 4096) return "batches above 4 need hidden <= 4096";
     s.rows_h = s.rows_qkv = s.rows_f = kWideRows;
   }
   s.workers_per_cu = o.workers_per_cu ? o.workers_per_cu : 2;
@@ -163,13 +166,17 @@ namespace {
 
 Dag finish_dag(const Shape& s, Emitter& e);
 
-// Wide plans (batch above kMaxBatchGemv).  Per layer: a norm tile per
-// sequence; QKV row blocks of one head each (two segments, dimensions
-// [0, D/2) and [D/2, D), so a RoPE pair is rows i and i + D/2 of the tile), attention of kv head g waiting on its q, k and v heads;
-// output-projection slices, each waiting only on the combines of the heads in
-// its K slice; a norm tile per sequence; gate/up row blocks (32 gate + 32 up
-// rows); down slices, each waiting only on the gate/up row blocks of its K
-// slice.  Then a final norm tile per sequence and the LM-head row blocks.
+// Wide plans (batch above kMaxBatchGemv).  Layer 0 starts with a tile per
+// sequence that writes the embedding row as the first QKV operand.  Per layer:
+// QKV row blocks of one head each (two segments, dimensions [0, D/2) and
+// [D/2, D), so a RoPE pair is rows i and i + D/2 of the tile), attention of kv
+// head g waiting on its q, k and v heads; output-projection slices, each
+// waiting only on the combines of the heads in its K slice; gate/up row blocks
+// (32 gate + 32 up rows) waiting on the o-proj; down slices, each waiting only
+// on the gate/up row blocks of its K slice.  Then the LM-head row blocks.  The
+// RMSNorms need no tiles of their own: the o-proj and down epilogues write
+// gain * x and per-block sums of squares, and the QKV, gate/up and LM-head
+// epilogues divide by the root mean square.
 void build_wide(const Shape& s, Emitter& e) {
   const int32_t D = s.D;
   const int32_t n_os = s.H / kWideK;            // o-proj K slices
@@ -178,13 +185,16 @@ void build_wide(const Shape& s, Emitter& e) {
   auto same = [](int32_t w) { return [w](int32_t) { return w; }; };
   int32_t g_x = -1;
   for (int32_t l = 0; l < s.L; ++l) {
-    const int32_t g_qkv_in = e.group();
-    for (int32_t b = 0; b < s.B; ++b) e.tile(T_NORM, l, g_x, g_qkv_in).b = b;
+    int32_t g_qkv_in = g_x;
+    if (l == 0) {
+      g_qkv_in = e.group();
+      for (int32_t b = 0; b < s.B; ++b) e.tile(T_NORM, 0, -1, g_qkv_in).b = b;
+    }
     std::vector<int32_t> g_attn(s.Hkv), g_comb(s.B * s.Hkv), g_o(n_os), g_dn(n_ds);
     for (auto& g : g_attn) g = e.group();
     for (auto& g : g_comb) g = e.group();
     for (auto& g : g_o) g = e.group();
-    const int32_t g_xm = e.group(), g_gu = e.group();
+    const int32_t g_xm = e.group();
     for (auto& g : g_dn) g = e.group();
     const int32_t g_next = e.group();
     for (int32_t g = 0; g < s.Hkv; ++g) {
@@ -219,18 +229,15 @@ void build_wide(const Shape& s, Emitter& e) {
     }
     for (int32_t r = 0; r < s.H; r += kWideRows)
       e.wide(T_OPROJ, l, [&](int32_t c) { return g_o[c]; }, g_xm, r, r + kWideRows, kWideRows, s.H);
-    for (int32_t b = 0; b < s.B; ++b) e.tile(T_NORM2, l, g_xm, g_gu).b = b;
     for (int32_t j = 0; j < s.F; j += hpb)
-      e.wide(T_GATEUP, l, same(g_gu), g_dn[j / kWideK], j, j, hpb, s.H);
+      e.wide(T_GATEUP, l, same(g_xm), g_dn[j / kWideK], j, j, hpb, s.H);
     for (int32_t r = 0; r < s.H; r += kWideRows)
       e.wide(T_DOWN, l, [&](int32_t c) { return g_dn[c]; }, g_next, r, r + kWideRows, kWideRows, s.F);
     g_x = g_next;
   }
-  const int32_t g_nf = e.group();
-  for (int32_t b = 0; b < s.B; ++b) e.tile(T_NORMF, s.L - 1, g_x, g_nf).b = b;
   const int32_t g_am = e.group();
   for (int32_t r = 0; r < s.V; r += kWideRows)
-    e.wide(T_LM, s.L - 1, same(g_nf), g_am, r, r + kWideRows, kWideRows, s.H);
+    e.wide(T_LM, s.L - 1, same(g_x), g_am, r, r + kWideRows, kWideRows, s.H);
   e.tile(T_ARGMAX, s.L - 1, g_am, -1);
 }
 
@@ -428,9 +435,7 @@ void outputs(const Shape& s, const Tile& t, std::vector<std::pair<int64_t, int64
       out.emplace_back(0, s.B);
       break;
     case T_NORM:
-    case T_NORM2:
-    case T_NORMF:
-      out.emplace_back(t.b, t.b + 1);  // one sequence's normalised row
+      out.emplace_back(t.b, t.b + 1);  // one sequence's operand row
       break;
   }
 }
@@ -455,11 +460,11 @@ void inputs(const Shape& s, const Tile& t, std::vector<Need>& need) {
       for (int32_t c = 0; c < gemm_slices(s, type); ++c) need.push_back({layer, type, c * lim + a, c * lim + b});
     };
     switch (t.type) {
-      case T_NORM:
-        if (l > 0) rows(l - 1, T_DOWN, 0, s.H);
+      case T_NORM:  // layer 0 only: the embedding rows
         break;
-      case T_QKV:
-        need.push_back({l, T_NORM, 0, s.B});
+      case T_QKV:  // the operand and sums of squares of every row block of x
+        if (l == 0) need.push_back({0, T_NORM, 0, s.B});
+        else rows(l - 1, T_DOWN, 0, s.H);
         break;
       case T_ATTN:
       case T_ATTNC: {
@@ -481,20 +486,14 @@ void inputs(const Shape& s, const Tile& t, std::vector<Need>& need) {
           need.push_back({l, T_COMBINE, a, a + kWideK});
         }
         break;
-      case T_NORM2:
-        rows(l, T_OPROJ, 0, s.H);
-        break;
       case T_GATEUP:
-        need.push_back({l, T_NORM2, 0, s.B});
+        rows(l, T_OPROJ, 0, s.H);
         break;
       case T_DOWN:  // the h columns of its K slice
         rows(l, T_GATEUP, (int64_t)t.c * kWideK, (int64_t)(t.c + 1) * kWideK);
         break;
-      case T_NORMF:
-        rows(s.L - 1, T_DOWN, 0, s.H);
-        break;
       case T_LM:
-        need.push_back({s.L - 1, T_NORMF, 0, s.B});
+        rows(s.L - 1, T_DOWN, 0, s.H);
         break;
       case T_ARGMAX:
         rows(s.L - 1, T_LM, 0, s.V);

@@ -53,6 +53,12 @@ ActLayout act_layout(const Shape& s) {
   a.xn2 = at;   at += r64(wb * s.H);
   a.xh = at;    at += r64(wb * s.F);
   a.xnf = at;   at += r64(wb * s.H);
+  // wide plans: per 64-row block and sequence, the sum of squares of the
+  // RMSNorm input rows (attention input, MLP input, final)
+  const int64_t ssz = s.wide ? (int64_t)(s.H / kWideRows) * kMaxBatch : 0;
+  a.ss1 = at;   at += r64(ssz);
+  a.ss2 = at;   at += r64(ssz);
+  a.ssf = at;   at += r64(ssz);
   a.per_layer = at;
   a.total = at * s.L;
   return a;
@@ -84,6 +90,9 @@ void fill_layers(const Shape& s, const wpk_model_desc& d, float* act, std::vecto
     lb.xnf = (uint16_t*)(base + a.xnf);
     lb.x_in = l == 0 ? nullptr : out[l - 1].x_out;
     lb.final_norm = (const float*)d.final_norm;
+    lb.ss1 = base + a.ss1;
+    lb.ss2 = base + a.ss2;
+    lb.ssf = base + a.ssf;
   }
 }
 
@@ -159,6 +168,26 @@ int32_t token_of(Ctx& c, int b) {
 inline float xget(const uint16_t* x, int K, int b, int i) {
   const int64_t at = (int64_t)b * K + i;
   return bf16v(x[at]) + bf16v(x[(int64_t)kMaxBatch * K + at]);
+}
+
+// Wide plans: the RMSNorm split between the tile that produces a 64-row
+// block of x (it writes gain * x as the bf16 operand and the block's sum of
+// squares) and the tile that consumes the operand (its epilogue divides by
+// the root mean square, read from all blocks' sums in block order).
+void put_norm_rows(const Params& P, uint16_t* plane, float* ss, const float* gain, int b, int64_t r0,
+                   const float* x) {
+  float sq = 0.f;
+  for (int r = 0; r < kWideRows; ++r) {
+    xput(plane, P.H, b, (int)(r0 + r), gain[r0 + r] * x[r]);
+    sq += x[r] * x[r];
+  }
+  ss[(r0 / kWideRows) * kMaxBatch + b] = sq;
+}
+
+float inv_rms(const Params& P, const float* ss, int b) {
+  float sum = 0.f;
+  for (int rb = 0; rb < P.H / kWideRows; ++rb) sum += ss[rb * kMaxBatch + b];
+  return 1.0f / std::sqrt(sum / (float)P.H + P.eps);
 }
 
 // Input vector of a GEMV tile for sequence b, with its RMSNorm prologue.  In
@@ -263,6 +292,12 @@ void run_gemv(Ctx& c, const Tile& T) {
         for (int sl = 0; sl < T.b; ++sl) acc += part(sl, r, b);
         y[r] = acc;
       }
+      // the RMSNorm of the operand, divided out here
+      const float* ss = T.type == T_QKV ? lb.ss1 : T.type == T_GATEUP ? lb.ss2 : T.type == T_LM ? lb.ssf : nullptr;
+      if (ss) {
+        const float inv = inv_rms(P, ss, b);
+        for (int r = 0; r < T.rows; ++r) y[r] *= inv;
+      }
     } else {
       gemv_input(c, T, b, x);
       for (int r = 0; r < T.rows; ++r) {
@@ -319,6 +354,7 @@ void run_gemv(Ctx& c, const Tile& T) {
           else xin = lb.x_in[(int64_t)b * P.H + row];
           lb.x_mid[(int64_t)b * P.H + row] = xin + y[r];
         }
+        if (P.wide) put_norm_rows(P, lb.xn2, lb.ss2, lb.mlp_norm, b, T.r0, lb.x_mid + (int64_t)b * P.H + T.r0);
         break;
       case T_GATEUP:
         for (int i = 0; i < T.rs; ++i) {
@@ -335,6 +371,15 @@ void run_gemv(Ctx& c, const Tile& T) {
           const int64_t row = T.r0 + r;
           if (row >= P.H) continue;
           lb.x_out[(int64_t)b * P.H + row] = lb.x_mid[(int64_t)b * P.H + row] + y[r];
+        }
+        if (P.wide) {  // the next layer's attention input, or the final norm's
+          const float* xo = lb.x_out + (int64_t)b * P.H + T.r0;
+          if (T.layer + 1 < P.L) {
+            const LayerBufs& nx = P.layers[T.layer + 1];
+            put_norm_rows(P, nx.xn1, nx.ss1, nx.attn_norm, b, T.r0, xo);
+          } else {
+            put_norm_rows(P, lb.xnf, lb.ssf, P.final_norm, b, T.r0, xo);
+          }
         }
         break;
       case T_LM: {
@@ -504,45 +549,22 @@ void run_argmax(Ctx& c) {
   }
 }
 
-// Wide plans: one sequence's row, normalised and scaled by the gain, rounded
-// to the bf16 operand of the matrix-core tiles.
+// Wide plans, layer 0: one sequence's embedding row as the first QKV operand.
 void run_norm(Ctx& c, const Tile& T) {
   const Params& P = c.P;
-  const LayerBufs& lb = P.layers[T.layer];
+  const LayerBufs& lb = P.layers[0];
   const int b = T.b, K = P.H;
-  std::vector<float> x(K);
-  const float* gain;
-  uint16_t* dst;
-  if (T.type == T_NORM) {
-    gain = lb.attn_norm;
-    dst = lb.xn1;
-    if (T.layer == 0) {
-      const int64_t tok = token_of(c, b);
-      for (int i = 0; i < K; ++i) x[i] = wval(P.embed, P.dtype, tok * K + i);
-    } else {
-      for (int i = 0; i < K; ++i) x[i] = lb.x_in[(int64_t)b * K + i];
-    }
-  } else if (T.type == T_NORM2) {
-    gain = lb.mlp_norm;
-    dst = lb.xn2;
-    for (int i = 0; i < K; ++i) x[i] = lb.x_mid[(int64_t)b * K + i];
-  } else {
-    const LayerBufs& last = P.layers[P.L - 1];
-    gain = P.final_norm;
-    dst = last.xnf;
-    for (int i = 0; i < K; ++i) x[i] = last.x_out[(int64_t)b * K + i];
+  const int64_t tok = token_of(c, b);
+  std::vector<float> x(kWideRows);
+  for (int r0 = 0; r0 < K; r0 += kWideRows) {
+    for (int r = 0; r < kWideRows; ++r) x[r] = wval(P.embed, P.dtype, tok * K + r0 + r);
+    put_norm_rows(P, lb.xn1, lb.ss1, lb.attn_norm, b, r0, x.data());
   }
-  float ss = 0.f;
-  for (int i = 0; i < K; ++i) ss += x[i] * x[i];
-  const float inv = 1.0f / std::sqrt(ss / (float)K + P.eps);
-  for (int i = 0; i < K; ++i) xput(dst, K, b, i, x[i] * inv * gain[i]);
 }
 
 void run_tile(Ctx& c, const Tile& T) {
   switch (T.type) {
-    case T_NORM:
-    case T_NORM2:
-    case T_NORMF: run_norm(c, T); break;
+    case T_NORM: run_norm(c, T); break;
     case T_ATTN: run_attn(c, T); break;
     case T_COMBINE: run_combine(c, T); break;
     case T_ATTNC: run_attnc(c, T); break;

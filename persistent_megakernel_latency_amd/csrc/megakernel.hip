@@ -49,6 +49,7 @@
 namespace wpk {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
@@ -143,6 +144,12 @@ __device__ __forceinline__ u32x4 ld_sc1_x4(const float* base, int32_t float_off)
 __device__ __forceinline__ void st_sc1_x4(void* base, uint32_t byte_off, u32x4 v) {
   const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7FFFFFFF, 0x00020000);
   __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, 16 /* sc1 */);
+}
+
+// 8 bytes stored with a device-coherent (sc1) buffer store.
+__device__ __forceinline__ void st_sc1_x2(void* base, uint32_t byte_off, u32x2 v) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7FFFFFFF, 0x00020000);
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, byte_off, 0, 16 /* sc1 */);
 }
 
 // Read-only tables (tiles, groups, queues) through the constant address space:
@@ -1183,8 +1190,9 @@ __device__ __forceinline__ void st_hilo(uint16_t* plane0, size_t plane_elems, si
 // arrival; the row block's last slice loads the others (LDS-direct, into the
 // operand area, up to 64 KiB at a time), adds all of them in slice order and
 // runs the epilogue.  Lane l holds sequence 16h + l % 16 of rows l / 16 + 4m.
+// True if this was the last slice (the operand area was overwritten).
 template <typename WT, int KMAX>
-__device__ __forceinline__ void ctl_wide_post(const Params& P, const Tile& T0, Smem<WT, KMAX>& sm, int lane0) {
+__device__ __forceinline__ bool ctl_wide_post(const Params& P, const Tile& T0, Smem<WT, KMAX>& sm, int lane0) {
   const int lane = opaque(lane0);
   const Tile T = uni(T0);
   const int nh = P.B > 16 ? 2 : 1;
@@ -1197,7 +1205,7 @@ __device__ __forceinline__ void ctl_wide_post(const Params& P, const Tile& T0, S
   uint32_t old = 0;
   if (lane == 0) old = atomic_add(&P.fixc[(size_t)T.fix * kLine], 1u);
   old = __builtin_amdgcn_readfirstlane(__shfl(old, 0));
-  if ((int)old + 1 != T.b) return;
+  if ((int)old + 1 != T.b) return false;
   // the last slice: no other slice of this row block touches the counter
   // again this step; it counts from zero in the next
   if (lane == 0) st_sc1(&P.fixc[(size_t)T.fix * kLine], 0u);
@@ -1205,46 +1213,82 @@ __device__ __forceinline__ void ctl_wide_post(const Params& P, const Tile& T0, S
 #pragma unroll
   for (int i = 0; i < 32; ++i) y[i] = 0.f;
   const int q = lane >> 4, s16 = lane & 15;
-  // o-proj and down: the residual, loaded together with the other slices'
-  // partial sums (one round trip for both)
+  const int l = T.layer;
+  // o-proj and down: the residual and the next RMSNorm's gain, loaded together
+  // with the other slices' partial sums (one round trip for all)
   const bool resid = T.type == T_OPROJ || T.type == T_DOWN;
   float rv[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i) rv[i] = 0.f;
+  // RMSNorm site this epilogue writes (o-proj: the MLP input of this layer;
+  // down: the next layer's attention input, or after the last layer the final
+  // norm's input): 0 attention input, 1 MLP input, 2 final
+  const int last = l == P.L - 1;
+  const int site = T.type == T_OPROJ ? 1 : 2 * last;
+  const LayerBufs* nb = P.layers + (T.type == T_OPROJ ? l : l + 1 - last);
   if (resid) {
-    const LayerBufs* lbp = P.layers + T.layer;
+    // in the store mapping of the epilogue: entry 4i + k of lane l is row
+    // 4(l % 16) + k of sequence 4i + l / 16
+    const LayerBufs* lbp = P.layers + l;
     // o-proj: x_in (layer 0: the embedding row); down: x_mid (consecutive table fields)
     const float* res = cload((const float* const*)&lbp->x_in, T.type == T_OPROJ ? 0 : 1);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int n = 16 * h + s16;
-      if (h >= nh || n >= P.B) continue;
-#pragma unroll
-      for (int m = 0; m < 16; ++m) {
-        const int row = T.r0 + q + 4 * m;
-        if (res) {
-          rv[h * 16 + m] = ld_sc1(res + (size_t)n * P.H + row);
-        } else {
-          const WT* ep = (const WT*)P.embed + (size_t)sm.tok[n] * P.H + row;
-          rv[h * 16 + m] = sizeof(WT) == 2 ? bf16_lo(*(const uint16_t*)ep) : *(const float*)ep;
-        }
+    for (int i = 0; i < 8; ++i) {
+      const int n = 4 * i + q;
+      if (i >= 4 * nh || n >= P.B) continue;
+      if (res) {
+        const u32x4 v = ld_sc1_x4(res, n * P.H + T.r0 + 4 * s16);
+        rv[4 * i + 0] = __uint_as_float(v.x);
+        rv[4 * i + 1] = __uint_as_float(v.y);
+        rv[4 * i + 2] = __uint_as_float(v.z);
+        rv[4 * i + 3] = __uint_as_float(v.w);
+      } else {  // layer 0: the token's embedding row (bf16 weights: wide plans are bf16 only)
+        const uint2 e = *(const uint2*)((const uint16_t*)P.embed + (size_t)sm.tok[n] * P.H + T.r0 + 4 * s16);
+        rv[4 * i + 0] = __uint_as_float(e.x << 16);
+        rv[4 * i + 1] = __uint_as_float(e.x & 0xFFFF0000u);
+        rv[4 * i + 2] = __uint_as_float(e.y << 16);
+        rv[4 * i + 3] = __uint_as_float(e.y & 0xFFFF0000u);
       }
     }
+    const float* gsel = cload((const float* const*)&nb->attn_norm, site == 1 ? 1 : 0);
+    const float* gfin = cload((const float* const*)&nb->final_norm, 0);
+    const float* gain = site == 2 ? gfin : gsel;
+    // the row block's 64 gains into the (otherwise unused) row-sum area
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(gain), (__attribute__((address_space(3))) void*)&sm.red[0][0], 4,
+                                             (uint32_t)lane * 4u, T.r0 * 4, 0, 0);
   }
+  // QKV, gate/up and LM head: the sums of squares of their operand's rows
+  // (every 64-row block, per sequence), into the top of the operand area
+  const bool consumer = T.type == T_QKV || T.type == T_GATEUP || T.type == T_LM;
+  const int nrb = P.H / kWideRows;
+  const int ssp = nrb / 8;  // 1 KiB pieces of the table [nrb][32]
+  if (consumer) {
+    const float* ssc = cload((const float* const*)&P.layers[l].ss1, T.type == T_QKV ? 0 : T.type == T_GATEUP ? 1 : 2);
+    const __amdgpu_buffer_rsrc_t r = rsrc(ssc);
+    for (int i = 0; i < ssp; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void*)(sm.xs + (kWideFrags - ssp + i) * 256), 16,
+          (uint32_t)lane * 16u, i * 1024, 0, 16 /* sc1 */);
+  }
+  // slices of a batch in LDS slots, the own slice skipped (it stays in the
+  // compute waves' partial-sum area)
   const int fit = 16 / nh;  // slots the operand area holds
-  for (int s0 = 0; s0 < T.b; s0 += fit) {
-    const int s1 = min(T.b, s0 + fit);
+  for (int s0 = 0; s0 < T.b; s0 += fit + (T.c >= s0 && T.c < s0 + fit + 1 ? 1 : 0)) {
+    const int own = T.c >= s0 && T.c < s0 + fit + 1;
+    const int s1 = min(T.b, s0 + fit + own);
     for (int sl = s0; sl < s1; ++sl) {
       if (sl == T.c) continue;
+      const int slot = sl - s0 - (sl > T.c ? own : 0);
       const __amdgpu_buffer_rsrc_t r = rsrc(P.wpart + (size_t)(T.pslot + sl) * kWidePart);
       for (int i = 0; i < per; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            r, (__attribute__((address_space(3))) void*)(sm.xs + ((sl - s0) * per + i) * 256), 16,
+            r, (__attribute__((address_space(3))) void*)(sm.xs + (slot * per + i) * 256), 16,
             (uint32_t)lane * 16u, i * 1024, 0, 16 /* sc1 */);
     }
     __builtin_amdgcn_s_waitcnt(0);
     for (int sl = s0; sl < s1; ++sl) {
-      const float* src = sl == T.c ? cp : sm.xs + (sl - s0) * per * 256;
+      const int slot = sl - s0 - (sl > T.c ? own : 0);
+      const float* src = sl == T.c ? cp : sm.xs + slot * per * 256;
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -1252,7 +1296,19 @@ __device__ __forceinline__ void ctl_wide_post(const Params& P, const Tile& T0, S
           if (h < nh) y[h * 16 + m] += src[(h * kWideRows + q + 4 * m) * 16 + s16];
     }
   }
-  const int l = T.layer;
+  if (consumer) {  // divide by the root mean square of the operand's row
+    const float* ssl = sm.xs + (kWideFrags - ssp) * 256;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int n = 16 * h + s16;
+      if (h >= nh) break;
+      float sum = 0.f;
+      for (int rb = 0; rb < nrb; ++rb) sum += ssl[rb * kMaxBatch + n];
+      const float inv = 1.0f / sqrtf(sum / (float)P.H + P.eps);
+#pragma unroll
+      for (int m = 0; m < 16; ++m) y[h * 16 + m] *= inv;
+    }
+  }
   switch (T.type) {
     case T_QKV: {
       const int half = P.D / 2;
@@ -1293,19 +1349,48 @@ __device__ __forceinline__ void ctl_wide_post(const Params& P, const Tile& T0, S
     }
     case T_OPROJ:
     case T_DOWN: {
-      // o-proj: x_mid = x_in + y; down: x_out = x_mid + y (consecutive table fields)
+      // o-proj: x_mid = x_in + y; down: x_out = x_mid + y (consecutive table
+      // fields); then gain * x as the next RMSNorm's operand and this row
+      // block's sums of squares.  The sums go through LDS ([sequence][row],
+      // pitch 68: conflict-free both ways) into the store mapping, where a
+      // lane owns four consecutive rows and sixteen lanes a sequence's 64.
       const LayerBufs* lbp = P.layers + l;
       float* dst = cload((float* const*)&lbp->x_mid, T.type == T_OPROJ ? 0 : 1);
+      uint16_t* plane = cload((uint16_t* const*)&nb->xn1, 2 * site);
+      float* ssd = cload((float* const*)&nb->ss1, site);
+      constexpr int TP = 68;
+      float* tr = sm.xs;  // the operand area is free after the slice sums
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         if (h >= nh) break;
-        const int n = 16 * h + s16;
-        if (n >= P.B) continue;
 #pragma unroll
-        for (int m = 0; m < 16; ++m) {
-          const int row = T.r0 + q + 4 * m;
-          st_sc1(dst + (size_t)n * P.H + row, rv[h * 16 + m] + y[h * 16 + m]);
+        for (int m = 0; m < 16; ++m) tr[(16 * h + s16) * TP + q + 4 * m] = y[h * 16 + m];
+      }
+      const f32x4 g4 = *(const f32x4*)&sm.red[0][4 * s16];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (i >= 4 * nh) break;
+        const int n = 4 * i + q;
+        const f32x4 v = *(const f32x4*)&tr[n * TP + 4 * s16];
+        const float x0 = rv[4 * i] + v.x, x1 = rv[4 * i + 1] + v.y, x2 = rv[4 * i + 2] + v.z,
+                    x3 = rv[4 * i + 3] + v.w;
+        float sq = fmaf(x3, x3, fmaf(x2, x2, fmaf(x1, x1, x0 * x0)));
+        if (n < P.B) {
+          const uint32_t at = (uint32_t)(n * P.H + T.r0 + 4 * s16);
+          st_sc1_x4(dst, at * 4u,
+                    u32x4{__float_as_uint(x0), __float_as_uint(x1), __float_as_uint(x2), __float_as_uint(x3)});
+          const float g0 = g4.x * x0, g1 = g4.y * x1, g2 = g4.z * x2, g3 = g4.w * x3;
+          const uint16_t h0 = to_bf16(g0), h1 = to_bf16(g1), h2 = to_bf16(g2), h3 = to_bf16(g3);
+          st_sc1_x2(plane, at * 2u,
+                    u32x2{(uint32_t)h0 | ((uint32_t)h1 << 16), (uint32_t)h2 | ((uint32_t)h3 << 16)});
+          const uint16_t l0 = to_bf16(g0 - bf16_lo(h0)), l1 = to_bf16(g1 - bf16_lo(h1)),
+                         l2 = to_bf16(g2 - bf16_lo(h2)), l3 = to_bf16(g3 - bf16_lo(h3));
+          st_sc1_x2(plane, (uint32_t)(kMaxBatch * P.H) * 2u + at * 2u,
+                    u32x2{(uint32_t)l0 | ((uint32_t)l1 << 16), (uint32_t)l2 | ((uint32_t)l3 << 16)});
         }
+#pragma unroll
+        for (int x = 1; x < 16; x <<= 1) sq += __shfl_xor(sq, x);
+        if (s16 == 0 && n < P.B) st_sc1(ssd + (T.r0 / kWideRows) * kMaxBatch + n, sq);
       }
       break;
     }
@@ -1353,66 +1438,49 @@ __device__ __forceinline__ void ctl_wide_post(const Params& P, const Tile& T0, S
       break;
     }
   }
+  return true;
 }
 
-// A norm tile of a wide plan: one sequence's row (the embedding row at layer
-// 0), x / sqrt(mean(x^2) + eps) * gain, to the hi/lo operand planes.  Lane l
-// holds columns 512g + 8l .. +7.
+// The layer-0 tile of one sequence in a wide plan: its embedding row as the
+// first QKV operand, gain * x in the hi/lo planes, and the row's sum of
+// squares per 64-column block (the QKV epilogue divides by the root mean
+// square).  Lane l holds columns 512g + 8l .. +7, so eight consecutive lanes
+// cover one block.
 template <typename WT, int KMAX>
 __device__ __forceinline__ void ctl_norm(const Params& P, const Tile& T0, const Smem<WT, KMAX>& sm, int lane0) {
   const int lane = opaque(lane0);
   const Tile T = uni(T0);
-  const int l = T.layer, b = T.b, K = P.H;
+  const int b = T.b, K = P.H;
   const int ng = K / 512;
-  // Source row, gain and destination by indexing runs of consecutive pointers
-  // of the per-layer table (x_in, x_mid, x_out), (attn_norm, mlp_norm) and
-  // (xn1, xattn, xn2, xh, xnf): no select between pointers.  Final-norm tiles
-  // belong to the last layer.
-  const LayerBufs* lbp = P.layers + l;
-  const int which = T.type - T_NORM;  // 0 attention input, 1 MLP input, 2 final
-  const float* src = cload((const float* const*)&lbp->x_in, which);  // null: layer 0's embedding row
-  const float* gain = cload((const float* const*)&lbp->attn_norm, which < 2 ? which : 0);
-  const float* gf = cload((const float* const*)&lbp->final_norm, 0);
-  if (which == 2) gain = gf;
-  uint16_t* dst = cload((uint16_t* const*)&lbp->xn1, 2 * which);
-  float v[32];
+  const LayerBufs* lbp = P.layers;
+  const float* gain = cload((const float* const*)&lbp->attn_norm, 0);
+  uint16_t* dst = cload((uint16_t* const*)&lbp->xn1, 0);
+  float* ss = cload((float* const*)&lbp->ss1, 0);
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     if (g >= ng) break;
     const int e = 512 * g + 8 * lane;
-    if (src) {
-      const u32x4 a = ld_sc1_x4(src, b * K + e), c = ld_sc1_x4(src, b * K + e + 4);
-      v[8 * g + 0] = __uint_as_float(a.x); v[8 * g + 1] = __uint_as_float(a.y);
-      v[8 * g + 2] = __uint_as_float(a.z); v[8 * g + 3] = __uint_as_float(a.w);
-      v[8 * g + 4] = __uint_as_float(c.x); v[8 * g + 5] = __uint_as_float(c.y);
-      v[8 * g + 6] = __uint_as_float(c.z); v[8 * g + 7] = __uint_as_float(c.w);
-    } else {  // layer 0: the embedding row (bf16)
-      const u32x4 c = *(const u32x4*)((const uint16_t*)P.embed + (size_t)sm.tok[b] * K + e);
-      unpack<uint16_t>(c, &v[8 * g]);
-    }
-  }
-  float ss = 0.f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i)
-    if (i < 8 * ng) ss = fmaf(v[i], v[i], ss);
-  ss = wave_sum(ss);
-  const float inv = 1.0f / sqrtf(ss / (float)K + P.eps);
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    if (g >= ng) break;
-    const int e = 512 * g + 8 * lane;
+    float v[8];
+    const u32x4 c = *(const u32x4*)((const uint16_t*)P.embed + (size_t)sm.tok[b] * K + e);
+    unpack<uint16_t>(c, v);
     const f32x4 g0 = *(const f32x4*)(gain + e), g1 = *(const f32x4*)(gain + e + 4);
     const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
     uint32_t hw[4], lw[4];
+    float sq = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; i += 2) {
-      const float y0 = v[8 * g + i] * inv * gg[i], y1 = v[8 * g + i + 1] * inv * gg[i + 1];
+      const float y0 = v[i] * gg[i], y1 = v[i + 1] * gg[i + 1];
+      sq = fmaf(v[i], v[i], sq);
+      sq = fmaf(v[i + 1], v[i + 1], sq);
       const uint16_t h0 = to_bf16(y0), h1 = to_bf16(y1);
       hw[i / 2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
       lw[i / 2] = (uint32_t)to_bf16(y0 - bf16_lo(h0)) | ((uint32_t)to_bf16(y1 - bf16_lo(h1)) << 16);
     }
     st_sc1_x4(dst, (uint32_t)(b * K + e) * 2u, u32x4{hw[0], hw[1], hw[2], hw[3]});
     st_sc1_x4(dst, (uint32_t)((kMaxBatch + b) * K + e) * 2u, u32x4{lw[0], lw[1], lw[2], lw[3]});
+#pragma unroll
+    for (int x = 1; x < 8; x <<= 1) sq += __shfl_xor(sq, x);
+    if ((lane & 7) == 0) st_sc1(ss + (8 * g + lane / 8) * kMaxBatch + b, sq);
   }
 }
 
@@ -1422,8 +1490,20 @@ __device__ __forceinline__ EpiIn ctl_pre(const Params& P, const Tile& T, int b, 
   constexpr int KH = CPR_H * 16 / sizeof(WT), KF = CPR_F * 16 / sizeof(WT);
   EpiIn e{0.f, 1.f, 0.f};
   if constexpr (WIDE) {
-    if (is_gemv(T.type)) ctl_stage_x<WT>(P, T, sm, lane);
-    else if (is_attn(T.type)) ctl_attn_in<WT>(P, T, sm, lane, b == 0);
+    if (is_gemv(T.type)) {
+      // The operand slice stays in LDS for the worker's next tile of the
+      // same operator and K slice (with queues dealt round-robin, a worker
+      // keeps meeting the same slice of a four-slice operator), unless a
+      // row-block reduction or an attention tile has overwritten it since.
+      const int key = (T.layer * T_NTYPES + T.type) * 64 + T.c;
+      if (key != xkey) {
+        ctl_stage_x<WT>(P, T, sm, lane);
+        xkey = key;
+      }
+    } else if (is_attn(T.type)) {
+      ctl_attn_in<WT>(P, T, sm, lane, b == 0);
+      xkey = -1;
+    }
     return e;
   }
   if (is_gemv(T.type)) {
@@ -1458,18 +1538,18 @@ __device__ __forceinline__ EpiIn ctl_pre(const Params& P, const Tile& T, int b, 
 
 template <typename WT, int CPR_H, int CPR_F, bool WIDE, int KMAX>
 __device__ __forceinline__ void ctl_post(const Params& P, const Tile& T, int b, Smem<WT, KMAX>& sm, const EpiIn& e,
-                                         int lane) {
+                                         int lane, int& xkey) {
   if constexpr (WIDE) {
     switch (T.type) {
       case T_QKV:
       case T_OPROJ:
       case T_GATEUP:
       case T_DOWN:
-      case T_LM: ctl_wide_post<WT>(P, T, sm, lane); break;
+      case T_LM:
+        if (ctl_wide_post<WT>(P, T, sm, lane)) xkey = -1;  // the reduction used the operand area
+        break;
       case T_ARGMAX: ctl_argmax<WT>(P, sm, lane); break;  // attention: merged by the caller
-      case T_NORM:
-      case T_NORM2:
-      case T_NORMF: ctl_norm<WT>(P, T, sm, lane); break;
+      case T_NORM: ctl_norm<WT>(P, T, sm, lane); break;
       default: break;
     }
     return;
@@ -1620,7 +1700,7 @@ __device__ __forceinline__ void control_loop(const Params& P, Smem<WT, KMAX>& sm
         t_ready = sm.t_ready;
         t_done = sm.t_done;
       }
-      ctl_post<WT, CPR_H, CPR_F, WIDE>(P, Tb, b, sm, e, lane);
+      ctl_post<WT, CPR_H, CPR_F, WIDE>(P, Tb, b, sm, e, lane, xkey);
       if (WIDE && is_attn(T.type) && attn_count(P, Tb, sm.pos[T.b]) > 0) attn_run_merge(P, run, sm, lane);
     }
     if (WIDE && T.type == T_ATTN) attn_run_partial(P, T, run, sm, lane);
@@ -1880,7 +1960,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
       const EpiIn e = ctl_pre<WT, CPR_H, CPR_F, WIDE>(P, Tb, b, sm, lane, xkey);
       __syncthreads();  // A
       __syncthreads();  // B
-      ctl_post<WT, CPR_H, CPR_F, WIDE>(P, Tb, b, sm, e, lane);
+      ctl_post<WT, CPR_H, CPR_F, WIDE>(P, Tb, b, sm, e, lane, xkey);
       if (WIDE && is_attn(T.type) && attn_count(P, Tb, sm.pos[T.b]) > 0) attn_run_merge(P, run, sm, lane);
     }
     if (WIDE && T.type == T_ATTN) attn_run_partial(P, T, run, sm, lane);

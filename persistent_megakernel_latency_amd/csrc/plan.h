@@ -22,11 +22,12 @@ enum TileType : int32_t {
   T_DOWN = 5,     // down projection + residual
   T_LM = 6,       // final RMSNorm prologue, tied LM-head rows, partial argmax
   T_ARGMAX = 7,   // greedy token, seq_len advance (output conversion)
-  // wide plans (batch above kMaxBatchGemv) normalise each sequence's row once,
-  // into the bf16 operand the matrix-core tiles read
-  T_NORM = 8,     // attention-input RMSNorm (layer 0: of the embedding row)
-  T_NORM2 = 9,    // MLP-input RMSNorm
-  T_NORMF = 10,   // final RMSNorm before the LM head
+  // wide plans (batch above kMaxBatchGemv): the layer-0 embedding row of each
+  // sequence into the bf16 operand the matrix-core tiles read (later RMSNorm
+  // inputs are written by the tiles that produce them)
+  T_NORM = 8,
+  T_NORM2 = 9,    // not emitted (former per-sequence MLP-input norm)
+  T_NORMF = 10,   // not emitted (former per-sequence final norm)
   // LDS forwarding: attention over every KV chunk of one (sequence, kv head),
   // each chunk's partial merged on chip into the next (the combine chained
   // onto the same worker; no partials in global memory, no combine tile)
@@ -109,12 +110,21 @@ struct LayerBufs {
   // to bf16, lo the remainder rounded to bf16: about 16 significant bits).
   // Rows past B stay zero.
   // (xn1, xattn, xn2, xh, xnf are consecutive: the kernels index them)
-  uint16_t* xn1;      // normalised attention input
+  uint16_t* xn1;      // attention input (gain-scaled, see below)
   uint16_t* xattn;    // attention output
-  uint16_t* xn2;      // normalised MLP input
+  uint16_t* xn2;      // MLP input (gain-scaled)
   uint16_t* xh;       // SwiGLU output
-  uint16_t* xnf;      // normalised final hidden state (last layer only)
+  uint16_t* xnf;      // final hidden state (gain-scaled; last layer only)
   const float* final_norm;  // the final RMSNorm gain (same in every layer)
+  // Wide plans: the RMSNorm is split between producer and consumer.  The
+  // operand planes xn1, xn2 and xnf hold gain * x (not yet divided by the
+  // root mean square); the tile that writes a 64-row block of x also writes
+  // that block's sum of squares per sequence here, [H/64][32], and the
+  // consumer's epilogue scales its sums by 1 / sqrt(mean + eps).
+  // (ss1, ss2, ssf are consecutive: the kernels index them)
+  float* ss1;         // attention input
+  float* ss2;         // MLP input
+  float* ssf;         // final (last layer only)
 };
 
 // Per-layer weights as the kernels see them: kept inside the kernel arguments

@@ -28,6 +28,7 @@ void rope_table(const Shape& s, std::vector<float>& cos_t, std::vector<float>& s
 struct ActLayout {
   int64_t x_mid, x_out, q, part, attn, h;  // float offsets within a layer
   int64_t xn1, xattn, xn2, xh, xnf;        // wide plans: bf16 hi/lo planes [2][32][K] (float offsets; 0 size otherwise)
+  int64_t ss1, ss2, ssf;                   // wide plans: RMSNorm sums of squares [H/64][32] (0 size otherwise)
   int64_t per_layer;
   int64_t total;                                      // floats for all layers
 };

@@ -75,8 +75,9 @@ std::string check_shape(const wpk_model_desc& d, int32_t batch, int32_t ctx_len,
     if (s.H % kWideK || s.F % kWideK) return "batches above 4 need hidden and ffn to be multiples of 512";
     if (s.D != kWideRows) return "batches above 4 need head_dim 64";
     // the last slice of a K = hidden row block loads the other slices'
-    // partial sums and the RMSNorm sums of squares into one 64 KiB LDS area
-    if (s.H > 4096) return "batches above 4 need hidden <= 4096";
+    // partial sums, the RoPE factors and the RMSNorm sums of squares into one
+    // 64 KiB LDS area
+    if (s.H > 2048) return "batches above 4 need hidden <= 2048";
     s.rows_h = s.rows_qkv = s.rows_f = kWideRows;
   }
   s.workers_per_cu = o.workers_per_cu ? o.workers_per_cu : 2;

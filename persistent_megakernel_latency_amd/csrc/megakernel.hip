@@ -1270,6 +1270,24 @@ __device__ __forceinline__ bool ctl_wide_post(const Params& P, const Tile& T0, S
           r, (__attribute__((address_space(3))) void*)(sm.xs + (kWideFrags - ssp + i) * 256), 16,
           (uint32_t)lane * 16u, i * 1024, 0, 16 /* sc1 */);
   }
+  // q and k rows: the RoPE factors of each sequence's position, [n][D/2] cos
+  // then sin, into pieces 48..55 of the operand area (above the slices of a
+  // K = hidden row block, below the sums of squares)
+  float* const rl = sm.xs + 48 * 256;
+  if (T.type == T_QKV && T.kind < 2) {
+    const __amdgpu_buffer_rsrc_t rc = rsrc(P.rope_cos), rs = rsrc(P.rope_sin);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = 8 * j + (lane >> 3);
+      int p = n < P.B ? sm.pos[n] : 0;
+      p = p < 0 || p >= P.cap ? 0 : p;
+      const uint32_t voff = (uint32_t)(p * (kHeadDim / 2) + 4 * (lane & 7)) * 4u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (__attribute__((address_space(3))) void*)(rl + j * 256), 16,
+                                               voff, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(rl + (4 + j) * 256),
+                                               16, voff, 0, 0, 0);
+    }
+  }
   // slices of a batch in LDS slots, the own slice skipped (it stays in the
   // compute waves' partial-sum area)
   const int fit = 16 / nh;  // slots the operand area holds
@@ -1309,40 +1327,57 @@ __device__ __forceinline__ bool ctl_wide_post(const Params& P, const Tile& T0, S
       for (int m = 0; m < 16; ++m) y[h * 16 + m] *= inv;
     }
   }
+  // The sums into LDS ([sequence][row], pitch 68: conflict-free both ways;
+  // the operand area is free after the slice sums), read back in the store
+  // mapping: lane l owns rows 4(l % 16) .. +3 of sequence 4i + l / 16, so
+  // sixteen lanes store a sequence's 64 rows with full 16- or 8-byte stores.
+  constexpr int TP = 68;
+  float* tr = sm.xs;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (h >= nh) break;
+#pragma unroll
+    for (int m = 0; m < 16; ++m) tr[(16 * h + s16) * TP + q + 4 * m] = y[h * 16 + m];
+  }
+  const int r4 = 4 * s16;
   switch (T.type) {
     case T_QKV: {
-      const int half = P.D / 2;
+      // rows [0, 32) are head dimensions [0, 32), rows [32, 64) dimensions
+      // [32, 64): a RoPE pair is rows d and d + 32, on lanes s16 and s16 + 8
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        if (h >= nh) break;
-        const int n = 16 * h + s16;
+      for (int i = 0; i < 8; ++i) {
+        if (i >= 4 * nh) break;
+        const int n = 4 * i + q;
         const int p = n < P.B ? sm.pos[n] : -1;
         if (p < 0) continue;  // past the batch, or an inactive slot: nothing to append
         if (p >= P.cap) {
           latch_error(P, WPK_E_CTX_FULL, T.id);
           continue;
         }
-        if (T.kind < 2) {
+        const f32x4 own = *(const f32x4*)&tr[n * TP + r4];
+        const size_t at = ((((size_t)l * P.B + n) * P.Hkv + T.g) * P.cap + p) * P.D + r4;
+        if (T.kind == 2) {
+          st_sc1_x2((uint16_t*)P.vc, (uint32_t)(at * 2),
+                    u32x2{(uint32_t)to_bf16(own.x) | ((uint32_t)to_bf16(own.y) << 16),
+                          (uint32_t)to_bf16(own.z) | ((uint32_t)to_bf16(own.w) << 16)});
+          continue;
+        }
+        const int lo = r4 < 32;  // this lane holds the first rows of its pairs
+        const f32x4 oth = *(const f32x4*)&tr[n * TP + (lo ? r4 + 32 : r4 - 32)];
+        const int d = r4 & 31;
+        const f32x4 cs = *(const f32x4*)&rl[n * 32 + d], sn = *(const f32x4*)&rl[1024 + n * 32 + d];
+        // dimension d: a cos - b sin; dimension d + 32: b cos + a sin (a = row d, b = row d + 32)
+        const float sg = lo ? -1.f : 1.f;
+        const float o0 = own.x * cs.x + sg * oth.x * sn.x, o1 = own.y * cs.y + sg * oth.y * sn.y,
+                    o2 = own.z * cs.z + sg * oth.z * sn.z, o3 = own.w * cs.w + sg * oth.w * sn.w;
+        if (T.kind == 0) {
           float* qd = act(P, l, P.off_q) + (size_t)n * P.Hq * P.D + T.g * P.D;
-          const size_t at = ((((size_t)l * P.B + n) * P.Hkv + T.g) * P.cap + p) * P.D;
-#pragma unroll
-          for (int m = 0; m < 8; ++m) {
-            const int dim = q + 4 * m;
-            const float a = y[h * 16 + m], b = y[h * 16 + m + 8];  // rows dim and dim + D/2
-            const float cs = P.rope_cos[p * half + dim], sn = P.rope_sin[p * half + dim];
-            const float ra = a * cs - b * sn, rb = b * cs + a * sn;
-            if (T.kind == 0) {
-              st_sc1(qd + dim, ra);
-              st_sc1(qd + dim + half, rb);
-            } else {
-              st_sc1((uint16_t*)P.kc + at + dim, to_bf16(ra));
-              st_sc1((uint16_t*)P.kc + at + dim + half, to_bf16(rb));
-            }
-          }
+          st_sc1_x4(qd, (uint32_t)r4 * 4u,
+                    u32x4{__float_as_uint(o0), __float_as_uint(o1), __float_as_uint(o2), __float_as_uint(o3)});
         } else {
-          const size_t at = ((((size_t)l * P.B + n) * P.Hkv + T.g) * P.cap + p) * P.D;
-#pragma unroll
-          for (int m = 0; m < 16; ++m) st_sc1((uint16_t*)P.vc + at + q + 4 * m, to_bf16(y[h * 16 + m]));
+          st_sc1_x2((uint16_t*)P.kc, (uint32_t)(at * 2),
+                    u32x2{(uint32_t)to_bf16(o0) | ((uint32_t)to_bf16(o1) << 16),
+                          (uint32_t)to_bf16(o2) | ((uint32_t)to_bf16(o3) << 16)});
         }
       }
       break;
@@ -1358,14 +1393,6 @@ __device__ __forceinline__ bool ctl_wide_post(const Params& P, const Tile& T0, S
       float* dst = cload((float* const*)&lbp->x_mid, T.type == T_OPROJ ? 0 : 1);
       uint16_t* plane = cload((uint16_t* const*)&nb->xn1, 2 * site);
       float* ssd = cload((float* const*)&nb->ss1, site);
-      constexpr int TP = 68;
-      float* tr = sm.xs;  // the operand area is free after the slice sums
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        if (h >= nh) break;
-#pragma unroll
-        for (int m = 0; m < 16; ++m) tr[(16 * h + s16) * TP + q + 4 * m] = y[h * 16 + m];
-      }
       const f32x4 g4 = *(const f32x4*)&sm.red[0][4 * s16];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -1395,43 +1422,51 @@ __device__ __forceinline__ bool ctl_wide_post(const Params& P, const Tile& T0, S
       break;
     }
     case T_GATEUP: {
+      // rows [0, 32) are gate rows, [32, 64) the up rows of the same h columns
       uint16_t* xh = (uint16_t*)act(P, l, P.off_xh);
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        if (h >= nh) break;
-        const int n = 16 * h + s16;
-        if (n >= P.B) continue;
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-          const float g = y[h * 16 + m], u = y[h * 16 + m + 8];  // gate row j, up row j
-          st_hilo(xh, (size_t)kMaxBatch * P.F, (size_t)n * P.F + T.r0 + q + 4 * m, g / (1.0f + __expf(-g)) * u);
-        }
+      for (int i = 0; i < 8; ++i) {
+        if (i >= 4 * nh) break;
+        const int n = 4 * i + q;
+        if (n >= P.B || s16 >= 8) continue;
+        const f32x4 g = *(const f32x4*)&tr[n * TP + r4], u = *(const f32x4*)&tr[n * TP + 32 + r4];
+        const float h0 = g.x / (1.0f + __expf(-g.x)) * u.x, h1 = g.y / (1.0f + __expf(-g.y)) * u.y,
+                    h2 = g.z / (1.0f + __expf(-g.z)) * u.z, h3 = g.w / (1.0f + __expf(-g.w)) * u.w;
+        const uint32_t at = (uint32_t)(n * P.F + T.r0 + r4) * 2u;
+        const uint16_t a0 = to_bf16(h0), a1 = to_bf16(h1), a2 = to_bf16(h2), a3 = to_bf16(h3);
+        st_sc1_x2(xh, at, u32x2{(uint32_t)a0 | ((uint32_t)a1 << 16), (uint32_t)a2 | ((uint32_t)a3 << 16)});
+        const uint16_t b0 = to_bf16(h0 - bf16_lo(a0)), b1 = to_bf16(h1 - bf16_lo(a1)),
+                       b2 = to_bf16(h2 - bf16_lo(a2)), b3 = to_bf16(h3 - bf16_lo(a3));
+        st_sc1_x2(xh, (uint32_t)(kMaxBatch * P.F) * 2u + at,
+                  u32x2{(uint32_t)b0 | ((uint32_t)b1 << 16), (uint32_t)b2 | ((uint32_t)b3 << 16)});
       }
       break;
     }
     default: {  // LM head: logits and the block's per-sequence maximum
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        if (h >= nh) break;
-        const int n = 16 * h + s16;
+      for (int i = 0; i < 8; ++i) {
+        if (i >= 4 * nh) break;
+        const int n = 4 * i + q;
         unsigned long long key = 0;
         if (n < P.B) {
+          const f32x4 v = *(const f32x4*)&tr[n * TP + r4];
+          const float vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-          for (int m = 0; m < 16; ++m) {
-            const int row = T.r0 + q + 4 * m;
+          for (int k = 0; k < 4; ++k) {
+            const int row = T.r0 + r4 + k;
             if (row < P.V) {
-              P.logits[(size_t)n * P.V + row] = y[h * 16 + m];
-              const unsigned long long k = pack_max(y[h * 16 + m], row);
-              key = k > key ? k : key;
+              P.logits[(size_t)n * P.V + row] = vv[k];
+              const unsigned long long c = pack_max(vv[k], row);
+              key = c > key ? c : key;
             }
           }
         }
 #pragma unroll
-        for (int x = 16; x < 64; x <<= 1) {
+        for (int x = 1; x < 16; x <<= 1) {
           const unsigned long long o = __shfl_xor(key, x);
           key = o > key ? o : key;
         }
-        if (q == 0 && n < P.B)
+        if (s16 == 0 && n < P.B)
           __hip_atomic_fetch_max(&P.argmax[n * kArgmaxShards + T.id % kArgmaxShards], key, __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT);
       }

@@ -1688,6 +1688,9 @@ __device__ __forceinline__ void control_loop(const Params& P, Smem<WT, KMAX>& sm
   // LM-head tiles feed only the final argmax: a worker publishes its run of
   // them with one wait and one increment when the run ends
   int lm_group = -1, lm_count = 0;
+  // the control wave's polls and publishes go ahead of the compute waves'
+  // weight loads in the CU's instruction arbitration
+  __builtin_amdgcn_s_setprio(3);
   while (cur < qn) {
     // lane index made opaque per tile, so per-lane address arithmetic of all
     // tile types is not hoisted out of the loop and kept live across it

@@ -1696,7 +1696,9 @@ __device__ __forceinline__ void control_loop(const Params& P, Smem<WT, KMAX>& sm
     // tile types is not hoisted out of the loop and kept live across it
     const int lane = opaque(lane0);
     const uint64_t t_claim = LOG ? __builtin_amdgcn_s_memrealtime() : 0;
-    const Tile T = WIDE && it ? get_tile(sm.tnext[it & 1]) : cload(P.qtiles, qb + cur);
+    // the descriptor: loaded at the end of the previous iteration (narrow
+    // plans) or by compute wave 1 (wide plans), and left in LDS
+    const Tile T = it ? get_tile(sm.tnext[WIDE ? it & 1 : 0]) : cload(P.qtiles, qb + cur);
     const int id = T.id;
     if (lm_count && T.type != T_LM) flush_lm(P, lm_group, lm_count, lane);
     int32_t delta = 0;
@@ -1780,6 +1782,10 @@ __device__ __forceinline__ void control_loop(const Params& P, Smem<WT, KMAX>& sm
     // queue behind the next weights, which then stream without a gap.  The
     // next claim was written by compute wave 1 before this tile's barrier B.
     const int nxt = __builtin_amdgcn_readfirstlane(sm.ids[(it + 1) & 1]);
+    // narrow plans: the next descriptor, fetched after the publish (so the
+    // scalar-cache miss delays neither the publish nor the next poll) and
+    // left in LDS for this wave and, past barrier C, the compute waves
+    if (!WIDE && nxt < qn) put_tile(sm.tnext[0], cload(P.qtiles, qb + nxt), lane);
     if (need_c<WIDE>(T, WIDE && nxt < qn ? __builtin_amdgcn_readfirstlane(sm.tnext[(it + 1) & 1][0]) : -1))
       __syncthreads();
     cur = nxt;
@@ -1807,6 +1813,7 @@ __device__ __forceinline__ void compute_loop(const Params& P, Smem<WT, KMAX>& sm
   for (int j = 0; j < kChunks; ++j) s.c[j] = u32x4{0u, 0u, 0u, 0u};
   int it = -1;  // claim iteration of the current tile
   int nx = cur;
+  bool c_taken = false;  // the previous tile ended with barrier C
   while (nx < qn) {
     // The slot is free (the previous tile's arithmetic is done and its
     // barrier B passed, so the control wave is already running that tile's
@@ -1816,7 +1823,10 @@ __device__ __forceinline__ void compute_loop(const Params& P, Smem<WT, KMAX>& sm
     // memory operations complete in issue order, so an atomic (slow while the
     // weights stream) would hold up every later wait of the control wave,
     // while here it returns ahead of the weights this wave waits for anyway.
-    const Tile T = WIDE && it >= 0 ? get_tile(sm.tnext[(it + 1) & 1]) : cload(P.qtiles, qb + nx);
+    // wide plans: from LDS (compute wave 1 fetched it); narrow plans: from
+    // LDS after barrier C (the control wave fetched it), else loaded here
+    const Tile T = it >= 0 && (WIDE || c_taken) ? get_tile(sm.tnext[WIDE ? (it + 1) & 1 : 0])
+                                                : cload(P.qtiles, qb + nx);
     uint32_t ahead = 0;
     if (tc0 == 0) ahead = atomic_add(head, 1u);
     // without weight prefetch (an ablation), the weights are loaded only once
@@ -1875,8 +1885,8 @@ __device__ __forceinline__ void compute_loop(const Params& P, Smem<WT, KMAX>& sm
     // above it would keep two slots live.
     __builtin_amdgcn_sched_barrier(0);
     nx = __builtin_amdgcn_readfirstlane(sm.ids[(it + 1) & 1]);
-    if (need_c<WIDE>(T, WIDE && nx < qn ? __builtin_amdgcn_readfirstlane(sm.tnext[(it + 1) & 1][0]) : -1))
-      __syncthreads();  // C
+    c_taken = need_c<WIDE>(T, WIDE && nx < qn ? __builtin_amdgcn_readfirstlane(sm.tnext[(it + 1) & 1][0]) : -1);
+    if (c_taken) __syncthreads();  // C
   }
 }
 

@@ -1604,24 +1604,29 @@ __device__ __forceinline__ void ctl_post(const Params& P, const Tile& T, int b, 
 // The control wave waits until the tile's counter group is complete for this
 // step.  Bounded: past the watchdog budget it latches WPK_E_TIMEOUT naming the
 // tile and raises the abort flag, which every other waiting worker also sees.
+template <bool WIDE>
 __device__ __forceinline__ bool wait_group(const Params& P, const Tile& T, uint32_t epoch, int32_t* delta,
                                            int lane) {
   const Group G = cload(P.groups, T.wait);
   const uint32_t target = (epoch + 1u) * (uint32_t)G.producers;
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-  for (;;) {
+  for (uint32_t n = 0;; ++n) {
     const uint32_t v = lane < G.shards ? ld_sc1(&P.counters[(size_t)(G.shard0 + lane) * kLine]) : 0u;
     const uint32_t sum = wave_sum_u32(v);
     if ((int32_t)(sum - target) >= 0) {
       *delta = (int32_t)(sum - target);
       return true;
     }
-    if (ld_sc1(&P.ctl[CTL_ABORT])) return false;
+    // Narrow plans read the abort flag every 16th poll: a round trip per poll
+    // to one line that every waiting worker reads halves the poll rate (1.2%
+    // of a batch-1 step).  Wide plans read it every poll: their faster polls
+    // add more load than they save (+2% at batch 32).
+    if ((WIDE || (n & 15u) == 15u) && ld_sc1(&P.ctl[CTL_ABORT])) return false;
     if (__builtin_amdgcn_s_memrealtime() - t0 > P.watchdog_ticks) {
       if (lane == 0) latch_error(P, WPK_E_TIMEOUT, T.id);
       return false;
     }
-    __builtin_amdgcn_s_sleep(1);
+    __builtin_amdgcn_s_sleep(WIDE ? 1 : 2);
   }
 }
 
@@ -1708,7 +1713,7 @@ __device__ __forceinline__ void control_loop(const Params& P, Smem<WT, KMAX>& sm
     // logged steps, which check that every tile starts after its producers
     const bool idle = is_attn(T.type) && attn_count(P, T, sm.pos[T.b]) == 0;
     if (T.wait >= 0 && (LOG || (T.wait != done_group && !idle))) {
-      ok = wait_group(P, T, epoch, &delta, lane);
+      ok = wait_group<WIDE>(P, T, epoch, &delta, lane);
       if (ok) done_group = T.wait;
     }
     if (lane == 0) sm.stop = ok ? 0 : 1;

@@ -21,7 +21,7 @@ struct Shape {
   int32_t rows_qkv;  // rows of a QKV tile (RoPE pairs (i, i+D/2) stay together)
   int32_t rows_f;    // rows of a K=ffn GEMV tile
   int32_t tile_bytes, workers_per_cu, queue_shards;
-  int32_t wide;      // batch above kMaxBatchGemv: matrix-core tiles and per-sequence norm tiles
+  int32_t wide;      // batch above kMaxBatchGemv: matrix-core tiles, RMSNorm split between epilogues
   int32_t attn_sub;  // KV chunks per attention tile (one slot holds up to 64 KiB of K and V)
   int32_t forward;   // chained attention tiles (LDS forwarding of the partials to the combine)
   float theta, eps;

@@ -191,7 +191,8 @@ float inv_rms(const Params& P, const float* ss, int b) {
 }
 
 // Input vector of a GEMV tile for sequence b, with its RMSNorm prologue.  In
-// a wide plan it is the operand row the norm tile or the producer wrote.
+// a wide plan it is the operand row (gain * x for the normalised inputs) the
+// producing tile wrote; the consumer's epilogue divides by the root mean square.
 void gemv_input(Ctx& c, const Tile& T, int b, std::vector<float>& x) {
   const Params& P = c.P;
   const LayerBufs& lb = P.layers[T.layer];

@@ -392,6 +392,120 @@ __global__ __launch_bounds__(256) void k_pp_loaded(unsigned* ctr, int iters, con
   if (acc == 0x9e3779b9u) sink[blockIdx.x * blockDim.x + t] = acc;
 }
 
+// ---- publish detection: block 0 publishes (stores a timestamp, waits for it,
+// adds 1 to line i % lines) every 20 us; blocks 1..N poll the sum over the
+// lines with device-coherent loads and a short sleep, and record when they saw
+// publish i.  out[2b] = summed detection ticks, out[2b+1] = the largest.
+__global__ __launch_bounds__(64) void k_detect(unsigned* ctr, int lines, int iters, unsigned long long* tpub,
+                                               unsigned long long* out, int* fail) {
+  const int lane = threadIdx.x;
+  if (blockIdx.x == 0) {
+    if (lane != 0) return;
+    for (int i = 1; i <= iters; ++i) {
+      const unsigned long long w = __builtin_amdgcn_s_memrealtime();
+      while (__builtin_amdgcn_s_memrealtime() - w < 2000) __builtin_amdgcn_s_sleep(2);
+      const unsigned long long t = __builtin_amdgcn_s_memrealtime();
+      __hip_atomic_store(&tpub[i], t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_s_waitcnt(0);
+      __hip_atomic_fetch_add(&ctr[(i % lines) * 64], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return;
+  }
+  unsigned long long acc = 0, mx = 0;
+  for (int i = 1; i <= iters; ++i) {
+    const unsigned long long w0 = __builtin_amdgcn_s_memrealtime();
+    bool ok = false;
+    while (__builtin_amdgcn_s_memrealtime() - w0 < kSpinBudgetTicks) {
+      unsigned v = lane < lines ? __hip_atomic_load(&ctr[lane * 64], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m);
+      if (v >= (unsigned)i) { ok = true; break; }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    const unsigned long long t = __builtin_amdgcn_s_memrealtime();
+    if (!ok) { if (lane == 0) atomicAdd(fail, 1); break; }
+    const unsigned long long tp = __hip_atomic_load(&tpub[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned long long d = t > tp ? t - tp : 0;
+    acc += d;
+    mx = d > mx ? d : mx;
+  }
+  if (lane == 0) { out[2 * blockIdx.x] = acc; out[2 * blockIdx.x + 1] = mx; }
+}
+
+// ---- round trip under load, by bytes in flight per streaming block: blocks 0
+// and 1 (one lane each) bounce a counter; blocks 2.. stream 64 KiB tiles with
+// NL 16-byte loads per thread in flight (NL/16 of a tile), until block 0 is
+// done.  out[0] = ticks for the round trips, out[1] = 1 if a wait ran out,
+// out[b] (b >= 2) = bytes block b streamed.
+template <int NL>
+__global__ __launch_bounds__(256) void k_rt_inflight(unsigned* ctr, int iters, const u32x4* src, long n_tiles,
+                                                     unsigned long long* out, unsigned* sink) {
+  const int t = threadIdx.x;
+  if (blockIdx.x < 2) {
+    if (t != 0) return;
+    const bool first = blockIdx.x == 0;
+    unsigned* mine = ctr + (first ? 0 : 64);
+    unsigned* theirs = ctr + (first ? 64 : 0);
+    const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+    bool timed_out = false;
+    for (int i = 1; i <= iters && !timed_out; ++i) {
+      if (first) __hip_atomic_fetch_add(mine, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const unsigned long long w0 = __builtin_amdgcn_s_memrealtime();
+      while (__hip_atomic_load(theirs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (unsigned)i) {
+        if (__builtin_amdgcn_s_memrealtime() - w0 > kSpinBudgetTicks) { timed_out = true; break; }
+      }
+      if (!first) __hip_atomic_fetch_add(mine, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (first) {
+      out[0] = __builtin_amdgcn_s_memrealtime() - t0;
+      out[1] = timed_out ? 1 : 0;
+      __hip_atomic_store(ctr + 128, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return;
+  }
+  uint32_t acc = 0;
+  unsigned long long bytes = 0;
+  const long nb = gridDim.x - 2;
+  long tile = blockIdx.x - 2;
+  const unsigned long long w0 = __builtin_amdgcn_s_memrealtime();
+  while (true) {
+    if (__hip_atomic_load(ctr + 128, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) break;
+    if (__builtin_amdgcn_s_memrealtime() - w0 > kSpinBudgetTicks) break;
+    const u32x4* p = src + tile * 4096;
+#pragma unroll
+    for (int j0 = 0; j0 < 16; j0 += NL) {
+      u32x4 v[NL];
+#pragma unroll
+      for (int j = 0; j < NL; ++j) v[j] = __builtin_nontemporal_load(p + (j0 + j) * 256 + t);
+#pragma unroll
+      for (int j = 0; j < NL; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+      __builtin_amdgcn_s_waitcnt(0);
+    }
+    bytes += 65536;
+    tile += nb;
+    if (tile >= n_tiles) tile = blockIdx.x - 2;
+  }
+  if (t == 0) out[blockIdx.x] = bytes;
+  if (acc == 0x9e3779b9u) sink[blockIdx.x * 256 + t] = acc;
+}
+
+// ---- re-read bandwidth: 64 KiB tiles [tile0, tile0 + n_tiles) read by a
+// grid-stride loop (whether a buffer that fits the memory-side cache is
+// served faster the second time).
+__global__ __launch_bounds__(256) void k_reread(const u32x4* __restrict__ src, long n_tiles, long tile0, unsigned* sink) {
+  const int t = threadIdx.x;
+  unsigned acc = 0;
+  for (long k = blockIdx.x; k < n_tiles; k += gridDim.x) {
+    const u32x4* p = src + (tile0 + k) * 4096;
+    u32x4 v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = p[j * 256 + t];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+  }
+  if (acc == 0x12345678u) sink[blockIdx.x] = acc;
+}
+
 // ---- plain copy of a known number of bytes: the calibration kernel for the
 // FETCH_SIZE / WRITE_SIZE hardware counters (16 bytes per thread per step).
 __global__ __launch_bounds__(256) void k_copy(const u32x4* __restrict__ src, u32x4* __restrict__ dst, long n16) {
@@ -511,6 +625,104 @@ int main(int argc, char** argv) {
     CHECK(hipFree(d_out));
     CHECK(hipFree(ctr));
     CHECK(hipFree(snk));
+    return 0;
+  }
+  if (which == "detect") {
+    const int iters = 200;
+    unsigned* ctr = nullptr;
+    unsigned long long *tpub = nullptr, *d_out = nullptr;
+    int* fail = nullptr;
+    CHECK(hipMalloc(&ctr, 64 * 64 * sizeof(unsigned)));
+    CHECK(hipMalloc(&tpub, (iters + 1) * sizeof(unsigned long long)));
+    CHECK(hipMalloc(&d_out, 2 * 1024 * sizeof(unsigned long long)));
+    CHECK(hipMalloc(&fail, sizeof(int)));
+    for (int lines : {1, 4, 16})
+      for (int pollers : {16, 128, 512}) {
+        CHECK(hipMemset(ctr, 0, 64 * 64 * sizeof(unsigned)));
+        CHECK(hipMemset(tpub, 0, (iters + 1) * sizeof(unsigned long long)));
+        CHECK(hipMemset(d_out, 0, 2 * 1024 * sizeof(unsigned long long)));
+        CHECK(hipMemset(fail, 0, sizeof(int)));
+        hipLaunchKernelGGL(k_detect, dim3(pollers + 1), dim3(64), 0, 0, ctr, lines, iters, tpub, d_out, fail);
+        CHECK(hipDeviceSynchronize());
+        CHECK(hipGetLastError());
+        std::vector<unsigned long long> h(2 * (pollers + 1));
+        int hf = 0;
+        CHECK(hipMemcpy(h.data(), d_out, h.size() * sizeof(unsigned long long), hipMemcpyDeviceToHost));
+        CHECK(hipMemcpy(&hf, fail, sizeof(int), hipMemcpyDeviceToHost));
+        double sum = 0, mx = 0;
+        for (int b = 1; b <= pollers; ++b) {
+          sum += (double)h[2 * b];
+          mx = (double)h[2 * b + 1] > mx ? (double)h[2 * b + 1] : mx;
+        }
+        printf("{\"bench\": \"publish_detect\", \"lines\": %d, \"pollers\": %d, \"mean_us\": %.2f, \"max_us\": %.2f, "
+               "\"timeouts\": %d}\n", lines, pollers, sum / pollers / iters / 100.0, mx / 100.0, hf);
+        fflush(stdout);
+      }
+    CHECK(hipFree(ctr));
+    CHECK(hipFree(tpub));
+    CHECK(hipFree(d_out));
+    CHECK(hipFree(fail));
+    return 0;
+  }
+  if (which == "rtload") {
+    const int iters = 2000;
+    const long rt_tiles = 32768;  // the first 2 GiB of the read buffer
+    unsigned long long* d_out = nullptr;
+    unsigned* ctr = nullptr;
+    CHECK(hipMalloc(&d_out, 4096 * sizeof(unsigned long long)));
+    CHECK(hipMalloc(&ctr, 4096 * sizeof(unsigned)));
+    const u32x4* s4 = reinterpret_cast<const u32x4*>(src);
+    for (int grid : {2, 2 + n_cu, 2 + 2 * n_cu})
+      for (int nl : {4, 8, 16}) {
+        CHECK(hipMemset(ctr, 0, 4096 * sizeof(unsigned)));
+        CHECK(hipMemset(d_out, 0, 4096 * sizeof(unsigned long long)));
+        if (nl == 4) hipLaunchKernelGGL(k_rt_inflight<4>, dim3(grid), dim3(256), 0, 0, ctr, iters, s4, rt_tiles, d_out, sink);
+        if (nl == 8) hipLaunchKernelGGL(k_rt_inflight<8>, dim3(grid), dim3(256), 0, 0, ctr, iters, s4, rt_tiles, d_out, sink);
+        if (nl == 16) hipLaunchKernelGGL(k_rt_inflight<16>, dim3(grid), dim3(256), 0, 0, ctr, iters, s4, rt_tiles, d_out, sink);
+        CHECK(hipDeviceSynchronize());
+        CHECK(hipGetLastError());
+        std::vector<unsigned long long> h(grid);
+        CHECK(hipMemcpy(h.data(), d_out, grid * sizeof(unsigned long long), hipMemcpyDeviceToHost));
+        double tot = 0;
+        for (int b = 2; b < grid; ++b) tot += (double)h[b];
+        const double us = h[0] / 100.0;
+        printf("{\"bench\": \"round_trip_under_load\", \"streamers\": %d, \"inflight_KiB_per_streamer\": %d, "
+               "\"round_trip_ns\": %.0f, \"stream_GBps\": %.0f, \"timed_out\": %llu}\n",
+               grid - 2, nl * 4, us * 1000.0 / iters, us > 0 ? tot / us / 1e3 : 0.0, h[1]);
+        fflush(stdout);
+      }
+    CHECK(hipFree(d_out));
+    CHECK(hipFree(ctr));
+    return 0;
+  }
+  if (which == "reread") {
+    const u32x4* s4 = reinterpret_cast<const u32x4*>(src);
+    const long flush_tiles = 16384, flush0 = n_tiles - flush_tiles;  // the last GiB, other data
+    for (long mib : {16L, 64L, 128L, 192L, 256L, 320L, 512L, 1024L}) {
+      const long nt = mib * 16;  // 64 KiB tiles
+      const long reps = mib <= 256 ? 20 : 4;
+      float best = 1e30f, cold = 0;
+      for (int trial = 0; trial < 3; ++trial) {
+        hipLaunchKernelGGL(k_reread, dim3(2 * n_cu), dim3(256), 0, 0, s4, flush_tiles, flush0, sink);
+        CHECK(hipEventRecord(e0));
+        hipLaunchKernelGGL(k_reread, dim3(2 * n_cu), dim3(256), 0, 0, s4, nt, 0L, sink);
+        CHECK(hipEventRecord(e1));
+        CHECK(hipEventSynchronize(e1));
+        cold = (float)time_ms(e0, e1);
+        CHECK(hipEventRecord(e0));
+        for (long r = 0; r < reps; ++r)
+          hipLaunchKernelGGL(k_reread, dim3(2 * n_cu), dim3(256), 0, 0, s4, nt, 0L, sink);
+        CHECK(hipEventRecord(e1));
+        CHECK(hipEventSynchronize(e1));
+        const float ms = (float)time_ms(e0, e1) / reps;
+        best = ms < best ? ms : best;
+      }
+      CHECK(hipGetLastError());
+      const double b = (double)nt * 65536;
+      printf("{\"bench\": \"reread\", \"MiB\": %ld, \"first_read_GBps\": %.0f, \"reread_GBps\": %.0f}\n", mib,
+             b / cold / 1e6, b / best / 1e6);
+      fflush(stdout);
+    }
     return 0;
   }
   if (which == "resid") {

@@ -190,6 +190,20 @@ __device__ __forceinline__ uint16_t to_bf16(float f) {
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
+// two finite floats rounded to bf16 (to nearest, ties to even) in one word,
+// a in the low half
+__device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+
+// a.lo * b.lo + a.hi * b.hi + c over the bf16 halves of two 32-bit words
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+
 template <typename WT>
 __device__ __forceinline__ void unpack(u32x4 c, float* o);
 template <>
@@ -428,6 +442,28 @@ __device__ __forceinline__ void cmp_gemv(const Slot& s, Smem<WT, KMAX>& sm, int 
       for (int e = 0; e < EPC; ++e) x[e] *= __uint_as_float(s.g[e / 4][e % 4]);
     }
   }
+  if constexpr (sizeof(WT) == 2 && G::LPR == 1) {
+    // bf16 weights, one column chunk per thread: the chunk's activations as
+    // hi + lo bf16 pairs (about 16 significant bits), split once per tile, so
+    // each pair of weights takes two bf16 dot products instead of two unpacks
+    // and two fp32 multiply-adds
+    uint32_t xh[EPC / 2], xl[EPC / 2];
+#pragma unroll
+    for (int i = 0; i < EPC / 2; ++i) {
+      xh[i] = cvt_bf16x2(x[2 * i], x[2 * i + 1]);
+      xl[i] = cvt_bf16x2(x[2 * i] - bf16_lo(xh[i]), x[2 * i + 1] - bf16_hi(xh[i]));
+    }
+#pragma unroll
+    for (int j = 0; j < kChunks; ++j) {
+      float a = acc[j];
+#pragma unroll
+      for (int i = 0; i < EPC / 2; ++i) {
+        a = dot2_bf16(s.c[j][i], xh[i], a);
+        a = dot2_bf16(s.c[j][i], xl[i], a);
+      }
+      acc[j] = a;
+    }
+  } else {
 #pragma unroll
   for (int j = 0; j < kChunks; ++j) {
     if (G::LPR > 1) {  // chunks cycle through LPR columns: read this one from LDS
@@ -442,6 +478,7 @@ __device__ __forceinline__ void cmp_gemv(const Slot& s, Smem<WT, KMAX>& sm, int 
     unpack<WT>(s.c[j], w);
 #pragma unroll
     for (int e = 0; e < EPC; ++e) acc[j / G::LPR] = fmaf(w[e], x[e], acc[j / G::LPR]);
+  }
   }
   const float r = wave_reduce_scatter<G::NV>(acc, lane);
   if (lane < G::NV) sm.red[cw][scatter_index<G::NV>(lane)] = r;

@@ -506,6 +506,28 @@ __global__ __launch_bounds__(256) void k_reread(const u32x4* __restrict__ src, l
   if (acc == 0x12345678u) sink[blockIdx.x] = acc;
 }
 
+// ---- weight-tile layouts: 64 KiB tiles streamed with non-temporal loads,
+// 16 per thread, either as 1 KiB wave-contiguous pieces (FRAG = false) or in
+// the matrix-core A-fragment order (FRAG = true: the tile viewed as 16 pieces
+// of 4 KiB, wave w reading 512 columns of every piece, lane l piece l % 16 at
+// 16-byte column group 4 (w * 16 + j) + l / 16), whose every load touches 64
+// bytes of 16 pieces.
+template <bool FRAG>
+__global__ __launch_bounds__(256) void k_frag(const u32x4* __restrict__ src, long n_tiles, unsigned* sink) {
+  const int t = threadIdx.x, w = t >> 6, l = t & 63;
+  unsigned acc = 0;
+  for (long k = blockIdx.x; k < n_tiles; k += gridDim.x) {
+    const u32x4* p = src + k * 4096;
+    u32x4 v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      v[j] = __builtin_nontemporal_load(FRAG ? p + (l & 15) * 256 + w * 64 + j * 4 + (l >> 4) : p + j * 256 + t);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+  }
+  if (acc == 0x12345678u) sink[blockIdx.x] = acc;
+}
+
 // ---- plain copy of a known number of bytes: the calibration kernel for the
 // FETCH_SIZE / WRITE_SIZE hardware counters (16 bytes per thread per step).
 __global__ __launch_bounds__(256) void k_copy(const u32x4* __restrict__ src, u32x4* __restrict__ dst, long n16) {
@@ -723,6 +745,29 @@ int main(int argc, char** argv) {
              b / cold / 1e6, b / best / 1e6);
       fflush(stdout);
     }
+    return 0;
+  }
+  if (which == "frag") {
+    // 4 GiB of 64 KiB tiles, contiguous pieces against A-fragment order
+    const u32x4* s4 = reinterpret_cast<const u32x4*>(src);
+    for (int frag : {0, 1, 0, 1})
+      for (int per_cu : {1, 2}) {
+        const int grid = n_cu * per_cu;
+        float best = 1e30f;
+        for (int rep = 0; rep < 3; ++rep) {
+          CHECK(hipEventRecord(e0));
+          if (frag) hipLaunchKernelGGL(k_frag<true>, dim3(grid), dim3(256), 0, 0, s4, n_tiles, sink);
+          else hipLaunchKernelGGL(k_frag<false>, dim3(grid), dim3(256), 0, 0, s4, n_tiles, sink);
+          CHECK(hipEventRecord(e1));
+          CHECK(hipEventSynchronize(e1));
+          CHECK(hipGetLastError());
+          const float ms = (float)time_ms(e0, e1);
+          best = ms < best ? ms : best;
+        }
+        printf("{\"bench\": \"tile_layout\", \"fragment_order\": %d, \"blocks_per_cu\": %d, \"ms\": %.3f, "
+               "\"GBps\": %.0f}\n", frag, per_cu, best, bytes / (best * 1e6));
+        fflush(stdout);
+      }
     return 0;
   }
   if (which == "resid") {

@@ -222,42 +222,113 @@ __device__ __forceinline__ float elt(const WT* a, int i) {
   return ((const float*)a)[i];
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m);
-  return v;
+// ---- cross-lane exchanges in registers ----------------------------------------------------
+// (data-parallel-primitive moves within a row of 16 lanes, and the lane-swap
+// moves between rows; a shuffle through the LDS crossbar would cost a round
+// trip to the LDS per step)
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
 }
+// The value of lane l ^ M, for M below 16.
+template <int M>
+__device__ __forceinline__ uint32_t xlane(uint32_t v) {
+  static_assert(M == 1 || M == 2 || M == 4 || M == 8, "within a row of 16 lanes");
+  if constexpr (M == 1) return dpp_u32<0xB1>(v);                   // quad permute 1,0,3,2
+  else if constexpr (M == 2) return dpp_u32<0x4E>(v);              // quad permute 2,3,0,1
+  else if constexpr (M == 4) return dpp_u32<0x141>(dpp_u32<0x1B>(v));  // quad reverse, then half-row mirror
+  else return dpp_u32<0x128>(v);                                   // row rotate by 8
+}
+// The values of lanes l and l ^ M, in an order that depends on the lane (for
+// commutative combinations: the result is the same bits in both lanes).
+template <int M>
+__device__ __forceinline__ void xpair(uint32_t v, uint32_t& a, uint32_t& b) {
+  static_assert(M >= 1 && M <= 32 && (M & (M - 1)) == 0, "lane distance");
+  if constexpr (M < 16) {
+    a = v;
+    b = xlane<M>(v);
+  } else if constexpr (M == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    a = r[0];
+    b = r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    a = r[0];
+    b = r[1];
+  }
+}
+template <int M>
+__device__ __forceinline__ float xsum(float v) {
+  uint32_t a, b;
+  xpair<M>(__float_as_uint(v), a, b);
+  return __uint_as_float(a) + __uint_as_float(b);
+}
+template <int M>
+__device__ __forceinline__ float xmax(float v) {
+  uint32_t a, b;
+  xpair<M>(__float_as_uint(v), a, b);
+  return fmaxf(__uint_as_float(a), __uint_as_float(b));
+}
+template <int M>
+__device__ __forceinline__ unsigned long long xmax_u64(unsigned long long v) {
+  uint32_t al, bl, ah, bh;
+  xpair<M>((uint32_t)v, al, bl);
+  xpair<M>((uint32_t)(v >> 32), ah, bh);
+  const unsigned long long a = (unsigned long long)ah << 32 | al, b = (unsigned long long)bh << 32 | bl;
+  return a > b ? a : b;
+}
+// Sum or maximum over aligned groups of N lanes (N a power of two up to 64).
+template <int N, int M = 1>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (M < N) return group_sum<N, 2 * M>(xsum<M>(v));
+  else return v;
+}
+template <int N, int M = 1>
+__device__ __forceinline__ float group_max(float v) {
+  if constexpr (M < N) return group_max<N, 2 * M>(xmax<M>(v));
+  else return v;
+}
+template <int N, int M = 1>
+__device__ __forceinline__ unsigned long long group_max_u64(unsigned long long v) {
+  if constexpr (M < N) return group_max_u64<N, 2 * M>(xmax_u64<M>(v));
+  else return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
 __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) v += (uint32_t)__shfl_xor((int)v, m);
   return v;
 }
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
-  return v;
-}
+__device__ __forceinline__ float wave_max(float v) { return group_max<64>(v); }
 
-// Reduce-scatter of N per-lane values over the 64 lanes of a wave: after it,
 // lane l holds the wave-wide sum of value index scatter_index<N>(l).
-template <int N>
-__device__ __forceinline__ float wave_reduce_scatter(float (&v)[N], int lane) {
-#pragma unroll
-  for (int s = 0, n = N; n > 1; ++s, n >>= 1) {
-    const int m = 1 << s;
-    const bool up = (lane & m) != 0;
+// One level of the reduce-scatter: lanes exchange half their values with
+// the lane M away, keeping the half their bit M selects.
+template <int N, int M, int n>
+__device__ __forceinline__ void rs_level(float (&v)[N], int lane) {
+  if constexpr (n > 1) {
+    const bool up = (lane & M) != 0;
 #pragma unroll
     for (int i = 0; i < n / 2; ++i) {
       const float lo = v[i], hi = v[i + n / 2];  // selects on values, not on an index
       const float send = up ? lo : hi;
       const float keep = up ? hi : lo;
-      v[i] = keep + __shfl_xor(send, m);
+      v[i] = keep + __uint_as_float(xlane<M>(__float_as_uint(send)));
     }
+    rs_level<N, 2 * M, n / 2>(v, lane);
   }
-  float r = v[0];
-#pragma unroll
-  for (int m = N; m < 64; m <<= 1) r += __shfl_xor(r, m);
-  return r;
+}
+template <int N, int M>
+__device__ __forceinline__ float rs_tail(float r) {
+  if constexpr (M < 64) return rs_tail<N, 2 * M>(xsum<M>(r));
+  else return r;
+}
+template <int N>
+__device__ __forceinline__ float wave_reduce_scatter(float (&v)[N], int lane) {
+  static_assert(N <= 16, "levels exchange within rows of 16 lanes");
+  rs_level<N, 1, N>(v, lane);
+  return rs_tail<N, N>(v[0]);
 }
 template <int N>
 __device__ __forceinline__ int scatter_index(int lane) {
@@ -725,18 +796,14 @@ __device__ __forceinline__ void cmp_combine(const Params& P, const Tile& T, cons
     float o[16];
 #pragma unroll
     for (int c = 0; c < 16; ++c) o[c] = c < nb ? ld_sc1(part + (size_t)(c0 + c) * stride + 2 + lane) : 0.f;
-    float mb = mk;
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1) mb = fmaxf(mb, __shfl_xor(mb, m));
+    const float mb = group_max<16>(mk);
     const float Mn = fmaxf(M, mb);
     const float keep = __expf(M - Mn);
     const float wk = k < nb ? __expf(mk - Mn) : 0.f;
-    float lb = wk * lk;
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1) lb += __shfl_xor(lb, m);
+    const float lb = group_sum<16>(wk * lk);
     float ob = 0.f;
 #pragma unroll
-    for (int c = 0; c < 16; ++c) ob = fmaf(__shfl(wk, c), o[c], ob);
+    for (int c = 0; c < 16; ++c) ob = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), c)), o[c], ob);
     L = fmaf(L, keep, lb);
     O = fmaf(O, keep, ob);
     M = Mn;
@@ -1091,11 +1158,7 @@ __device__ __forceinline__ void ctl_gemv_out(const Params& P, const Tile& T, int
         P.logits[(size_t)b * P.V + row] = y;
         key = pack_max(y, row);
       }
-#pragma unroll
-      for (int m = 1; m < 64; m <<= 1) {
-        const unsigned long long o = __shfl_xor(key, m);
-        key = o > key ? o : key;
-      }
+      key = group_max_u64<64>(key);
       if (lane == 0)
         __hip_atomic_fetch_max(&P.argmax[b * kArgmaxShards + T.id % kArgmaxShards], key, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
@@ -1174,11 +1237,7 @@ __device__ __forceinline__ void ctl_argmax(const Params& P, const Smem<WT, KMAX>
     if (b < P.B)
       best = __hip_atomic_exchange(&P.argmax[(size_t)b0 * kArgmaxShards + lane], 0ull, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-    for (int m = 1; m < kArgmaxShards; m <<= 1) {
-      const unsigned long long o = __shfl_xor(best, m);
-      best = o > best ? o : best;
-    }
+    best = group_max_u64<kArgmaxShards>(best);
     if (b < P.B && lane % kArgmaxShards == 0) {
       const int p = sm.pos[b];
       if (p >= 0 && p < P.cap) {
@@ -1452,8 +1511,7 @@ __device__ __forceinline__ bool ctl_wide_post(const Params& P, const Tile& T0, S
           st_sc1_x2(plane, (uint32_t)(kMaxBatch * P.H) * 2u + at * 2u,
                     u32x2{(uint32_t)l0 | ((uint32_t)l1 << 16), (uint32_t)l2 | ((uint32_t)l3 << 16)});
         }
-#pragma unroll
-        for (int x = 1; x < 16; x <<= 1) sq += __shfl_xor(sq, x);
+        sq = group_sum<16>(sq);
         if (s16 == 0 && n < P.B) st_sc1(ssd + (T.r0 / kWideRows) * kMaxBatch + n, sq);
       }
       break;
@@ -1498,11 +1556,7 @@ __device__ __forceinline__ bool ctl_wide_post(const Params& P, const Tile& T0, S
             }
           }
         }
-#pragma unroll
-        for (int x = 1; x < 16; x <<= 1) {
-          const unsigned long long o = __shfl_xor(key, x);
-          key = o > key ? o : key;
-        }
+        key = group_max_u64<16>(key);
         if (s16 == 0 && n < P.B)
           __hip_atomic_fetch_max(&P.argmax[n * kArgmaxShards + T.id % kArgmaxShards], key, __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT);
@@ -1550,8 +1604,7 @@ __device__ __forceinline__ void ctl_norm(const Params& P, const Tile& T0, const 
     }
     st_sc1_x4(dst, (uint32_t)(b * K + e) * 2u, u32x4{hw[0], hw[1], hw[2], hw[3]});
     st_sc1_x4(dst, (uint32_t)((kMaxBatch + b) * K + e) * 2u, u32x4{lw[0], lw[1], lw[2], lw[3]});
-#pragma unroll
-    for (int x = 1; x < 8; x <<= 1) sq += __shfl_xor(sq, x);
+    sq = group_sum<8>(sq);
     if ((lane & 7) == 0) st_sc1(ss + (8 * g + lane / 8) * kMaxBatch + b, sq);
   }
 }

@@ -295,10 +295,13 @@ __device__ __forceinline__ unsigned long long group_max_u64(unsigned long long v
 }
 
 __device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
-__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) v += (uint32_t)__shfl_xor((int)v, m);
-  return v;
+// Sum over lanes 0 .. 15, wave-uniform (the other lanes' values are ignored).
+__device__ __forceinline__ uint32_t sum16_u32(uint32_t v) {
+  v += xlane<1>(v);
+  v += xlane<2>(v);
+  v += xlane<4>(v);
+  v += xlane<8>(v);
+  return __builtin_amdgcn_readfirstlane(v);
 }
 __device__ __forceinline__ float wave_max(float v) { return group_max<64>(v); }
 
@@ -1100,7 +1103,8 @@ __device__ __forceinline__ void ctl_gemv_out(const Params& P, const Tile& T, int
                                              const EpiIn& e, int lane0) {
   const int lane = opaque(lane0);
   const float y = row_sum<CPR>(sm, lane);
-  const float y2 = __shfl(y, min(lane + T.rs, 63));  // the paired row (RoPE / gate-up)
+  // the paired row (RoPE / gate-up): lane + rs, within a row of lanes for rs = 8
+  const float y2 = T.rs == 8 ? __uint_as_float(xlane<8>(__float_as_uint(y))) : __shfl(y, min(lane + T.rs, 63));
   const int l = T.layer;
   const int p = sm.pos[b];
   switch (T.type) {
@@ -1702,7 +1706,7 @@ __device__ __forceinline__ bool wait_group(const Params& P, const Tile& T, uint3
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
   for (uint32_t n = 0;; ++n) {
     const uint32_t v = lane < G.shards ? ld_sc1(&P.counters[(size_t)(G.shard0 + lane) * kLine]) : 0u;
-    const uint32_t sum = wave_sum_u32(v);
+    const uint32_t sum = sum16_u32(v);  // G.shards <= kMaxShards = 16
     if ((int32_t)(sum - target) >= 0) {
       *delta = (int32_t)(sum - target);
       return true;

@@ -324,7 +324,7 @@ Dag finish_dag(const Shape& s, Emitter& e) {
     if (t.signal >= 0) d.groups[t.signal].producers++;
   int32_t slot = 0;
   for (Group& g : d.groups) {
-    int32_t want = (g.producers + 31) / 32, sh = 1;
+    int32_t want = (g.producers + 1) / 2, sh = 1;
     while (sh < want && sh < kMaxShards) sh *= 2;
     g.shards = sh;
     g.shard0 = slot;

@@ -295,13 +295,17 @@ __device__ __forceinline__ unsigned long long group_max_u64(unsigned long long v
 }
 
 __device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
-// Sum over lanes 0 .. 15, wave-uniform (the other lanes' values are ignored).
-__device__ __forceinline__ uint32_t sum16_u32(uint32_t v) {
+// Sum over the wave, wave-uniform.
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
   v += xlane<1>(v);
   v += xlane<2>(v);
   v += xlane<4>(v);
   v += xlane<8>(v);
-  return __builtin_amdgcn_readfirstlane(v);
+  uint32_t a, b;
+  xpair<16>(v, a, b);
+  v = a + b;
+  xpair<32>(v, a, b);
+  return __builtin_amdgcn_readfirstlane(a + b);
 }
 __device__ __forceinline__ float wave_max(float v) { return group_max<64>(v); }
 
@@ -1706,7 +1710,7 @@ __device__ __forceinline__ bool wait_group(const Params& P, const Tile& T, uint3
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
   for (uint32_t n = 0;; ++n) {
     const uint32_t v = lane < G.shards ? ld_sc1(&P.counters[(size_t)(G.shard0 + lane) * kLine]) : 0u;
-    const uint32_t sum = sum16_u32(v);  // G.shards <= kMaxShards = 16
+    const uint32_t sum = wave_sum_u32(v);  // G.shards <= kMaxShards = 64
     if ((int32_t)(sum - target) >= 0) {
       *delta = (int32_t)(sum - target);
       return true;

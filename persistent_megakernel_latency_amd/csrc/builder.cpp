@@ -319,7 +319,8 @@ namespace {
 
 Dag finish_dag(const Shape& s, Emitter& e) {
   Dag& d = e.d;
-  // producers and shards
+  // producers and shards: two producers per shard, up to kMaxShards (a
+  // phase's increments of one counter line serialise)
   for (const Tile& t : d.tiles)
     if (t.signal >= 0) d.groups[t.signal].producers++;
   int32_t slot = 0;

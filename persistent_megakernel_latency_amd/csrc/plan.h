@@ -67,7 +67,7 @@ constexpr int kAttnChunk = 64;                        // KV positions per attent
 constexpr int kHeadDim = 64;                          // the only head size built
 constexpr int kMaxGroupHeads = 4;                     // q heads per kv head
 constexpr int kArgmaxShards = 16;
-constexpr int kMaxShards = 64;  // one per lane of a polling wave
+constexpr int kMaxShards = 128;  // two per lane of a polling wave
 constexpr int kMaxBatch = 32;
 constexpr int kMaxBatchGemv = 4;   // above it a plan is wide: matrix-core tiles over all sequences
 // Wide (matrix-core) tiles: 64 weight rows x a 512-column slice of K (64 KiB

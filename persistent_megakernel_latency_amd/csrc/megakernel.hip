@@ -91,6 +91,7 @@ struct alignas(16) Smem {
   int ids[2];          // claim index of the next tile, by iteration parity
   alignas(16) int tnext[2][16];  // the next tile's descriptor, by iteration parity (compute wave 1 fetches it)
   uint64_t t_ready, t_done;  // logged steps: compute wave 1 saw its slot, finished its arithmetic
+  float xinv;  // 1 / RMS of the staged activation row (1 without a norm), applied with the gains
   int first;
   int stop;
 };
@@ -520,8 +521,9 @@ __device__ __forceinline__ void cmp_gemv(const Slot& s, Smem<WT, KMAX>& sm, int 
       x[e] = v.x; x[e + 1] = v.y; x[e + 2] = v.z; x[e + 3] = v.w;
     }
     if (GAIN) {
+      const float xi = sm.xinv;
 #pragma unroll
-      for (int e = 0; e < EPC; ++e) x[e] *= __uint_as_float(s.g[e / 4][e % 4]);
+      for (int e = 0; e < EPC; ++e) x[e] *= __uint_as_float(s.g[e / 4][e % 4]) * xi;
     }
   }
   if constexpr (sizeof(WT) == 2 && G::LPR == 1) {
@@ -1000,7 +1002,10 @@ __device__ __forceinline__ void ctl_input(const Params& P, const float* src, con
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)&sm.xs[256 * i], 16,
                                                (uint32_t)lane * 16u, 1024 * i, 0, 16 /* sc1 */);
     __builtin_amdgcn_s_waitcnt(0);
-    if (!gain) return;
+    if (!gain) {
+      sm.xinv = 1.f;
+      return;
+    }
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < NQ; ++i) {
@@ -1008,14 +1013,8 @@ __device__ __forceinline__ void ctl_input(const Params& P, const float* src, con
       ss = fmaf(v.x, v.x, ss); ss = fmaf(v.y, v.y, ss); ss = fmaf(v.z, v.z, ss); ss = fmaf(v.w, v.w, ss);
     }
     ss = wave_sum(ss);
-    const float inv = 1.0f / sqrtf(ss / (float)K + P.eps);
-    asm volatile("" ::: "memory");  // re-read the row rather than hold K/64 values in registers
-#pragma unroll
-    for (int i = 0; i < NQ; ++i) {
-      f32x4 v = *(const f32x4*)&sm.xs[256 * i + 4 * lane];
-      v.x *= inv; v.y *= inv; v.z *= inv; v.w *= inv;
-      *(f32x4*)&sm.xs[256 * i + 4 * lane] = v;
-    }
+    // the compute waves scale the row by 1 / RMS together with the gains
+    sm.xinv = 1.0f / sqrtf(ss / (float)K + P.eps);
     return;
   }
   if constexpr (!EMBED) return;
@@ -1044,6 +1043,7 @@ __device__ __forceinline__ void ctl_input(const Params& P, const float* src, con
       o.w = v[g * EPC + c + 3] * inv;
       *(f32x4*)&sm.xs[(lane + 64 * g) * EPC + c] = o;
     }
+  sm.xinv = 1.f;
 }
 
 // Values the epilogue needs, loaded together with the inputs.

@@ -137,9 +137,13 @@ inline void xput(uint16_t* x, int K, int b, int i, float v) {
   x[(int64_t)kMaxBatch * K + at] = to_bf16(v - bf16v(hi));
 }
 
+// Greedy choice key, as on the device: float order, then the lowest index;
+// -0 counts as +0 and a NaN is never chosen.
 inline uint64_t pack_max(float v, int32_t idx) {
   uint32_t u;
   std::memcpy(&u, &v, 4);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0;
+  if (u == 0x80000000u) u = 0u;
   u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
   return ((uint64_t)u << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)idx);
 }

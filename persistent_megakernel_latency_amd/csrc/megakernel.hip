@@ -366,10 +366,36 @@ __device__ __forceinline__ bool is_gemv(int type) {
   return type == T_QKV || type == T_OPROJ || type == T_GATEUP || type == T_DOWN || type == T_LM;
 }
 
+// Greedy choice key: the float's bits mapped so that unsigned order is float
+// order, then the inverted index, so a 64-bit maximum picks the largest value
+// and, among equal values, the lowest index.  -0 is taken as +0 (they compare
+// equal, so the lower index wins between them) and a NaN gives the key 0,
+// below every number: it is never chosen, as a float comparison never
+// prefers it.
 __device__ __forceinline__ unsigned long long pack_max(float v, int idx) {
   uint32_t u = __float_as_uint(v);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0ull;
+  if (u == 0x80000000u) u = 0u;
   u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
   return ((unsigned long long)u << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)idx);
+}
+
+// Compiler-only ordering points of the hand-off protocol (no instruction is
+// emitted).  The publish is a relaxed device-scope increment issued after the
+// wave's device-coherent stores have completed (s_waitcnt); the consumer reads
+// inputs with device-coherent loads after its poll saw the group complete.
+// Nothing in the relaxed atomics themselves stops the compiler from moving a
+// store below the completion wait or an input load above the successful poll,
+// so both sides are pinned here.
+__device__ __forceinline__ void compiler_order() { asm volatile("" ::: "memory"); }
+
+// Wait until every memory operation this wave issued has completed (stores
+// performed, loads and LDS-direct loads landed), with no memory access of the
+// surrounding code moved across the wait.
+__device__ __forceinline__ void wait_all_memory() {
+  compiler_order();
+  __builtin_amdgcn_s_waitcnt(0);
+  compiler_order();
 }
 
 // ---- GEMV geometry ------------------------------------------------------------------------
@@ -831,7 +857,7 @@ __device__ __forceinline__ void cmp_combine(const Params& P, const Tile& T, cons
   } else {
     st_sc1(dst + lane, o);
   }
-  __builtin_amdgcn_s_waitcnt(0);
+  wait_all_memory();
 }
 
 // ---- wide (matrix-core) tiles ---------------------------------------------------------------
@@ -1001,7 +1027,7 @@ __device__ __forceinline__ void ctl_input(const Params& P, const float* src, con
     for (int i = 0; i < NQ; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)&sm.xs[256 * i], 16,
                                                (uint32_t)lane * 16u, 1024 * i, 0, 16 /* sc1 */);
-    __builtin_amdgcn_s_waitcnt(0);
+    wait_all_memory();
     if (!gain) {
       sm.xinv = 1.f;
       return;
@@ -1285,7 +1311,7 @@ __device__ __forceinline__ void ctl_stage_x(const Params& P, const Tile& T0, Sme
             r, (__attribute__((address_space(3))) void*)(sm.xs + wfrag(ks, h, pl) * 256), 16, voff, soff, 0,
             16 /* sc1 */);
       }
-  __builtin_amdgcn_s_waitcnt(0);
+  wait_all_memory();
 }
 
 __device__ __forceinline__ void st_hilo(uint16_t* plane0, size_t plane_elems, size_t at, float v) {
@@ -1309,11 +1335,12 @@ __device__ __forceinline__ bool ctl_wide_post(const Params& P, const Tile& T0, S
   float* mine = P.wpart + (size_t)(T.pslot + T.c) * kWidePart;
   for (int i = 0; i < per; ++i)
     st_sc1_x4(mine, (uint32_t)(i * 64 + lane) * 16u, *(const u32x4*)(cp + (i * 64 + lane) * 4));
-  __builtin_amdgcn_s_waitcnt(0);
+  wait_all_memory();
   uint32_t old = 0;
   if (lane == 0) old = atomic_add(&P.fixc[(size_t)T.fix * kLine], 1u);
   old = __builtin_amdgcn_readfirstlane(__shfl(old, 0));
   if ((int)old + 1 != T.b) return false;
+  compiler_order();  // the other slices' partial sums are read only after their arrivals are counted
   // the last slice: no other slice of this row block touches the counter
   // again this step; it counts from zero in the next
   if (lane == 0) st_sc1(&P.fixc[(size_t)T.fix * kLine], 0u);
@@ -1411,7 +1438,7 @@ __device__ __forceinline__ bool ctl_wide_post(const Params& P, const Tile& T0, S
             r, (__attribute__((address_space(3))) void*)(sm.xs + (slot * per + i) * 256), 16,
             (uint32_t)lane * 16u, i * 1024, 0, 16 /* sc1 */);
     }
-    __builtin_amdgcn_s_waitcnt(0);
+    wait_all_memory();
     for (int sl = s0; sl < s1; ++sl) {
       const int slot = sl - s0 - (sl > T.c ? own : 0);
       const float* src = sl == T.c ? cp : sm.xs + slot * per * 256;
@@ -1718,6 +1745,7 @@ __device__ __forceinline__ bool wait_group(const Params& P, const Tile& T, uint3
     const uint32_t sum = wave_sum_u32(v0 + v1);  // G.shards <= kMaxShards = 128
     if ((int32_t)(sum - target) >= 0) {
       *delta = (int32_t)(sum - target);
+      compiler_order();  // the tile's input loads stay after the poll that saw them complete
       return true;
     }
     // Narrow plans read the abort flag every 16th poll: a round trip per poll
@@ -1779,7 +1807,7 @@ __device__ __forceinline__ Tile get_tile(const int* src) {
 // argmax updates have completed, then one increment by the run's length (the
 // group counts its total over all shards, so any shard serves).
 __device__ __forceinline__ void flush_lm(const Params& P, int group, int& count, int lane) {
-  __builtin_amdgcn_s_waitcnt(0);
+  wait_all_memory();
   if (lane == 0) {
     const Group G = cload(P.groups, group);
     atomic_add(&P.counters[(size_t)(G.shard0 + (int)blockIdx.x % G.shards) * kLine], (uint32_t)count);
@@ -1860,7 +1888,7 @@ __device__ __forceinline__ void control_loop(const Params& P, Smem<WT, KMAX>& sm
       lm_group = T.signal;
       lm_count += id != P.drop_tile;
     } else {
-      __builtin_amdgcn_s_waitcnt(0);
+      wait_all_memory();
     }
     if (lane == 0) {
       if (LOG) {
@@ -1975,7 +2003,7 @@ __device__ __forceinline__ void compute_loop(const Params& P, Smem<WT, KMAX>& sm
         break;
       }
       if (LOG) {  // timing only: the slot's loads are complete here (latest compute wave)
-        __builtin_amdgcn_s_waitcnt(0);
+        wait_all_memory();
         if ((tc & 63) == 0)
           __hip_atomic_fetch_max(&sm.t_ready, (uint64_t)__builtin_amdgcn_s_memrealtime(), __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_WORKGROUP);

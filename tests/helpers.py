@@ -70,23 +70,34 @@ def dag_edges(wait: List[int], signal: List[int]):
     return prod
 
 
+LOG_DTYPE = np.dtype([("exec_count", "<i4"), ("wait_delta", "<i4"), ("worker", "<i4"), ("claim", "<i4"),
+                      ("t_start", "<i8"), ("t_end", "<i8")])
+
+
+def log_array(log) -> np.ndarray:
+    """The wpk_log_rec records as a numpy structured array (no copy)."""
+    return np.frombuffer(log, dtype=LOG_DTYPE)
+
+
 def check_log(log, wait, signal, canonical_only: bool = False) -> None:
     """Canonical log: every tile ran once with its counter exactly complete;
     and the raw order is a linear extension of the DAG (every producer ended
     before its consumer started)."""
+    a = log_array(log)
+    wait = np.asarray(wait, np.int64)
+    signal = np.asarray(signal, np.int64)
     n = len(wait)
-    ex = np.array([log[i].exec_count for i in range(n)])
-    de = np.array([log[i].wait_delta for i in range(n)])
+    a = a[:n]
+    ex, de = a["exec_count"], a["wait_delta"]
     assert np.all(ex == 1), f"tiles not run exactly once: {np.nonzero(ex != 1)[0][:10]}"
     assert np.all(de == 0), f"counters not exactly complete at start: {np.nonzero(de != 0)[0][:10]}"
     if canonical_only:
         return
-    start = np.array([log[i].t_start for i in range(n)], dtype=np.int64)
-    end = np.array([log[i].t_end for i in range(n)], dtype=np.int64)
-    prod = dag_edges(wait, signal)
-    for v in range(n):
-        g = wait[v]
-        if g < 0:
-            continue
-        pe = end[prod[g]]
-        assert pe.max() <= start[v], f"tile {v} started before producer ended"
+    start, end = a["t_start"], a["t_end"]
+    n_groups = int(max(wait.max(), signal.max())) + 1
+    last_end = np.full(n_groups, np.iinfo(np.int64).min, np.int64)
+    prod = signal >= 0
+    np.maximum.at(last_end, signal[prod], end[prod])
+    cons = np.nonzero(wait >= 0)[0]
+    bad = cons[last_end[wait[cons]] > start[cons]]
+    assert bad.size == 0, f"tiles started before a producer ended: {bad[:10]}"

@@ -89,10 +89,12 @@ def test_mini_wide_graph_baseline_equals_megakernel_bitwise():
     b.close()
 
 
-def test_llama_1b_batch32_sampled_sequences():
-    """Llama-1B shape at batch 32, contexts U{256..1024}: every sequence runs
-    on the GPU, four of them (including the shortest and the longest) are
-    checked against the oracle, teacher-forced, for two steps."""
+@pytest.mark.timeout(900)
+def test_llama_1b_batch32_all_sequences():
+    """Llama-1B shape at batch 32, contexts U{256..1024}: all 32 sequences
+    against the oracle, teacher-forced, for three steps, with the per-tile log
+    checked at every step (every tile once, counter exactly complete, device
+    order a linear extension of the DAG)."""
     cfg = synth.LLAMA_1B
     announce("generating Llama-1B-shaped weights")
     w = synth.make_weights(cfg, gain_std=0.1)
@@ -101,26 +103,29 @@ def test_llama_1b_batch32_sampled_sequences():
     lens = synth.context_lengths(batch)
     kc, vc = synth.synthetic_kv(cfg, batch, cap, lens)
     tok = synth.prompt_tokens(cfg, batch, 1)[:, 0].astype(np.int32)
-    sub = sorted({0, int(np.argmin(lens)), int(np.argmax(lens)), batch - 1})
-    okc, ovc, osl = kc[:, sub].copy(), vc[:, sub].copy(), lens[sub].copy()
     announce("llama-1b b32 build")
     g = GpuPlan(cfg, w, batch, cap, kc, vc, lens, tok)
-    del kc, vc
-    worst = 0.0
-    for s in range(2):
+    wpk.check(wpk.wpk_set_option(g.plan, wpk.WPK_OPT_LOG, 1), g.plan)
+    ty, layer, wait, signal = g.dag()
+    osl = lens.copy()
+    worst, ties = 0.0, []
+    for s in range(3):
         announce(f"llama-1b b32 step {s}")
+        g.set_tokens(tok)
         g.step()
         _, _, gsl, gtok, glog = g.state()
-        olog, otok = model.step(tok[sub], okc, ovc, osl)
-        for i, b in enumerate(sub):
-            err = float(np.max(np.abs(glog[b] - olog[i])))
+        check_log(g.log(), wait, signal)
+        announce(f"llama-1b b32 oracle step {s}")
+        olog, otok = model.step(tok, kc, vc, osl)
+        for b in range(batch):
+            err = float(np.max(np.abs(glog[b] - olog[b])))
             worst = max(worst, err)
             assert err <= 2e-2, f"step {s} seq {b}: max |logit err| {err}"
-            ok, why = tokens_agree(int(gtok[b]), int(otok[i]), olog[i], err)
+            ok, why = tokens_agree(int(gtok[b]), int(otok[b]), olog[b], err)
             assert ok, f"step {s} seq {b}: {why}"
-            assert gsl[b] == osl[i]
-        tok = gtok.copy()
-        tok[sub] = otok
-        g.set_tokens(tok)
-    print(f"llama-1b b32 max logit error {worst}")
+            if why:
+                ties.append((s, b, why))
+        assert np.array_equal(gsl, osl)
+        tok = otok
+    print(f"llama-1b b32 max logit error {worst:.3g}, near ties {ties}")
     g.close()

@@ -94,7 +94,7 @@ def test_serial_executor_matches_oracle_and_is_order_independent():
         ok_, ov_, osl = kc.copy(), vc.copy(), sl.copy()
         olog, otok = model.step(tok, ok_, ov_, osl)
         results = []
-        for seed in range(12 if step == 0 else 3):
+        for seed in range(100):
             st = HostState(kc, vc, sl, tok, cfg.vocab)
             assert st.serial(plan, seed, poison=(seed % 2 == 1)) == 0, wpk.wpk_last_error(plan)
             rc, log = wpk.wpk_get_log(plan, n)

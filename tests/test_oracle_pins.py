@@ -40,6 +40,36 @@ def test_round_bf16_matches_torch_on_float32_values():
     assert np.array_equal(got, want)
 
 
+def test_round_bf16_on_float64_values_off_the_float32_grid():
+    """Rounding straight from float64 to bf16, with expected bits from the
+    definition (8 significant bits, nearest, ties to even).  Inputs sit
+    between float32 values, so rounding through float32 first (a double
+    rounding) fails: 1 + 2^-8 + 2^-30 is above the halfway point between the
+    bf16 neighbours 1 and 1 + 2^-7, but its float32 rounding is the exact tie
+    1 + 2^-8, which goes to even (1.0)."""
+    e = 2.0 ** -8  # half a bf16 ulp at 1
+    cases = [
+        (1.0 + e, 0x3F80),                    # exact tie: to even (1.0)
+        (1.0 + 3 * e, 0x3F82),                # exact tie: to even (1 + 2^-6)
+        (1.0 + e + 2.0 ** -40, 0x3F81),       # just above the tie: up
+        (1.0 + e + 2.0 ** -30, 0x3F81),       # above the tie, float32 rounds it onto the tie
+        (1.0 + e - 2.0 ** -40, 0x3F80),       # just below the tie: down
+        (1.0 + 3 * e - 2.0 ** -40, 0x3F81),   # below an odd-side tie: down to odd
+        (-(1.0 + e + 2.0 ** -40), 0xBF81),    # the sign is kept
+        (3.0 + 2.0 ** -7 + 2.0 ** -45, 0x4041),  # [2, 4): ulp 2^-6, above the tie at 3 + 2^-7
+        (2.0 ** -130 * (1 + 2.0 ** -30), 0x0001 << 3),  # subnormal: 2^-130 = 8 quanta of 2^-133
+        (2.0 ** -134 + 2.0 ** -160, 0x0001),  # half a subnormal quantum and a bit: up
+        (2.0 ** -134, 0x0000),                # exactly half the smallest subnormal: to even (zero)
+        (2.0 ** 128 - 2.0 ** 120 + 2.0 ** 100, 0x7F7F),  # the largest bf16 plus a little: down to it
+        (2.0 ** 128 - 2.0 ** 119 + 2.0 ** 100, 0x7F80),  # past the largest bf16 + half an ulp: inf
+    ]
+    for x, bits in cases:
+        assert oracle.round_bf16(x) == bits, (x, hex(oracle.round_bf16(x)), hex(bits))
+    # the double-rounding case really differs from rounding through float32
+    x = 1.0 + e + 2.0 ** -30
+    assert _torch_bf16_bits(np.array([x], np.float32))[0] == 0x3F80
+
+
 def test_bf16_value_round_trip():
     bits = np.arange(0, 65536, 7, dtype=np.uint16)
     for b in bits:
@@ -222,6 +252,10 @@ def test_argmax_brute_force_and_ties():
     assert np.float32(y[3]) == np.float32(y[7])
     assert oracle.argmax_f32(y) == 3
     assert oracle.argmax_f32(np.array([-5.0, -1.0, -1.0, -7.0])) == 1
+    # -0 and +0 compare equal (the lower index wins); a NaN is never chosen
+    assert oracle.argmax_f32(np.array([-1.0, -0.0, 0.0])) == 1
+    assert oracle.argmax_f32(np.array([-1.0, 0.0, -0.0])) == 1
+    assert oracle.argmax_f32(np.array([np.nan, -3.0, np.nan, -2.0])) == 3
 
 
 # ---- whole decode step -------------------------------------------------------------------------

@@ -215,6 +215,23 @@ int32_t wpk_get_dag(const wpk_plan* plan, int32_t* type, int32_t* layer, int32_t
  * the first wpk_step and re-captured if tokens/kv/logits pointers change. */
 wpk_plan* wpk_build_graph_baseline(const wpk_model_desc* desc, int32_t batch, int32_t ctx_len);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * plan as wpk_build, with its whole workspace placed in a static device array
+ * of WPK_STATIC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends; no hipMalloc, hipFree or other allocating call is
+ * made for device memory (host bookkeeping uses the C++ heap).  The caller
+ * still passes tokens, the KV cache and logits to wpk_step.  A plan whose
+ * workspace does not fit is refused (NULL; wpk_last_error(NULL) gives the
+ * bytes it needs).  All static plans of one GPU share its array: building one
+ * clears the part it uses and takes the array over, after which an earlier
+ * static plan of that GPU refuses to step (WPK_E_STATE) until rebuilt.  Steps
+ * of two static plans that overlap in time on one GPU race on the array.  The
+ * batch-1 Llama-3.2-1B-shaped plan needs about 12 MiB; matrix-core plans
+ * (batches above 4) of that model do not fit. */
+#define WPK_STATIC_SCRATCH_BYTES (32u << 20)
+wpk_plan* wpk_build_static(const wpk_model_desc* desc, int32_t batch, int32_t ctx_len);
+
 /* ---- host-side executors (no GPU) ----------------------------------------------
  * wpk_build_host compiles the same DAG for a model in HOST memory.
  * wpk_serial_step runs one step's tiles on the CPU, one at a time, in a

@@ -31,6 +31,8 @@ WPK_E_NO_GPU = -9
 WPK_F32 = 0
 WPK_BF16 = 1
 
+WPK_STATIC_SCRATCH_BYTES = 32 << 20
+
 WPK_OPT_LOG = 1
 WPK_OPT_WATCHDOG_US = 2
 WPK_OPT_PERTURB_SEED = 3
@@ -91,6 +93,7 @@ _SIGNATURES = {
     "wpk_get_info": (_i32, [_vp, ctypes.POINTER(wpk_plan_info)]),
     "wpk_get_dag": (_i32, [_vp, _vp, _vp, _vp, _vp]),
     "wpk_build_graph_baseline": (_vp, [ctypes.POINTER(wpk_model_desc), _i32, _i32]),
+    "wpk_build_static": (_vp, [ctypes.POINTER(wpk_model_desc), _i32, _i32]),
     "wpk_build_host": (_vp, [ctypes.POINTER(wpk_model_desc), _i32, _i32, ctypes.POINTER(wpk_build_opts)]),
     "wpk_serial_step": (_i32, [_vp, _vp, ctypes.POINTER(wpk_kv), _vp, ctypes.c_uint64, _i32]),
     "wpk_emulate_step": (_i32, [_vp, _vp, ctypes.POINTER(wpk_kv), _vp, _i32, ctypes.c_uint64]),
@@ -176,6 +179,10 @@ def wpk_get_dag(plan, n_tiles: int):
 
 def wpk_build_graph_baseline(desc: wpk_model_desc, batch: int, ctx_len: int):
     return lib().wpk_build_graph_baseline(ctypes.byref(desc), batch, ctx_len)
+
+
+def wpk_build_static(desc: wpk_model_desc, batch: int, ctx_len: int):
+    return lib().wpk_build_static(ctypes.byref(desc), batch, ctx_len)
 
 
 def wpk_build_host(desc: wpk_model_desc, batch: int, ctx_len: int, opts: Optional[wpk_build_opts] = None):

@@ -11,6 +11,8 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -20,12 +22,18 @@
 extern "C" int wpk_dev_kernels(int dtype, int cpr_h, int cpr_f, int wide, const void** mk, const void** mk_log,
                                const void** phase, int* dyn_lds);
 extern "C" int wpk_dev_block_threads();
+extern "C" int wpk_dev_static_scratch(int device, void** ptr, size_t* bytes);
 
 using namespace wpk;
 
 namespace {
 
 thread_local std::string g_err;
+
+// The static plan that currently owns each device's scratch array (plans
+// built by wpk_build_static share one array per device; the latest owns it).
+std::mutex g_owner_mu;
+std::map<int, const wpk_plan*> g_scratch_owner;
 
 wpk_plan* fail(const std::string& m) {
   g_err = m;
@@ -108,7 +116,7 @@ bool desc_ok(const wpk_model_desc* d, std::string* why) {
 }
 
 wpk_plan* build_device(const wpk_model_desc* desc, int32_t batch, int32_t ctx_len, const wpk_build_opts* opts,
-                       bool baseline) {
+                       bool baseline, bool static_ws = false) {
   std::string why;
   if (!desc_ok(desc, &why)) return fail(why);
   wpk_build_opts o{};
@@ -170,9 +178,26 @@ wpk_plan* build_device(const wpk_model_desc* desc, int32_t batch, int32_t ctx_le
   }
 
   const Layout L = layout(s, p->dag, p->max_workers);
-  e = hipMalloc((void**)&p->d_ws, L.total);
-  if (e != hipSuccess) return fail(hip_msg("hipMalloc workspace", e));
+  if (static_ws) {
+    // no allocation: the workspace is this device's scratch array
+    void* sp = nullptr;
+    size_t cap_bytes = 0;
+    const int rc = wpk_dev_static_scratch(dev, &sp, &cap_bytes);
+    if (rc != WPK_OK) return fail("static scratch: address lookup failed on device " + std::to_string(dev));
+    if ((size_t)L.total > cap_bytes)
+      return fail("static scratch: this plan needs a " + std::to_string(L.total) + "-byte workspace, above the " +
+                  std::to_string(cap_bytes) + "-byte static array (use wpk_build)");
+    p->d_ws = (char*)sp;
+    p->static_ws = true;
+  } else {
+    e = hipMalloc((void**)&p->d_ws, L.total);
+    if (e != hipSuccess) return fail(hip_msg("hipMalloc workspace", e));
+  }
   p->ws_bytes = L.total;
+  auto release_ws = [&]() {
+    if (!p->static_ws) (void)hipFree(p->d_ws);
+    p->d_ws = nullptr;
+  };
   char* w = p->d_ws;
   auto up = [&](int64_t off, const void* src, size_t bytes) { return hipMemcpy(w + off, src, bytes, hipMemcpyHostToDevice); };
   e = hipMemset(w, 0, L.total);
@@ -191,7 +216,7 @@ wpk_plan* build_device(const wpk_model_desc* desc, int32_t batch, int32_t ctx_le
   if (e == hipSuccess) e = up(L.rope_cos, rc.data(), rc.size() * 4);
   if (e == hipSuccess) e = up(L.rope_sin, rsn.data(), rsn.size() * 4);
   if (e != hipSuccess) {
-    (void)hipFree(p->d_ws);
+    release_ws();
     return fail(hip_msg("workspace upload", e));
   }
   Params& P = p->P;
@@ -252,10 +277,14 @@ wpk_plan* build_device(const wpk_model_desc* desc, int32_t batch, int32_t ctx_le
     hipStream_t cs;
     e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
     if (e != hipSuccess) {
-      (void)hipFree(p->d_ws);
+      release_ws();
       return fail(hip_msg("hipStreamCreate", e));
     }
     p->cap_stream = cs;
+  }
+  if (static_ws) {
+    std::lock_guard<std::mutex> lk(g_owner_mu);
+    g_scratch_owner[dev] = p.get();
   }
   return p.release();
 }
@@ -315,12 +344,22 @@ wpk_plan* wpk_build_graph_baseline(const wpk_model_desc* desc, int32_t batch, in
   return build_device(desc, batch, ctx_len, nullptr, true);
 }
 
+wpk_plan* wpk_build_static(const wpk_model_desc* desc, int32_t batch, int32_t ctx_len) {
+  return build_device(desc, batch, ctx_len, nullptr, false, true);
+}
+
 int32_t wpk_step(wpk_plan* p, int32_t* tokens, wpk_kv* kv, void* logits, wpk_stream_t stream) {
   if (!p) return plan_fail(nullptr, WPK_E_ARG, "null plan");
   if (p->host) return plan_fail(p, WPK_E_ARG, "host plan: use wpk_serial_step / wpk_emulate_step");
   if (p->latched) return plan_fail(p, WPK_E_STATE, "plan holds device error " + std::to_string(p->latched) + "; reset it");
   if (!tokens || !kv || !kv->k || !kv->v || !kv->seq_len || !logits)
     return plan_fail(p, WPK_E_ARG, "null tokens, kv or logits");
+  if (p->static_ws) {
+    std::lock_guard<std::mutex> lk(g_owner_mu);
+    if (g_scratch_owner[p->device] != p)
+      return plan_fail(p, WPK_E_STATE, "the static scratch of device " + std::to_string(p->device) +
+                                           " now holds a later static plan's workspace; rebuild this plan");
+  }
   hipStream_t st = (hipStream_t)stream;
   Params& P = p->P;
   P.tokens = tokens;
@@ -405,7 +444,12 @@ void wpk_destroy(wpk_plan* p) {
   if (p->cap_stream) (void)hipStreamDestroy((hipStream_t)p->cap_stream);
   if (p->d_ws) {
     (void)hipDeviceSynchronize();
-    (void)hipFree(p->d_ws);
+    if (p->static_ws) {
+      std::lock_guard<std::mutex> lk(g_owner_mu);
+      if (g_scratch_owner[p->device] == p) g_scratch_owner.erase(p->device);
+    } else {
+      (void)hipFree(p->d_ws);
+    }
   }
   delete p;
 }

@@ -46,6 +46,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 
 #include "plan.h"
 #include "wpk.h"
@@ -2204,3 +2205,34 @@ extern "C" int wpk_dev_kernels(int dtype, int cpr_h, int cpr_f, int wide, const 
 
 // Threads per worker the kernels are built for (one control wave + compute waves).
 extern "C" int wpk_dev_block_threads() { return wpk::kBlock; }
+
+// ---- workspace for plans built without allocation ---------------------------------------
+//
+// A plan built by wpk_build_static keeps its whole workspace (counters, queues,
+// tile tables, activations, partial sums, log) in this array instead of a
+// hipMalloc allocation.  Every GPU the library runs on holds its own copy from
+// module load until the process ends.  In host code `scratch` only names the
+// host-side shadow of the symbol: its device address on the current device
+// comes from hipGetSymbolAddress, looked up once per device below.
+namespace {
+constexpr size_t kScratchBytes = size_t(32) << 20;
+constexpr int kScratchDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices];
+}  // namespace
+
+// Device address and size of this device's scratch array.  The caller makes
+// `device` current first.  Returns 0, or a negative code from wpk.h.
+extern "C" int wpk_dev_static_scratch(int device, void** ptr, size_t* bytes) {
+  if (device < 0 || device >= kScratchDevices || !ptr || !bytes) return WPK_E_ARG;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[device]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return WPK_E_HIP;
+    g_scratch_ptr[device] = p;
+  }
+  *ptr = g_scratch_ptr[device];
+  *bytes = kScratchBytes;
+  return WPK_OK;
+}

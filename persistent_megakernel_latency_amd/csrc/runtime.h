@@ -63,6 +63,7 @@ struct wpk_plan {
   int n_cu = 0;
   int workers = 0, max_workers = 0;
   char* d_ws = nullptr;             // one allocation holding everything the plan owns
+  bool static_ws = false;           // d_ws is the device's static scratch array (wpk_build_static)
   int64_t ws_bytes = 0;
   wpk::Params P{};                  // device pointers; step I/O filled per call
   const void* k_mega = nullptr;     // kernel handles

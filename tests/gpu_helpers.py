@@ -30,7 +30,8 @@ def from_dev(t: torch.Tensor, like: np.ndarray) -> np.ndarray:
 class GpuPlan:
     """A plan plus the caller-owned device buffers one step reads and writes."""
 
-    def __init__(self, cfg, weights, batch, cap, kc, vc, seq_len, tokens, baseline=False, opts=None, desc=None):
+    def __init__(self, cfg, weights, batch, cap, kc, vc, seq_len, tokens, baseline=False, opts=None, desc=None,
+                 static=False):
         self.cfg = cfg
         if desc is None:
             desc, self.tensors = wpk.model_from_weights(cfg, weights, "cuda")
@@ -44,6 +45,8 @@ class GpuPlan:
         self.kv = wpk.wpk_kv(self.kc.data_ptr(), self.vc.data_ptr(), self.seq_len.data_ptr())
         if baseline:
             self.plan = wpk.wpk_build_graph_baseline(self.desc.desc, batch, cap)
+        elif static:
+            self.plan = wpk.wpk_build_static(self.desc.desc, batch, cap)
         else:
             self.plan = wpk.wpk_build_ex(self.desc.desc, batch, cap, opts)
         assert self.plan, wpk.wpk_last_error(None)

@@ -134,7 +134,14 @@ wpk_plan* wpk_build_ex(const wpk_model_desc* desc, int32_t batch, int32_t ctx_le
  * The call returns once the launch is enqueued; use wpk_sync to wait. */
 int32_t wpk_step(wpk_plan* plan, int32_t* tokens, wpk_kv* kv, void* logits, wpk_stream_t stream);
 
-/* Wait for the plan's last step and return the latched device status. */
+/* Wait for the plan's last step and return the latched device status.
+ * Source: "Why real-time inference wants a megakernel", section "What a
+ * megakernel does not solve", under "It increases compiler and verification
+ * burden": a megakernel must surface its failures (deadlock, a stuck
+ * dependency) and keep enough execution state to locate them.  Device-side
+ * errors are latched by the workers, never raised mid-step; wpk_sync is where
+ * the host learns of them, with the failing tile, worker and step, and for a
+ * watchdog timeout the first counter group that was short of publishes. */
 int32_t wpk_sync(wpk_plan* plan);
 
 void wpk_destroy(wpk_plan* plan);
@@ -142,7 +149,18 @@ void wpk_destroy(wpk_plan* plan);
 /* Last error message of the plan, or of the calling thread if plan is NULL. */
 const char* wpk_last_error(const wpk_plan* plan);
 
-/* Runtime options (keys below).  Returns WPK_E_ARG for an unknown key/value. */
+/* Runtime options (keys below).  Returns WPK_E_ARG for an unknown key/value.
+ * Sources: the ablation keys switch the features that "One Megakernel is Not
+ * Enough", Table I, models one at a time -- WPK_OPT_PREFETCH the weight
+ * prefetch into the per-worker staging slot, WPK_OPT_WORKERS the worker count
+ * W -- and WPK_OPT_LAUNCH the residency guarantee the persistent-threads page
+ * asks of a persistent kernel (section 2: every worker resident for the whole
+ * run).  WPK_OPT_LOG, WPK_OPT_WATCHDOG_US, WPK_OPT_DEBUG_DROP_TILE and
+ * WPK_OPT_RESET serve the failure handling of "Why real-time inference wants a
+ * megakernel", "What a megakernel does not solve" (find and survive a stuck
+ * dependency); WPK_OPT_PERTURB_SEED exercises other claim and completion
+ * orders, which must not change the numbers (same section: preserve numerical
+ * behaviour through reordering).  Every key applies to later steps only. */
 #define WPK_OPT_LOG 1             /* 1: record the per-tile execution log each step */
 #define WPK_OPT_WATCHDOG_US 2     /* bound on any single wait, microseconds (default 2,000,000) */
 #define WPK_OPT_PERTURB_SEED 3    /* != 0: sleep a pseudo-random time before each tile */
@@ -157,7 +175,14 @@ const char* wpk_last_error(const wpk_plan* plan);
                                      anyone waits on */
 int32_t wpk_set_option(wpk_plan* plan, int32_t key, int64_t value);
 
-/* Per-tile execution log of the last logged step, one record per tile id. */
+/* Per-tile execution log of the last logged step, one record per tile id.
+ * Source: "Why real-time inference wants a megakernel", "What a megakernel
+ * does not solve" ("It increases compiler and verification burden"): the
+ * runtime records enough execution state to check that every task ran once,
+ * after its dependencies, and to locate a failure.  Layout: dst receives
+ * wpk_log_rec records (host memory, caller-owned, `bytes` long); returns
+ * WPK_E_ARG if bytes cannot hold n_tiles records, WPK_E_HIP if the copy
+ * fails.  Synchronous. */
 typedef struct wpk_log_rec {
   int32_t exec_count;   /* times the tile ran this step (must be 1) */
   int32_t wait_delta;   /* counter sum observed at start minus its target (must be 0) */
@@ -209,7 +234,12 @@ int32_t wpk_get_info(const wpk_plan* plan, wpk_plan_info* out);
 int32_t wpk_get_dag(const wpk_plan* plan, int32_t* type, int32_t* layer, int32_t* wait,
                     int32_t* signal);
 
-/* The same decode step as one kernel per operation (about 6 per layer),
+/* Source: the conventional execution the pages measure megakernels against --
+ * "persistent-threads-megakernels", section 3 (one launch per operation, the
+ * boundaries between them replayed from a captured graph) and section 7
+ * (compare against the graph-replayed baseline) -- and the TensorRT-style
+ * one-kernel-per-operator design of "One Megakernel is Not Enough".
+ * The same decode step as one kernel per operation (about 6 per layer),
  * captured once into a hipGraph and replayed by wpk_step: the conventional
  * baseline, sharing the megakernel's tile bodies.  The graph is captured on
  * the first wpk_step and re-captured if tokens/kv/logits pointers change. */

@@ -8,21 +8,23 @@ decoding.  Weights, tokens and the cached context are seeded synthetic inputs
 of a 496-token prefill); everything is resident in HBM before timing starts.
 
 A step is one decode step of the whole model, one megakernel launch; tokens
-chain on the device from step to step.  K steps are timed between a
-synchronize on each side; each launch is also bracketed by HIP events on the
-stream it runs on, which gives the per-step latency distribution and the
-kernel duration used for the roofline.  The same K steps are then run through
-the per-operator hipGraph baseline, and the CPU oracle is timed on a bounded
-sample of the same workload.  A second workload, batch 32 with per-sequence
-contexts drawn from U{256..1024} (the matrix-core path), is reported in the
-same line under "batch32", with its own graph baseline.
+chain on the device from step to step.  After W warmup steps, K steps are
+timed between a synchronize on each side (`value`); each launch is also
+bracketed by HIP events on the stream it runs on.  The same K steps are then
+repeated R-1 more times from the same starting state (sequence lengths and
+tokens reset, the same K/V positions rewritten), so the per-launch latency
+distribution has R*K samples.  The per-operator hipGraph baseline runs the same
+blocks, the ablations (Table I features switched off one at a time) run one
+block each, and the CPU oracle is timed on a bounded sample of the same
+workload.  A second workload, batch 32 with per-sequence contexts drawn from
+U{256..1024} (the matrix-core path), is reported under "batch32".
 
-    python bench.py [--steps 64] [--warmup 3] [--batch 1] [--no-cpu] [--no-baseline] [--no-batch32]
+    python bench.py [--steps 64] [--warmup 3] [--reps 5] [--no-cpu] [--no-baseline]
+                    [--no-batch32] [--no-ablations]
 """
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -35,15 +37,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode step latency (µs) + achieved HBM GB/s, Llama-1B-shape, batch 1 and 32"
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 CONTEXT = 496
-
-
-def source_hash() -> str:
-    h = hashlib.sha256()
-    for f in ("megakernel.hip", "plan.h"):
-        with open(os.path.join(ROOT, "persistent_megakernel_latency_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
 
 
 def step_bytes(cfg, batch: int, positions_before: np.ndarray) -> float:
@@ -56,86 +51,138 @@ def step_bytes(cfg, batch: int, positions_before: np.ndarray) -> float:
     return w + float(np.sum(n * kv_per_pos + kv_per_pos + cfg.hidden * cfg.elt_bytes + cfg.vocab * 4))
 
 
-def traffic_from_profile(shash: str, per_launch_bytes: float, name: str = "megakernel_llama1b_b1_traffic.json"):
+def profile_record(name: str, shash: str):
+    """A recorded profile summary (profiles/<name>), if it was taken on the
+    current sources."""
     path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("source_hash") != shash:
-        return None  # the kernel changed since the counters were taken
-    return t.get("hbm_bytes_per_launch")
+    return t if t.get("source_hash") == shash else None
 
 
-def measure(wpk, torch, cfg, desc, batch, lens0, tok0, args, dev, baseline: bool):
-    """Times K decode steps of one workload on the megakernel (and, if asked,
-    on the per-operator graph baseline) from the same starting state."""
-    cap = int(np.ceil((int(lens0.max()) + args.warmup + args.steps + 2) / 64.0) * 64)
-    kc_np, vc_np = synth_kv(cfg, batch, cap, lens0)
-    kc = torch.from_numpy(kc_np.view(np.int16)).to(dev)
-    vc = torch.from_numpy(vc_np.view(np.int16)).to(dev)
-    seq = torch.from_numpy(lens0.copy()).to(dev)
-    tokens = torch.from_numpy(tok0.copy()).to(dev)
-    logits = torch.empty((batch, cfg.vocab), dtype=torch.float32, device=dev)
-    kv = wpk.wpk_kv(kc.data_ptr(), vc.data_ptr(), seq.data_ptr())
-    stream = torch.cuda.current_stream(dev)
-
-    def reset_state():
-        seq.copy_(torch.from_numpy(lens0))
-        tokens.copy_(torch.from_numpy(tok0))
-        torch.cuda.synchronize(dev)
-
-    def timed(plan, label):
-        reset_state()
-        for _ in range(args.warmup):
-            wpk.check(wpk.wpk_step(plan, tokens.data_ptr(), kv, logits.data_ptr(), stream.cuda_stream), plan)
-        wpk.check(wpk.wpk_sync(plan), plan, label)
-        positions = seq.cpu().numpy().astype(np.int64)
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-        torch.cuda.synchronize(dev)
-        w0 = time.perf_counter()
-        for e0, e1 in ev:
-            e0.record(stream)
-            wpk.check(wpk.wpk_step(plan, tokens.data_ptr(), kv, logits.data_ptr(), stream.cuda_stream), plan)
-            e1.record(stream)
-        torch.cuda.synchronize(dev)
-        wall = time.perf_counter() - w0
-        wpk.check(wpk.wpk_sync(plan), plan, label)
-        per = np.array([a.elapsed_time(b) * 1000.0 for a, b in ev])  # microseconds per launch
-        byts = np.array([step_bytes(cfg, batch, positions + i) for i in range(args.steps)])
-        return wall, per, byts
-
-    plan = wpk.wpk_build(desc.desc, batch, cap)
-    if not plan:
-        raise RuntimeError("wpk_build: " + wpk.wpk_last_error(None))
-    info = wpk.wpk_get_info(plan)
-    wall, per, byts = timed(plan, "megakernel")
-    wpk.wpk_destroy(plan)
-    out = {"wall": wall, "per": per, "bytes": byts, "info": info, "kv": (kc_np, vc_np)}
-    if baseline:
-        bplan = wpk.wpk_build_graph_baseline(desc.desc, batch, cap)
-        if not bplan:
-            raise RuntimeError("baseline build: " + wpk.wpk_last_error(None))
-        bwall, bper, _ = timed(bplan, "graph baseline")
-        wpk.wpk_destroy(bplan)
-        out["baseline"] = {"value": round(bwall / args.steps * 1e6, 2), "unit": "µs/step",
-                           "latency_us": {"mean": round(float(bper.mean()), 2),
-                                          "p50": round(float(np.percentile(bper, 50)), 2),
-                                          "p95": round(float(np.percentile(bper, 95)), 2)},
-                           "megakernel_speedup": round(float(bper.mean() / per.mean()), 3)}
-    return out
-
-
-def synth_kv(cfg, batch, cap, lens):
-    import synth
-
-    return synth.synthetic_kv(cfg, batch, cap, lens)
+def tile_read_ceiling():
+    """The repository's measured streaming ceiling: the best tile-read
+    bandwidth of the microbenchmark (64 KiB tiles into registers, the
+    megakernel's load shape), from its recorded output."""
+    path = os.path.join(ROOT, "profiles", "microbench_gfx950.md")
+    best = None
+    if os.path.exists(path):
+        for line in open(path):
+            line = line.strip()
+            if line.startswith('{"bench": "tile_read", "mode": 0,'):
+                best = max(best or 0.0, json.loads(line)["GBps"])
+    return best
 
 
 def lat(per):
     return {"mean": round(float(per.mean()), 2), "p50": round(float(np.percentile(per, 50)), 2),
             "p95": round(float(np.percentile(per, 95)), 2), "p99": round(float(np.percentile(per, 99)), 2),
-            "min": round(float(per.min()), 2)}
+            "min": round(float(per.min()), 2), "samples": int(per.size)}
+
+
+class Workload:
+    """Device state of one workload: KV cache, lengths, tokens, logits."""
+
+    def __init__(self, wpk, torch, cfg, batch, lens0, tok0, cap, dev):
+        import synth
+        self.wpk, self.torch, self.cfg, self.batch, self.dev = wpk, torch, cfg, batch, dev
+        self.lens0, self.tok0, self.cap = lens0, tok0, cap
+        kc_np, vc_np = synth.synthetic_kv(cfg, batch, cap, lens0)
+        self.kc = torch.from_numpy(kc_np.view(np.int16)).to(dev)
+        self.vc = torch.from_numpy(vc_np.view(np.int16)).to(dev)
+        self.seq = torch.from_numpy(lens0.copy()).to(dev)
+        self.tokens = torch.from_numpy(tok0.copy()).to(dev)
+        self.logits = torch.empty((batch, cfg.vocab), dtype=torch.float32, device=dev)
+        self.kv = wpk.wpk_kv(self.kc.data_ptr(), self.vc.data_ptr(), self.seq.data_ptr())
+        self.stream = torch.cuda.current_stream(dev)
+
+    def reset(self):
+        self.seq.copy_(self.torch.from_numpy(self.lens0))
+        self.tokens.copy_(self.torch.from_numpy(self.tok0))
+        self.torch.cuda.synchronize(self.dev)
+
+    def step(self, plan):
+        self.wpk.check(self.wpk.wpk_step(plan, self.tokens.data_ptr(), self.kv, self.logits.data_ptr(),
+                                         self.stream.cuda_stream), plan, "wpk_step")
+
+    def block(self, plan, warmup, steps, label):
+        """Warmup, then `steps` launches each bracketed by HIP events on the
+        launch stream, between synchronizes.  Returns (wall seconds, per-launch
+        µs, algorithmic bytes per launch)."""
+        torch, wpk = self.torch, self.wpk
+        self.reset()
+        for _ in range(warmup):
+            self.step(plan)
+        wpk.check(wpk.wpk_sync(plan), plan, label)
+        positions = self.seq.cpu().numpy().astype(np.int64)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        torch.cuda.synchronize(self.dev)
+        w0 = time.perf_counter()
+        for e0, e1 in ev:
+            e0.record(self.stream)
+            self.step(plan)
+            e1.record(self.stream)
+        torch.cuda.synchronize(self.dev)
+        wall = time.perf_counter() - w0
+        wpk.check(wpk.wpk_sync(plan), plan, label)
+        per = np.array([a.elapsed_time(b) * 1000.0 for a, b in ev])
+        byts = np.array([step_bytes(self.cfg, self.batch, positions + i) for i in range(steps)])
+        return wall, per, byts
+
+
+def measure(wpk, W: Workload, desc, args, baseline: bool, ablations):
+    """The timed block (value), R-1 repeated blocks for the latency
+    distribution, the graph baseline's blocks and one block per ablation."""
+    plan = wpk.wpk_build(desc.desc, W.batch, W.cap)
+    if not plan:
+        raise RuntimeError("wpk_build: " + wpk.wpk_last_error(None))
+    info = wpk.wpk_get_info(plan)
+    blocks = [W.block(plan, args.warmup, args.steps, "megakernel") for _ in range(args.reps)]
+    wpk.wpk_destroy(plan)
+    out = {"wall": blocks[0][0], "per": np.concatenate([b[1] for b in blocks]), "bytes": blocks[0][2],
+           "block_us": [round(b[0] / args.steps * 1e6, 2) for b in blocks], "info": info}
+    if baseline:
+        bplan = wpk.wpk_build_graph_baseline(desc.desc, W.batch, W.cap)
+        if not bplan:
+            raise RuntimeError("baseline build: " + wpk.wpk_last_error(None))
+        bb = [W.block(bplan, args.warmup, args.steps, "graph baseline") for _ in range(args.reps)]
+        wpk.wpk_destroy(bplan)
+        bper = np.concatenate([b[1] for b in bb])
+        out["baseline"] = {"value": round(bb[0][0] / args.steps * 1e6, 2), "unit": "µs/step",
+                           "latency_us": lat(bper),
+                           "megakernel_speedup": round(float(bper.mean() / out["per"].mean()), 3)}
+    res = {}
+    for name, opts, option in ablations:
+        p = wpk.wpk_build_ex(desc.desc, W.batch, W.cap, opts)
+        if not p:
+            res[name] = {"error": wpk.wpk_last_error(None)}
+            continue
+        if option:
+            wpk.check(wpk.wpk_set_option(p, option[0], option[1]), p, name)
+        wall, per, _ = W.block(p, args.warmup, args.steps, name)
+        wpk.wpk_destroy(p)
+        res[name] = {"value": round(wall / args.steps * 1e6, 2), "unit": "µs/step",
+                     "latency_mean_us": round(float(per.mean()), 2),
+                     "vs_default": round(float(per.mean() / out["per"].mean()), 3)}
+    if res:
+        out["ablations"] = res
+    return out
+
+
+def roofline(byts, per, shash, kernel_key, traffic_name):
+    achieved = float(np.mean(byts) / (per.mean() * 1e-6) / 1e9)
+    traffic = profile_record(traffic_name, shash)
+    kd = profile_record("megakernel_kernel_durations.json", shash)
+    rk = kd.get(kernel_key) if kd else None
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic.get("hbm_bytes_per_launch") if traffic else None,
+            "bytes_per_launch": round(float(np.mean(byts))),
+            "kernel": "wpk::megakernel", "kernel_us_events": round(float(per.mean()), 2),
+            "kernel_us_rocprof": rk["average_us"] if rk else None,
+            "tile_read_ceiling_GBps": tile_read_ceiling(), "source_hash": shash}
 
 
 def run(args):
@@ -145,18 +192,25 @@ def run(args):
     import synth
 
     cfg = synth.LLAMA_1B
-    batch = args.batch
     torch.cuda.init()
     dev = torch.device("cuda", 0)
     t0 = time.time()
     weights = synth.make_weights(cfg)
     desc, tensors = wpk.model_from_weights(cfg, weights, dev)
+    batch = 1
     lens0 = np.full(batch, CONTEXT, np.int32)
     tok0 = synth.prompt_tokens(cfg, batch, CONTEXT)[:, -1].astype(np.int32)
+    cap = int(np.ceil((CONTEXT + args.warmup + args.steps + 2) / 64.0) * 64)
+    W1 = Workload(wpk, torch, cfg, batch, lens0, tok0, cap, dev)
     setup_s = time.time() - t0
-    m = measure(wpk, torch, cfg, desc, batch, lens0, tok0, args, dev, not args.no_baseline)
+    ab1 = [] if args.no_ablations else [
+        ("weight_prefetch_off", None, (wpk.WPK_OPT_PREFETCH, 0)),
+        ("barrier_edges", wpk.wpk_build_opts(barrier_edges=1), None),
+        ("cooperative_launch", None, (wpk.WPK_OPT_LAUNCH, 1)),
+    ]
+    m = measure(wpk, W1, desc, args, not args.no_baseline, ab1)
     wall, per, byts, info = m["wall"], m["per"], m["bytes"], m["info"]
-
+    shash = wpk.source_hash()
     result = {
         "metric": METRIC,
         "value": round(wall / args.steps * 1e6, 2),
@@ -174,47 +228,52 @@ def run(args):
                    "batch": batch, "context": CONTEXT, "layers": cfg.n_layers, "hidden": cfg.hidden,
                    "q_heads": cfg.n_q_heads, "kv_heads": cfg.n_kv_heads, "ffn": cfg.ffn, "vocab": cfg.vocab,
                    "workers": info.workers, "tiles_per_step": info.n_tiles},
+        "repetitions": {"reps": args.reps, "block_us_per_step": m["block_us"]},
         "latency_us": lat(per),
         "tokens_per_s": round(batch * args.steps / wall, 1),
     }
-    achieved = float(np.mean(byts) / (per.mean() * 1e-6) / 1e9)
-    shash = source_hash()
-    traffic = traffic_from_profile(shash, float(np.mean(byts)))
-    result["hbm_GBps"] = round(achieved, 1)
-    result["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                          "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                          "bytes_per_launch": round(float(np.mean(byts))), "kernel": "wpk::megakernel",
-                          "kernel_us": round(float(per.mean()), 2), "source_hash": shash}
+    rl = roofline(byts, per, shash, "batch1", "megakernel_llama1b_b1_traffic.json")
+    result["hbm_GBps"] = rl["achieved"]
+    result["roofline"] = rl
     if "baseline" in m:
         result["graph_baseline"] = m["baseline"]
+    if "ablations" in m:
+        result["ablations"] = m["ablations"]
+    del W1
 
     if not args.no_batch32:
-        # the batch-32 workload: contexts U{256..1024}, matrix-core projections
         b32 = 32
         lens32 = synth.context_lengths(b32)
         tok32 = synth.prompt_tokens(cfg, b32, 1)[:, 0].astype(np.int32)
-        m32 = measure(wpk, torch, cfg, desc, b32, lens32, tok32, args, dev, not args.no_baseline)
+        cap32 = int(np.ceil((int(lens32.max()) + args.warmup + args.steps + 2) / 64.0) * 64)
+        W32 = Workload(wpk, torch, cfg, b32, lens32, tok32, cap32, dev)
+        ab32 = [] if args.no_ablations else [
+            ("lds_forwarding_chained_attention", wpk.wpk_build_opts(forward=1), None),
+            ("barrier_edges", wpk.wpk_build_opts(barrier_edges=1), None),
+            ("weight_prefetch_off", None, (wpk.WPK_OPT_PREFETCH, 0)),
+        ]
+        m32 = measure(wpk, W32, desc, args, not args.no_baseline, ab32)
         w32, per32, by32 = m32["wall"], m32["per"], m32["bytes"]
-        gb = float(np.mean(by32) / (per32.mean() * 1e-6) / 1e9)
         flops = 2.0 * cfg.n_matrix_params() * b32  # projections, MLP and LM head
+        rl32 = roofline(by32, per32, shash, "batch32", "megakernel_llama1b_b32_traffic.json")
         result["batch32"] = {
             "workload": "Llama-3.2-1B-shape decode step, batch 32, contexts U{256..1024}, greedy",
             "value": round(w32 / args.steps * 1e6, 2), "unit": "µs/step", "latency_us": lat(per32),
-            "tokens_per_s": round(b32 * args.steps / w32, 1), "hbm_GBps": round(gb, 1),
-            "roofline": {"bound": "hbm", "achieved": round(gb, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": round(gb / HBM_PEAK_GBPS, 4),
-                         "traffic": traffic_from_profile(shash, float(np.mean(by32)),
-                                                         "megakernel_llama1b_b32_traffic.json"),
-                         "bytes_per_launch": round(float(np.mean(by32))), "kernel_us": round(float(per32.mean()), 2)},
+            "repetitions": {"reps": args.reps, "block_us_per_step": m32["block_us"]},
+            "tokens_per_s": round(b32 * args.steps / w32, 1), "hbm_GBps": rl32["achieved"],
+            "roofline": rl32,
             "mfma": {"flops_per_step": flops, "achieved_TFLOPs": round(flops / (per32.mean() * 1e-6) / 1e12, 2),
-                     "peak_TFLOPs": 2500.0,
-                     "frac": round(flops / (per32.mean() * 1e-6) / 2.5e15, 4)},
+                     "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
+                     "frac": round(flops / (per32.mean() * 1e-6) / (MFMA_BF16_PEAK_TFLOPS * 1e12), 4)},
             "workers": m32["info"].workers, "tiles_per_step": m32["info"].n_tiles}
         if "baseline" in m32:
             result["batch32"]["graph_baseline"] = m32["baseline"]
+        if "ablations" in m32:
+            result["batch32"]["ablations"] = m32["ablations"]
+        del W32
 
     if not args.no_cpu:
-        kc_np, vc_np = m["kv"]
+        kc_np, vc_np = synth.synthetic_kv(cfg, batch, cap, lens0)
         result["cpu_baseline"] = cpu_baseline(cfg, weights, batch, kc_np, vc_np, lens0, tok0, args.cpu_seconds)
     result["setup_s"] = round(setup_s, 1)
     return result
@@ -246,15 +305,19 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=64)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--reps", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-baseline", action="store_true")
     ap.add_argument("--no-batch32", action="store_true")
+    ap.add_argument("--no-ablations", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: this build runs on a "
               "single GPU (batched sequences would shard across GPUs with no exchange)", file=sys.stderr)
+        sys.exit(2)
+    if args.reps < 1 or args.steps < 1:
+        print("--reps and --steps must be positive", file=sys.stderr)
         sys.exit(2)
     print(json.dumps(run(args)))
 

@@ -112,6 +112,10 @@ typedef struct wpk_build_opts {
                                tile per (sequence, kv head) walks its KV chunks and merges their
                                partials on chip, with no combine tiles.  1: on; 0 (default) or -1:
                                off (split tiles and combine tiles; faster at the built shapes) */
+  int32_t barrier_edges;    /* ablation of the tile-to-tile tensor edges ("One Megakernel is Not
+                               Enough", Table I, cross-kernel readiness): 1 makes every tile wait
+                               for ALL tiles of the operator it reads from, as a per-operator
+                               barrier would; 0 (default): only for the tiles producing its inputs */
 } wpk_build_opts;
 
 typedef struct wpk_plan wpk_plan;
@@ -173,6 +177,10 @@ const char* wpk_last_error(const wpk_plan* plan);
                                      more per step).  Both are safe: claims follow the topological
                                      order, so a worker that is not yet resident holds no tile that
                                      anyone waits on */
+#define WPK_OPT_FIXED_REDUCER 9   /* host plans only, wpk_emulate_step: 1 makes each wide row block's
+                                     last slice in claim order its reducer, which waits for the other
+                                     slices' arrivals, instead of the last slice to arrive; device plans
+                                     refuse it (a device run of this scheme once faulted, cause unknown) */
 int32_t wpk_set_option(wpk_plan* plan, int32_t key, int64_t value);
 
 /* Per-tile execution log of the last logged step, one record per tile id.

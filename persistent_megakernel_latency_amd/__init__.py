@@ -41,6 +41,7 @@ WPK_OPT_RESET = 5
 WPK_OPT_PREFETCH = 6
 WPK_OPT_WORKERS = 7
 WPK_OPT_LAUNCH = 8
+WPK_OPT_FIXED_REDUCER = 9
 
 TILE_TYPES = ["qkv", "attn", "combine", "oproj", "gateup", "down", "lm", "argmax", "norm", "norm2", "normf",
               "attnc"]
@@ -66,7 +67,7 @@ class wpk_kv(ctypes.Structure):
 
 class wpk_build_opts(ctypes.Structure):
     _fields_ = [("tile_bytes", _i32), ("workers_per_cu", _i32), ("queue_shards", _i32), ("attn_chunk", _i32),
-                ("forward", _i32)]
+                ("forward", _i32), ("barrier_edges", _i32)]
 
 
 class wpk_log_rec(ctypes.Structure):
@@ -260,6 +261,18 @@ def model_from_weights(cfg, weights: Dict[str, object], device="cuda"):
         ptrs[key] = [lt[key].data_ptr() for lt in tensors["layers"]]
     keep = [tensors["embed"], tensors["final_norm"]] + [t for lt in tensors["layers"] for t in lt.values()]
     return ModelDesc(cfg, ptrs, keep), tensors
+
+
+def source_hash() -> str:
+    """Hash of the sources that decide what the megakernel does at run time
+    (kernel, tile geometry, DAG builder, launch path); recorded profiles are
+    only reported while it matches."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("megakernel.hip", "plan.h", "builder.cpp", "builder.h", "capi.cpp", "runtime.h"):
+        with open(os.path.join(_HERE, "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def check(rc: int, plan=None, what: str = "wpk call") -> None:

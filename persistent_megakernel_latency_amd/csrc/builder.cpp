@@ -94,6 +94,8 @@ std::string check_shape(const wpk_model_desc& d, int32_t batch, int32_t ctx_len,
   if (o.forward < -1 || o.forward > 1) return "forward must be -1, 0 or 1";
   s.forward = o.forward == 1;  // measured slower at the built shapes: off unless asked for
   if (s.forward && !s.wide) return "LDS forwarding of attention partials is built for batches above 4";
+  if (o.barrier_edges != 0 && o.barrier_edges != 1) return "barrier_edges must be 0 or 1";
+  s.barrier_edges = o.barrier_edges;
   *out = s;
   return "";
 }
@@ -167,6 +169,15 @@ namespace {
 
 Dag finish_dag(const Shape& s, Emitter& e);
 
+// The counter groups of one operator's consumers: one per consumer input
+// region (tile-to-tile edges), or, as the barrier-edge ablation, a single
+// group shared by all of them, so that every consumer waits for the whole
+// producing operator.
+void fill_groups(Emitter& e, std::vector<int32_t>& gs, int32_t barrier) {
+  const int32_t one = barrier ? e.group() : -1;
+  for (auto& g : gs) g = barrier ? one : e.group();
+}
+
 // Wide plans (batch above kMaxBatchGemv).  Layer 0 starts with a tile per
 // sequence that writes the embedding row as the first QKV operand.  Per layer:
 // QKV row blocks of one head each (two segments, dimensions [0, D/2) and
@@ -192,11 +203,11 @@ void build_wide(const Shape& s, Emitter& e) {
       for (int32_t b = 0; b < s.B; ++b) e.tile(T_NORM, 0, -1, g_qkv_in).b = b;
     }
     std::vector<int32_t> g_attn(s.Hkv), g_comb(s.B * s.Hkv), g_o(n_os), g_dn(n_ds);
-    for (auto& g : g_attn) g = e.group();
-    for (auto& g : g_comb) g = e.group();
-    for (auto& g : g_o) g = e.group();
+    fill_groups(e, g_attn, s.barrier_edges);
+    fill_groups(e, g_comb, s.barrier_edges);
+    fill_groups(e, g_o, s.barrier_edges);
     const int32_t g_xm = e.group();
-    for (auto& g : g_dn) g = e.group();
+    fill_groups(e, g_dn, s.barrier_edges);
     const int32_t g_next = e.group();
     for (int32_t g = 0; g < s.Hkv; ++g) {
       for (int32_t k = 0; k < s.G; ++k) {
@@ -254,8 +265,8 @@ Dag build_dag(const Shape& s) {
   int32_t g_x = -1;  // group the current layer's QKV tiles wait on (-1: layer 0)
   for (int32_t l = 0; l < s.L; ++l) {
     std::vector<int32_t> g_attn(s.Hkv), g_comb(s.B * s.Hkv);
-    for (auto& g : g_attn) g = e.group();
-    for (auto& g : g_comb) g = e.group();
+    fill_groups(e, g_attn, s.barrier_edges);
+    fill_groups(e, g_comb, s.barrier_edges);
     const int32_t g_o = e.group(), g_gu = e.group(), g_dn = e.group();
     const int32_t g_qkv_in = g_x;
 

@@ -24,6 +24,7 @@ struct Shape {
   int32_t wide;      // batch above kMaxBatchGemv: matrix-core tiles, RMSNorm split between epilogues
   int32_t attn_sub;  // KV chunks per attention tile (one slot holds up to 64 KiB of K and V)
   int32_t forward;   // chained attention tiles (LDS forwarding of the partials to the combine)
+  int32_t barrier_edges;  // ablation: each consumer waits on its whole producing operator
   float theta, eps;
 };
 

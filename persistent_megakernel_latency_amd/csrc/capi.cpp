@@ -485,6 +485,11 @@ int32_t wpk_set_option(wpk_plan* p, int32_t key, int64_t value) {
       if (value != 0 && value != 1) return plan_fail(p, WPK_E_ARG, "launch must be 0 or 1");
       p->cooperative = (int32_t)value;
       return WPK_OK;
+    case WPK_OPT_FIXED_REDUCER:
+      if (!p->host) return plan_fail(p, WPK_E_ARG, "the fixed reducer is an option of the host emulator only");
+      if (value != 0 && value != 1) return plan_fail(p, WPK_E_ARG, "fixed reducer must be 0 or 1");
+      p->emu_fixed_reducer = (int32_t)value;
+      return WPK_OK;
     case WPK_OPT_WORKERS:
       if (value < (int64_t)p->s.queue_shards || value > p->max_workers)
         return plan_fail(p, WPK_E_ARG, "workers must be in [queue shards, max co-resident]");

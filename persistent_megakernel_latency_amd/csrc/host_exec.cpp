@@ -6,14 +6,23 @@
 //    must give bit-identical results, and with NaN-poisoned intermediates a
 //    tile that runs before one of its producers poisons the logits;
 //  * the emulator runs the device protocol itself -- claim from the sharded
-//    queues in topological order, wait for a counter group with acquire loads,
-//    publish with a release increment -- on std::threads with random delays,
-//    so a data race in the protocol is visible to ThreadSanitizer.
+//    queues in topological order, poll a counter group, publish with one
+//    increment -- on std::threads with random delays.  The orderings are the
+//    device's, written in the C++ memory model: the device publishes with a
+//    relaxed atomic after waiting for its own stores to complete and reads its
+//    inputs after the poll that saw them complete, so here a release fence
+//    precedes each relaxed publish and an acquire fence follows each satisfied
+//    relaxed poll.  ThreadSanitizer does not model standalone fences, so a
+//    build with WPK_TSAN_ORDERINGS folds each fence into its atomic (release
+//    increment, acquire poll loads: the same happens-before edges), which lets
+//    a sanitizer build of the emulator check every data access the protocol is
+//    meant to order.
 // The "final participant publishes" and phase-barrier logic of the WPK design
 // ("Why real-time inference wants a megakernel", one WPK update) is replaced
 // here, as on the device, by counter groups released per tile.
 #include "host_exec.h"
 
+#include <atomic>
 #include <chrono>
 #include <cmath>
 #include <cstring>
@@ -152,7 +161,32 @@ struct Ctx {
   const Params& P;
   std::atomic<unsigned long long>* argmax;
   std::atomic<int32_t>* status;
+  int64_t wpart_len = 0;   // floats of the partial-sum slots (bounds of every access)
+  int64_t fixc_len = 0;    // words of the arrival counters
+  bool fixed_reducer = false;         // emulator option, wide plans (see run_gemv)
+  const std::atomic<int32_t>* abort = nullptr;
 };
+
+// The device protocol's orderings (see the file comment).
+inline void publish_fence() {
+#ifndef WPK_TSAN_ORDERINGS
+  std::atomic_thread_fence(std::memory_order_release);
+#endif
+}
+inline void acquire_fence() {
+#ifndef WPK_TSAN_ORDERINGS
+  std::atomic_thread_fence(std::memory_order_acquire);
+#endif
+}
+#ifdef WPK_TSAN_ORDERINGS
+constexpr std::memory_order kPublishOrder = std::memory_order_release;
+constexpr std::memory_order kPollOrder = std::memory_order_acquire;
+constexpr int kPublishOrderB = __ATOMIC_RELEASE, kPollOrderB = __ATOMIC_ACQUIRE, kArriveOrder = __ATOMIC_ACQ_REL;
+#else
+constexpr std::memory_order kPublishOrder = std::memory_order_relaxed;
+constexpr std::memory_order kPollOrder = std::memory_order_relaxed;
+constexpr int kPublishOrderB = __ATOMIC_RELAXED, kPollOrderB = __ATOMIC_RELAXED, kArriveOrder = __ATOMIC_RELAXED;
+#endif
 
 void set_status(Ctx& c, int32_t code) {
   int32_t z = 0;
@@ -210,8 +244,11 @@ void gemv_input(Ctx& c, const Tile& T, int b, std::vector<float>& x) {
       case T_DOWN: src = lb.xh; K = P.F; break;
       default: src = P.layers[P.L - 1].xnf; break;
     }
-    x.resize(K);
-    for (int i = 0; i < K; ++i) x[i] = xget(src, K, b, i);
+    // only this tile's K slice: it waits for the tiles producing those
+    // columns and no others, so the rest of the row may still be being written
+    x.assign(K, 0.f);
+    const int k0 = T.c * kWideK, k1 = std::min(K, k0 + kWideK);
+    for (int i = k0; i < k1; ++i) x[i] = xget(src, K, b, i);
     return;
   }
   const float* gain = nullptr;
@@ -270,8 +307,16 @@ void run_gemv(Ctx& c, const Tile& T) {
   // wide plans: this tile's K slice; its partial sums go to its slot, and the
   // row block's last slice adds all slots in slice order
   const int k0 = P.wide ? T.c * kWideK : 0, k1 = P.wide ? k0 + kWideK : K;
+  // partial sums of slice `slice`, bounds-checked against the slot area
+  float dummy = 0.f;
   auto part = [&](int slice, int r, int b) -> float& {
-    return P.wpart[(int64_t)(T.pslot + slice) * kWidePart + ((b / 16) * kWideRows + r) * 16 + b % 16];
+    const int64_t i = (int64_t)(T.pslot + slice) * kWidePart + ((b / 16) * kWideRows + r) * 16 + b % 16;
+    if (slice < 0 || slice >= T.b || r < 0 || r >= kWideRows || b < 0 || b >= kMaxBatch || i < 0 ||
+        i >= c.wpart_len) {
+      set_status(c, WPK_E_ARG);
+      return dummy;
+    }
+    return P.wpart[i];
   };
   if (P.wide) {
     for (int b = 0; b < P.B; ++b) {
@@ -285,8 +330,40 @@ void run_gemv(Ctx& c, const Tile& T) {
         part(T.c, r, b) = acc;
       }
     }
-    const uint32_t old = __atomic_fetch_add(&P.fixc[(int64_t)T.fix * kLine], 1u, __ATOMIC_ACQ_REL);
-    if ((int32_t)(old + 1u) != T.b) return;  // not the row block's last slice
+    const int64_t fi = (int64_t)T.fix * kLine;
+    if (fi < 0 || fi >= c.fixc_len || T.c < 0 || T.c >= T.b) {
+      set_status(c, WPK_E_ARG);
+      return;
+    }
+    uint32_t* arrivals = &P.fixc[fi];
+    if (!c.fixed_reducer) {
+      // the last slice to arrive adds up the row block (the device's scheme)
+      publish_fence();
+      const uint32_t old = __atomic_fetch_add(arrivals, 1u, kArriveOrder);
+      if ((int32_t)(old + 1u) != T.b) return;  // not the row block's last slice
+      acquire_fence();
+    } else if (T.c != T.b - 1) {
+      // a fixed reducer, the row block's last slice in claim order: the others
+      // only count their arrival and go on (no reply awaited)
+      publish_fence();
+      __atomic_fetch_add(arrivals, 1u, kPublishOrderB);
+      return;
+    } else {
+      // the reducer waits, bounded, until every other slice has arrived; its
+      // siblings precede it in the topological claim order, so the lowest
+      // unfinished tile always progresses and the wait ends
+      const auto t0 = std::chrono::steady_clock::now();
+      while (__atomic_load_n(arrivals, kPollOrderB) != (uint32_t)(T.b - 1)) {
+        if ((c.abort && c.abort->load(std::memory_order_relaxed)) ||
+            std::chrono::steady_clock::now() - t0 > std::chrono::seconds(20)) {
+          set_status(c, WPK_E_TIMEOUT);
+          return;
+        }
+        std::this_thread::yield();
+      }
+      acquire_fence();
+      __atomic_store_n(arrivals, 0u, __ATOMIC_RELAXED);  // no other slice touches it again this step
+    }
   }
   for (int b = 0; b < P.B; ++b) {
     const int32_t p = P.seq_len[b];
@@ -715,6 +792,8 @@ int32_t host_serial_step(wpk_plan* p, int32_t* tokens, wpk_kv* kv, float* logits
   if (poison_on) poison(p, P);
   std::atomic<int32_t> status{0};
   Ctx c{P, p->hw.argmax.get(), &status};
+  c.wpart_len = (int64_t)p->hw.wpart.size();
+  c.fixc_len = (int64_t)p->hw.fixc.size();
   const auto& tiles = p->dag.tiles;
   const auto& groups = p->dag.groups;
   const int32_t n = (int32_t)tiles.size();
@@ -766,6 +845,9 @@ int32_t host_emulate_step(wpk_plan* p, int32_t* tokens, wpk_kv* kv, float* logit
   std::fill(p->hw.fixc.begin(), p->hw.fixc.end(), 0u);
   std::atomic<int32_t> status{0};
   Ctx c{P, p->hw.argmax.get(), &status};
+  c.wpart_len = (int64_t)p->hw.wpart.size();
+  c.fixc_len = (int64_t)p->hw.fixc.size();
+  c.fixed_reducer = p->emu_fixed_reducer != 0;
   std::unique_ptr<std::atomic<uint32_t>[]> counters(new std::atomic<uint32_t>[d.n_shard_slots]);
   for (int i = 0; i < d.n_shard_slots; ++i) counters[i].store(0);
   std::unique_ptr<std::atomic<uint32_t>[]> heads(new std::atomic<uint32_t>[nq]);
@@ -774,6 +856,7 @@ int32_t host_emulate_step(wpk_plan* p, int32_t* tokens, wpk_kv* kv, float* logit
   std::unique_ptr<std::atomic<int32_t>[]> exec(new std::atomic<int32_t>[n]);
   for (int i = 0; i < n; ++i) exec[i].store(0);
   std::atomic<int32_t> abort{0};
+  c.abort = &abort;
   std::fill(p->log.begin(), p->log.end(), wpk_log_rec{});
   const auto t0 = std::chrono::steady_clock::now();
   auto now_ns = [&] {
@@ -796,9 +879,10 @@ int32_t host_emulate_step(wpk_plan* p, int32_t* tokens, wpk_kv* kv, float* logit
         const auto w0 = std::chrono::steady_clock::now();
         for (;;) {
           uint32_t sum = 0;
-          for (int s = 0; s < G.shards; ++s) sum += counters[G.shard0 + s].load(std::memory_order_acquire);
+          for (int s = 0; s < G.shards; ++s) sum += counters[G.shard0 + s].load(kPollOrder);
           if ((int32_t)(sum - (uint32_t)G.producers) >= 0) {
             delta = (int32_t)(sum - (uint32_t)G.producers);
+            acquire_fence();  // the tile's input reads stay after the poll that saw them complete
             break;
           }
           if (abort.load(std::memory_order_relaxed)) return;
@@ -821,7 +905,8 @@ int32_t host_emulate_step(wpk_plan* p, int32_t* tokens, wpk_kv* kv, float* logit
       L.t_end = now_ns();
       if (T.signal >= 0) {
         const Group& G = d.groups[T.signal];
-        counters[G.shard0 + T.shard].fetch_add(1, std::memory_order_release);
+        publish_fence();  // the tile's output writes happen before its publish
+        counters[G.shard0 + T.shard].fetch_add(1, kPublishOrder);
       }
     }
   };

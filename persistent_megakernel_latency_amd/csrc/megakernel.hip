@@ -49,6 +49,7 @@
 #include <mutex>
 
 #include "plan.h"
+#include "wide_layout.h"
 #include "wpk.h"
 
 namespace wpk {
@@ -874,7 +875,8 @@ __device__ __forceinline__ void cmp_combine(const Params& P, const Tile& T, cons
 // arrive adds them in slice order and runs the epilogue.
 
 constexpr int kWideSteps = kWideK / 32;                     // k-steps of a slice
-constexpr int kWideFrags = kWideSteps * 2 * 2;              // x sequence halves x hi/lo planes
+constexpr int kWideFrags = kWidePieces;                     // x sequence halves x hi/lo planes
+static_assert(kWideFrags == kWideSteps * 2 * 2, "one 1 KiB B fragment per k-step, half and plane");
 constexpr int kWideKmax = kWideFrags * 256 + kWidePart;     // LDS floats: B fragments, then the partial sums
 
 __device__ __forceinline__ int wfrag(int ks, int h, int pl) { return (ks * 2 + h) * 2 + pl; }
@@ -1331,7 +1333,7 @@ __device__ __forceinline__ bool ctl_wide_post(const Params& P, const Tile& T0, S
   const int lane = opaque(lane0);
   const Tile T = uni(T0);
   const int nh = P.B > 16 ? 2 : 1;
-  const int per = 4 * nh;  // 1 KiB pieces of a partial-sum slot
+  const int per = wide_slot_pieces(nh);  // 1 KiB pieces of a partial-sum slot
   const float* cp = cpart(sm);
   float* mine = P.wpart + (size_t)(T.pslot + T.c) * kWidePart;
   for (int i = 0; i < per; ++i)
@@ -1397,19 +1399,19 @@ __device__ __forceinline__ bool ctl_wide_post(const Params& P, const Tile& T0, S
   // (every 64-row block, per sequence), into the top of the operand area
   const bool consumer = T.type == T_QKV || T.type == T_GATEUP || T.type == T_LM;
   const int nrb = P.H / kWideRows;
-  const int ssp = nrb / 8;  // 1 KiB pieces of the table [nrb][32]
+  const int ssp = wide_ss_pieces(P.H);  // 1 KiB pieces of the table [nrb][32]
   if (consumer) {
     const float* ssc = cload((const float* const*)&P.layers[l].ss1, T.type == T_QKV ? 0 : T.type == T_GATEUP ? 1 : 2);
     const __amdgpu_buffer_rsrc_t r = rsrc(ssc);
     for (int i = 0; i < ssp; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          r, (__attribute__((address_space(3))) void*)(sm.xs + (kWideFrags - ssp + i) * 256), 16,
+          r, (__attribute__((address_space(3))) void*)(sm.xs + (wide_ss_first(P.H) + i) * 256), 16,
           (uint32_t)lane * 16u, i * 1024, 0, 16 /* sc1 */);
   }
   // q and k rows: the RoPE factors of each sequence's position, [n][D/2] cos
   // then sin, into pieces 48..55 of the operand area (above the slices of a
   // K = hidden row block, below the sums of squares)
-  float* const rl = sm.xs + 48 * 256;
+  float* const rl = sm.xs + kWideRopePiece * 256;
   if (T.type == T_QKV && T.kind < 2) {
     const __amdgpu_buffer_rsrc_t rc = rsrc(P.rope_cos), rs = rsrc(P.rope_sin);
 #pragma unroll
@@ -1426,13 +1428,13 @@ __device__ __forceinline__ bool ctl_wide_post(const Params& P, const Tile& T0, S
   }
   // slices of a batch in LDS slots, the own slice skipped (it stays in the
   // compute waves' partial-sum area)
-  const int fit = 16 / nh;  // slots the operand area holds
-  for (int s0 = 0; s0 < T.b; s0 += fit + (T.c >= s0 && T.c < s0 + fit + 1 ? 1 : 0)) {
-    const int own = T.c >= s0 && T.c < s0 + fit + 1;
-    const int s1 = min(T.b, s0 + fit + own);
+  const int fit = wide_fit(nh);  // slots the operand area holds
+  for (int s0 = 0; s0 < T.b; s0 += fit + wide_batch_has_own(s0, T.c, fit)) {
+    const int own = wide_batch_has_own(s0, T.c, fit);
+    const int s1 = wide_batch_end(s0, T.c, fit, T.b);
     for (int sl = s0; sl < s1; ++sl) {
       if (sl == T.c) continue;
-      const int slot = sl - s0 - (sl > T.c ? own : 0);
+      const int slot = wide_slot_of(sl, s0, T.c, own);
       const __amdgpu_buffer_rsrc_t r = rsrc(P.wpart + (size_t)(T.pslot + sl) * kWidePart);
       for (int i = 0; i < per; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -1441,7 +1443,7 @@ __device__ __forceinline__ bool ctl_wide_post(const Params& P, const Tile& T0, S
     }
     wait_all_memory();
     for (int sl = s0; sl < s1; ++sl) {
-      const int slot = sl - s0 - (sl > T.c ? own : 0);
+      const int slot = wide_slot_of(sl, s0, T.c, own);
       const float* src = sl == T.c ? cp : sm.xs + slot * per * 256;
 #pragma unroll
       for (int h = 0; h < 2; ++h)
@@ -1451,7 +1453,7 @@ __device__ __forceinline__ bool ctl_wide_post(const Params& P, const Tile& T0, S
     }
   }
   if (consumer) {  // divide by the root mean square of the operand's row
-    const float* ssl = sm.xs + (kWideFrags - ssp) * 256;
+    const float* ssl = sm.xs + wide_ss_first(P.H) * 256;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int n = 16 * h + s16;
@@ -1467,7 +1469,7 @@ __device__ __forceinline__ bool ctl_wide_post(const Params& P, const Tile& T0, S
   // the operand area is free after the slice sums), read back in the store
   // mapping: lane l owns rows 4(l % 16) .. +3 of sequence 4i + l / 16, so
   // sixteen lanes store a sequence's 64 rows with full 16- or 8-byte stores.
-  constexpr int TP = 68;
+  constexpr int TP = kWideTransposePitch;
   float* tr = sm.xs;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {

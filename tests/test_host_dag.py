@@ -312,3 +312,59 @@ def test_lds_forwarded_attention_matches_split_attention(cfg_name, batch, forwar
     assert np.max(np.abs(st.logits[act] - olog[act])) < 1e-3
     assert np.array_equal(st.tokens[act], otok[act])
     wpk.wpk_destroy(plan)
+
+
+@pytest.mark.parametrize("batch", [1, 8])
+def test_barrier_edge_ablation_same_results_and_coarser_groups(batch):
+    """The barrier-edge ablation (every consumer waits for its whole producing
+    operator) builds a valid DAG with fewer, larger counter groups, and the
+    serial executor gives bit-identical results to the tile-edge DAG."""
+    cfg = synth.MINI
+    w = synth.make_weights(cfg, gain_std=0.1)
+    cap = 140
+    lens = np.array([63, 100, 7, 128, 1, 64, 65, 90][:batch], np.int32)
+    kc, vc = synth.synthetic_kv(cfg, batch, cap, lens)
+    tok = (np.arange(batch, dtype=np.int32) * 113 + 5) % cfg.vocab
+    d = host_desc(cfg, w)
+    outs = []
+    for be in (0, 1):
+        plan = wpk.wpk_build_host(d.desc, batch, cap, wpk.wpk_build_opts(barrier_edges=be))
+        assert plan, wpk.wpk_last_error(None)
+        info = wpk.wpk_get_info(plan)
+        _, _, wait, signal = wpk.wpk_get_dag(plan, info.n_tiles)
+        outs.append((info, HostState(kc, vc, lens, tok, cfg.vocab)))
+        assert outs[-1][1].serial(plan, 3, poison=True) == 0, wpk.wpk_last_error(plan)
+        rc, log = wpk.wpk_get_log(plan, info.n_tiles)
+        check_log(log, wait, signal)
+        wpk.wpk_destroy(plan)
+    (i0, s0), (i1, s1) = outs
+    assert i1.n_tiles == i0.n_tiles and i1.n_groups < i0.n_groups
+    assert np.array_equal(s0.logits, s1.logits) and np.array_equal(s0.kc, s1.kc)
+
+
+def test_emulated_fixed_reducer_matches_serial_on_a_matrix_core_plan():
+    """The fixed-reducer scheme (each wide row block reduced by its last slice
+    in claim order, which waits for its siblings) through the C ABI's host
+    emulator: bitwise equal to the serial executor, every tile once; device
+    plans do not offer it."""
+    cfg = synth.MINI
+    w = synth.make_weights(cfg, gain_std=0.1)
+    batch, cap = 8, 140
+    lens = np.array([63, 100, 7, 128, 1, 64, 65, -1], np.int32)
+    kc, vc = synth.synthetic_kv(cfg, batch, cap, np.maximum(lens, 0))
+    tok = (np.arange(batch, dtype=np.int32) * 113 + 5) % cfg.vocab
+    d = host_desc(cfg, w)
+    plan = wpk.wpk_build_host(d.desc, batch, cap)
+    n = wpk.wpk_get_info(plan).n_tiles
+    _, _, wait, signal = wpk.wpk_get_dag(plan, n)
+    ref = HostState(kc, vc, lens, tok, cfg.vocab)
+    assert ref.serial(plan, 5) == 0
+    assert wpk.wpk_set_option(plan, wpk.WPK_OPT_FIXED_REDUCER, 1) == 0
+    for seed in (1, 2):
+        st = HostState(kc, vc, lens, tok, cfg.vocab)
+        assert st.emulate(plan, 16, seed) == 0, wpk.wpk_last_error(plan)
+        rc, log = wpk.wpk_get_log(plan, n)
+        check_log(log, wait, signal, canonical_only=True)
+        assert np.array_equal(st.logits, ref.logits) and np.array_equal(st.kc, ref.kc)
+    assert wpk.wpk_set_option(plan, wpk.WPK_OPT_FIXED_REDUCER, 2) == wpk.WPK_E_ARG
+    wpk.wpk_destroy(plan)

@@ -61,6 +61,7 @@ extern "C" {
 #define WPK_E_TOKEN (-7)        /* an input token id is outside [0, vocab) (device) */
 #define WPK_E_STATE (-8)        /* plan holds a latched device error; reset it */
 #define WPK_E_NO_GPU (-9)       /* no usable gfx950 device */
+#define WPK_E_IDLE (-10)        /* a persistent grid waited longer than its idle limit for a step and left */
 
 /* ---- data types --------------------------------------------------------------- */
 #define WPK_F32 0               /* float32 weights and KV cache */
@@ -181,6 +182,8 @@ const char* wpk_last_error(const wpk_plan* plan);
                                      last slice in claim order its reducer, which waits for the other
                                      slices' arrivals, instead of the last slice to arrive; device plans
                                      refuse it (a device run of this scheme once faulted, cause unknown) */
+#define WPK_OPT_PERSIST_IDLE_US 10 /* persistent sessions: a grid left this long without a step leaves
+                                      by itself and reports WPK_E_IDLE (default 2,000,000) */
 int32_t wpk_set_option(wpk_plan* plan, int32_t key, int64_t value);
 
 /* Per-tile execution log of the last logged step, one record per tile id.
@@ -252,6 +255,40 @@ int32_t wpk_get_dag(const wpk_plan* plan, int32_t* type, int32_t* layer, int32_t
  * baseline, sharing the megakernel's tile bodies.  The graph is captured on
  * the first wpk_step and re-captured if tokens/kv/logits pointers change. */
 wpk_plan* wpk_build_graph_baseline(const wpk_model_desc* desc, int32_t batch, int32_t ctx_len);
+
+/* ---- cross-step persistence ------------------------------------------------------
+ * Source: "Why real-time inference wants a megakernel", section "The unit of
+ * execution" (the grid of a WPK stays resident across updates instead of
+ * being launched per update) and section "A concrete design: one WPK update"
+ * (the host keeps admission and delivery; the device publishes completion).
+ * A session keeps the megakernel's grid resident and runs one decode step per
+ * step the host rings, with no launch in between: the host writes a doorbell
+ * in pinned host memory, worker 0 turns it into a grant in device memory,
+ * every worker runs the step, and the last worker out advances the epoch and
+ * writes the count of finished steps back to pinned host memory.  Steps chain
+ * their tokens on the device, as with wpk_step (free-running greedy decoding);
+ * tokens, kv and logits are device memory, caller-owned, and must not be
+ * touched by the caller while the session runs.  The grid is launched
+ * cooperatively (all workers co-resident) on `stream`.
+ *
+ * wpk_persist_begin: opens the session (the plan must be idle, with the log
+ *   off); returns WPK_E_STATE if one is open or an error is latched.
+ * wpk_persist_ring: asks for n_steps more steps (non-blocking).
+ * wpk_persist_wait: waits until `steps` of the rung steps have finished;
+ *   WPK_E_TIMEOUT after timeout_us (negative: no limit), WPK_E_STATE if the
+ *   grid has already left.
+ * wpk_persist_end: lets the rung steps finish, stops the grid, waits for it and
+ *   returns its latched status, as wpk_sync does (WPK_E_IDLE if it left after
+ *   the idle limit, WPK_OPT_PERSIST_IDLE_US).  wpk_step and wpk_sync refuse to
+ *   run while a session is open; wpk_destroy ends an open session.
+ * wpk_persist_times: after the session, two s_memrealtime stamps (100 MHz) per
+ *   step into dst[2 * i], dst[2 * i + 1]: when worker 0 saw step i granted and
+ *   when the last worker left it (the first n_steps of a 4096-entry ring). */
+int32_t wpk_persist_begin(wpk_plan* plan, int32_t* tokens, wpk_kv* kv, void* logits, wpk_stream_t stream);
+int32_t wpk_persist_ring(wpk_plan* plan, int32_t n_steps);
+int32_t wpk_persist_wait(wpk_plan* plan, int32_t steps, int64_t timeout_us);
+int32_t wpk_persist_end(wpk_plan* plan);
+int32_t wpk_persist_times(wpk_plan* plan, int64_t* dst, int32_t n_steps);
 
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same

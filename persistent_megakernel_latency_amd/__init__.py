@@ -27,6 +27,7 @@ WPK_E_CTX_FULL = -6
 WPK_E_TOKEN = -7
 WPK_E_STATE = -8
 WPK_E_NO_GPU = -9
+WPK_E_IDLE = -10
 
 WPK_F32 = 0
 WPK_BF16 = 1
@@ -42,6 +43,7 @@ WPK_OPT_PREFETCH = 6
 WPK_OPT_WORKERS = 7
 WPK_OPT_LAUNCH = 8
 WPK_OPT_FIXED_REDUCER = 9
+WPK_OPT_PERSIST_IDLE_US = 10
 
 TILE_TYPES = ["qkv", "attn", "combine", "oproj", "gateup", "down", "lm", "argmax", "norm", "norm2", "normf",
               "attnc"]
@@ -95,6 +97,11 @@ _SIGNATURES = {
     "wpk_get_dag": (_i32, [_vp, _vp, _vp, _vp, _vp]),
     "wpk_build_graph_baseline": (_vp, [ctypes.POINTER(wpk_model_desc), _i32, _i32]),
     "wpk_build_static": (_vp, [ctypes.POINTER(wpk_model_desc), _i32, _i32]),
+    "wpk_persist_begin": (_i32, [_vp, _vp, ctypes.POINTER(wpk_kv), _vp, _vp]),
+    "wpk_persist_ring": (_i32, [_vp, _i32]),
+    "wpk_persist_wait": (_i32, [_vp, _i32, ctypes.c_int64]),
+    "wpk_persist_end": (_i32, [_vp]),
+    "wpk_persist_times": (_i32, [_vp, _vp, _i32]),
     "wpk_build_host": (_vp, [ctypes.POINTER(wpk_model_desc), _i32, _i32, ctypes.POINTER(wpk_build_opts)]),
     "wpk_serial_step": (_i32, [_vp, _vp, ctypes.POINTER(wpk_kv), _vp, ctypes.c_uint64, _i32]),
     "wpk_emulate_step": (_i32, [_vp, _vp, ctypes.POINTER(wpk_kv), _vp, _i32, ctypes.c_uint64]),
@@ -184,6 +191,30 @@ def wpk_build_graph_baseline(desc: wpk_model_desc, batch: int, ctx_len: int):
 
 def wpk_build_static(desc: wpk_model_desc, batch: int, ctx_len: int):
     return lib().wpk_build_static(ctypes.byref(desc), batch, ctx_len)
+
+
+def wpk_persist_begin(plan, tokens_ptr: int, kv: wpk_kv, logits_ptr: int, stream_ptr: int = 0) -> int:
+    return lib().wpk_persist_begin(plan, tokens_ptr, ctypes.byref(kv), logits_ptr, stream_ptr or None)
+
+
+def wpk_persist_ring(plan, n_steps: int) -> int:
+    return lib().wpk_persist_ring(plan, n_steps)
+
+
+def wpk_persist_wait(plan, steps: int, timeout_us: int = -1) -> int:
+    return lib().wpk_persist_wait(plan, steps, timeout_us)
+
+
+def wpk_persist_end(plan) -> int:
+    return lib().wpk_persist_end(plan)
+
+
+def wpk_persist_times(plan, n_steps: int):
+    """(rc, int64 array [n_steps][2]) of s_memrealtime stamps: grant seen, last worker out."""
+    import numpy as np
+    out = np.zeros((n_steps, 2), np.int64)
+    rc = lib().wpk_persist_times(plan, out.ctypes.data, n_steps)
+    return rc, out
 
 
 def wpk_build_host(desc: wpk_model_desc, batch: int, ctx_len: int, opts: Optional[wpk_build_opts] = None):

@@ -8,6 +8,7 @@
 // memory plan once; wpk_step is then a single launch.
 #include <hip/hip_runtime.h>
 
+#include <chrono>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -21,6 +22,7 @@
 
 extern "C" int wpk_dev_kernels(int dtype, int cpr_h, int cpr_f, int wide, const void** mk, const void** mk_log,
                                const void** phase, int* dyn_lds);
+extern "C" int wpk_dev_persist_kernel(int dtype, int cpr_h, int cpr_f, int wide, const void** k);
 extern "C" int wpk_dev_block_threads();
 extern "C" int wpk_dev_static_scratch(int device, void** ptr, size_t* bytes);
 
@@ -46,7 +48,7 @@ int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
 
 struct Layout {
   int64_t ctl, heads, counters, argmax, tiles, qtiles, groups, queue, queue_off, layers, rope_cos, rope_sin, act, log,
-      wpart, fixc, total;
+      wpart, fixc, step_times, total;
 };
 
 Layout layout(const Shape& s, const Dag& d, int32_t max_workers) {
@@ -75,6 +77,7 @@ Layout layout(const Shape& s, const Dag& d, int32_t max_workers) {
   L.log = take((3 * (int64_t)d.tiles.size() + max_workers) * sizeof(wpk_log_rec));
   L.wpart = take((int64_t)d.n_pslots * kWidePart * 4);
   L.fixc = take((int64_t)d.n_fix * kLine * 4);
+  L.step_times = take((int64_t)kPersistTimes * 2 * 8);
   L.total = at;
   return L;
 }
@@ -134,8 +137,9 @@ wpk_plan* build_device(const wpk_model_desc* desc, int32_t batch, int32_t ctx_le
   if (e != hipSuccess) return fail(hip_msg("hipGetDeviceProperties", e));
   if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
     return fail(std::string("built for gfx950, found ") + prop.gcnArchName);
-  const void *mk = nullptr, *mk_log = nullptr, *phase = nullptr;
+  const void *mk = nullptr, *mk_log = nullptr, *phase = nullptr, *persist = nullptr;
   int dyn = 0;
+  (void)wpk_dev_persist_kernel(s.dtype, s.cpr_h, s.cpr_f, s.wide, &persist);
   if (!wpk_dev_kernels(s.dtype, s.cpr_h, s.cpr_f, s.wide, &mk, &mk_log, &phase, &dyn))
     return fail("no kernel instance for this dtype / hidden / ffn / batch (cpr_h=" + std::to_string(s.cpr_h) +
                 ", cpr_f=" + std::to_string(s.cpr_f) + ", wide=" + std::to_string(s.wide) + ")");
@@ -161,6 +165,7 @@ wpk_plan* build_device(const wpk_model_desc* desc, int32_t batch, int32_t ctx_le
   p->k_mega = mk;
   p->k_mega_log = mk_log;
   p->k_phase = phase;
+  p->k_persist = persist;
   p->dyn_lds = dyn;
 
   int per_cu = 0, per_cu_log = 0;
@@ -272,6 +277,9 @@ wpk_plan* build_device(const wpk_model_desc* desc, int32_t batch, int32_t ctx_le
   P.drop_tile = -1;
   P.perturb = 0;
   P.watchdog_ticks = p->watchdog_us * 100;
+  P.persist = 0;
+  P.step_times = (uint64_t*)(w + L.step_times);
+  p->d_step_times = P.step_times;
   p->log.assign(p->dag.tiles.size(), wpk_log_rec{});
   if (baseline) {
     hipStream_t cs;
@@ -352,6 +360,7 @@ int32_t wpk_step(wpk_plan* p, int32_t* tokens, wpk_kv* kv, void* logits, wpk_str
   if (!p) return plan_fail(nullptr, WPK_E_ARG, "null plan");
   if (p->host) return plan_fail(p, WPK_E_ARG, "host plan: use wpk_serial_step / wpk_emulate_step");
   if (p->latched) return plan_fail(p, WPK_E_STATE, "plan holds device error " + std::to_string(p->latched) + "; reset it");
+  if (p->persist_open) return plan_fail(p, WPK_E_STATE, "a persistent session is open on this plan");
   if (!tokens || !kv || !kv->k || !kv->v || !kv->seq_len || !logits)
     return plan_fail(p, WPK_E_ARG, "null tokens, kv or logits");
   if (p->static_ws) {
@@ -403,6 +412,7 @@ int32_t wpk_step(wpk_plan* p, int32_t* tokens, wpk_kv* kv, void* logits, wpk_str
 int32_t wpk_sync(wpk_plan* p) {
   if (!p) return plan_fail(nullptr, WPK_E_ARG, "null plan");
   if (p->host) return WPK_OK;
+  if (p->persist_open) return plan_fail(p, WPK_E_STATE, "a persistent session is open: use wpk_persist_end");
   hipError_t e = hipStreamSynchronize((hipStream_t)p->last_stream);
   if (e != hipSuccess) return plan_fail(p, WPK_E_HIP, hip_msg("hipStreamSynchronize", e));
   uint32_t st[4];
@@ -439,6 +449,8 @@ int32_t wpk_sync(wpk_plan* p) {
 
 void wpk_destroy(wpk_plan* p) {
   if (!p) return;
+  if (p->persist_open) (void)wpk_persist_end(p);
+  if (p->host_words) (void)hipHostFree(p->host_words);
   if (p->graph_exec) (void)hipGraphExecDestroy((hipGraphExec_t)p->graph_exec);
   if (p->graph) (void)hipGraphDestroy((hipGraph_t)p->graph);
   if (p->cap_stream) (void)hipStreamDestroy((hipStream_t)p->cap_stream);
@@ -484,6 +496,10 @@ int32_t wpk_set_option(wpk_plan* p, int32_t key, int64_t value) {
     case WPK_OPT_LAUNCH:
       if (value != 0 && value != 1) return plan_fail(p, WPK_E_ARG, "launch must be 0 or 1");
       p->cooperative = (int32_t)value;
+      return WPK_OK;
+    case WPK_OPT_PERSIST_IDLE_US:
+      if (value <= 0) return plan_fail(p, WPK_E_ARG, "idle limit must be positive");
+      p->persist_idle_us = (uint64_t)value;
       return WPK_OK;
     case WPK_OPT_FIXED_REDUCER:
       if (!p->host) return plan_fail(p, WPK_E_ARG, "the fixed reducer is an option of the host emulator only");
@@ -590,6 +606,119 @@ int32_t wpk_debug_read_act(wpk_plan* p, void* dst, size_t bytes, size_t* out_byt
   hipError_t e = hipDeviceSynchronize();
   if (e == hipSuccess) e = hipMemcpy(dst, p->P.act, need, hipMemcpyDeviceToHost);
   if (e != hipSuccess) return plan_fail(p, WPK_E_HIP, hip_msg("activation read", e));
+  return WPK_OK;
+}
+
+// ---- cross-step persistence ---------------------------------------------------------------
+
+int32_t wpk_persist_begin(wpk_plan* p, int32_t* tokens, wpk_kv* kv, void* logits, wpk_stream_t stream) {
+  if (!p) return plan_fail(nullptr, WPK_E_ARG, "null plan");
+  if (p->host || p->baseline) return plan_fail(p, WPK_E_ARG, "persistent sessions run megakernel device plans");
+  if (!p->k_persist)
+    return plan_fail(p, WPK_E_ARG, "persistent sessions are built for batches up to 4 (no matrix-core instance)");
+  if (p->persist_open) return plan_fail(p, WPK_E_STATE, "a persistent session is already open");
+  if (p->latched) return plan_fail(p, WPK_E_STATE, "plan holds device error " + std::to_string(p->latched) + "; reset it");
+  if (p->log_on) return plan_fail(p, WPK_E_ARG, "the per-tile log records one step: switch it off first");
+  if (!tokens || !kv || !kv->k || !kv->v || !kv->seq_len || !logits)
+    return plan_fail(p, WPK_E_ARG, "null tokens, kv or logits");
+  if (p->static_ws) {
+    std::lock_guard<std::mutex> lk(g_owner_mu);
+    if (g_scratch_owner[p->device] != p)
+      return plan_fail(p, WPK_E_STATE, "the static scratch now holds a later static plan's workspace");
+  }
+  hipError_t e = hipSuccess;
+  if (!p->host_words) {
+    e = hipHostMalloc((void**)&p->host_words, 512, hipHostMallocCoherent | hipHostMallocMapped);
+    if (e != hipSuccess) return plan_fail(p, WPK_E_NOMEM, hip_msg("hipHostMalloc doorbell", e));
+  }
+  // the plan is idle: its last step (if any) is finished
+  if (p->last_stream) {
+    e = hipStreamSynchronize((hipStream_t)p->last_stream);
+    if (e != hipSuccess) return plan_fail(p, WPK_E_HIP, hip_msg("hipStreamSynchronize", e));
+  }
+  uint32_t epoch = 0;
+  e = hipMemcpy(&epoch, p->P.ctl + CTL_EPOCH, 4, hipMemcpyDeviceToHost);
+  if (e == hipSuccess) e = hipMemcpy(p->P.ctl + CTL_GO, &epoch, 4, hipMemcpyHostToDevice);  // nothing granted yet
+  if (e != hipSuccess) return plan_fail(p, WPK_E_HIP, hip_msg("session setup", e));
+  __atomic_store_n(&p->host_words[0], 0u, __ATOMIC_RELEASE);
+  __atomic_store_n(&p->host_words[64], 0u, __ATOMIC_RELEASE);
+  p->persist_requested = 0;
+  Params P = p->P;
+  P.tokens = tokens;
+  P.seq_len = kv->seq_len;
+  P.logits = (float*)logits;
+  P.kc = (char*)kv->k;
+  P.vc = (char*)kv->v;
+  P.log_on = 0;
+  P.persist = 1;
+  P.persist_base = epoch;
+  uint32_t* dev_words = nullptr;
+  e = hipHostGetDevicePointer((void**)&dev_words, p->host_words, 0);
+  if (e != hipSuccess || !dev_words) return plan_fail(p, WPK_E_HIP, hip_msg("hipHostGetDevicePointer", e));
+  P.host_bell = dev_words;
+  P.host_done = dev_words + 64;
+  P.idle_ticks = p->persist_idle_us * 100;
+  void* args[] = {(void*)&P};
+  // every worker waits for every other at each step boundary: the grid must
+  // be co-resident, which a cooperative launch guarantees (or refuses)
+  e = hipLaunchCooperativeKernel(p->k_persist, dim3(p->workers), dim3(wpk_dev_block_threads()), args, p->dyn_lds,
+                                 (hipStream_t)stream);
+  if (e != hipSuccess) return plan_fail(p, WPK_E_HIP, hip_msg("persistent launch", e));
+  p->last_stream = stream;
+  p->persist_open = true;
+  return WPK_OK;
+}
+
+int32_t wpk_persist_ring(wpk_plan* p, int32_t n_steps) {
+  if (!p) return plan_fail(nullptr, WPK_E_ARG, "null plan");
+  if (!p->persist_open) return plan_fail(p, WPK_E_STATE, "no persistent session is open");
+  if (n_steps <= 0 || (uint64_t)p->persist_requested + (uint64_t)n_steps >= kBellStop)
+    return plan_fail(p, WPK_E_ARG, "n_steps must be positive");
+  p->persist_requested += (uint32_t)n_steps;
+  __atomic_store_n(&p->host_words[0], p->persist_requested, __ATOMIC_RELEASE);
+  return WPK_OK;
+}
+
+int32_t wpk_persist_wait(wpk_plan* p, int32_t steps, int64_t timeout_us) {
+  if (!p) return plan_fail(nullptr, WPK_E_ARG, "null plan");
+  if (!p->persist_open) return plan_fail(p, WPK_E_STATE, "no persistent session is open");
+  if (steps < 0 || (uint32_t)steps > p->persist_requested)
+    return plan_fail(p, WPK_E_ARG, "can only wait for steps that were rung");
+  const auto t0 = std::chrono::steady_clock::now();
+  for (uint64_t k = 0;; ++k) {
+    if (__atomic_load_n(&p->host_words[64], __ATOMIC_ACQUIRE) >= (uint32_t)steps) return WPK_OK;
+    if ((k & 1023u) == 1023u) {
+      // the grid left early (an error, or its idle limit): report it
+      if (hipStreamQuery((hipStream_t)p->last_stream) == hipSuccess) {
+        if (__atomic_load_n(&p->host_words[64], __ATOMIC_ACQUIRE) >= (uint32_t)steps) return WPK_OK;
+        return plan_fail(p, WPK_E_STATE, "the persistent grid has left; wpk_persist_end reports why");
+      }
+      if (timeout_us >= 0 &&
+          std::chrono::steady_clock::now() - t0 > std::chrono::microseconds(timeout_us))
+        return plan_fail(p, WPK_E_TIMEOUT, "persistent steps not done within the timeout");
+    }
+  }
+}
+
+int32_t wpk_persist_end(wpk_plan* p) {
+  if (!p) return plan_fail(nullptr, WPK_E_ARG, "null plan");
+  if (!p->persist_open) return plan_fail(p, WPK_E_STATE, "no persistent session is open");
+  // the steps already rung run first; then the stop bell
+  (void)wpk_persist_wait(p, (int32_t)p->persist_requested, (int64_t)(p->persist_idle_us + p->watchdog_us) * 4);
+  __atomic_store_n(&p->host_words[0], kBellStop, __ATOMIC_RELEASE);
+  p->persist_open = false;
+  hipError_t e = hipStreamSynchronize((hipStream_t)p->last_stream);
+  if (e != hipSuccess) return plan_fail(p, WPK_E_HIP, hip_msg("hipStreamSynchronize", e));
+  return wpk_sync(p);
+}
+
+int32_t wpk_persist_times(wpk_plan* p, int64_t* dst, int32_t n_steps) {
+  if (!p || !dst) return plan_fail(p, WPK_E_ARG, "null argument");
+  if (p->host || !p->d_step_times) return plan_fail(p, WPK_E_ARG, "device plans only");
+  if (p->persist_open) return plan_fail(p, WPK_E_STATE, "end the persistent session first");
+  if (n_steps < 0 || n_steps > kPersistTimes) return plan_fail(p, WPK_E_ARG, "at most 4096 steps are kept");
+  hipError_t e = hipMemcpy(dst, p->d_step_times, (size_t)n_steps * 16, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return plan_fail(p, WPK_E_HIP, hip_msg("step times read", e));
   return WPK_OK;
 }
 

@@ -84,8 +84,15 @@ enum : int32_t {
   CTL_EXIT = 64,     // workers that left the current step
   CTL_STATUS = 128,  // [0] error code, [1] tile, [2] worker, [3] epoch
   CTL_ABORT = 192,   // nonzero: every worker stops
-  CTL_WORDS = 256
+  CTL_GO = 256,      // persistent grids: steps granted so far (an epoch), or kGoStop
+  CTL_WORDS = 320
 };
+
+// Persistent grids: CTL_GO value that makes every worker leave, and the host
+// doorbell value that asks for it.
+constexpr uint32_t kGoStop = 0xFFFFFFFFu;
+constexpr uint32_t kBellStop = 0xFFFFFFFFu;
+constexpr int kPersistTimes = 4096;  // per-step device times kept (a ring)
 
 // Per-layer pointers: weights (caller-owned) and this layer's activations.
 // Field order matters to the wide kernels, which index runs of consecutive
@@ -178,6 +185,17 @@ struct Params {
   int32_t log_on, prefetch, drop_tile;
   uint32_t perturb;
   uint64_t watchdog_ticks;  // s_memrealtime ticks (100 MHz)
+  // Cross-step persistence: with persist set the grid stays resident and runs
+  // one step per grant.  The host rings host_bell (pinned host memory: the
+  // number of steps it has asked for since the session began, or kBellStop);
+  // worker 0 relays it to CTL_GO as the absolute epoch persist_base + bell;
+  // the last worker out of each step publishes the steps done to host_done.
+  int32_t persist;
+  uint32_t persist_base;
+  const uint32_t* host_bell;
+  uint32_t* host_done;
+  uint64_t idle_ticks;      // a grid left without a grant this long stops by itself
+  uint64_t* step_times;     // [kPersistTimes][2]: grant seen, last worker out (s_memrealtime)
 };
 
 }  // namespace wpk

@@ -52,6 +52,12 @@ struct wpk_plan {
   int32_t latched = 0;              // device error seen by wpk_sync
   int32_t log_on = 0, prefetch = 1, drop_tile = -1, cooperative = 0;
   int32_t emu_fixed_reducer = 0;    // host emulator: fixed reducer per wide row block (WPK_OPT_FIXED_REDUCER)
+  // cross-step persistence (wpk_persist_*)
+  bool persist_open = false;
+  uint32_t* host_words = nullptr;   // pinned host memory: [0] doorbell, [64] steps done
+  uint32_t persist_requested = 0;   // steps rung since the session began
+  uint64_t persist_idle_us = 2000000;
+  uint64_t* d_step_times = nullptr; // inside the workspace: [kPersistTimes][2]
   uint32_t perturb = 0;
   uint64_t watchdog_us = 2000000;
   int64_t weight_bytes = 0;
@@ -70,6 +76,7 @@ struct wpk_plan {
   const void* k_mega = nullptr;     // kernel handles
   const void* k_mega_log = nullptr;
   const void* k_phase = nullptr;
+  const void* k_persist = nullptr;  // persistent grid kernel (narrow plans only)
   int dyn_lds = 0;                  // dynamic LDS bytes of the kernels (wide plans)
   void* last_stream = nullptr;
   // baseline graph

@@ -1,0 +1,100 @@
+"""Cross-step persistence: one resident grid running the steps the host rings
+(wpk_persist_*), through the C ABI, against the same steps launched one by one
+(wpk_step).  The kernels and their arithmetic are the same, so the final
+state -- K/V cache, sequence lengths, greedy tokens, last logits -- must be
+bitwise equal.  Also: the idle limit ends a session nobody rings, and a plan
+refuses ordinary steps while a session is open."""
+import numpy as np
+import pytest
+
+import oracle
+import persistent_megakernel_latency_amd as wpk
+import synth
+from tests.gpu_helpers import GpuPlan, announce
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(name):
+    if name == "tiny-b1":
+        cfg = synth.TINY
+        lens = np.array([40], np.int32)
+        tok = np.array([5], np.int32)
+        cap = 80
+    elif name == "mini-b3":
+        cfg = synth.MINI
+        lens = np.array([63, 150, 5], np.int32)
+        tok = np.array([11, 500, 999], np.int32)
+        cap = 200
+    else:  # matrix-core plan with an inactive slot
+        cfg = synth.MINI
+        lens = np.array([63, 64, 1, 100, -1, 128, 90, 7], np.int32)
+        tok = (np.arange(8, dtype=np.int32) * 113 + 5) % cfg.vocab
+        cap = 160
+    w = synth.make_weights(cfg, gain_std=0.1)
+    kc, vc = synth.synthetic_kv(cfg, len(lens), cap, np.maximum(lens, 0))
+    return cfg, w, kc, vc, lens, tok, cap
+
+
+@pytest.mark.parametrize("name", ["tiny-b1", "mini-b3"])
+def test_persistent_session_equals_launched_steps(name):
+    cfg, w, kc, vc, lens, tok, cap = _case(name)
+    batch = len(lens)
+    launched = GpuPlan(cfg, w, batch, cap, kc, vc, lens, tok)
+    for s in range(8):
+        announce(f"persist {name}: launched step {s}")
+        launched.step()
+    g = GpuPlan(cfg, w, batch, cap, kc, vc, lens, tok, desc=launched.desc)
+    g.step()  # one ordinary step first: the session starts from a later epoch
+    announce(f"persist {name}: session")
+    wpk.check(wpk.wpk_persist_begin(g.plan, g.tokens.data_ptr(), g.kv, g.logits.data_ptr(), 0), g.plan, "begin")
+    assert wpk.wpk_step(g.plan, g.tokens.data_ptr(), g.kv, g.logits.data_ptr(), 0) == wpk.WPK_E_STATE
+    wpk.check(wpk.wpk_persist_ring(g.plan, 3), g.plan, "ring")
+    wpk.check(wpk.wpk_persist_wait(g.plan, 3, 10_000_000), g.plan, "wait 3")
+    wpk.check(wpk.wpk_persist_ring(g.plan, 4), g.plan, "ring")
+    wpk.check(wpk.wpk_persist_wait(g.plan, 7, 10_000_000), g.plan, "wait 7")
+    wpk.check(wpk.wpk_persist_end(g.plan), g.plan, "end")
+    for x, y in zip(launched.state(), g.state()):
+        assert np.array_equal(x, y)
+    rc, times = wpk.wpk_persist_times(g.plan, 7)
+    assert rc == 0
+    assert np.all(times[:, 1] > times[:, 0]) and np.all(np.diff(times[:, 0]) > 0)
+    assert np.all(times[1:, 0] >= times[:-1, 1])  # each step starts after the previous one ended
+    # ordinary steps work again after the session
+    launched.step()
+    g.step()
+    for x, y in zip(launched.state(), g.state()):
+        assert np.array_equal(x, y)
+    launched.close()
+    g.close()
+
+
+def test_matrix_core_plans_refuse_persistent_sessions():
+    """Batches above four have no persistent instance (a matrix-core kernel
+    compiled with the persistent round loop faulted the device once, cause not
+    found; that kernel is not built), so the session is refused before any
+    launch."""
+    cfg, w, kc, vc, lens, tok, cap = _case("mini-wide-b8")
+    g = GpuPlan(cfg, w, len(lens), cap, kc, vc, lens, tok)
+    rc = wpk.wpk_persist_begin(g.plan, g.tokens.data_ptr(), g.kv, g.logits.data_ptr(), 0)
+    assert rc == wpk.WPK_E_ARG and "batches up to 4" in wpk.wpk_last_error(g.plan)
+    g.close()
+
+
+def test_persistent_session_idle_limit_and_reset():
+    cfg, w, kc, vc, lens, tok, cap = _case("tiny-b1")
+    g = GpuPlan(cfg, w, 1, cap, kc, vc, lens, tok)
+    wpk.check(wpk.wpk_set_option(g.plan, wpk.WPK_OPT_PERSIST_IDLE_US, 20000), g.plan)
+    announce("persist idle limit")
+    wpk.check(wpk.wpk_persist_begin(g.plan, g.tokens.data_ptr(), g.kv, g.logits.data_ptr(), 0), g.plan, "begin")
+    # nobody rings: the grid leaves by itself after 20 ms
+    assert wpk.wpk_persist_end(g.plan) == wpk.WPK_E_IDLE
+    assert "-10" in wpk.wpk_last_error(g.plan)
+    wpk.check(wpk.wpk_set_option(g.plan, wpk.WPK_OPT_RESET, 1), g.plan)
+    ref = GpuPlan(cfg, w, 1, cap, kc, vc, lens, tok, desc=g.desc)
+    g.step()
+    ref.step()
+    for x, y in zip(ref.state(), g.state()):
+        assert np.array_equal(x, y)
+    ref.close()
+    g.close()

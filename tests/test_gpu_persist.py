@@ -4,6 +4,8 @@
 state -- K/V cache, sequence lengths, greedy tokens, last logits -- must be
 bitwise equal.  Also: the idle limit ends a session nobody rings, and a plan
 refuses ordinary steps while a session is open."""
+import time
+
 import numpy as np
 import pytest
 
@@ -87,7 +89,10 @@ def test_persistent_session_idle_limit_and_reset():
     wpk.check(wpk.wpk_set_option(g.plan, wpk.WPK_OPT_PERSIST_IDLE_US, 20000), g.plan)
     announce("persist idle limit")
     wpk.check(wpk.wpk_persist_begin(g.plan, g.tokens.data_ptr(), g.kv, g.logits.data_ptr(), 0), g.plan, "begin")
-    # nobody rings: the grid leaves by itself after 20 ms
+    # nobody rings: the grid leaves by itself after 20 ms, which a wait for a
+    # step that was never rung notices
+    time.sleep(0.3)
+    assert wpk.wpk_persist_wait(g.plan, 0, 1000) == wpk.WPK_OK  # nothing was asked for
     assert wpk.wpk_persist_end(g.plan) == wpk.WPK_E_IDLE
     assert "-10" in wpk.wpk_last_error(g.plan)
     wpk.check(wpk.wpk_set_option(g.plan, wpk.WPK_OPT_RESET, 1), g.plan)

@@ -14,13 +14,14 @@ bracketed by HIP events on the stream it runs on.  The same K steps are then
 repeated R-1 more times from the same starting state (sequence lengths and
 tokens reset, the same K/V positions rewritten), so the per-launch latency
 distribution has R*K samples.  The per-operator hipGraph baseline runs the same
-blocks, the ablations (Table I features switched off one at a time) run one
+blocks; at batch 1 the same K steps also run in one persistent session (the
+grid kept resident, steps rung from the host) under "persistent"; the ablations (Table I features switched off one at a time) run one
 block each, and the CPU oracle is timed on a bounded sample of the same
 workload.  A second workload, batch 32 with per-sequence contexts drawn from
 U{256..1024} (the matrix-core path), is reported under "batch32".
 
     python bench.py [--steps 64] [--warmup 3] [--reps 5] [--no-cpu] [--no-baseline]
-                    [--no-batch32] [--no-ablations]
+                    [--no-batch32] [--no-ablations] [--no-persistent]
 """
 from __future__ import annotations
 
@@ -153,6 +154,8 @@ def measure(wpk, W: Workload, desc, args, baseline: bool, ablations):
         out["baseline"] = {"value": round(bb[0][0] / args.steps * 1e6, 2), "unit": "µs/step",
                            "latency_us": lat(bper),
                            "megakernel_speedup": round(float(bper.mean() / out["per"].mean()), 3)}
+    if W.batch <= 4 and not args.no_persistent:
+        out["persistent"] = persistent_block(wpk, W, desc, args, out["per"])
     res = {}
     for name, opts, option in ablations:
         p = wpk.wpk_build_ex(desc.desc, W.batch, W.cap, opts)
@@ -169,6 +172,36 @@ def measure(wpk, W: Workload, desc, args, baseline: bool, ablations):
     if res:
         out["ablations"] = res
     return out
+
+
+def persistent_block(wpk, W: Workload, desc, args, launched_per):
+    """The same K steps run by one resident grid (a persistent session): the
+    host rings all K at once after W warmup steps and waits for the count of
+    finished steps in pinned host memory; the device stamps each step (grant
+    seen, last worker out)."""
+    plan = wpk.wpk_build(desc.desc, W.batch, W.cap)
+    if not plan:
+        raise RuntimeError("wpk_build: " + wpk.wpk_last_error(None))
+    W.reset()
+    wpk.check(wpk.wpk_persist_begin(plan, W.tokens.data_ptr(), W.kv, W.logits.data_ptr(), W.stream.cuda_stream),
+              plan, "persist begin")
+    wpk.check(wpk.wpk_persist_ring(plan, args.warmup), plan, "ring")
+    wpk.check(wpk.wpk_persist_wait(plan, args.warmup, 60_000_000), plan, "wait")
+    t0 = time.perf_counter()
+    wpk.check(wpk.wpk_persist_ring(plan, args.steps), plan, "ring")
+    wpk.check(wpk.wpk_persist_wait(plan, args.warmup + args.steps, 60_000_000), plan, "wait")
+    wall = time.perf_counter() - t0
+    wpk.check(wpk.wpk_persist_end(plan), plan, "persist end")
+    rc, t = wpk.wpk_persist_times(plan, args.warmup + args.steps)
+    wpk.check(rc, plan, "persist times")
+    wpk.wpk_destroy(plan)
+    t = t[args.warmup:].astype(np.float64) / 100.0  # s_memrealtime ticks (100 MHz) -> µs
+    dev = t[:, 1] - t[:, 0]
+    gaps = t[1:, 0] - t[:-1, 1]
+    return {"value": round(wall / args.steps * 1e6, 2), "unit": "µs/step",
+            "device_step_us": lat(dev), "step_boundary_us": lat(gaps) if gaps.size else None,
+            "vs_launched_event_mean": round(float(launched_per.mean() / (wall / args.steps * 1e6)), 3),
+            "how": "one cooperative grid for all steps; K steps rung at once; host waits on pinned memory"}
 
 
 def roofline(byts, per, shash, kernel_key, traffic_name):
@@ -237,6 +270,8 @@ def run(args):
     result["roofline"] = rl
     if "baseline" in m:
         result["graph_baseline"] = m["baseline"]
+    if "persistent" in m:
+        result["persistent"] = m["persistent"]
     if "ablations" in m:
         result["ablations"] = m["ablations"]
     del W1
@@ -310,6 +345,7 @@ def main():
     ap.add_argument("--no-baseline", action="store_true")
     ap.add_argument("--no-batch32", action="store_true")
     ap.add_argument("--no-ablations", action="store_true")
+    ap.add_argument("--no-persistent", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args()
     if args.gpus != 1:

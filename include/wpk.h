@@ -307,6 +307,46 @@ int32_t wpk_persist_times(wpk_plan* plan, int64_t* dst, int32_t n_steps);
 #define WPK_STATIC_SCRATCH_BYTES (32u << 20)
 wpk_plan* wpk_build_static(const wpk_model_desc* desc, int32_t batch, int32_t ctx_len);
 
+/* ---- planner: the step time of a candidate design, predicted ----------------------
+ * Source: "One Megakernel is Not Enough: Predicting Where to Cut for Streaming
+ * Inference" -- the abstract and Table I: a planner takes per-operator
+ * profiles, simulates the tile and event graph of each candidate design under
+ * the modelled features (tile-to-tile readiness edges vs barrier edges,
+ * weight prefetch into a one-slot staging buffer, the worker count W, kernel
+ * boundaries of the conventional design) and picks the fastest.
+ * wpk_simulate runs that simulation on the plan's own DAG and claim queues
+ * (build it with the options of the candidate: barrier_edges, queue count;
+ * a host plan is enough).  Costs are per tile type (indices of wpk_get_dag's
+ * types), in microseconds: input staging after the wait, compute once the
+ * weights are in, epilogue through the publish.  positions: host int32[batch],
+ * the sequence lengths at step start (attention tiles stream the K/V of the
+ * chunks holding positions; NULL counts none).  The conventional design
+ * (conventional = 1) runs each operator as one kernel over `workers`
+ * workgroups, separated by launch_gap_us, with no hops.  Returns WPK_E_ARG on a
+ * bad parameter; deterministic; host only. */
+#define WPK_SIM_TYPES 12
+typedef struct wpk_sim_params {
+  double hbm_GBps;           /* streaming bandwidth (one first-come server) */
+  double load_latency_us;    /* latency of a staged load, on top of its streaming time */
+  double hop_us;             /* last producer's publish to the consumer seeing its group complete */
+  double launch_gap_us;      /* conventional design: between two operators' kernels */
+  int32_t workers;           /* W (at least the plan's queue count) */
+  int32_t prefetch;          /* 1: weights load when the slot frees; 0: once the inputs are complete */
+  int32_t conventional;      /* 1: one kernel per operator instead of the megakernel */
+  int32_t pad;
+  double stage_us[WPK_SIM_TYPES];
+  double compute_us[WPK_SIM_TYPES];
+  double epilogue_us[WPK_SIM_TYPES];
+} wpk_sim_params;
+typedef struct wpk_sim_result {
+  double step_us;            /* predicted step time (last publish or last kernel end) */
+  double hbm_bytes;          /* bytes the simulated step streamed */
+  double achieved_GBps;      /* hbm_bytes / step_us */
+  double worker_busy_frac;   /* share of worker time between a tile's start and its publish */
+} wpk_sim_result;
+int32_t wpk_simulate(const wpk_plan* plan, const wpk_sim_params* params, const int32_t* positions,
+                     wpk_sim_result* out);
+
 /* ---- host-side executors (no GPU) ----------------------------------------------
  * wpk_build_host compiles the same DAG for a model in HOST memory.
  * wpk_serial_step runs one step's tiles on the CPU, one at a time, in a

@@ -83,6 +83,21 @@ class wpk_plan_info(ctypes.Structure):
                 ("attn_chunk", _i32), ("workspace_bytes", ctypes.c_int64), ("weight_bytes", ctypes.c_int64)]
 
 
+WPK_SIM_TYPES = 12
+
+
+class wpk_sim_params(ctypes.Structure):
+    _fields_ = [("hbm_GBps", ctypes.c_double), ("load_latency_us", ctypes.c_double), ("hop_us", ctypes.c_double),
+                ("launch_gap_us", ctypes.c_double), ("workers", _i32), ("prefetch", _i32), ("conventional", _i32),
+                ("pad", _i32), ("stage_us", ctypes.c_double * WPK_SIM_TYPES),
+                ("compute_us", ctypes.c_double * WPK_SIM_TYPES), ("epilogue_us", ctypes.c_double * WPK_SIM_TYPES)]
+
+
+class wpk_sim_result(ctypes.Structure):
+    _fields_ = [("step_us", ctypes.c_double), ("hbm_bytes", ctypes.c_double), ("achieved_GBps", ctypes.c_double),
+                ("worker_busy_frac", ctypes.c_double)]
+
+
 # Every symbol include/wpk.h declares, with its ctypes signature.
 _SIGNATURES = {
     "wpk_build": (_vp, [ctypes.POINTER(wpk_model_desc), _i32, _i32]),
@@ -97,6 +112,7 @@ _SIGNATURES = {
     "wpk_get_dag": (_i32, [_vp, _vp, _vp, _vp, _vp]),
     "wpk_build_graph_baseline": (_vp, [ctypes.POINTER(wpk_model_desc), _i32, _i32]),
     "wpk_build_static": (_vp, [ctypes.POINTER(wpk_model_desc), _i32, _i32]),
+    "wpk_simulate": (_i32, [_vp, ctypes.POINTER(wpk_sim_params), _vp, ctypes.POINTER(wpk_sim_result)]),
     "wpk_persist_begin": (_i32, [_vp, _vp, ctypes.POINTER(wpk_kv), _vp, _vp]),
     "wpk_persist_ring": (_i32, [_vp, _i32]),
     "wpk_persist_wait": (_i32, [_vp, _i32, ctypes.c_int64]),
@@ -191,6 +207,18 @@ def wpk_build_graph_baseline(desc: wpk_model_desc, batch: int, ctx_len: int):
 
 def wpk_build_static(desc: wpk_model_desc, batch: int, ctx_len: int):
     return lib().wpk_build_static(ctypes.byref(desc), batch, ctx_len)
+
+
+def wpk_simulate(plan, params: wpk_sim_params, positions=None):
+    """(rc, wpk_sim_result) of the simulated step; positions: int32 per sequence or None."""
+    import numpy as np
+    res = wpk_sim_result()
+    ptr = None
+    if positions is not None:
+        positions = np.ascontiguousarray(positions, dtype=np.int32)
+        ptr = positions.ctypes.data
+    rc = lib().wpk_simulate(plan, ctypes.byref(params), ptr, ctypes.byref(res))
+    return rc, res
 
 
 def wpk_persist_begin(plan, tokens_ptr: int, kv: wpk_kv, logits_ptr: int, stream_ptr: int = 0) -> int:

@@ -28,7 +28,7 @@ HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-D__HIP_PLATFORM_AMD__",
               "-I" + os.path.join(ROOT, "include"), "-I" + CSRC, "-I/opt/rocm/include"]
 
 DEVICE_SOURCES = ["megakernel.hip", "persist.hip"]
-HOST_SOURCES = ["capi.cpp", "builder.cpp", "host_exec.cpp"]
+HOST_SOURCES = ["capi.cpp", "builder.cpp", "host_exec.cpp", "planner.cpp"]
 
 
 def _run(cmd):

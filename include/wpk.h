@@ -318,7 +318,8 @@ wpk_plan* wpk_build_static(const wpk_model_desc* desc, int32_t batch, int32_t ct
  * (build it with the options of the candidate: barrier_edges, queue count;
  * a host plan is enough).  Costs are per tile type (indices of wpk_get_dag's
  * types), in microseconds: input staging after the wait, compute once the
- * weights are in, epilogue through the publish.  positions: host int32[batch],
+ * weights are in, epilogue through the publish, and for matrix-core plans the
+ * row-block reduction of the last K slice.  positions: host int32[batch],
  * the sequence lengths at step start (attention tiles stream the K/V of the
  * chunks holding positions; NULL counts none).  The conventional design
  * (conventional = 1) runs each operator as one kernel over `workers`
@@ -337,6 +338,8 @@ typedef struct wpk_sim_params {
   double stage_us[WPK_SIM_TYPES];
   double compute_us[WPK_SIM_TYPES];
   double epilogue_us[WPK_SIM_TYPES];
+  double reduce_us[WPK_SIM_TYPES];  /* matrix-core plans: added to the epilogue of the K slice whose
+                                       arrival completes its row block (it adds up the others) */
 } wpk_sim_params;
 typedef struct wpk_sim_result {
   double step_us;            /* predicted step time (last publish or last kernel end) */

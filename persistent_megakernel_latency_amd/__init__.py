@@ -90,7 +90,8 @@ class wpk_sim_params(ctypes.Structure):
     _fields_ = [("hbm_GBps", ctypes.c_double), ("load_latency_us", ctypes.c_double), ("hop_us", ctypes.c_double),
                 ("launch_gap_us", ctypes.c_double), ("workers", _i32), ("prefetch", _i32), ("conventional", _i32),
                 ("pad", _i32), ("stage_us", ctypes.c_double * WPK_SIM_TYPES),
-                ("compute_us", ctypes.c_double * WPK_SIM_TYPES), ("epilogue_us", ctypes.c_double * WPK_SIM_TYPES)]
+                ("compute_us", ctypes.c_double * WPK_SIM_TYPES), ("epilogue_us", ctypes.c_double * WPK_SIM_TYPES),
+                ("reduce_us", ctypes.c_double * WPK_SIM_TYPES)]
 
 
 class wpk_sim_result(ctypes.Structure):

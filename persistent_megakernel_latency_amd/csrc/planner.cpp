@@ -119,6 +119,7 @@ struct Sim {
   std::vector<int32_t> remaining;         // per group: publishes still missing
   std::vector<double> done_at;            // per group: completion time
   std::vector<std::vector<int>> waiters;  // per group: workers whose next tile waits on it
+  std::vector<int32_t> arrivals;          // matrix-core plans: K slices started, per row block
   std::priority_queue<Event, std::vector<Event>, std::greater<Event>> ev;
   uint64_t seq = 0;
   void push(double t, int kind, int w, size_t k) { ev.push(Event{t, kind, w, k, seq++}); }
@@ -134,6 +135,15 @@ struct Sim {
   bool barrier_c(const Tile& t) const {
     const bool gemm = t.type == T_QKV || t.type == T_OPROJ || t.type == T_GATEUP || t.type == T_DOWN || t.type == T_LM;
     return !(t.type == T_LM || (s.wide && gemm));
+  }
+
+  // A matrix-core K slice's share of its row block's reduction: the slice
+  // that arrives last (here: starts last) adds up the others.
+  double reduction(const Tile& T) {
+    if (!s.wide || T.fix < 0 || T.fix >= (int32_t)arrivals.size() || T.b <= 1) return 0.0;
+    const bool gemm = T.type == T_QKV || T.type == T_OPROJ || T.type == T_GATEUP || T.type == T_DOWN || T.type == T_LM;
+    if (!gemm) return 0.0;
+    return ++arrivals[T.fix] == T.b ? cost(sp.reduce_us, T.type) : 0.0;
   }
 
   void schedule_top(int w, size_t k) {
@@ -189,6 +199,7 @@ struct Sim {
     done_at.assign(d.groups.size(), 0.0);
     waiters.assign(d.groups.size(), {});
     for (size_t g = 0; g < d.groups.size(); ++g) remaining[g] = d.groups[g].producers;
+    arrivals.assign(d.n_fix, 0);
     for (int w = 0; w < sp.workers; ++w) {
       ws[w].q = w % nq;
       push(0.0, CLAIM, w, 0);
@@ -224,7 +235,7 @@ struct Sim {
           }
           const double in = e.t + cost(sp.stage_us, T.type);
           r.c1 = std::max(in, r.load_end) + cost(sp.compute_us, T.type);
-          r.pub = r.c1 + cost(sp.epilogue_us, T.type);
+          r.pub = r.c1 + cost(sp.epilogue_us, T.type) + reduction(T);
           busy += r.pub - e.t;
           W.slot_free = barrier_c(T) ? r.pub : r.c1;
           W.slot_known = true;
@@ -250,6 +261,7 @@ struct Sim {
   }
 
   void run_conventional() {
+    arrivals.assign(d.n_fix, 0);
     double t = 0;
     for (const auto& ph : d.phases) {
       t += sp.launch_gap_us;
@@ -264,7 +276,8 @@ struct Sim {
         bytes += b;
         const double le = hbm.load(ts, b);
         const double in = ts + cost(sp.stage_us, T.type);
-        const double te = std::max(in, le) + cost(sp.compute_us, T.type) + cost(sp.epilogue_us, T.type);
+        const double te = std::max(in, le) + cost(sp.compute_us, T.type) + cost(sp.epilogue_us, T.type) +
+                          reduction(T);
         busy += te - ts;
         slots.push(te);
         phase_end = std::max(phase_end, te);

@@ -133,6 +133,11 @@ class Workload:
         return wall, per, byts
 
 
+def progress(msg: str) -> None:
+    """A progress line on stderr (the JSON line stays alone on stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def measure(wpk, W: Workload, desc, args, baseline: bool, ablations):
     """The timed block (value), R-1 repeated blocks for the latency
     distribution, the graph baseline's blocks and one block per ablation."""
@@ -141,6 +146,7 @@ def measure(wpk, W: Workload, desc, args, baseline: bool, ablations):
         raise RuntimeError("wpk_build: " + wpk.wpk_last_error(None))
     info = wpk.wpk_get_info(plan)
     blocks = [W.block(plan, args.warmup, args.steps, "megakernel") for _ in range(args.reps)]
+    progress(f"batch {W.batch}: megakernel, {args.reps} x {args.steps} steps")
     wpk.wpk_destroy(plan)
     out = {"wall": blocks[0][0], "per": np.concatenate([b[1] for b in blocks]), "bytes": blocks[0][2],
            "block_us": [round(b[0] / args.steps * 1e6, 2) for b in blocks], "info": info}
@@ -149,6 +155,7 @@ def measure(wpk, W: Workload, desc, args, baseline: bool, ablations):
         if not bplan:
             raise RuntimeError("baseline build: " + wpk.wpk_last_error(None))
         bb = [W.block(bplan, args.warmup, args.steps, "graph baseline") for _ in range(args.reps)]
+        progress(f"batch {W.batch}: graph baseline")
         wpk.wpk_destroy(bplan)
         bper = np.concatenate([b[1] for b in bb])
         out["baseline"] = {"value": round(bb[0][0] / args.steps * 1e6, 2), "unit": "µs/step",
@@ -156,6 +163,7 @@ def measure(wpk, W: Workload, desc, args, baseline: bool, ablations):
                            "megakernel_speedup": round(float(bper.mean() / out["per"].mean()), 3)}
     if W.batch <= 4 and not args.no_persistent:
         out["persistent"] = persistent_block(wpk, W, desc, args, out["per"])
+        progress(f"batch {W.batch}: persistent session")
     res = {}
     for name, opts, option in ablations:
         p = wpk.wpk_build_ex(desc.desc, W.batch, W.cap, opts)
@@ -166,6 +174,7 @@ def measure(wpk, W: Workload, desc, args, baseline: bool, ablations):
             wpk.check(wpk.wpk_set_option(p, option[0], option[1]), p, name)
         wall, per, _ = W.block(p, args.warmup, args.steps, name)
         wpk.wpk_destroy(p)
+        progress(f"batch {W.batch}: ablation {name}")
         res[name] = {"value": round(wall / args.steps * 1e6, 2), "unit": "µs/step",
                      "latency_mean_us": round(float(per.mean()), 2),
                      "vs_default": round(float(per.mean() / out["per"].mean()), 3)}
@@ -308,6 +317,7 @@ def run(args):
         del W32
 
     if not args.no_cpu:
+        progress("cpu baseline (oracle)")
         kc_np, vc_np = synth.synthetic_kv(cfg, batch, cap, lens0)
         result["cpu_baseline"] = cpu_baseline(cfg, weights, batch, kc_np, vc_np, lens0, tok0, args.cpu_seconds)
     result["setup_s"] = round(setup_s, 1)

@@ -334,7 +334,7 @@ typedef struct wpk_sim_params {
   int32_t workers;           /* W (at least the plan's queue count) */
   int32_t prefetch;          /* 1: weights load when the slot frees; 0: once the inputs are complete */
   int32_t conventional;      /* 1: one kernel per operator instead of the megakernel */
-  int32_t pad;
+  int32_t slots;             /* staging slots per worker (0 or 1: one; a design candidate above 1) */
   double stage_us[WPK_SIM_TYPES];
   double compute_us[WPK_SIM_TYPES];
   double epilogue_us[WPK_SIM_TYPES];

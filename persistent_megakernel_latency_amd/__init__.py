@@ -89,7 +89,7 @@ WPK_SIM_TYPES = 12
 class wpk_sim_params(ctypes.Structure):
     _fields_ = [("hbm_GBps", ctypes.c_double), ("load_latency_us", ctypes.c_double), ("hop_us", ctypes.c_double),
                 ("launch_gap_us", ctypes.c_double), ("workers", _i32), ("prefetch", _i32), ("conventional", _i32),
-                ("pad", _i32), ("stage_us", ctypes.c_double * WPK_SIM_TYPES),
+                ("slots", _i32), ("stage_us", ctypes.c_double * WPK_SIM_TYPES),
                 ("compute_us", ctypes.c_double * WPK_SIM_TYPES), ("epilogue_us", ctypes.c_double * WPK_SIM_TYPES),
                 ("reduce_us", ctypes.c_double * WPK_SIM_TYPES)]
 
@@ -329,7 +329,8 @@ def source_hash() -> str:
     only reported while it matches."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("megakernel.hip", "plan.h", "builder.cpp", "builder.h", "capi.cpp", "runtime.h"):
+    for f in ("megakernel.hip", "worker.h", "wide_layout.h", "persist.hip", "plan.h", "builder.cpp", "builder.h",
+              "capi.cpp", "runtime.h"):
         with open(os.path.join(_HERE, "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

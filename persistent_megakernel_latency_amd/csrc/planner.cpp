@@ -8,10 +8,12 @@
 //    claims its next tile when it stages the current one's weights (the
 //    kernel's claim-ahead), so it holds at most one staged and one claimed
 //    tile;
-//  * one staging slot per worker: a tile's weights start loading when the
-//    slot is free (weight prefetch, Table I) or, without prefetch, once its
-//    inputs are complete; HBM is one first-come server at the streaming
-//    bandwidth, each load also paying a fixed latency;
+//  * one staging slot per worker (or S slots, a design candidate): a tile's
+//    weights start loading when its slot is free -- the slot of the tile S
+//    places earlier on the same worker (weight prefetch, Table I) -- or,
+//    without prefetch, once its inputs are complete; HBM is one first-come
+//    server at the streaming bandwidth, each load also paying a fixed
+//    latency;
 //  * a tile starts when its counter group is complete plus a hop (publish
 //    seen by the poller) and its worker's previous tile has published; then
 //    input staging, compute (once its weights are in) and epilogue, per tile
@@ -82,6 +84,7 @@ struct Hbm {
 struct Rec {
   int32_t tile = -1;
   double claim = 0, top = kInf, load_end = kInf, start = kInf, c1 = kInf, pub = kInf;
+  double frees = kInf;  // when this tile's slot takes another tile's weights (final once started)
   bool top_sched = false, start_sched = false, waiting = false;
 };
 
@@ -89,8 +92,6 @@ struct Worker {
   int q = 0;
   std::vector<Rec> recs;  // tiles in claim order
   size_t cur = 0;         // the tile the control wave works on next
-  double slot_free = 0;   // when the slot takes the next tile's weights
-  bool slot_known = true; // slot_free is final
 };
 
 enum Ev { TOP = 0, CLAIM = 1, START = 2, PUBLISH = 3 };
@@ -125,8 +126,11 @@ struct Sim {
   void push(double t, int kind, int w, size_t k) { ev.push(Event{t, kind, w, k, seq++}); }
   double end = 0, busy = 0, bytes = 0;
 
+  int slots = 1;
+
   Sim(const Shape& s_, const Dag& d_, const wpk_sim_params& sp_, const int32_t* pos_)
-      : s(s_), d(d_), sp(sp_), pos(pos_), hbm{sp_.hbm_GBps * 1e3, sp_.load_latency_us} {}
+      : s(s_), d(d_), sp(sp_), pos(pos_), hbm{sp_.hbm_GBps * 1e3, sp_.load_latency_us},
+        slots(std::max(1, sp_.slots)) {}
 
   double cost(const double* a, int type) const { return type >= 0 && type < WPK_SIM_TYPES ? a[type] : 0.0; }
 
@@ -146,12 +150,19 @@ struct Sim {
     return ++arrivals[T.fix] == T.b ? cost(sp.reduce_us, T.type) : 0.0;
   }
 
+  // Tile k of a worker stages into the slot that tile k - S frees.
   void schedule_top(int w, size_t k) {
     Worker& W = ws[w];
     Rec& r = W.recs[k];
-    if (r.top_sched || !W.slot_known) return;
+    if (r.top_sched) return;
+    double free_at = 0.0;
+    if (k >= (size_t)slots) {
+      const Rec& o = W.recs[k - slots];
+      if (!o.start_sched || o.start >= kInf) return;  // not final until that tile has started
+      free_at = o.frees;
+    }
     r.top_sched = true;
-    push(std::max(r.claim, W.slot_free), TOP, w, k);
+    push(std::max(r.claim, free_at), TOP, w, k);
   }
 
   // The control wave takes its next tile once the previous one has published
@@ -215,7 +226,6 @@ struct Sim {
         case TOP: {
           Rec& r = W.recs[e.k];
           r.top = e.t;
-          W.slot_known = false;  // held until this tile has computed
           if (sp.prefetch) {
             const double b = tile_bytes(s, d.tiles[r.tile], pos);
             bytes += b;
@@ -237,9 +247,8 @@ struct Sim {
           r.c1 = std::max(in, r.load_end) + cost(sp.compute_us, T.type);
           r.pub = r.c1 + cost(sp.epilogue_us, T.type) + reduction(T);
           busy += r.pub - e.t;
-          W.slot_free = barrier_c(T) ? r.pub : r.c1;
-          W.slot_known = true;
-          if (e.k + 1 < W.recs.size()) schedule_top(e.w, e.k + 1);
+          r.frees = barrier_c(T) ? r.pub : r.c1;
+          if (e.k + slots < W.recs.size()) schedule_top(e.w, e.k + slots);
           push(r.pub, PUBLISH, e.w, e.k);
           break;
         }

@@ -219,7 +219,9 @@ typedef struct wpk_tile_timing {
   int64_t t_compute_done;  /* the last compute wave finished its arithmetic */
   int64_t t_partials;      /* all partial sums ready: the control wave passed barrier B */
   int64_t t_end;           /* epilogue stores complete, before the publish */
-  int64_t reserved[2];
+  int64_t t_stored;        /* matrix-core GEMM tiles: the K slice's partial sums stored (else 0) */
+  int64_t t_arrived;       /* matrix-core GEMM tiles: its arrival counted; bit 63 set for the last
+                              slice of its row block, which then adds up the others (else 0) */
 } wpk_tile_timing;
 int32_t wpk_get_log(wpk_plan* plan, void* host_dst, size_t bytes);
 

@@ -1334,8 +1334,15 @@ __device__ __forceinline__ void st_hilo(uint16_t* plane0, size_t plane_elems, si
 // operand area, up to 64 KiB at a time), adds all of them in slice order and
 // runs the epilogue.  Lane l holds sequence 16h + l % 16 of rows l / 16 + 4m.
 // True if this was the last slice (the operand area was overwritten).
-template <typename WT, int KMAX>
-__device__ __forceinline__ bool ctl_wide_post(const Params& P, const Tile& T0, Smem<WT, KMAX>& sm, int lane0) {
+// Logged steps: tw[0] = partial sums stored, tw[1] = arrival counted (its
+// sign bit set for the last slice).
+#ifndef WPK_WIDE_SUM_READS
+#define WPK_WIDE_SUM_READS 4
+#endif
+constexpr int kWideSumReads = WPK_WIDE_SUM_READS;  // 16-byte LDS reads in flight per group of adds
+template <typename WT, int KMAX, bool LOG = false>
+__device__ __forceinline__ bool ctl_wide_post(const Params& P, const Tile& T0, Smem<WT, KMAX>& sm, int lane0,
+                                              uint64_t* tw = nullptr) {
   const int lane = opaque(lane0);
   const Tile T = uni(T0);
   const int nh = P.B > 16 ? 2 : 1;
@@ -1345,25 +1352,29 @@ __device__ __forceinline__ bool ctl_wide_post(const Params& P, const Tile& T0, S
   for (int i = 0; i < per; ++i)
     st_sc1_x4(mine, (uint32_t)(i * 64 + lane) * 16u, *(const u32x4*)(cp + (i * 64 + lane) * 4));
   wait_all_memory();
+  if constexpr (LOG) tw[0] = __builtin_amdgcn_s_memrealtime();
   uint32_t old = 0;
   if (lane == 0) old = atomic_add(&P.fixc[(size_t)T.fix * kLine], 1u);
   old = __builtin_amdgcn_readfirstlane(__shfl(old, 0));
+  if constexpr (LOG) tw[1] = __builtin_amdgcn_s_memrealtime() | ((int)old + 1 == T.b ? (1ull << 63) : 0ull);
   if ((int)old + 1 != T.b) return false;
   compiler_order();  // the other slices' partial sums are read only after their arrivals are counted
   // the last slice: no other slice of this row block touches the counter
   // again this step; it counts from zero in the next
   if (lane == 0) st_sc1(&P.fixc[(size_t)T.fix * kLine], 0u);
-  float y[32];
+  // the slice sums: z[4h + k] holds rows lane / 4 + 16k of sequences
+  // 16h + 4(lane % 4) .. +3, which is 16 consecutive bytes of a partial-sum
+  // slot ([half][row][16 sequences] floats): one 16-byte LDS read per value
+  // group, the 64 lanes of a read covering 1 KiB without bank conflicts
+  float z[32];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) y[i] = 0.f;
+  for (int i = 0; i < 32; ++i) z[i] = 0.f;
   const int q = lane >> 4, s16 = lane & 15;
   const int l = T.layer;
   // o-proj and down: the residual and the next RMSNorm's gain, loaded together
   // with the other slices' partial sums (one round trip for all)
   const bool resid = T.type == T_OPROJ || T.type == T_DOWN;
-  float rv[32];
-#pragma unroll
-  for (int i = 0; i < 32; ++i) rv[i] = 0.f;
+  float rv[32];  // set (and live) only on the residual path
   // RMSNorm site this epilogue writes (o-proj: the MLP input of this layer;
   // down: the next layer's attention input, or after the last layer the final
   // norm's input): 0 attention input, 1 MLP input, 2 final
@@ -1371,6 +1382,8 @@ __device__ __forceinline__ bool ctl_wide_post(const Params& P, const Tile& T0, S
   const int site = T.type == T_OPROJ ? 1 : 2 * last;
   const LayerBufs* nb = P.layers + (T.type == T_OPROJ ? l : l + 1 - last);
   if (resid) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) rv[i] = 0.f;
     // in the store mapping of the epilogue: entry 4i + k of lane l is row
     // 4(l % 16) + k of sequence 4i + l / 16
     const LayerBufs* lbp = P.layers + l;
@@ -1452,23 +1465,57 @@ __device__ __forceinline__ bool ctl_wide_post(const Params& P, const Tile& T0, S
       const int slot = WPK_WIDE_SLOT_OF(sl, s0, T.c, own);
       const float* src = sl == T.c ? cp : sm.xs + slot * per * 256;
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < 2; ++h) {
+        if (h >= nh) break;
+        // a half's four reads in flight together, then the adds (slice order
+        // per value: the sums do not depend on the lane mapping)
 #pragma unroll
-        for (int m = 0; m < 16; ++m)
-          if (h < nh) y[h * 16 + m] += src[(h * kWideRows + q + 4 * m) * 16 + s16];
+        for (int k0 = 0; k0 < 4; k0 += kWideSumReads) {
+          f32x4 t[kWideSumReads];
+#pragma unroll
+          for (int k = 0; k < kWideSumReads; ++k) t[k] = *(const f32x4*)(src + h * 1024 + (k0 + k) * 256 + 4 * lane);
+#pragma unroll
+          for (int k = 0; k < kWideSumReads; ++k) {
+            float* zz = z + 4 * (4 * h + k0 + k);
+            zz[0] += t[k].x;
+            zz[1] += t[k].y;
+            zz[2] += t[k].z;
+            zz[3] += t[k].w;
+          }
+        }
+      }
     }
   }
   if (consumer) {  // divide by the root mean square of the operand's row
+    // sequence n = lane % 32: lanes n and n + 32 add the even and the odd row
+    // blocks (at most 32: hidden <= 2048), each with its reads in flight
+    // together and a fixed tree, then each other's sum; the 32 factors go
+    // through LDS (the attention query area, unused by GEMM tiles) to the
+    // lanes holding those sequences
     const float* ssl = sm.xs + (kWideFrags - ssp) * 256;
+    const int n = lane & 31, par = lane >> 5;
+    float a[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) a[j] = 2 * j + par < nrb ? ssl[(2 * j + par) * kMaxBatch + n] : 0.f;
+#pragma unroll
+    for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+      for (int j = 0; j < w; ++j) a[j] += a[j + w];
+    const float sum = xsum<32>(a[0]);
+    float* inv = &sm.qs[0][0];
+    if (par == 0) inv[n] = 1.0f / sqrtf(sum / (float)P.H + P.eps);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int n = 16 * h + s16;
       if (h >= nh) break;
-      float sum = 0.f;
-      for (int rb = 0; rb < nrb; ++rb) sum += ssl[rb * kMaxBatch + n];
-      const float inv = 1.0f / sqrtf(sum / (float)P.H + P.eps);
+      const f32x4 iv = *(const f32x4*)&inv[16 * h + 4 * (lane & 3)];
 #pragma unroll
-      for (int m = 0; m < 16; ++m) y[h * 16 + m] *= inv;
+      for (int k = 0; k < 4; ++k) {
+        float* zz = z + 4 * (4 * h + k);
+        zz[0] *= iv.x;
+        zz[1] *= iv.y;
+        zz[2] *= iv.z;
+        zz[3] *= iv.w;
+      }
     }
   }
   // The sums into LDS ([sequence][row], pitch 68: conflict-free both ways;
@@ -1478,11 +1525,21 @@ __device__ __forceinline__ bool ctl_wide_post(const Params& P, const Tile& T0, S
   constexpr int TP = 68;
   static_assert(TP == kWideTransposePitch, "the transposition pitch of the reduction layout");
   float* tr = sm.xs;
+  {
+    const int rr = lane >> 2, sq = 4 * (lane & 3);
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    if (h >= nh) break;
+    for (int h = 0; h < 2; ++h) {
+      if (h >= nh) break;
 #pragma unroll
-    for (int m = 0; m < 16; ++m) tr[(16 * h + s16) * TP + q + 4 * m] = y[h * 16 + m];
+      for (int k = 0; k < 4; ++k) {
+        const float* v = z + 4 * (4 * h + k);
+        float* d = tr + (16 * h + sq) * TP + rr + 16 * k;
+        d[0] = v[0];
+        d[TP] = v[1];
+        d[2 * TP] = v[2];
+        d[3 * TP] = v[3];
+      }
+    }
   }
   const int r4 = 4 * s16;
   switch (T.type) {
@@ -1710,9 +1767,9 @@ __device__ __forceinline__ EpiIn ctl_pre(const Params& P, const Tile& T, int b, 
   return e;
 }
 
-template <typename WT, int CPR_H, int CPR_F, bool WIDE, int KMAX>
+template <typename WT, int CPR_H, int CPR_F, bool WIDE, int KMAX, bool LOG = false>
 __device__ __forceinline__ void ctl_post(const Params& P, const Tile& T, int b, Smem<WT, KMAX>& sm, const EpiIn& e,
-                                         int lane, int& xkey) {
+                                         int lane, int& xkey, uint64_t* tw = nullptr) {
   if constexpr (WIDE) {
     switch (T.type) {
       case T_QKV:
@@ -1720,7 +1777,7 @@ __device__ __forceinline__ void ctl_post(const Params& P, const Tile& T, int b, 
       case T_GATEUP:
       case T_DOWN:
       case T_LM:
-        if (ctl_wide_post<WT>(P, T, sm, lane)) xkey = -1;  // the reduction used the operand area
+        if (ctl_wide_post<WT, KMAX, LOG>(P, T, sm, lane, tw)) xkey = -1;  // the reduction used the operand area
         break;
       case T_ARGMAX: ctl_argmax<WT>(P, sm, lane); break;  // attention: merged by the caller
       case T_NORM: ctl_norm<WT>(P, T, sm, lane); break;
@@ -1869,6 +1926,7 @@ __device__ __forceinline__ void control_loop(const Params& P, Smem<WT, KMAX>& sm
     const uint64_t t_start = LOG ? __builtin_amdgcn_s_memrealtime() : 0;
     const int npairs = n_passes<WIDE>(P, T, sm.pos[T.b]);
     uint64_t t_inputs = 0, t_partials = 0, t_ready = 0, t_done = 0;
+    uint64_t tw[2] = {0, 0};  // logged matrix-core GEMM tiles: partials stored, arrival counted
     AttnRun run;
     attn_run_init(run);
     for (int b = 0; b < npairs; ++b) {
@@ -1886,7 +1944,7 @@ __device__ __forceinline__ void control_loop(const Params& P, Smem<WT, KMAX>& sm
         t_ready = sm.t_ready;
         t_done = sm.t_done;
       }
-      ctl_post<WT, CPR_H, CPR_F, WIDE>(P, Tb, b, sm, e, lane, xkey);
+      ctl_post<WT, CPR_H, CPR_F, WIDE, KMAX, LOG>(P, Tb, b, sm, e, lane, xkey, tw);
       if (WIDE && is_attn(T.type) && attn_count(P, Tb, sm.pos[T.b]) > 0) attn_run_merge(P, run, sm, lane);
     }
     if (WIDE && T.type == T_ATTN) attn_run_partial(P, T, run, sm, lane);
@@ -1917,6 +1975,8 @@ __device__ __forceinline__ void control_loop(const Params& P, Smem<WT, KMAX>& sm
         tm[3] = t_done;
         tm[4] = t_partials;
         tm[5] = t_end;
+        tm[6] = tw[0];
+        tm[7] = tw[1];
       }
       if (!batch && T.signal >= 0 && id != P.drop_tile) {
         const Group G = cload(P.groups, T.signal);

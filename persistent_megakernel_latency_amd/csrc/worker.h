@@ -963,18 +963,51 @@ __device__ __forceinline__ void cmp_wide(const Params& P, const Slot& s, Smem<WT
   const bool two = P.B > 16;
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   const uint32_t* xf = (const uint32_t*)sm.xs + lane * 4;
+  // the k-step loop in two straight-line versions (one or two sequence
+  // halves), the B fragments of step ks + 1 read while step ks multiplies, so
+  // the LDS reads are in flight behind the matrix-core work instead of each
+  // one waited for
+  if (two) {
+    bf16x8 b[4];
 #pragma unroll
-  for (int ks = 0; ks < kWideSteps; ++ks) {
-    const bf16x8 a = __builtin_bit_cast(bf16x8, s.c[ks]);
-    const bf16x8 h0 = *(const bf16x8*)(xf + wfrag(ks, 0, 0) * 256);
-    const bf16x8 l0 = *(const bf16x8*)(xf + wfrag(ks, 0, 1) * 256);
-    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, h0, acc0, 0, 0, 0);
-    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, l0, acc0, 0, 0, 0);
-    if (two) {
-      const bf16x8 h1 = *(const bf16x8*)(xf + wfrag(ks, 1, 0) * 256);
-      const bf16x8 l1 = *(const bf16x8*)(xf + wfrag(ks, 1, 1) * 256);
-      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, h1, acc1, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, l1, acc1, 0, 0, 0);
+    for (int f = 0; f < 4; ++f) b[f] = *(const bf16x8*)(xf + wfrag(0, f >> 1, f & 1) * 256);
+#pragma unroll
+    for (int ks = 0; ks < kWideSteps; ++ks) {
+      bf16x8 nb[4];
+      if (ks + 1 < kWideSteps) {
+#pragma unroll
+        for (int f = 0; f < 4; ++f) nb[f] = *(const bf16x8*)(xf + wfrag(ks + 1, f >> 1, f & 1) * 256);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // the next step's reads stay ahead of this step's products
+      const bf16x8 a = __builtin_bit_cast(bf16x8, s.c[ks]);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[0], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[2], acc1, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[1], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[3], acc1, 0, 0, 0);
+      if (ks + 1 < kWideSteps) {
+#pragma unroll
+        for (int f = 0; f < 4; ++f) b[f] = nb[f];
+      }
+    }
+  } else {
+    bf16x8 b[2];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) b[f] = *(const bf16x8*)(xf + wfrag(0, 0, f) * 256);
+#pragma unroll
+    for (int ks = 0; ks < kWideSteps; ++ks) {
+      bf16x8 nb[2];
+      if (ks + 1 < kWideSteps) {
+#pragma unroll
+        for (int f = 0; f < 2; ++f) nb[f] = *(const bf16x8*)(xf + wfrag(ks + 1, 0, f) * 256);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      const bf16x8 a = __builtin_bit_cast(bf16x8, s.c[ks]);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[0], acc0, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[1], acc0, 0, 0, 0);
+      if (ks + 1 < kWideSteps) {
+#pragma unroll
+        for (int f = 0; f < 2; ++f) b[f] = nb[f];
+      }
     }
   }
   float* cp = cpart(sm);

@@ -760,6 +760,10 @@ __device__ __forceinline__ void attn_run_store(const Params& P, const Tile& T, c
 }
 
 
+#ifndef WPK_ATTN_GROUP
+#define WPK_ATTN_GROUP 1
+#endif
+
 // Attention partial: compute wave h = q head h of the group, lane = position
 // (scores) then lane = head dimension (weighted values).  Both loops are
 // unrolled so that the LDS reads of a row are in flight together.
@@ -770,21 +774,53 @@ __device__ __forceinline__ void cmp_attn(const Params& P, const Tile& T, Smem<WT
   const int lane = tc & 63, h = tc >> 6;
   const int cnt = attn_count(P, T, sm.pos[T.b]);
   if (h >= P.G || cnt == 0) return;
+  // Both loops go over groups of two 16-byte row chunks; the next group's LDS
+  // reads are issued before this group's products (scheduling barriers keep
+  // them there), so the reads overlap the arithmetic instead of each one
+  // being waited for.  The multiply-add order is the plain loop's.
+  constexpr int QPC = EPC / 4;  // 16-byte query (or weight) reads per row chunk
+  constexpr int GC = WPK_ATTN_GROUP;  // row chunks per group
   float sc = -INFINITY;
   if (lane < cnt) {
     const WT* kr = sm.ks + lane * KP;
+    const float* qh = &sm.qs[h][0];
     float d0 = 0.f, d1 = 0.f;
+    u32x4 kc[GC];
+    f32x4 qc[GC * QPC];
 #pragma unroll
-    for (int d = 0; d < kHeadDim; d += EPC) {
-      float k[EPC];
-      unpack<WT>(*(const u32x4*)(kr + d), k);
+    for (int i = 0; i < GC; ++i) kc[i] = *(const u32x4*)(kr + i * EPC);
 #pragma unroll
-      for (int e = 0; e < EPC; e += 4) {
-        const f32x4 q = *(const f32x4*)&sm.qs[h][d + e];
-        d0 = fmaf(q.x, k[e], d0);
-        d1 = fmaf(q.y, k[e + 1], d1);
-        d0 = fmaf(q.z, k[e + 2], d0);
-        d1 = fmaf(q.w, k[e + 3], d1);
+    for (int j = 0; j < GC * QPC; ++j) qc[j] = *(const f32x4*)(qh + 4 * j);
+#pragma unroll
+    for (int g = 0; g < kHeadDim / (GC * EPC); ++g) {
+      const int dn = (g + 1) * GC * EPC;
+      u32x4 kn[GC];
+      f32x4 qn[GC * QPC];
+      if (dn < kHeadDim) {
+#pragma unroll
+        for (int i = 0; i < GC; ++i) kn[i] = *(const u32x4*)(kr + dn + i * EPC);
+#pragma unroll
+        for (int j = 0; j < GC * QPC; ++j) qn[j] = *(const f32x4*)(qh + dn + 4 * j);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < GC; ++i) {
+        float k[EPC];
+        unpack<WT>(kc[i], k);
+#pragma unroll
+        for (int e = 0; e < EPC; e += 4) {
+          const f32x4 q = qc[i * QPC + e / 4];
+          d0 = fmaf(q.x, k[e], d0);
+          d1 = fmaf(q.y, k[e + 1], d1);
+          d0 = fmaf(q.z, k[e + 2], d0);
+          d1 = fmaf(q.w, k[e + 3], d1);
+        }
+      }
+      if (dn < kHeadDim) {
+#pragma unroll
+        for (int i = 0; i < GC; ++i) kc[i] = kn[i];
+#pragma unroll
+        for (int j = 0; j < GC * QPC; ++j) qc[j] = qn[j];
       }
     }
     sc = (d0 + d1) * P.attn_scale;
@@ -797,18 +833,45 @@ __device__ __forceinline__ void cmp_attn(const Params& P, const Tile& T, Smem<WT
   // at a time over the whole chunk (all reads in flight together); positions
   // past the chunk's count hold no data and are masked
   const WT* vr = sm.vt + lane * KP;
+  const float* ph = &sm.ps[h][0];
   float o0 = 0.f, o1 = 0.f;
+  u32x4 vc[GC];
+  f32x4 pc[GC * QPC];
 #pragma unroll
-  for (int j0 = 0; j0 < kAttnChunk; j0 += EPC) {
-    float v[EPC];
-    unpack<WT>(*(const u32x4*)(vr + j0), v);
+  for (int i = 0; i < GC; ++i) vc[i] = *(const u32x4*)(vr + i * EPC);
 #pragma unroll
-    for (int u = 0; u < EPC; u += 4) {
-      const f32x4 pw = *(const f32x4*)&sm.ps[h][j0 + u];
-      o0 = fmaf(pw.x, j0 + u < cnt ? v[u] : 0.f, o0);
-      o1 = fmaf(pw.y, j0 + u + 1 < cnt ? v[u + 1] : 0.f, o1);
-      o0 = fmaf(pw.z, j0 + u + 2 < cnt ? v[u + 2] : 0.f, o0);
-      o1 = fmaf(pw.w, j0 + u + 3 < cnt ? v[u + 3] : 0.f, o1);
+  for (int j = 0; j < GC * QPC; ++j) pc[j] = *(const f32x4*)(ph + 4 * j);
+#pragma unroll
+  for (int g = 0; g < kAttnChunk / (GC * EPC); ++g) {
+    const int jn = (g + 1) * GC * EPC;
+    u32x4 vn[GC];
+    f32x4 pn[GC * QPC];
+    if (jn < kAttnChunk) {
+#pragma unroll
+      for (int i = 0; i < GC; ++i) vn[i] = *(const u32x4*)(vr + jn + i * EPC);
+#pragma unroll
+      for (int j = 0; j < GC * QPC; ++j) pn[j] = *(const f32x4*)(ph + jn + 4 * j);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < GC; ++i) {
+      const int j0 = g * GC * EPC + i * EPC;
+      float v[EPC];
+      unpack<WT>(vc[i], v);
+#pragma unroll
+      for (int u = 0; u < EPC; u += 4) {
+        const f32x4 pw = pc[i * QPC + u / 4];
+        o0 = fmaf(pw.x, j0 + u < cnt ? v[u] : 0.f, o0);
+        o1 = fmaf(pw.y, j0 + u + 1 < cnt ? v[u + 1] : 0.f, o1);
+        o0 = fmaf(pw.z, j0 + u + 2 < cnt ? v[u + 2] : 0.f, o0);
+        o1 = fmaf(pw.w, j0 + u + 3 < cnt ? v[u + 3] : 0.f, o1);
+      }
+    }
+    if (jn < kAttnChunk) {
+#pragma unroll
+      for (int i = 0; i < GC; ++i) vc[i] = vn[i];
+#pragma unroll
+      for (int j = 0; j < GC * QPC; ++j) pc[j] = pn[j];
     }
   }
   sm.outs[h][2 + lane] = o0 + o1;

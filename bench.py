@@ -249,6 +249,7 @@ def run(args):
         ("weight_prefetch_off", None, (wpk.WPK_OPT_PREFETCH, 0)),
         ("barrier_edges", wpk.wpk_build_opts(barrier_edges=1), None),
         ("cooperative_launch", None, (wpk.WPK_OPT_LAUNCH, 1)),
+        ("co_resident_split_attention_128", wpk.wpk_build_opts(split_workers=128), None),
     ]
     m = measure(wpk, W1, desc, args, not args.no_baseline, ab1)
     wall, per, byts, info = m["wall"], m["per"], m["bytes"], m["info"]
@@ -295,6 +296,8 @@ def run(args):
             ("lds_forwarding_chained_attention", wpk.wpk_build_opts(forward=1), None),
             ("barrier_edges", wpk.wpk_build_opts(barrier_edges=1), None),
             ("weight_prefetch_off", None, (wpk.WPK_OPT_PREFETCH, 0)),
+            ("co_resident_split_attention_128", wpk.wpk_build_opts(split_workers=128), None),
+            ("co_resident_split_attention_256", wpk.wpk_build_opts(split_workers=256), None),
         ]
         m32 = measure(wpk, W32, desc, args, not args.no_baseline, ab32)
         w32, per32, by32 = m32["wall"], m32["per"], m32["bytes"]

@@ -117,6 +117,18 @@ typedef struct wpk_build_opts {
                                Enough", Table I, cross-kernel readiness): 1 makes every tile wait
                                for ALL tiles of the operator it reads from, as a per-operator
                                barrier would; 0 (default): only for the tiles producing its inputs */
+  int32_t split_workers;    /* two co-resident megakernels ("One Megakernel is Not Enough": the
+                               abstract, several megakernels sharing the GPU; Table I, smaller CTA
+                               budget): 0 (default) runs the step as one megakernel; N > 0 gives the
+                               attention and combine tiles a megakernel of their own: the last N
+                               workers of the launch claim only from the attention and combine
+                               queues, the others only from the queues of every other tile, and the
+                               two wait on each other's tiles through the same counters.  Each needs
+                               at least one worker per claim queue.  The workers' placement on CUs
+                               is the dispatcher's (a CU-masked stream per megakernel, the MI355X
+                               analogue of partitioning the streaming multiprocessors, could not be
+                               created on the test machine).  Device plans from wpk_build_ex; no
+                               persistent session; WPK_OPT_WORKERS is refused. */
 } wpk_build_opts;
 
 typedef struct wpk_plan wpk_plan;

@@ -96,6 +96,8 @@ std::string check_shape(const wpk_model_desc& d, int32_t batch, int32_t ctx_len,
   if (s.forward && !s.wide) return "LDS forwarding of attention partials is built for batches above 4";
   if (o.barrier_edges != 0 && o.barrier_edges != 1) return "barrier_edges must be 0 or 1";
   s.barrier_edges = o.barrier_edges;
+  if (o.split_workers < 0) return "split_workers must be >= 0";
+  s.split_workers = o.split_workers;
   *out = s;
   return "";
 }
@@ -347,14 +349,25 @@ Dag finish_dag(const Shape& s, Emitter& e) {
   for (Tile& t : d.tiles)
     if (t.signal >= 0) t.shard = seen[t.signal]++ % d.groups[t.signal].shards;
 
-  // claim queues: the topological order dealt round-robin
+  // claim queues: the topological order dealt round-robin (split plans: each
+  // region's tiles, in topological order, over that region's queues)
   const int32_t nq = s.queue_shards;
-  d.queue_off.assign(nq + 1, 0);
-  for (int32_t q = 0; q < nq; ++q) {
-    d.queue_off[q] = (int32_t)d.queue.size();
-    for (size_t i = q; i < d.tiles.size(); i += nq) d.queue.push_back((int32_t)i);
+  const int32_t nr = s.split_workers > 0 ? 2 : 1;
+  auto region = [&](const Tile& t) {
+    return nr == 2 && (t.type == T_ATTN || t.type == T_ATTNC || t.type == T_COMBINE) ? 1 : 0;
+  };
+  d.queue_off.assign(nr * nq + 1, 0);
+  for (int32_t r = 0; r < nr; ++r) {
+    std::vector<int32_t> ids;
+    for (size_t i = 0; i < d.tiles.size(); ++i)
+      if (region(d.tiles[i]) == r) ids.push_back((int32_t)i);
+    for (int32_t q = 0; q < nq; ++q) {
+      d.queue_off[r * nq + q] = (int32_t)d.queue.size();
+      for (size_t i = q; i < ids.size(); i += nq) d.queue.push_back(ids[i]);
+    }
   }
-  d.queue_off[nq] = (int32_t)d.queue.size();
+  d.queue_off[nr * nq] = (int32_t)d.queue.size();
+  d.split_queues = nr == 2 ? nq : 0;
 
   // operator runs for the baseline
   for (size_t i = 0; i < d.tiles.size();) {

@@ -25,6 +25,7 @@ struct Shape {
   int32_t attn_sub;  // KV chunks per attention tile (one slot holds up to 64 KiB of K and V)
   int32_t forward;   // chained attention tiles (LDS forwarding of the partials to the combine)
   int32_t barrier_edges;  // ablation: each consumer waits on its whole producing operator
+  int32_t split_workers;  // > 0: attention and combine tiles in a second co-resident megakernel
   float theta, eps;
 };
 
@@ -36,6 +37,9 @@ struct Dag {
   int32_t n_shard_slots = 0;
   int32_t n_fix = 0;     // wide plans: row blocks (arrival counters)
   int32_t n_pslots = 0;  // wide plans: partial-sum slots (one per wide GEMM tile)
+  // split plans: queues [0, split_queues) hold every tile but attention and
+  // combine (the first megakernel), the rest those (the second); 0: one region
+  int32_t split_queues = 0;
   // runs of tiles of one (layer, type), in order: the operators of the
   // conventional one-kernel-per-operator baseline
   std::vector<std::pair<int32_t, int32_t>> phases;

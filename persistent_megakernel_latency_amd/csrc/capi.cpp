@@ -48,7 +48,7 @@ int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
 
 struct Layout {
   int64_t ctl, heads, counters, argmax, tiles, qtiles, groups, queue, queue_off, layers, rope_cos, rope_sin, act, log,
-      wpart, fixc, step_times, total;
+      wpart, fixc, step_times, wqueue, total;
 };
 
 Layout layout(const Shape& s, const Dag& d, int32_t max_workers) {
@@ -78,6 +78,7 @@ Layout layout(const Shape& s, const Dag& d, int32_t max_workers) {
   L.wpart = take((int64_t)d.n_pslots * kWidePart * 4);
   L.fixc = take((int64_t)d.n_fix * kLine * 4);
   L.step_times = take((int64_t)kPersistTimes * 2 * 8);
+  L.wqueue = take((int64_t)max_workers * 4);
   L.total = at;
   return L;
 }
@@ -181,6 +182,14 @@ wpk_plan* build_device(const wpk_model_desc* desc, int32_t batch, int32_t ctx_le
     g_err = "occupancy too low: " + std::to_string(p->max_workers) + " co-resident workers";
     return nullptr;
   }
+  if (s.split_workers > 0) {
+    if (baseline || static_ws) return fail("split_workers: megakernel plans from wpk_build_ex only");
+    const int w1 = s.split_workers;
+    if (w1 < s.queue_shards || p->workers - w1 < s.queue_shards)
+      return fail("split_workers must leave each megakernel at least one worker per claim queue (" +
+                  std::to_string(s.queue_shards) + ") of the " + std::to_string(p->workers) + " workers");
+    p->split_workers = w1;
+  }
 
   const Layout L = layout(s, p->dag, p->max_workers);
   if (static_ws) {
@@ -220,6 +229,16 @@ wpk_plan* build_device(const wpk_model_desc* desc, int32_t batch, int32_t ctx_le
   if (e == hipSuccess) e = up(L.layers, lbs.data(), lbs.size() * sizeof(LayerBufs));
   if (e == hipSuccess) e = up(L.rope_cos, rc.data(), rc.size() * 4);
   if (e == hipSuccess) e = up(L.rope_sin, rsn.data(), rsn.size() * 4);
+  {
+    // each worker's claim queue (split plans: the first megakernel's workers
+    // over its queues, the last split_workers over the attention queues)
+    const int32_t nq = (int32_t)p->dag.queue_off.size() - 1, q0 = p->dag.split_queues;
+    const int32_t w0 = p->workers - p->split_workers;
+    std::vector<int32_t> wq(p->max_workers);
+    for (int32_t w = 0; w < p->max_workers; ++w)
+      wq[w] = !p->split_workers ? w % nq : w < w0 ? w % q0 : q0 + (w - w0) % (nq - q0);
+    if (e == hipSuccess) e = up(L.wqueue, wq.data(), wq.size() * 4);
+  }
   if (e != hipSuccess) {
     release_ws();
     return fail(hip_msg("workspace upload", e));
@@ -230,7 +249,8 @@ wpk_plan* build_device(const wpk_model_desc* desc, int32_t batch, int32_t ctx_le
   P.attn_sub = s.attn_sub;
   P.n_tiles = (int32_t)p->dag.tiles.size();
   P.n_queues = (int32_t)p->dag.queue_off.size() - 1;
-  P.n_workers = p->workers;
+  P.n_workers = p->workers;  // both megakernels' workers: the exit count
+  P.worker_queue = (const int32_t*)(w + L.wqueue);
   P.dtype = s.dtype;
   P.eps = s.eps;
   P.attn_scale = 1.0f / std::sqrt((float)s.D);
@@ -454,6 +474,7 @@ void wpk_destroy(wpk_plan* p) {
   if (p->graph_exec) (void)hipGraphExecDestroy((hipGraphExec_t)p->graph_exec);
   if (p->graph) (void)hipGraphDestroy((hipGraph_t)p->graph);
   if (p->cap_stream) (void)hipStreamDestroy((hipStream_t)p->cap_stream);
+
   if (p->d_ws) {
     (void)hipDeviceSynchronize();
     if (p->static_ws) {
@@ -509,6 +530,7 @@ int32_t wpk_set_option(wpk_plan* p, int32_t key, int64_t value) {
     case WPK_OPT_WORKERS:
       if (value < (int64_t)p->s.queue_shards || value > p->max_workers)
         return plan_fail(p, WPK_E_ARG, "workers must be in [queue shards, max co-resident]");
+      if (p->split_workers) return plan_fail(p, WPK_E_ARG, "a split plan's worker counts are fixed when it is built");
       p->workers = (int32_t)value;
       P.n_workers = (int32_t)value;
       return WPK_OK;
@@ -616,6 +638,7 @@ int32_t wpk_persist_begin(wpk_plan* p, int32_t* tokens, wpk_kv* kv, void* logits
   if (p->host || p->baseline) return plan_fail(p, WPK_E_ARG, "persistent sessions run megakernel device plans");
   if (!p->k_persist)
     return plan_fail(p, WPK_E_ARG, "persistent sessions are built for batches up to 4 (no matrix-core instance)");
+  if (p->split_workers) return plan_fail(p, WPK_E_ARG, "persistent sessions run one megakernel (not a split plan)");
   if (p->persist_open) return plan_fail(p, WPK_E_STATE, "a persistent session is already open");
   if (p->latched) return plan_fail(p, WPK_E_STATE, "plan holds device error " + std::to_string(p->latched) + "; reset it");
   if (p->log_on) return plan_fail(p, WPK_E_ARG, "the per-tile log records one step: switch it off first");

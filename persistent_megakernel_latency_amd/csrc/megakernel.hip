@@ -21,7 +21,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
   }
   SM& sm = *smp;
   const int t = wpk_tid(), lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int q = (int)blockIdx.x % P.n_queues;
+  const int q = cload(P.worker_queue, (int)blockIdx.x);
   const int qb = cload(P.queue_off, q), qn = cload(P.queue_off, q + 1) - qb;
   uint32_t* head = P.heads + (size_t)q * kLine;
   uint32_t epoch = 0;

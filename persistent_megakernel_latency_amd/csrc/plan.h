@@ -196,6 +196,10 @@ struct Params {
   uint32_t* host_done;
   uint64_t idle_ticks;      // a grid left without a grant this long stops by itself
   uint64_t* step_times;     // [kPersistTimes][2]: grant seen, last worker out (s_memrealtime)
+  // The claim queue of each worker (blockIdx.x): w mod n_queues for one
+  // megakernel; with two co-resident megakernels (split plans) the first's
+  // workers deal over its queues and the second's over the others.
+  const int32_t* worker_queue;
 };
 
 }  // namespace wpk

@@ -18,7 +18,10 @@
 //    seen by the poller) and its worker's previous tile has published; then
 //    input staging, compute (once its weights are in) and epilogue, per tile
 //    type, from measured profiles; its publish counts towards its group;
-//  * barrier edges are a property of the DAG (build with barrier_edges=1);
+//  * barrier edges are a property of the DAG (build with barrier_edges=1), and
+//    so is a split into two co-resident megakernels (split_workers): the last
+//    split_workers workers then claim only the attention and combine queues,
+//    the others only the rest;
 //  * the conventional design runs each operator as one kernel over W
 //    resident workgroups (ceil(tiles / W) waves), kernels separated by a
 //    launch gap, with no hops (kernel boundaries order the operators).
@@ -211,8 +214,12 @@ struct Sim {
     waiters.assign(d.groups.size(), {});
     for (size_t g = 0; g < d.groups.size(); ++g) remaining[g] = d.groups[g].producers;
     arrivals.assign(d.n_fix, 0);
+    // split plans: the first megakernel's workers claim from its queues, the
+    // second's (the last split_workers) from the attention and combine queues
+    const int q0 = d.split_queues ? d.split_queues : nq, w1 = d.split_queues ? s.split_workers : 0;
+    const int w0 = sp.workers - w1;
     for (int w = 0; w < sp.workers; ++w) {
-      ws[w].q = w % nq;
+      ws[w].q = w < w0 ? w % q0 : q0 + (w - w0) % (nq - q0);
       push(0.0, CLAIM, w, 0);
     }
     while (!ev.empty()) {
@@ -305,7 +312,11 @@ using namespace wpk;
 extern "C" int32_t wpk_simulate(const wpk_plan* p, const wpk_sim_params* sp, const int32_t* positions,
                                 wpk_sim_result* out) {
   if (!p || !sp || !out) return WPK_E_ARG;
-  if (sp->workers < (int32_t)p->dag.queue_off.size() - 1 || sp->workers > 65536 || !(sp->hbm_GBps > 0) ||
+  const int32_t nq = (int32_t)p->dag.queue_off.size() - 1;
+  if (p->dag.split_queues && !sp->conventional &&
+      (p->s.split_workers < nq - p->dag.split_queues || sp->workers - p->s.split_workers < p->dag.split_queues))
+    return WPK_E_ARG;  // each megakernel needs a worker per queue
+  if (sp->workers < nq || sp->workers > 65536 || !(sp->hbm_GBps > 0) ||
       sp->load_latency_us < 0 || sp->hop_us < 0 || sp->launch_gap_us < 0)
     return WPK_E_ARG;
   Sim sim(p->s, p->dag, *sp, positions);

@@ -78,6 +78,9 @@ struct wpk_plan {
   const void* k_phase = nullptr;
   const void* k_persist = nullptr;  // persistent grid kernel (narrow plans only)
   int dyn_lds = 0;                  // dynamic LDS bytes of the kernels (wide plans)
+  // two co-resident megakernels (wpk_build_opts.split_workers): the last
+  // split_workers workers of the launch form the second
+  int split_workers = 0;
   void* last_stream = nullptr;
   // baseline graph
   void* graph_exec = nullptr;

@@ -368,3 +368,33 @@ def test_emulated_fixed_reducer_matches_serial_on_a_matrix_core_plan():
         assert np.array_equal(st.logits, ref.logits) and np.array_equal(st.kc, ref.kc)
     assert wpk.wpk_set_option(plan, wpk.WPK_OPT_FIXED_REDUCER, 2) == wpk.WPK_E_ARG
     wpk.wpk_destroy(plan)
+
+
+@pytest.mark.parametrize("batch", [1, 8])
+def test_split_plan_emulated_matches_serial(batch):
+    """A plan split into two co-resident megakernels (attention and combine
+    tiles in their own claim queues) runs on the emulator's workers to the
+    serial executor's results bit for bit, with a valid log; a negative worker
+    count is refused."""
+    cfg = synth.MINI
+    w = synth.make_weights(cfg, gain_std=0.1)
+    cap = 140
+    lens = np.array([63, 100, 7, 128, 1, 64, 65, 90][:batch], np.int32)
+    kc, vc = synth.synthetic_kv(cfg, batch, cap, lens)
+    tok = (np.arange(batch, dtype=np.int32) * 113 + 5) % cfg.vocab
+    d = host_desc(cfg, w)
+    assert not wpk.wpk_build_host(d.desc, batch, cap, wpk.wpk_build_opts(split_workers=-1))
+    plan = wpk.wpk_build_host(d.desc, batch, cap, wpk.wpk_build_opts(split_workers=64))
+    assert plan, wpk.wpk_last_error(None)
+    info = wpk.wpk_get_info(plan)
+    _, _, wait, signal = wpk.wpk_get_dag(plan, info.n_tiles)
+    ref = HostState(kc, vc, lens, tok, cfg.vocab)
+    assert ref.serial(plan, 1, poison=True) == 0, wpk.wpk_last_error(plan)
+    st = HostState(kc, vc, lens, tok, cfg.vocab)
+    assert st.emulate(plan, 16, 7) == 0, wpk.wpk_last_error(plan)
+    rc, log = wpk.wpk_get_log(plan, info.n_tiles)
+    check_log(log, wait, signal)
+    assert np.array_equal(st.logits, ref.logits) and np.array_equal(st.kc, ref.kc)
+    # 8 claim queues per megakernel: fewer than 16 emulated workers is refused
+    assert HostState(kc, vc, lens, tok, cfg.vocab).emulate(plan, 8, 7) != 0
+    wpk.wpk_destroy(plan)

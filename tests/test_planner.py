@@ -94,3 +94,21 @@ def test_conventional_design_sums_its_operators():
     r = _sim(p, _params(1, gap=3.0, conventional=1, compute=1.0))
     assert r.step_us == pytest.approx(n * 1.0 + phases * 3.0, rel=1e-6)
     wpk.wpk_destroy(p)
+
+
+def test_split_plan_regions_in_the_simulation():
+    """A split plan's second megakernel (its last split_workers workers) only
+    claims attention and combine tiles: with the same per-tile costs the
+    simulated step is no shorter than the single megakernel's, and a worker
+    count that leaves a region's queues without a worker is refused."""
+    cfg = synth.MINI
+    one = _plan(cfg, 8, 140)
+    two = _plan(cfg, 8, 140, split_workers=64)
+    sp = _params(512, bw=5000.0, lat=2.0, hop=1.0, stage=0.5, compute=1.0, epi=0.5)
+    r1, r2 = _sim(one, sp), _sim(two, sp)
+    assert r2.step_us >= r1.step_us - 1e-9
+    assert r2.hbm_bytes == pytest.approx(r1.hbm_bytes, rel=1e-12)
+    rc, _ = wpk.wpk_simulate(two, _params(64 + 4, stage=0.5, compute=1.0, epi=0.5))
+    assert rc == wpk.WPK_E_ARG
+    wpk.wpk_destroy(one)
+    wpk.wpk_destroy(two)

@@ -2,9 +2,11 @@
 profiles, and how well they rank against measured ones.
 
 A candidate design is the megakernel with tile-to-tile edges (the default),
-with barrier edges, without weight prefetch, with 256 workers, or the
-conventional one-kernel-per-operator graph ("One Megakernel is Not Enough",
-Table I features and the conventional design it is compared with).  Each is
+with barrier edges, without weight prefetch, with 256 workers, the
+conventional one-kernel-per-operator graph, or two co-resident megakernels
+(attention and combine tiles in one of 128 or 256 workers) ("One Megakernel
+is Not Enough": the abstract's split into several megakernels, Table I
+features, and the conventional design it is compared with).  Each is
 predicted by wpk_simulate on its own DAG from the profiles that
 planner_profile.py records (per-tile-type costs and the hop latency of the
 default design at that batch).  Two machine constants are fixed from batch 1
@@ -30,7 +32,7 @@ if os.path.dirname(HERE) not in sys.path:
 
 import persistent_megakernel_latency_amd as wpk  # noqa: E402
 
-DESIGNS = ("tile_edges", "barrier_edges", "no_prefetch", "workers_256", "conventional")
+DESIGNS = ("tile_edges", "barrier_edges", "no_prefetch", "workers_256", "conventional", "split_128", "split_256")
 HBM_GBPS = 6215.6   # the repository's tile-read ceiling (profiles/microbench_gfx950.md)
 CAP = 1152          # context capacity of the plans (covers every position of the profiles)
 
@@ -51,10 +53,11 @@ class Planner:
         self.desc = _dummy_desc(self.cfg)
         self.plans = {}
 
-    def plan(self, batch, barrier):
-        key = (batch, barrier)
+    def plan(self, batch, barrier, split=0):
+        key = (batch, barrier, split)
         if key not in self.plans:
-            p = wpk.wpk_build_host(self.desc.desc, batch, CAP, wpk.wpk_build_opts(barrier_edges=int(barrier)))
+            p = wpk.wpk_build_host(self.desc.desc, batch, CAP,
+                                   wpk.wpk_build_opts(barrier_edges=int(barrier), split_workers=split))
             if not p:
                 raise RuntimeError(wpk.wpk_last_error(None))
             self.plans[key] = p
@@ -80,7 +83,8 @@ class Planner:
         """Predicted step time (µs): the simulated step plus one launch (the
         megakernel is one launch per step; the graph pays a gap per kernel)."""
         entry = self.prof["batches"][str(batch)]
-        p = self.plan(batch, design == "barrier_edges")
+        split = int(design.split("_")[1]) if design.startswith("split_") else 0
+        p = self.plan(batch, design == "barrier_edges", split)
         rc, r = wpk.wpk_simulate(p, self.params(entry, design, latency_us, gap_us),
                                  np.array(entry["positions"], np.int32))
         if rc != 0:
@@ -101,11 +105,13 @@ class Planner:
                     hi = mid
             return 0.5 * (lo + hi)
 
-        lat = solve(lambda x: self.predict(1, "tile_edges", x, 0.0), m["tile_edges"] - 0.0, 0.0, 20.0)
-        gap = solve(lambda x: self.predict(1, "conventional", lat, x), m["conventional"], 0.0, 20.0)
-        # the megakernel's own launch is part of its measured step: refit the
-        # latency with the gap in place
-        lat = solve(lambda x: self.predict(1, "tile_edges", x, gap), m["tile_edges"], 0.0, 20.0)
+        # each fit depends on the other (the megakernel's own launch is part of
+        # its measured step; the graph's kernels also load with the latency):
+        # alternate until both meet their measurements
+        lat, gap = 0.0, 0.0
+        for _ in range(4):
+            lat = solve(lambda x: self.predict(1, "tile_edges", x, gap), m["tile_edges"], 0.0, 20.0)
+            gap = solve(lambda x: self.predict(1, "conventional", lat, x), m["conventional"], 0.0, 20.0)
         return lat, gap
 
     def evaluate(self):
@@ -113,16 +119,17 @@ class Planner:
         rows, pairs_ok, pairs, best_ok, regret = [], 0, 0, 0, []
         for b in sorted(self.prof["batches"], key=int):
             meas = self.prof["batches"][b]["measured_us"]
-            pred = {d: self.predict(int(b), d, lat, gap) for d in DESIGNS}
-            for x, y in itertools.combinations(DESIGNS, 2):
+            designs = [d for d in DESIGNS if d in meas]
+            pred = {d: self.predict(int(b), d, lat, gap) for d in designs}
+            for x, y in itertools.combinations(designs, 2):
                 pairs += 1
                 pairs_ok += (pred[x] < pred[y]) == (meas[x] < meas[y])
             pb, mb = min(pred, key=pred.get), min(meas, key=meas.get)
             best_ok += pb == mb
             regret.append(meas[pb] / meas[mb] - 1.0)
-            rows.append({"batch": int(b), "predicted_us": {d: round(pred[d], 1) for d in DESIGNS},
+            rows.append({"batch": int(b), "predicted_us": {d: round(pred[d], 1) for d in designs},
                          "measured_us": meas, "predicted_best": pb, "measured_best": mb,
-                         "error": {d: round(pred[d] / meas[d] - 1.0, 3) for d in DESIGNS}})
+                         "error": {d: round(pred[d] / meas[d] - 1.0, 3) for d in designs}})
         return {"load_latency_us": round(lat, 3), "launch_gap_us": round(gap, 3), "rows": rows,
                 "pairwise_agreement": round(pairs_ok / pairs, 3), "pairs": pairs,
                 "best_design_correct": best_ok, "batches": len(rows),
@@ -132,7 +139,7 @@ class Planner:
 def markdown(ev) -> str:
     out = ["| batch | design | predicted µs | measured µs | error |", "|---|---|---|---|---|"]
     for r in ev["rows"]:
-        for d in DESIGNS:
+        for d in r["predicted_us"]:
             mark = (" (predicted best)" if d == r["predicted_best"] else "") + \
                    (" (measured best)" if d == r["measured_best"] else "")
             out.append(f"| {r['batch']} | {d}{mark} | {r['predicted_us'][d]} | {r['measured_us'][d]} | "

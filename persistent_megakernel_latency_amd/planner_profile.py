@@ -8,7 +8,9 @@ epilogue through the publish: medians over the step's tiles of that type) and
 the hop latency (median time from the last producer's publish to a waiting
 consumer's start).  It then times the candidate designs on the same inputs:
 the megakernel with tile-to-tile edges (default), with barrier edges, without
-weight prefetch, with 256 workers, and the per-operator hipGraph baseline.
+weight prefetch, with 256 workers, the per-operator hipGraph baseline, and two
+co-resident megakernels (attention and combine tiles in one of 128 or 256
+workers, every other tile in the other).
 
     python -m persistent_megakernel_latency_amd.planner_profile --out profiles/planner_profiles.json
 """
@@ -32,6 +34,7 @@ TIMING = np.dtype([("t_claim", "<i8"), ("t_inputs", "<i8"), ("t_ready", "<i8"), 
 
 
 GEMM_TYPES = (0, 3, 4, 5, 6)  # qkv, o-proj, gate/up, down, LM head
+SPLITS = (128, 256)  # workers of the attention megakernel in the two-megakernel designs
 
 
 def tile_costs(wpk, plan, info, wide, hidden, ffn):
@@ -159,6 +162,10 @@ def run(batches, steps, warmup):
         plan = wpk.wpk_build_graph_baseline(desc.desc, batch, cap)
         entry["measured_us"]["conventional"] = timed(plan)
         wpk.wpk_destroy(plan)
+        for w1 in SPLITS:
+            plan = wpk.wpk_build_ex(desc.desc, batch, cap, wpk.wpk_build_opts(split_workers=w1))
+            entry["measured_us"][f"split_{w1}"] = timed(plan)
+            wpk.wpk_destroy(plan)
         out["batches"][str(batch)] = entry
         print(json.dumps({"batch": batch, **entry["measured_us"], "hop_us": entry["hop_us"]}), flush=True)
         del kc, vc

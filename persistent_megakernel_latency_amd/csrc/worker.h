@@ -197,18 +197,19 @@ __device__ __forceinline__ const float* x_in(const Params& P, int l) {
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
 
-__device__ __forceinline__ uint16_t to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (uint16_t)((u >> 16) | 0x40u);
-  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-}
-
-// two finite floats rounded to bf16 (to nearest, ties to even) in one word,
-// a in the low half
+// two floats rounded to bf16 (to nearest, ties to even; one v_cvt_pk_bf16_f32,
+// which matches the bit-level rounding on every non-NaN input, denormals
+// included, and gives a quiet NaN for a NaN) in one word, a in the low half
 __device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   typedef float f32x2 __attribute__((ext_vector_type(2)));
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+__device__ __forceinline__ uint16_t to_bf16(float f) { return (uint16_t)(cvt_bf16x2(f, 0.f) & 0xFFFFu); }
+// f as bf16 hi + lo parts: two words, element pairs (a, b) in the low and high halves
+__device__ __forceinline__ void split_hilo2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = cvt_bf16x2(a, b);
+  lo = cvt_bf16x2(a - bf16_lo(hi), b - bf16_hi(hi));
 }
 
 // a.lo * b.lo + a.hi * b.hi + c over the bf16 halves of two 32-bit words
@@ -1655,9 +1656,7 @@ __device__ __forceinline__ bool ctl_wide_post(const Params& P, const Tile& T0, S
         const f32x4 own = *(const f32x4*)&tr[n * TP + r4];
         const size_t at = ((((size_t)l * P.B + n) * P.Hkv + T.g) * P.cap + p) * P.D + r4;
         if (T.kind == 2) {
-          st_sc1_x2((uint16_t*)P.vc, (uint32_t)(at * 2),
-                    u32x2{(uint32_t)to_bf16(own.x) | ((uint32_t)to_bf16(own.y) << 16),
-                          (uint32_t)to_bf16(own.z) | ((uint32_t)to_bf16(own.w) << 16)});
+          st_sc1_x2((uint16_t*)P.vc, (uint32_t)(at * 2), u32x2{cvt_bf16x2(own.x, own.y), cvt_bf16x2(own.z, own.w)});
           continue;
         }
         const int lo = r4 < 32;  // this lane holds the first rows of its pairs
@@ -1673,9 +1672,7 @@ __device__ __forceinline__ bool ctl_wide_post(const Params& P, const Tile& T0, S
           st_sc1_x4(qd, (uint32_t)r4 * 4u,
                     u32x4{__float_as_uint(o0), __float_as_uint(o1), __float_as_uint(o2), __float_as_uint(o3)});
         } else {
-          st_sc1_x2((uint16_t*)P.kc, (uint32_t)(at * 2),
-                    u32x2{(uint32_t)to_bf16(o0) | ((uint32_t)to_bf16(o1) << 16),
-                          (uint32_t)to_bf16(o2) | ((uint32_t)to_bf16(o3) << 16)});
+          st_sc1_x2((uint16_t*)P.kc, (uint32_t)(at * 2), u32x2{cvt_bf16x2(o0, o1), cvt_bf16x2(o2, o3)});
         }
       }
       break;
@@ -1705,13 +1702,11 @@ __device__ __forceinline__ bool ctl_wide_post(const Params& P, const Tile& T0, S
           st_sc1_x4(dst, at * 4u,
                     u32x4{__float_as_uint(x0), __float_as_uint(x1), __float_as_uint(x2), __float_as_uint(x3)});
           const float g0 = g4.x * x0, g1 = g4.y * x1, g2 = g4.z * x2, g3 = g4.w * x3;
-          const uint16_t h0 = to_bf16(g0), h1 = to_bf16(g1), h2 = to_bf16(g2), h3 = to_bf16(g3);
-          st_sc1_x2(plane, at * 2u,
-                    u32x2{(uint32_t)h0 | ((uint32_t)h1 << 16), (uint32_t)h2 | ((uint32_t)h3 << 16)});
-          const uint16_t l0 = to_bf16(g0 - bf16_lo(h0)), l1 = to_bf16(g1 - bf16_lo(h1)),
-                         l2 = to_bf16(g2 - bf16_lo(h2)), l3 = to_bf16(g3 - bf16_lo(h3));
-          st_sc1_x2(plane, (uint32_t)(kMaxBatch * P.H) * 2u + at * 2u,
-                    u32x2{(uint32_t)l0 | ((uint32_t)l1 << 16), (uint32_t)l2 | ((uint32_t)l3 << 16)});
+          uint32_t h01, l01, h23, l23;
+          split_hilo2(g0, g1, h01, l01);
+          split_hilo2(g2, g3, h23, l23);
+          st_sc1_x2(plane, at * 2u, u32x2{h01, h23});
+          st_sc1_x2(plane, (uint32_t)(kMaxBatch * P.H) * 2u + at * 2u, u32x2{l01, l23});
         }
         sq = group_sum<16>(sq);
         if (s16 == 0 && n < P.B) st_sc1(ssd + (T.r0 / kWideRows) * kMaxBatch + n, sq);
@@ -1730,12 +1725,11 @@ __device__ __forceinline__ bool ctl_wide_post(const Params& P, const Tile& T0, S
         const float h0 = g.x / (1.0f + __expf(-g.x)) * u.x, h1 = g.y / (1.0f + __expf(-g.y)) * u.y,
                     h2 = g.z / (1.0f + __expf(-g.z)) * u.z, h3 = g.w / (1.0f + __expf(-g.w)) * u.w;
         const uint32_t at = (uint32_t)(n * P.F + T.r0 + r4) * 2u;
-        const uint16_t a0 = to_bf16(h0), a1 = to_bf16(h1), a2 = to_bf16(h2), a3 = to_bf16(h3);
-        st_sc1_x2(xh, at, u32x2{(uint32_t)a0 | ((uint32_t)a1 << 16), (uint32_t)a2 | ((uint32_t)a3 << 16)});
-        const uint16_t b0 = to_bf16(h0 - bf16_lo(a0)), b1 = to_bf16(h1 - bf16_lo(a1)),
-                       b2 = to_bf16(h2 - bf16_lo(a2)), b3 = to_bf16(h3 - bf16_lo(a3));
-        st_sc1_x2(xh, (uint32_t)(kMaxBatch * P.F) * 2u + at,
-                  u32x2{(uint32_t)b0 | ((uint32_t)b1 << 16), (uint32_t)b2 | ((uint32_t)b3 << 16)});
+        uint32_t a01, b01, a23, b23;
+        split_hilo2(h0, h1, a01, b01);
+        split_hilo2(h2, h3, a23, b23);
+        st_sc1_x2(xh, at, u32x2{a01, a23});
+        st_sc1_x2(xh, (uint32_t)(kMaxBatch * P.F) * 2u + at, u32x2{b01, b23});
       }
       break;
     }
@@ -1800,9 +1794,7 @@ __device__ __forceinline__ void ctl_norm(const Params& P, const Tile& T0, const 
       const float y0 = v[i] * gg[i], y1 = v[i + 1] * gg[i + 1];
       sq = fmaf(v[i], v[i], sq);
       sq = fmaf(v[i + 1], v[i + 1], sq);
-      const uint16_t h0 = to_bf16(y0), h1 = to_bf16(y1);
-      hw[i / 2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-      lw[i / 2] = (uint32_t)to_bf16(y0 - bf16_lo(h0)) | ((uint32_t)to_bf16(y1 - bf16_lo(h1)) << 16);
+      split_hilo2(y0, y1, hw[i / 2], lw[i / 2]);
     }
     st_sc1_x4(dst, (uint32_t)(b * K + e) * 2u, u32x4{hw[0], hw[1], hw[2], hw[3]});
     st_sc1_x4(dst, (uint32_t)((kMaxBatch + b) * K + e) * 2u, u32x4{lw[0], lw[1], lw[2], lw[3]});

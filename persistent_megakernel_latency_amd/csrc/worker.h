@@ -1668,8 +1668,10 @@ __device__ __forceinline__ bool ctl_wide_post(const Params& P, const Tile& T0, S
         const float o0 = own.x * cs.x + sg * oth.x * sn.x, o1 = own.y * cs.y + sg * oth.y * sn.y,
                     o2 = own.z * cs.z + sg * oth.z * sn.z, o3 = own.w * cs.w + sg * oth.w * sn.w;
         if (T.kind == 0) {
-          float* qd = act(P, l, P.off_q) + (size_t)n * P.Hq * P.D + T.g * P.D;
-          st_sc1_x4(qd, (uint32_t)r4 * 4u,
+          // a wave-uniform base (the buffer descriptor lives in scalar
+          // registers); the sequence goes into the per-lane offset
+          float* qd = act(P, l, P.off_q) + T.g * P.D;
+          st_sc1_x4(qd, (uint32_t)(n * P.Hq * P.D + r4) * 4u,
                     u32x4{__float_as_uint(o0), __float_as_uint(o1), __float_as_uint(o2), __float_as_uint(o3)});
         } else {
           st_sc1_x2((uint16_t*)P.kc, (uint32_t)(at * 2), u32x2{cvt_bf16x2(o0, o1), cvt_bf16x2(o2, o3)});
@@ -1742,12 +1744,19 @@ __device__ __forceinline__ bool ctl_wide_post(const Params& P, const Tile& T0, S
         if (n < P.B) {
           const f32x4 v = *(const f32x4*)&tr[n * TP + r4];
           const float vv[4] = {v.x, v.y, v.z, v.w};
+          const int row0 = T.r0 + r4;
+          float* lg = P.logits + (size_t)n * P.V + row0;
+          if (row0 + 3 < P.V && (P.V & 3) == 0) {
+            *(f32x4*)lg = v;  // four logits in one 16-byte store (rows of a vocab that is a multiple of 4)
+          } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              if (row0 + k < P.V) lg[k] = vv[k];
+          }
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
-            const int row = T.r0 + r4 + k;
-            if (row < P.V) {
-              P.logits[(size_t)n * P.V + row] = vv[k];
-              const unsigned long long c = pack_max(vv[k], row);
+            if (row0 + k < P.V) {
+              const unsigned long long c = pack_max(vv[k], row0 + k);
               key = c > key ? c : key;
             }
           }

@@ -18,10 +18,12 @@ blocks; at batch 1 the same K steps also run in one persistent session (the
 grid kept resident, steps rung from the host) under "persistent"; the ablations (Table I features switched off one at a time) run one
 block each, and the CPU oracle is timed on a bounded sample of the same
 workload.  A second workload, batch 32 with per-sequence contexts drawn from
-U{256..1024} (the matrix-core path), is reported under "batch32".
+U{256..1024} (the matrix-core path), is reported under "batch32"; the time
+to first token of 496-token prompts at batch 16 (the prefill: one megakernel,
+two co-resident megakernels, the per-operator graph) under "ttft".
 
     python bench.py [--steps 64] [--warmup 3] [--reps 5] [--no-cpu] [--no-baseline]
-                    [--no-batch32] [--no-ablations] [--no-persistent]
+                    [--no-batch32] [--no-ablations] [--no-persistent] [--no-ttft] [--ttft-runs 10]
 """
 from __future__ import annotations
 
@@ -40,6 +42,7 @@ METRIC = "decode step latency (µs) + achieved HBM GB/s, Llama-1B-shape, batch 1
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 CONTEXT = 496
+TTFT_PROMPT = 496
 
 
 def step_bytes(cfg, batch: int, positions_before: np.ndarray) -> float:
@@ -213,6 +216,74 @@ def persistent_block(wpk, W: Workload, desc, args, launched_per):
             "how": "one cooperative grid for all steps; K steps rung at once; host waits on pinned memory"}
 
 
+def ttft_block(wpk, torch, cfg, desc, args, dev):
+    """Time to first token (the Table III workload of "One Megakernel is Not
+    Enough" at the Llama-3.2-1B shape): batch 16, a 496-token prompt of
+    seeded random ids, prefill through every layer and the LM head on each
+    sequence's last prompt row (the first greedy token).  Run as one
+    megakernel, as two co-resident megakernels (attention tiles in their own
+    worker pool) and as the per-operator hipGraph; each run is bracketed by
+    HIP events on the launch stream."""
+    import synth
+    batch, P, cap = 16, TTFT_PROMPT, 512
+    prompt = torch.from_numpy(synth.prompt_tokens(cfg, batch, P, seed=4).astype(np.int32)).to(dev)
+    shape = (cfg.n_layers, batch, cfg.n_kv_heads, cap, cfg.head_dim)
+    kc = torch.zeros(shape, dtype=torch.int16, device=dev)
+    vc = torch.zeros(shape, dtype=torch.int16, device=dev)
+    seq = torch.zeros(batch, dtype=torch.int32, device=dev)
+    logits = torch.empty((batch, cfg.vocab), dtype=torch.float32, device=dev)
+    tok = torch.empty(batch, dtype=torch.int32, device=dev)
+    kv = wpk.wpk_kv(kc.data_ptr(), vc.data_ptr(), seq.data_ptr())
+    stream = torch.cuda.current_stream(dev)
+    out = {"workload": f"Llama-3.2-1B-shape prefill, batch {batch}, {P}-token prompts, first greedy token",
+           "batch": batch, "prompt": P}
+    first = None
+    for name, mode in (("megakernel", wpk.WPK_PREFILL_MEGAKERNEL), ("split", wpk.WPK_PREFILL_SPLIT),
+                       ("graph_baseline", wpk.WPK_PREFILL_GRAPH)):
+        plan = wpk.wpk_build_prefill(desc.desc, batch, cap, P, wpk.wpk_prefill_opts(mode=mode))
+        if not plan:
+            raise RuntimeError("wpk_build_prefill: " + wpk.wpk_prefill_last_error(None))
+        info = wpk.wpk_prefill_get_info(plan)
+
+        def go():
+            wpk.check_prefill(wpk.wpk_prefill(plan, prompt.data_ptr(), kv, logits.data_ptr(), tok.data_ptr(),
+                                              stream.cuda_stream), plan, name)
+        for _ in range(args.warmup):
+            go()
+        wpk.check_prefill(wpk.wpk_prefill_sync(plan), plan, name)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.ttft_runs)]
+        torch.cuda.synchronize(dev)
+        w0 = time.perf_counter()
+        for e0, e1 in ev:
+            e0.record(stream)
+            go()
+            e1.record(stream)
+        torch.cuda.synchronize(dev)
+        wall = time.perf_counter() - w0
+        wpk.check_prefill(wpk.wpk_prefill_sync(plan), plan, name)
+        per = np.array([a.elapsed_time(b) * 1000.0 for a, b in ev])
+        toks = tok.cpu().numpy().tolist()
+        if first is None:
+            first = toks
+        wpk.wpk_prefill_destroy(plan)
+        progress(f"ttft: {name}")
+        out[name] = {"value": round(wall / args.ttft_runs * 1e6, 1), "unit": "µs", "latency_us": lat(per),
+                     "workers": info.workers, "split_workers": info.split_workers, "tiles": info.n_tiles,
+                     "kernels": 1 if mode != wpk.WPK_PREFILL_GRAPH else info.n_phases,
+                     "same_tokens_as_megakernel": toks == first}
+        out["flops"] = info.flops
+    mk = out["megakernel"]["latency_us"]["mean"]
+    achieved = out["flops"] / (mk * 1e-6) / 1e12
+    out["mfma"] = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                   "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                   "kernel": "wpk::prefill_megakernel", "source_hash": wpk.prefill_source_hash()}
+    out["split_vs_megakernel"] = round(out["split"]["latency_us"]["mean"] / mk, 3)
+    out["graph_vs_megakernel"] = round(out["graph_baseline"]["latency_us"]["mean"] / mk, 3)
+    out["first_tokens"] = first
+    return out
+
+
 def roofline(byts, per, shash, kernel_key, traffic_name):
     achieved = float(np.mean(byts) / (per.mean() * 1e-6) / 1e9)
     traffic = profile_record(traffic_name, shash)
@@ -319,6 +390,9 @@ def run(args):
             result["batch32"]["ablations"] = m32["ablations"]
         del W32
 
+    if not args.no_ttft:
+        result["ttft"] = ttft_block(wpk, torch, cfg, desc, args, dev)
+
     if not args.no_cpu:
         progress("cpu baseline (oracle)")
         kc_np, vc_np = synth.synthetic_kv(cfg, batch, cap, lens0)
@@ -360,6 +434,8 @@ def main():
     ap.add_argument("--no-ablations", action="store_true")
     ap.add_argument("--no-persistent", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-ttft", action="store_true")
+    ap.add_argument("--ttft-runs", type=int, default=10)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: this build runs on a "

@@ -390,6 +390,97 @@ int32_t wpk_debug_drop_edge(wpk_plan* plan, int32_t tile);
  * first.  Returns 0 or a negative WPK_E code. */
 int32_t wpk_debug_read_act(wpk_plan* plan, void* host_dst, size_t bytes, size_t* out_bytes);
 
+/* ---- prompt prefill: time to first token ---------------------------------------
+ * Source: "One Megakernel is Not Enough", Table III (the Llama 3.2 1B row:
+ * time to first token for a 496-token prompt, batches up to 48) and the
+ * abstract and Table I (producer-consumer overlap of a split region with its
+ * own smaller CTA budget; one megakernel against several co-resident ones and
+ * against the conventional per-operator execution).  The prefill runs the
+ * whole prompt of every sequence through every layer at once -- RMSNorm, QKV
+ * with RoPE, the K/V of all prompt positions appended to the cache, causal
+ * grouped-query attention over the prompt, o-projection, SwiGLU MLP -- and
+ * the tied LM head on each sequence's last prompt position gives the first
+ * generated token (greedy, lowest index on ties).  Matrix products run on the
+ * matrix cores in bf16 with fp32 accumulation: activations, queries and
+ * attention probabilities are rounded to bf16 at each product's input; the
+ * residual stream, RMSNorm, RoPE and softmax run in fp32.
+ *
+ * wpk_build_prefill: model (DEVICE pointers, bf16 weights, hidden and ffn
+ *   multiples of 128 and 64, n_q_heads + 2 n_kv_heads even), batch in [1, 32],
+ *   ctx_len (the KV cache capacity), prompt_len in [1, ctx_len].  opts (NULL:
+ *   defaults) picks the execution:
+ *     WPK_PREFILL_MEGAKERNEL: one persistent kernel, all tiles;
+ *     WPK_PREFILL_SPLIT: two co-resident megakernels in one launch -- the last
+ *       split_workers workers (default an eighth) claim only the attention
+ *       tiles, the others every other tile, and they wait on each other
+ *       through the same counters;
+ *     WPK_PREFILL_GRAPH: the conventional baseline, one kernel per (layer,
+ *       operator) over the same tile bodies, captured once into a hipGraph.
+ *   Returns NULL on error (wpk_prefill_last_error(NULL) says why).
+ * wpk_build_prefill_host: the same DAG without a device (inspection only:
+ *   get_info / get_dag; wpk_prefill refuses it).
+ * wpk_prefill: prompt is device int32[batch][prompt_len]; kv as for wpk_step
+ *   (the cache positions [0, prompt_len) of every sequence are overwritten,
+ *   seq_len is set to prompt_len); logits: device float32[batch][vocab], the
+ *   last prompt position's; tokens_out: device int32[batch], the first
+ *   generated token.  One launch (or graph launch) enqueued on stream.  A token
+ *   id outside [0, vocab) latches WPK_E_TOKEN (read by wpk_prefill_sync).
+ * wpk_prefill_sync: waits for the last prefill and returns the latched device
+ *   status (as wpk_sync); a latched plan refuses to run until WPK_OPT_RESET.
+ * wpk_prefill_set_option: WPK_OPT_LOG (megakernel modes: per-tile log),
+ *   WPK_OPT_WATCHDOG_US, WPK_OPT_RESET.
+ * wpk_prefill_get_log: n_tiles wpk_log_rec of the last logged prefill
+ *   (exec_count, wait_delta, worker, claim, start / end stamps).
+ * wpk_prefill_get_dag: per tile id its type (wpk_prefill tile types below),
+ *   layer, waited and signalled groups, and (if queue is not NULL) its claim
+ *   queue.  Arrays of n_tiles.
+ * Ownership and errors as for the decode step. */
+#define WPK_PREFILL_MEGAKERNEL 0
+#define WPK_PREFILL_SPLIT 1
+#define WPK_PREFILL_GRAPH 2
+typedef struct wpk_prefill_opts {
+  int32_t mode;            /* WPK_PREFILL_* (default 0) */
+  int32_t split_workers;   /* WPK_PREFILL_SPLIT: workers of the attention megakernel (0: an eighth) */
+  int32_t workers_per_cu;  /* resident workers per compute unit, 1 or 2 (0: 2) */
+} wpk_prefill_opts;
+typedef struct wpk_prefill_info {
+  int32_t n_tiles, n_groups, n_queues;
+  int32_t workers;            /* workers launched (both megakernels of a split plan) */
+  int32_t max_workers;        /* co-residency limit found at build */
+  int32_t split_workers;      /* workers of the attention megakernel (split plans) */
+  int32_t n_phases;           /* kernels of the per-operator baseline */
+  int32_t rows_per_sequence;  /* prompt rows padded to the 128-row blocks */
+  int64_t workspace_bytes;
+  double flops;               /* matrix-product FLOPs of one prefill (2 per multiply-add) */
+} wpk_prefill_info;
+/* tile types of wpk_prefill_get_dag */
+#define WPK_PTILE_EMBED 0
+#define WPK_PTILE_NORM1 1
+#define WPK_PTILE_QKV 2
+#define WPK_PTILE_ATTN 3
+#define WPK_PTILE_OPROJ 4
+#define WPK_PTILE_NORM2 5
+#define WPK_PTILE_GATEUP 6
+#define WPK_PTILE_DOWN 7
+#define WPK_PTILE_NORMF 8
+#define WPK_PTILE_LM 9
+#define WPK_PTILE_ARGMAX 10
+typedef struct wpk_prefill_plan wpk_prefill_plan;
+wpk_prefill_plan* wpk_build_prefill(const wpk_model_desc* desc, int32_t batch, int32_t ctx_len, int32_t prompt_len,
+                                    const wpk_prefill_opts* opts);
+wpk_prefill_plan* wpk_build_prefill_host(const wpk_model_desc* desc, int32_t batch, int32_t ctx_len,
+                                         int32_t prompt_len, const wpk_prefill_opts* opts);
+int32_t wpk_prefill(wpk_prefill_plan* plan, const int32_t* prompt, wpk_kv* kv, void* logits, int32_t* tokens_out,
+                    wpk_stream_t stream);
+int32_t wpk_prefill_sync(wpk_prefill_plan* plan);
+void wpk_prefill_destroy(wpk_prefill_plan* plan);
+const char* wpk_prefill_last_error(const wpk_prefill_plan* plan);
+int32_t wpk_prefill_set_option(wpk_prefill_plan* plan, int32_t key, int64_t value);
+int32_t wpk_prefill_get_log(wpk_prefill_plan* plan, void* host_dst, size_t bytes);
+int32_t wpk_prefill_get_info(const wpk_prefill_plan* plan, wpk_prefill_info* out);
+int32_t wpk_prefill_get_dag(const wpk_prefill_plan* plan, int32_t* type, int32_t* layer, int32_t* wait,
+                            int32_t* signal, int32_t* queue);
+
 #ifdef __cplusplus
 }
 #endif

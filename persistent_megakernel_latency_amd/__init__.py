@@ -99,6 +99,23 @@ class wpk_sim_result(ctypes.Structure):
                 ("worker_busy_frac", ctypes.c_double)]
 
 
+WPK_PREFILL_MEGAKERNEL = 0
+WPK_PREFILL_SPLIT = 1
+WPK_PREFILL_GRAPH = 2
+
+PREFILL_TILE_TYPES = ["embed", "norm1", "qkv", "attn", "oproj", "norm2", "gateup", "down", "normf", "lm", "argmax"]
+
+
+class wpk_prefill_opts(ctypes.Structure):
+    _fields_ = [("mode", _i32), ("split_workers", _i32), ("workers_per_cu", _i32)]
+
+
+class wpk_prefill_info(ctypes.Structure):
+    _fields_ = [("n_tiles", _i32), ("n_groups", _i32), ("n_queues", _i32), ("workers", _i32), ("max_workers", _i32),
+                ("split_workers", _i32), ("n_phases", _i32), ("rows_per_sequence", _i32),
+                ("workspace_bytes", ctypes.c_int64), ("flops", ctypes.c_double)]
+
+
 # Every symbol include/wpk.h declares, with its ctypes signature.
 _SIGNATURES = {
     "wpk_build": (_vp, [ctypes.POINTER(wpk_model_desc), _i32, _i32]),
@@ -124,6 +141,17 @@ _SIGNATURES = {
     "wpk_emulate_step": (_i32, [_vp, _vp, ctypes.POINTER(wpk_kv), _vp, _i32, ctypes.c_uint64]),
     "wpk_debug_drop_edge": (_i32, [_vp, _i32]),
     "wpk_debug_read_act": (_i32, [_vp, _vp, ctypes.c_size_t, ctypes.POINTER(ctypes.c_size_t)]),
+    "wpk_build_prefill": (_vp, [ctypes.POINTER(wpk_model_desc), _i32, _i32, _i32, ctypes.POINTER(wpk_prefill_opts)]),
+    "wpk_build_prefill_host": (_vp, [ctypes.POINTER(wpk_model_desc), _i32, _i32, _i32,
+                                     ctypes.POINTER(wpk_prefill_opts)]),
+    "wpk_prefill": (_i32, [_vp, _vp, ctypes.POINTER(wpk_kv), _vp, _vp, _vp]),
+    "wpk_prefill_sync": (_i32, [_vp]),
+    "wpk_prefill_destroy": (None, [_vp]),
+    "wpk_prefill_last_error": (ctypes.c_char_p, [_vp]),
+    "wpk_prefill_set_option": (_i32, [_vp, _i32, ctypes.c_int64]),
+    "wpk_prefill_get_log": (_i32, [_vp, _vp, ctypes.c_size_t]),
+    "wpk_prefill_get_info": (_i32, [_vp, ctypes.POINTER(wpk_prefill_info)]),
+    "wpk_prefill_get_dag": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp]),
 }
 
 _lib = None
@@ -270,6 +298,80 @@ def wpk_debug_read_act(plan):
     out = np.empty(n.value // 4, np.float32)
     check(lib().wpk_debug_read_act(plan, out.ctypes.data, n.value, ctypes.byref(n)), plan, "wpk_debug_read_act")
     return out
+
+
+# ---- prompt prefill ---------------------------------------------------------------------
+
+def wpk_build_prefill(desc: wpk_model_desc, batch: int, ctx_len: int, prompt_len: int,
+                      opts: Optional[wpk_prefill_opts] = None):
+    return lib().wpk_build_prefill(ctypes.byref(desc), batch, ctx_len, prompt_len,
+                                   ctypes.byref(opts) if opts else None)
+
+
+def wpk_build_prefill_host(desc: wpk_model_desc, batch: int, ctx_len: int, prompt_len: int,
+                           opts: Optional[wpk_prefill_opts] = None):
+    return lib().wpk_build_prefill_host(ctypes.byref(desc), batch, ctx_len, prompt_len,
+                                        ctypes.byref(opts) if opts else None)
+
+
+def wpk_prefill(plan, prompt_ptr: int, kv: wpk_kv, logits_ptr: int, tokens_out_ptr: int, stream_ptr: int = 0) -> int:
+    return lib().wpk_prefill(plan, prompt_ptr, ctypes.byref(kv), logits_ptr, tokens_out_ptr, stream_ptr or None)
+
+
+def wpk_prefill_sync(plan) -> int:
+    return lib().wpk_prefill_sync(plan)
+
+
+def wpk_prefill_destroy(plan) -> None:
+    lib().wpk_prefill_destroy(plan)
+
+
+def wpk_prefill_last_error(plan=None) -> str:
+    r = lib().wpk_prefill_last_error(plan)
+    return r.decode() if r else ""
+
+
+def wpk_prefill_set_option(plan, key: int, value: int) -> int:
+    return lib().wpk_prefill_set_option(plan, key, value)
+
+
+def wpk_prefill_get_log(plan, n_tiles: int):
+    buf = (wpk_log_rec * n_tiles)()
+    rc = lib().wpk_prefill_get_log(plan, ctypes.cast(buf, _vp), ctypes.sizeof(buf))
+    return rc, buf
+
+
+def wpk_prefill_get_info(plan) -> wpk_prefill_info:
+    info = wpk_prefill_info()
+    rc = lib().wpk_prefill_get_info(plan, ctypes.byref(info))
+    if rc != WPK_OK:
+        raise RuntimeError(f"wpk_prefill_get_info failed: {rc}")
+    return info
+
+
+def wpk_prefill_get_dag(plan, n_tiles: int):
+    """[type, layer, wait, signal, queue] lists, one entry per tile id."""
+    arrs = [(_i32 * n_tiles)() for _ in range(5)]
+    rc = lib().wpk_prefill_get_dag(plan, *[ctypes.cast(a, _vp) for a in arrs])
+    if rc != WPK_OK:
+        raise RuntimeError(f"wpk_prefill_get_dag failed: {rc}")
+    return [list(a) for a in arrs]
+
+
+def check_prefill(rc: int, plan=None, what: str = "wpk_prefill call") -> None:
+    if rc != WPK_OK:
+        raise RuntimeError(f"{what} failed ({rc}): {wpk_prefill_last_error(plan)}")
+
+
+def prefill_source_hash() -> str:
+    """Hash of the sources that decide what the prefill kernels do."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("prefill.hip", "prefill_plan.h", "prefill_builder.cpp", "prefill_builder.h", "prefill_capi.cpp",
+              "worker.h", "plan.h"):
+        with open(os.path.join(_HERE, "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 # ---- descriptor marshalling ------------------------------------------------------------

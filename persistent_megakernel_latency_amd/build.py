@@ -27,8 +27,8 @@ HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-D__HIP_PLATFORM_AMD__",
               "-I" + os.path.join(ROOT, "include"), "-I" + CSRC, "-I/opt/rocm/include"]
 
-DEVICE_SOURCES = ["megakernel.hip", "persist.hip"]
-HOST_SOURCES = ["capi.cpp", "builder.cpp", "host_exec.cpp", "planner.cpp"]
+DEVICE_SOURCES = ["megakernel.hip", "persist.hip", "prefill.hip"]
+HOST_SOURCES = ["capi.cpp", "builder.cpp", "host_exec.cpp", "planner.cpp", "prefill_builder.cpp", "prefill_capi.cpp"]
 
 
 def _run(cmd):

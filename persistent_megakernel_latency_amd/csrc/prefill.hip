@@ -1,0 +1,680 @@
+// prefill.hip -- the prompt prefill (time to first token) as one persistent
+// kernel on gfx950, and the conventional one-kernel-per-operator baseline
+// built from the same tile bodies.
+//
+// A worker is four waves that all compute: prefill tiles are compute-bound
+// (a matrix-core tile is 128 x 128 x K), so the decode step's split into a
+// latency-hiding control wave and weight-streaming compute waves buys
+// nothing here.  Wave 0 polls the tile's counter group; thread 0 claims the
+// next tile while the current one runs, then publishes.
+//
+// Coherence.  The eight XCDs' L2 caches are not coherent with each other.
+// Outputs are written with device-coherent (sc1, write-through) stores, and
+// the publish is a relaxed device-scope increment after they completed (the
+// decode step's protocol).  Inputs are read with ordinary, cacheable loads:
+// every activation buffer of a layer is written exactly once per prefill and
+// read only after its counter group completed, so no L2 or L1 can hold a
+// stale copy of a line a tile reads (a cache only holds lines read during
+// this launch, and each line is read only after its one write; the caches
+// start clean at every kernel boundary).  This lets the 24 QKV tiles of a
+// row block share its operand rows through the L2 of their XCD.
+#include "prefill_plan.h"
+#include "worker.h"
+
+namespace wpk {
+namespace {
+
+constexpr int kVtPitch = 40;  // bf16 elements per transposed V row (32 keys + pad)
+
+struct PSmem {
+  alignas(16) uint16_t vt[2][kHeadDim][kVtPitch];  // attention: one key step of V, [dim][key]
+  int claim[2];
+  int stop;
+};
+
+__device__ __forceinline__ void p_latch(const PParams& P, int32_t code, int32_t tile) {
+  uint32_t zero = 0;
+  if (__hip_atomic_compare_exchange_strong(&P.ctl[CTL_STATUS], &zero, (uint32_t)code, __ATOMIC_RELAXED,
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+    st_sc1(&P.ctl[CTL_STATUS + 1], (uint32_t)tile);
+    st_sc1(&P.ctl[CTL_STATUS + 2], (uint32_t)blockIdx.x);
+    st_sc1(&P.ctl[CTL_STATUS + 3], ld_sc1(&P.ctl[CTL_EPOCH]));
+  }
+  st_sc1(&P.ctl[CTL_ABORT], 1u);
+}
+
+// Bounded wait for the tile's counter group (wave 0; the same sharded
+// counters and epoch targets as the decode step).
+__device__ __forceinline__ bool p_wait(const PParams& P, const Tile& T, uint32_t epoch, int32_t* delta, int lane) {
+  const Group G = cload(P.groups, T.wait);
+  const uint32_t target = (epoch + 1u) * (uint32_t)G.producers;
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  for (;;) {
+    const uint32_t v0 = lane < G.shards ? ld_sc1(&P.counters[(size_t)(G.shard0 + lane) * kLine]) : 0u;
+    const uint32_t v1 = lane + 64 < G.shards ? ld_sc1(&P.counters[(size_t)(G.shard0 + lane + 64) * kLine]) : 0u;
+    const uint32_t sum = wave_sum_u32(v0 + v1);
+    if ((int32_t)(sum - target) >= 0) {
+      *delta = (int32_t)(sum - target);
+      compiler_order();
+      return true;
+    }
+    if (ld_sc1(&P.ctl[CTL_ABORT])) return false;
+    if (__builtin_amdgcn_s_memrealtime() - t0 > P.watchdog_ticks) {
+      if (lane == 0) p_latch(P, WPK_E_TIMEOUT, T.id);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(4);
+  }
+}
+
+__device__ __forceinline__ u32x4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ u32x2 bf16x4(f32x4 v) { return u32x2{cvt_bf16x2(v[0], v[1]), cvt_bf16x2(v[2], v[3])}; }
+// Four fp32 values as bf16 hi + lo parts (value = hi + lo), stored 8 bytes
+// into each plane of an operand buffer (lo plane `plane` elements after hi).
+__device__ __forceinline__ void st_hilo4(uint16_t* hi, size_t plane, uint32_t byte_off, f32x4 v) {
+  uint32_t h0, h1, l0, l1;
+  split_hilo2(v[0], v[1], h0, l0);
+  split_hilo2(v[2], v[3], h1, l1);
+  st_sc1_x2(hi, byte_off, u32x2{h0, h1});
+  st_sc1_x2(hi + plane, byte_off, u32x2{l0, l1});
+}
+// Eight fp32 values as a bf16x8 hi part and a bf16x8 lo part.
+__device__ __forceinline__ bf16x8 hilo8(f32x4 a, f32x4 b, bf16x8& lo) {
+  uint32_t h[4], l[4];
+  split_hilo2(a[0], a[1], h[0], l[0]);
+  split_hilo2(a[2], a[3], h[1], l[1]);
+  split_hilo2(b[0], b[1], h[2], l[2]);
+  split_hilo2(b[2], b[3], h[3], l[3]);
+  lo = as_bf16x8(u32x4{l[0], l[1], l[2], l[3]});
+  return as_bf16x8(u32x4{h[0], h[1], h[2], h[3]});
+}
+
+// ---- RMSNorm of rows -------------------------------------------------------------------------
+// y = x / sqrt(mean(x^2) + eps) * gain, stored as the hi and lo bf16 planes
+// of the matrix-core operand.  One wave per row at a time: each lane sums the squares of its
+// 16-byte chunks in order, then a fixed wave tree; a second pass re-reads the
+// row (from the cache) to scale it.
+template <bool EMBED>
+__device__ __forceinline__ void norm_row(const PParams& P, const float* x, const uint16_t* emb, const float* gain,
+                                         float* x_copy, uint16_t* y, size_t plane, int lane) {
+  const int nc = P.H / 4;
+  float ss = 0.f;
+  for (int c = lane; c < nc; c += 64) {
+    f32x4 v;
+    if (EMBED) {
+      const u32x2 e = *(const u32x2*)(emb + 4 * c);
+      v = f32x4{bf16_lo(e.x), bf16_hi(e.x), bf16_lo(e.y), bf16_hi(e.y)};
+    } else {
+      v = *(const f32x4*)(x + 4 * c);
+    }
+    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+  }
+  ss = wave_sum(ss);
+  const float inv = 1.0f / sqrtf(ss / (float)P.H + P.eps);
+  for (int c = lane; c < nc; c += 64) {
+    f32x4 v;
+    if (EMBED) {
+      const u32x2 e = *(const u32x2*)(emb + 4 * c);
+      v = f32x4{bf16_lo(e.x), bf16_hi(e.x), bf16_lo(e.y), bf16_hi(e.y)};
+      st_sc1_x4(x_copy, (uint32_t)c * 16u, __builtin_bit_cast(u32x4, v));
+    } else {
+      v = *(const f32x4*)(x + 4 * c);
+    }
+    const f32x4 g = *(const f32x4*)(gain + 4 * c);
+    st_hilo4(y, plane, (uint32_t)c * 8u, v * inv * g);
+  }
+}
+
+// A row block's norm: wave w takes rows 32w .. 32w+31.  Layer 0 gathers the
+// embedding rows (token ids checked; padding rows past the prompt are zero).
+__device__ void norm_tile(const PParams& P, const Tile& T, int tid) {
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const PLayer Lw = cload(P.layers, T.layer);
+  const size_t plane = (size_t)P.R * P.H;
+  for (int k = 0; k < kPRows / 4; ++k) {
+    const int r = T.r0 * kPRows + w * (kPRows / 4) + k;
+    const int b = r / P.Pp, p = r - b * P.Pp;
+    const size_t ro = (size_t)r * P.H;
+    if (T.type == P_EMBED) {
+      if (p >= P.P) {
+        for (int c = lane; c < P.H / 4; c += 64) {
+          st_sc1_x4(P.x0 + ro, (uint32_t)c * 16u, u32x4{0u, 0u, 0u, 0u});
+          st_sc1_x2(Lw.xn1 + ro, (uint32_t)c * 8u, u32x2{0u, 0u});
+          st_sc1_x2(Lw.xn1 + plane + ro, (uint32_t)c * 8u, u32x2{0u, 0u});
+        }
+        continue;
+      }
+      int tok = P.prompt[(size_t)b * P.P + p];
+      if (tok < 0 || tok >= P.V) {
+        if (lane == 0) p_latch(P, WPK_E_TOKEN, T.id);
+        tok = 0;
+      }
+      norm_row<true>(P, nullptr, P.embed + (size_t)tok * P.H, Lw.attn_norm, P.x0 + ro, Lw.xn1 + ro, plane, lane);
+    } else if (T.type == P_NORM1) {
+      norm_row<false>(P, Lw.x_in + ro, nullptr, Lw.attn_norm, nullptr, Lw.xn1 + ro, plane, lane);
+    } else {
+      norm_row<false>(P, Lw.x_mid + ro, nullptr, Lw.mlp_norm, nullptr, Lw.xn2 + ro, plane, lane);
+    }
+  }
+}
+
+// The final norm of one sequence's last prompt row (wave 0).
+__device__ void normf_tile(const PParams& P, const Tile& T, int tid) {
+  if (tid >= 64) return;
+  const PLayer Lw = cload(P.layers, P.L - 1);
+  const size_t r = (size_t)T.b * P.Pp + (P.P - 1);
+  norm_row<false>(P, Lw.x_out + r * P.H, nullptr, P.final_norm, nullptr, P.xf + (size_t)T.b * P.H,
+                  (size_t)kMaxBatch * P.H, tid);
+}
+
+// ---- matrix-core tiles: 128 prompt rows x 128 output columns x all of K ----------------------
+//
+// v_mfma_f32_16x16x32_bf16 with the weights as the A operand (lane l: weight
+// row l % 16, eight K values from 8 (l / 16)) and the activations as B (lane
+// l: prompt row l % 16, the same K values), twice: the operand's hi and lo
+// bf16 planes (bf16 weights are exact, so the two products keep about 16
+// significant bits of the activations); the 16 x 16 result leaves lane l
+// four consecutive output columns 4 (l / 16) + e of prompt row l % 16, so
+// epilogues store 8 or 16 contiguous bytes per lane.  Wave w computes rows
+// 64 (w & 1) .. +63 and columns 64 (w >> 1) .. +63 (one head of QKV): four
+// column blocks j x four row blocks i.  Fragments stream from the caches
+// straight into registers, the next k-step's loads in flight behind this
+// step's products.
+__device__ void gemm_tile(const PParams& P, const Tile& T0, int tid) {
+  const Tile T = uni(T0);
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = w & 1, wc = w >> 1;
+  const PLayer Lw = cload(P.layers, T.layer);
+  const uint16_t* A;
+  const uint16_t* W0;
+  const uint16_t* W1;
+  int K, wrow0, wrow1;  // weight rows of column blocks 0-1 and 2-3 (lane offset added below)
+  switch (T.type) {
+    case P_QKV:
+      A = Lw.xn1, W0 = W1 = Lw.w_qkv, K = P.H;
+      wrow0 = T.r1 * kPCols + 64 * wc, wrow1 = wrow0 + 32;
+      break;
+    case P_OPROJ:
+      A = Lw.ao, W0 = W1 = Lw.w_o, K = P.H;
+      wrow0 = T.r1 * kPCols + 64 * wc, wrow1 = wrow0 + 32;
+      break;
+    case P_GATEUP:
+      A = Lw.xn2, W0 = Lw.w_gate, W1 = Lw.w_up, K = P.H;
+      wrow0 = wrow1 = T.r1 * kPFfnCols + 32 * wc;
+      break;
+    default:  // P_DOWN
+      A = Lw.h, W0 = W1 = Lw.w_down, K = P.F;
+      wrow0 = T.r1 * kPCols + 64 * wc, wrow1 = wrow0 + 32;
+      break;
+  }
+  const int row0 = T.r0 * kPRows + 64 * wr;
+  const __amdgpu_buffer_rsrc_t ra = rsrc(A), rl = rsrc(A + (size_t)P.R * K), rw0 = rsrc(W0), rw1 = rsrc(W1);
+  const uint32_t kb = 16u * (uint32_t)(lane >> 4);  // byte offset of the lane's eight K values
+  uint32_t va[4], vw[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) va[i] = (uint32_t)(row0 + 16 * i + (lane & 15)) * (uint32_t)K * 2u + kb;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    vw[j] = (uint32_t)((j < 2 ? wrow0 + 16 * j : wrow1 + 16 * (j - 2)) + (lane & 15)) * (uint32_t)K * 2u + kb;
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 a[4], al[4], b[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[i] = ld16(ra, va[i], 0);
+    al[i] = ld16(rl, va[i], 0);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) b[j] = ld16(j < 2 ? rw0 : rw1, vw[j], 0);
+  for (int k0 = 0;; k0 += 32) {
+    const bool more = k0 + 32 < K;
+    u32x4 na[4], nal[4], nb[4];
+    if (more) {
+      const uint32_t so = (uint32_t)(k0 + 32) * 2u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        na[i] = ld16(ra, va[i], so);
+        nal[i] = ld16(rl, va[i], so);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) nb[j] = ld16(j < 2 ? rw0 : rw1, vw[j], so);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // the next step's loads stay ahead of this step's products
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[j][i] = mfma(as_bf16x8(b[j]), as_bf16x8(a[i]), acc[j][i]);
+        acc[j][i] = mfma(as_bf16x8(b[j]), as_bf16x8(al[i]), acc[j][i]);
+      }
+    if (!more) break;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] = na[i];
+      al[i] = nal[i];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = nb[j];
+  }
+
+  // epilogues: lane holds columns c_j + 4 (lane / 16) + e of prompt row r_i
+  const int e4 = 4 * (lane >> 4);
+  switch (T.type) {
+    case P_QKV: {
+      const int hh = 2 * T.r1 + wc;  // head of this wave's 64 columns: q heads, then k, then v
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = row0 + 16 * i + (lane & 15);
+        const int bq = r / P.Pp, p = r - bq * P.Pp;
+        if (p >= P.P) continue;  // padding rows: nothing stored
+        f32x4 y[4] = {acc[0][i], acc[1][i], acc[2][i], acc[3][i]};
+        if (hh < P.Hq + P.Hkv) {
+          // rotate-half RoPE: dims d < 32 pair with d + 32 (blocks j and j + 2)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const f32x4 cs = *(const f32x4*)(P.rope_cos + (size_t)p * 32 + 16 * j + e4);
+            const f32x4 sn = *(const f32x4*)(P.rope_sin + (size_t)p * 32 + 16 * j + e4);
+            const f32x4 x1 = acc[j][i], x2 = acc[j + 2][i];
+            y[j] = x1 * cs - x2 * sn;
+            y[j + 2] = x2 * cs + x1 * sn;
+          }
+        }
+        if (hh < P.Hq) {
+          float* qd = Lw.q + (size_t)r * P.Hq * kHeadDim + hh * kHeadDim;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) st_sc1_x4(qd, (uint32_t)(16 * j + e4) * 4u, __builtin_bit_cast(u32x4, y[j]));
+        } else {
+          const bool isk = hh < P.Hq + P.Hkv;
+          const int kh = isk ? hh - P.Hq : hh - P.Hq - P.Hkv;
+          uint16_t* cd = (isk ? P.kc : P.vc) +
+                         ((((size_t)T.layer * P.B + bq) * P.Hkv + kh) * P.cap + p) * kHeadDim;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) st_sc1_x2(cd, (uint32_t)(16 * j + e4) * 2u, bf16x4(y[j]));
+        }
+      }
+      break;
+    }
+    case P_OPROJ:
+    case P_DOWN: {
+      const float* xs = T.type == P_OPROJ ? Lw.x_in : Lw.x_mid;
+      float* xd = T.type == P_OPROJ ? Lw.x_mid : Lw.x_out;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const size_t ro = (size_t)(row0 + 16 * i + (lane & 15)) * P.H;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int c = wrow0 + 16 * j + e4;
+          const f32x4 v = *(const f32x4*)(xs + ro + c) + acc[j][i];
+          st_sc1_x4(xd + ro, (uint32_t)c * 4u, __builtin_bit_cast(u32x4, v));
+        }
+      }
+      break;
+    }
+    default: {  // P_GATEUP: h = silu(gate) * up, blocks 0-1 gate and 2-3 up of the same columns
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const size_t ro = (size_t)(row0 + 16 * i + (lane & 15)) * P.F;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const f32x4 g = acc[j][i], u = acc[j + 2][i];
+          f32x4 hv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) hv[e] = g[e] / (1.0f + __expf(-g[e])) * u[e];
+          st_hilo4(Lw.h + ro, (size_t)P.R * P.F, (uint32_t)(wrow0 + 16 * j + e4) * 2u, hv);
+        }
+      }
+      break;
+    }
+  }
+}
+
+// ---- causal attention: (sequence, kv head, 32 queries), one q head per wave --------------------
+//
+// Per step of 32 keys, on the matrix cores:
+//  * S^T = K Q^T: A = K rows from the cache (lane l: key l % 16, dims
+//    8 (l / 16) ..), B = the wave's queries (query l % 16), scaled by 1/sqrt(D)
+//    and split into hi + lo bf16 parts (two products; K in the cache is bf16
+//    and exact).  Lane l gets keys 4 (l / 16) + e of query l % 16 for each
+//    16-key block.
+//  * The online softmax (max, rescale, exponentials) runs per query in that
+//    layout; the four lanes of a query combine maxima with lane swaps.
+//  * O^T += V^T P^T: B = the lane's own eight probabilities (hi + lo bf16), in
+//    K order 8 (l / 16) + 4 kb + e <-> key 16 kb + 4 (l / 16) + e; A = V from
+//    LDS, staged transposed ([dim][key]) by all four waves, read in that
+//    same key order.  Lane l accumulates dims 4 (l / 16) + e of query l % 16.
+// Causality masks keys past each query and past the prompt; V rows past the
+// prompt are staged as zeros, K rows past it re-read the last prompt row.
+// Rounding the queries or the probabilities to plain bf16 alone moves the
+// last-position logits of the 16-layer model by about 2e-2, hence the pairs.
+constexpr int kPQB = kPQueries / 16;  // 16-query blocks per wave
+
+__device__ void attn_tile(const PParams& P, const Tile& T0, PSmem& sm, int tid) {
+  const Tile T = uni(T0);
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const PLayer Lw = cload(P.layers, T.layer);
+  const int q0 = T.c * kPQueries, nq = min(kPQueries, P.P - q0), kend = q0 + nq;
+  const int nsteps = (kend + kPKeys - 1) / kPKeys;
+  const bool active = w < P.G;
+  const int h = T.g * P.G + (active ? w : 0);
+  const size_t kvpos = (((size_t)T.layer * P.B + T.b) * P.Hkv + T.g) * P.cap;  // position 0 of this kv head
+  const __amdgpu_buffer_rsrc_t rk = rsrc(P.kc + kvpos * kHeadDim), rv = rsrc(P.vc + kvpos * kHeadDim);
+  const int l15 = lane & 15, g4 = lane >> 4;
+
+  // queries (B operand) as hi + lo bf16
+  bf16x8 qh[kPQB][2], ql[kPQB][2];
+#pragma unroll
+  for (int i = 0; i < kPQB; ++i) {
+    const float* qr = Lw.q + ((size_t)T.b * P.Pp + q0 + 16 * i + l15) * P.Hq * kHeadDim + h * kHeadDim;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const f32x4 x0 = *(const f32x4*)(qr + 32 * s + 8 * g4) * P.attn_scale;
+      const f32x4 x1 = *(const f32x4*)(qr + 32 * s + 8 * g4 + 4) * P.attn_scale;
+      qh[i][s] = hilo8(x0, x1, ql[i][s]);
+    }
+  }
+  // K fragments of a step (A operand), rows clamped into the prompt
+  auto kload = [&](int k0, u32x4 (&kf)[2][2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int key = min(k0 + 16 * kb + l15, kend - 1);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) kf[kb][s] = ld16(rk, (uint32_t)(key * kHeadDim + 32 * s + 8 * g4) * 2u, 0);
+    }
+  };
+  // V staging: thread t loads dims 8 (t % 8) .. +7 of key t / 8 of the step
+  const int vkey = tid >> 3, vd0 = 8 * (tid & 7);
+  auto vload = [&](int k0) -> u32x4 {
+    const int key = k0 + vkey;
+    if (key >= kend) return u32x4{0u, 0u, 0u, 0u};
+    return ld16(rv, (uint32_t)(key * kHeadDim + vd0) * 2u, 0);
+  };
+  auto vstore = [&](int buf, u32x4 v) {
+    const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sm.vt[buf][vd0 + 2 * e][vkey] = (uint16_t)(wv[e] & 0xFFFFu);
+      sm.vt[buf][vd0 + 2 * e + 1][vkey] = (uint16_t)(wv[e] >> 16);
+    }
+  };
+
+  float m[kPQB], lsum[kPQB];
+  f32x4 o[4][kPQB];  // [dim block][query block]
+#pragma unroll
+  for (int i = 0; i < kPQB; ++i) {
+    m[i] = -INFINITY;
+    lsum[i] = 0.f;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) o[db][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  u32x4 kf[2][2], vreg = vload(0);
+  if (active) kload(0, kf);
+  for (int ks = 0; ks < nsteps; ++ks) {
+    const int k0 = ks * kPKeys, buf = ks & 1;
+    vstore(buf, vreg);
+    __syncthreads();  // this step's V staged; every wave is past step ks - 1 (its buffer is free)
+    u32x4 nkf[2][2];
+    if (ks + 1 < nsteps) {
+      vreg = vload(k0 + kPKeys);
+      if (active) kload(k0 + kPKeys, nkf);
+    }
+    if (active) {
+      f32x4 st[2][kPQB];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < kPQB; ++i) {
+          f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            z = mfma(as_bf16x8(kf[kb][s]), qh[i][s], z);
+            z = mfma(as_bf16x8(kf[kb][s]), ql[i][s], z);
+          }
+          st[kb][i] = z;
+        }
+      bf16x8 ph[kPQB], pl[kPQB];
+#pragma unroll
+      for (int i = 0; i < kPQB; ++i) {
+        const int qpos = q0 + 16 * i + l15;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int key = k0 + 16 * kb + 4 * g4 + e;
+            const float v = (key <= qpos && key < kend) ? st[kb][i][e] : -INFINITY;
+            st[kb][i][e] = v;
+            mx = fmaxf(mx, v);
+          }
+        mx = xmax<16>(mx);
+        mx = xmax<32>(mx);
+        const float mn = fmaxf(m[i], mx);
+        const float alpha = __expf(m[i] - mn);
+        m[i] = mn;
+        f32x4 p0, p1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          p0[e] = __expf(st[0][i][e] - mn);
+          p1[e] = __expf(st[1][i][e] - mn);
+        }
+        lsum[i] = lsum[i] * alpha + ((p0[0] + p0[1]) + (p0[2] + p0[3])) + ((p1[0] + p1[1]) + (p1[2] + p1[3]));
+#pragma unroll
+        for (int db = 0; db < 4; ++db) o[db][i] *= alpha;
+        ph[i] = hilo8(p0, p1, pl[i]);
+      }
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const uint16_t* vr = &sm.vt[buf][16 * db + l15][0];
+        const u32x2 v0 = *(const u32x2*)(vr + 4 * g4);
+        const u32x2 v1 = *(const u32x2*)(vr + 16 + 4 * g4);
+        const bf16x8 vf = as_bf16x8(u32x4{v0.x, v0.y, v1.x, v1.y});
+#pragma unroll
+        for (int i = 0; i < kPQB; ++i) {
+          o[db][i] = mfma(vf, ph[i], o[db][i]);
+          o[db][i] = mfma(vf, pl[i], o[db][i]);
+        }
+      }
+    }
+    if (ks + 1 < nsteps && active) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) kf[kb][s] = nkf[kb][s];
+    }
+  }
+  if (!active) return;
+  const size_t plane = (size_t)P.R * P.Hq * kHeadDim;
+#pragma unroll
+  for (int i = 0; i < kPQB; ++i) {
+    float lt = xsum<16>(lsum[i]);
+    lt = xsum<32>(lt);
+    const int qpos = q0 + 16 * i + l15;
+    if (qpos >= P.P) continue;
+    const float inv = 1.0f / lt;
+    uint16_t* od = Lw.ao + ((size_t)T.b * P.Pp + qpos) * P.Hq * kHeadDim + h * kHeadDim;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) st_hilo4(od, plane, (uint32_t)(16 * db + 4 * g4) * 2u, o[db][i] * inv);
+  }
+}
+
+// ---- LM head on the last prompt rows: 128 vocabulary columns per tile ------------------------
+// Wave w: vocabulary rows 32 w .. +31 of the tile (two 16-row blocks) against
+// 16 sequences at a time (the final-normed rows, hi and lo bf16 planes).  Logits are stored in
+// fp32; the partial greedy choice (value, lowest index) goes to one of 16
+// shards per sequence with a 64-bit atomic maximum.
+__device__ void lm_tile(const PParams& P, const Tile& T0, int tid) {
+  const Tile T = uni(T0);
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l15 = lane & 15, g4 = lane >> 4;
+  const int v0 = T.r1 * kPLmCols + 32 * w;
+  const __amdgpu_buffer_rsrc_t re = rsrc(P.embed), rx = rsrc(P.xf), rxl = rsrc(P.xf + (size_t)kMaxBatch * P.H);
+  uint32_t ve[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) ve[j] = (uint32_t)min(v0 + 16 * j + l15, P.V - 1) * (uint32_t)P.H * 2u + 16u * g4;
+  for (int sg = 0; sg * 16 < P.B; ++sg) {
+    const uint32_t vx = (uint32_t)(16 * sg + l15) * (uint32_t)P.H * 2u + 16u * g4;
+    f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll 8
+    for (int k0 = 0; k0 < P.H; k0 += 32) {
+      const uint32_t so = (uint32_t)k0 * 2u;
+      const bf16x8 x = as_bf16x8(ld16(rx, vx, so)), xl = as_bf16x8(ld16(rxl, vx, so));
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const bf16x8 e = as_bf16x8(ld16(re, ve[j], so));
+        acc[j] = mfma(e, x, acc[j]);
+        acc[j] = mfma(e, xl, acc[j]);
+      }
+    }
+    const int seq = 16 * sg + l15;
+    unsigned long long best = 0;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int v = v0 + 16 * j + 4 * g4;
+      if (seq < P.B) {
+        float* lg = P.logits + (size_t)seq * P.V;
+        if (v + 3 < P.V && (P.V & 3) == 0) {
+          *(f32x4*)(lg + v) = acc[j];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (v + e < P.V) lg[v + e] = acc[j][e];
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (v + e < P.V) {
+          const unsigned long long k = pack_max(acc[j][e], v + e);
+          best = k > best ? k : best;
+        }
+    }
+    best = xmax_u64<16>(best);
+    best = xmax_u64<32>(best);
+    if (g4 == 0 && seq < P.B && best)
+      __hip_atomic_fetch_max(&P.argmax[(size_t)seq * kArgmaxShards + (T.r1 * 4 + w) % kArgmaxShards], best,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// The first generated token: the shards' maximum per sequence (and the shards
+// cleared for the next prefill), seq_len = prompt length.
+__device__ void argmax_tile(const PParams& P, int tid) {
+  if (tid >= 64) return;
+  const int lane = tid;
+  constexpr int SEQS = 64 / kArgmaxShards;
+  for (int b0 = 0; b0 < P.B; b0 += SEQS) {
+    const int b = b0 + lane / kArgmaxShards;
+    unsigned long long best = 0;
+    if (b < P.B)
+      best = __hip_atomic_exchange(&P.argmax[(size_t)b0 * kArgmaxShards + lane], 0ull, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+    best = group_max_u64<kArgmaxShards>(best);
+    if (b < P.B && lane % kArgmaxShards == 0) {
+      st_sc1(&P.tokens_out[b], (int32_t)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull)));
+      st_sc1(&P.seq_len[b], P.P);
+    }
+  }
+}
+
+__device__ __forceinline__ void run_tile(const PParams& P, const Tile& T, PSmem& sm, int tid) {
+  switch (T.type) {
+    case P_EMBED:
+    case P_NORM1:
+    case P_NORM2: norm_tile(P, T, tid); break;
+    case P_QKV:
+    case P_OPROJ:
+    case P_GATEUP:
+    case P_DOWN: gemm_tile(P, T, tid); break;
+    case P_ATTN: attn_tile(P, T, sm, tid); break;
+    case P_NORMF: normf_tile(P, T, tid); break;
+    case P_LM: lm_tile(P, T, tid); break;
+    default: argmax_tile(P, tid); break;
+  }
+}
+
+}  // namespace
+
+// The persistent prefill: each worker claims from its queue in topological
+// order (the next claim in flight while a tile runs), waits for the tile's
+// group, runs it with all four waves, waits for its stores and publishes.
+// The last worker out rewinds the queues and advances the epoch.
+template <bool LOG>
+__global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2))) void prefill_megakernel(PParams P) {
+  __shared__ PSmem sm;
+  const int tid = wpk_tid(), lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q = cload(P.worker_queue, (int)blockIdx.x);
+  const int qb = cload(P.queue_off, q), qn = cload(P.queue_off, q + 1) - qb;
+  uint32_t* head = P.heads + (size_t)q * kLine;
+  const uint32_t epoch = ld_sc1(&P.ctl[CTL_EPOCH]);
+  if (tid == 0) {
+    sm.claim[0] = ld_sc1(&P.ctl[CTL_STATUS]) != 0u ? qn : (int)atomic_add(head, 1u);
+    sm.stop = 0;
+  }
+  __syncthreads();
+  int cur = __builtin_amdgcn_readfirstlane(sm.claim[0]);
+  for (int it = 0; cur < qn; ++it) {
+    const Tile T = uni(cload(P.qtiles, qb + cur));
+    if (tid == 0) sm.claim[(it + 1) & 1] = (int)atomic_add(head, 1u);
+    int32_t delta = 0;
+    if (wave == 0 && T.wait >= 0) {
+      if (!p_wait(P, T, epoch, &delta, lane) && lane == 0) sm.stop = 1;
+    }
+    __syncthreads();
+    if (__builtin_amdgcn_readfirstlane(sm.stop)) break;
+    const uint64_t t_start = LOG ? __builtin_amdgcn_s_memrealtime() : 0;
+    run_tile(P, T, sm, tid);
+    wait_all_memory();
+    __syncthreads();
+    if (tid == 0) {
+      if (LOG) {
+        int32_t* rec = P.log + (size_t)T.id * 8;
+        __hip_atomic_fetch_add(rec, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        rec[1] = delta;
+        rec[2] = (int32_t)blockIdx.x;
+        rec[3] = cur;
+        *(uint64_t*)(rec + 4) = t_start;
+        *(uint64_t*)(rec + 6) = __builtin_amdgcn_s_memrealtime();
+        wait_all_memory();
+      }
+      if (T.signal >= 0) {
+        const Group G = cload(P.groups, T.signal);
+        atomic_add(&P.counters[(size_t)(G.shard0 + T.shard) * kLine], 1u);
+      }
+    }
+    cur = __builtin_amdgcn_readfirstlane(sm.claim[(it + 1) & 1]);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t old = atomic_add(&P.ctl[CTL_EXIT], 1u);
+    if (old == (uint32_t)P.n_workers - 1u) {
+      for (int i = 0; i < P.n_queues; ++i) st_sc1(&P.heads[(size_t)i * kLine], 0u);
+      st_sc1(&P.ctl[CTL_EXIT], 0u);
+      st_sc1(&P.ctl[CTL_EPOCH], epoch + 1u);
+    }
+  }
+}
+
+// One operator of the conventional baseline: one workgroup per tile, no
+// counters; kernel boundaries order the operators.
+__global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2))) void prefill_phase(PParams P,
+                                                                                                      int first) {
+  __shared__ PSmem sm;
+  const Tile T = uni(cload(P.tiles, first + (int)blockIdx.x));
+  run_tile(P, T, sm, wpk_tid());
+}
+
+}  // namespace wpk
+
+extern "C" int wpk_dev_prefill_kernels(const void** mk, const void** mk_log, const void** phase) {
+  *mk = reinterpret_cast<const void*>(&wpk::prefill_megakernel<false>);
+  *mk_log = reinterpret_cast<const void*>(&wpk::prefill_megakernel<true>);
+  *phase = reinterpret_cast<const void*>(&wpk::prefill_phase);
+  return 1;
+}

@@ -405,8 +405,9 @@ int32_t wpk_debug_read_act(wpk_plan* plan, void* host_dst, size_t bytes, size_t*
  * attention probabilities are rounded to bf16 at each product's input; the
  * residual stream, RMSNorm, RoPE and softmax run in fp32.
  *
- * wpk_build_prefill: model (DEVICE pointers, bf16 weights, hidden and ffn
- *   multiples of 128 and 64, n_q_heads + 2 n_kv_heads even), batch in [1, 32],
+ * wpk_build_prefill: model (DEVICE pointers, bf16 weights, hidden a multiple
+ *   of 128 up to 4096, ffn a multiple of 128, n_q_heads + 2 n_kv_heads even),
+ *   batch in [1, 32],
  *   ctx_len (the KV cache capacity), prompt_len in [1, ctx_len].  opts (NULL:
  *   defaults) picks the execution:
  *     WPK_PREFILL_MEGAKERNEL: one persistent kernel, all tiles;
@@ -434,7 +435,11 @@ int32_t wpk_debug_read_act(wpk_plan* plan, void* host_dst, size_t bytes, size_t*
  * wpk_prefill_get_dag: per tile id its type (wpk_prefill tile types below),
  *   layer, waited and signalled groups, and (if queue is not NULL) its claim
  *   queue.  Arrays of n_tiles.
- * Ownership and errors as for the decode step. */
+ * Ownership and errors as for the decode step, except that a prefill plan
+ * copies the layer matrices at build, repacked into the fragment-major
+ * layout its matrix-core tiles load (about the size of the layer weights;
+ * the embedding is still read from the caller's table): weights changed
+ * after the build are not seen by the prefill. */
 #define WPK_PREFILL_MEGAKERNEL 0
 #define WPK_PREFILL_SPLIT 1
 #define WPK_PREFILL_GRAPH 2
@@ -450,7 +455,7 @@ typedef struct wpk_prefill_info {
   int32_t split_workers;      /* workers of the attention megakernel (split plans) */
   int32_t n_phases;           /* kernels of the per-operator baseline */
   int32_t rows_per_sequence;  /* prompt rows padded to the 128-row blocks */
-  int64_t workspace_bytes;
+  int64_t workspace_bytes;    /* device memory the plan owns, the repacked weights included */
   double flops;               /* matrix-product FLOPs of one prefill (2 per multiply-add) */
 } wpk_prefill_info;
 /* tile types of wpk_prefill_get_dag */

@@ -26,8 +26,13 @@ namespace {
 
 constexpr int kVtPitch = 40;  // bf16 elements per transposed V row (32 keys + pad)
 
+constexpr int kGBlocks = 24;  // 1 KiB fragment blocks of a matrix-core k-step: 8 weight, 8 operand hi, 8 lo
+
 struct PSmem {
-  alignas(16) uint16_t vt[2][kHeadDim][kVtPitch];  // attention: one key step of V, [dim][key]
+  union alignas(16) {
+    uint16_t vt[2][kHeadDim][kVtPitch];  // attention: one key step of V, [dim][key]
+    u32x4 gs[3][kGBlocks][64];           // matrix-core tiles: three k-steps of fragments, 16 bytes per lane
+  };
   int claim[2];
   int stop;
 };
@@ -67,6 +72,17 @@ __device__ __forceinline__ bool p_wait(const PParams& P, const Tile& T, uint32_t
   }
 }
 
+// A buffer resource from a pointer that is the same in every lane, built from
+// scalar copies of it: the compiler would otherwise keep a resource chosen by
+// a select or derived through a switch in vector registers and wrap every
+// load in a loop over its distinct values.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t urs(const void* p) {
+  const uint64_t a = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return rsrc((const void*)(((uint64_t)hi << 32) | lo));
+}
+
 __device__ __forceinline__ u32x4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
 }
@@ -75,14 +91,22 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ u32x2 bf16x4(f32x4 v) { return u32x2{cvt_bf16x2(v[0], v[1]), cvt_bf16x2(v[2], v[3])}; }
-// Four fp32 values as bf16 hi + lo parts (value = hi + lo), stored 8 bytes
-// into each plane of an operand buffer (lo plane `plane` elements after hi).
-__device__ __forceinline__ void st_hilo4(uint16_t* hi, size_t plane, uint32_t byte_off, f32x4 v) {
+// Device-coherent (sc1) stores through a wave-uniform buffer resource; the
+// per-lane part of the address is the byte offset.
+__device__ __forceinline__ void st16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 16 /* sc1 */);
+}
+__device__ __forceinline__ void st8(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 16 /* sc1 */);
+}
+// Four fp32 values as bf16 hi + lo parts (value = hi + lo), 8 bytes into each
+// plane of an operand buffer.
+__device__ __forceinline__ void st_hilo4(__amdgpu_buffer_rsrc_t hi, __amdgpu_buffer_rsrc_t lo, uint32_t off, f32x4 v) {
   uint32_t h0, h1, l0, l1;
   split_hilo2(v[0], v[1], h0, l0);
   split_hilo2(v[2], v[3], h1, l1);
-  st_sc1_x2(hi, byte_off, u32x2{h0, h1});
-  st_sc1_x2(hi + plane, byte_off, u32x2{l0, l1});
+  st8(hi, off, u32x2{h0, h1});
+  st8(lo, off, u32x2{l0, l1});
 }
 // Eight fp32 values as a bf16x8 hi part and a bf16x8 lo part.
 __device__ __forceinline__ bf16x8 hilo8(f32x4 a, f32x4 b, bf16x8& lo) {
@@ -95,82 +119,137 @@ __device__ __forceinline__ bf16x8 hilo8(f32x4 a, f32x4 b, bf16x8& lo) {
   return as_bf16x8(u32x4{h[0], h[1], h[2], h[3]});
 }
 
+// Fragment-major ("packed") layout of a bf16 matrix-core operand with K
+// columns: blocks of 16 rows x 32 columns, one 1 KiB block per (16 rows,
+// k-step) in row-block-major order, and inside a block lane l's 16 bytes at
+// 16 l hold row l % 16, columns 8 (l / 16) .. +7 -- the register layout of a
+// v_mfma_f32_16x16x32_bf16 operand.  A wave then loads a fragment as one
+// contiguous KiB (eight whole cache lines); in row-major order the same
+// fragment is sixteen half-used lines, and the loads, not the matrix cores,
+// set the pace (measured: a 128 x 128 x 2048 tile took 88 us row-major).
+// Byte offset of element (r, k), 4-element aligned groups stay contiguous.
+__device__ __forceinline__ uint32_t pk(uint32_t r, uint32_t k, uint32_t K) {
+  return (((r >> 4) * (K >> 5) + (k >> 5)) * 64u + (r & 15u) + 16u * ((k & 31u) >> 3)) * 16u + (k & 7u) * 2u;
+}
+
 // ---- RMSNorm of rows -------------------------------------------------------------------------
 // y = x / sqrt(mean(x^2) + eps) * gain, stored as the hi and lo bf16 planes
-// of the matrix-core operand.  One wave per row at a time: each lane sums the squares of its
-// 16-byte chunks in order, then a fixed wave tree; a second pass re-reads the
-// row (from the cache) to scale it.
-template <bool EMBED>
-__device__ __forceinline__ void norm_row(const PParams& P, const float* x, const uint16_t* emb, const float* gain,
-                                         float* x_copy, uint16_t* y, size_t plane, int lane) {
-  const int nc = P.H / 4;
+// of the packed matrix-core operand.  A wave takes 16 rows at a time in the
+// fragment layout: lane l holds row l % 16, columns 8 (l / 16) .. +7 of each
+// 32-column k-step, so every store is one contiguous KiB per wave.  First
+// pass: each lane sums the squares of its columns in order, then the four
+// lanes of a row combine with lane swaps (a fixed order); second pass: the
+// rows are read again (from the cache), scaled and stored.
+// src(r, k) gives 8 fp32 values of row r from column k; rows past the prompt
+// (zero) are produced the same way.
+template <typename SRC>
+__device__ __forceinline__ void norm_rows16(const PParams& P, int r0, const SRC& src, const float* gain,
+                                            __amdgpu_buffer_rsrc_t yh, __amdgpu_buffer_rsrc_t yl,
+                                            __amdgpu_buffer_rsrc_t xc, bool copy, int lane) {
+  const int r = r0 + (lane & 15), c8 = 8 * (lane >> 4), nks = P.H / 32;
   float ss = 0.f;
-  for (int c = lane; c < nc; c += 64) {
-    f32x4 v;
-    if (EMBED) {
-      const u32x2 e = *(const u32x2*)(emb + 4 * c);
-      v = f32x4{bf16_lo(e.x), bf16_hi(e.x), bf16_lo(e.y), bf16_hi(e.y)};
-    } else {
-      v = *(const f32x4*)(x + 4 * c);
-    }
-    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+#pragma unroll 4
+  for (int ks = 0; ks < nks; ++ks) {
+    f32x4 a, b;
+    src(r, 32 * ks + c8, a, b);
+    ss += ((a[0] * a[0] + a[1] * a[1]) + (a[2] * a[2] + a[3] * a[3])) +
+          ((b[0] * b[0] + b[1] * b[1]) + (b[2] * b[2] + b[3] * b[3]));
   }
-  ss = wave_sum(ss);
+  ss = xsum<16>(ss);
+  ss = xsum<32>(ss);
   const float inv = 1.0f / sqrtf(ss / (float)P.H + P.eps);
-  for (int c = lane; c < nc; c += 64) {
-    f32x4 v;
-    if (EMBED) {
-      const u32x2 e = *(const u32x2*)(emb + 4 * c);
-      v = f32x4{bf16_lo(e.x), bf16_hi(e.x), bf16_lo(e.y), bf16_hi(e.y)};
-      st_sc1_x4(x_copy, (uint32_t)c * 16u, __builtin_bit_cast(u32x4, v));
-    } else {
-      v = *(const f32x4*)(x + 4 * c);
+  const uint32_t blk = (uint32_t)(r0 >> 4) * (uint32_t)nks * 1024u + (uint32_t)lane * 16u;
+#pragma unroll 4
+  for (int ks = 0; ks < nks; ++ks) {
+    const int k = 32 * ks + c8;
+    f32x4 a, b;
+    src(r, k, a, b);
+    if (copy) {
+      const uint32_t xo = ((uint32_t)r * (uint32_t)P.H + (uint32_t)k) * 4u;
+      st16(xc, xo, __builtin_bit_cast(u32x4, a));
+      st16(xc, xo + 16u, __builtin_bit_cast(u32x4, b));
     }
-    const f32x4 g = *(const f32x4*)(gain + 4 * c);
-    st_hilo4(y, plane, (uint32_t)c * 8u, v * inv * g);
+    const f32x4 ga = *(const f32x4*)(gain + k), gb = *(const f32x4*)(gain + k + 4);
+    a = a * inv * ga;
+    b = b * inv * gb;
+    uint32_t h[4], l[4];
+    split_hilo2(a[0], a[1], h[0], l[0]);
+    split_hilo2(a[2], a[3], h[1], l[1]);
+    split_hilo2(b[0], b[1], h[2], l[2]);
+    split_hilo2(b[2], b[3], h[3], l[3]);
+    st16(yh, blk + (uint32_t)ks * 1024u, u32x4{h[0], h[1], h[2], h[3]});
+    st16(yl, blk + (uint32_t)ks * 1024u, u32x4{l[0], l[1], l[2], l[3]});
   }
 }
 
-// A row block's norm: wave w takes rows 32w .. 32w+31.  Layer 0 gathers the
-// embedding rows (token ids checked; padding rows past the prompt are zero).
+// A row block's norm: wave w takes rows 32w .. 32w+31 (two groups of 16).
+// Layer 0 gathers the embedding rows (token ids checked; padding rows past
+// the prompt are zero) and keeps them as the residual stream.
 __device__ void norm_tile(const PParams& P, const Tile& T, int tid) {
   const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const PLayer Lw = cload(P.layers, T.layer);
   const size_t plane = (size_t)P.R * P.H;
-  for (int k = 0; k < kPRows / 4; ++k) {
-    const int r = T.r0 * kPRows + w * (kPRows / 4) + k;
-    const int b = r / P.Pp, p = r - b * P.Pp;
-    const size_t ro = (size_t)r * P.H;
+  uint16_t* y = T.type == P_NORM2 ? Lw.xn2 : Lw.xn1;
+  const __amdgpu_buffer_rsrc_t yh = urs(y), yl = urs(y + plane), xc = urs(P.x0);
+  for (int grp = 0; grp < 2; ++grp) {
+    const int r0 = T.r0 * kPRows + w * 32 + 16 * grp;
     if (T.type == P_EMBED) {
-      if (p >= P.P) {
-        for (int c = lane; c < P.H / 4; c += 64) {
-          st_sc1_x4(P.x0 + ro, (uint32_t)c * 16u, u32x4{0u, 0u, 0u, 0u});
-          st_sc1_x2(Lw.xn1 + ro, (uint32_t)c * 8u, u32x2{0u, 0u});
-          st_sc1_x2(Lw.xn1 + plane + ro, (uint32_t)c * 8u, u32x2{0u, 0u});
+      const int r = r0 + (lane & 15), b = r / P.Pp, p = r - b * P.Pp;
+      int tok = 0;
+      if (p < P.P) {
+        tok = P.prompt[(size_t)b * P.P + p];
+        if (tok < 0 || tok >= P.V) {
+          p_latch(P, WPK_E_TOKEN, T.id);
+          tok = 0;
         }
-        continue;
       }
-      int tok = P.prompt[(size_t)b * P.P + p];
-      if (tok < 0 || tok >= P.V) {
-        if (lane == 0) p_latch(P, WPK_E_TOKEN, T.id);
-        tok = 0;
-      }
-      norm_row<true>(P, nullptr, P.embed + (size_t)tok * P.H, Lw.attn_norm, P.x0 + ro, Lw.xn1 + ro, plane, lane);
-    } else if (T.type == P_NORM1) {
-      norm_row<false>(P, Lw.x_in + ro, nullptr, Lw.attn_norm, nullptr, Lw.xn1 + ro, plane, lane);
+      const uint16_t* er = P.embed + (size_t)tok * P.H;
+      const bool pad = p >= P.P;
+      auto src = [&](int, int k, f32x4& a, f32x4& bb) {
+        const u32x4 e = *(const u32x4*)(er + k);
+        a = pad ? f32x4{0.f, 0.f, 0.f, 0.f} : f32x4{bf16_lo(e.x), bf16_hi(e.x), bf16_lo(e.y), bf16_hi(e.y)};
+        bb = pad ? f32x4{0.f, 0.f, 0.f, 0.f} : f32x4{bf16_lo(e.z), bf16_hi(e.z), bf16_lo(e.w), bf16_hi(e.w)};
+      };
+      norm_rows16(P, r0, src, Lw.attn_norm, yh, yl, xc, true, lane);
     } else {
-      norm_row<false>(P, Lw.x_mid + ro, nullptr, Lw.mlp_norm, nullptr, Lw.xn2 + ro, plane, lane);
+      const float* x = T.type == P_NORM1 ? Lw.x_in : Lw.x_mid;
+      auto src = [&](int r, int k, f32x4& a, f32x4& bb) {
+        const float* xr = x + (size_t)r * P.H + k;
+        a = *(const f32x4*)xr;
+        bb = *(const f32x4*)(xr + 4);
+      };
+      norm_rows16(P, r0, src, T.type == P_NORM1 ? Lw.attn_norm : Lw.mlp_norm, yh, yl, xc, false, lane);
     }
   }
 }
 
-// The final norm of one sequence's last prompt row (wave 0).
+// The final norm of one sequence's last prompt row (xf row b): wave 0, the
+// 64 lanes across the row (all of its chunks loaded at once), stored into
+// row b of the packed xf.  Only row b is touched: the other sequences' rows
+// may not be complete yet, and reading a line before its producer has
+// written it could leave a stale copy in this XCD's cache.
+constexpr int kNormChunks = 16;  // 16-byte chunks per lane for hidden up to 4096
 __device__ void normf_tile(const PParams& P, const Tile& T, int tid) {
   if (tid >= 64) return;
+  const int lane = tid, nc = P.H / 4;
   const PLayer Lw = cload(P.layers, P.L - 1);
-  const size_t r = (size_t)T.b * P.Pp + (P.P - 1);
-  norm_row<false>(P, Lw.x_out + r * P.H, nullptr, P.final_norm, nullptr, P.xf + (size_t)T.b * P.H,
-                  (size_t)kMaxBatch * P.H, tid);
+  const float* x = Lw.x_out + ((size_t)T.b * P.Pp + P.P - 1) * P.H;
+  f32x4 v[kNormChunks];
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < kNormChunks; ++k)
+    if (lane + 64 * k < nc) v[k] = *(const f32x4*)(x + 4 * (lane + 64 * k));
+#pragma unroll
+  for (int k = 0; k < kNormChunks; ++k)
+    if (lane + 64 * k < nc) ss += (v[k][0] * v[k][0] + v[k][1] * v[k][1]) + (v[k][2] * v[k][2] + v[k][3] * v[k][3]);
+  ss = wave_sum(ss);
+  const float inv = 1.0f / sqrtf(ss / (float)P.H + P.eps);
+  const __amdgpu_buffer_rsrc_t yh = urs(P.xf), yl = urs(P.xf + (size_t)kMaxBatch * P.H);
+#pragma unroll
+  for (int k = 0; k < kNormChunks; ++k) {
+    const int c = lane + 64 * k;
+    if (c < nc) st_hilo4(yh, yl, pk((uint32_t)T.b, 4u * c, (uint32_t)P.H), v[k] * inv * *(const f32x4*)(P.final_norm + 4 * c));
+  }
 }
 
 // ---- matrix-core tiles: 128 prompt rows x 128 output columns x all of K ----------------------
@@ -183,94 +262,149 @@ __device__ void normf_tile(const PParams& P, const Tile& T, int tid) {
 // four consecutive output columns 4 (l / 16) + e of prompt row l % 16, so
 // epilogues store 8 or 16 contiguous bytes per lane.  Wave w computes rows
 // 64 (w & 1) .. +63 and columns 64 (w >> 1) .. +63 (one head of QKV): four
-// column blocks j x four row blocks i.  Fragments stream from the caches
-// straight into registers, the next k-step's loads in flight behind this
-// step's products.
-__device__ void gemm_tile(const PParams& P, const Tile& T0, int tid) {
+// column blocks j x four row blocks i.
+//
+// A k-step (32 of K) needs 24 fragment blocks of 1 KiB (16 bytes per lane in
+// fragment order): 8 weight blocks of 16 rows, 8 operand blocks of 16 rows in
+// the hi plane and 8 in the lo plane.  Each wave loads 6 of them into
+// registers two k-steps ahead and writes them to one of two LDS stages; after
+// a barrier every wave reads its 12 blocks from LDS.  Each block is fetched
+// from the caches once per tile instead of once per wave that uses it.
+__device__ void gemm_tile(const PParams& P, const Tile& T0, PSmem& sm, int tid) {
   const Tile T = uni(T0);
   const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wr = w & 1, wc = w >> 1;
+  const int wr = w & 1, wc = w >> 1, l15 = lane & 15, g4 = lane >> 4;
   const PLayer Lw = cload(P.layers, T.layer);
   const uint16_t* A;
   const uint16_t* W0;
   const uint16_t* W1;
-  int K, wrow0, wrow1;  // weight rows of column blocks 0-1 and 2-3 (lane offset added below)
+  int K, wrow0;  // first weight row of this wave's column blocks (gate/up: of its gate and up halves)
   switch (T.type) {
-    case P_QKV:
-      A = Lw.xn1, W0 = W1 = Lw.w_qkv, K = P.H;
-      wrow0 = T.r1 * kPCols + 64 * wc, wrow1 = wrow0 + 32;
-      break;
-    case P_OPROJ:
-      A = Lw.ao, W0 = W1 = Lw.w_o, K = P.H;
-      wrow0 = T.r1 * kPCols + 64 * wc, wrow1 = wrow0 + 32;
-      break;
-    case P_GATEUP:
-      A = Lw.xn2, W0 = Lw.w_gate, W1 = Lw.w_up, K = P.H;
-      wrow0 = wrow1 = T.r1 * kPFfnCols + 32 * wc;
-      break;
-    default:  // P_DOWN
-      A = Lw.h, W0 = W1 = Lw.w_down, K = P.F;
-      wrow0 = T.r1 * kPCols + 64 * wc, wrow1 = wrow0 + 32;
-      break;
+    case P_QKV: A = Lw.xn1, W0 = W1 = Lw.w_qkv, K = P.H, wrow0 = T.r1 * kPCols + 64 * wc; break;
+    case P_OPROJ: A = Lw.ao, W0 = W1 = Lw.w_o, K = P.H, wrow0 = T.r1 * kPCols + 64 * wc; break;
+    case P_GATEUP: A = Lw.xn2, W0 = Lw.w_gate, W1 = Lw.w_up, K = P.H, wrow0 = T.r1 * kPFfnCols + 32 * wc; break;
+    default: A = Lw.h, W0 = W1 = Lw.w_down, K = P.F, wrow0 = T.r1 * kPCols + 64 * wc; break;
   }
+  const bool gu = T.type == P_GATEUP;
   const int row0 = T.r0 * kPRows + 64 * wr;
-  const __amdgpu_buffer_rsrc_t ra = rsrc(A), rl = rsrc(A + (size_t)P.R * K), rw0 = rsrc(W0), rw1 = rsrc(W1);
-  const uint32_t kb = 16u * (uint32_t)(lane >> 4);  // byte offset of the lane's eight K values
-  uint32_t va[4], vw[4];
+  // this wave's loads: weight blocks 2w, 2w+1 (block jj: column group jj / 4, block jj % 4 of it),
+  // operand blocks 2w, 2w+1 of the hi and of the lo plane
+  const __amdgpu_buffer_rsrc_t ra = urs(A), rl = urs(A + (size_t)P.R * K);
+  uint32_t gv[6];
+  __amdgpu_buffer_rsrc_t gr[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) va[i] = (uint32_t)(row0 + 16 * i + (lane & 15)) * (uint32_t)K * 2u + kb;
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    vw[j] = (uint32_t)((j < 2 ? wrow0 + 16 * j : wrow1 + 16 * (j - 2)) + (lane & 15)) * (uint32_t)K * 2u + kb;
+  for (int q = 0; q < 2; ++q) {
+    const int jj = 2 * w + q, c = jj >> 2, j = jj & 3;
+    const int row = gu ? T.r1 * kPFfnCols + 32 * c + 16 * (j & 1) : T.r1 * kPCols + 16 * jj;
+    gr[q] = urs(gu && j >= 2 ? W1 : W0);
+    // packed operands: the fragment of 16 rows at k-step ks is the KiB at
+    // (row block * K / 32 + ks) * 1024, the lane's 16 bytes at 16 lane
+    gv[q] = ((uint32_t)(row >> 4) * (uint32_t)(K >> 5) * 64u + lane) * 16u;
+    gv[2 + q] = ((uint32_t)(T.r0 * (kPRows / 16) + 2 * w + q) * (uint32_t)(K >> 5) * 64u + lane) * 16u;
+  }
+  auto gload = [&](u32x4 (&G)[6], int ks) {
+    const uint32_t so = (uint32_t)ks * 1024u;
+    G[0] = ld16(gr[0], gv[0], so);
+    G[1] = ld16(gr[1], gv[1], so);
+    G[2] = ld16(ra, gv[2], so);
+    G[3] = ld16(ra, gv[3], so);
+    G[4] = ld16(rl, gv[2], so);
+    G[5] = ld16(rl, gv[3], so);
+  };
+  auto lput = [&](int st, const u32x4 (&G)[6]) {
+    sm.gs[st][2 * w][lane] = G[0];
+    sm.gs[st][2 * w + 1][lane] = G[1];
+    sm.gs[st][8 + 2 * w][lane] = G[2];
+    sm.gs[st][8 + 2 * w + 1][lane] = G[3];
+    sm.gs[st][16 + 2 * w][lane] = G[4];
+    sm.gs[st][16 + 2 * w + 1][lane] = G[5];
+  };
   f32x4 acc[4][4];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  u32x4 a[4], al[4], b[4];
+  // fragments of one k-step from an LDS stage: 4 weight blocks, the hi and lo
+  // planes of 4 operand blocks
+  struct Frag {
+    bf16x8 b[4], a[4], al[4];
+  };
+  auto fread = [&](int st, Frag& f) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    a[i] = ld16(ra, va[i], 0);
-    al[i] = ld16(rl, va[i], 0);
-  }
+    for (int j = 0; j < 4; ++j) f.b[j] = as_bf16x8(sm.gs[st][4 * wc + j][lane]);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) b[j] = ld16(j < 2 ? rw0 : rw1, vw[j], 0);
-  for (int k0 = 0;; k0 += 32) {
-    const bool more = k0 + 32 < K;
-    u32x4 na[4], nal[4], nb[4];
-    if (more) {
-      const uint32_t so = (uint32_t)(k0 + 32) * 2u;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        na[i] = ld16(ra, va[i], so);
-        nal[i] = ld16(rl, va[i], so);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) nb[j] = ld16(j < 2 ? rw0 : rw1, vw[j], so);
+    for (int i = 0; i < 4; ++i) {
+      f.a[i] = as_bf16x8(sm.gs[st][8 + 4 * wr + i][lane]);
+      f.al[i] = as_bf16x8(sm.gs[st][16 + 4 * wr + i][lane]);
     }
-    __builtin_amdgcn_sched_barrier(0);  // the next step's loads stay ahead of this step's products
+  };
+  // the hi products, then the lo products: no two consecutive products share an accumulator
+  auto products = [&](const Frag& f) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[j][i] = mfma(as_bf16x8(b[j]), as_bf16x8(a[i]), acc[j][i]);
-        acc[j][i] = mfma(as_bf16x8(b[j]), as_bf16x8(al[i]), acc[j][i]);
-      }
-    if (!more) break;
+      for (int i = 0; i < 4; ++i) acc[j][i] = mfma(f.b[j], f.a[i], acc[j][i]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      a[i] = na[i];
-      al[i] = nal[i];
-    }
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = nb[j];
+      for (int i = 0; i < 4; ++i) acc[j][i] = mfma(f.b[j], f.al[i], acc[j][i]);
+  };
+  // Pipeline over k-steps h: three LDS stages (step h in stage h % 3) and two
+  // register groups in turn (group h % 2 carries step h + 2 from its loads to
+  // its stage write), and two fragment sets.  In step h a wave writes step
+  // h + 2 into its stage, issues the loads of step h + 4, reads step h + 1's
+  // fragments from LDS (written in step h - 1, visible after that step's
+  // barrier), runs step h's products, and meets the others at a barrier
+  // (after which step h + 2's stage is complete, and step h + 1's stage of
+  // the step before is no longer read).  So the fragment reads overlap the
+  // products instead of following a barrier.  Every load and stage write is
+  // unconditional (past the last step they repeat it and are never used), so
+  // the compiler's count of loads in flight stays exact; scheduling barriers
+  // keep each group's loads ahead of the products they overlap.
+  const int nk = K / 32;
+  auto kc = [&](int ks) { return min(ks, nk - 1); };
+  u32x4 G0[6], G1[6];
+  Frag F0, F1;
+  gload(G0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  gload(G1, kc(1));
+  __builtin_amdgcn_sched_barrier(0);
+  lput(0, G0);
+  gload(G0, kc(2));
+  __builtin_amdgcn_sched_barrier(0);
+  lput(1, G1);
+  gload(G1, kc(3));
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+  fread(0, F0);
+#define WPK_GEMM_STEP(I, GW, FN, FC)                                        \
+  {                                                                         \
+    const int h = h0 + (I);                                                 \
+    lput(((I) + 2) % 3, GW);                                                \
+    gload(GW, kc(h + 4));                                                   \
+    __builtin_amdgcn_sched_barrier(0);                                      \
+    fread(((I) + 1) % 3, FN);                                               \
+    if (h < nk) products(FC);                                               \
+    __syncthreads();                                                        \
   }
+  for (int h0 = 0; h0 < nk; h0 += 6) {
+    WPK_GEMM_STEP(0, G0, F1, F0)
+    WPK_GEMM_STEP(1, G1, F0, F1)
+    WPK_GEMM_STEP(2, G0, F1, F0)
+    WPK_GEMM_STEP(3, G1, F0, F1)
+    WPK_GEMM_STEP(4, G0, F1, F0)
+    WPK_GEMM_STEP(5, G1, F0, F1)
+  }
+#undef WPK_GEMM_STEP
 
   // epilogues: lane holds columns c_j + 4 (lane / 16) + e of prompt row r_i
   const int e4 = 4 * (lane >> 4);
   switch (T.type) {
     case P_QKV: {
       const int hh = 2 * T.r1 + wc;  // head of this wave's 64 columns: q heads, then k, then v
+      const bool isq = hh < P.Hq, isk = !isq && hh < P.Hq + P.Hkv;
+      const __amdgpu_buffer_rsrc_t rd = urs(isq ? (void*)Lw.q : isk ? (void*)P.kc : (void*)P.vc);
+      const int kh = isk ? hh - P.Hq : hh - P.Hq - P.Hkv;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = row0 + 16 * i + (lane & 15);
@@ -288,17 +422,14 @@ __device__ void gemm_tile(const PParams& P, const Tile& T0, int tid) {
             y[j + 2] = x2 * cs + x1 * sn;
           }
         }
-        if (hh < P.Hq) {
-          float* qd = Lw.q + (size_t)r * P.Hq * kHeadDim + hh * kHeadDim;
+        if (isq) {
+          const uint32_t o = ((uint32_t)r * (uint32_t)P.Hq + (uint32_t)hh) * kHeadDim;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) st_sc1_x4(qd, (uint32_t)(16 * j + e4) * 4u, __builtin_bit_cast(u32x4, y[j]));
+          for (int j = 0; j < 4; ++j) st16(rd, (o + 16 * j + e4) * 4u, __builtin_bit_cast(u32x4, y[j]));
         } else {
-          const bool isk = hh < P.Hq + P.Hkv;
-          const int kh = isk ? hh - P.Hq : hh - P.Hq - P.Hkv;
-          uint16_t* cd = (isk ? P.kc : P.vc) +
-                         ((((size_t)T.layer * P.B + bq) * P.Hkv + kh) * P.cap + p) * kHeadDim;
+          const uint32_t o = (uint32_t)(((((size_t)T.layer * P.B + bq) * P.Hkv + kh) * P.cap + p) * kHeadDim);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) st_sc1_x2(cd, (uint32_t)(16 * j + e4) * 2u, bf16x4(y[j]));
+          for (int j = 0; j < 4; ++j) st8(rd, (o + 16 * j + e4) * 2u, bf16x4(y[j]));
         }
       }
       break;
@@ -306,30 +437,31 @@ __device__ void gemm_tile(const PParams& P, const Tile& T0, int tid) {
     case P_OPROJ:
     case P_DOWN: {
       const float* xs = T.type == P_OPROJ ? Lw.x_in : Lw.x_mid;
-      float* xd = T.type == P_OPROJ ? Lw.x_mid : Lw.x_out;
+      const __amdgpu_buffer_rsrc_t rd = urs(T.type == P_OPROJ ? Lw.x_mid : Lw.x_out);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const size_t ro = (size_t)(row0 + 16 * i + (lane & 15)) * P.H;
+        const uint32_t ro = (uint32_t)(row0 + 16 * i + (lane & 15)) * (uint32_t)P.H;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int c = wrow0 + 16 * j + e4;
+          const uint32_t c = (uint32_t)(wrow0 + 16 * j + e4);
           const f32x4 v = *(const f32x4*)(xs + ro + c) + acc[j][i];
-          st_sc1_x4(xd + ro, (uint32_t)c * 4u, __builtin_bit_cast(u32x4, v));
+          st16(rd, (ro + c) * 4u, __builtin_bit_cast(u32x4, v));
         }
       }
       break;
     }
     default: {  // P_GATEUP: h = silu(gate) * up, blocks 0-1 gate and 2-3 up of the same columns
+      const __amdgpu_buffer_rsrc_t hh = urs(Lw.h), hl = urs(Lw.h + (size_t)P.R * P.F);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const size_t ro = (size_t)(row0 + 16 * i + (lane & 15)) * P.F;
+        const uint32_t ro = (uint32_t)(row0 + 16 * i + (lane & 15)) * (uint32_t)P.F;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const f32x4 g = acc[j][i], u = acc[j + 2][i];
           f32x4 hv;
 #pragma unroll
           for (int e = 0; e < 4; ++e) hv[e] = g[e] / (1.0f + __expf(-g[e])) * u[e];
-          st_hilo4(Lw.h + ro, (size_t)P.R * P.F, (uint32_t)(wrow0 + 16 * j + e4) * 2u, hv);
+          st_hilo4(hh, hl, pk((uint32_t)(row0 + 16 * i + (lane & 15)), (uint32_t)(wrow0 + 16 * j + e4), (uint32_t)P.F), hv);
         }
       }
       break;
@@ -366,7 +498,7 @@ __device__ void attn_tile(const PParams& P, const Tile& T0, PSmem& sm, int tid) 
   const bool active = w < P.G;
   const int h = T.g * P.G + (active ? w : 0);
   const size_t kvpos = (((size_t)T.layer * P.B + T.b) * P.Hkv + T.g) * P.cap;  // position 0 of this kv head
-  const __amdgpu_buffer_rsrc_t rk = rsrc(P.kc + kvpos * kHeadDim), rv = rsrc(P.vc + kvpos * kHeadDim);
+  const __amdgpu_buffer_rsrc_t rk = urs(P.kc + kvpos * kHeadDim), rv = urs(P.vc + kvpos * kHeadDim);
   const int l15 = lane & 15, g4 = lane >> 4;
 
   // queries (B operand) as hi + lo bf16
@@ -394,8 +526,8 @@ __device__ void attn_tile(const PParams& P, const Tile& T0, PSmem& sm, int tid) 
   const int vkey = tid >> 3, vd0 = 8 * (tid & 7);
   auto vload = [&](int k0) -> u32x4 {
     const int key = k0 + vkey;
-    if (key >= kend) return u32x4{0u, 0u, 0u, 0u};
-    return ld16(rv, (uint32_t)(key * kHeadDim + vd0) * 2u, 0);
+    const u32x4 v = ld16(rv, (uint32_t)(min(key, kend - 1) * kHeadDim + vd0) * 2u, 0);
+    return key < kend ? v : u32x4{0u, 0u, 0u, 0u};
   };
   auto vstore = [&](int buf, u32x4 v) {
     const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
@@ -416,16 +548,16 @@ __device__ void attn_tile(const PParams& P, const Tile& T0, PSmem& sm, int tid) 
     for (int db = 0; db < 4; ++db) o[db][i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   u32x4 kf[2][2], vreg = vload(0);
-  if (active) kload(0, kf);
+  kload(0, kf);
   for (int ks = 0; ks < nsteps; ++ks) {
     const int k0 = ks * kPKeys, buf = ks & 1;
     vstore(buf, vreg);
     __syncthreads();  // this step's V staged; every wave is past step ks - 1 (its buffer is free)
+    // the next step's loads, unconditional (past the last step they repeat it)
+    const int kn = min(ks + 1, nsteps - 1) * kPKeys;
     u32x4 nkf[2][2];
-    if (ks + 1 < nsteps) {
-      vreg = vload(k0 + kPKeys);
-      if (active) kload(k0 + kPKeys, nkf);
-    }
+    vreg = vload(kn);
+    kload(kn, nkf);
     if (active) {
       f32x4 st[2][kPQB];
 #pragma unroll
@@ -483,15 +615,13 @@ __device__ void attn_tile(const PParams& P, const Tile& T0, PSmem& sm, int tid) 
         }
       }
     }
-    if (ks + 1 < nsteps && active) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int s = 0; s < 2; ++s) kf[kb][s] = nkf[kb][s];
-    }
+      for (int s = 0; s < 2; ++s) kf[kb][s] = nkf[kb][s];
   }
   if (!active) return;
-  const size_t plane = (size_t)P.R * P.Hq * kHeadDim;
+  const __amdgpu_buffer_rsrc_t oh = urs(Lw.ao), ol = urs(Lw.ao + (size_t)P.R * P.Hq * kHeadDim);
 #pragma unroll
   for (int i = 0; i < kPQB; ++i) {
     float lt = xsum<16>(lsum[i]);
@@ -499,9 +629,10 @@ __device__ void attn_tile(const PParams& P, const Tile& T0, PSmem& sm, int tid) 
     const int qpos = q0 + 16 * i + l15;
     if (qpos >= P.P) continue;
     const float inv = 1.0f / lt;
-    uint16_t* od = Lw.ao + ((size_t)T.b * P.Pp + qpos) * P.Hq * kHeadDim + h * kHeadDim;
+    const uint32_t orow = (uint32_t)T.b * P.Pp + qpos, ocol = (uint32_t)h * kHeadDim + 4 * g4;
 #pragma unroll
-    for (int db = 0; db < 4; ++db) st_hilo4(od, plane, (uint32_t)(16 * db + 4 * g4) * 2u, o[db][i] * inv);
+    for (int db = 0; db < 4; ++db)
+      st_hilo4(oh, ol, pk(orow, ocol + 16 * db, (uint32_t)(P.Hq * kHeadDim)), o[db][i] * inv);
   }
 }
 
@@ -515,17 +646,17 @@ __device__ void lm_tile(const PParams& P, const Tile& T0, int tid) {
   const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l15 = lane & 15, g4 = lane >> 4;
   const int v0 = T.r1 * kPLmCols + 32 * w;
-  const __amdgpu_buffer_rsrc_t re = rsrc(P.embed), rx = rsrc(P.xf), rxl = rsrc(P.xf + (size_t)kMaxBatch * P.H);
+  const __amdgpu_buffer_rsrc_t re = urs(P.embed), rx = urs(P.xf), rxl = urs(P.xf + (size_t)kMaxBatch * P.H);
   uint32_t ve[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) ve[j] = (uint32_t)min(v0 + 16 * j + l15, P.V - 1) * (uint32_t)P.H * 2u + 16u * g4;
   for (int sg = 0; sg * 16 < P.B; ++sg) {
-    const uint32_t vx = (uint32_t)(16 * sg + l15) * (uint32_t)P.H * 2u + 16u * g4;
+    const uint32_t vx = ((uint32_t)sg * (uint32_t)(P.H >> 5) * 64u + lane) * 16u;  // packed xf
     f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll 8
     for (int k0 = 0; k0 < P.H; k0 += 32) {
-      const uint32_t so = (uint32_t)k0 * 2u;
-      const bf16x8 x = as_bf16x8(ld16(rx, vx, so)), xl = as_bf16x8(ld16(rxl, vx, so));
+      const uint32_t so = (uint32_t)k0 * 2u, sx = (uint32_t)k0 * 32u;
+      const bf16x8 x = as_bf16x8(ld16(rx, vx, sx)), xl = as_bf16x8(ld16(rxl, vx, sx));
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const bf16x8 e = as_bf16x8(ld16(re, ve[j], so));
@@ -591,7 +722,7 @@ __device__ __forceinline__ void run_tile(const PParams& P, const Tile& T, PSmem&
     case P_QKV:
     case P_OPROJ:
     case P_GATEUP:
-    case P_DOWN: gemm_tile(P, T, tid); break;
+    case P_DOWN: gemm_tile(P, T, sm, tid); break;
     case P_ATTN: attn_tile(P, T, sm, tid); break;
     case P_NORMF: normf_tile(P, T, tid); break;
     case P_LM: lm_tile(P, T, tid); break;
@@ -629,7 +760,9 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2))) 
     __syncthreads();
     if (__builtin_amdgcn_readfirstlane(sm.stop)) break;
     const uint64_t t_start = LOG ? __builtin_amdgcn_s_memrealtime() : 0;
-    run_tile(P, T, sm, tid);
+    // the thread index made opaque per tile: the tile bodies' per-lane address
+    // arithmetic is then not hoisted out of the loop and kept live across it
+    run_tile(P, T, sm, opaque(tid));
     wait_all_memory();
     __syncthreads();
     if (tid == 0) {
@@ -671,6 +804,28 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2))) 
 }
 
 }  // namespace wpk
+
+namespace wpk {
+// Repacks a row-major bf16 matrix [rows][K] (rows a multiple of 16, K of 32)
+// into the packed fragment-major layout the matrix-core tiles load: one
+// thread per 16-byte chunk.
+__global__ __launch_bounds__(256) void prefill_pack(const uint16_t* src, uint16_t* dst, int rows, int K) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t per_row = (size_t)K / 8;
+  if (i >= (size_t)rows * per_row) return;
+  const uint32_t r = (uint32_t)(i / per_row), k = (uint32_t)(i % per_row) * 8u;
+  *(u32x4*)((char*)dst + pk(r, k, (uint32_t)K)) = *(const u32x4*)(src + i * 8);
+}
+}  // namespace wpk
+
+// Launches the repacking of one matrix on `stream` (asynchronous).
+extern "C" int wpk_dev_prefill_pack(const void* src, void* dst, int rows, int K, void* stream) {
+  const size_t chunks = (size_t)rows * (size_t)K / 8;
+  const unsigned grid = (unsigned)((chunks + 255) / 256);
+  hipLaunchKernelGGL(wpk::prefill_pack, dim3(grid), dim3(256), 0, (hipStream_t)stream, (const uint16_t*)src,
+                     (uint16_t*)dst, rows, K);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
 
 extern "C" int wpk_dev_prefill_kernels(const void** mk, const void** mk_log, const void** phase) {
   *mk = reinterpret_cast<const void*>(&wpk::prefill_megakernel<false>);

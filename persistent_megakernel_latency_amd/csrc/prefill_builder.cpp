@@ -54,8 +54,8 @@ std::string check_prefill_shape(const wpk_model_desc& d, int32_t batch, int32_t 
   s.G = s.Hq / s.Hkv;
   if (s.G > kMaxGroupHeads) return "at most 4 q heads per kv head";
   if (s.Hq * s.D != s.H) return "n_q_heads * head_dim must equal hidden";
-  if (s.H % kPCols) return "hidden must be a multiple of 128";
-  if (s.F % kPFfnCols) return "ffn must be a multiple of 64";
+  if (s.H % kPCols || s.H > 4096) return "hidden must be a multiple of 128, at most 4096";
+  if (s.F % kPCols) return "ffn must be a multiple of 128";
   s.qkv_rows = (s.Hq + 2 * s.Hkv) * s.D;
   if (s.qkv_rows % kPCols) return "n_q_heads + 2 n_kv_heads must be even (QKV tiles hold two heads)";
   if (batch < 1 || batch > kMaxBatch) return "batch must be in [1, 32]";

@@ -20,6 +20,7 @@
 #include "wpk.h"
 
 extern "C" int wpk_dev_prefill_kernels(const void** mk, const void** mk_log, const void** phase);
+extern "C" int wpk_dev_prefill_pack(const void* src, void* dst, int rows, int K, void* stream);
 
 using namespace wpk;
 
@@ -34,6 +35,10 @@ struct wpk_prefill_plan {
   int device = -1, n_cu = 0, workers = 0, max_workers = 0, split_workers = 0;
   char* d_ws = nullptr;
   int64_t ws_bytes = 0;
+  // the layer matrices repacked at build into the fragment-major layout the
+  // matrix-core tiles load (the caller's row-major weights are not read later)
+  uint16_t* d_wpk = nullptr;
+  int64_t wpk_bytes = 0;
   PParams P{};
   const void* k_mega = nullptr;
   const void* k_mega_log = nullptr;
@@ -199,15 +204,37 @@ wpk_prefill_plan* build(const wpk_model_desc* desc, int32_t batch, int32_t ctx_l
   // queries and attention outputs (never written) and the rows of xf past
   // the batch
   e = hipMemset(w, 0, L.total);
+  // packed copies of the layer matrices: qkv, o, gate, up, down per layer
+  const int64_t per_layer_w = (int64_t)s.qkv_rows * s.H + (int64_t)s.H * s.H + 3 * (int64_t)s.F * s.H;
+  p->wpk_bytes = per_layer_w * s.L * 2;
+  if (e == hipSuccess) e = hipMalloc((void**)&p->d_wpk, p->wpk_bytes);
+  if (e != hipSuccess) {
+    (void)hipFree(p->d_ws);
+    p->d_ws = nullptr;
+    p->d_wpk = nullptr;
+    return pfail(hip_msg("hipMalloc packed weights", e));
+  }
   std::vector<PLayer> lay(s.L);
   for (int l = 0; l < s.L; ++l) {
     char* a = w + L.act + (int64_t)l * L.act_layer;
     PLayer& y = lay[l];
-    y.w_qkv = (const uint16_t*)desc->w_qkv[l];
-    y.w_o = (const uint16_t*)desc->w_o[l];
-    y.w_gate = (const uint16_t*)desc->w_gate[l];
-    y.w_up = (const uint16_t*)desc->w_up[l];
-    y.w_down = (const uint16_t*)desc->w_down[l];
+    uint16_t* wl = p->d_wpk + per_layer_w * l;
+    const struct {
+      const void* src;
+      int rows, K;
+    } mats[5] = {{desc->w_qkv[l], s.qkv_rows, s.H}, {desc->w_o[l], s.H, s.H}, {desc->w_gate[l], s.F, s.H},
+                 {desc->w_up[l], s.F, s.H}, {desc->w_down[l], s.H, s.F}};
+    uint16_t* dst[5];
+    for (int m = 0; m < 5; ++m) {
+      dst[m] = wl;
+      if (wpk_dev_prefill_pack(mats[m].src, wl, mats[m].rows, mats[m].K, nullptr) != 0) e = hipErrorLaunchFailure;
+      wl += (int64_t)mats[m].rows * mats[m].K;
+    }
+    y.w_qkv = dst[0];
+    y.w_o = dst[1];
+    y.w_gate = dst[2];
+    y.w_up = dst[3];
+    y.w_down = dst[4];
     y.attn_norm = desc->attn_norm[l];
     y.mlp_norm = desc->mlp_norm[l];
     y.x_mid = (float*)(a + L.x_mid);
@@ -242,10 +269,13 @@ wpk_prefill_plan* build(const wpk_model_desc* desc, int32_t batch, int32_t ctx_l
   if (e == hipSuccess) e = up(L.rope_cos, rc.data(), rc.size() * 4);
   if (e == hipSuccess) e = up(L.rope_sin, rsn.data(), rsn.size() * 4);
   if (e == hipSuccess) e = up(L.wqueue, wq.data(), wq.size() * 4);
+  if (e == hipSuccess) e = hipDeviceSynchronize();  // the weight repacking
   if (e != hipSuccess) {
     (void)hipFree(p->d_ws);
+    (void)hipFree(p->d_wpk);
     p->d_ws = nullptr;
-    return pfail(hip_msg("prefill workspace upload", e));
+    p->d_wpk = nullptr;
+    return pfail(hip_msg("prefill workspace upload / weight repacking", e));
   }
   PParams& P = p->P;
   P.L = s.L; P.H = s.H; P.Hq = s.Hq; P.Hkv = s.Hkv; P.D = s.D; P.F = s.F; P.V = s.V;
@@ -279,7 +309,9 @@ wpk_prefill_plan* build(const wpk_model_desc* desc, int32_t batch, int32_t ctx_l
     e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
     if (e != hipSuccess) {
       (void)hipFree(p->d_ws);
+      (void)hipFree(p->d_wpk);
       p->d_ws = nullptr;
+      p->d_wpk = nullptr;
       return pfail(hip_msg("hipStreamCreate", e));
     }
     p->cap_stream = cs;
@@ -390,9 +422,10 @@ void wpk_prefill_destroy(wpk_prefill_plan* p) {
   if (p->graph_exec) (void)hipGraphExecDestroy((hipGraphExec_t)p->graph_exec);
   if (p->graph) (void)hipGraphDestroy((hipGraph_t)p->graph);
   if (p->cap_stream) (void)hipStreamDestroy((hipStream_t)p->cap_stream);
-  if (p->d_ws) {
+  if (p->d_ws || p->d_wpk) {
     (void)hipDeviceSynchronize();
-    (void)hipFree(p->d_ws);
+    if (p->d_ws) (void)hipFree(p->d_ws);
+    if (p->d_wpk) (void)hipFree(p->d_wpk);
   }
   delete p;
 }
@@ -451,7 +484,7 @@ int32_t wpk_prefill_get_info(const wpk_prefill_plan* p, wpk_prefill_info* out) {
   out->split_workers = p->split_workers;
   out->n_phases = (int32_t)p->dag.phases.size();
   out->rows_per_sequence = p->s.Pp;
-  out->workspace_bytes = p->ws_bytes;
+  out->workspace_bytes = p->ws_bytes + p->wpk_bytes;
   out->flops = prefill_flops(p->s);
   return WPK_OK;
 }

@@ -33,6 +33,7 @@ struct PSmem {
     uint16_t vt[2][kHeadDim][kVtPitch];  // attention: one key step of V, [dim][key]
     u32x4 gs[3][kGBlocks][64];           // matrix-core tiles: three k-steps of fragments, 16 bytes per lane
   };
+  float nss[4][16];  // norm tiles: each wave's sums of squares of the 16 rows
   int claim[2];
   int stop;
 };
@@ -134,22 +135,23 @@ __device__ __forceinline__ uint32_t pk(uint32_t r, uint32_t k, uint32_t K) {
 
 // ---- RMSNorm of rows -------------------------------------------------------------------------
 // y = x / sqrt(mean(x^2) + eps) * gain, stored as the hi and lo bf16 planes
-// of the packed matrix-core operand.  A wave takes 16 rows at a time in the
-// fragment layout: lane l holds row l % 16, columns 8 (l / 16) .. +7 of each
-// 32-column k-step, so every store is one contiguous KiB per wave.  First
-// pass: each lane sums the squares of its columns in order, then the four
-// lanes of a row combine with lane swaps (a fixed order); second pass: the
-// rows are read again (from the cache), scaled and stored.
-// src(r, k) gives 8 fp32 values of row r from column k; rows past the prompt
-// (zero) are produced the same way.
+// of the packed matrix-core operand.  A norm tile takes 16 rows; wave w takes
+// a quarter of the columns in the fragment layout (lane l: row l % 16,
+// columns 8 (l / 16) .. +7 of each 32-column k-step), so every store is one
+// contiguous KiB per wave and all of a wave's loads of a pass are in flight
+// at once.  Sums of squares: each lane in column order, the four lanes of a
+// row with lane swaps, then the four waves' quarters in wave order through
+// LDS (a fixed order).  Second pass: the rows are read again (from the
+// cache), scaled and stored.  src(r, k, a, b) gives 8 fp32 values of row r
+// from column k.
 template <typename SRC>
 __device__ __forceinline__ void norm_rows16(const PParams& P, int r0, const SRC& src, const float* gain,
                                             __amdgpu_buffer_rsrc_t yh, __amdgpu_buffer_rsrc_t yl,
-                                            __amdgpu_buffer_rsrc_t xc, bool copy, int lane) {
-  const int r = r0 + (lane & 15), c8 = 8 * (lane >> 4), nks = P.H / 32;
+                                            __amdgpu_buffer_rsrc_t xc, bool copy, PSmem& sm, int w, int lane) {
+  const int r = r0 + (lane & 15), c8 = 8 * (lane >> 4), nks = P.H / 32, q = nks / 4, k0 = w * q;
   float ss = 0.f;
-#pragma unroll 4
-  for (int ks = 0; ks < nks; ++ks) {
+#pragma unroll 16
+  for (int ks = k0; ks < k0 + q; ++ks) {
     f32x4 a, b;
     src(r, 32 * ks + c8, a, b);
     ss += ((a[0] * a[0] + a[1] * a[1]) + (a[2] * a[2] + a[3] * a[3])) +
@@ -157,10 +159,14 @@ __device__ __forceinline__ void norm_rows16(const PParams& P, int r0, const SRC&
   }
   ss = xsum<16>(ss);
   ss = xsum<32>(ss);
-  const float inv = 1.0f / sqrtf(ss / (float)P.H + P.eps);
+  if (lane < 16) sm.nss[w][lane] = ss;
+  __syncthreads();
+  const int rr = lane & 15;
+  const float tot = (sm.nss[0][rr] + sm.nss[1][rr]) + (sm.nss[2][rr] + sm.nss[3][rr]);
+  const float inv = 1.0f / sqrtf(tot / (float)P.H + P.eps);
   const uint32_t blk = (uint32_t)(r0 >> 4) * (uint32_t)nks * 1024u + (uint32_t)lane * 16u;
-#pragma unroll 4
-  for (int ks = 0; ks < nks; ++ks) {
+#pragma unroll 16
+  for (int ks = k0; ks < k0 + q; ++ks) {
     const int k = 32 * ks + c8;
     f32x4 a, b;
     src(r, k, a, b);
@@ -182,44 +188,42 @@ __device__ __forceinline__ void norm_rows16(const PParams& P, int r0, const SRC&
   }
 }
 
-// A row block's norm: wave w takes rows 32w .. 32w+31 (two groups of 16).
-// Layer 0 gathers the embedding rows (token ids checked; padding rows past
-// the prompt are zero) and keeps them as the residual stream.
-__device__ void norm_tile(const PParams& P, const Tile& T, int tid) {
+// A norm tile: rows 16 sub .. +15 of its row block.  Layer 0 gathers the
+// embedding rows (token ids checked; padding rows past the prompt are zero)
+// and keeps them as the residual stream.
+__device__ void norm_tile(const PParams& P, const Tile& T, PSmem& sm, int tid) {
   const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const PLayer Lw = cload(P.layers, T.layer);
   const size_t plane = (size_t)P.R * P.H;
   uint16_t* y = T.type == P_NORM2 ? Lw.xn2 : Lw.xn1;
   const __amdgpu_buffer_rsrc_t yh = urs(y), yl = urs(y + plane), xc = urs(P.x0);
-  for (int grp = 0; grp < 2; ++grp) {
-    const int r0 = T.r0 * kPRows + w * 32 + 16 * grp;
-    if (T.type == P_EMBED) {
-      const int r = r0 + (lane & 15), b = r / P.Pp, p = r - b * P.Pp;
-      int tok = 0;
-      if (p < P.P) {
-        tok = P.prompt[(size_t)b * P.P + p];
-        if (tok < 0 || tok >= P.V) {
-          p_latch(P, WPK_E_TOKEN, T.id);
-          tok = 0;
-        }
+  const int r0 = T.r0 * kPRows + 16 * T.r1;
+  if (T.type == P_EMBED) {
+    const int r = r0 + (lane & 15), b = r / P.Pp, p = r - b * P.Pp;
+    int tok = 0;
+    if (p < P.P) {
+      tok = P.prompt[(size_t)b * P.P + p];
+      if (tok < 0 || tok >= P.V) {
+        if (w == 0) p_latch(P, WPK_E_TOKEN, T.id);
+        tok = 0;
       }
-      const uint16_t* er = P.embed + (size_t)tok * P.H;
-      const bool pad = p >= P.P;
-      auto src = [&](int, int k, f32x4& a, f32x4& bb) {
-        const u32x4 e = *(const u32x4*)(er + k);
-        a = pad ? f32x4{0.f, 0.f, 0.f, 0.f} : f32x4{bf16_lo(e.x), bf16_hi(e.x), bf16_lo(e.y), bf16_hi(e.y)};
-        bb = pad ? f32x4{0.f, 0.f, 0.f, 0.f} : f32x4{bf16_lo(e.z), bf16_hi(e.z), bf16_lo(e.w), bf16_hi(e.w)};
-      };
-      norm_rows16(P, r0, src, Lw.attn_norm, yh, yl, xc, true, lane);
-    } else {
-      const float* x = T.type == P_NORM1 ? Lw.x_in : Lw.x_mid;
-      auto src = [&](int r, int k, f32x4& a, f32x4& bb) {
-        const float* xr = x + (size_t)r * P.H + k;
-        a = *(const f32x4*)xr;
-        bb = *(const f32x4*)(xr + 4);
-      };
-      norm_rows16(P, r0, src, T.type == P_NORM1 ? Lw.attn_norm : Lw.mlp_norm, yh, yl, xc, false, lane);
     }
+    const uint16_t* er = P.embed + (size_t)tok * P.H;
+    const bool pad = p >= P.P;
+    auto src = [&](int, int k, f32x4& a, f32x4& bb) {
+      const u32x4 e = *(const u32x4*)(er + k);
+      a = pad ? f32x4{0.f, 0.f, 0.f, 0.f} : f32x4{bf16_lo(e.x), bf16_hi(e.x), bf16_lo(e.y), bf16_hi(e.y)};
+      bb = pad ? f32x4{0.f, 0.f, 0.f, 0.f} : f32x4{bf16_lo(e.z), bf16_hi(e.z), bf16_lo(e.w), bf16_hi(e.w)};
+    };
+    norm_rows16(P, r0, src, Lw.attn_norm, yh, yl, xc, true, sm, w, lane);
+  } else {
+    const float* x = T.type == P_NORM1 ? Lw.x_in : Lw.x_mid;
+    auto src = [&](int r, int k, f32x4& a, f32x4& bb) {
+      const float* xr = x + (size_t)r * P.H + k;
+      a = *(const f32x4*)xr;
+      bb = *(const f32x4*)(xr + 4);
+    };
+    norm_rows16(P, r0, src, T.type == P_NORM1 ? Lw.attn_norm : Lw.mlp_norm, yh, yl, xc, false, sm, w, lane);
   }
 }
 
@@ -718,7 +722,7 @@ __device__ __forceinline__ void run_tile(const PParams& P, const Tile& T, PSmem&
   switch (T.type) {
     case P_EMBED:
     case P_NORM1:
-    case P_NORM2: norm_tile(P, T, tid); break;
+    case P_NORM2: norm_tile(P, T, sm, tid); break;
     case P_QKV:
     case P_OPROJ:
     case P_GATEUP:

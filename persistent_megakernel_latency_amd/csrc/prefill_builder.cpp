@@ -120,8 +120,11 @@ PDag build_prefill_dag(const PShape& s) {
       dn_g[rb] = group();
     }
     auto rq = [&](int rb) { return rb % nq0; };  // row-block tiles: one queue (XCD) per row block
+    // norms: kPNormSplit tiles of 16 rows per row block (a norm is on every
+    // layer's critical path; one tile per row block took ~130 us)
     for (int rb = 0; rb < nrb; ++rb)
-      add(l == 0 ? P_EMBED : P_NORM1, l, l == 0 ? -1 : down_g[rb], n1_g[rb], rb, 0, rb / s.nrb_s, 0, 0, rq(rb));
+      for (int sub = 0; sub < kPNormSplit; ++sub)
+        add(l == 0 ? P_EMBED : P_NORM1, l, l == 0 ? -1 : down_g[rb], n1_g[rb], rb, sub, rb / s.nrb_s, 0, 0, rq(rb));
     for (int rb = 0; rb < nrb; ++rb)
       for (int cb = 0; cb < ncq; ++cb)
         add(P_QKV, l, n1_g[rb], qkv_g[rb / s.nrb_s], rb, cb, rb / s.nrb_s, 0, 0, rq(rb));
@@ -134,7 +137,8 @@ PDag build_prefill_dag(const PShape& s) {
         }
     for (int rb = 0; rb < nrb; ++rb)
       for (int cb = 0; cb < nch; ++cb) add(P_OPROJ, l, at_g[rb], o_g[rb], rb, cb, rb / s.nrb_s, 0, 0, rq(rb));
-    for (int rb = 0; rb < nrb; ++rb) add(P_NORM2, l, o_g[rb], n2_g[rb], rb, 0, rb / s.nrb_s, 0, 0, rq(rb));
+    for (int rb = 0; rb < nrb; ++rb)
+      for (int sub = 0; sub < kPNormSplit; ++sub) add(P_NORM2, l, o_g[rb], n2_g[rb], rb, sub, rb / s.nrb_s, 0, 0, rq(rb));
     for (int rb = 0; rb < nrb; ++rb)
       for (int cb = 0; cb < ncf; ++cb) add(P_GATEUP, l, n2_g[rb], gu_g[rb], rb, cb, rb / s.nrb_s, 0, 0, rq(rb));
     for (int rb = 0; rb < nrb; ++rb)
@@ -215,7 +219,7 @@ std::string validate_prefill_dag(const PShape& s, const PDag& d) {
   std::map<std::tuple<int, int, int, int, int>, int> cnt;  // (type, layer, a, b, c)
   for (const Tile& t : d.tiles) {
     switch (t.type) {
-      case P_EMBED: case P_NORM1: case P_NORM2: cnt[{t.type, t.layer, t.r0, 0, 0}]++; break;
+      case P_EMBED: case P_NORM1: case P_NORM2: cnt[{t.type, t.layer, t.r0, t.r1, 0}]++; break;
       case P_QKV: case P_OPROJ: case P_GATEUP: case P_DOWN: cnt[{t.type, t.layer, t.r0, t.r1, 0}]++; break;
       case P_ATTN: cnt[{t.type, t.layer, t.b, t.g, t.c}]++; break;
       case P_NORMF: cnt[{t.type, t.layer, t.b, 0, 0}]++; break;
@@ -226,7 +230,7 @@ std::string validate_prefill_dag(const PShape& s, const PDag& d) {
   for (const auto& kv : cnt)
     if (kv.second != 1) return "an output region is produced more than once";
   const int ncq = s.qkv_rows / kPCols, nch = s.H / kPCols, ncf = s.F / kPFfnCols;
-  const int64_t want = (int64_t)s.L * nrb * (2 + ncq + 2 * nch + ncf) + (int64_t)s.L * s.B * s.nqb * s.Hkv + s.B +
+  const int64_t want = (int64_t)s.L * nrb * (2 * kPNormSplit + ncq + 2 * nch + ncf) + (int64_t)s.L * s.B * s.nqb * s.Hkv + s.B +
                        ceil_div(s.V, kPLmCols) + 1;
   if ((int64_t)cnt.size() != want || (int64_t)n != want) return "the tiles do not cover the prefill";
   // inputs: each consumer's group holds exactly the producers of what it reads
@@ -249,7 +253,7 @@ std::string validate_prefill_dag(const PShape& s, const PDag& d) {
   auto want_producers = [&](const Tile& t) -> int64_t {
     switch (t.type) {
       case P_NORM1: case P_NORM2: return nch;
-      case P_QKV: case P_GATEUP: return 1;
+      case P_QKV: case P_GATEUP: return kPNormSplit;
       case P_ATTN: return (int64_t)s.nrb_s * ncq;
       case P_OPROJ: {
         const int j = t.r0 % s.nrb_s;

@@ -33,7 +33,8 @@ enum PrefillTileType : int32_t {
 
 // Tile fields (the 64-byte Tile of plan.h): type, layer, wait, signal, shard,
 // id as in the decode step; r0 = row block (b * blocks per sequence + j),
-// r1 = column block, b = sequence, g = kv head, c = 32-query block.
+// r1 = column block (norm tiles: which 16 rows of the row block), b =
+// sequence, g = kv head, c = 32-query block.
 
 constexpr int kPRows = 128;     // prompt rows of a row block (a matrix-core tile, a norm tile)
 constexpr int kPCols = 128;     // output columns of a QKV / o / down tile (two heads)
@@ -42,6 +43,7 @@ constexpr int kPQueries = 32;   // queries of an attention tile
 constexpr int kPKeys = 32;      // keys per attention step
 constexpr int kPLmCols = 128;   // vocabulary columns of an LM-head tile
 constexpr int kPThreads = 256;  // four waves per worker, all computing
+constexpr int kPNormSplit = kPRows / 16;  // norm tiles per row block (16 rows each)
 
 // Per-layer device pointers.  Every activation buffer is per layer and
 // written once per prefill, so a consumer never meets a line that was

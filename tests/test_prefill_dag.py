@@ -31,8 +31,8 @@ def _expected_counts(cfg, batch, prompt):
     nqb = math.ceil(prompt / 32)
     L = cfg.n_layers
     return {
-        "embed": nrb, "norm1": (L - 1) * nrb, "qkv": L * nrb * cfg.qkv_rows // 128,
-        "attn": L * batch * nqb * cfg.n_kv_heads, "oproj": L * nrb * cfg.hidden // 128, "norm2": L * nrb,
+        "embed": 8 * nrb, "norm1": 8 * (L - 1) * nrb, "qkv": L * nrb * cfg.qkv_rows // 128,
+        "attn": L * batch * nqb * cfg.n_kv_heads, "oproj": L * nrb * cfg.hidden // 128, "norm2": 8 * L * nrb,
         "gateup": L * nrb * cfg.ffn // 64, "down": L * nrb * cfg.hidden // 128, "normf": batch,
         "lm": math.ceil(cfg.vocab / 128), "argmax": 1,
     }
@@ -105,8 +105,8 @@ def test_prefill_dag_edges_follow_row_blocks():
             if signal[u] >= 0:
                 prod.setdefault(int(signal[u]), []).append(u)
         nrb_s = 2
-        per = {"qkv": 1, "attn": nrb_s * cfg.qkv_rows // 128, "norm2": cfg.hidden // 128,
-               "gateup": 1, "down": cfg.ffn // 64, "norm1": cfg.hidden // 128, "lm": batch,
+        per = {"qkv": 8, "attn": nrb_s * cfg.qkv_rows // 128, "norm2": cfg.hidden // 128,
+               "gateup": 8, "down": cfg.ffn // 64, "norm1": cfg.hidden // 128, "lm": batch,
                "argmax": math.ceil(cfg.vocab / 128), "normf": cfg.hidden // 128}
         src = {"qkv": ("embed", "norm1"), "attn": ("qkv",), "oproj": ("attn",), "norm2": ("oproj",),
                "gateup": ("norm2",), "down": ("gateup",), "norm1": ("down",), "normf": ("down",), "lm": ("normf",),

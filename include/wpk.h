@@ -486,6 +486,35 @@ int32_t wpk_prefill_get_info(const wpk_prefill_plan* plan, wpk_prefill_info* out
 int32_t wpk_prefill_get_dag(const wpk_prefill_plan* plan, int32_t* type, int32_t* layer, int32_t* wait,
                             int32_t* signal, int32_t* queue);
 
+/* The planner's prediction for a prefill design (source: "One Megakernel is
+ * Not Enough", the abstract and Table I -- candidate designs simulated on
+ * their tile and event graphs from per-operator profiles).  A discrete-event
+ * replay of the plan's own DAG and claim queues: W workers (a split plan's
+ * last split_workers claim only the attention queues), a tile starting when
+ * its worker is free and its counter group complete plus hop_us, lasting its
+ * measured cost (tile_us of its type; attention adds attn_step_us per
+ * 32-key step of its causal span); with conventional = 1 each (layer,
+ * operator) phase is one kernel over W workgroup slots, kernels separated by
+ * launch_gap_us.  Prefill tiles are compute-bound, so no bandwidth server is
+ * modelled (hbm_bytes and achieved_GBps are 0).  Host or device plans;
+ * split_workers must be positive exactly for split plans.  Deterministic. */
+typedef struct wpk_prefill_sim_params {
+  double tile_us[11];      /* per WPK_PTILE_* type */
+  double attn_step_us;
+  double hop_us;
+  double launch_gap_us;
+  int32_t workers;
+  int32_t split_workers;
+  int32_t conventional;
+  int32_t pad;
+} wpk_prefill_sim_params;
+int32_t wpk_prefill_simulate(const wpk_prefill_plan* plan, const wpk_prefill_sim_params* params,
+                             wpk_sim_result* out);
+/* Per tile id: the 32-key steps of an attention tile's causal span (the
+ * keys of its last query, rounded up), 0 for other tiles -- the term the
+ * simulation scales attn_step_us by.  Array of n_tiles. */
+int32_t wpk_prefill_get_key_steps(const wpk_prefill_plan* plan, int32_t* key_steps);
+
 #ifdef __cplusplus
 }
 #endif

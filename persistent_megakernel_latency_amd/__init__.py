@@ -116,6 +116,12 @@ class wpk_prefill_info(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_int64), ("flops", ctypes.c_double)]
 
 
+class wpk_prefill_sim_params(ctypes.Structure):
+    _fields_ = [("tile_us", ctypes.c_double * 11), ("attn_step_us", ctypes.c_double), ("hop_us", ctypes.c_double),
+                ("launch_gap_us", ctypes.c_double), ("workers", _i32), ("split_workers", _i32),
+                ("conventional", _i32), ("pad", _i32)]
+
+
 # Every symbol include/wpk.h declares, with its ctypes signature.
 _SIGNATURES = {
     "wpk_build": (_vp, [ctypes.POINTER(wpk_model_desc), _i32, _i32]),
@@ -152,6 +158,8 @@ _SIGNATURES = {
     "wpk_prefill_get_log": (_i32, [_vp, _vp, ctypes.c_size_t]),
     "wpk_prefill_get_info": (_i32, [_vp, ctypes.POINTER(wpk_prefill_info)]),
     "wpk_prefill_get_dag": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp]),
+    "wpk_prefill_simulate": (_i32, [_vp, ctypes.POINTER(wpk_prefill_sim_params), ctypes.POINTER(wpk_sim_result)]),
+    "wpk_prefill_get_key_steps": (_i32, [_vp, _vp]),
 }
 
 _lib = None
@@ -356,6 +364,21 @@ def wpk_prefill_get_dag(plan, n_tiles: int):
     if rc != WPK_OK:
         raise RuntimeError(f"wpk_prefill_get_dag failed: {rc}")
     return [list(a) for a in arrs]
+
+
+def wpk_prefill_simulate(plan, params: wpk_prefill_sim_params):
+    """(rc, wpk_sim_result) of the simulated prefill design."""
+    res = wpk_sim_result()
+    rc = lib().wpk_prefill_simulate(plan, ctypes.byref(params), ctypes.byref(res))
+    return rc, res
+
+
+def wpk_prefill_get_key_steps(plan, n_tiles: int):
+    arr = (_i32 * n_tiles)()
+    rc = lib().wpk_prefill_get_key_steps(plan, ctypes.cast(arr, _vp))
+    if rc != WPK_OK:
+        raise RuntimeError(f"wpk_prefill_get_key_steps failed: {rc}")
+    return list(arr)
 
 
 def check_prefill(rc: int, plan=None, what: str = "wpk_prefill call") -> None:

@@ -17,7 +17,9 @@
 
 #include <algorithm>
 #include <cstdio>
+#include <functional>
 #include <map>
+#include <queue>
 #include <set>
 #include <tuple>
 
@@ -300,6 +302,95 @@ std::string validate_prefill_dag(const PShape& s, const PDag& d) {
   for (int32_t i = 0; i < n; ++i)
     if (seen[i] != 1) return "the claim queues do not partition the tiles";
   return "";
+}
+
+// The prefill as the planner sees it ("One Megakernel is Not Enough": the
+// tile and event graph of a candidate design simulated from per-operator
+// profiles).  Prefill tiles are compute-bound, so a tile's time is its
+// measured cost (attention: a fixed part plus one per 32-key step of its
+// causal span); no bandwidth server is modelled.
+//  * megakernel / split: W workers, worker w claiming from its queue (w mod Q,
+//    or its region's queues in a split plan), in queue order, a tile when its
+//    worker is free; it starts when its counter group is complete plus a hop
+//    and ends its cost later, publishing then;
+//  * conventional: each (layer, operator) phase is one kernel over W
+//    workgroup slots (a tile goes to the earliest free slot), the next
+//    kernel starting a launch gap after the last tile of the previous one.
+double simulate_prefill(const PShape& s, const PDag& d, const PSimCost& c, int workers, int split_workers,
+                        bool conventional, double* busy_frac) {
+  const int32_t n = (int32_t)d.tiles.size();
+  std::vector<double> cost(n);
+  double work = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const Tile& t = d.tiles[i];
+    const double u = c.tile_us[t.type] + c.attn_step_us * prefill_key_steps(s, t);
+    cost[i] = u;
+    work += u;
+  }
+  double span = 0;
+  if (conventional) {
+    double t0 = 0;
+    for (const auto& ph : d.phases) {
+      std::priority_queue<double, std::vector<double>, std::greater<double>> slots;
+      for (int w = 0; w < std::min(workers, ph.second); ++w) slots.push(t0);
+      double end = t0;
+      for (int32_t k = 0; k < ph.second; ++k) {
+        const double st = slots.top();
+        slots.pop();
+        const double e = st + cost[ph.first + k];
+        end = std::max(end, e);
+        slots.push(e);
+      }
+      span = end;
+      t0 = end + c.launch_gap_us;
+    }
+  } else {
+    const int32_t nq = (int32_t)d.queue_off.size() - 1, q0 = d.split_queues ? d.split_queues : nq;
+    const int w0 = workers - split_workers;
+    // groups: producers remaining and completion time
+    std::vector<int32_t> left(d.groups.size());
+    std::vector<double> done(d.groups.size(), 0.0);
+    for (size_t g = 0; g < d.groups.size(); ++g) left[g] = d.groups[g].producers;
+    std::vector<double> end(n, -1.0);
+    // each queue: its workers' free times; a queue's next tile goes to its
+    // earliest free worker.  Tiles are processed in global claim (id) order,
+    // which is topological, so every producer's end is known first.
+    std::vector<std::priority_queue<double, std::vector<double>, std::greater<double>>> free_at(nq);
+    for (int w = 0; w < workers; ++w) {
+      const int q = !split_workers ? w % nq : w < w0 ? w % q0 : q0 + (w - w0) % (nq - q0);
+      free_at[q].push(0.0);
+    }
+    std::vector<int32_t> queue_of(n);
+    for (int32_t q = 0; q < nq; ++q)
+      for (int32_t k = d.queue_off[q]; k < d.queue_off[q + 1]; ++k) queue_of[d.queue[k]] = q;
+    // Claims within a queue happen in queue order as workers come free; with
+    // ids in topological order and each queue's tiles in id order, replaying
+    // tiles in id order assigns each to its queue's earliest free worker at
+    // that point, as the device does up to ties.
+    for (int32_t i = 0; i < n; ++i) {
+      const Tile& t = d.tiles[i];
+      auto& fq = free_at[queue_of[i]];
+      const double wf = fq.top();
+      fq.pop();
+      double st = wf;
+      if (t.wait >= 0) st = std::max(st, done[t.wait] + c.hop_us);
+      end[i] = st + cost[i];
+      fq.push(end[i]);
+      if (t.signal >= 0) {
+        done[t.signal] = std::max(done[t.signal], end[i]);
+        --left[t.signal];
+      }
+      span = std::max(span, end[i]);
+    }
+  }
+  if (busy_frac) *busy_frac = span > 0 ? work / (span * workers) : 0.0;
+  return span;
+}
+
+int32_t prefill_key_steps(const PShape& s, const Tile& t) {
+  if (t.type != P_ATTN) return 0;
+  const int kend = std::min(s.P, (t.c + 1) * kPQueries);
+  return (kend + kPKeys - 1) / kPKeys;
 }
 
 double prefill_flops(const PShape& s) {

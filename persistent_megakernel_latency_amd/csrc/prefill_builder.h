@@ -41,6 +41,22 @@ PDag build_prefill_dag(const PShape& s);
 // tile's inputs produced by the group it waits on.  Empty string when valid.
 std::string validate_prefill_dag(const PShape& s, const PDag& d);
 
+// The planner's prediction for a prefill design: a discrete-event replay of
+// the plan's DAG and claim queues with measured per-tile costs (see
+// prefill_builder.cpp).  workers: W; split_workers: the attention pool of a
+// split plan (0 otherwise); conventional: one kernel per operator phase.
+struct PSimCost {
+  double tile_us[P_NTYPES];  // per tile type (attention: fixed part)
+  double attn_step_us;       // attention: per 32-key step of the tile's causal span
+  double hop_us;             // a publish seen by a waiting worker
+  double launch_gap_us;      // conventional: between two operators' kernels
+};
+double simulate_prefill(const PShape& s, const PDag& d, const PSimCost& c, int workers, int split_workers,
+                        bool conventional, double* busy_frac);
+
+// 32-key steps of an attention tile's causal span (0 for other tiles).
+int32_t prefill_key_steps(const PShape& s, const Tile& t);
+
 // FLOPs of the prefill's matrix products (QKV, o, gate/up, down over all
 // prompt rows, causal QK and PV over the prompt, the LM head on the last rows).
 double prefill_flops(const PShape& s);

@@ -506,4 +506,35 @@ int32_t wpk_prefill_get_dag(const wpk_prefill_plan* p, int32_t* type, int32_t* l
   return WPK_OK;
 }
 
+int32_t wpk_prefill_simulate(const wpk_prefill_plan* p, const wpk_prefill_sim_params* sp, wpk_sim_result* out) {
+  if (!p || !sp || !out) return WPK_E_ARG;
+  if (sp->workers < p->s.queue_shards * (p->s.split ? 2 : 1)) return WPK_E_ARG;
+  if ((sp->split_workers > 0) != (p->s.split != 0) || sp->split_workers < 0) return WPK_E_ARG;
+  if (p->s.split && (sp->split_workers < p->s.queue_shards || sp->workers - sp->split_workers < p->s.queue_shards))
+    return WPK_E_ARG;
+  if (sp->conventional != 0 && sp->conventional != 1) return WPK_E_ARG;
+  if (sp->conventional && p->s.split) return WPK_E_ARG;
+  PSimCost c{};
+  for (int k = 0; k < P_NTYPES; ++k) {
+    if (!(sp->tile_us[k] >= 0)) return WPK_E_ARG;
+    c.tile_us[k] = sp->tile_us[k];
+  }
+  if (!(sp->attn_step_us >= 0) || !(sp->hop_us >= 0) || !(sp->launch_gap_us >= 0)) return WPK_E_ARG;
+  c.attn_step_us = sp->attn_step_us;
+  c.hop_us = sp->hop_us;
+  c.launch_gap_us = sp->launch_gap_us;
+  double busy = 0;
+  out->step_us = simulate_prefill(p->s, p->dag, c, sp->workers, sp->split_workers, sp->conventional != 0, &busy);
+  out->hbm_bytes = 0;
+  out->achieved_GBps = 0;
+  out->worker_busy_frac = busy;
+  return WPK_OK;
+}
+
+int32_t wpk_prefill_get_key_steps(const wpk_prefill_plan* p, int32_t* key_steps) {
+  if (!p || !key_steps) return WPK_E_ARG;
+  for (size_t i = 0; i < p->dag.tiles.size(); ++i) key_steps[i] = prefill_key_steps(p->s, p->dag.tiles[i]);
+  return WPK_OK;
+}
+
 }  // extern "C"

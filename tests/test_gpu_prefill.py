@@ -252,3 +252,29 @@ def test_prefill_bad_token_latches():
         g.run(prompt)
     finally:
         g.close()
+
+
+def test_split_prefill_log_places_attention_in_its_pool():
+    """Two co-resident megakernels: the canonical log holds, and the attention
+    tiles -- and only they -- ran on the last split_workers workers."""
+    cfg = synth.MINI
+    w = synth.make_weights(cfg, gain_std=0.1)
+    batch, cap, P, w1 = 3, 200, 150, 64
+    prompt = synth.prompt_tokens(cfg, batch, P, seed=13)
+    announce("prefill split log")
+    g = Prefill(cfg, w, batch, cap, P, mode=wpk.WPK_PREFILL_SPLIT, split_workers=w1)
+    try:
+        assert g.info.split_workers == w1
+        wpk.check_prefill(wpk.wpk_prefill_set_option(g.plan, wpk.WPK_OPT_LOG, 1), g.plan)
+        g.run(prompt)
+        ty, layer, wait, signal, queue = g.dag()
+        log = g.log()
+        check_log(log, wait, signal)
+        from tests.helpers import log_array
+        a = log_array(log)
+        w0 = g.info.workers - w1
+        attn = np.asarray(ty) == wpk.PREFILL_TILE_TYPES.index("attn")
+        assert np.all(a["worker"][attn] >= w0)
+        assert np.all(a["worker"][~attn] < w0)
+    finally:
+        g.close()

@@ -222,7 +222,7 @@ def ttft_block(wpk, torch, cfg, desc, args, dev):
     seeded random ids, prefill through every layer and the LM head on each
     sequence's last prompt row (the first greedy token).  Run as one
     megakernel, as two co-resident megakernels (attention tiles in their own
-    worker pool of 64, 128 or 256 of the 512 workers) and as the per-operator
+    worker pool of 32, 64 or 128 of the 256 workers) and as the per-operator
     hipGraph; each run is bracketed by HIP events on the launch stream."""
     import synth
     batch, P, cap = 16, TTFT_PROMPT, 512
@@ -238,8 +238,8 @@ def ttft_block(wpk, torch, cfg, desc, args, dev):
     out = {"workload": f"Llama-3.2-1B-shape prefill, batch {batch}, {P}-token prompts, first greedy token",
            "batch": batch, "prompt": P}
     first = None
-    for name, mode, w1 in (("megakernel", wpk.WPK_PREFILL_MEGAKERNEL, 0), ("split_64", wpk.WPK_PREFILL_SPLIT, 64),
-                           ("split_128", wpk.WPK_PREFILL_SPLIT, 128), ("split_256", wpk.WPK_PREFILL_SPLIT, 256),
+    for name, mode, w1 in (("megakernel", wpk.WPK_PREFILL_MEGAKERNEL, 0), ("split_32", wpk.WPK_PREFILL_SPLIT, 32),
+                           ("split_64", wpk.WPK_PREFILL_SPLIT, 64), ("split_128", wpk.WPK_PREFILL_SPLIT, 128),
                            ("graph_baseline", wpk.WPK_PREFILL_GRAPH, 0)):
         plan = wpk.wpk_build_prefill(desc.desc, batch, cap, P, wpk.wpk_prefill_opts(mode=mode, split_workers=w1))
         if not plan:
@@ -279,7 +279,7 @@ def ttft_block(wpk, torch, cfg, desc, args, dev):
     out["mfma"] = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                    "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
                    "kernel": "wpk::prefill_megakernel", "source_hash": wpk.prefill_source_hash()}
-    best = min(("split_64", "split_128", "split_256"), key=lambda k: out[k]["latency_us"]["mean"])
+    best = min(("split_32", "split_64", "split_128"), key=lambda k: out[k]["latency_us"]["mean"])
     out["best_split"] = best
     out["split_vs_megakernel"] = round(out[best]["latency_us"]["mean"] / mk, 3)
     out["graph_vs_megakernel"] = round(out["graph_baseline"]["latency_us"]["mean"] / mk, 3)

@@ -446,7 +446,7 @@ int32_t wpk_debug_read_act(wpk_plan* plan, void* host_dst, size_t bytes, size_t*
 typedef struct wpk_prefill_opts {
   int32_t mode;            /* WPK_PREFILL_* (default 0) */
   int32_t split_workers;   /* WPK_PREFILL_SPLIT: workers of the attention megakernel (0: an eighth) */
-  int32_t workers_per_cu;  /* resident workers per compute unit, 1 or 2 (0: 2) */
+  int32_t workers_per_cu;  /* 0 or 1: one eight-wave worker per compute unit (others are refused) */
 } wpk_prefill_opts;
 typedef struct wpk_prefill_info {
   int32_t n_tiles, n_groups, n_queues;

@@ -2,11 +2,14 @@
 // kernel on gfx950, and the conventional one-kernel-per-operator baseline
 // built from the same tile bodies.
 //
-// A worker is four waves that all compute: prefill tiles are compute-bound
-// (a matrix-core tile is 128 x 128 x K), so the decode step's split into a
-// latency-hiding control wave and weight-streaming compute waves buys
-// nothing here.  Wave 0 polls the tile's counter group; thread 0 claims the
-// next tile while the current one runs, then publishes.
+// A worker is one workgroup of eight waves per compute unit, all computing:
+// prefill tiles are compute-bound (a matrix-core tile is 128 x 256 x K), so
+// the decode step's split into a latency-hiding control wave and
+// weight-streaming compute waves buys nothing here, and one wide tile per CU
+// fetches each k-step's fragments once for all eight waves (two 128 x 128
+// tiles side by side on one CU would fetch the operand rows twice).  Wave 0
+// polls the tile's counter group; thread 0 claims the next tile while the
+// current one runs, then publishes.
 //
 // Coherence.  The eight XCDs' L2 caches are not coherent with each other.
 // Outputs are written with device-coherent (sc1, write-through) stores, and
@@ -26,14 +29,14 @@ namespace {
 
 constexpr int kVtPitch = 40;  // bf16 elements per transposed V row (32 keys + pad)
 
-constexpr int kGBlocks = 24;  // 1 KiB fragment blocks of a matrix-core k-step: 8 weight, 8 operand hi, 8 lo
+constexpr int kGBlocks = 32;  // 1 KiB fragment blocks of a matrix-core k-step: 16 weight, 8 operand hi, 8 lo
 
 struct PSmem {
   union alignas(16) {
     uint16_t vt[2][kHeadDim][kVtPitch];  // attention: one key step of V, [dim][key]
     u32x4 gs[3][kGBlocks][64];           // matrix-core tiles: three k-steps of fragments, 16 bytes per lane
   };
-  float nss[4][16];  // norm tiles: each wave's sums of squares of the 16 rows
+  float nss[kPWaves][16];  // norm tiles: each wave's sums of squares of the 16 rows
   int claim[2];
   int stop;
 };
@@ -136,19 +139,19 @@ __device__ __forceinline__ uint32_t pk(uint32_t r, uint32_t k, uint32_t K) {
 // ---- RMSNorm of rows -------------------------------------------------------------------------
 // y = x / sqrt(mean(x^2) + eps) * gain, stored as the hi and lo bf16 planes
 // of the packed matrix-core operand.  A norm tile takes 16 rows; wave w takes
-// a quarter of the columns in the fragment layout (lane l: row l % 16,
+// an eighth of the columns in the fragment layout (lane l: row l % 16,
 // columns 8 (l / 16) .. +7 of each 32-column k-step), so every store is one
 // contiguous KiB per wave and all of a wave's loads of a pass are in flight
 // at once.  Sums of squares: each lane in column order, the four lanes of a
-// row with lane swaps, then the four waves' quarters in wave order through
-// LDS (a fixed order).  Second pass: the rows are read again (from the
+// row with lane swaps, then the eight waves' parts in a fixed order through
+// LDS.  Second pass: the rows are read again (from the
 // cache), scaled and stored.  src(r, k, a, b) gives 8 fp32 values of row r
 // from column k.
 template <typename SRC>
 __device__ __forceinline__ void norm_rows16(const PParams& P, int r0, const SRC& src, const float* gain,
                                             __amdgpu_buffer_rsrc_t yh, __amdgpu_buffer_rsrc_t yl,
                                             __amdgpu_buffer_rsrc_t xc, bool copy, PSmem& sm, int w, int lane) {
-  const int r = r0 + (lane & 15), c8 = 8 * (lane >> 4), nks = P.H / 32, q = nks / 4, k0 = w * q;
+  const int r = r0 + (lane & 15), c8 = 8 * (lane >> 4), nks = P.H / 32, q = nks / kPWaves, k0 = w * q;
   float ss = 0.f;
 #pragma unroll 16
   for (int ks = k0; ks < k0 + q; ++ks) {
@@ -162,7 +165,8 @@ __device__ __forceinline__ void norm_rows16(const PParams& P, int r0, const SRC&
   if (lane < 16) sm.nss[w][lane] = ss;
   __syncthreads();
   const int rr = lane & 15;
-  const float tot = (sm.nss[0][rr] + sm.nss[1][rr]) + (sm.nss[2][rr] + sm.nss[3][rr]);
+  const float tot = ((sm.nss[0][rr] + sm.nss[1][rr]) + (sm.nss[2][rr] + sm.nss[3][rr])) +
+                    ((sm.nss[4][rr] + sm.nss[5][rr]) + (sm.nss[6][rr] + sm.nss[7][rr]));
   const float inv = 1.0f / sqrtf(tot / (float)P.H + P.eps);
   const uint32_t blk = (uint32_t)(r0 >> 4) * (uint32_t)nks * 1024u + (uint32_t)lane * 16u;
 #pragma unroll 16
@@ -256,7 +260,7 @@ __device__ void normf_tile(const PParams& P, const Tile& T, int tid) {
   }
 }
 
-// ---- matrix-core tiles: 128 prompt rows x 128 output columns x all of K ----------------------
+// ---- matrix-core tiles: 128 prompt rows x 256 output columns x all of K ----------------------
 //
 // v_mfma_f32_16x16x32_bf16 with the weights as the A operand (lane l: weight
 // row l % 16, eight K values from 8 (l / 16)) and the activations as B (lane
@@ -268,11 +272,11 @@ __device__ void normf_tile(const PParams& P, const Tile& T, int tid) {
 // 64 (w & 1) .. +63 and columns 64 (w >> 1) .. +63 (one head of QKV): four
 // column blocks j x four row blocks i.
 //
-// A k-step (32 of K) needs 24 fragment blocks of 1 KiB (16 bytes per lane in
-// fragment order): 8 weight blocks of 16 rows, 8 operand blocks of 16 rows in
-// the hi plane and 8 in the lo plane.  Each wave loads 6 of them into
-// registers two k-steps ahead and writes them to one of two LDS stages; after
-// a barrier every wave reads its 12 blocks from LDS.  Each block is fetched
+// A k-step (32 of K) needs 32 fragment blocks of 1 KiB (16 bytes per lane in
+// fragment order): 16 weight blocks of 16 rows, 8 operand blocks of 16 rows
+// in the hi plane and 8 in the lo plane.  Each wave loads 4 of them into
+// registers two k-steps ahead and writes them to an LDS stage; after a
+// barrier every wave reads its 12 blocks from LDS.  Each block is fetched
 // from the caches once per tile instead of once per wave that uses it.
 __device__ void gemm_tile(const PParams& P, const Tile& T0, PSmem& sm, int tid) {
   const Tile T = uni(T0);
@@ -292,9 +296,9 @@ __device__ void gemm_tile(const PParams& P, const Tile& T0, PSmem& sm, int tid) 
   const bool gu = T.type == P_GATEUP;
   const int row0 = T.r0 * kPRows + 64 * wr;
   // this wave's loads: weight blocks 2w, 2w+1 (block jj: column group jj / 4, block jj % 4 of it),
-  // operand blocks 2w, 2w+1 of the hi and of the lo plane
+  // operand block w of the hi and of the lo plane
   const __amdgpu_buffer_rsrc_t ra = urs(A), rl = urs(A + (size_t)P.R * K);
-  uint32_t gv[6];
+  uint32_t gv[3];
   __amdgpu_buffer_rsrc_t gr[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
@@ -304,24 +308,20 @@ __device__ void gemm_tile(const PParams& P, const Tile& T0, PSmem& sm, int tid) 
     // packed operands: the fragment of 16 rows at k-step ks is the KiB at
     // (row block * K / 32 + ks) * 1024, the lane's 16 bytes at 16 lane
     gv[q] = ((uint32_t)(row >> 4) * (uint32_t)(K >> 5) * 64u + lane) * 16u;
-    gv[2 + q] = ((uint32_t)(T.r0 * (kPRows / 16) + 2 * w + q) * (uint32_t)(K >> 5) * 64u + lane) * 16u;
   }
-  auto gload = [&](u32x4 (&G)[6], int ks) {
+  gv[2] = ((uint32_t)(T.r0 * (kPRows / 16) + w) * (uint32_t)(K >> 5) * 64u + lane) * 16u;
+  auto gload = [&](u32x4 (&G)[4], int ks) {
     const uint32_t so = (uint32_t)ks * 1024u;
     G[0] = ld16(gr[0], gv[0], so);
     G[1] = ld16(gr[1], gv[1], so);
     G[2] = ld16(ra, gv[2], so);
-    G[3] = ld16(ra, gv[3], so);
-    G[4] = ld16(rl, gv[2], so);
-    G[5] = ld16(rl, gv[3], so);
+    G[3] = ld16(rl, gv[2], so);
   };
-  auto lput = [&](int st, const u32x4 (&G)[6]) {
+  auto lput = [&](int st, const u32x4 (&G)[4]) {
     sm.gs[st][2 * w][lane] = G[0];
     sm.gs[st][2 * w + 1][lane] = G[1];
-    sm.gs[st][8 + 2 * w][lane] = G[2];
-    sm.gs[st][8 + 2 * w + 1][lane] = G[3];
-    sm.gs[st][16 + 2 * w][lane] = G[4];
-    sm.gs[st][16 + 2 * w + 1][lane] = G[5];
+    sm.gs[st][16 + w][lane] = G[2];
+    sm.gs[st][24 + w][lane] = G[3];
   };
   f32x4 acc[4][4];
 #pragma unroll
@@ -338,8 +338,8 @@ __device__ void gemm_tile(const PParams& P, const Tile& T0, PSmem& sm, int tid) 
     for (int j = 0; j < 4; ++j) f.b[j] = as_bf16x8(sm.gs[st][4 * wc + j][lane]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      f.a[i] = as_bf16x8(sm.gs[st][8 + 4 * wr + i][lane]);
-      f.al[i] = as_bf16x8(sm.gs[st][16 + 4 * wr + i][lane]);
+      f.a[i] = as_bf16x8(sm.gs[st][16 + 4 * wr + i][lane]);
+      f.al[i] = as_bf16x8(sm.gs[st][24 + 4 * wr + i][lane]);
     }
   };
   // the hi products, then the lo products: no two consecutive products share an accumulator
@@ -367,7 +367,7 @@ __device__ void gemm_tile(const PParams& P, const Tile& T0, PSmem& sm, int tid) 
   // keep each group's loads ahead of the products they overlap.
   const int nk = K / 32;
   auto kc = [&](int ks) { return min(ks, nk - 1); };
-  u32x4 G0[6], G1[6];
+  u32x4 G0[4], G1[4];
   Frag F0, F1;
   gload(G0, 0);
   __builtin_amdgcn_sched_barrier(0);
@@ -405,7 +405,7 @@ __device__ void gemm_tile(const PParams& P, const Tile& T0, PSmem& sm, int tid) 
   const int e4 = 4 * (lane >> 4);
   switch (T.type) {
     case P_QKV: {
-      const int hh = 2 * T.r1 + wc;  // head of this wave's 64 columns: q heads, then k, then v
+      const int hh = T.r1 * (kPCols / kHeadDim) + wc;  // head of this wave's 64 columns: q heads, then k, then v
       const bool isq = hh < P.Hq, isk = !isq && hh < P.Hq + P.Hkv;
       const __amdgpu_buffer_rsrc_t rd = urs(isq ? (void*)Lw.q : isk ? (void*)P.kc : (void*)P.vc);
       const int kh = isk ? hh - P.Hq : hh - P.Hq - P.Hkv;
@@ -473,8 +473,11 @@ __device__ void gemm_tile(const PParams& P, const Tile& T0, PSmem& sm, int tid) 
   }
 }
 
-// ---- causal attention: (sequence, kv head, 32 queries), one q head per wave --------------------
+// ---- causal attention: (sequence, kv head, 64 queries) ------------------------------------------
 //
+// Wave w takes q head w % 4 of the kv head's group and queries 32 (w / 4) ..
+// +31 of the tile (waves past the group size idle); every wave of the
+// worker shares the staged V of a step.
 // Per step of 32 keys, on the matrix cores:
 //  * S^T = K Q^T: A = K rows from the cache (lane l: key l % 16, dims
 //    8 (l / 16) ..), B = the wave's queries (query l % 16), scaled by 1/sqrt(D)
@@ -485,13 +488,14 @@ __device__ void gemm_tile(const PParams& P, const Tile& T0, PSmem& sm, int tid) 
 //    layout; the four lanes of a query combine maxima with lane swaps.
 //  * O^T += V^T P^T: B = the lane's own eight probabilities (hi + lo bf16), in
 //    K order 8 (l / 16) + 4 kb + e <-> key 16 kb + 4 (l / 16) + e; A = V from
-//    LDS, staged transposed ([dim][key]) by all four waves, read in that
+//    LDS, staged transposed ([dim][key]) by all eight waves, read in that
 //    same key order.  Lane l accumulates dims 4 (l / 16) + e of query l % 16.
 // Causality masks keys past each query and past the prompt; V rows past the
 // prompt are staged as zeros, K rows past it re-read the last prompt row.
 // Rounding the queries or the probabilities to plain bf16 alone moves the
 // last-position logits of the 16-layer model by about 2e-2, hence the pairs.
-constexpr int kPQB = kPQueries / 16;  // 16-query blocks per wave
+constexpr int kPQB = 2;  // 16-query blocks per wave
+static_assert(kPQueries == 2 * 16 * kPQB && kPWaves == 2 * kMaxGroupHeads, "attention waves: 4 heads x 2 query halves");
 
 __device__ void attn_tile(const PParams& P, const Tile& T0, PSmem& sm, int tid) {
   const Tile T = uni(T0);
@@ -499,8 +503,9 @@ __device__ void attn_tile(const PParams& P, const Tile& T0, PSmem& sm, int tid) 
   const PLayer Lw = cload(P.layers, T.layer);
   const int q0 = T.c * kPQueries, nq = min(kPQueries, P.P - q0), kend = q0 + nq;
   const int nsteps = (kend + kPKeys - 1) / kPKeys;
-  const bool active = w < P.G;
-  const int h = T.g * P.G + (active ? w : 0);
+  const int hw = w & (kMaxGroupHeads - 1), qw = q0 + 16 * kPQB * (w >> 2);  // this wave's first query
+  const bool active = hw < P.G && qw < kend;  // waves whose queries are all padding idle too
+  const int h = T.g * P.G + (hw < P.G ? hw : 0);
   const size_t kvpos = (((size_t)T.layer * P.B + T.b) * P.Hkv + T.g) * P.cap;  // position 0 of this kv head
   const __amdgpu_buffer_rsrc_t rk = urs(P.kc + kvpos * kHeadDim), rv = urs(P.vc + kvpos * kHeadDim);
   const int l15 = lane & 15, g4 = lane >> 4;
@@ -509,7 +514,7 @@ __device__ void attn_tile(const PParams& P, const Tile& T0, PSmem& sm, int tid) 
   bf16x8 qh[kPQB][2], ql[kPQB][2];
 #pragma unroll
   for (int i = 0; i < kPQB; ++i) {
-    const float* qr = Lw.q + ((size_t)T.b * P.Pp + q0 + 16 * i + l15) * P.Hq * kHeadDim + h * kHeadDim;
+    const float* qr = Lw.q + ((size_t)T.b * P.Pp + qw + 16 * i + l15) * P.Hq * kHeadDim + h * kHeadDim;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const f32x4 x0 = *(const f32x4*)(qr + 32 * s + 8 * g4) * P.attn_scale;
@@ -526,20 +531,19 @@ __device__ void attn_tile(const PParams& P, const Tile& T0, PSmem& sm, int tid) 
       for (int s = 0; s < 2; ++s) kf[kb][s] = ld16(rk, (uint32_t)(key * kHeadDim + 32 * s + 8 * g4) * 2u, 0);
     }
   };
-  // V staging: thread t loads dims 8 (t % 8) .. +7 of key t / 8 of the step
-  const int vkey = tid >> 3, vd0 = 8 * (tid & 7);
-  auto vload = [&](int k0) -> u32x4 {
+  // V staging: thread t loads dims 4 (t % 16) .. +3 of key t / 16 of the step
+  static_assert(kPThreads == kPKeys * kHeadDim / 4, "V staging: one 8-byte chunk per thread");
+  const int vkey = tid >> 4, vd0 = 4 * (tid & 15);
+  auto vload = [&](int k0) -> u32x2 {
     const int key = k0 + vkey;
-    const u32x4 v = ld16(rv, (uint32_t)(min(key, kend - 1) * kHeadDim + vd0) * 2u, 0);
-    return key < kend ? v : u32x4{0u, 0u, 0u, 0u};
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rv, (uint32_t)(min(key, kend - 1) * kHeadDim + vd0) * 2u, 0, 0);
+    return key < kend ? v : u32x2{0u, 0u};
   };
-  auto vstore = [&](int buf, u32x4 v) {
-    const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      sm.vt[buf][vd0 + 2 * e][vkey] = (uint16_t)(wv[e] & 0xFFFFu);
-      sm.vt[buf][vd0 + 2 * e + 1][vkey] = (uint16_t)(wv[e] >> 16);
-    }
+  auto vstore = [&](int buf, u32x2 v) {
+    sm.vt[buf][vd0][vkey] = (uint16_t)(v.x & 0xFFFFu);
+    sm.vt[buf][vd0 + 1][vkey] = (uint16_t)(v.x >> 16);
+    sm.vt[buf][vd0 + 2][vkey] = (uint16_t)(v.y & 0xFFFFu);
+    sm.vt[buf][vd0 + 3][vkey] = (uint16_t)(v.y >> 16);
   };
 
   float m[kPQB], lsum[kPQB];
@@ -551,7 +555,8 @@ __device__ void attn_tile(const PParams& P, const Tile& T0, PSmem& sm, int tid) 
 #pragma unroll
     for (int db = 0; db < 4; ++db) o[db][i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  u32x4 kf[2][2], vreg = vload(0);
+  u32x4 kf[2][2];
+  u32x2 vreg = vload(0);
   kload(0, kf);
   for (int ks = 0; ks < nsteps; ++ks) {
     const int k0 = ks * kPKeys, buf = ks & 1;
@@ -562,7 +567,9 @@ __device__ void attn_tile(const PParams& P, const Tile& T0, PSmem& sm, int tid) 
     u32x4 nkf[2][2];
     vreg = vload(kn);
     kload(kn, nkf);
-    if (active) {
+    // a step past this wave's last query is masked whole: skipped (the wave's
+    // SIMD partner, the other query half of the same head, runs alone)
+    if (active && k0 <= qw + 16 * kPQB - 1) {
       f32x4 st[2][kPQB];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -579,7 +586,7 @@ __device__ void attn_tile(const PParams& P, const Tile& T0, PSmem& sm, int tid) 
       bf16x8 ph[kPQB], pl[kPQB];
 #pragma unroll
       for (int i = 0; i < kPQB; ++i) {
-        const int qpos = q0 + 16 * i + l15;
+        const int qpos = qw + 16 * i + l15;
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -630,7 +637,7 @@ __device__ void attn_tile(const PParams& P, const Tile& T0, PSmem& sm, int tid) 
   for (int i = 0; i < kPQB; ++i) {
     float lt = xsum<16>(lsum[i]);
     lt = xsum<32>(lt);
-    const int qpos = q0 + 16 * i + l15;
+    const int qpos = qw + 16 * i + l15;
     if (qpos >= P.P) continue;
     const float inv = 1.0f / lt;
     const uint32_t orow = (uint32_t)T.b * P.Pp + qpos, ocol = (uint32_t)h * kHeadDim + 4 * g4;
@@ -640,7 +647,7 @@ __device__ void attn_tile(const PParams& P, const Tile& T0, PSmem& sm, int tid) 
   }
 }
 
-// ---- LM head on the last prompt rows: 128 vocabulary columns per tile ------------------------
+// ---- LM head on the last prompt rows: 256 vocabulary columns per tile ------------------------
 // Wave w: vocabulary rows 32 w .. +31 of the tile (two 16-row blocks) against
 // 16 sequences at a time (the final-normed rows, hi and lo bf16 planes).  Logits are stored in
 // fp32; the partial greedy choice (value, lowest index) goes to one of 16
@@ -693,7 +700,7 @@ __device__ void lm_tile(const PParams& P, const Tile& T0, int tid) {
     best = xmax_u64<16>(best);
     best = xmax_u64<32>(best);
     if (g4 == 0 && seq < P.B && best)
-      __hip_atomic_fetch_max(&P.argmax[(size_t)seq * kArgmaxShards + (T.r1 * 4 + w) % kArgmaxShards], best,
+      __hip_atomic_fetch_max(&P.argmax[(size_t)seq * kArgmaxShards + (T.r1 * kPWaves + w) % kArgmaxShards], best,
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
@@ -738,7 +745,7 @@ __device__ __forceinline__ void run_tile(const PParams& P, const Tile& T, PSmem&
 
 // The persistent prefill: each worker claims from its queue in topological
 // order (the next claim in flight while a tile runs), waits for the tile's
-// group, runs it with all four waves, waits for its stores and publishes.
+// group, runs it with all eight waves, waits for its stores and publishes.
 // The last worker out rewinds the queues and advances the epoch.
 template <bool LOG>
 __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2))) void prefill_megakernel(PParams P) {

@@ -3,11 +3,11 @@
 // Per layer, in claim order (operator-major across sequences, so the first
 // sequences' later operators become ready while the last sequences' earlier
 // ones still run):
-//   NORM1 / EMBED (row block)  ->  QKV (row block, 2 heads)
+//   NORM1 / EMBED (row block)  ->  QKV (row block, 4 heads)
 //   ->  ATTN (sequence, kv head, query block: waits for the whole sequence's
 //       K and V, the causal span of its last query block)
-//   ->  OPROJ (row block, 128 columns)  ->  NORM2 (row block)
-//   ->  GATEUP (row block, 64 ffn columns)  ->  DOWN (row block, 128 columns)
+//   ->  OPROJ (row block, 256 columns)  ->  NORM2 (row block)
+//   ->  GATEUP (row block, 128 ffn columns)  ->  DOWN (row block, 256 columns)
 //   ->  the next layer's NORM1 of the same row block.
 // After the last layer: NORMF per sequence (its last prompt row), the LM-head
 // tiles, and one ARGMAX tile.  Counter groups are per row block (per
@@ -56,10 +56,10 @@ std::string check_prefill_shape(const wpk_model_desc& d, int32_t batch, int32_t 
   s.G = s.Hq / s.Hkv;
   if (s.G > kMaxGroupHeads) return "at most 4 q heads per kv head";
   if (s.Hq * s.D != s.H) return "n_q_heads * head_dim must equal hidden";
-  if (s.H % kPCols || s.H > 4096) return "hidden must be a multiple of 128, at most 4096";
-  if (s.F % kPCols) return "ffn must be a multiple of 128";
+  if (s.H % kPCols || s.H > 4096) return "hidden must be a multiple of 256, at most 4096";
+  if (s.F % kPFfnCols) return "ffn must be a multiple of 128";
   s.qkv_rows = (s.Hq + 2 * s.Hkv) * s.D;
-  if (s.qkv_rows % kPCols) return "n_q_heads + 2 n_kv_heads must be even (QKV tiles hold two heads)";
+  if (s.qkv_rows % kPCols) return "n_q_heads + 2 n_kv_heads must be a multiple of 4 (QKV tiles hold four heads)";
   if (batch < 1 || batch > kMaxBatch) return "batch must be in [1, 32]";
   if (ctx_len < 1) return "ctx_len must be positive";
   if (prompt_len < 1 || prompt_len > ctx_len) return "prompt_len must be in [1, ctx_len]";

@@ -149,8 +149,8 @@ wpk_prefill_plan* build(const wpk_model_desc* desc, int32_t batch, int32_t ctx_l
   if (o.mode < WPK_PREFILL_MEGAKERNEL || o.mode > WPK_PREFILL_GRAPH) return pfail("unknown prefill mode");
   if (o.split_workers < 0) return pfail("split_workers must be >= 0");
   if (o.split_workers && o.mode != WPK_PREFILL_SPLIT) return pfail("split_workers applies to the split mode only");
-  const int wpc = o.workers_per_cu ? o.workers_per_cu : 2;
-  if (wpc < 1 || wpc > 2) return pfail("workers_per_cu must be 1 or 2");
+  const int wpc = o.workers_per_cu ? o.workers_per_cu : 1;
+  if (wpc != 1) return pfail("workers_per_cu must be 1: a prefill worker is eight waves and fills a compute unit");
   PShape s;
   why = check_prefill_shape(*desc, batch, ctx_len, prompt_len, o.mode == WPK_PREFILL_SPLIT, &s);
   if (!why.empty()) return pfail(why);

@@ -7,8 +7,8 @@
 // LM head on each sequence's last prompt position gives the first generated
 // token.  The prefill is lowered to a tile DAG like the decode step (counter
 // groups, claim queues in topological order), with tiles sized for a
-// compute-bound workload: 128 prompt rows x 128 output columns x all of K per
-// matrix-core tile, 32 queries x one kv head per attention tile.
+// compute-bound workload: 128 prompt rows x 256 output columns x all of K per
+// matrix-core tile, 64 queries x one kv head per attention tile.
 #pragma once
 #include <stdint.h>
 
@@ -19,14 +19,14 @@ namespace wpk {
 enum PrefillTileType : int32_t {
   P_EMBED = 0,   // layer 0: embedding rows of a row block -> residual stream, and their RMSNorm -> operand
   P_NORM1 = 1,   // attention-input RMSNorm of a row block (layers above 0)
-  P_QKV = 2,     // QKV for (row block, two heads): RoPE, queries out, K/V appended to the cache
-  P_ATTN = 3,    // causal attention for (sequence, kv head, 32-query block), the kv head's q heads together
-  P_OPROJ = 4,   // o-projection + residual for (row block, 128 columns)
+  P_QKV = 2,     // QKV for (row block, four heads): RoPE, queries out, K/V appended to the cache
+  P_ATTN = 3,    // causal attention for (sequence, kv head, 64-query block), the kv head's q heads together
+  P_OPROJ = 4,   // o-projection + residual for (row block, 256 columns)
   P_NORM2 = 5,   // MLP-input RMSNorm of a row block
-  P_GATEUP = 6,  // gate and up for (row block, 64 ffn columns) + SwiGLU
-  P_DOWN = 7,    // down projection + residual for (row block, 128 columns)
+  P_GATEUP = 6,  // gate and up for (row block, 128 ffn columns) + SwiGLU
+  P_DOWN = 7,    // down projection + residual for (row block, 256 columns)
   P_NORMF = 8,   // final RMSNorm of one sequence's last prompt row
-  P_LM = 9,      // tied LM head on the last rows, 128 vocabulary columns, partial argmax
+  P_LM = 9,      // tied LM head on the last rows, 256 vocabulary columns, partial argmax
   P_ARGMAX = 10, // the first generated token of every sequence, seq_len = prompt length
   P_NTYPES = 11
 };
@@ -34,15 +34,16 @@ enum PrefillTileType : int32_t {
 // Tile fields (the 64-byte Tile of plan.h): type, layer, wait, signal, shard,
 // id as in the decode step; r0 = row block (b * blocks per sequence + j),
 // r1 = column block (norm tiles: which 16 rows of the row block), b =
-// sequence, g = kv head, c = 32-query block.
+// sequence, g = kv head, c = 64-query block.
 
 constexpr int kPRows = 128;     // prompt rows of a row block (a matrix-core tile, a norm tile)
-constexpr int kPCols = 128;     // output columns of a QKV / o / down tile (two heads)
-constexpr int kPFfnCols = 64;   // SwiGLU columns of a gate/up tile (64 gate + 64 up weight rows)
-constexpr int kPQueries = 32;   // queries of an attention tile
+constexpr int kPCols = 256;     // output columns of a QKV / o / down tile (four heads)
+constexpr int kPFfnCols = 128;  // SwiGLU columns of a gate/up tile (128 gate + 128 up weight rows)
+constexpr int kPQueries = 64;   // queries of an attention tile (32 per wave, two waves per q head)
 constexpr int kPKeys = 32;      // keys per attention step
-constexpr int kPLmCols = 128;   // vocabulary columns of an LM-head tile
-constexpr int kPThreads = 256;  // four waves per worker, all computing
+constexpr int kPLmCols = 256;   // vocabulary columns of an LM-head tile
+constexpr int kPThreads = 512;  // eight waves per worker (one worker per CU), all computing
+constexpr int kPWaves = kPThreads / 64;
 constexpr int kPNormSplit = kPRows / 16;  // norm tiles per row block (16 rows each)
 
 // Per-layer device pointers.  Every activation buffer is per layer and

@@ -5,7 +5,7 @@ abstract and Table I) applied to the prefill workload of its Table III
 Llama 3.2 1B row.
 
 Candidate designs: one megakernel, two co-resident megakernels with the
-attention tiles in a pool of 64, 128 or 256 of the workers, and the
+attention tiles in a pool of 32, 64 or 128 of the workers, and the
 conventional one kernel per (layer, operator) in a hipGraph.
 
 Profiles (GPU): one logged megakernel prefill of the workload; each tile
@@ -33,7 +33,7 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, os.path.dirname(HERE))
 
-DESIGNS = ("megakernel", "split_64", "split_128", "split_256", "conventional")
+DESIGNS = ("megakernel", "split_32", "split_64", "split_128", "conventional")
 LAUNCH_GAP_US = 2.0  # between two graph-replayed kernels (the decode baseline's fit is of this order)
 
 

@@ -28,13 +28,13 @@ def _host(cfg, batch, cap, prompt, mode=0, split_workers=0):
 
 def _expected_counts(cfg, batch, prompt):
     nrb = batch * math.ceil(prompt / 128)
-    nqb = math.ceil(prompt / 32)
+    nqb = math.ceil(prompt / 64)
     L = cfg.n_layers
     return {
-        "embed": 8 * nrb, "norm1": 8 * (L - 1) * nrb, "qkv": L * nrb * cfg.qkv_rows // 128,
-        "attn": L * batch * nqb * cfg.n_kv_heads, "oproj": L * nrb * cfg.hidden // 128, "norm2": 8 * L * nrb,
-        "gateup": L * nrb * cfg.ffn // 64, "down": L * nrb * cfg.hidden // 128, "normf": batch,
-        "lm": math.ceil(cfg.vocab / 128), "argmax": 1,
+        "embed": 8 * nrb, "norm1": 8 * (L - 1) * nrb, "qkv": L * nrb * cfg.qkv_rows // 256,
+        "attn": L * batch * nqb * cfg.n_kv_heads, "oproj": L * nrb * cfg.hidden // 256, "norm2": 8 * L * nrb,
+        "gateup": L * nrb * cfg.ffn // 128, "down": L * nrb * cfg.hidden // 256, "normf": batch,
+        "lm": math.ceil(cfg.vocab / 256), "argmax": 1,
     }
 
 
@@ -75,8 +75,11 @@ def test_prefill_dag_shape_and_order(cfg, batch, prompt):
         assert info.rows_per_sequence == 128 * math.ceil(prompt / 128)
         _replay(ty, wait, signal)
         # claim queues: each in claim order; row-block tiles of one row block share a queue
+        # (small prompts may leave some of the eight queues empty: their workers exit at once)
         q = np.asarray(queue)
-        assert q.min() == 0 and q.max() == info.n_queues - 1 == 7
+        assert q.min() == 0 and q.max() < info.n_queues == 8
+        if batch * math.ceil(prompt / 128) >= 8:
+            assert len(set(q.tolist())) == 8
         # phases of the per-operator baseline: one per (layer, type) run
         runs = 1 + int(np.sum((np.diff(ty) != 0) | (np.diff(layer) != 0)))
         assert info.n_phases == runs == 7 * cfg.n_layers + 3
@@ -105,9 +108,9 @@ def test_prefill_dag_edges_follow_row_blocks():
             if signal[u] >= 0:
                 prod.setdefault(int(signal[u]), []).append(u)
         nrb_s = 2
-        per = {"qkv": 8, "attn": nrb_s * cfg.qkv_rows // 128, "norm2": cfg.hidden // 128,
-               "gateup": 8, "down": cfg.ffn // 64, "norm1": cfg.hidden // 128, "lm": batch,
-               "argmax": math.ceil(cfg.vocab / 128), "normf": cfg.hidden // 128}
+        per = {"qkv": 8, "attn": nrb_s * cfg.qkv_rows // 256, "norm2": cfg.hidden // 256,
+               "gateup": 8, "down": cfg.ffn // 128, "norm1": cfg.hidden // 256, "lm": batch,
+               "argmax": math.ceil(cfg.vocab / 256), "normf": cfg.hidden // 256}
         src = {"qkv": ("embed", "norm1"), "attn": ("qkv",), "oproj": ("attn",), "norm2": ("oproj",),
                "gateup": ("norm2",), "down": ("gateup",), "norm1": ("down",), "normf": ("down",), "lm": ("normf",),
                "argmax": ("lm",)}
@@ -121,8 +124,8 @@ def test_prefill_dag_edges_follow_row_blocks():
             assert max(ps) < v
             if name in per:
                 assert len(ps) == per[name], (v, name, len(ps))
-            else:  # oproj: the attention tiles of the row block (4 query blocks x kv heads, fewer if ragged)
-                assert len(ps) in tuple(k * cfg.n_kv_heads for k in (1, 2, 3, 4))
+            else:  # oproj: the attention tiles of the row block (2 query blocks x kv heads, 1 if ragged)
+                assert len(ps) in tuple(k * cfg.n_kv_heads for k in (1, 2))
             lay = {"norm1": -1}.get(name, 0)
             if name not in ("lm", "argmax", "normf"):
                 assert all(layer[p] == layer[v] + lay for p in ps)

@@ -765,6 +765,116 @@ __device__ __forceinline__ void attn_run_store(const Params& P, const Tile& T, c
 #define WPK_ATTN_GROUP 1
 #endif
 
+// Attention partial of a bf16 KV chunk on the matrix cores
+// (v_mfma_f32_16x16x32_bf16), the kv head's q heads as the columns:
+//  * scores S^T = K Q^T: A = K rows from LDS (lane l: position l % 16 of a
+//    16-position block, dims 8 (l / 16) + 32 s ..), B = the queries scaled
+//    by 1/sqrt(D) as hi + lo bf16 parts (lane l: q head l % 16, zero past the
+//    group; K is bf16 and exact, so the two products keep ~16 bits of q).
+//    Every compute wave computes all 64 positions (16 products): lane l then
+//    holds positions 16 kb + 4 (l / 16) + e of head l % 16, and the softmax
+//    over the chunk (positions past its count masked) needs only exchanges
+//    between the four lanes of a head.
+//  * weighted values O^T = V^T P^T: wave w takes head dims 16 w .. +15; A =
+//    the transposed V rows from LDS, B = the lane's own probabilities as hi +
+//    lo bf16, both in the K order 8 (l / 16) + 4 j + e <-> position
+//    32 t + 16 j + 4 (l / 16) + e of 32-position step t.  V values of
+//    positions past the count are zeroed (the cache holds anything there).
+// Lane l ends with dims 16 w + 4 (l / 16) + e of head l % 16.
+// Used by the matrix-core plans (batch 5-32).  Measured at batch 32: the
+// pass's arithmetic fell from ~1.4 us on the vector units to ~0.3 us, the step
+// by ~1% (2216 -> 2194 us): an attention tile's time is its K/V chunks
+// streaming in (~7.6 us from its start to its inputs being staged), not its
+// arithmetic.  Narrow plans keep the vector-unit pass below: in their
+// 128-register budget, next to the 64-register slot, this one spilled and the
+// batch-1 step was ~1% slower.
+template <typename WT, int KMAX>
+__device__ __forceinline__ void cmp_attn_mx(const Params& P, const Tile& T, Smem<WT, KMAX>& sm, int tc0) {
+  static_assert(sizeof(WT) == 2 && kHeadDim == 64 && kAttnChunk == 64 && kWaves == 4, "bf16, 64 dims, 64 positions");
+  constexpr int KP = WT_<WT>::KP;
+  const int tc = opaque(tc0);
+  const int lane = tc & 63, w = __builtin_amdgcn_readfirstlane(tc >> 6);
+  const int cnt = attn_count(P, T, sm.pos[T.b]);
+  if (cnt == 0) return;
+  const int l15 = lane & 15, g4 = lane >> 4;
+  const bool live = l15 < P.G;
+  bf16x8 qh[2], ql[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const float* qr = &sm.qs[live ? l15 : 0][32 * s + 8 * g4];
+    const float sc = live ? P.attn_scale : 0.f;
+    const f32x4 a = *(const f32x4*)qr * sc, b = *(const f32x4*)(qr + 4) * sc;
+    uint32_t h[4], l[4];
+    split_hilo2(a[0], a[1], h[0], l[0]);
+    split_hilo2(a[2], a[3], h[1], l[1]);
+    split_hilo2(b[0], b[1], h[2], l[2]);
+    split_hilo2(b[2], b[3], h[3], l[3]);
+    qh[s] = __builtin_bit_cast(bf16x8, u32x4{h[0], h[1], h[2], h[3]});
+    ql[s] = __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], l[2], l[3]});
+  }
+  const uint16_t* ks = (const uint16_t*)sm.ks;
+  f32x4 st[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const uint16_t* kr = ks + (16 * kb + l15) * KP + 8 * g4;
+    const bf16x8 k0 = *(const bf16x8*)kr, k1 = *(const bf16x8*)(kr + 32);
+    f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qh[0], z, 0, 0, 0);
+    z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, ql[0], z, 0, 0, 0);
+    z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qh[1], z, 0, 0, 0);
+    z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, ql[1], z, 0, 0, 0);
+    st[kb] = z;
+  }
+  float m = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float v = 16 * kb + 4 * g4 + e < cnt ? st[kb][e] : -INFINITY;
+      st[kb][e] = v;
+      m = fmaxf(m, v);
+    }
+  m = xmax<32>(xmax<16>(m));
+  float l = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) st[kb][e] = __expf(st[kb][e] - m);
+    l += (st[kb][0] + st[kb][1]) + (st[kb][2] + st[kb][3]);
+  }
+  l = xsum<32>(xsum<16>(l));
+  const uint16_t* vr = (const uint16_t*)sm.vt + (16 * w + l15) * KP + 4 * g4;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    uint32_t ph[4], pl[4], vv[4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const f32x4 pr = st[2 * t + j];
+      split_hilo2(pr[0], pr[1], ph[2 * j], pl[2 * j]);
+      split_hilo2(pr[2], pr[3], ph[2 * j + 1], pl[2 * j + 1]);
+      const int p0 = 32 * t + 16 * j + 4 * g4;  // positions p0 .. p0 + 3
+      const u32x2 v = *(const u32x2*)(vr + 32 * t + 16 * j);
+      vv[2 * j] = p0 + 1 < cnt ? v.x : p0 < cnt ? (v.x & 0xFFFFu) : 0u;
+      vv[2 * j + 1] = p0 + 3 < cnt ? v.y : p0 + 2 < cnt ? (v.y & 0xFFFFu) : 0u;
+    }
+    const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{vv[0], vv[1], vv[2], vv[3]});
+    o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, __builtin_bit_cast(bf16x8, u32x4{ph[0], ph[1], ph[2], ph[3]}), o,
+                                                0, 0, 0);
+    o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, __builtin_bit_cast(bf16x8, u32x4{pl[0], pl[1], pl[2], pl[3]}), o,
+                                                0, 0, 0);
+  }
+  if (live) {
+    float* out = &sm.outs[l15][2 + 16 * w + 4 * g4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[e] = o[e];
+    if (w == 0 && g4 == 0) {
+      sm.outs[l15][0] = m;
+      sm.outs[l15][1] = l;
+    }
+  }
+}
+
 // Attention partial: compute wave h = q head h of the group, lane = position
 // (scores) then lane = head dimension (weighted values).  Both loops are
 // unrolled so that the LDS reads of a row are in flight together.
@@ -1094,7 +1204,10 @@ __device__ __forceinline__ void compute(const Params& P, const Tile& T, const Sl
       case T_DOWN:
       case T_LM: cmp_wide<WT>(P, s, sm, tc); break;
       case T_ATTN:
-      case T_ATTNC: cmp_attn<WT>(P, T, sm, tc); break;
+      case T_ATTNC:
+        if constexpr (sizeof(WT) == 2) cmp_attn_mx<WT>(P, T, sm, tc);
+        else cmp_attn<WT>(P, T, sm, tc);
+        break;
       case T_COMBINE: cmp_combine<WT, true>(P, T, sm, tc); break;
       default: break;  // norm and argmax tiles are control-wave work
     }

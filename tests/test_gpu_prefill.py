@@ -28,7 +28,7 @@ pytestmark = pytest.mark.gpu
 
 
 class Prefill:
-    def __init__(self, cfg, w, batch, cap, prompt_len, mode=0, split_workers=0, desc=None):
+    def __init__(self, cfg, w, batch, cap, prompt_len, mode=0, split_workers=0, desc=None, fill=0):
         self.cfg = cfg
         if desc is None:
             desc, self.tensors = wpk.model_from_weights(cfg, w, "cuda")
@@ -38,8 +38,8 @@ class Prefill:
         assert self.plan, wpk.wpk_prefill_last_error(None)
         self.info = wpk.wpk_prefill_get_info(self.plan)
         shape = (cfg.n_layers, batch, cfg.n_kv_heads, cap, cfg.head_dim)
-        self.kc = torch.zeros(shape, dtype=torch.int16, device="cuda")
-        self.vc = torch.zeros(shape, dtype=torch.int16, device="cuda")
+        self.kc = torch.full(shape, fill, dtype=torch.int16, device="cuda")
+        self.vc = torch.full(shape, fill, dtype=torch.int16, device="cuda")
         self.seq = torch.full((batch,), -5, dtype=torch.int32, device="cuda")
         self.logits = torch.zeros((batch, cfg.vocab), dtype=torch.float32, device="cuda")
         self.tok = torch.full((batch,), -1, dtype=torch.int32, device="cuda")
@@ -71,7 +71,9 @@ def _bf16(a):
     return (a.astype(np.uint32) << 16).view(np.float32)
 
 
-def _compare(cfg, w, batch, cap, prompt_len, seed, log=True, kv_tol=3e-2):
+def _compare(cfg, w, batch, cap, prompt_len, seed, log=True, kv_tol=3e-2, fill=0):
+    """fill: the cache's initial 16-bit pattern (0, or a NaN whose rows past
+    the prompt must come back unchanged)."""
     prompt = synth.prompt_tokens(cfg, batch, prompt_len, seed=seed)
     model = oracle.Model(cfg, w)
     okc, ovc = model.new_cache(batch, cap)
@@ -79,7 +81,7 @@ def _compare(cfg, w, batch, cap, prompt_len, seed, log=True, kv_tol=3e-2):
     announce(f"prefill {cfg.name} b{batch} P{prompt_len}: oracle")
     olog, otok = model.prefill(prompt, okc, ovc, osl)
     announce(f"prefill {cfg.name} b{batch} P{prompt_len}: build")
-    g = Prefill(cfg, w, batch, cap, prompt_len)
+    g = Prefill(cfg, w, batch, cap, prompt_len, fill=fill)
     try:
         if log:
             wpk.check_prefill(wpk.wpk_prefill_set_option(g.plan, wpk.WPK_OPT_LOG, 1), g.plan)
@@ -98,7 +100,7 @@ def _compare(cfg, w, batch, cap, prompt_len, seed, log=True, kv_tol=3e-2):
             assert float(d.max()) <= kv_tol, f"{name} cache: max |err| {float(d.max())}"
             assert float(d.mean()) <= kv_tol / 10, f"{name} cache: mean |err| {float(d.mean())}"
             # positions past the prompt untouched
-            assert not np.any(got[:, :, :, prompt_len:]), f"{name} cache written past the prompt"
+            assert np.all(got[:, :, :, prompt_len:] == np.uint16(fill & 0xFFFF)), f"{name} cache written past the prompt"
         if log:
             ty, layer, wait, signal, queue = g.dag()
             check_log(g.log(), wait, signal)
@@ -114,6 +116,15 @@ def test_mini_prefill_matches_oracle(batch, prompt_len, cap):
     cfg = synth.MINI
     w = synth.make_weights(cfg, gain_std=0.1)
     _compare(cfg, w, batch, cap, prompt_len, seed=7 + prompt_len)
+
+
+def test_mini_prefill_over_a_nan_filled_cache():
+    """The cache starts as NaN bit patterns: the prefill reads no cache row it
+    has not written (attention keys stay inside the prompt), so logits and
+    tokens match the oracle and rows past the prompt keep their bits."""
+    cfg = synth.MINI
+    w = synth.make_weights(cfg, gain_std=0.1)
+    _compare(cfg, w, 3, 200, 150, seed=41, fill=0x7FC0)
 
 
 def test_llama_prefill_short_prompt_matches_oracle():

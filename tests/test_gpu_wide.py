@@ -129,3 +129,58 @@ def test_llama_1b_batch32_all_sequences():
         tok = otok
     print(f"llama-1b b32 max logit error {worst:.3g}, near ties {ties}")
     g.close()
+
+
+@pytest.mark.parametrize("batch", [3, 8])
+def test_cache_garbage_past_each_sequence_is_never_read(batch):
+    """Cache rows at and past each sequence's length hold NaN (K) and
+    alternating +Inf / NaN (V) bit patterns -- a caller's cache may hold
+    anything there.  Attention must mask them (scores by selection, V values
+    of masked positions zeroed before the weighted sum: 0 * NaN would poison
+    it), so logits and tokens match the oracle, which reads only positions
+    0..p; rows past the appended ones keep their bits.  Batch 3 runs the
+    vector-unit attention pass, batch 8 the matrix-core one."""
+    cfg = synth.MINI
+    w = synth.make_weights(cfg, gain_std=0.1)
+    cap, steps = 200, 3
+    rng = np.random.default_rng(29)
+    lens = rng.integers(1, cap - 8, size=batch).astype(np.int32)
+    lens[0], lens[1] = 63, -1  # a chunk edge and an inactive slot
+    kc, vc = synth.synthetic_kv(cfg, batch, cap, np.maximum(lens, 0))
+    pos = np.arange(cap)[None, None, :, None]
+    past = pos >= np.maximum(lens, 0).reshape(1, batch, 1, 1, 1)
+    nan, inf = np.uint16(0x7FC0), np.uint16(0x7F80)
+    kc = np.where(past, nan, kc)
+    vmask = np.where((np.arange(cfg.head_dim) % 2 == 0)[None, None, None, None, :], inf, nan)
+    vc = np.where(past, vmask, vc)
+    tok = rng.integers(0, cfg.vocab, size=batch).astype(np.int32)
+    model = oracle.Model(cfg, w)
+    announce(f"cache garbage b{batch} build")
+    g = GpuPlan(cfg, w, batch, cap, kc, vc, lens, tok)
+    wpk.check(wpk.wpk_set_option(g.plan, wpk.WPK_OPT_LOG, 1), g.plan)
+    ty, layer, wait, signal = g.dag()
+    k_in, v_in = kc.copy(), vc.copy()
+    osl = lens.copy()
+    for s in range(steps):
+        announce(f"cache garbage b{batch} step {s}")
+        g.set_tokens(tok)
+        g.step()
+        _, _, gsl, gtok, glog = g.state()
+        olog, otok = model.step(tok, kc, vc, osl)
+        assert np.array_equal(gsl, osl)
+        for b in range(batch):
+            if lens[b] < 0:
+                continue
+            assert np.all(np.isfinite(glog[b])), f"step {s} seq {b}: non-finite logits"
+            err = float(np.max(np.abs(glog[b] - olog[b])))
+            assert err <= 2e-2, f"step {s} seq {b}: max |logit err| {err}"
+            ok, why = tokens_agree(int(gtok[b]), int(otok[b]), olog[b], err)
+            assert ok, f"step {s} seq {b}: {why}"
+        check_log(g.log(), wait, signal)
+        tok = otok
+    gk, gv, _, _, _ = g.state()
+    for b in range(batch):
+        n = max(int(lens[b]), 0) + (steps if lens[b] >= 0 else 0)
+        assert np.array_equal(gk[:, b, :, n:], k_in[:, b, :, n:]), f"seq {b}: K rows past the sequence changed"
+        assert np.array_equal(gv[:, b, :, n:], v_in[:, b, :, n:]), f"seq {b}: V rows past the sequence changed"
+    g.close()

@@ -62,6 +62,7 @@ extern "C" {
 #define WPK_E_STATE (-8)        /* plan holds a latched device error; reset it */
 #define WPK_E_NO_GPU (-9)       /* no usable gfx950 device */
 #define WPK_E_IDLE (-10)        /* a persistent grid waited longer than its idle limit for a step and left */
+#define WPK_E_RANGE (-11)       /* a prefill activation of the fp16 products overflowed |x| >= 65520 (device) */
 
 /* ---- data types --------------------------------------------------------------- */
 #define WPK_F32 0               /* float32 weights and KV cache */
@@ -401,13 +402,18 @@ int32_t wpk_debug_read_act(wpk_plan* plan, void* host_dst, size_t bytes, size_t*
  * grouped-query attention over the prompt, o-projection, SwiGLU MLP -- and
  * the tied LM head on each sequence's last prompt position gives the first
  * generated token (greedy, lowest index on ties).  Matrix products run on the
- * matrix cores in bf16 with fp32 accumulation: activations, queries and
- * attention probabilities are rounded to bf16 at each product's input; the
- * residual stream, RMSNorm, RoPE and softmax run in fp32.
+ * matrix cores with fp32 accumulation.  QKV, the attention products and the
+ * LM head take bf16 weights (or K/V) against activations split into bf16 hi +
+ * lo parts (two products, ~16 significant bits); the o-projection, gate/up
+ * and down take fp16 copies of their weights against fp16 activations (one
+ * product, 11 bits).  The residual stream, RMSNorm, RoPE and softmax run in
+ * fp32.  An activation entering an fp16 product that overflows (|x| >=
+ * 65520) latches WPK_E_RANGE.
  *
  * wpk_build_prefill: model (DEVICE pointers, bf16 weights, hidden a multiple
- *   of 128 up to 4096, ffn a multiple of 128, n_q_heads + 2 n_kv_heads even),
- *   batch in [1, 32],
+ *   of 256 up to 4096, ffn a multiple of 128, n_q_heads + 2 n_kv_heads a
+ *   multiple of 4; o-proj, gate, up and down weights inside the fp16 range,
+ *   |w| < 65520), batch in [1, 32],
  *   ctx_len (the KV cache capacity), prompt_len in [1, ctx_len].  opts (NULL:
  *   defaults) picks the execution:
  *     WPK_PREFILL_MEGAKERNEL: one persistent kernel, all tiles;
@@ -437,9 +443,10 @@ int32_t wpk_debug_read_act(wpk_plan* plan, void* host_dst, size_t bytes, size_t*
  *   queue.  Arrays of n_tiles.
  * Ownership and errors as for the decode step, except that a prefill plan
  * copies the layer matrices at build, repacked into the fragment-major
- * layout its matrix-core tiles load (about the size of the layer weights;
- * the embedding is still read from the caller's table): weights changed
- * after the build are not seen by the prefill. */
+ * layout its matrix-core tiles load (QKV in bf16, the others in fp16; about
+ * the size of the layer weights; the embedding is still read from the
+ * caller's table): weights changed after the build are not seen by the
+ * prefill. */
 #define WPK_PREFILL_MEGAKERNEL 0
 #define WPK_PREFILL_SPLIT 1
 #define WPK_PREFILL_GRAPH 2

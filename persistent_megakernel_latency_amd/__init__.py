@@ -28,6 +28,7 @@ WPK_E_TOKEN = -7
 WPK_E_STATE = -8
 WPK_E_NO_GPU = -9
 WPK_E_IDLE = -10
+WPK_E_RANGE = -11
 
 WPK_F32 = 0
 WPK_BF16 = 1

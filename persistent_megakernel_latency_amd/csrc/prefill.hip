@@ -127,6 +127,30 @@ __device__ __forceinline__ bf16x8 hilo8(f32x4 a, f32x4 b, bf16x8& lo) {
   return as_bf16x8(u32x4{h[0], h[1], h[2], h[3]});
 }
 
+// fp16 operands (the o-projection, gate/up and down products): one plane,
+// one product per fragment.
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
+__device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+// two floats as fp16 (round to nearest even), a in the low half; over is set
+// if a finite value is beyond the fp16 range (it would round to infinity)
+__device__ __forceinline__ uint32_t cvt_f16x2(float a, float b, bool& over) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  over |= (fabsf(a) >= 65520.f) | (fabsf(b) >= 65520.f);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, f16x2));
+}
+// Four fp32 values as fp16, 8 bytes into an operand plane.
+__device__ __forceinline__ void st_f16x4(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v, bool& over) {
+  st8(r, off, u32x2{cvt_f16x2(v[0], v[1], over), cvt_f16x2(v[2], v[3], over)});
+}
+// A wave that saw an fp16 overflow latches WPK_E_RANGE.
+__device__ __forceinline__ void range_check(const PParams& P, const Tile& T, bool over, int lane) {
+  if (__builtin_amdgcn_ballot_w64(over) != 0 && lane == 0) p_latch(P, WPK_E_RANGE, T.id);
+}
+
 // Fragment-major ("packed") layout of a bf16 matrix-core operand with K
 // columns: blocks of 16 rows x 32 columns, one 1 KiB block per (16 rows,
 // k-step) in row-block-major order, and inside a block lane l's 16 bytes at
@@ -142,7 +166,8 @@ __device__ __forceinline__ uint32_t pk(uint32_t r, uint32_t k, uint32_t K) {
 
 // ---- RMSNorm of rows -------------------------------------------------------------------------
 // y = x / sqrt(mean(x^2) + eps) * gain, stored as the hi and lo bf16 planes
-// of the packed matrix-core operand.  A norm tile takes 16 rows; wave w takes
+// of the packed matrix-core operand (F16: one fp16 plane).  Returns whether a
+// value overflowed fp16.  A norm tile takes 16 rows; wave w takes
 // an eighth of the columns in the fragment layout (lane l: row l % 16,
 // columns 8 (l / 16) .. +7 of each 32-column k-step), so every store is one
 // contiguous KiB per wave and all of a wave's loads of a pass are in flight
@@ -151,8 +176,8 @@ __device__ __forceinline__ uint32_t pk(uint32_t r, uint32_t k, uint32_t K) {
 // LDS.  Second pass: the rows are read again (from the
 // cache), scaled and stored.  src(r, k, a, b) gives 8 fp32 values of row r
 // from column k.
-template <typename SRC>
-__device__ __forceinline__ void norm_rows16(const PParams& P, int r0, const SRC& src, const float* gain,
+template <bool F16, typename SRC>
+__device__ __forceinline__ bool norm_rows16(const PParams& P, int r0, const SRC& src, const float* gain,
                                             __amdgpu_buffer_rsrc_t yh, __amdgpu_buffer_rsrc_t yl,
                                             __amdgpu_buffer_rsrc_t xc, bool copy, PSmem& sm, int w, int lane) {
   const int r = r0 + (lane & 15), c8 = 8 * (lane >> 4), nks = P.H / 32, q = nks / kPWaves, k0 = w * q;
@@ -173,6 +198,7 @@ __device__ __forceinline__ void norm_rows16(const PParams& P, int r0, const SRC&
                     ((sm.nss[4][rr] + sm.nss[5][rr]) + (sm.nss[6][rr] + sm.nss[7][rr]));
   const float inv = 1.0f / sqrtf(tot / (float)P.H + P.eps);
   const uint32_t blk = (uint32_t)(r0 >> 4) * (uint32_t)nks * 1024u + (uint32_t)lane * 16u;
+  bool over = false;
 #pragma unroll 16
   for (int ks = k0; ks < k0 + q; ++ks) {
     const int k = 32 * ks + c8;
@@ -186,14 +212,21 @@ __device__ __forceinline__ void norm_rows16(const PParams& P, int r0, const SRC&
     const f32x4 ga = *(const f32x4*)(gain + k), gb = *(const f32x4*)(gain + k + 4);
     a = a * inv * ga;
     b = b * inv * gb;
-    uint32_t h[4], l[4];
-    split_hilo2(a[0], a[1], h[0], l[0]);
-    split_hilo2(a[2], a[3], h[1], l[1]);
-    split_hilo2(b[0], b[1], h[2], l[2]);
-    split_hilo2(b[2], b[3], h[3], l[3]);
-    st16(yh, blk + (uint32_t)ks * 1024u, u32x4{h[0], h[1], h[2], h[3]});
-    st16(yl, blk + (uint32_t)ks * 1024u, u32x4{l[0], l[1], l[2], l[3]});
+    if (F16) {
+      st16(yh, blk + (uint32_t)ks * 1024u,
+           u32x4{cvt_f16x2(a[0], a[1], over), cvt_f16x2(a[2], a[3], over), cvt_f16x2(b[0], b[1], over),
+                 cvt_f16x2(b[2], b[3], over)});
+    } else {
+      uint32_t h[4], l[4];
+      split_hilo2(a[0], a[1], h[0], l[0]);
+      split_hilo2(a[2], a[3], h[1], l[1]);
+      split_hilo2(b[0], b[1], h[2], l[2]);
+      split_hilo2(b[2], b[3], h[3], l[3]);
+      st16(yh, blk + (uint32_t)ks * 1024u, u32x4{h[0], h[1], h[2], h[3]});
+      st16(yl, blk + (uint32_t)ks * 1024u, u32x4{l[0], l[1], l[2], l[3]});
+    }
   }
+  return over;
 }
 
 // A norm tile: rows 16 sub .. +15 of its row block.  Layer 0 gathers the
@@ -223,7 +256,7 @@ __device__ void norm_tile(const PParams& P, const Tile& T, PSmem& sm, int tid) {
       a = pad ? f32x4{0.f, 0.f, 0.f, 0.f} : f32x4{bf16_lo(e.x), bf16_hi(e.x), bf16_lo(e.y), bf16_hi(e.y)};
       bb = pad ? f32x4{0.f, 0.f, 0.f, 0.f} : f32x4{bf16_lo(e.z), bf16_hi(e.z), bf16_lo(e.w), bf16_hi(e.w)};
     };
-    norm_rows16(P, r0, src, Lw.attn_norm, yh, yl, xc, true, sm, w, lane);
+    norm_rows16<false>(P, r0, src, Lw.attn_norm, yh, yl, xc, true, sm, w, lane);
   } else {
     const float* x = T.type == P_NORM1 ? Lw.x_in : Lw.x_mid;
     auto src = [&](int r, int k, f32x4& a, f32x4& bb) {
@@ -231,7 +264,12 @@ __device__ void norm_tile(const PParams& P, const Tile& T, PSmem& sm, int tid) {
       a = *(const f32x4*)xr;
       bb = *(const f32x4*)(xr + 4);
     };
-    norm_rows16(P, r0, src, T.type == P_NORM1 ? Lw.attn_norm : Lw.mlp_norm, yh, yl, xc, false, sm, w, lane);
+    if (T.type == P_NORM1) {
+      norm_rows16<false>(P, r0, src, Lw.attn_norm, yh, yl, xc, false, sm, w, lane);
+    } else {  // the gate/up operand: fp16
+      const bool over = norm_rows16<true>(P, r0, src, Lw.mlp_norm, yh, yl, xc, false, sm, w, lane);
+      range_check(P, T, over, lane);
+    }
   }
 }
 
@@ -287,6 +325,10 @@ __device__ void normf_tile(const PParams& P, const Tile& T, int tid) {
 // ds_write cost a k-step about 0.75 us against 0.54 us this way (measured,
 // 8 waves per CU, products included), LDS writes being the slow half of the
 // LDS's bandwidth.
+// F16 (o-projection, gate/up, down): fp16 weights against one fp16 operand
+// plane -- 24 blocks per k-step (16 weight, 8 operand), each wave fetching
+// weight blocks 2w, 2w+1 and operand block w, and 16 products per wave.
+template <bool F16>
 __device__ void gemm_tile(const PParams& P, const Tile& T0, PSmem& sm, int tid) {
   const Tile T = uni(T0);
   const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -325,7 +367,7 @@ __device__ void gemm_tile(const PParams& P, const Tile& T0, PSmem& sm, int tid) 
     __builtin_amdgcn_raw_ptr_buffer_load_lds(gr[0], lds_ptr(&sm.gs[st][2 * w][0]), 16, gv[0], so, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(gr[1], lds_ptr(&sm.gs[st][2 * w + 1][0]), 16, gv[1], so, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, lds_ptr(&sm.gs[st][16 + w][0]), 16, gv[2], so, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, lds_ptr(&sm.gs[st][24 + w][0]), 16, gv[2], so, 0, 0);
+    if (!F16) __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, lds_ptr(&sm.gs[st][24 + w][0]), 16, gv[2], so, 0, 0);
   };
   f32x4 acc[4][4];
 #pragma unroll
@@ -343,11 +385,20 @@ __device__ void gemm_tile(const PParams& P, const Tile& T0, PSmem& sm, int tid) 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       f.a[i] = as_bf16x8(sm.gs[st][16 + 4 * wr + i][lane]);
-      f.al[i] = as_bf16x8(sm.gs[st][24 + 4 * wr + i][lane]);
+      if (!F16) f.al[i] = as_bf16x8(sm.gs[st][24 + 4 * wr + i][lane]);
     }
   };
-  // the hi products, then the lo products: no two consecutive products share an accumulator
+  // the hi products, then the lo products: no two consecutive products share
+  // an accumulator (fp16: the one product per pair)
   auto products = [&](const Frag& f) {
+    if (F16) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[j][i] = mfma16(__builtin_bit_cast(f16x8, f.b[j]), __builtin_bit_cast(f16x8, f.a[i]), acc[j][i]);
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -446,20 +497,22 @@ __device__ void gemm_tile(const PParams& P, const Tile& T0, PSmem& sm, int tid) 
       }
       break;
     }
-    default: {  // P_GATEUP: h = silu(gate) * up, blocks 0-1 gate and 2-3 up of the same columns
-      const __amdgpu_buffer_rsrc_t hh = urs(Lw.h), hl = urs(Lw.h + (size_t)P.R * P.F);
+    default: {  // P_GATEUP: h = silu(gate) * up, blocks 0-1 gate and 2-3 up of the same columns; the down operand (fp16)
+      const __amdgpu_buffer_rsrc_t hh = urs(Lw.h);
+      bool over = false;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t ro = (uint32_t)(row0 + 16 * i + (lane & 15)) * (uint32_t)P.F;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const f32x4 g = acc[j][i], u = acc[j + 2][i];
           f32x4 hv;
 #pragma unroll
           for (int e = 0; e < 4; ++e) hv[e] = g[e] / (1.0f + __expf(-g[e])) * u[e];
-          st_hilo4(hh, hl, pk((uint32_t)(row0 + 16 * i + (lane & 15)), (uint32_t)(wrow0 + 16 * j + e4), (uint32_t)P.F), hv);
+          st_f16x4(hh, pk((uint32_t)(row0 + 16 * i + (lane & 15)), (uint32_t)(wrow0 + 16 * j + e4), (uint32_t)P.F), hv,
+                   over);
         }
       }
+      range_check(P, T, over, lane);
       break;
     }
   }
@@ -624,7 +677,9 @@ __device__ void attn_tile(const PParams& P, const Tile& T0, PSmem& sm, int tid) 
       for (int s = 0; s < 2; ++s) kf[kb][s] = nkf[kb][s];
   }
   if (!active) return;
-  const __amdgpu_buffer_rsrc_t oh = urs(Lw.ao), ol = urs(Lw.ao + (size_t)P.R * P.Hq * kHeadDim);
+  // the o-projection's operand: one fp16 plane
+  const __amdgpu_buffer_rsrc_t oh = urs(Lw.ao);
+  bool over = false;
 #pragma unroll
   for (int i = 0; i < kPQB; ++i) {
     float lt = xsum<16>(lsum[i]);
@@ -634,9 +689,9 @@ __device__ void attn_tile(const PParams& P, const Tile& T0, PSmem& sm, int tid) 
     const float inv = 1.0f / lt;
     const uint32_t orow = (uint32_t)T.b * P.Pp + qpos, ocol = (uint32_t)h * kHeadDim + 4 * g4;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
-      st_hilo4(oh, ol, pk(orow, ocol + 16 * db, (uint32_t)(P.Hq * kHeadDim)), o[db][i] * inv);
+    for (int db = 0; db < 4; ++db) st_f16x4(oh, pk(orow, ocol + 16 * db, (uint32_t)(P.Hq * kHeadDim)), o[db][i] * inv, over);
   }
+  range_check(P, T, over, lane);
 }
 
 // ---- LM head on the last prompt rows: 256 vocabulary columns per tile ------------------------
@@ -722,10 +777,10 @@ __device__ __forceinline__ void run_tile(const PParams& P, const Tile& T, PSmem&
     case P_EMBED:
     case P_NORM1:
     case P_NORM2: norm_tile(P, T, sm, tid); break;
-    case P_QKV:
+    case P_QKV: gemm_tile<false>(P, T, sm, tid); break;
     case P_OPROJ:
     case P_GATEUP:
-    case P_DOWN: gemm_tile(P, T, sm, tid); break;
+    case P_DOWN: gemm_tile<true>(P, T, sm, tid); break;
     case P_ATTN: attn_tile(P, T, sm, tid); break;
     case P_NORMF: normf_tile(P, T, tid); break;
     case P_LM: lm_tile(P, T, tid); break;
@@ -811,22 +866,35 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2))) 
 namespace wpk {
 // Repacks a row-major bf16 matrix [rows][K] (rows a multiple of 16, K of 32)
 // into the packed fragment-major layout the matrix-core tiles load: one
-// thread per 16-byte chunk.
-__global__ __launch_bounds__(256) void prefill_pack(const uint16_t* src, uint16_t* dst, int rows, int K) {
+// thread per 16-byte chunk.  to_f16: the values converted to fp16 (exact for
+// bf16 magnitudes in [2^-14, 65504]; smaller ones become fp16 subnormals,
+// within 2^-25 of the value), and *flag set if one is beyond the fp16 range.
+__global__ __launch_bounds__(256) void prefill_pack(const uint16_t* src, uint16_t* dst, int rows, int K, int to_f16,
+                                                    int* flag) {
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   const size_t per_row = (size_t)K / 8;
   if (i >= (size_t)rows * per_row) return;
   const uint32_t r = (uint32_t)(i / per_row), k = (uint32_t)(i % per_row) * 8u;
-  *(u32x4*)((char*)dst + pk(r, k, (uint32_t)K)) = *(const u32x4*)(src + i * 8);
+  u32x4 v = *(const u32x4*)(src + i * 8);
+  if (to_f16) {
+    bool over = false;
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = cvt_f16x2(bf16_lo(w[e]), bf16_hi(w[e]), over);
+    v = u32x4{o[0], o[1], o[2], o[3]};
+    if (over) __hip_atomic_fetch_or(flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  *(u32x4*)((char*)dst + pk(r, k, (uint32_t)K)) = v;
 }
 }  // namespace wpk
 
 // Launches the repacking of one matrix on `stream` (asynchronous).
-extern "C" int wpk_dev_prefill_pack(const void* src, void* dst, int rows, int K, void* stream) {
+extern "C" int wpk_dev_prefill_pack(const void* src, void* dst, int rows, int K, int to_f16, int* flag, void* stream) {
   const size_t chunks = (size_t)rows * (size_t)K / 8;
   const unsigned grid = (unsigned)((chunks + 255) / 256);
   hipLaunchKernelGGL(wpk::prefill_pack, dim3(grid), dim3(256), 0, (hipStream_t)stream, (const uint16_t*)src,
-                     (uint16_t*)dst, rows, K);
+                     (uint16_t*)dst, rows, K, to_f16, flag);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -20,7 +20,7 @@
 #include "wpk.h"
 
 extern "C" int wpk_dev_prefill_kernels(const void** mk, const void** mk_log, const void** phase);
-extern "C" int wpk_dev_prefill_pack(const void* src, void* dst, int rows, int K, void* stream);
+extern "C" int wpk_dev_prefill_pack(const void* src, void* dst, int rows, int K, int to_f16, int* flag, void* stream);
 
 using namespace wpk;
 
@@ -91,7 +91,7 @@ bool desc_ok(const wpk_model_desc* d, std::string* why) {
 
 struct PLayout {
   int64_t ctl, heads, counters, argmax, tiles, qtiles, groups, queue_off, layers, rope_cos, rope_sin, x0, xf, act,
-      act_layer, log, wqueue, total;
+      act_layer, log, wqueue, pack_flag, total;
   // per-layer buffer offsets within act_layer bytes
   int64_t x_mid, x_out, xn1, xn2, q, ao, h;
 };
@@ -120,6 +120,7 @@ PLayout playout(const PShape& s, const PDag& d, int32_t max_workers) {
   L.xf = take((int64_t)kMaxBatch * s.H * 4);  // hi and lo planes
   L.log = take((int64_t)d.tiles.size() * sizeof(wpk_log_rec));
   L.wqueue = take((int64_t)max_workers * 4);
+  L.pack_flag = take(4);  // set by the weight repacking if a weight is outside the fp16 range
   // per-layer activations, each buffer 256-byte aligned
   int64_t la = 0;
   auto lt = [&](int64_t bytes) {
@@ -129,11 +130,11 @@ PLayout playout(const PShape& s, const PDag& d, int32_t max_workers) {
   };
   L.x_mid = lt(R * s.H * 4);
   L.x_out = lt(R * s.H * 4);
-  L.xn1 = lt(R * s.H * 4);  // hi and lo planes
-  L.xn2 = lt(R * s.H * 4);
+  L.xn1 = lt(R * s.H * 4);  // the QKV operand: bf16 hi and lo planes
+  L.xn2 = lt(R * s.H * 2);  // the o-proj, gate/up and down operands: one fp16 plane
   L.q = lt(R * s.Hq * s.D * 4);
-  L.ao = lt(R * s.Hq * s.D * 4);
-  L.h = lt(R * s.F * 4);
+  L.ao = lt(R * s.Hq * s.D * 2);
+  L.h = lt(R * s.F * 2);
   L.act_layer = la;
   L.act = take(la * s.L);
   L.total = at;
@@ -227,7 +228,11 @@ wpk_prefill_plan* build(const wpk_model_desc* desc, int32_t batch, int32_t ctx_l
     uint16_t* dst[5];
     for (int m = 0; m < 5; ++m) {
       dst[m] = wl;
-      if (wpk_dev_prefill_pack(mats[m].src, wl, mats[m].rows, mats[m].K, nullptr) != 0) e = hipErrorLaunchFailure;
+      // QKV stays bf16 (its operand is the hi + lo bf16 pair); o, gate, up and
+      // down become fp16, the format of their single-plane operands
+      if (wpk_dev_prefill_pack(mats[m].src, wl, mats[m].rows, mats[m].K, m > 0 ? 1 : 0, (int*)(w + L.pack_flag),
+                               nullptr) != 0)
+        e = hipErrorLaunchFailure;
       wl += (int64_t)mats[m].rows * mats[m].K;
     }
     y.w_qkv = dst[0];
@@ -270,11 +275,16 @@ wpk_prefill_plan* build(const wpk_model_desc* desc, int32_t batch, int32_t ctx_l
   if (e == hipSuccess) e = up(L.rope_sin, rsn.data(), rsn.size() * 4);
   if (e == hipSuccess) e = up(L.wqueue, wq.data(), wq.size() * 4);
   if (e == hipSuccess) e = hipDeviceSynchronize();  // the weight repacking
-  if (e != hipSuccess) {
+  int32_t out_of_range = 0;
+  if (e == hipSuccess) e = hipMemcpy(&out_of_range, w + L.pack_flag, 4, hipMemcpyDeviceToHost);
+  if (e != hipSuccess || out_of_range) {
     (void)hipFree(p->d_ws);
     (void)hipFree(p->d_wpk);
     p->d_ws = nullptr;
     p->d_wpk = nullptr;
+    if (e == hipSuccess)
+      return pfail("an o-proj, gate, up or down weight is outside the fp16 range (|w| >= 65520): the prefill "
+                   "multiplies those matrices in fp16");
     return pfail(hip_msg("prefill workspace upload / weight repacking", e));
   }
   PParams& P = p->P;

@@ -265,6 +265,48 @@ def test_prefill_bad_token_latches():
         g.close()
 
 
+def test_prefill_refuses_weights_outside_the_fp16_range():
+    """The o-projection, gate/up and down products run in fp16: a down
+    weight of ~1e5 cannot be converted, and the build says so."""
+    cfg = synth.MINI
+    w = synth.make_weights(cfg)
+    w["layers"][1]["w_down"][5, 7] = np.uint16(0x47C3)  # bf16 99840
+    desc, tensors = wpk.model_from_weights(cfg, w, "cuda")
+    announce("prefill fp16 weight range")
+    plan = wpk.wpk_build_prefill(desc.desc, 2, 64, 10, None)
+    assert not plan
+    assert "fp16" in wpk.wpk_prefill_last_error(None)
+    w["layers"][1]["w_down"][5, 7] = np.uint16(0x477F)  # bf16 65280: inside the range
+    desc, tensors = wpk.model_from_weights(cfg, w, "cuda")
+    plan = wpk.wpk_build_prefill(desc.desc, 2, 64, 10, None)
+    assert plan, wpk.wpk_prefill_last_error(None)
+    wpk.wpk_prefill_destroy(plan)
+
+
+def test_prefill_fp16_activation_overflow_latches():
+    """An MLP RMSNorm gain of 1e5 drives the gate/up operand past the fp16
+    range: the norm tile latches WPK_E_RANGE (every worker then leaves through
+    the abort flag), the plan refuses to run until reset, and runs again
+    after it (latching the same error: the gains are the caller's)."""
+    cfg = synth.MINI
+    w = synth.make_weights(cfg)
+    w["layers"][0]["mlp_norm"][:] = np.float32(1e5)
+    g = Prefill(cfg, w, 2, 64, 10)
+    try:
+        prompt = synth.prompt_tokens(cfg, 2, 10, seed=3)
+        p = torch.from_numpy(prompt.astype(np.int32)).cuda()
+        announce("prefill fp16 activation overflow")
+        for _ in range(2):
+            wpk.check_prefill(wpk.wpk_prefill(g.plan, p.data_ptr(), g.kv, g.logits.data_ptr(), g.tok.data_ptr(), 0),
+                              g.plan)
+            assert wpk.wpk_prefill_sync(g.plan) == wpk.WPK_E_RANGE
+            assert wpk.wpk_prefill(g.plan, p.data_ptr(), g.kv, g.logits.data_ptr(), g.tok.data_ptr(), 0) == \
+                wpk.WPK_E_STATE
+            wpk.check_prefill(wpk.wpk_prefill_set_option(g.plan, wpk.WPK_OPT_RESET, 1), g.plan)
+    finally:
+        g.close()
+
+
 def test_split_prefill_log_places_attention_in_its_pool():
     """Two co-resident megakernels: the canonical log holds, and the attention
     tiles -- and only they -- ran on the last split_workers workers."""

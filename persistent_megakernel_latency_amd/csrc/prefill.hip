@@ -30,11 +30,12 @@ namespace {
 constexpr int kVtPitch = 40;  // bf16 elements per transposed V row (32 keys + pad)
 
 constexpr int kGBlocks = 32;  // 1 KiB fragment blocks of a matrix-core k-step: 16 weight, 8 operand hi, 8 lo
+constexpr int kGStages = 4;   // LDS stages of the matrix-core k-loop (128 KiB)
 
 struct PSmem {
   union alignas(16) {
     uint16_t vt[2][kHeadDim][kVtPitch];  // attention: one key step of V, [dim][key]
-    u32x4 gs[3][kGBlocks][64];           // matrix-core tiles: three k-steps of fragments, 16 bytes per lane
+    u32x4 gs[kGStages][kGBlocks][64];    // matrix-core tiles: four k-steps of fragments, 16 bytes per lane
   };
   float nss[kPWaves][16];  // norm tiles: each wave's sums of squares of the 16 rows
   int claim[2];
@@ -408,39 +409,49 @@ __device__ void gemm_tile(const PParams& P, const Tile& T0, PSmem& sm, int tid) 
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[j][i] = mfma(f.b[j], f.al[i], acc[j][i]);
   };
-  // Pipeline over k-steps h: three LDS stages (step h in stage h % 3) and two
-  // fragment sets in turn.  In step h a wave issues the fetch of step h + 2
-  // into its stage (last read in step h - 2), reads step h + 1's fragments
-  // from LDS (fetched in step h - 1, complete since that step's barrier), runs
-  // step h's products, waits for its fetch and meets the others at a barrier.
-  // So the fetch has a whole step of products to land in, and the fragment
-  // reads overlap the products instead of following a barrier.  Past the last
-  // step the fetch repeats it (never used).
+  // Pipeline over k-steps h: four LDS stages (step h in stage h % 4) and two
+  // fragment sets in turn.  In step h a wave issues the fetch of step h + 3
+  // into its stage (last read in step h - 2: its reads completed before that
+  // data's products in step h - 1), reads step h + 1's fragments from LDS,
+  // runs step h's products, waits for its fetch of step h + 2 (issued in
+  // step h - 1; only this step's NF fetches may still be in flight) and
+  // meets the others at a barrier, after which step h + 2's stage is
+  // complete.  So a fetch has two steps of products to land in.  The k-loop
+  // issues no other vector-memory operation, and the counter retires them in
+  // order, so "at most NF outstanding" is exactly "step h + 2 has landed".
+  // The barrier is a bare s_barrier between compiler-only fences: a
+  // workgroup fence there would wait for every outstanding LDS-destination
+  // load, this step's included.  Past the last step the fetch repeats it
+  // (never used).
+  constexpr int NF = F16 ? 3 : 4;  // fetches per wave and k-step
   const int nk = K / 32;
   auto kc = [&](int ks) { return min(ks, nk - 1); };
+  auto step_barrier = [&]() {
+    __builtin_amdgcn_s_waitcnt(0x0F70 | NF);  // vmcnt(NF), expcnt and lgkmcnt unconstrained
+    compiler_order();
+    __builtin_amdgcn_s_barrier();
+    compiler_order();
+  };
   Frag F0, F1;
   fetch(0, 0);
   fetch(1, kc(1));
-  wait_all_memory();
-  __syncthreads();
+  fetch(2, kc(2));
+  step_barrier();  // steps 0 and 1 landed
   fread(0, F0);
 #define WPK_GEMM_STEP(I, FN, FC)                                            \
   {                                                                         \
     const int h = h0 + (I);                                                 \
-    fetch(((I) + 2) % 3, kc(h + 2));                                        \
+    fetch(((I) + 3) % 4, kc(h + 3));                                        \
     __builtin_amdgcn_sched_barrier(0);                                      \
-    fread(((I) + 1) % 3, FN);                                               \
+    fread(((I) + 1) % 4, FN);                                               \
     if (h < nk) products(FC);                                               \
-    wait_all_memory();                                                      \
-    __syncthreads();                                                        \
+    step_barrier();                                                         \
   }
-  for (int h0 = 0; h0 < nk; h0 += 6) {
+  for (int h0 = 0; h0 < nk; h0 += 4) {
     WPK_GEMM_STEP(0, F1, F0)
     WPK_GEMM_STEP(1, F0, F1)
     WPK_GEMM_STEP(2, F1, F0)
     WPK_GEMM_STEP(3, F0, F1)
-    WPK_GEMM_STEP(4, F1, F0)
-    WPK_GEMM_STEP(5, F0, F1)
   }
 #undef WPK_GEMM_STEP
 
@@ -808,12 +819,18 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2))) 
   }
   __syncthreads();
   int cur = __builtin_amdgcn_readfirstlane(sm.claim[0]);
+  // a group wave 0 has seen complete (groups never un-complete within a
+  // launch): consecutive tiles of a queue mostly wait on the same row block's
+  // group, and each poll is a memory round trip (logged runs poll every tile:
+  // the log records the counter each start saw)
+  int done_group = -1;
   for (int it = 0; cur < qn; ++it) {
     const Tile T = uni(cload(P.qtiles, qb + cur));
     if (tid == 0) sm.claim[(it + 1) & 1] = (int)atomic_add(head, 1u);
     int32_t delta = 0;
-    if (wave == 0 && T.wait >= 0) {
-      if (!p_wait(P, T, epoch, &delta, lane) && lane == 0) sm.stop = 1;
+    if (wave == 0 && T.wait >= 0 && (LOG || T.wait != done_group)) {
+      if (p_wait(P, T, epoch, &delta, lane)) done_group = T.wait;
+      else if (lane == 0) sm.stop = 1;
     }
     __syncthreads();
     if (__builtin_amdgcn_readfirstlane(sm.stop)) break;

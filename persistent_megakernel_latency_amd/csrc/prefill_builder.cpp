@@ -121,7 +121,13 @@ PDag build_prefill_dag(const PShape& s) {
       gu_g[rb] = group();
       dn_g[rb] = group();
     }
-    auto rq = [&](int rb) { return rb % nq0; };  // row-block tiles: one queue (XCD) per row block
+    auto rq = [&](int rb) { return rb % nq0; };  // norm tiles: one queue (XCD) per row block
+    // matrix-core tiles: the tile's index within its operator, round robin over
+    // the queues (as a grid's workgroups go round robin over the XCDs).  With
+    // 8, 64 or 8 column blocks per row block (o, gate/up, down) each XCD keeps
+    // a fixed eighth of the weight columns for every row block, reused from
+    // its L2, instead of streaming the whole matrix once per row block.
+    auto cq = [&](int rb, int cb, int ncols) { return (rb * ncols + cb) % nq0; };
     // norms: kPNormSplit tiles of 16 rows per row block (a norm is on every
     // layer's critical path; one tile per row block took ~130 us)
     for (int rb = 0; rb < nrb; ++rb)
@@ -129,7 +135,7 @@ PDag build_prefill_dag(const PShape& s) {
         add(l == 0 ? P_EMBED : P_NORM1, l, l == 0 ? -1 : down_g[rb], n1_g[rb], rb, sub, rb / s.nrb_s, 0, 0, rq(rb));
     for (int rb = 0; rb < nrb; ++rb)
       for (int cb = 0; cb < ncq; ++cb)
-        add(P_QKV, l, n1_g[rb], qkv_g[rb / s.nrb_s], rb, cb, rb / s.nrb_s, 0, 0, rq(rb));
+        add(P_QKV, l, n1_g[rb], qkv_g[rb / s.nrb_s], rb, cb, rb / s.nrb_s, 0, 0, cq(rb, cb, ncq));
     for (int b = 0; b < s.B; ++b)
       for (int qb = 0; qb < s.nqb; ++qb)
         for (int g = 0; g < s.Hkv; ++g) {
@@ -138,13 +144,13 @@ PDag build_prefill_dag(const PShape& s) {
           add(P_ATTN, l, qkv_g[b], at_g[rb], rb, 0, b, g, qb, s.split ? nq0 + q : q);
         }
     for (int rb = 0; rb < nrb; ++rb)
-      for (int cb = 0; cb < nch; ++cb) add(P_OPROJ, l, at_g[rb], o_g[rb], rb, cb, rb / s.nrb_s, 0, 0, rq(rb));
+      for (int cb = 0; cb < nch; ++cb) add(P_OPROJ, l, at_g[rb], o_g[rb], rb, cb, rb / s.nrb_s, 0, 0, cq(rb, cb, nch));
     for (int rb = 0; rb < nrb; ++rb)
       for (int sub = 0; sub < kPNormSplit; ++sub) add(P_NORM2, l, o_g[rb], n2_g[rb], rb, sub, rb / s.nrb_s, 0, 0, rq(rb));
     for (int rb = 0; rb < nrb; ++rb)
-      for (int cb = 0; cb < ncf; ++cb) add(P_GATEUP, l, n2_g[rb], gu_g[rb], rb, cb, rb / s.nrb_s, 0, 0, rq(rb));
+      for (int cb = 0; cb < ncf; ++cb) add(P_GATEUP, l, n2_g[rb], gu_g[rb], rb, cb, rb / s.nrb_s, 0, 0, cq(rb, cb, ncf));
     for (int rb = 0; rb < nrb; ++rb)
-      for (int cb = 0; cb < nch; ++cb) add(P_DOWN, l, gu_g[rb], dn_g[rb], rb, cb, rb / s.nrb_s, 0, 0, rq(rb));
+      for (int cb = 0; cb < nch; ++cb) add(P_DOWN, l, gu_g[rb], dn_g[rb], rb, cb, rb / s.nrb_s, 0, 0, cq(rb, cb, nch));
     down_g = dn_g;
   }
   const int nf_g = group(), lm_g = group();

@@ -27,10 +27,7 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, os.path.dirname(HERE))
 
-LOG = np.dtype([("exec_count", "<i4"), ("wait_delta", "<i4"), ("worker", "<i4"), ("claim", "<i4"),
-                ("t_start", "<i8"), ("t_end", "<i8")])
-TIMING = np.dtype([("t_claim", "<i8"), ("t_inputs", "<i8"), ("t_ready", "<i8"), ("t_done", "<i8"),
-                   ("t_partials", "<i8"), ("t_end", "<i8"), ("r0", "<i8"), ("r1", "<i8")])
+from persistent_megakernel_latency_amd.timeline import LOG, TIMING  # noqa: E402  (the log's record layouts)
 
 
 GEMM_TYPES = (0, 3, 4, 5, 6)  # qkv, o-proj, gate/up, down, LM head

@@ -48,8 +48,10 @@ TIMING = np.dtype([("t_claim", "<i8"), ("t_inputs", "<i8"), ("t_ready", "<i8"), 
 
 TILE_TYPES = ["qkv", "attn", "combine", "oproj", "gateup", "down", "lm", "argmax", "norm", "norm2", "normf",
               "attnc"]
+PREFILL_TILE_TYPES = ["embed", "norm1", "qkv", "attn", "oproj", "norm2", "gateup", "down", "normf", "lm", "argmax"]
 # operators in the order a layer runs them (the phase table's rows)
-PHASE_ORDER = ["norm", "qkv", "attn", "attnc", "combine", "oproj", "gateup", "down", "lm", "argmax"]
+PHASE_ORDER = ["embed", "norm", "norm1", "qkv", "attn", "attnc", "combine", "oproj", "norm2", "gateup", "down",
+               "normf", "lm", "argmax"]
 
 
 def split_log(raw: bytes, n_tiles: int, max_workers: int):
@@ -154,12 +156,13 @@ def phase_table(rec, dag: Sequence[Sequence[int]], type_names=TILE_TYPES, layers
     tiles) and the median tile duration."""
     ty, layer = np.asarray(dag[0]), np.asarray(dag[1])
     ran = rec["exec_count"] > 0
+    qkv = type_names.index("qkv")
     out = {}
     for l in sorted(set(layer[ran].tolist())) if layers is None else layers:
         m = ran & (layer == l)
         if not m.any():
             continue
-        q = m & (ty == 0)
+        q = m & (ty == qkv)
         base = int(rec["t_start"][q].min()) if q.any() else int(rec["t_start"][m].min())
         rows = {}
         for t in sorted(set(ty[m].tolist())):
@@ -215,11 +218,11 @@ def layer_spans(rec, dag) -> Dict[int, float]:
 
 
 def markdown_summary(title: str, command: str, table, spans, step_us: float, layers=(1, 7, 14),
-                     weights_mb: Optional[Dict[str, float]] = None, breakdown=None) -> str:
+                     weights_mb: Optional[Dict[str, float]] = None, breakdown=None, what: str = "step",
+                     note: str = "a logged step also waits for each slot's loads before its arithmetic, so it runs "
+                                 "slightly slower than a timed one") -> str:
     lines = [f"# {title}", "", "Command (committed files only):", "", "```", command, "```", "",
-             f"Logged step: {step_us:.1f} µs from the first tile start to the last tile end "
-             "(a logged step also waits for each slot's loads before its arithmetic, so it runs slightly "
-             "slower than a timed one).", ""]
+             f"Logged {what}: {step_us:.1f} µs from the first tile start to the last tile end ({note}).", ""]
     for l in layers:
         if l not in table:
             continue
@@ -319,15 +322,75 @@ def run(batch: int, trace_path: Optional[str], summary_path: Optional[str], comm
             "layer_span_us": spans}
 
 
+def run_prefill(trace_path: Optional[str], summary_path: Optional[str], command: str) -> Dict[str, object]:
+    """One logged prompt prefill of the Llama-3.2-1B-shaped decoder (batch
+    16, 496-token prompts, one megakernel) after one untimed prefill: the
+    tile records (the prefill keeps no timing records) as a trace and a
+    phase table."""
+    import torch
+
+    import persistent_megakernel_latency_amd as wpk
+    import synth
+
+    cfg = synth.LLAMA_1B
+    dev = torch.device("cuda", 0)
+    desc, tensors = wpk.model_from_weights(cfg, synth.make_weights(cfg), dev)
+    batch, P, cap = 16, 496, 512
+    prompt = torch.from_numpy(synth.prompt_tokens(cfg, batch, P, seed=4).astype(np.int32)).to(dev)
+    shape = (cfg.n_layers, batch, cfg.n_kv_heads, cap, cfg.head_dim)
+    kc = torch.zeros(shape, dtype=torch.int16, device=dev)
+    vc = torch.zeros(shape, dtype=torch.int16, device=dev)
+    seq = torch.zeros(batch, dtype=torch.int32, device=dev)
+    logits = torch.empty((batch, cfg.vocab), dtype=torch.float32, device=dev)
+    tok = torch.empty(batch, dtype=torch.int32, device=dev)
+    kv = wpk.wpk_kv(kc.data_ptr(), vc.data_ptr(), seq.data_ptr())
+    plan = wpk.wpk_build_prefill(desc.desc, batch, cap, P, wpk.wpk_prefill_opts(mode=wpk.WPK_PREFILL_MEGAKERNEL))
+    if not plan:
+        raise RuntimeError("wpk_build_prefill: " + wpk.wpk_prefill_last_error(None))
+    try:
+        info = wpk.wpk_prefill_get_info(plan)
+        go = lambda: wpk.check_prefill(wpk.wpk_prefill(plan, prompt.data_ptr(), kv, logits.data_ptr(),  # noqa: E731
+                                                       tok.data_ptr(), 0), plan, "wpk_prefill")
+        go()
+        wpk.check_prefill(wpk.wpk_prefill_set_option(plan, wpk.WPK_OPT_LOG, 1), plan, "log on")
+        go()
+        wpk.check_prefill(wpk.wpk_prefill_sync(plan), plan, "wpk_prefill_sync")
+        rc, log = wpk.wpk_prefill_get_log(plan, info.n_tiles)
+        wpk.check_prefill(rc, plan, "wpk_prefill_get_log")
+        dag = wpk.wpk_prefill_get_dag(plan, info.n_tiles)[:4]
+    finally:
+        wpk.wpk_prefill_destroy(plan)
+    rec = np.frombuffer(bytes(log), dtype=LOG)
+    if not (rec["exec_count"] == 1).all():
+        raise RuntimeError("logged prefill: a tile did not run exactly once")
+    ran = rec["exec_count"] > 0
+    span = (int(rec["t_end"][ran].max()) - int(rec["t_start"][ran].min())) * TICK_US
+    table = phase_table(rec, dag, PREFILL_TILE_TYPES)
+    spans = layer_spans(rec, dag)
+    if trace_path:
+        os.makedirs(os.path.dirname(os.path.abspath(trace_path)), exist_ok=True)
+        opener = gzip.open if trace_path.endswith(".gz") else open
+        with opener(trace_path, "wt") as f:
+            json.dump(chrome_trace(rec, dag, type_names=PREFILL_TILE_TYPES), f, separators=(",", ":"))
+    if summary_path:
+        title = "Per-tile timeline of one logged prompt prefill: Llama-3.2-1B shape, batch 16, 496-token prompts"
+        with open(summary_path, "w") as f:
+            f.write(markdown_summary(title, command, table, spans, span, what="prefill",
+                                     note="one megakernel; a logged prefill records each tile's start and end"))
+    return {"prefill": True, "step_us": round(span, 1), "tiles": int(info.n_tiles), "phases": table,
+            "layer_span_us": spans}
+
+
 def main(argv=None) -> None:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--prefill", action="store_true", help="the batch-16 prompt prefill instead of a decode step")
     ap.add_argument("--trace", default=None, help="Chrome/Perfetto trace JSON to write (gzip if it ends in .gz)")
     ap.add_argument("--summary", default=None, help="markdown phase table to write")
     a = ap.parse_args(argv)
     cmd = "python -m persistent_megakernel_latency_amd.timeline " + " ".join(argv if argv is not None else sys.argv[1:])
-    res = run(a.batch, a.trace, a.summary, cmd)
-    print(json.dumps({"batch": res["batch"], "step_us": res["step_us"], "tiles": res["tiles"],
+    res = run_prefill(a.trace, a.summary, cmd) if a.prefill else run(a.batch, a.trace, a.summary, cmd)
+    print(json.dumps({"batch": res.get("batch", 16), "step_us": res["step_us"], "tiles": res["tiles"],
                       "median_layer_span_us": float(np.median([v for k, v in res["layer_span_us"].items()
                                                                if 0 < k < max(res["layer_span_us"])]))}))
 

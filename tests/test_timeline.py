@@ -123,3 +123,29 @@ def test_split_log_and_nested_parts_from_device_records():
     s = sorted((e["ts"], e["tid"]) for e in ev if e["ph"] == "s")
     f = sorted((e["ts"], e["tid"]) for e in ev if e["ph"] == "f")
     assert s == [(2.0, 0), (5.0, 1)] and f == [(3.0, 1), (6.0, 1)]
+
+
+def test_prefill_phase_table_on_a_prefill_dag():
+    """The prefill's tile types and layers, with synthetic times in tile-id
+    order (a topological order of the prefill DAG)."""
+    from tests.helpers import dummy_desc
+    cfg = synth.MINI
+    d = dummy_desc(cfg)
+    plan = wpk.wpk_build_prefill_host(d.desc, 2, 64, 48, wpk.wpk_prefill_opts(mode=wpk.WPK_PREFILL_MEGAKERNEL))
+    assert plan, wpk.wpk_prefill_last_error(None)
+    n = wpk.wpk_prefill_get_info(plan).n_tiles
+    dag = wpk.wpk_prefill_get_dag(plan, n)[:4]
+    wpk.wpk_prefill_destroy(plan)
+    rec = np.zeros(n, tl.LOG)
+    rec["exec_count"] = 1
+    rec["t_start"] = 100 * np.arange(n)
+    rec["t_end"] = 100 * np.arange(n) + 50
+    table = tl.phase_table(rec, dag, tl.PREFILL_TILE_TYPES)
+    assert sorted(table) == list(range(cfg.n_layers))
+    for l, rows in table.items():
+        assert rows["qkv"]["first_start_us"] == 0.0
+        assert rows["qkv"]["last_end_us"] <= rows["oproj"]["last_end_us"] <= rows["down"]["last_end_us"]
+        assert all(r["median_tile_us"] == 0.5 for r in rows.values())
+    assert "embed" in table[0] and "lm" in table[cfg.n_layers - 1]
+    tr = tl.chrome_trace(rec, dag, type_names=tl.PREFILL_TILE_TYPES, flows=False)
+    assert sum(1 for e in tr["traceEvents"] if e["ph"] == "X") == n
